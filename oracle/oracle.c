@@ -1,0 +1,127 @@
+/*
+ * oracle.c -- fp64 CPU oracle of the delta-rule forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg load it.  It shares no source with the GPU path.
+ *
+ * What it computes is the plain token-by-token recurrence, in fp64, with no
+ * chunking, blocking or reordering:
+ *
+ *   S <- S0 (or 0)                                  S is d_k x d_v
+ *   for each token i:
+ *       S <- g_i * S                                (gate, once per token)
+ *       for each sub-step j = 0 .. n_h-1, t = i*n_h + j:
+ *           e <- v_t - S^T k_t                      (prediction residual)
+ *           S <- S + beta_t * k_t e^T               (rank-1 write of the residual)
+ *       o_i <- scale * S^T q_i                      (read after the last sub-step)
+ *   S_final <- S
+ *
+ * Sources (cited by page title and section):
+ *  - "08 linear delta rule & DPLR" page, section 1.2 (Householder form
+ *    S_t = (I - beta k k^T) S_{t-1} + beta k v^T) and the recurrent reference
+ *    routine after section 2.3 (read v_old = S^T k, write beta k (v - v_old)^T,
+ *    output S^T (q*scale)).
+ *  - same page, section 3 (Gated DeltaNet): S_t = (I - beta k k^T) alpha_t S_{t-1}
+ *    + beta k v^T; alpha is a scalar, so the decay may be applied first.
+ *  - DeltaProduct reading notes, sections 2.2 and 2.6 (n_h ordered Householder
+ *    steps per token, H_{i,0} = g_i H_{i-1}, the pseudocode of the gated
+ *    recurrence) and section 4.1 (keys/values/betas laid out as an expanded
+ *    sequence, one output per token after its last sub-step).
+ *
+ * The gate enters as log g (fp32), exponentiated here in fp64; log g = -inf is
+ * an exact reset (g = 0).  Inputs are float32 arrays holding exactly the values
+ * the GPU receives (bf16 values are exact in float32); all arithmetic is fp64.
+ *
+ * Layouts (row-major, contiguous):
+ *   q [B, L, H, dk]      k [B, L*n_h, H, dk]   v [B, L*n_h, H, dv]
+ *   beta [B, L*n_h, H]   g_log [B, L, H] or NULL (ungated)
+ *   S0 [B, H, dk, dv] or NULL (zeros)
+ *   O [B, L, H, dv] fp64 out;  S_final [B, H, dk, dv] fp64 out or NULL.
+ *
+ * Pins: tests/test_oracle_pins.py checks this function against closed forms
+ * (Householder eigenvalues, exact write at beta = 1, the n_h = 2 mod-3 rotation,
+ * identical/orthogonal keys, beta = 2 twice, swap permutations, norm bound),
+ * brute-force materialised products, the chunked UT/WY form and the DPLR loop.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Returns 0 on success, -1 on allocation failure or bad sizes. */
+int oracle_fwd(int B, int L, int H, int dk, int dv, int nh, double scale,
+               const float* q, const float* k, const float* v, const float* beta,
+               const float* g_log, const float* S0, double* O, double* S_final,
+               int nthreads) {
+    if (B < 0 || L < 0 || H <= 0 || dk <= 0 || dv <= 0 || nh <= 0) return -1;
+    const long Lx = (long)L * nh;
+    int fail = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+#endif
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !e) { free(S); free(e); fail |= 1; continue; }
+        /* S <- S0 (or 0) */
+        for (int r = 0; r < dk; ++r)
+            for (int c = 0; c < dv; ++c)
+                S[(size_t)r * dv + c] =
+                    S0 ? (double)S0[(((size_t)b * H + h) * dk + r) * dv + c] : 0.0;
+        for (long i = 0; i < L; ++i) {
+            /* gate once per token, before its Householder steps */
+            if (g_log) {
+                const double g = exp((double)g_log[((size_t)b * L + i) * H + h]);
+                for (size_t x = 0; x < (size_t)dk * dv; ++x) S[x] *= g;
+            }
+            for (int j = 0; j < nh; ++j) {
+                const long t = i * nh + j;
+                const float* kt = k + (((size_t)b * Lx + t) * H + h) * dk;
+                const float* vt = v + (((size_t)b * Lx + t) * H + h) * dv;
+                const double bt = (double)beta[((size_t)b * Lx + t) * H + h];
+                /* e = v_t - S^T k_t */
+                for (int c = 0; c < dv; ++c) e[c] = (double)vt[c];
+                for (int r = 0; r < dk; ++r) {
+                    const double kr = (double)kt[r];
+                    const double* Sr = S + (size_t)r * dv;
+                    for (int c = 0; c < dv; ++c) e[c] -= Sr[c] * kr;
+                }
+                /* S = S + beta_t k_t e^T */
+                for (int r = 0; r < dk; ++r) {
+                    const double a = bt * (double)kt[r];
+                    double* Sr = S + (size_t)r * dv;
+                    for (int c = 0; c < dv; ++c) Sr[c] += a * e[c];
+                }
+            }
+            /* o_i = scale * S^T q_i */
+            const float* qi = q + (((size_t)b * L + i) * H + h) * dk;
+            double* oi = O + (((size_t)b * L + i) * H + h) * dv;
+            for (int c = 0; c < dv; ++c) oi[c] = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                const double qr = (double)qi[r];
+                const double* Sr = S + (size_t)r * dv;
+                for (int c = 0; c < dv; ++c) oi[c] += Sr[c] * qr;
+            }
+            for (int c = 0; c < dv; ++c) oi[c] *= scale;
+        }
+        if (S_final)
+            memcpy(S_final + ((size_t)b * H + h) * (size_t)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        free(S);
+        free(e);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Number of threads OpenMP would use (for reporting the CPU baseline). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
