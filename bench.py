@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise delta-rule forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-others]
+
+One step = one full forward pass (intra-chunk kernel, then inter-chunk kernel) over one batch of
+synthetic inputs already resident in HBM.  W untimed warm-up steps, then K timed steps bracketed
+by device synchronisation.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+Default workload: Gated DeltaNet, B=2, H=16, L=8192, d_k=d_v=128, bf16 inputs, fp32 state,
+chunk 64 (the H=16, d=128, L=8K shape the tokens/s metric is quoted on).  tokens = B * L.
+
+The line carries:
+  roofline      for the dominant kernel: algorithmic bytes per launch / its mean launch time
+                (HIP events on the launch stream over the timed steps), against 8 TB/s HBM
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the same workload
+  others        the other workloads (DeltaNet 4x8x2K, DeltaProduct n_h=2, GDN 64K, and the
+                batch-64 decode step), measured the same way, unless --no-others
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work per launch
+
+def intra_bytes(w) -> int:
+    """Kernel (a): reads k, beta, log g; writes T (input dtype) and the gate prefix."""
+    es = 2 if w.dtype == "bf16" else 4
+    NT = -(-w.Lx // w.chunk)
+    b = w.B * w.Lx * w.H * (w.dk * es + 4)
+    if w.gate:
+        b += w.B * w.L * w.H * 4
+    b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)
+    return b
+
+
+def inter_bytes(w) -> int:
+    """Kernel (b): reads q, k, v, T, gate prefix, S0; writes O, S_final."""
+    es = 2 if w.dtype == "bf16" else 4
+    NT = -(-w.Lx // w.chunk)
+    b = w.B * w.L * w.H * (w.dk + w.dv) * es           # q, O
+    b += w.B * w.Lx * w.H * (w.dk + w.dv) * es         # k, v
+    b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)  # T, gate prefix
+    b += w.B * w.H * w.dk * w.dv * 4 * (2 if w.s0 is not None else 1)
+    return b
+
+
+def inter_flops(w) -> int:
+    """Kernel (b) algorithmic flops (causal/triangular counts) per launch."""
+    C, dk, dv, nh = w.chunk, w.dk, w.dv, w.n_h
+    QR = C // nh
+    per_chunk = (2 * C * dk * dv          # K S
+                 + C * (C + 1) * dv       # T Y (lower triangular incl. diagonal)
+                 + 2 * QR * dk * dv       # Q S
+                 + 2 * C * dk * dv)       # K^T V~
+    reach = sum(t * nh + nh for t in range(QR))   # positions each token row reads
+    per_chunk += 2 * reach * (dk + dv)            # causal Q K^T and A V~
+    NT = -(-w.Lx // C)
+    return w.B * w.H * NT * per_chunk
+
+
+def intra_flops(w) -> int:
+    C, dk = w.chunk, w.dk
+    NT = -(-w.Lx // C)
+    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3)
+
+
+def decode_bytes(w) -> int:
+    es = 2 if w.dtype == "bf16" else 4
+    BH = w.B * w.H
+    return BH * (2 * w.dk * w.dv * 4 + (w.dk + w.n_h * (w.dk + w.dv) + w.dv) * es + w.n_h * 4 + (4 if w.gate else 0))
+
+
+# ------------------------------------------------------------------ timing
+
+def time_prefill(w, steps, warmup):
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    import workloads as W
+    log("[bench] generating %s" % (w,))
+    inp = W.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(x, d):
+        return None if x is None else torch.from_numpy(x).to(d).cuda()
+
+    q, k, v = dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt)
+    beta, g, S0 = dev(inp["beta"], torch.float32), dev(inp["g_log"], torch.float32), dev(inp["S0"], torch.float32)
+    del inp
+    O = torch.empty((w.B, w.L, w.H, w.dv), dtype=dt, device="cuda")
+    SF = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    nbytes = D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk, D.BF16 if w.dtype == "bf16" else D.F32)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        D.fwd_intra(k, beta, g, ws, L=w.L, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
+        D.fwd_inter(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        D.fwd_intra(k, beta, g, ws, L=w.L, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
+        ev[i][1].record()
+        D.fwd_inter(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    intra_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    inter_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "intra_ms": intra_ms, "inter_ms": inter_ms,
+            "tokens_per_s": w.B * w.L * steps / wall}
+
+
+def roofline_of(w, r):
+    """Roofline record for the dominant (longest) kernel of one prefill step."""
+    if r["inter_ms"] >= r["intra_ms"]:
+        name, ms, nb, nf = "inter_chunk", r["inter_ms"], inter_bytes(w), inter_flops(w)
+    else:
+        name, ms, nb, nf = "intra_chunk", r["intra_ms"], intra_bytes(w), intra_flops(w)
+    gbs = nb / (ms * 1e-3) / 1e9
+    tflops = nf / (ms * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": name, "kernel_ms": round(ms, 5), "bytes_per_launch": nb, "flops_per_launch": nf,
+            "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / mfma_peak, 4)}
+
+
+def time_decode(w, steps, n_states=8):
+    """`steps` back-to-back decode calls cycling over n_states independent states (8 x 64 MiB
+    exceeds the 256 MB Infinity Cache, so each step streams its state from HBM)."""
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    import workloads as W
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log("[bench] generating decode inputs %s" % (w,))
+    S0 = torch.from_numpy(W.make_decode_state(w)).cuda()
+    states = [S0.clone() for _ in range(n_states)]
+    steps_in = []
+    for t in range(steps):
+        x = W.make_decode_inputs(w, t)
+        steps_in.append({kk: (None if vv is None else torch.from_numpy(vv).to(torch.float32 if kk in ("beta", "g_log")
+                                                                              else dt).cuda())
+                         for kk, vv in x.items()})
+    O = torch.empty((w.B, 1, w.H, w.dv), dtype=dt, device="cuda")
+
+    def run(i, S):
+        x = steps_in[i]
+        D.decode(x["q"], x["k"], x["v"], x["beta"], x["g_log"], S, n_h=w.n_h, O=O)
+
+    for i in range(min(5, steps)):
+        run(i, states[i % n_states])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        run(i, states[i % n_states])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    per_step_us = ms * 1e3 / steps
+    gbs = decode_bytes(w) / (per_step_us * 1e-6) / 1e9
+    # the same loop on one state (warm: it stays in the Infinity Cache)
+    e0.record()
+    for i in range(steps):
+        run(i, states[0])
+    e1.record()
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1e3 / steps
+    return {"us_per_step": round(per_step_us, 3), "tokens_per_s": w.B * steps / (ms * 1e-3),
+            "wall_tokens_per_s": w.B * steps / wall, "achieved_GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "warm_us_per_step": round(warm_us, 3),
+            "warm_GBs": round(decode_bytes(w) / (warm_us * 1e-6) / 1e9, 1)}
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle as it stands, on the host cores, on a bounded sample of the workload: all
+    (b, h) sequences over a prefix of the tokens, sized for about `budget_s` seconds."""
+    import oracle
+    import workloads as W
+    probe_L = 128
+    x = W.make_inputs(w.replace(L=probe_L))
+    t0 = time.perf_counter()
+    oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["g_log"], x["S0"], n_h=w.n_h)
+    per_tok = (time.perf_counter() - t0) / probe_L
+    Ls = int(min(w.L, max(probe_L, budget_s / max(per_tok, 1e-9))))
+    x = W.make_inputs(w.replace(L=Ls))
+    t0 = time.perf_counter()
+    oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["g_log"], x["S0"], n_h=w.n_h)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.B * Ls / dt, 1), "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "all %d (b,h) sequences, first %d of %d tokens (%s), fp64, %.1f s" % (
+                w.B * w.H, Ls, w.L, "whole workload" if Ls == w.L else "prefix", dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdn_b2h16_l8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (one (b, h) shard of the work); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    import workloads as W
+    D.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = W.get(args.workload)
+    r = time_prefill(w, args.steps, args.warmup)
+    log("[bench] %s: %.3f ms/step (intra %.4f ms, inter %.4f ms), %.3e tokens/s" % (
+        w.name, r["ms_per_step"], r["intra_ms"], r["inter_ms"], r["tokens_per_s"]))
+    line = {
+        "metric": "tokens/s of chunkwise delta-rule fwd (H=16,d=128,L=8K) + % MFMA/HBM roofline",
+        "value": round(r["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded generators shaped like the pages' models)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
+                   "n_h": w.n_h, "chunk": w.chunk, "gate": w.gate, "state": "fp32",
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
+        "roofline": roofline_of(w, r),
+        "kernels_ms": {"intra_chunk": round(r["intra_ms"], 5), "inter_chunk": round(r["inter_ms"], 5)},
+    }
+    if not args.no_others:
+        others = {}
+        for name in ("deltanet_b4h8_l2k", "gdp2_b2h16_l4k", "gdn_b1h16_l64k"):
+            if name == w.name:
+                continue
+            try:
+                wo = W.get(name)
+                ro = time_prefill(wo, max(5, args.steps // 5), 2)
+                others[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1), "ms_per_step": round(ro["ms_per_step"], 5),
+                                "roofline": roofline_of(wo, ro)}
+                log("[bench] %s: %.3f ms/step, %.3e tokens/s" % (name, ro["ms_per_step"], ro["tokens_per_s"]))
+            except Exception as e:  # an auxiliary line must not hide the main one
+                others[name] = {"error": repr(e)}
+        try:
+            dec = time_decode(W.DECODE, W.DECODE_STEPS)
+            others[W.DECODE.name] = dec
+            log("[bench] decode: %s" % dec)
+        except Exception as e:
+            others[W.DECODE.name] = {"error": repr(e)}
+        line["others"] = others
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

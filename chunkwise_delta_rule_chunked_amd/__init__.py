@@ -1,0 +1,234 @@
+"""MI355X (gfx950) delta-rule forward pass: chunkwise prefill and recurrent decode.
+
+Thin Python binding over the C ABI of libdelta.so (include/delta.h).  It only
+marshals arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory (tensors, allocated by torch's caching
+allocator) and the current HIP stream.  There is no CPU fallback: if the HIP
+library is missing or a tensor is not on the GPU, the call raises.
+
+    import torch, chunkwise_delta_rule_chunked_amd as delta
+    O, S_final = delta.fwd(q, k, v, beta, g_log, S0, n_h=1, chunk=64)
+    O = delta.decode(q, k, v, beta, g_log, S)        # S updated in place
+
+Layouts (contiguous): q [B,L,H,dk]; k [B,L*n_h,H,dk]; v [B,L*n_h,H,dv] in bf16 or
+fp32; beta [B,L*n_h,H] and g_log [B,L,H] (log of the gate) in fp32; states
+[B,H,dk,dv] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+__all__ = ["fwd", "fwd_intra", "fwd_inter", "decode", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+           "load_library", "F32", "BF16"]
+
+F32, BF16 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libdelta.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "delta.h")
+_lib = None
+
+
+class DeltaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %d (%s)" % (where, code, strerror(code)))
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("n_h", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load_library():
+    """Load libdelta.so (built by chunkwise_delta_rule_chunked_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        raise ImportError("libdelta.so not found at %s; build it with "
+                          "`python -m chunkwise_delta_rule_chunked_amd.build`" % _LIB)
+    lib = ctypes.CDLL(_LIB)
+    P, SP = ctypes.c_void_p, ctypes.POINTER(Shape)
+    lib.delta_fwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.delta_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_inter.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_chunk_wy.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+    lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
+    lib.delta_strerror.argtypes = [ctypes.c_int]
+    lib.delta_strerror.restype = ctypes.c_char_p
+    for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_intra, lib.delta_fwd_inter,
+              lib.delta_chunk_wy, lib.delta_decode):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/delta.h declares."""
+    txt = open(_HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(delta_\w+)\s*\(", txt, flags=re.M)
+
+
+def strerror(code: int) -> str:
+    return load_library().delta_strerror(int(code)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise DeltaError(rc, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t, name, dtype=None):
+    """Pointer of a contiguous GPU tensor (or None)."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def make_shape(B, L, H, dk, dv, n_h=1, chunk=64, dtype=BF16, scale=1.0) -> Shape:
+    return Shape(int(B), int(L), int(H), int(dk), int(dv), int(n_h), int(chunk), int(dtype), float(scale))
+
+
+def workspace_bytes(B, L, H, dk, dv, n_h=1, chunk=64, dtype=BF16) -> int:
+    n = ctypes.c_size_t(0)
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, dtype)
+    _check(load_library().delta_fwd_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)),
+           "delta_fwd_workspace_bytes")
+    return int(n.value)
+
+
+def fwd(q, k, v, beta, g_log=None, S0=None, *, n_h: int = 1, chunk: int = 64, scale: float = 1.0,
+        O=None, S_final=None, workspace=None, stream=None, want_state: bool = True):
+    """Chunkwise forward pass.  Returns (O, S_final); S_final is None if want_state is False
+    and no S_final buffer is given.  Pass S_final=S0 to update the state in place."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, L, H, d]")
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, dt, scale)
+    if O is None:
+        O = torch.empty((B, L, H, dv), dtype=q.dtype, device=q.device)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(B, L, H, dk, dv, n_h, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.delta_fwd(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+                       _dev(beta, "beta", torch.float32), _dev(g_log, "g_log", torch.float32),
+                       _dev(S0, "S0", torch.float32), _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32),
+                       _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                       _stream(stream))
+    _check(rc, "delta_fwd")
+    return O, S_final
+
+
+def fwd_intra(k, beta, g_log, workspace, *, L: int, n_h: int = 1, chunk: int = 64, dv: int = None,
+              stream=None):
+    """Intra-chunk phase of fwd: T and the gate prefix into `workspace` (a uint8 GPU tensor of
+    at least workspace_bytes(...)).  dv is only used for validation (defaults to dk)."""
+    torch = _torch()
+    B, Lx, H, dk = k.shape
+    sh = make_shape(B, L, H, dk, dv or dk, n_h, chunk, _dtype_code(k))
+    rc = load_library().delta_fwd_intra(ctypes.byref(sh), _dev(k, "k", k.dtype), _dev(beta, "beta", torch.float32),
+                                        _dev(g_log, "g_log", torch.float32), _dev(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "delta_fwd_intra")
+
+
+def fwd_inter(q, k, v, S0, workspace, *, n_h: int = 1, chunk: int = 64, scale: float = 1.0, O=None,
+              S_final=None, stream=None):
+    """Inter-chunk phase of fwd, using a workspace filled by fwd_intra for the same k/beta/g_log."""
+    torch = _torch()
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, _dtype_code(q), scale)
+    rc = load_library().delta_fwd_inter(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype),
+                                        _dev(v, "v", q.dtype), _dev(S0, "S0", torch.float32),
+                                        _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32),
+                                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    _check(rc, "delta_fwd_inter")
+    return O, S_final
+
+
+def chunk_wy(k, v, beta, g_log=None, *, L: int, n_h: int = 1, chunk: int = 64, want_wu: bool = True,
+             stream=None):
+    """Intra-chunk factors T, W, U, gc (fp32) per (b, h, chunk)."""
+    torch = _torch()
+    lib = load_library()
+    B, Lx, H, dk = k.shape
+    dv = v.shape[-1]
+    if Lx != L * n_h:
+        raise ValueError("k has %d positions, expected L*n_h = %d" % (Lx, L * n_h))
+    dt = _dtype_code(k)
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, dt)
+    NT = -(-Lx // chunk)
+    dev = k.device
+    T = torch.empty((B, H, NT, chunk, chunk), dtype=torch.float32, device=dev)
+    gc = torch.empty((B, H, NT, chunk), dtype=torch.float32, device=dev)
+    W = torch.empty((B, H, NT, chunk, dk), dtype=torch.float32, device=dev) if want_wu else None
+    U = torch.empty((B, H, NT, chunk, dv), dtype=torch.float32, device=dev) if want_wu else None
+    rc = lib.delta_chunk_wy(ctypes.byref(sh), _dev(k, "k", k.dtype), _dev(v, "v", k.dtype),
+                            _dev(beta, "beta", torch.float32), _dev(g_log, "g_log", torch.float32),
+                            _dev(T, "T"), _dev(W, "W"), _dev(U, "U"), _dev(gc, "gc"), _stream(stream))
+    _check(rc, "delta_chunk_wy")
+    return {"T": T, "W": W, "U": U, "gc": gc}
+
+
+def decode(q, k, v, beta, g_log, S, *, n_h: int = 1, scale: float = 1.0, O=None, stream=None):
+    """One recurrent step per (b, h); S [B,H,dk,dv] fp32 is updated in place.  Returns O [B,1,H,dv]."""
+    torch = _torch()
+    lib = load_library()
+    B, one, H, dk = q.shape
+    if one != 1:
+        raise ValueError("decode takes one token: q must be [B, 1, H, dk]")
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    sh = make_shape(B, 1, H, dk, dv, n_h, 64, dt, scale)
+    if O is None:
+        O = torch.empty((B, 1, H, dv), dtype=q.dtype, device=q.device)
+    rc = lib.delta_decode(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+                          _dev(beta, "beta", torch.float32), _dev(g_log, "g_log", torch.float32),
+                          _dev(S, "S", torch.float32), _dev(O, "O", q.dtype), _stream(stream))
+    _check(rc, "delta_decode")
+    return O

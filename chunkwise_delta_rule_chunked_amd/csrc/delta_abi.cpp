@@ -1,0 +1,288 @@
+// C ABI of the delta-rule library: argument validation, workspace layout and kernel
+// dispatch.  Every entry point validates everything before enqueuing any work and
+// never allocates device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/delta.h"
+#include "kernels.h"
+
+using delta::DecodeParams;
+using delta::FwdParams;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, unsigned a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+size_t esize(int dtype) { return dtype == DELTA_BF16 ? 2 : 4; }
+
+// Shape checks common to all entry points.
+int check_shape(const delta_shape* s) {
+  if (!s) return DELTA_ERR_NULL_ARG;
+  if (s->B < 0 || s->L < 0 || s->H < 0 || s->n_h < 1) return DELTA_ERR_BAD_SHAPE;
+  if (s->dtype != DELTA_F32 && s->dtype != DELTA_BF16) return DELTA_ERR_UNSUPPORTED_DIM;
+  if (s->dk != 16 && s->dk != 32 && s->dk != 64 && s->dk != 128) return DELTA_ERR_UNSUPPORTED_DIM;
+  if (s->dv < 16 || s->dv > 256 || s->dv % 16 != 0) return DELTA_ERR_UNSUPPORTED_DIM;
+  // grid sizes and 64-bit element counts stay well inside what the kernels index
+  const long long Lx = (long long)s->L * s->n_h;
+  if (Lx > (1LL << 31) || (long long)s->B * s->H > (1LL << 24)) return DELTA_ERR_BAD_SHAPE;
+  return DELTA_OK;
+}
+
+int check_chunk(const delta_shape* s) {
+  if (s->chunk != 16 && s->chunk != 32 && s->chunk != 48 && s->chunk != 64) return DELTA_ERR_UNSUPPORTED_DIM;
+  if (s->chunk % s->n_h != 0) return DELTA_ERR_BAD_SHAPE;
+  const long long NT = ((long long)s->L * s->n_h + s->chunk - 1) / s->chunk;
+  if ((long long)s->B * s->H * NT > (1LL << 31) - 1) return DELTA_ERR_BAD_SHAPE;
+  return DELTA_OK;
+}
+
+FwdParams make_params(const delta_shape* s) {
+  FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = s->B;
+  p.L = s->L;
+  p.H = s->H;
+  p.DK = s->dk;
+  p.DV = s->dv;
+  p.nh = s->n_h;
+  p.C = s->chunk;
+  p.Lx = s->L * s->n_h;
+  p.NT = (p.Lx + p.C - 1) / p.C;
+  p.scale = s->scale;
+  return p;
+}
+
+size_t t_bytes(const FwdParams& p, size_t es) { return (size_t)p.B * p.H * p.NT * p.C * p.C * es; }
+size_t gc_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.C * 4; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DELTA_OK : DELTA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_chunk(s))) return rc;
+  if (!bytes) return DELTA_ERR_NULL_ARG;
+  const FwdParams p = make_params(s);
+  *bytes = align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p));
+  return DELTA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validates a forward call and fills p.  `phase`: 0 = whole pass, 1 = intra-chunk phase only
+// (needs k, beta, g_log, workspace), 2 = inter-chunk phase only (needs q, k, v, S0, O, S_final,
+// workspace).  Pointers a phase does not use are ignored.
+int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, const void* v,
+                const float* beta, const float* g_log, const float* S0, void* O, float* S_final,
+                void* workspace, size_t workspace_bytes, FwdParams& p) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_chunk(s))) return rc;
+  p = make_params(s);
+  const bool use_intra = phase != 2, use_inter = phase != 1;
+  if (!use_intra) beta = nullptr, g_log = nullptr;
+  if (!use_inter) q = nullptr, v = nullptr, S0 = nullptr, O = nullptr, S_final = nullptr;
+  const size_t es = esize(s->dtype);
+  const size_t sz_q = (size_t)p.B * p.L * p.H * p.DK * es, sz_k = (size_t)p.B * p.Lx * p.H * p.DK * es,
+               sz_v = (size_t)p.B * p.Lx * p.H * p.DV * es, sz_b = (size_t)p.B * p.Lx * p.H * 4,
+               sz_g = (size_t)p.B * p.L * p.H * 4, sz_S = (size_t)p.B * p.H * p.DK * p.DV * 4,
+               sz_o = (size_t)p.B * p.L * p.H * p.DV * es;
+  // a pointer is required when its tensor is not empty
+  if ((sz_k && !k) || (use_inter && ((sz_q && !q) || (sz_v && !v) || (sz_o && !O))) ||
+      (use_intra && sz_b && !beta))
+    return DELTA_ERR_NULL_ARG;
+  size_t need = 0;
+  delta_fwd_workspace_bytes(s, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DELTA_ERR_WORKSPACE;
+  // q, k, v, O, the states and the workspace are moved with 16-byte vector accesses; beta and
+  // g_log are read as scalars
+  const void* ptrs[] = {q, k, v, S0, O, S_final, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4) || !aligned(g_log, 4)) return DELTA_ERR_MISALIGNED;
+
+  const Range in[] = {range(q, q ? sz_q : 0), range(k, sz_k), range(v, v ? sz_v : 0),
+                      range(beta, beta ? sz_b : 0), range(g_log, g_log ? sz_g : 0), range(S0, S0 ? sz_S : 0)};
+  const Range ro = range(O, O ? sz_o : 0), rs = range(S_final, S_final ? sz_S : 0), rw = range(workspace, need);
+  for (const Range& r : in) {
+    if (overlap(ro, r) || overlap(rw, r)) return DELTA_ERR_ALIAS;
+    // S_final may be exactly S0 (in-place); any other overlap with an input is an error
+    if (overlap(rs, r) && !(S0 && S_final == S0 && r.lo == reinterpret_cast<uintptr_t>(S0))) return DELTA_ERR_ALIAS;
+  }
+  if (overlap(ro, rs) || overlap(ro, rw) || overlap(rs, rw)) return DELTA_ERR_ALIAS;
+
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g_log = g_log;
+  p.S0 = S0;
+  p.O = O;
+  p.S_final = S_final;
+  p.T = workspace;
+  p.gc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(t_bytes(p, es)));
+  return DELTA_OK;
+}
+
+int run_intra(const FwdParams& p, bool bf, hipStream_t st) {
+  if (p.B * p.H * p.NT == 0) return DELTA_OK;
+  return hip_status(delta::launch_intra_chunk(p, bf, false, st));
+}
+
+int run_inter(const FwdParams& p, bool bf, hipStream_t st) {
+  if (p.B * p.H == 0) return DELTA_OK;
+  // L == 0: no chunks; the inter-chunk kernel still writes S_final = S0 (or zeros)
+  if (p.NT == 0 && !p.S_final) return DELTA_OK;
+  return hip_status(delta::launch_inter_chunk(p, bf, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+              const float* g_log, const float* S0, void* O, float* S_final, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  FwdParams p;
+  int rc = prepare_fwd(s, 0, q, k, v, beta, g_log, S0, O, S_final, workspace, workspace_bytes, p);
+  if (rc) return rc;
+  const bool bf = s->dtype == DELTA_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = run_intra(p, bf, st))) return rc;
+  return run_inter(p, bf, st);
+}
+
+int delta_fwd_intra(const delta_shape* s, const void* k, const float* beta, const float* g_log,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  FwdParams p;
+  int rc = prepare_fwd(s, 1, nullptr, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
+                       workspace_bytes, p);
+  if (rc) return rc;
+  return run_intra(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream));
+}
+
+int delta_fwd_inter(const delta_shape* s, const void* q, const void* k, const void* v, const float* S0,
+                    void* O, float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdParams p;
+  int rc = prepare_fwd(s, 2, q, k, v, nullptr, nullptr, S0, O, S_final, workspace, workspace_bytes, p);
+  if (rc) return rc;
+  return run_inter(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream));
+}
+
+int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const float* beta,
+                   const float* g_log, float* T, float* W, float* U, float* gc, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_chunk(s))) return rc;
+  FwdParams p = make_params(s);
+  const size_t es = esize(s->dtype);
+  if (p.B * p.H * p.NT > 0 && (!k || !beta || !T || !gc || (U && !v))) return DELTA_ERR_NULL_ARG;
+  const void* ptrs[] = {k, v, T, W, U, gc};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4) || !aligned(g_log, 4)) return DELTA_ERR_MISALIGNED;
+  const Range in[] = {range(k, (size_t)p.B * p.Lx * p.H * p.DK * es),
+                      range(v, v ? (size_t)p.B * p.Lx * p.H * p.DV * es : 0),
+                      range(beta, (size_t)p.B * p.Lx * p.H * 4),
+                      range(g_log, g_log ? (size_t)p.B * p.L * p.H * 4 : 0)};
+  const Range out[] = {range(T, t_bytes(p, 4)), range(gc, gc_bytes(p)),
+                       range(W, W ? (size_t)p.B * p.H * p.NT * p.C * p.DK * 4 : 0),
+                       range(U, U ? (size_t)p.B * p.H * p.NT * p.C * p.DV * 4 : 0)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return DELTA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return DELTA_ERR_ALIAS;
+  }
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g_log = g_log;
+  p.T = T;
+  p.gc = gc;
+  p.W = W;
+  p.U = U;
+  const bool bf = s->dtype == DELTA_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.B * p.H * p.NT == 0) return DELTA_OK;
+  if ((rc = hip_status(delta::launch_intra_chunk(p, bf, true, st)))) return rc;
+  if (W || U) return hip_status(delta::launch_wy_factors(p, bf, st));
+  return DELTA_OK;
+}
+
+int delta_decode(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+                 const float* g_log, float* S, void* O, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->L != 1) return DELTA_ERR_BAD_SHAPE;
+  if ((size_t)s->B * s->H > 0 && (!q || !k || !v || !beta || !S || !O)) return DELTA_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, S, O};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4) || !aligned(g_log, 4)) return DELTA_ERR_MISALIGNED;
+  const size_t es = esize(s->dtype);
+  const size_t BH = (size_t)s->B * s->H;
+  const Range in[] = {range(q, BH * s->dk * es), range(k, BH * s->n_h * s->dk * es),
+                      range(v, BH * s->n_h * s->dv * es), range(beta, BH * s->n_h * 4),
+                      range(g_log, g_log ? BH * 4 : 0)};
+  const Range rS = range(S, BH * s->dk * s->dv * 4), rO = range(O, BH * s->dv * es);
+  for (const Range& r : in)
+    if (overlap(rS, r) || overlap(rO, r)) return DELTA_ERR_ALIAS;
+  if (overlap(rS, rO)) return DELTA_ERR_ALIAS;
+
+  if (BH == 0) return DELTA_OK;
+  DecodeParams p;
+  p.B = s->B;
+  p.H = s->H;
+  p.DK = s->dk;
+  p.DV = s->dv;
+  p.nh = s->n_h;
+  p.scale = s->scale;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g_log = g_log;
+  p.S = S;
+  p.O = O;
+  return hip_status(delta::launch_decode(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+const char* delta_strerror(int code) {
+  switch (code) {
+    case DELTA_OK: return "ok";
+    case DELTA_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case DELTA_ERR_BAD_SHAPE: return "bad shape (negative size, n_h < 1, chunk not a multiple of n_h, or too large)";
+    case DELTA_ERR_UNSUPPORTED_DIM:
+      return "unsupported dimension (dk in {16,32,64,128}, dv a multiple of 16 in [16,256], chunk in "
+             "{16,32,48,64}, dtype f32 or bf16)";
+    case DELTA_ERR_MISALIGNED: return "a tensor pointer is misaligned (16 bytes; 4 for beta and g_log)";
+    case DELTA_ERR_WORKSPACE: return "workspace missing or smaller than delta_fwd_workspace_bytes";
+    case DELTA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case DELTA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Launch interface between the C ABI (delta_abi.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace delta {
+
+// One forward problem after validation.  Lx = L * nh expanded positions, NT chunks.
+struct FwdParams {
+  int B, L, H, DK, DV, nh, C, Lx, NT;
+  float scale;
+  const void* q;        // [B, L, H, DK]
+  const void* k;        // [B, Lx, H, DK]
+  const void* v;        // [B, Lx, H, DV]
+  const float* beta;    // [B, Lx, H]
+  const float* g_log;   // [B, L, H] or nullptr
+  const float* S0;      // [B, H, DK, DV] or nullptr
+  void* O;              // [B, L, H, DV]
+  float* S_final;       // [B, H, DK, DV] or nullptr
+  void* T;              // [B, H, NT, C, C]: element type of the inputs, or float for chunk_wy
+  float* gc;            // [B, H, NT, C] cumulative in-chunk log gate
+  float* W;             // chunk_wy only: [B, H, NT, C, DK]
+  float* U;             // chunk_wy only: [B, H, NT, C, DV]
+};
+
+struct DecodeParams {
+  int B, H, DK, DV, nh;
+  float scale;
+  const void* q;        // [B, 1, H, DK]
+  const void* k;        // [B, nh, H, DK]
+  const void* v;        // [B, nh, H, DV]
+  const float* beta;    // [B, nh, H]
+  const float* g_log;   // [B, 1, H] or nullptr
+  float* S;             // [B, H, DK, DV], in place
+  void* O;              // [B, 1, H, DV]
+};
+
+// Each returns hipSuccess or the launch error.  `bf16` selects the element type of
+// q/k/v/O (true: bfloat16, false: float32).
+hipError_t launch_intra_chunk(const FwdParams& p, bool bf16, bool t_as_float, hipStream_t st);
+hipError_t launch_wy_factors(const FwdParams& p, bool bf16, hipStream_t st);
+hipError_t launch_inter_chunk(const FwdParams& p, bool bf16, hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
+
+}  // namespace delta

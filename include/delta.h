@@ -1,0 +1,152 @@
+/*
+ * delta.h -- C ABI of the MI355X (gfx950) delta-rule forward library.
+ *
+ * The operation is the fast-weight recurrence
+ *
+ *     S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale * S_t^T q_t
+ *
+ * with S of shape d_k x d_v, covering DeltaNet (g = 1), Gated DeltaNet (scalar g_t)
+ * and DeltaProduct (n_h Householder steps per token).  Sources, by page and section:
+ *   - "08 linear delta rule & DPLR" page: section 1.2 (Householder form), section 2
+ *     (WY representation, UT transform, chunkwise algorithm), section 3 (Gated
+ *     DeltaNet and its chunkwise form with decays).
+ *   - DeltaProduct reading notes: sections 2.2, 2.6 (n_h ordered steps per token,
+ *     gate applied once before them) and 4.1 (expanded-sequence layout: keys,
+ *     values and betas of a token's sub-steps adjacent; one output per token after
+ *     its last sub-step).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or retains them.  All tensors are contiguous, row-major.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream); no entry point synchronises the host.
+ *   - Argument errors are detected before anything is enqueued: the call returns
+ *     a negative code and writes nothing.  Launch failures return DELTA_ERR_HIP.
+ *   - The library keeps no state between calls and may be called from several
+ *     host threads at once.
+ *   - Keys are used as given: L2 normalisation belongs to the caller.
+ *   - g_log is the LOG of the gate (finite, <= 0 expected; a positive value is
+ *     computed as given but the chunk form's decay ratios may overflow).
+ */
+#ifndef DELTA_H
+#define DELTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and O.  beta, g_log and the state are always float32. */
+enum { DELTA_F32 = 0, DELTA_BF16 = 1 };
+
+/* Return codes. */
+enum {
+  DELTA_OK = 0,
+  DELTA_ERR_NULL_ARG = -1,        /* a required pointer is NULL */
+  DELTA_ERR_BAD_SHAPE = -2,       /* negative size, n_h < 1, chunk not a multiple of n_h, too large */
+  DELTA_ERR_UNSUPPORTED_DIM = -3, /* dk not in {16,32,64,128}, dv not a multiple of 16 in [16,256],
+                                     chunk not in {16,32,48,64}, unknown dtype */
+  DELTA_ERR_MISALIGNED = -4,      /* a tensor pointer is not 16-byte aligned (beta, g_log: 4-byte) */
+  DELTA_ERR_WORKSPACE = -5,       /* workspace NULL or smaller than delta_fwd_workspace_bytes */
+  DELTA_ERR_ALIAS = -6,           /* S_final partially overlaps S0, or an output overlaps an input */
+  DELTA_ERR_HIP = -7              /* a HIP launch or runtime call failed */
+};
+
+/* Problem description shared by all entry points. */
+typedef struct delta_shape {
+  int32_t B;      /* batch size, >= 0 (0: nothing to do) */
+  int32_t L;      /* tokens per sequence (NOT expanded), >= 0 (delta_decode: must be 1);
+                     L = 0 writes S_final = S0 (or zeros) and no output */
+  int32_t H;      /* heads, >= 0 (0: nothing to do) */
+  int32_t dk;     /* key/query head dim: 16, 32, 64 or 128 */
+  int32_t dv;     /* value head dim: a multiple of 16 in [16, 256] */
+  int32_t n_h;    /* Householder steps per token (DeltaProduct), >= 1; 1 = DeltaNet / GDN */
+  int32_t chunk;  /* chunk length C in expanded positions: 16, 32, 48 or 64, a multiple of n_h.
+                     Results do not depend on C beyond rounding. */
+  int32_t dtype;  /* DELTA_F32 or DELTA_BF16 */
+  float scale;    /* readout scale: o = scale * S^T q */
+} delta_shape;
+
+/*
+ * Bytes of device workspace delta_fwd needs for this shape (a function of B, H, L,
+ * n_h, chunk and dtype only).  Holds, per chunk, the UT-transform matrix T and the
+ * in-chunk cumulative log gate.  Returns DELTA_OK and sets *bytes, or an error code.
+ */
+int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes);
+
+/*
+ * Chunkwise-parallel forward pass ("08 linear delta rule & DPLR", sections 2.2-2.3 and
+ * section 3; DeltaProduct notes, section 4.1).
+ *
+ *   q      [B, L, H, dk]          dtype      queries, one per token
+ *   k      [B, L*n_h, H, dk]      dtype      keys; the n_h sub-steps of a token are adjacent
+ *   v      [B, L*n_h, H, dv]      dtype      values, same layout as k
+ *   beta   [B, L*n_h, H]          float32    write strengths (any real; (0,2) allows negative
+ *                                            eigenvalues)
+ *   g_log  [B, L, H]              float32    log gate per token, or NULL for an ungated model;
+ *                                            applied once per token, before its first sub-step
+ *   S0     [B, H, dk, dv]         float32    initial state, or NULL for zeros
+ *   O      [B, L, H, dv]          dtype      output (written, rounded to nearest even for bf16)
+ *   S_final[B, H, dk, dv]         float32    final state, or NULL; may equal S0 exactly
+ *                                            (in-place update), must not partially overlap it
+ *   workspace                     device memory of at least delta_fwd_workspace_bytes bytes,
+ *                                 16-byte aligned; contents on entry are ignored; may be NULL
+ *                                 when that size is 0
+ *
+ * L*n_h need not be a multiple of the chunk: the tail chunk is padded internally with
+ * zero keys, values and betas, which leave the state unchanged.
+ * Tensor pointers must be 16-byte aligned, except beta and g_log (4-byte).
+ */
+int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
+              const float* beta, const float* g_log, const float* S0, void* O,
+              float* S_final, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two phases of delta_fwd, for callers that schedule them separately (and for per-kernel
+ * timing).  delta_fwd_intra computes, per chunk, the UT-transform matrix T and the in-chunk
+ * cumulative log gate into the workspace (from k, beta, g_log only); delta_fwd_inter then runs
+ * the state recurrence and the outputs from q, k, v, S0 and that workspace.  Calling
+ * delta_fwd_intra then delta_fwd_inter on one stream with the same arguments and workspace
+ * computes exactly what delta_fwd computes.  Arguments as for delta_fwd.
+ */
+int delta_fwd_intra(const delta_shape* s, const void* k, const float* beta, const float* g_log,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int delta_fwd_inter(const delta_shape* s, const void* q, const void* k, const void* v,
+                    const float* S0, void* O, float* S_final, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Intra-chunk factors only, for inspection and testing ("08 linear delta rule & DPLR",
+ * section 2.2 UT transform, section 3 gated form).  Per chunk n of each (b, h):
+ *   gc[i]  = sum_{j<=i} log g at position j of the chunk (g at each token's first sub-step)
+ *   T      = (I + strictLower(diag(beta) (Gamma * K K^T)))^-1 diag(beta),
+ *            Gamma_ij = exp(gc_i - gc_j)
+ *   W      = T (exp(gc) * K),   U = T V
+ * Outputs (float32, device): T [B, H, NT, C, C], W [B, H, NT, C, dk], U [B, H, NT, C, dv],
+ * gc [B, H, NT, C], with NT = ceil(L*n_h / C).  W and U may be NULL (then k/v need not be
+ * read for them); T and gc are required.  Inputs as for delta_fwd.
+ */
+int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const float* beta,
+                   const float* g_log, float* T, float* W, float* U, float* gc, void* stream);
+
+/*
+ * Recurrent decode step: one token per (b, h), updating the state in place
+ * ("08 linear delta rule & DPLR", recurrent reference after section 2.3; DeltaProduct
+ * notes, section 2.6 pseudocode).  s->L must be 1; s->chunk is ignored.
+ *   q [B, 1, H, dk], k [B, n_h, H, dk], v [B, n_h, H, dv]   dtype
+ *   beta [B, n_h, H], g_log [B, 1, H] or NULL               float32
+ *   S [B, H, dk, dv] float32, read and overwritten with  g (prod_j F_j) S + ...
+ *   O [B, 1, H, dv] dtype
+ */
+int delta_decode(const delta_shape* s, const void* q, const void* k, const void* v,
+                 const float* beta, const float* g_log, float* S, void* O, void* stream);
+
+/* Static description of a return code. */
+const char* delta_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DELTA_H */

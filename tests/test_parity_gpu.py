@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs.  Bar: err <= 1e-4 (float32 inputs) or <= 2e-2 (bf16 inputs, fp32 state), with err the
+per-head relative error defined in tests/parity.py."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import TOL, head_rel_err, inputs_to_dev, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import chunkwise_delta_rule_chunked_amd as D  # noqa: E402
+
+
+def run_gpu(w, inp, chunk=None, **kw):
+    d = inputs_to_dev(inp, w.dtype)
+    O, S = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], n_h=w.n_h,
+                 chunk=chunk or w.chunk, **kw)
+    torch.cuda.synchronize()
+    return to_np(O), to_np(S)
+
+
+def check(w, inp, chunk=None, tol=None, heads=None):
+    """Run GPU and oracle; compare O and S_final.  heads: optional list of (b, h) to sample."""
+    say("case", w, "chunk", chunk or w.chunk)
+    O, S = run_gpu(w, inp, chunk)
+    if heads is None:
+        Or, Sr = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g_log"], inp["S0"], n_h=w.n_h)
+    else:
+        Or = np.zeros(O.shape[:1] + O.shape[1:])
+        outs = []
+        for b, h in heads:
+            q = inp["q"][b:b + 1, :, h:h + 1]
+            k = inp["k"][b:b + 1, :, h:h + 1]
+            v = inp["v"][b:b + 1, :, h:h + 1]
+            be = inp["beta"][b:b + 1, :, h:h + 1]
+            g = None if inp["g_log"] is None else inp["g_log"][b:b + 1, :, h:h + 1]
+            S0 = None if inp["S0"] is None else inp["S0"][b:b + 1, h:h + 1]
+            outs.append(oracle.fwd(q, k, v, be, g, S0, n_h=w.n_h))
+        O = np.concatenate([O[b:b + 1, :, h:h + 1] for b, h in heads], axis=2)
+        S = np.concatenate([S[b:b + 1, h:h + 1] for b, h in heads], axis=1)
+        Or = np.concatenate([o for o, _ in outs], axis=2)
+        Sr = np.concatenate([s for _, s in outs], axis=1)
+    eo = head_rel_err(O, Or, (0, 2))
+    es = head_rel_err(S, Sr, (0, 1))
+    tol = tol if tol is not None else TOL[w.dtype]
+    say("  err O %.3e  S %.3e  (tol %.0e)" % (eo, es, tol))
+    assert np.isfinite(O).all() and np.isfinite(S).all()
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+# ---------------------------------------------------------------- small cases (whole oracle)
+
+def wl(name, **kw):
+    base = dict(B=2, H=2, L=100, dk=64, dv=64, chunk=32, dtype="bf16", cfg_id=90)
+    base.update(kw)
+    return W.Workload(name, **base)
+
+
+F32_CASES = [
+    W.CONFIGS["tiny_deltanet_f32"],
+    wl("f32_gated_ragged", dtype="f32", L=77, dk=32, dv=48, chunk=32, gate="weak", s0=0.1),
+    wl("f32_dp3_c48", dtype="f32", L=50, dk=64, dv=16, chunk=48, n_h=3, gate="cfg3", key="silu_l2n",
+       beta="2sigmoid", s0=0.1),
+    wl("f32_d128_c64", dtype="f32", B=1, L=130, dk=128, dv=128, chunk=64, gate="cfg3", s0=0.1),
+    wl("f32_dk16_dv256_c16_dp2", dtype="f32", B=1, H=3, L=41, dk=16, dv=256, chunk=16, n_h=2,
+       gate="weak"),
+    wl("f32_nh4_c16", dtype="f32", B=1, L=23, dk=32, dv=32, chunk=16, n_h=4, beta="2sigmoid"),
+]
+
+BF16_CASES = [
+    wl("bf16_deltanet_d128", B=2, H=2, L=333, dk=128, dv=128, chunk=64),
+    wl("bf16_gdn_d128", B=2, H=2, L=333, dk=128, dv=128, chunk=64, gate="cfg3", s0=0.1),
+    wl("bf16_gdn_weak_d128", B=1, H=2, L=700, dk=128, dv=128, chunk=64, gate="weak", s0=0.1),
+    wl("bf16_gdp2_d128", B=1, H=2, L=300, dk=128, dv=128, chunk=64, n_h=2, gate="cfg3",
+       key="silu_l2n", beta="2sigmoid"),
+    wl("bf16_gdp2_weak_s0", B=1, H=2, L=257, dk=128, dv=128, chunk=64, n_h=2, gate="weak",
+       key="silu_l2n", beta="2sigmoid", s0=0.1),
+    wl("bf16_dp4_c32", B=1, H=3, L=90, dk=64, dv=64, chunk=32, n_h=4, key="silu_l2n", beta="2sigmoid",
+       gate="weak"),
+    wl("bf16_dp3_c48", B=2, H=1, L=95, dk=32, dv=80, chunk=48, n_h=3, gate="cfg3", key="silu_l2n",
+       beta="2sigmoid", s0=0.1),
+    wl("bf16_c16_dk16", B=2, H=2, L=61, dk=16, dv=16, chunk=16, gate="weak", s0=0.1),
+    wl("bf16_c48_dk32_dv256", B=1, H=2, L=150, dk=32, dv=256, chunk=48, gate="cfg3"),
+    wl("bf16_nh16_c16", B=1, H=2, L=20, dk=64, dv=32, chunk=16, n_h=16, key="silu_l2n", beta="2sigmoid"),
+]
+
+
+@pytest.mark.parametrize("w", F32_CASES, ids=lambda w: w.name)
+def test_fwd_f32(w):
+    check(w, W.make_inputs(w))
+
+
+@pytest.mark.parametrize("w", BF16_CASES, ids=lambda w: w.name)
+def test_fwd_bf16(w):
+    check(w, W.make_inputs(w))
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 48, 64])
+def test_chunk_size_invariance(chunk):
+    """Results do not depend on the chunk beyond rounding: every chunk size meets the bar."""
+    w = wl("bf16_weak_chunks", B=1, H=2, L=200, dk=64, dv=64, gate="weak", s0=0.1)
+    check(w, W.make_inputs(w), chunk=chunk)
+    wf = w.replace(dtype="f32")
+    check(wf, W.make_inputs(wf), chunk=chunk)
+
+
+@pytest.mark.parametrize("L", [1, 5, 16, 17, 63, 64, 65])
+def test_short_and_ragged(L):
+    for dt in ("f32", "bf16"):
+        w = wl("short", B=1, H=2, L=L, dk=64, dv=32, chunk=64 if L > 16 else 16, dtype=dt, gate="cfg3",
+               s0=0.1)
+        check(w, W.make_inputs(w))
+
+
+@pytest.mark.parametrize("beta", ["zero", "one", "two"])
+def test_beta_extremes(beta):
+    for dt in ("f32", "bf16"):
+        w = wl("beta_" + beta, B=1, H=2, L=130, dk=64, dv=32, chunk=64, dtype=dt, gate="weak", s0=0.1,
+               beta=beta)
+        check(w, W.make_inputs(w))
+
+
+def test_empty_sequence_copies_state():
+    w = wl("empty", B=2, H=2, L=0, dk=32, dv=32, dtype="f32", s0=0.1)
+    inp = W.make_inputs(w)
+    d = inputs_to_dev(inp, "f32")
+    O, S = D.fwd(d["q"], d["k"], d["v"], d["beta"], None, d["S0"], chunk=32)
+    torch.cuda.synchronize()
+    assert O.numel() == 0 and np.array_equal(to_np(S), inp["S0"])
+    O, S = D.fwd(d["q"], d["k"], d["v"], d["beta"], None, None, chunk=32)
+    torch.cuda.synchronize()
+    assert np.all(to_np(S) == 0)
+
+
+def test_in_place_state_and_determinism():
+    w = wl("inplace", B=2, H=2, L=150, dk=128, dv=64, chunk=64, gate="weak", s0=0.1)
+    inp = W.make_inputs(w)
+    d = inputs_to_dev(inp, "bf16")
+    O1, S1 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=64)
+    O2, S2 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=64)
+    Sin = d["S0"].clone()
+    O3, S3 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], Sin, chunk=64, S_final=Sin)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(S1, S2)      # bitwise deterministic
+    assert torch.equal(O1, O3) and torch.equal(S1, S3) and S3.data_ptr() == Sin.data_ptr()
+
+
+def test_segment_split():
+    """S_final of one call as S0 of the next reproduces a single call (the state is the resume point)."""
+    w = wl("split", B=1, H=2, L=300, dk=64, dv=64, chunk=64, gate="weak", s0=0.1, n_h=2,
+           key="silu_l2n", beta="2sigmoid")
+    inp = W.make_inputs(w)
+    d = inputs_to_dev(inp, "bf16")
+    c = 111
+    Oa, Sa = D.fwd(d["q"][:, :c].contiguous(), d["k"][:, :2 * c].contiguous(), d["v"][:, :2 * c].contiguous(),
+                   d["beta"][:, :2 * c].contiguous(), d["g_log"][:, :c].contiguous(), d["S0"], n_h=2)
+    Ob, Sb = D.fwd(d["q"][:, c:].contiguous(), d["k"][:, 2 * c:].contiguous(), d["v"][:, 2 * c:].contiguous(),
+                   d["beta"][:, 2 * c:].contiguous(), d["g_log"][:, c:].contiguous(), Sa, n_h=2)
+    torch.cuda.synchronize()
+    Or, Sr = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g_log"], inp["S0"], n_h=2)
+    O = np.concatenate([to_np(Oa), to_np(Ob)], axis=1)
+    assert head_rel_err(O, Or, (0, 2)) <= TOL["bf16"]
+    assert head_rel_err(to_np(Sb), Sr, (0, 1)) <= TOL["bf16"]
+
+
+def test_scale():
+    w = wl("scale", B=1, H=2, L=70, dk=32, dv=32, chunk=32, dtype="f32", gate="cfg3")
+    inp = W.make_inputs(w)
+    d = inputs_to_dev(inp, "f32")
+    O, _ = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], None, chunk=32, scale=0.125)
+    torch.cuda.synchronize()
+    Or, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g_log"], None, scale=0.125)
+    assert head_rel_err(to_np(O), Or, (0, 2)) <= TOL["f32"]
+
+
+# ---------------------------------------------------------------- intra-chunk factors
+
+@pytest.mark.parametrize("dt,chunk,n_h,gate", [("f32", 16, 1, None), ("f32", 64, 2, "cfg3"),
+                                               ("bf16", 64, 1, "cfg3"), ("bf16", 48, 3, "weak"),
+                                               ("bf16", 32, 1, None)])
+def test_chunk_wy_factors(dt, chunk, n_h, gate):
+    """T, W, U, gc of the intra-chunk kernel against oracle.ut_factors (fp64 definitions).
+    Inputs are the same (bf16-rounded) values on both sides; T is computed in fp32 on the GPU."""
+    w = wl("wy", B=1, H=2, L=(150 // n_h), dk=64, dv=48, chunk=chunk, n_h=n_h, gate=gate, dtype=dt,
+           key="silu_l2n", beta="2sigmoid")
+    inp = W.make_inputs(w)
+    say("case chunk_wy", w)
+    d = inputs_to_dev(inp, dt)
+    f = D.chunk_wy(d["k"], d["v"], d["beta"], d["g_log"], L=w.L, n_h=n_h, chunk=chunk)
+    torch.cuda.synchronize()
+    ref = oracle.ut_factors(inp["k"], inp["v"], inp["beta"], inp["g_log"], n_h=n_h, chunk=chunk)
+    for name in ("gc", "T", "W", "U"):
+        got, want = to_np(f[name]), ref[name]
+        err = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
+        say("  %s err %.3e" % (name, err))
+        assert err < 1e-4, (name, err)
+
+
+# ---------------------------------------------------------------- decode
+
+def decode_sequence(w, S, steps, heads=None):
+    """Run `steps` decode calls on the GPU from state S; return per-step O, final S (GPU) and the
+    oracle's O and S_final for the same tokens taken as one sequence (optionally only `heads`)."""
+    Sd = torch.from_numpy(S).cuda()
+    Os, stack = [], []
+    for step in range(steps):
+        inp = W.make_decode_inputs(w, step)
+        d = inputs_to_dev(dict(inp, S0=None), w.dtype)
+        Os.append(to_np(D.decode(d["q"], d["k"], d["v"], d["beta"], d["g_log"], Sd, n_h=w.n_h)))
+        stack.append(inp)
+    torch.cuda.synchronize()
+    cat = lambda key: None if stack[0][key] is None else np.concatenate([x[key] for x in stack], axis=1)
+    q, k, v, beta, g = (cat(x) for x in ("q", "k", "v", "beta", "g_log"))
+    O = np.concatenate(Os, axis=1)
+    Sg = Sd.cpu().numpy()
+    if heads is not None:
+        bs = [b for b, _ in heads]
+        hs = [h for _, h in heads]
+        pick = lambda x: None if x is None else np.stack([x[b, :, h] for b, h in heads], 1)[None]
+        q, k, v, beta, g = (pick(x) for x in (q, k, v, beta, g))
+        S = np.stack([S[b, h] for b, h in heads])[None]
+        O = np.stack([O[b, :, h] for b, h in heads], 1)[None]
+        Sg = np.stack([Sg[b, h] for b, h in heads])[None]
+    Or, Sr = oracle.fwd(q, k, v, beta, g, S, n_h=w.n_h)
+    return O, Sg, Or, Sr
+
+
+@pytest.mark.parametrize("dt,n_h,dk,dv,gate", [("f32", 1, 128, 128, "cfg3"), ("bf16", 1, 128, 128, "cfg3"),
+                                               ("bf16", 2, 128, 128, "weak"), ("f32", 3, 64, 48, None),
+                                               ("bf16", 1, 16, 16, "cfg3"), ("f32", 2, 32, 96, "weak")])
+def test_decode_steps(dt, n_h, dk, dv, gate):
+    w = W.Workload("dec", B=3, H=2, L=1, dk=dk, dv=dv, n_h=n_h, dtype=dt, gate=gate, s0=0.1, cfg_id=91,
+                   key="silu_l2n" if n_h > 1 else "l2n", beta="2sigmoid" if n_h > 1 else "sigmoid")
+    say("case decode", w)
+    O, S, Or, Sr = decode_sequence(w, W.make_decode_state(w), steps=7)
+    eo, es = head_rel_err(O, Or, (0, 2)), head_rel_err(S, Sr, (0, 1))
+    say("  err O %.3e S %.3e" % (eo, es))
+    assert eo <= TOL[dt] and es <= TOL[dt]
