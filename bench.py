@@ -41,23 +41,23 @@ def log(*a):
 # ------------------------------------------------------------------ algorithmic work per launch
 
 def intra_bytes(w) -> int:
-    """Kernel (a): reads k, beta, log g; writes T (input dtype) and the gate prefix."""
+    """Kernel (a): reads q, k, beta, log g; writes T and A (input dtype) and the gate prefix."""
     es = 2 if w.dtype == "bf16" else 4
     NT = -(-w.Lx // w.chunk)
-    b = w.B * w.Lx * w.H * (w.dk * es + 4)
+    b = w.B * w.Lx * w.H * (w.dk * es + 4) + w.B * w.L * w.H * w.dk * es
     if w.gate:
         b += w.B * w.L * w.H * 4
-    b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)
+    b += w.B * w.H * NT * w.chunk * (2 * w.chunk * es + 4)
     return b
 
 
 def inter_bytes(w) -> int:
-    """Kernel (b): reads q, k, v, T, gate prefix, S0; writes O, S_final."""
+    """Kernel (b): reads q, k, v, T, A, gate prefix, S0; writes O, S_final."""
     es = 2 if w.dtype == "bf16" else 4
     NT = -(-w.Lx // w.chunk)
     b = w.B * w.L * w.H * (w.dk + w.dv) * es           # q, O
     b += w.B * w.Lx * w.H * (w.dk + w.dv) * es         # k, v
-    b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)  # T, gate prefix
+    b += w.B * w.H * NT * w.chunk * (2 * w.chunk * es + 4)  # T, A, gate prefix
     b += w.B * w.H * w.dk * w.dv * 4 * (2 if w.s0 is not None else 1)
     return b
 
@@ -71,15 +71,17 @@ def inter_flops(w) -> int:
                  + 2 * QR * dk * dv       # Q S
                  + 2 * C * dk * dv)       # K^T V~
     reach = sum(t * nh + nh for t in range(QR))   # positions each token row reads
-    per_chunk += 2 * reach * (dk + dv)            # causal Q K^T and A V~
+    per_chunk += 2 * reach * dv                   # A V~ (causal)
     NT = -(-w.Lx // C)
     return w.B * w.H * NT * per_chunk
 
 
 def intra_flops(w) -> int:
-    C, dk = w.chunk, w.dk
+    """Kernel (a): strictly-lower Gram, the triangular inverse, causal Q K^T."""
+    C, dk, nh = w.chunk, w.dk, w.n_h
     NT = -(-w.Lx // C)
-    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3)
+    reach = sum(t * nh + nh for t in range(C // nh))
+    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3 + 2 * reach * dk)
 
 
 def decode_bytes(w) -> int:
@@ -110,7 +112,7 @@ def time_prefill(w, steps, warmup):
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
     def step():
-        D.fwd_intra(k, beta, g, ws, L=w.L, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
+        D.fwd_intra(q, k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
         D.fwd_inter(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)
 
     for _ in range(warmup):
@@ -121,7 +123,7 @@ def time_prefill(w, steps, warmup):
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        D.fwd_intra(k, beta, g, ws, L=w.L, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
+        D.fwd_intra(q, k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
         ev[i][1].record()
         D.fwd_inter(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)
         ev[i][2].record()

@@ -59,7 +59,7 @@ def load_library():
     P, SP = ctypes.c_void_p, ctypes.POINTER(Shape)
     lib.delta_fwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.delta_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-    lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_inter.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_chunk_wy.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
@@ -162,14 +162,16 @@ def fwd(q, k, v, beta, g_log=None, S0=None, *, n_h: int = 1, chunk: int = 64, sc
     return O, S_final
 
 
-def fwd_intra(k, beta, g_log, workspace, *, L: int, n_h: int = 1, chunk: int = 64, dv: int = None,
+def fwd_intra(q, k, beta, g_log, workspace, *, n_h: int = 1, chunk: int = 64, dv: int = None,
               stream=None):
-    """Intra-chunk phase of fwd: T and the gate prefix into `workspace` (a uint8 GPU tensor of
-    at least workspace_bytes(...)).  dv is only used for validation (defaults to dk)."""
+    """Intra-chunk phase of fwd: T, the gated causal Q K^T and the gate prefix into `workspace`
+    (a uint8 GPU tensor of at least workspace_bytes(...)).  dv is only used for validation
+    (defaults to dk)."""
     torch = _torch()
-    B, Lx, H, dk = k.shape
+    B, L, H, dk = q.shape
     sh = make_shape(B, L, H, dk, dv or dk, n_h, chunk, _dtype_code(k))
-    rc = load_library().delta_fwd_intra(ctypes.byref(sh), _dev(k, "k", k.dtype), _dev(beta, "beta", torch.float32),
+    rc = load_library().delta_fwd_intra(ctypes.byref(sh), _dev(q, "q", k.dtype), _dev(k, "k", k.dtype),
+                                        _dev(beta, "beta", torch.float32),
                                         _dev(g_log, "g_log", torch.float32), _dev(workspace, "workspace"),
                                         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "delta_fwd_intra")

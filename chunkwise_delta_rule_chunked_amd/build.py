@@ -19,8 +19,11 @@ LIB = os.path.join(HERE, "libdelta.so")
 SOURCES = ["intra_chunk.hip", "inter_chunk.hip", "decode.hip", "delta_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# packed fp32 VALU ops are disabled for all device code (-packed-fp32-ops)
-CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+# packed fp32 VALU ops are disabled for all device code (-packed-fp32-ops); the kernels move
+# tiles between registers and LDS through vector types of other element types, so type-based
+# alias analysis is off (-fno-strict-aliasing)
+CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-fno-strict-aliasing", "-Wall",
+          "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -61,15 +61,20 @@ struct Mfma<float> {
 
 // C(16x16) += A(16 x K) * B(K x 16): A rows at a_row0 (stride lda elements),
 // B^T rows at b_row0 (stride ldb).  K must be a multiple of 16 (of 4 for float).
+// One accumulation chain uses one instruction shape: a contraction whose K is not a
+// multiple of the long step runs entirely on the 16-deep instruction (a dependent
+// 16x16x32 -> 16x16x16 pair on one accumulator gave intermittently wrong sums on gfx950).
 template <typename E>
 __device__ inline floatx4 mma_tile(floatx4 acc, const E* a_row0, int lda, const E* b_row0, int ldb,
                                    int K, int lane) {
   const E* a = a_row0 + (lane & 15) * lda;
   const E* b = b_row0 + (lane & 15) * ldb;
-  const int Kfull = K - K % Mfma<E>::KSTEP;
-  for (int k0 = 0; k0 < Kfull; k0 += Mfma<E>::KSTEP)
-    acc = Mfma<E>::mma(Mfma<E>::load(a, k0, lane), Mfma<E>::load(b, k0, lane), acc);
-  for (int k0 = Kfull; k0 < K; k0 += Mfma<E>::KTAIL) acc = Mfma<E>::mma_tail(a, b, k0, lane, acc);
+  if (K % Mfma<E>::KSTEP == 0) {
+    for (int k0 = 0; k0 < K; k0 += Mfma<E>::KSTEP)
+      acc = Mfma<E>::mma(Mfma<E>::load(a, k0, lane), Mfma<E>::load(b, k0, lane), acc);
+  } else {
+    for (int k0 = 0; k0 < K; k0 += Mfma<E>::KTAIL) acc = Mfma<E>::mma_tail(a, b, k0, lane, acc);
+  }
   return acc;
 }
 

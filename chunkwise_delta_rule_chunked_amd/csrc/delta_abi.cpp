@@ -82,7 +82,8 @@ int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
   if ((rc = check_chunk(s))) return rc;
   if (!bytes) return DELTA_ERR_NULL_ARG;
   const FwdParams p = make_params(s);
-  *bytes = align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p));
+  // T and A (element type of the inputs), then the gate prefix
+  *bytes = 2 * align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p));
   return DELTA_OK;
 }
 
@@ -91,8 +92,8 @@ int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
 namespace {
 
 // Validates a forward call and fills p.  `phase`: 0 = whole pass, 1 = intra-chunk phase only
-// (needs k, beta, g_log, workspace), 2 = inter-chunk phase only (needs q, k, v, S0, O, S_final,
-// workspace).  Pointers a phase does not use are ignored.
+// (needs q, k, beta, g_log, workspace), 2 = inter-chunk phase only (needs q, k, v, S0, O,
+// S_final, workspace).  Pointers a phase does not use are ignored.
 int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, const void* v,
                 const float* beta, const float* g_log, const float* S0, void* O, float* S_final,
                 void* workspace, size_t workspace_bytes, FwdParams& p) {
@@ -102,14 +103,14 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
   p = make_params(s);
   const bool use_intra = phase != 2, use_inter = phase != 1;
   if (!use_intra) beta = nullptr, g_log = nullptr;
-  if (!use_inter) q = nullptr, v = nullptr, S0 = nullptr, O = nullptr, S_final = nullptr;
+  if (!use_inter) v = nullptr, S0 = nullptr, O = nullptr, S_final = nullptr;
   const size_t es = esize(s->dtype);
   const size_t sz_q = (size_t)p.B * p.L * p.H * p.DK * es, sz_k = (size_t)p.B * p.Lx * p.H * p.DK * es,
                sz_v = (size_t)p.B * p.Lx * p.H * p.DV * es, sz_b = (size_t)p.B * p.Lx * p.H * 4,
                sz_g = (size_t)p.B * p.L * p.H * 4, sz_S = (size_t)p.B * p.H * p.DK * p.DV * 4,
                sz_o = (size_t)p.B * p.L * p.H * p.DV * es;
   // a pointer is required when its tensor is not empty
-  if ((sz_k && !k) || (use_inter && ((sz_q && !q) || (sz_v && !v) || (sz_o && !O))) ||
+  if ((sz_k && !k) || (sz_q && !q) || (use_inter && ((sz_v && !v) || (sz_o && !O))) ||
       (use_intra && sz_b && !beta))
     return DELTA_ERR_NULL_ARG;
   size_t need = 0;
@@ -141,7 +142,8 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
   p.O = O;
   p.S_final = S_final;
   p.T = workspace;
-  p.gc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(t_bytes(p, es)));
+  p.A = static_cast<char*>(workspace) + align_up(t_bytes(p, es));
+  p.gc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * align_up(t_bytes(p, es)));
   return DELTA_OK;
 }
 
@@ -173,10 +175,10 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
   return run_inter(p, bf, st);
 }
 
-int delta_fwd_intra(const delta_shape* s, const void* k, const float* beta, const float* g_log,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const float* beta,
+                    const float* g_log, void* workspace, size_t workspace_bytes, void* stream) {
   FwdParams p;
-  int rc = prepare_fwd(s, 1, nullptr, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
+  int rc = prepare_fwd(s, 1, q, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
                        workspace_bytes, p);
   if (rc) return rc;
   return run_intra(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream));

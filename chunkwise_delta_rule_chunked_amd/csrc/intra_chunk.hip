@@ -1,18 +1,24 @@
 // Intra-chunk kernel: per (b, h, chunk) tile, the gate prefix, the Gram matrix K K^T on
-// MFMA and the UT transform T = (I + strictLower(diag(beta) (Gamma * K K^T)))^-1 diag(beta)
-// by forward substitution.
+// MFMA, the UT transform T = (I + strictLower(diag(beta) (Gamma * K K^T)))^-1 diag(beta),
+// and the gated causal Q K^T of the chunk.
 //
-// Sources: "08 linear delta rule & DPLR" page, section 2.2 (UT transform, triangular
-// inverse by forward substitution, small enough to stay on chip at C = 64) and section 3
-// (gated chunk form: in-chunk cumulative log decay restarting every chunk, Gram matrix
-// weighted by Gamma_ij = gamma_i / gamma_j).  DeltaProduct notes, section 4.1: on the
-// expanded sequence the token's log gate sits at its first sub-step, 0 at the others.
+// Sources: "08 linear delta rule & DPLR" page, section 2.2 (UT transform; the triangular
+// inverse by forward substitution fits on chip at C = 64; prior art blocks it as 16 x 16
+// diagonal blocks merged exactly) and section 3 (gated chunk form: in-chunk cumulative log
+// decay restarting every chunk, Gram matrix weighted by Gamma_ij = gamma_i / gamma_j).
+// DeltaProduct notes, section 4.1: on the expanded sequence the token's log gate sits at its
+// first sub-step, 0 at the others.
 //
-// One wavefront per tile.  The tile's keys are staged in LDS; the lower-triangular
-// 16x16 blocks of K K^T come from MFMA (fp32 accumulation) and are kept in registers
-// until the key tile is dead, then the scaled strictly-lower matrix A replaces it in LDS.
-// Lane c then solves column c of N = (I + A)^-1 by forward substitution with the column
-// in registers (rows of A are LDS broadcasts), and T = N diag(beta) is written row-major.
+// One workgroup of 4 wavefronts per tile.  Keys and queries are staged in LDS; the lower
+// 16 x 16 blocks of K K^T and of K Q^T come from MFMA (fp32 accumulation).  Q K^T depends
+// only on the chunk's own inputs, so it is formed here once per chunk (the inter-chunk
+// kernel would otherwise form it once per value slab).
+//
+// The unit-lower-triangular inverse N = (I + A)^-1 (A strictly lower, fp32) is blocked in
+// 16 x 16 tiles: each diagonal tile is inverted by forward substitution (lane c owns column
+// c), then the tiles below the diagonal follow diagonal by diagonal from the exact identity
+//     N_ij = -N_ii * sum_{k=j}^{i-1} A_ik N_kj          (i > j),
+// with the 16 x 16 products on fp32 MFMA.  T = N diag(beta) is written row-major.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,102 +27,192 @@ namespace delta {
 template <typename E, int DK, int C>
 struct IntraLds {
   static constexpr int PAD = 16 / sizeof(E);
-  static constexpr int LDK = DK + PAD;  // key row stride (elements)
-  static constexpr int LDA = C + 4;     // A row stride (floats), keeps 16-byte rows
-  static constexpr int KBYTES = C * LDK * (int)sizeof(E);
-  static constexpr int ABYTES = C * LDA * 4;
-  static constexpr int BYTES = KBYTES > ABYTES ? KBYTES : ABYTES;
+  static constexpr int LDK = DK + PAD;  // key / query row stride (elements)
+  static constexpr int LDA = C + 4;     // fp32 row stride of A and N
+  static constexpr int KQBYTES = 2 * C * LDK * (int)sizeof(E);
+  static constexpr int ANBYTES = 2 * C * LDA * 4 + 4 * 16 * 20 * 4;  // A, N, one 16x16 tile per wave
+  static constexpr int BYTES = KQBYTES > ANBYTES ? KQBYTES : ANBYTES;
 };
 
 template <typename E, typename TO, int DK, int C>
-__global__ __launch_bounds__(64) void intra_chunk_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   using Lds = IntraLds<E, DK, C>;
   constexpr int LDK = Lds::LDK, LDA = Lds::LDA, NB = C / 16;
+  constexpr int NBLK = NB * (NB + 1) / 2;  // lower blocks of K K^T
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::BYTES];
   __shared__ float gcs[C], bs[C];
   E* Ks = reinterpret_cast<E*>(smem);
-  float* As = reinterpret_cast<float*>(smem);
+  E* Qs = Ks + C * LDK;
+  float* As = reinterpret_cast<float*>(smem);   // after the tiles are dead
+  float* Ns = As + C * LDA;
+  float* Ps = Ns + C * LDA;                     // 4 x [16][20] per-wave product tiles
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, rq = 4 * (lane >> 4);
   const int n = blockIdx.x % p.NT;
   const int bh = blockIdx.x / p.NT;
   const int b = bh / p.H, h = bh % p.H;
   const long P0 = (long)n * C;
+  const int nh = p.nh;
+  const int QR = C / nh;               // tokens in a chunk
+  const int NQT = (QR + 15) / 16;      // token row blocks
+  const bool want_a = p.A != nullptr;
 
-  // beta and log gate of position `lane`; padded positions carry beta = 0, log g = 0
-  float beta_i = 0.f, lg = 0.f;
-  if (lane < C) {
-    const long pos = P0 + lane;
-    if (pos < p.Lx) {
-      beta_i = p.beta[((long)b * p.Lx + pos) * p.H + h];
-      if (p.g_log && (pos % p.nh) == 0) lg = p.g_log[((long)b * p.L + pos / p.nh) * p.H + h];
+  // beta and log gate of position `lane` (wave 0); padded positions carry beta = 0, log g = 0
+  if (wave == 0) {
+    float beta_i = 0.f, lg = 0.f;
+    if (lane < C) {
+      const long pos = P0 + lane;
+      if (pos < p.Lx) {
+        beta_i = p.beta[((long)b * p.Lx + pos) * p.H + h];
+        if (p.g_log && (pos % nh) == 0) lg = p.g_log[((long)b * p.L + pos / nh) * p.H + h];
+      }
+    }
+    const float gc = wave_inclusive_scan(lane < C ? lg : 0.f, lane);
+    if (lane < C) {
+      gcs[lane] = gc;
+      bs[lane] = beta_i;
+      p.gc[((long)bh * p.NT + n) * C + lane] = gc;
     }
   }
-  const float gc = wave_inclusive_scan(lane < C ? lg : 0.f, lane);
-  if (lane < C) {
-    gcs[lane] = gc;
-    bs[lane] = beta_i;
-  }
 
-  // stage the key tile [C][DK] (zero rows past the end of the sequence)
+  // stage the key tile [C][DK] and the query tile (token rows, zero past the sequence)
   constexpr int VEC = 16 / sizeof(E);
   constexpr int PER_ROW = DK / VEC;
   const E* kbase = reinterpret_cast<const E*>(p.k);
-  for (int idx = lane; idx < C * PER_ROW; idx += WAVE) {
+  const E* qbase = reinterpret_cast<const E*>(p.q);
+  for (int idx = tid; idx < C * PER_ROW; idx += 256) {
     const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
     const long pos = P0 + r;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (pos < p.Lx) val = *reinterpret_cast<const u32x4*>(kbase + (((long)b * p.Lx + pos) * p.H + h) * DK + c);
     *reinterpret_cast<u32x4*>(Ks + r * LDK + c) = val;
+    if (want_a) {
+      const long tok = (long)n * QR + r;
+      u32x4 qv = {0u, 0u, 0u, 0u};
+      if (r < QR && tok < p.L) qv = *reinterpret_cast<const u32x4*>(qbase + (((long)b * p.L + tok) * p.H + h) * DK + c);
+      *reinterpret_cast<u32x4*>(Qs + r * LDK + c) = qv;
+    }
   }
   __syncthreads();
 
-  // lower-triangular blocks of K K^T (block row i >= block column j)
-  floatx4 G[NB * (NB + 1) / 2];
+  // lower-triangular blocks of K K^T, block t = (i, j) with i >= j, dealt round-robin to waves
+  floatx4 G[(NBLK + 3) / 4];
 #pragma unroll
-  for (int i = 0, t = 0; i < NB; ++i)
-#pragma unroll
-    for (int j = 0; j <= i; ++j, ++t) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      G[t] = mma_tile<E>(acc, Ks + 16 * i * LDK, LDK, Ks + 16 * j * LDK, LDK, DK, lane);
+  for (int u = 0; u < (NBLK + 3) / 4; ++u) {
+    const int t = wave + 4 * u;
+    G[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (t < NBLK) {
+      int i = 0;
+      while ((i + 1) * (i + 2) / 2 <= t) ++i;
+      const int j = t - i * (i + 1) / 2;
+      G[u] = mma_tile<E>(G[u], Ks + 16 * i * LDK, LDK, Ks + 16 * j * LDK, LDK, DK, lane);
     }
-  __syncthreads();  // the key tile is dead: A overwrites it
+  }
 
-  // A_rc = beta_r exp(gc_r - gc_c) (K K^T)_rc for r > c
+  // Gated causal Q K^T of the chunk, stored row-major [C][C] with zeros wherever a token
+  // row may not read a position (the inter-chunk kernel reads whole rows):
+  //   A[t][j] = q_t . k_j * exp(gc_p - gc_j) for j <= p = t*n_h + n_h - 1, else 0.
+  // The block (j, t) of K Q^T holds A^T: lane's D[m][n] = A[16 t + n][16 j + m], i.e. four
+  // consecutive columns of one row.  Blocks are dealt round-robin to waves.
+  if (want_a) {
+    E* Ag = reinterpret_cast<E*>(p.A) + ((long)bh * p.NT + n) * C * C;
+    for (int blk = wave; blk < NB * NB; blk += 4) {
+      const int t = blk / NB, j = blk % NB;
+      const int trow = 16 * t + col;
+      const int ptok = trow * nh + nh - 1;
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t < NQT && 16 * j <= (min(16 * t + 15, QR - 1) * nh + nh - 1)) {
+        floatx4 d = {0.f, 0.f, 0.f, 0.f};
+        d = mma_tile<E>(d, Ks + 16 * j * LDK, LDK, Qs + 16 * t * LDK, LDK, DK, lane);
 #pragma unroll
-  for (int i = 0, t = 0; i < NB; ++i)
+        for (int r = 0; r < 4; ++r) {
+          const int pc = 16 * j + rq + r;
+          if (trow < QR && pc <= ptok) a[r] = d[r] * expf(gcs[ptok] - gcs[pc]);
+        }
+      }
+      store4<E>(Ag + trow * C + 16 * j + rq, a[0], a[1], a[2], a[3]);
+    }
+  }
+  __syncthreads();  // the key/query tiles are dead: A and N overwrite them
+
+  // A_rc = beta_r exp(gc_r - gc_c) (K K^T)_rc for r > c (0 on and above the diagonal)
 #pragma unroll
-    for (int j = 0; j <= i; ++j, ++t) {
-      const int col = 16 * j + (lane & 15);
+  for (int u = 0; u < (NBLK + 3) / 4; ++u) {
+    const int t = wave + 4 * u;
+    if (t < NBLK) {
+      int i = 0;
+      while ((i + 1) * (i + 2) / 2 <= t) ++i;
+      const int j = t - i * (i + 1) / 2;
+      const int c = 16 * j + col;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * i + 4 * (lane >> 4) + r;
-        float a = 0.f;
-        if (row > col) a = bs[row] * expf(gcs[row] - gcs[col]) * G[t][r];
-        As[row * LDA + col] = a;
+        const int row = 16 * i + rq + r;
+        As[row * LDA + c] = (row > c) ? bs[row] * expf(gcs[row] - gcs[c]) * G[u][r] : 0.f;
       }
     }
+  }
+  // N starts as zero above the block diagonal (never read there) -- only the computed tiles
+  // are read, so no clearing is needed.
   __syncthreads();
 
-  // forward substitution, lane c owns column c of N = (I + A)^-1:
-  //   N_ic = delta_ic - sum_{j<i} A_ij N_jc
-  float x[C];
+  // diagonal tiles: wave w inverts tile w by forward substitution, lane c < 16 owns column c
+  if (wave < NB && lane < 16) {
+    const int o = 16 * wave;
+    float x[16];
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    float acc = (i == lane) ? 1.f : 0.f;
-    const float* Ai = As + i * LDA;
+    for (int i = 0; i < 16; ++i) {
+      float a0 = (i == lane) ? 1.f : 0.f, a1 = 0.f;
+      const float* Ai = As + (o + i) * LDA + o;
 #pragma unroll
-    for (int j = 0; j < i; ++j) acc -= Ai[j] * x[j];
-    x[i] = acc;
+      for (int j = 0; j < i; j += 2) {
+        a0 -= Ai[j] * x[j];
+        if (j + 1 < i) a1 -= Ai[j + 1] * x[j + 1];
+      }
+      x[i] = a0 + a1;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ns[(o + i) * LDA + o + lane] = x[i];
+  }
+  __syncthreads();
+
+  // tiles below the diagonal, one block diagonal d at a time:
+  //   P = sum_{k=j}^{i-1} A_ik N_kj  (then through LDS),  N_ij = -N_ii P
+  float* Pw = Ps + wave * 16 * 20;
+  for (int d = 1; d < NB; ++d) {
+    const int i = wave + d, j = wave;   // wave w owns tile (w + d, w)
+    if (i < NB) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k) {
+        // A operand: rows of A_ik; B operand B[kk][n] = N[16k + kk][16j + n] read column-wise
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int kk = k0 + (lane >> 4);
+          acc = Mfma<float>::mma(As[(16 * i + col) * LDA + 16 * k + kk], Ns[(16 * k + kk) * LDA + 16 * j + col], acc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pw[(rq + r) * 20 + col] = acc[r];
+    }
+    __syncthreads();
+    if (i < NB) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const int kk = k0 + (lane >> 4);
+        acc = Mfma<float>::mma(Ns[(16 * i + col) * LDA + 16 * i + kk], Pw[kk * 20 + col], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ns[(16 * i + rq + r) * LDA + 16 * j + col] = -acc[r];
+    }
+    __syncthreads();
   }
 
-  // T = N diag(beta): column c scaled by beta_c; rows written coalesced across lanes
-  if (lane < C) {
-    const float bc = bs[lane];
-    TO* Tout = reinterpret_cast<TO*>(p.T) + ((long)bh * p.NT + n) * C * C;
-#pragma unroll
-    for (int i = 0; i < C; ++i) Tout[i * C + lane] = to_elem<TO>(x[i] * bc);
-    p.gc[((long)bh * p.NT + n) * C + lane] = gc;
+  // T = N diag(beta), row-major, zero above the diagonal
+  TO* Tout = reinterpret_cast<TO*>(p.T) + ((long)bh * p.NT + n) * C * C;
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int r = idx / C, c = idx % C;
+    Tout[idx] = to_elem<TO>(c <= r ? Ns[r * LDA + c] * bs[c] : 0.f);
   }
 }
 
@@ -164,7 +260,7 @@ __global__ __launch_bounds__(64) void wy_factors_kernel(FwdParams p) {
 
 template <typename E, typename TO, int DK>
 static hipError_t intra_by_c(const FwdParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)(p.B * p.H * p.NT)), block(WAVE);
+  const dim3 grid((unsigned)(p.B * p.H * p.NT)), block(256);
   switch (p.C) {
     case 16: hipLaunchKernelGGL((intra_chunk_kernel<E, TO, DK, 16>), grid, block, 0, st, p); break;
     case 32: hipLaunchKernelGGL((intra_chunk_kernel<E, TO, DK, 32>), grid, block, 0, st, p); break;

@@ -71,8 +71,9 @@ typedef struct delta_shape {
 
 /*
  * Bytes of device workspace delta_fwd needs for this shape (a function of B, H, L,
- * n_h, chunk and dtype only).  Holds, per chunk, the UT-transform matrix T and the
- * in-chunk cumulative log gate.  Returns DELTA_OK and sets *bytes, or an error code.
+ * n_h, chunk and dtype only).  Holds, per chunk, the UT-transform matrix T, the gated
+ * causal Q K^T (both C x C in the input dtype) and the in-chunk cumulative log gate.
+ * Returns DELTA_OK and sets *bytes, or an error code.
  */
 int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes);
 
@@ -105,14 +106,15 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
 
 /*
  * The two phases of delta_fwd, for callers that schedule them separately (and for per-kernel
- * timing).  delta_fwd_intra computes, per chunk, the UT-transform matrix T and the in-chunk
- * cumulative log gate into the workspace (from k, beta, g_log only); delta_fwd_inter then runs
- * the state recurrence and the outputs from q, k, v, S0 and that workspace.  Calling
+ * timing).  delta_fwd_intra computes, per chunk, the UT-transform matrix T, the gated causal
+ * Q K^T and the in-chunk cumulative log gate into the workspace (from q, k, beta, g_log only);
+ * delta_fwd_inter then runs the state recurrence and the outputs from q, k, v, S0 and that
+ * workspace.  Calling
  * delta_fwd_intra then delta_fwd_inter on one stream with the same arguments and workspace
  * computes exactly what delta_fwd computes.  Arguments as for delta_fwd.
  */
-int delta_fwd_intra(const delta_shape* s, const void* k, const float* beta, const float* g_log,
-                    void* workspace, size_t workspace_bytes, void* stream);
+int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const float* beta,
+                    const float* g_log, void* workspace, size_t workspace_bytes, void* stream);
 int delta_fwd_inter(const delta_shape* s, const void* q, const void* k, const void* v,
                     const float* S0, void* O, float* S_final, void* workspace,
                     size_t workspace_bytes, void* stream);

@@ -52,9 +52,9 @@ def test_workspace_bytes(lib):
     t_bytes = 2 * 3 * NT * 32 * 32 * 2
     gc_bytes = 2 * 3 * NT * 32 * 4
     up = lambda x: (x + 255) // 256 * 256
-    assert rc == 0 and n == up(t_bytes) + up(gc_bytes)
+    assert rc == 0 and n == 2 * up(t_bytes) + up(gc_bytes)
     rc, n32 = ws(shape(dtype=D.F32))
-    assert rc == 0 and n32 == up(t_bytes * 2) + up(gc_bytes)
+    assert rc == 0 and n32 == 2 * up(t_bytes * 2) + up(gc_bytes)
     assert ws(shape(L=0)) == (0, 0)
 
 

@@ -149,6 +149,26 @@ def test_in_place_state_and_determinism():
     assert torch.equal(O1, O3) and torch.equal(S1, S3) and S3.data_ptr() == Sin.data_ptr()
 
 
+@pytest.mark.parametrize("dk", [32, 128])
+def test_chunk48_repeatable(dk):
+    """Chunk 48 mixes 32- and 16-deep contractions; repeated calls must agree bitwise and meet the
+    bar (a dependent 16x16x32 -> 16x16x16 MFMA pair on one accumulator once gave intermittent
+    wrong sums here)."""
+    w = wl("c48_repeat", B=1, H=2, L=150, dk=dk, dv=32, chunk=48, gate="weak", s0=0.1)
+    inp = W.make_inputs(w)
+    d = inputs_to_dev(inp, "bf16")
+    runs = []
+    for _ in range(6):
+        O, S = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=48)
+        runs.append((O.clone(), S.clone()))
+    torch.cuda.synchronize()
+    for O, S in runs[1:]:
+        assert torch.equal(O, runs[0][0]) and torch.equal(S, runs[0][1])
+    Or, Sr = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g_log"], inp["S0"])
+    assert head_rel_err(to_np(runs[0][0]), Or, (0, 2)) <= TOL["bf16"]
+    assert head_rel_err(to_np(runs[0][1]), Sr, (0, 1)) <= TOL["bf16"]
+
+
 def test_segment_split():
     """S_final of one call as S0 of the next reproduces a single call (the state is the resume point)."""
     w = wl("split", B=1, H=2, L=300, dk=64, dv=64, chunk=64, gate="weak", s0=0.1, n_h=2,
