@@ -5,7 +5,7 @@
 //                             B[8*(l/16) + 0..7][l%16], D[4*(l/16) + 0..3][l%16]
 //   v_mfma_f32_16x16x4_f32:   lane l holds A[l%16][l/16], B[l/16][l%16], D as above.
 // Operands are kept in LDS "K-contiguous": an A operand as [m][k] rows, a B operand
-// transposed as [n][k] rows, so each lane's fragment is one contiguous LDS read.
+// transposed as [n][k] rows, so each lane's fragment is one contiguous LDS read (Tile below).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,18 +28,14 @@ struct Mfma<bf16> {
   static constexpr int KSTEP = 32;  // k covered by one instruction
   static constexpr int KTAIL = 16;  // a 16-deep instruction finishes K % 32 == 16
   typedef bf16x8 frag;
-  // fragment of row `row` (pointer to its first element), k-step starting at k0
-  __device__ static inline frag load(const bf16* row, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8*>(row + k0 + 8 * (lane >> 4));
-  }
   __device__ static inline floatx4 mma(frag a, frag b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // v_mfma_f32_16x16x16_bf16: lane l holds A[l%16][4*(l/16) + 0..3], B[4*(l/16) + 0..3][l%16]
-  __device__ static inline floatx4 mma_tail(const bf16* a, const bf16* b, int k0, int lane, floatx4 c) {
-    bf16x4 fa = *reinterpret_cast<const bf16x4*>(a + k0 + 4 * (lane >> 4));
-    bf16x4 fb = *reinterpret_cast<const bf16x4*>(b + k0 + 4 * (lane >> 4));
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, c, 0, 0, 0);
+  // v_mfma_f32_16x16x16_bf16: lane l holds A[l%16][4*(l/16) + 0..3], B[4*(l/16) + 0..3][l%16];
+  // a and b point at this lane's four elements
+  __device__ static inline floatx4 mma_tail(const bf16* a, const bf16* b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*reinterpret_cast<const bf16x4*>(a),
+                                                      *reinterpret_cast<const bf16x4*>(b), c, 0, 0, 0);
   }
 };
 
@@ -48,32 +44,67 @@ struct Mfma<float> {
   static constexpr int KSTEP = 4;
   static constexpr int KTAIL = 4;
   typedef float frag;
-  __device__ static inline frag load(const float* row, int k0, int lane) {
-    return row[k0 + (lane >> 4)];
-  }
   __device__ static inline floatx4 mma(frag a, frag b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
-  __device__ static inline floatx4 mma_tail(const float* a, const float* b, int k0, int lane, floatx4 c) {
-    return mma(load(a, k0, lane), load(b, k0, lane), c);
+  __device__ static inline floatx4 mma_tail(const float* a, const float* b, floatx4 c) { return mma(*a, *b, c); }
+};
+
+// A matrix tile in LDS.  Element (r, e) lives at p + r * ld + swizzled column, where the
+// 16-byte chunks of a row are permuted by XOR with (r & mask).  With bf16 operands each lane
+// of an MFMA fragment read takes one 16-byte chunk of one of 16 rows; on gfx950 such a read
+// is free of bank conflicts when the rows are 128 or 256 bytes long and chunks are swizzled
+// (mask = chunks per row - 1), or when the row stride is an odd multiple of 32 bytes
+// (measured with rocprofv3 SQ_LDS_BANK_CONFLICT).  TileLayout picks one of the two.
+template <typename E>
+struct Tile {
+  E* p;
+  int ld;    // row stride in elements
+  int mask;  // chunk swizzle mask (0 = none)
+  __device__ inline E* at(int r, int e) const {
+    constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
+    return p + r * ld + ((((e / CH) ^ (r & mask))) * CH) + (e % CH);
   }
 };
 
-// C(16x16) += A(16 x K) * B(K x 16): A rows at a_row0 (stride lda elements),
-// B^T rows at b_row0 (stride ldb).  K must be a multiple of 16 (of 4 for float).
-// One accumulation chain uses one instruction shape: a contraction whose K is not a
-// multiple of the long step runs entirely on the 16-deep instruction (a dependent
-// 16x16x32 -> 16x16x16 pair on one accumulator gave intermittently wrong sums on gfx950).
+// Smallest odd multiple of 32 that is >= b.
+constexpr int odd_multiple_of_32(int b) {
+  return ((b + 31) / 32) % 2 ? (b + 31) / 32 * 32 : (b + 31) / 32 * 32 + 32;
+}
+
+// Layout of a tile whose rows hold L elements of E.
+template <typename E, int L>
+struct TileLayout {
+  static constexpr int BYTES = L * (int)sizeof(E);
+  static constexpr bool SWZ = sizeof(E) == 2 && (BYTES == 128 || BYTES == 256);
+  static constexpr int MASK = SWZ ? BYTES / 16 - 1 : 0;
+  // otherwise pad: bf16 rows to an odd multiple of 32 bytes, fp32 rows by 16 bytes
+  static constexpr int LD = SWZ ? L : (sizeof(E) == 2 ? odd_multiple_of_32(BYTES) / 2 : L + 4);
+};
+
+template <typename E, int L>
+__device__ inline Tile<E> make_tile(E* p) {
+  return Tile<E>{p, TileLayout<E, L>::LD, TileLayout<E, L>::MASK};
+}
+
+// C(16x16) += A(16 x K) * B(K x 16): A rows a_r0.. of tile a (K along the row), B^T rows
+// b_r0.. of tile b (the B operand stored transposed, K along the row).  K must be a multiple
+// of 16 (of 4 for float).  One accumulation chain uses one instruction shape: a contraction
+// whose K is not a multiple of the long step runs entirely on the 16-deep instruction (a
+// dependent 16x16x32 -> 16x16x16 pair on one accumulator gave intermittently wrong sums on
+// gfx950).
 template <typename E>
-__device__ inline floatx4 mma_tile(floatx4 acc, const E* a_row0, int lda, const E* b_row0, int ldb,
-                                   int K, int lane) {
-  const E* a = a_row0 + (lane & 15) * lda;
-  const E* b = b_row0 + (lane & 15) * ldb;
+__device__ inline floatx4 mma_tile(floatx4 acc, const Tile<E>& a, int a_r0, const Tile<E>& b, int b_r0, int K,
+                                   int lane) {
+  const int ra = a_r0 + (lane & 15), rb = b_r0 + (lane & 15);
   if (K % Mfma<E>::KSTEP == 0) {
+    const int ko = (Mfma<E>::KSTEP / 4) * (lane >> 4);  // 8 (bf16) or 1 (fp32) per lane group
     for (int k0 = 0; k0 < K; k0 += Mfma<E>::KSTEP)
-      acc = Mfma<E>::mma(Mfma<E>::load(a, k0, lane), Mfma<E>::load(b, k0, lane), acc);
+      acc = Mfma<E>::mma(*reinterpret_cast<const typename Mfma<E>::frag*>(a.at(ra, k0 + ko)),
+                         *reinterpret_cast<const typename Mfma<E>::frag*>(b.at(rb, k0 + ko)), acc);
   } else {
-    for (int k0 = 0; k0 < K; k0 += Mfma<E>::KTAIL) acc = Mfma<E>::mma_tail(a, b, k0, lane, acc);
+    const int ko = (Mfma<E>::KTAIL / 4) * (lane >> 4);
+    for (int k0 = 0; k0 < K; k0 += Mfma<E>::KTAIL) acc = Mfma<E>::mma_tail(a.at(ra, k0 + ko), b.at(rb, k0 + ko), acc);
   }
   return acc;
 }

@@ -48,6 +48,8 @@ int check_chunk(const delta_shape* s) {
   if (s->chunk % s->n_h != 0) return DELTA_ERR_BAD_SHAPE;
   const long long NT = ((long long)s->L * s->n_h + s->chunk - 1) / s->chunk;
   if ((long long)s->B * s->H * NT > (1LL << 31) - 1) return DELTA_ERR_BAD_SHAPE;
+  // the kernels address one chunk of one sequence with 32-bit element offsets
+  if ((long long)s->chunk * s->H * (s->dk > s->dv ? s->dk : s->dv) >= (1LL << 31)) return DELTA_ERR_BAD_SHAPE;
   return DELTA_OK;
 }
 

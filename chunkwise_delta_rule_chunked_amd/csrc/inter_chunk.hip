@@ -22,21 +22,24 @@
 // Forming V~ as T (V - gamma K S) instead of materialising W = T (gamma K) (C x d_k per
 // chunk) saves a C x C x d_k contraction per slab; both are the same product.
 //
-// Schedule per chunk (3 workgroup barriers; only the state chain S -> K S -> T Y ->
-// K^T V~ -> S is sequential across chunks):
-//   phase 1  X = K S (row block per wave) -> Y^T;  O1 = Q S (token block per wave);
-//            the next chunk's global loads are issued here into registers
+// Schedule: 8 wavefronts per workgroup.  Waves 0-3 compute and never touch global memory
+// inside the chunk loop; waves 4-7 move data: while the compute waves work on chunk n they
+// issue the loads of chunk n+2 into one register set, write chunk n+1 (loaded during the
+// previous chunk into the other set) into the other half of a double-buffered LDS stage, and
+// store the previous chunk's outputs from an LDS staging tile with 16-byte stores.  (With loads and compute in the same waves, the compiler's wait
+// placement stalled the compute on the prefetch.)  Per chunk, 3 workgroup barriers:
+//   phase 1  X = K S (row block per wave) -> Y^T;  O1 = Q S (token block per wave)
 //   phase 2  V~ = T Y -> V~^T, (gamma_C/gamma V~)^T
-//   phase 3  S update -> S^T;  O = gamma O1 + A V~ -> HBM;  prefetched chunk -> LDS
-// bf16 inputs double-buffer the staged chunk in LDS, so phase 3 can write the next
-// chunk while the current one is still read; fp32 inputs (twice the bytes) use one
-// buffer and an extra barrier.
+//   phase 3  S update -> S^T;  O = scale (gamma O1 + A V~) -> LDS staging
+// Only the state chain S -> K S -> T Y -> K^T V~ -> S is sequential across chunks.
+// fp32 inputs (twice the bytes) use one staging buffer and an extra barrier.
 //
-// MFMA operands live in LDS in K-contiguous rows: K and Q row-major (A operands, and B
-// operands of K Q^T), K^T (A operand of the state update; bf16 only -- fp32 fragments
-// are single elements and read K column-wise directly), T row-major, and S^T, Y^T,
-// V~^T, (gamma_C/gamma V~)^T as B operands.  Products with bf16 inputs round the
-// operands to bf16 and accumulate in fp32; the master state stays fp32.
+// MFMA operands live in LDS in K-contiguous rows: K and Q row-major (A operands), K^T (A
+// operand of the state update; bf16 only -- fp32 fragments are single elements and read K
+// column-wise directly), T and A row-major, and S^T, Y^T, V~^T, (gamma_C/gamma V~)^T as B
+// operands.  Rows of 128 or 256 bytes use XOR-swizzled 16-byte chunks, other lengths padding
+// (see Tile in common.h), so fragment reads are free of bank conflicts.  Products with bf16
+// inputs round the operands to bf16 and accumulate in fp32; the master state stays fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,20 +48,21 @@ namespace delta {
 template <typename E, int DK, int C>
 struct InterCfg {
   static constexpr bool BF = sizeof(E) == 2;
-  static constexpr int PAD = 16 / sizeof(E);
   static constexpr int VEC = 16 / sizeof(E);   // elements per 16-byte copy
-  static constexpr int LDK = DK + PAD;          // stride of K, Q, S^T rows
-  static constexpr int LDC = C + PAD;           // stride of K^T, T, Y^T, V~^T, A rows
   static constexpr int NBUF = BF ? 2 : 1;       // staged-chunk buffers
+  using RowDK = TileLayout<E, DK>;              // rows of K, Q, S^T
+  using RowC = TileLayout<E, C>;                // rows of K^T, T, A, Y^T, V~^T
+  using Row16 = TileLayout<E, 16>;              // rows of the V slab
+  static constexpr int OLD = BF ? 24 : 20;      // output staging row stride (conflict-free stores)
   // one staged chunk: K, Q (up to C token rows), K^T (bf16 only), T, A, V slab
-  static constexpr int KS = C * LDK, QS = C * LDK, KTS = BF ? DK * LDC : 0, TS = C * LDC, AS = C * LDC,
-                       VS = C * 16;
+  static constexpr int KS = C * RowDK::LD, QS = C * RowDK::LD, KTS = BF ? DK * RowC::LD : 0,
+                       TS = C * RowC::LD, AS = C * RowC::LD, VS = C * Row16::LD;
   static constexpr int IN = KS + QS + KTS + TS + AS + VS;
-  // per-workgroup work area: S^T, Y^T, V~^T, (D V~)^T
-  static constexpr int STS = 16 * LDK, YTS = 16 * LDC;
-  static constexpr int WORK = STS + 3 * YTS;
+  // per-workgroup work area: S^T, Y^T, V~^T, (D V~)^T, output staging [C][OLD]
+  static constexpr int STS = 16 * RowDK::LD, YTS = 16 * RowC::LD, OS = C * OLD;
+  static constexpr int WORK = STS + 3 * YTS + OS;
   static constexpr int ELEMS = NBUF * IN + WORK;
-  // prefetch slots per thread (256 threads)
+  // loader slots per loader thread (256 loader threads)
   static constexpr int KITEMS = (C / 2) * (DK / VEC);   // pairs of key rows x 16-byte columns
   static constexpr int NK = (KITEMS + 255) / 256;
   static constexpr int QITEMS = C * (DK / VEC);
@@ -66,6 +70,8 @@ struct InterCfg {
   static constexpr int TITEMS = C * (C / VEC);
   static constexpr int NT = (TITEMS + 255) / 256;
   static constexpr int VITEMS = C * (16 / VEC);          // <= 256
+  static constexpr int OITEMS = C * (16 / VEC);          // 16-byte pieces of the output tile
+  static_assert(2 * NK + NQ <= 31, "validity bits of one staged chunk must fit a word");
 };
 
 __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -79,26 +85,44 @@ struct Staged {
   u32x4 a[Cfg::NT];
   u32x4 v;
   float gc;
+  uint32_t valid;  // per-load row validity (bit 2i+s: key pair i row s; 2NK+i: query i; 31: value)
+};
+
+// The LDS tiles of one staged chunk.
+template <typename E, int DK, int C>
+struct ChunkTiles {
+  using Cfg = InterCfg<E, DK, C>;
+  Tile<E> K, Q, KT, T, A, V;
+  __device__ inline explicit ChunkTiles(E* base) {
+    K = make_tile<E, DK>(base);
+    Q = make_tile<E, DK>(base + Cfg::KS);
+    KT = make_tile<E, C>(base + Cfg::KS + Cfg::QS);
+    T = make_tile<E, C>(base + Cfg::KS + Cfg::QS + Cfg::KTS);
+    A = make_tile<E, C>(base + Cfg::KS + Cfg::QS + Cfg::KTS + Cfg::TS);
+    V = make_tile<E, 16>(base + Cfg::KS + Cfg::QS + Cfg::KTS + Cfg::TS + Cfg::AS);
+  }
 };
 
 template <typename E, int DK, int C>
-__global__ __launch_bounds__(256) void inter_chunk_kernel(FwdParams p) {
+__global__ __launch_bounds__(512) void inter_chunk_kernel(FwdParams p) {
   using Cfg = InterCfg<E, DK, C>;
-  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, VEC = Cfg::VEC, NBUF = Cfg::NBUF;
+  constexpr int VEC = Cfg::VEC, NBUF = Cfg::NBUF, OLD = Cfg::OLD;
   constexpr int NBC = C / 16;          // position blocks per chunk
   constexpr int NTS = DK / 16;         // state row tiles
-  constexpr int SLOTS = (NTS + 3) / 4; // state tiles per wave
+  constexpr int SLOTS = (NTS + 3) / 4; // state tiles per compute wave
   constexpr int KSTEP = Mfma<E>::KSTEP;
 
   __shared__ __attribute__((aligned(16))) E smem[Cfg::ELEMS];
   __shared__ float egs[NBUF][C], eds[NBUF][C];  // exp(gc), exp(gc_last - gc)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool loader = wave >= 4;
+  const int ltid = tid - 256;            // loader thread index (loader waves only)
   const int NSL = p.DV / 16;
   const int BH = p.B * p.H;
 
   // workgroup -> (head, slab).  Workgroups are dispatched round-robin over the 8 XCDs;
-  // place all slabs of one head on the same XCD so their shared K/Q/T reads hit one L2.
+  // place all slabs of one head on the same XCD so their shared K/Q/T/A reads hit one L2.
   int head, slab;
   {
     const int i = blockIdx.x;
@@ -127,119 +151,173 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(FwdParams p) {
 
   // staged-chunk buffers are addressed as smem + buf * IN (plain arithmetic on the LDS array,
   // so every access stays an LDS access)
-  E* StS = smem + NBUF * Cfg::IN;
-  E* YTs = StS + Cfg::STS;
-  E* VtTs = YTs + Cfg::YTS;
-  E* DVtTs = VtTs + Cfg::YTS;
+  E* work = smem + NBUF * Cfg::IN;
+  const Tile<E> St = make_tile<E, DK>(work);                          // S^T  [16][DK]
+  const Tile<E> Yt = make_tile<E, C>(work + Cfg::STS);                // Y^T  [16][C]
+  const Tile<E> Vt = make_tile<E, C>(work + Cfg::STS + Cfg::YTS);     // V~^T [16][C]
+  const Tile<E> DVt = make_tile<E, C>(work + Cfg::STS + 2 * Cfg::YTS);  // (D V~)^T
+  E* Os = work + Cfg::STS + 3 * Cfg::YTS;                              // [C][OLD]
 
-  // ---------------- global -> registers for chunk n (all loads issued, none waited on)
+  // ---------------- loader: global -> registers for chunk n.  Every lane issues the same
+  // loads on every chunk (rows past the end read row 0 of the sequence and are zeroed when
+  // written to LDS), so the number of outstanding loads is the same on all paths and the
+  // compiler can wait for one chunk's loads while the next chunk's stay in flight.
+  // Addresses are a per-chunk uniform base plus a per-lane 32-bit offset.
+  const long HDK = (long)p.H * DK, HDV = (long)p.H * p.DV;
   auto load_chunk = [&](int n, Staged<E, DK, C>& st) {
     const long P0 = (long)n * C;
+    const int krows = (int)min((long)C, p.Lx - P0);                  // valid positions
+    const int qrows = (int)min((long)QR, (long)p.L - (long)n * QR);   // valid tokens
+    const E* kb = kg + ((long)b * p.Lx + P0) * HDK + (long)h * DK;
+    const E* qb = qg + ((long)b * p.L + (long)n * QR) * HDK + (long)h * DK;
+    const E* vb = vg + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + slab * 16;
+    const E* Tc = Tg + ((long)head * p.NT + n) * C * C;
+    const E* Ac = Ag + ((long)head * p.NT + n) * C * C;
+    uint32_t valid = 0;
 #pragma unroll
     for (int i = 0; i < Cfg::NK; ++i) {
-      const int it = tid + 256 * i;
+      const int it = min(ltid + 256 * i, Cfg::KITEMS - 1);
       const int rp = it % (C / 2), cc = it / (C / 2);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const long pos = P0 + 2 * rp + s;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (it < Cfg::KITEMS && pos < p.Lx)
-          val = *reinterpret_cast<const u32x4*>(kg + (((long)b * p.Lx + pos) * p.H + h) * DK + cc * VEC);
-        st.k[i][s] = val;
+        const bool ok = 2 * rp + s < krows;
+        valid |= (uint32_t)ok << (2 * i + s);
+        st.k[i][s] = *reinterpret_cast<const u32x4*>(kb + (ok ? (2 * rp + s) * (int)HDK : 0) + cc * VEC);
       }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NQ; ++i) {
-      const int it = tid + 256 * i;
+      const int it = min(ltid + 256 * i, Cfg::QITEMS - 1);
       const int r = it / (DK / VEC), c = (it % (DK / VEC)) * VEC;
-      const long tok = (long)n * QR + r;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (it < Cfg::QITEMS && r < QR && tok < p.L)
-        val = *reinterpret_cast<const u32x4*>(qg + (((long)b * p.L + tok) * p.H + h) * DK + c);
-      st.q[i] = val;
+      const bool ok = r < qrows;
+      valid |= (uint32_t)ok << (2 * Cfg::NK + i);
+      st.q[i] = *reinterpret_cast<const u32x4*>(qb + (ok ? r * (int)HDK : 0) + c);
     }
-    const E* Tc = Tg + ((long)head * p.NT + n) * C * C;
-    const E* Ac = Ag + ((long)head * p.NT + n) * C * C;
 #pragma unroll
     for (int i = 0; i < Cfg::NT; ++i) {
-      const int it = tid + 256 * i;
-      u32x4 tv = {0u, 0u, 0u, 0u}, av = {0u, 0u, 0u, 0u};
-      if (it < Cfg::TITEMS) {
-        tv = *reinterpret_cast<const u32x4*>(Tc + it * VEC);
-        av = *reinterpret_cast<const u32x4*>(Ac + it * VEC);
-      }
-      st.t[i] = tv;
-      st.a[i] = av;
+      const int it = min(ltid + 256 * i, Cfg::TITEMS - 1);
+      st.t[i] = *reinterpret_cast<const u32x4*>(Tc + it * VEC);
+      st.a[i] = *reinterpret_cast<const u32x4*>(Ac + it * VEC);
     }
     {
-      const int r = tid / (16 / VEC), c = (tid % (16 / VEC)) * VEC;
-      const long pos = P0 + r;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (tid < Cfg::VITEMS && pos < p.Lx)
-        val = *reinterpret_cast<const u32x4*>(vg + (((long)b * p.Lx + pos) * p.H + h) * p.DV + slab * 16 + c);
-      st.v = val;
+      const int lv = min(ltid, Cfg::VITEMS - 1);
+      const int r = lv / (16 / VEC), c = (lv % (16 / VEC)) * VEC;
+      const bool ok = r < krows;
+      valid |= (uint32_t)ok << 31;
+      st.v = *reinterpret_cast<const u32x4*>(vb + (ok ? r * (int)HDV : 0) + c);
     }
-    st.gc = (tid < C) ? p.gc[((long)head * p.NT + n) * C + tid] : 0.f;
+    st.gc = p.gc[((long)head * p.NT + n) * C + min(ltid, C - 1)];
+    st.valid = valid;
   };
 
-  // ---------------- registers -> LDS buffer `buf`
+  // ---------------- loader: registers -> LDS buffer `buf`
   auto store_chunk = [&](const Staged<E, DK, C>& st, int buf) {
-    E* Ks = smem + buf * Cfg::IN;
-    E* Qs = Ks + Cfg::KS;
-    E* KTs = Qs + Cfg::QS;
-    E* Ts = KTs + Cfg::KTS;
-    E* As = Ts + Cfg::TS;
-    E* Vs = As + Cfg::AS;
+    const ChunkTiles<E, DK, C> in(smem + buf * Cfg::IN);
 #pragma unroll
     for (int i = 0; i < Cfg::NK; ++i) {
-      const int it = tid + 256 * i;
+      const int it = ltid + 256 * i;
       if (it < Cfg::KITEMS) {
         const int rp = it % (C / 2), cc = it / (C / 2);
-        *reinterpret_cast<u32x4*>(Ks + (2 * rp) * LDK + cc * VEC) = st.k[i][0];
-        *reinterpret_cast<u32x4*>(Ks + (2 * rp + 1) * LDK + cc * VEC) = st.k[i][1];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 k0 = (st.valid >> (2 * i)) & 1u ? st.k[i][0] : z;
+        const u32x4 k1 = (st.valid >> (2 * i + 1)) & 1u ? st.k[i][1] : z;
+        *reinterpret_cast<u32x4*>(in.K.at(2 * rp, cc * VEC)) = k0;
+        *reinterpret_cast<u32x4*>(in.K.at(2 * rp + 1, cc * VEC)) = k1;
         if constexpr (Cfg::BF) {
           // K^T rows: the two key rows of this pair are adjacent, so each K^T element pair is
           // one packed 4-byte write.  Dword w of a row holds elements 2w (low) and 2w+1 (high).
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const uint32_t a = st.k[i][0][w], c = st.k[i][1][w];
-            *reinterpret_cast<uint32_t*>(KTs + (cc * VEC + 2 * w) * LDC + 2 * rp) = (a & 0xFFFFu) | (c << 16);
-            *reinterpret_cast<uint32_t*>(KTs + (cc * VEC + 2 * w + 1) * LDC + 2 * rp) = (a >> 16) | (c & 0xFFFF0000u);
+            const uint32_t lo = k0[w], hi = k1[w];
+            *reinterpret_cast<uint32_t*>(in.KT.at(cc * VEC + 2 * w, 2 * rp)) = (lo & 0xFFFFu) | (hi << 16);
+            *reinterpret_cast<uint32_t*>(in.KT.at(cc * VEC + 2 * w + 1, 2 * rp)) = (lo >> 16) | (hi & 0xFFFF0000u);
           }
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NQ; ++i) {
-      const int it = tid + 256 * i;
+      const int it = ltid + 256 * i;
       if (it < Cfg::QITEMS) {
         const int r = it / (DK / VEC), c = (it % (DK / VEC)) * VEC;
-        *reinterpret_cast<u32x4*>(Qs + r * LDK + c) = st.q[i];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(in.Q.at(r, c)) = (st.valid >> (2 * Cfg::NK + i)) & 1u ? st.q[i] : z;
       }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NT; ++i) {
-      const int it = tid + 256 * i;
+      const int it = ltid + 256 * i;
       if (it < Cfg::TITEMS) {
         const int r = (it * VEC) / C, c = (it * VEC) % C;
-        *reinterpret_cast<u32x4*>(Ts + r * LDC + c) = st.t[i];
-        *reinterpret_cast<u32x4*>(As + r * LDC + c) = st.a[i];
+        *reinterpret_cast<u32x4*>(in.T.at(r, c)) = st.t[i];
+        *reinterpret_cast<u32x4*>(in.A.at(r, c)) = st.a[i];
       }
     }
-    if (tid < Cfg::VITEMS) {
-      const int r = tid / (16 / VEC), c = (tid % (16 / VEC)) * VEC;
-      *reinterpret_cast<u32x4*>(Vs + r * 16 + c) = st.v;
+    if (ltid < Cfg::VITEMS) {
+      const int r = ltid / (16 / VEC), c = (ltid % (16 / VEC)) * VEC;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(in.V.at(r, c)) = (st.valid >> 31) & 1u ? st.v : z;
     }
-    if (tid < 64) {  // C <= 64: wave 0 owns the gate arrays
+    if (ltid < 64) {  // C <= 64: the first loader wave owns the gate arrays
       const float gl = __shfl(st.gc, C - 1, 64);
-      if (tid < C) {
-        egs[buf][tid] = expf(st.gc);
-        eds[buf][tid] = expf(gl - st.gc);
+      if (ltid < C) {
+        egs[buf][ltid] = expf(st.gc);
+        eds[buf][ltid] = expf(gl - st.gc);
       }
     }
   };
 
-  // ---------------- initial state and the static zeros of A
+  // ---------------- loader: output staging tile of chunk n -> HBM (16-byte stores)
+  auto store_outputs = [&](int n) {
+    if (ltid < Cfg::OITEMS) {
+      const int r = ltid / (16 / VEC), c = (ltid % (16 / VEC)) * VEC;
+      const long tok = (long)n * QR + r;
+      if (r < QR && tok < p.L)
+        *reinterpret_cast<u32x4*>(Og + (((long)b * p.L + tok) * p.H + h) * p.DV + slab * 16 + c) =
+            *reinterpret_cast<const u32x4*>(Os + r * OLD + c);
+    }
+  };
+
+  // last position block a token row of tile t may read
+  auto jmax_of = [&](int t) { return (min(16 * t + 15, QR - 1) * nh + nh - 1) / 16; };
+
+  // The two roles run separate loops that execute the same sequence of workgroup barriers
+  // (3 per chunk, plus one for a single staging buffer), so the register allocator never
+  // keeps one role's values live in the other's code.
+  if (loader) {
+    // ---------------- loader waves
+    Staged<E, DK, C> stA, stB;   // register sets, used alternately
+    if (p.NT > 0) {
+      load_chunk(0, stB);
+      store_chunk(stB, 0);
+      load_chunk(min(1, p.NT - 1), stA);
+    }
+    __syncthreads();
+    // one chunk: `nxt` holds chunk n+1 (loads issued one chunk earlier), `ld` receives chunk
+    // n+2 -- two chunks of lead time to cover HBM latency
+    auto loader_step = [&](int n, Staged<E, DK, C>& nxt, Staged<E, DK, C>& ld) {
+      const int cur = (NBUF == 2) ? (n & 1) : 0;
+      const bool more = n + 1 < p.NT;
+      if (n > 0) store_outputs(n - 1);
+      load_chunk(min(n + 2, p.NT - 1), ld);   // past the end: a harmless repeat load
+      __syncthreads();  // phase 1 done
+      __syncthreads();  // phase 2 done
+      if (NBUF == 2 && more) store_chunk(nxt, cur ^ 1);
+      if constexpr (NBUF == 1) {
+        __syncthreads();
+        if (more) store_chunk(nxt, 0);
+      }
+      __syncthreads();  // phase 3 done
+    };
+    for (int n = 0; n < p.NT; n += 2) {
+      loader_step(n, stA, stB);
+      if (n + 1 < p.NT) loader_step(n + 1, stB, stA);
+    }
+    if (p.NT > 0) store_outputs(p.NT - 1);
+    return;
+  }
+
+  // ---------------- compute waves
   floatx4 S[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
@@ -250,98 +328,74 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(FwdParams p) {
       for (int r = 0; r < 4; ++r)
         S[s][r] = p.S0[((long)head * DK + 16 * t + rq + r) * p.DV + slab * 16 + col];
     }
-    if (t < NTS) store4<E>(StS + col * LDK + 16 * t + rq, S[s][0], S[s][1], S[s][2], S[s][3]);
-  }
-  if (p.NT > 0) {
-    Staged<E, DK, C> st;
-    load_chunk(0, st);
-    store_chunk(st, 0);
+    if (t < NTS) store4<E>(St.at(col, 16 * t + rq), S[s][0], S[s][1], S[s][2], S[s][3]);
   }
   __syncthreads();
 
-  // last position block a token row of tile t may read
-  auto jmax_of = [&](int t) { return (min(16 * t + 15, QR - 1) * nh + nh - 1) / 16; };
-
   for (int n = 0; n < p.NT; ++n) {
     const int cur = (NBUF == 2) ? (n & 1) : 0;
-    E* Ks = smem + cur * Cfg::IN;
-    E* Qs = Ks + Cfg::KS;
-    E* KTs = Qs + Cfg::QS;
-    E* Ts = KTs + Cfg::KTS;
-    E* Aqs = Ts + Cfg::TS;
-    E* Vs = Aqs + Cfg::AS;
+    const ChunkTiles<E, DK, C> in(smem + cur * Cfg::IN);
     const float* eg = egs[cur];
     const float* ed = eds[cur];
 
-    Staged<E, DK, C> st;
-    const bool more = n + 1 < p.NT;
-    if (more) load_chunk(n + 1, st);
-
     // ---------------- phase 1: Y = V - gamma (K S); O1 = Q S
+    floatx4 o1 = {0.f, 0.f, 0.f, 0.f};
     if (wave < NBC) {
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      x = mma_tile<E>(x, Ks + 16 * wave * LDK, LDK, StS, LDK, DK, lane);
+      x = mma_tile<E>(x, in.K, 16 * wave, St, 0, DK, lane);
       const int r0 = 16 * wave + rq;
       float y[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = to_float(Vs[(r0 + r) * 16 + col]) - eg[r0 + r] * x[r];
-      store4<E>(YTs + col * LDC + r0, y[0], y[1], y[2], y[3]);
+      for (int r = 0; r < 4; ++r) y[r] = to_float(*in.V.at(r0 + r, col)) - eg[r0 + r] * x[r];
+      store4<E>(Yt.at(col, r0), y[0], y[1], y[2], y[3]);
     }
-    floatx4 o1 = {0.f, 0.f, 0.f, 0.f};
-    if (wave < NQT) o1 = mma_tile<E>(o1, Qs + 16 * wave * LDK, LDK, StS, LDK, DK, lane);
+    if (wave < NQT) o1 = mma_tile<E>(o1, in.Q, 16 * wave, St, 0, DK, lane);
     __syncthreads();
 
     // ---------------- phase 2: V~ = T Y (T lower triangular: k up to the row block's end)
     if (wave < NBC) {
       floatx4 vt = {0.f, 0.f, 0.f, 0.f};
       const int K2 = min(round_up(16 * (wave + 1), KSTEP), C);
-      vt = mma_tile<E>(vt, Ts + 16 * wave * LDC, LDC, YTs, LDC, K2, lane);
+      vt = mma_tile<E>(vt, in.T, 16 * wave, Yt, 0, K2, lane);
       const int r0 = 16 * wave + rq;
-      store4<E>(VtTs + col * LDC + r0, vt[0], vt[1], vt[2], vt[3]);
-      store4<E>(DVtTs + col * LDC + r0, vt[0] * ed[r0], vt[1] * ed[r0 + 1], vt[2] * ed[r0 + 2],
-                vt[3] * ed[r0 + 3]);
+      store4<E>(Vt.at(col, r0), vt[0], vt[1], vt[2], vt[3]);
+      store4<E>(DVt.at(col, r0), vt[0] * ed[r0], vt[1] * ed[r0 + 1], vt[2] * ed[r0 + 2], vt[3] * ed[r0 + 3]);
     }
     __syncthreads();
 
-    // ---------------- phase 3: state update, outputs, next chunk into LDS
-    {
-      const float gC = eg[C - 1];
+    // ---------------- phase 3: state update and outputs
+    const float gC = eg[C - 1];
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        const int t = wave + 4 * s;
-        if (t < NTS) {
-          floatx4 acc = S[s] * gC;
-          if constexpr (Cfg::BF) {
-            acc = mma_tile<E>(acc, KTs + 16 * t * LDC, LDC, DVtTs, LDC, C, lane);
-          } else {
-            // fp32: A[d][r] = K[r][d] read column-wise from the row-major key tile
-            const E* bcol = DVtTs + col * LDC;
+    for (int s = 0; s < SLOTS; ++s) {
+      const int t = wave + 4 * s;
+      if (t < NTS) {
+        floatx4 acc = S[s] * gC;
+        if constexpr (Cfg::BF) {
+          acc = mma_tile<E>(acc, in.KT, 16 * t, DVt, 0, C, lane);
+        } else {
+          // fp32: A[d][r] = K[r][d] read column-wise from the row-major key tile
 #pragma unroll 4
-            for (int k0 = 0; k0 < C; k0 += 4) {
-              const int r = k0 + (lane >> 4);
-              acc = Mfma<E>::mma(Ks[r * LDK + 16 * t + col], bcol[r], acc);
-            }
+          for (int k0 = 0; k0 < C; k0 += 4) {
+            const int r = k0 + (lane >> 4);
+            acc = Mfma<E>::mma(*in.K.at(r, 16 * t + col), *DVt.at(col, r), acc);
           }
-          S[s] = acc;
-          store4<E>(StS + col * LDK + 16 * t + rq, acc[0], acc[1], acc[2], acc[3]);
         }
+        S[s] = acc;
+        store4<E>(St.at(col, 16 * t + rq), acc[0], acc[1], acc[2], acc[3]);
       }
     }
     if (wave < NQT) {
       floatx4 o2 = {0.f, 0.f, 0.f, 0.f};
       const int K3 = min(round_up(16 * (jmax_of(wave) + 1), KSTEP), C);
-      o2 = mma_tile<E>(o2, Aqs + 16 * wave * LDC, LDC, VtTs, LDC, K3, lane);
+      o2 = mma_tile<E>(o2, in.A, 16 * wave, Vt, 0, K3, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int trow = 16 * wave + rq + r;
-        const long tok = (long)n * QR + trow;
-        if (trow < QR && tok < p.L)
-          Og[(((long)b * p.L + tok) * p.H + h) * p.DV + slab * 16 + col] =
-              to_elem<E>(p.scale * (eg[trow * nh + nh - 1] * o1[r] + o2[r]));
+        const float gq = (trow < QR) ? eg[trow * nh + nh - 1] : 0.f;
+        Os[trow * OLD + col] = to_elem<E>(p.scale * (gq * o1[r] + o2[r]));
       }
     }
-    if constexpr (NBUF == 1) __syncthreads();  // the single staging buffer is still being read
-    if (more) store_chunk(st, NBUF == 2 ? cur ^ 1 : 0);
+    if constexpr (NBUF == 1) __syncthreads();
     __syncthreads();
   }
 
@@ -360,7 +414,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(FwdParams p) {
 
 template <typename E, int DK>
 static hipError_t inter_by_c(const FwdParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)(p.B * p.H * (p.DV / 16))), block(256);
+  const dim3 grid((unsigned)(p.B * p.H * (p.DV / 16))), block(512);
   switch (p.C) {
     case 16: hipLaunchKernelGGL((inter_chunk_kernel<E, DK, 16>), grid, block, 0, st, p); break;
     case 32: hipLaunchKernelGGL((inter_chunk_kernel<E, DK, 32>), grid, block, 0, st, p); break;

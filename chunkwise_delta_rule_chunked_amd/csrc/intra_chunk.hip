@@ -26,9 +26,8 @@ namespace delta {
 
 template <typename E, int DK, int C>
 struct IntraLds {
-  static constexpr int PAD = 16 / sizeof(E);
-  static constexpr int LDK = DK + PAD;  // key / query row stride (elements)
-  static constexpr int LDA = C + 4;     // fp32 row stride of A and N
+  static constexpr int LDK = TileLayout<E, DK>::LD;  // key / query row stride (elements)
+  static constexpr int LDA = C + 4;                  // fp32 row stride of A and N
   static constexpr int KQBYTES = 2 * C * LDK * (int)sizeof(E);
   static constexpr int ANBYTES = 2 * C * LDA * 4 + 4 * 16 * 20 * 4;  // A, N, one 16x16 tile per wave
   static constexpr int BYTES = KQBYTES > ANBYTES ? KQBYTES : ANBYTES;
@@ -41,8 +40,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   constexpr int NBLK = NB * (NB + 1) / 2;  // lower blocks of K K^T
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::BYTES];
   __shared__ float gcs[C], bs[C];
-  E* Ks = reinterpret_cast<E*>(smem);
-  E* Qs = Ks + C * LDK;
+  const Tile<E> Kt = make_tile<E, DK>(reinterpret_cast<E*>(smem));
+  const Tile<E> Qt = make_tile<E, DK>(reinterpret_cast<E*>(smem) + C * LDK);
   float* As = reinterpret_cast<float*>(smem);   // after the tiles are dead
   float* Ns = As + C * LDA;
   float* Ps = Ns + C * LDA;                     // 4 x [16][20] per-wave product tiles
@@ -86,12 +85,12 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
     const long pos = P0 + r;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (pos < p.Lx) val = *reinterpret_cast<const u32x4*>(kbase + (((long)b * p.Lx + pos) * p.H + h) * DK + c);
-    *reinterpret_cast<u32x4*>(Ks + r * LDK + c) = val;
+    *reinterpret_cast<u32x4*>(Kt.at(r, c)) = val;
     if (want_a) {
       const long tok = (long)n * QR + r;
       u32x4 qv = {0u, 0u, 0u, 0u};
       if (r < QR && tok < p.L) qv = *reinterpret_cast<const u32x4*>(qbase + (((long)b * p.L + tok) * p.H + h) * DK + c);
-      *reinterpret_cast<u32x4*>(Qs + r * LDK + c) = qv;
+      *reinterpret_cast<u32x4*>(Qt.at(r, c)) = qv;
     }
   }
   __syncthreads();
@@ -106,7 +105,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
       int i = 0;
       while ((i + 1) * (i + 2) / 2 <= t) ++i;
       const int j = t - i * (i + 1) / 2;
-      G[u] = mma_tile<E>(G[u], Ks + 16 * i * LDK, LDK, Ks + 16 * j * LDK, LDK, DK, lane);
+      G[u] = mma_tile<E>(G[u], Kt, 16 * i, Kt, 16 * j, DK, lane);
     }
   }
 
@@ -124,7 +123,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
       float a[4] = {0.f, 0.f, 0.f, 0.f};
       if (t < NQT && 16 * j <= (min(16 * t + 15, QR - 1) * nh + nh - 1)) {
         floatx4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma_tile<E>(d, Ks + 16 * j * LDK, LDK, Qs + 16 * t * LDK, LDK, DK, lane);
+        d = mma_tile<E>(d, Kt, 16 * j, Qt, 16 * t, DK, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pc = 16 * j + rq + r;
