@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdelta.so")
-SOURCES = ["intra_chunk.hip", "inter_chunk.hip", "decode.hip", "delta_abi.cpp"]
+SOURCES = ["intra_chunk.hip", "chunk_scan.hip", "decode.hip", "delta_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed fp32 VALU ops are disabled for all device code (-packed-fp32-ops); the kernels move

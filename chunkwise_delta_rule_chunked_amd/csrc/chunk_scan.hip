@@ -1,0 +1,638 @@
+// Inter-chunk pass: carries the state across chunks and produces the outputs.
+//
+// Sources: "08 linear delta rule & DPLR" page, section 2.3 (chunkwise algorithm:
+// pseudo-values V~ = U - W S, O = Q S + (Q K^T * M) V~, S <- S + K^T V~), section 2.5
+// (V~ contracts over all of d_k, so the key dimension cannot be split across workgroups)
+// and section 3 (gated form: queries decayed to the chunk start, keys to the chunk end,
+// S <- gamma_C S + (K * gamma_C / gamma)^T V~, Gamma-weighted Q K^T).  DeltaProduct notes,
+// section 4.1: on the expanded sequence only each token's last sub-step produces an output.
+// Parallel scan over the sequence: DeltaProduct notes, section 3 (the per-step maps are
+// affine in S, so they compose associatively).
+//
+// Per chunk, with T and A from the intra-chunk kernel and gamma_r = exp(gc_r):
+//   Y   = V - gamma * (K S)                    (the residual the writes must correct)
+//   V~  = T Y                                  (= U - W S with U = T V, W = T (gamma K))
+//   O   = scale * (gamma_p * (Q S) + A V~),    A = Q K^T weighted by Gamma, causal
+//   S  <- gamma_C S + K^T (gamma_C / gamma * V~)
+// Forming V~ as T (V - gamma K S) instead of materialising W = T (gamma K) saves a
+// C x C x d_k contraction per chunk; both are the same product.
+//
+// Sequence split.  The chunk map S -> gamma_C S + K^T D T (V - gamma K S) is affine, so a
+// segment of chunks maps its start state to  S_end = M S_start + S_loc  with M (d_k x d_k)
+// the product of the linear parts and S_loc the segment run from S = 0.  Three launches:
+//   summary  for each (head, segment but the last): S_loc, and M by running the same chain
+//            on d_k extra state columns that start as the identity and see V = 0 (segment 0
+//            instead runs from the true S0 and needs no M);
+//   combine  per (head, 16 state columns): S_start of every segment, in order, in fp32;
+//   outputs  for each (head, segment): the chain from S_start, writing O (and S_final for
+//            the last segment).
+// With one segment (enough heads to fill the GPU) only the outputs launch runs, from S0.
+//
+// Work split inside a workgroup: each of the 4 chain wavefronts owns CT 16-column tiles of
+// the state for the whole segment, so the chain needs no exchange between wavefronts.  The
+// state stays in MFMA accumulators: on gfx950 the accumulator layout of a 16x16 tile (lane l
+// holds rows 4(l/16)..4(l/16)+3 of column l%16) is exactly the B-operand layout of a 16-deep
+// bf16 MFMA, so S, Y and V~ feed the next product from registers (two tiles form one 32-deep
+// step with the k order permuted consistently in A and B).  A operands (K, Q, T, A rows and
+// K^T through LDS transpose reads) come from a staged chunk in LDS.  4 more wavefronts move
+// data: direct global -> LDS loads of chunk n+1 into the other half of a double-buffered
+// stage while chunk n is processed.  Only they have loads in flight; one workgroup barrier
+// per chunk publishes the next stage.  Barriers are issued without the compiler's
+// workgroup fence, which would otherwise wait for the loaders' in-flight loads.
+//
+// Padded positions of the last chunk: the intra-chunk kernel leaves T's padded rows and
+// columns and A's padded columns at exactly zero, so padded key, value and query rows may
+// hold any finite data -- they are loaded from row 0 of the sequence -- without reaching an
+// output (padded rows of V~ are 0 and add nothing to the state).
+#include "common.h"
+#include "kernels.h"
+
+namespace delta {
+
+// MFMA whose B operand is an accumulator tile in the D layout (see above).  `A` is the lane's
+// four consecutive A elements (row lane%16, columns 4(lane/16) .. +3 of a 16-wide k block).
+template <typename E>
+struct DOp;
+
+template <>
+struct DOp<bf16> {
+  typedef bf16x4 A;
+  typedef bf16x4 B;
+  __device__ static inline B cvt(floatx4 d) { return bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]}; }
+  __device__ static inline A row4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+  // M^T block: lane (g, i) gets M[r0 + 4g + j][c0 + i], j = 0..3 (transpose read; the lane
+  // addresses row r0 + 4g + i/4 at column c0 + 4(i%4))
+  __device__ static inline A col4(const Tile<bf16>& m, int r0, int c0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    return read_tr4(m.at(r0 + 4 * g + (i >> 2), c0 + 4 * (i & 3)));
+  }
+  __device__ static inline floatx4 mma1(A a, B b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // two 16-deep k blocks as one 32-deep instruction: k slot 8g+j <- block 0 row 4g+j,
+  // k slot 8g+4+j <- block 1 row 4g+j, in both operands
+  __device__ static inline floatx4 mma2(A a0, A a1, B b0, B b1, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
+  }
+  static constexpr bool PAIRS = true;  // mma2 is one instruction (a chain must not mix shapes)
+};
+
+template <>
+struct DOp<float> {
+  typedef floatx4 A;
+  typedef floatx4 B;
+  __device__ static inline B cvt(floatx4 d) { return d; }
+  __device__ static inline A row4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+  __device__ static inline A col4(const Tile<float>& m, int r0, int c0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    return floatx4{*m.at(r0 + 4 * g, c0 + i), *m.at(r0 + 4 * g + 1, c0 + i), *m.at(r0 + 4 * g + 2, c0 + i),
+                   *m.at(r0 + 4 * g + 3, c0 + i)};
+  }
+  // v_mfma_f32_16x16x4_f32 takes k = lane/16: step j uses k index 4(lane/16) + j of the block
+  __device__ static inline floatx4 mma1(A a, B b, floatx4 c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static inline floatx4 mma2(A a0, A a1, B b0, B b1, floatx4 c) { return mma1(a1, b1, mma1(a0, b0, c)); }
+  static constexpr bool PAIRS = false;
+};
+
+// Barrier without the compiler's workgroup fence: waits for this wave's own LDS operations
+// (and, for loading waves, its vector memory operations) and then synchronises.
+__device__ inline void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+__device__ inline void barrier_all() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Runtime-width variant of copy_rows_to_lds: rows of `cpr` 16-byte chunks, swizzle `mask`.
+template <typename E>
+__device__ inline void copy_rows_rt(E* tile, const E* g, int gstride, int nrows, int valid, int cpr, int mask, int w,
+                                    int nw, int lane) {
+  constexpr int VEC = 16 / sizeof(E);
+  const int total = nrows * cpr;
+  for (int i = w; i * WAVE < total; i += nw) {
+    const int q = i * WAVE + lane;
+    const int r = q / cpr, pc = q % cpr;
+    const int src = r < valid ? r : 0;
+    if (q < total) copy16_to_lds(g + src * gstride + (pc ^ (r & mask)) * VEC, tile + i * WAVE * VEC);
+  }
+}
+
+constexpr int SEG_THREADS = 8 * WAVE;  // 4 chain + 4 loading wavefronts
+constexpr int LDS_BUDGET = 160 * 1024;
+
+template <typename E, int DK, int C, int CT, bool SUM>
+struct SegCfg {
+  static constexpr int ES = sizeof(E);
+  static constexpr int TPG = 4 * CT;        // state column tiles per workgroup
+  static constexpr int VWMAX = 16 * TPG;    // value columns staged per chunk
+  static constexpr int KS = C * DK, QS = SUM ? 0 : C * DK, TS = C * C, AS = SUM ? 0 : C * C, VS = C * VWMAX;
+  static constexpr int GS = 3 * C * 4 / ES;              // gc, exp(gc), exp(gc_last - gc)
+  static constexpr int IN = KS + QS + TS + AS + VS + GS;   // one staged chunk (elements)
+  // bf16 outputs go through a per-wave staging tile O^T [16 CT][C]
+  static constexpr bool OSTAGE = !SUM && ES == 2;
+  static constexpr int OSW = 16 * CT * C;                  // per wave (elements)
+  static constexpr int OS = OSTAGE ? 4 * OSW : 0;
+  static constexpr int NSTAGE = (2 * IN + OS) * ES <= LDS_BUDGET ? 2 : 1;
+  static constexpr int ELEMS = NSTAGE * IN + OS;
+  static_assert(ELEMS * ES <= LDS_BUDGET, "LDS budget");
+};
+
+template <typename E, int DK, int C, int CT, bool SUM>
+__global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
+  using Cfg = SegCfg<E, DK, C, CT, SUM>;
+  using D = DOp<E>;
+  constexpr int NB = C / 16;     // position blocks per chunk
+  constexpr int NTS = DK / 16;   // state row tiles
+  constexpr int VEC = 16 / sizeof(E);
+  constexpr int TPG = Cfg::TPG;
+
+  __shared__ __attribute__((aligned(16))) E smem[Cfg::ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g4 = lane >> 4;
+  const int BH = p.B * p.H;
+  const int NCT = p.DV / 16;
+  const int MCT = SUM ? DK / 16 : 0;
+  const int G = (NCT + MCT + TPG - 1) / TPG;            // column groups
+  const int NSEG = SUM ? p.P - 1 : p.P;                 // segments this launch handles
+
+  // workgroup -> (segment, head, column group); the groups of one (segment, head) share
+  // its K and T reads, so they go to one XCD (workgroups are dealt round-robin over 8)
+  int unit, grp;
+  {
+    const int i = blockIdx.x;
+    if ((NSEG * BH) % 8 == 0) {
+      const int x = i % 8, j = i / 8;
+      unit = x + 8 * (j / G);
+      grp = j % G;
+    } else {
+      unit = i / G;
+      grp = i % G;
+    }
+  }
+  const int seg = unit / BH, head = unit % BH;
+  const int b = head / p.H, h = head % p.H;
+  const int n0 = seg * p.NS, n1 = min(p.NT, n0 + p.NS);  // chunks of this segment
+  const int nh = p.nh;
+  const int QR = C / nh;                                 // tokens per chunk
+  // value columns staged for this group
+  const int vt0 = grp * TPG;
+  const int vcnt = max(0, min(NCT - vt0, TPG));
+  const int VW = 16 * vcnt;
+  // segment 0 of the summary needs only the value columns
+  if (SUM && seg == 0 && vcnt == 0) return;
+
+  if (wave >= 4) {
+    // ---------------- loading wavefronts
+    const int dw = wave - 4;
+    const E* qg = reinterpret_cast<const E*>(p.q);
+    const E* kg = reinterpret_cast<const E*>(p.k);
+    const E* vg = reinterpret_cast<const E*>(p.v);
+    const E* Tg = reinterpret_cast<const E*>(p.T);
+    const E* Ag = reinterpret_cast<const E*>(p.A);
+    const int HDK = p.H * DK, HDV = p.H * p.DV;
+    const int vcpr = VW * (int)sizeof(E) / 16, vmask = vcpr > 0 ? pow2_part(vcpr) - 1 : 0;
+    auto issue = [&](int n, int stage) {
+      E* st = smem + stage * Cfg::IN;
+      const long P0 = (long)n * C;
+      const int krows = (int)min((long)C, p.Lx - P0);                  // valid positions
+      const long tok0 = (long)n * QR;
+      const int qrows = (int)min((long)QR, (long)p.L - tok0);           // valid tokens
+      copy_rows_to_lds<E, DK>(st, kg + ((long)b * p.Lx + P0) * HDK + (long)h * DK, HDK, C, krows, dw, 4, lane);
+      if (!SUM)
+        copy_rows_to_lds<E, DK>(st + Cfg::KS, qg + ((long)b * p.L + tok0) * HDK + (long)h * DK, HDK, QR, qrows, dw,
+                                4, lane);
+      copy_rows_to_lds<E, C>(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, C, C, C, dw, 4, lane);
+      if (!SUM)
+        copy_rows_to_lds<E, C>(st + Cfg::KS + Cfg::QS + Cfg::TS, Ag + ((long)head * p.NT + n) * C * C, C, C, C, dw, 4,
+                               lane);
+      if (VW > 0)
+        copy_rows_rt<E>(st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS,
+                        vg + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0, HDV, C, krows, vcpr, vmask, dw,
+                        4, lane);
+      copy_rows_to_lds<float, 4>(reinterpret_cast<float*>(st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS + Cfg::VS),
+                                 p.gc + ((long)head * p.NT + n) * C, 4, C / 4, C / 4, dw, 4, lane);
+    };
+    // exp(gc) and exp(gc_last - gc) of a staged chunk, once for all chain wavefronts
+    auto exps = [&](int stage) {
+      if (dw == 0 && lane < C) {
+        float* gcs = reinterpret_cast<float*>(smem + stage * Cfg::IN + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS + Cfg::VS);
+        const float x = gcs[lane], xl = gcs[C - 1];
+        gcs[C + lane] = expf(x);
+        gcs[2 * C + lane] = expf(xl - x);
+      }
+    };
+    if constexpr (Cfg::NSTAGE == 2) {
+      if (n0 < n1) issue(n0, 0);
+      wait_vmem();
+      if (n0 < n1) exps(0);
+      barrier_all();  // first chunk staged
+      for (int n = n0; n < n1; ++n) {
+        const int s1 = (n + 1 - n0) & 1;
+        if (n + 1 < n1) issue(n + 1, s1);
+        wait_vmem();
+        if (n + 1 < n1) exps(s1);
+        barrier_all();  // chunk n done, chunk n+1 staged
+      }
+    } else {
+      for (int n = n0; n < n1; ++n) {
+        issue(n, 0);
+        wait_vmem();
+        exps(0);
+        barrier_all();  // chunk n staged
+        barrier_all();  // chunk n done
+      }
+    }
+    return;
+  }
+
+  // ---------------- chain wavefronts: tiles vt0 + CT*wave + c, c < CT
+  int tile[CT];
+  bool live[CT], isv[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    tile[c] = vt0 + CT * wave + c;
+    isv[c] = tile[c] < NCT;
+    // segment 0 of the summary starts from the true S0 and needs no transition columns
+    live[c] = tile[c] < NCT + ((SUM && seg == 0) ? 0 : MCT);
+  }
+
+  // state init: rows 16t + 4 g4 + j, column m of tile c
+  floatx4 S[CT][NTS];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int t = 0; t < NTS; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * t + 4 * g4 + j;
+        float x = 0.f;
+        if (live[c]) {
+          if (isv[c]) {
+            const long col = 16 * tile[c] + m;
+            if (seg == 0) {
+              if (p.S0) x = p.S0[((long)head * DK + row) * p.DV + col];
+            } else if (!SUM) {
+              x = p.Sst[(((long)head * p.P + seg) * DK + row) * p.DV + col];
+            }
+          } else {
+            x = (row == 16 * (tile[c] - NCT) + m) ? 1.f : 0.f;  // identity columns of M
+          }
+        }
+        S[c][t][j] = x;
+      }
+    }
+
+  // Per-lane LDS element offsets of the fragments this lane reads.  A block of 16 rows further
+  // down a tile adds a constant: for r = 16 bb + x, r & mask == x & mask (every mask < 16).
+  constexpr int CH = 16 / sizeof(E);
+  constexpr int MK = PackedLayout<E, DK>::MASK, MC = PackedLayout<E, C>::MASK;
+  auto swz = [](int r, int e, int ld, int mask) { return r * ld + ((e / CH) ^ (r & mask)) * CH + e % CH; };
+  const int vmask = VW > 0 ? pow2_part(VW * (int)sizeof(E) / 16) - 1 : 0;
+  int offK[NTS], offKT[NTS], offT[NB], offV[CT];
+#pragma unroll
+  for (int t = 0; t < NTS; ++t) {
+    offK[t] = swz(m, 16 * t + 4 * g4, DK, MK);                          // K, Q rows
+    offKT[t] = swz(4 * g4 + (m >> 2), 16 * t + 4 * (m & 3), DK, MK);   // K^T transpose reads
+  }
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) offT[kb] = swz(m, 16 * kb + 4 * g4, C, MC);  // T, A rows
+#pragma unroll
+  for (int c = 0; c < CT; ++c)   // V transpose reads (D layout of the tile's 16 columns)
+    offV[c] = isv[c] ? swz(4 * g4 + (m >> 2), 16 * (tile[c] - vt0) + 4 * (m & 3), VW, vmask) : 0;
+
+  if constexpr (Cfg::NSTAGE == 2) barrier_lds();
+
+  E* Og = reinterpret_cast<E*>(p.O);
+  // bf16 outputs: per-wave staging of O^T [16 CT][C], written back with transpose reads
+  const Tile<E> Ost = make_packed_tile<E, C>(smem + Cfg::NSTAGE * Cfg::IN + (Cfg::OSTAGE ? wave * Cfg::OSW : 0));
+  const int NQT = (QR + 15) / 16;
+
+  for (int n = n0; n < n1; ++n) {
+    if constexpr (Cfg::NSTAGE == 1) barrier_lds();
+    const E* Kp = smem + ((Cfg::NSTAGE == 2) ? ((n - n0) & 1) : 0) * Cfg::IN;
+    const E* Qp = Kp + Cfg::KS;
+    const E* Tp = Qp + Cfg::QS;
+    const E* Ap = Tp + Cfg::TS;
+    const E* Vp = Ap + Cfg::AS;
+    const float* gcp = reinterpret_cast<const float*>(Vp + Cfg::VS);
+    const float* egp = gcp + C;        // exp(gc)
+    const float* edp = gcp + 2 * C;    // exp(gc_last - gc)
+
+    // chunk-start state as a B operand
+    typename D::B Sb[CT][NTS];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) Sb[c][t] = D::cvt(S[c][t]);
+
+    // ---- X = K S, contracting over d_k
+    constexpr int TSTEP = (D::PAIRS && NTS % 2 == 0) ? 2 : 1;
+    floatx4 X[CT][NB];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) X[c][bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NTS; t += TSTEP)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const typename D::A a0 = D::row4(Kp + 16 * bb * DK + offK[t]);
+        if constexpr (TSTEP == 2) {
+          const typename D::A a1 = D::row4(Kp + 16 * bb * DK + offK[t + 1]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) X[c][bb] = D::mma2(a0, a1, Sb[c][t], Sb[c][t + 1], X[c][bb]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < CT; ++c) X[c][bb] = D::mma1(a0, Sb[c][t], X[c][bb]);
+        }
+      }
+
+    // ---- Y = V - gamma X (transition columns see V = 0)
+    typename D::B Yb[CT][NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const floatx4 eg4 = *reinterpret_cast<const floatx4*>(egp + 16 * bb + 4 * g4);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        floatx4 v4 = {0.f, 0.f, 0.f, 0.f};
+        if (isv[c]) {
+          if constexpr (sizeof(E) == 2) {
+            const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Vp) + 16 * bb * VW + offV[c]);
+            v4 = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+          } else {
+            const Tile<E> V{const_cast<E*>(Vp), VW, vmask};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v4[j] = to_float(*V.at(16 * bb + 4 * g4 + j, 16 * (tile[c] - vt0) + m));
+          }
+        }
+        Yb[c][bb] = D::cvt(v4 - eg4 * X[c][bb]);
+      }
+    }
+
+    // ---- V~ = T Y (T lower triangular; a zero block above the diagonal may pair in)
+    typename D::B Vb[CT][NB], DVb[CT][NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      floatx4 vt[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) vt[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (D::PAIRS && ((bb + 2) & ~1) <= NB) {
+#pragma unroll
+        for (int kb = 0; kb <= bb; kb += 2) {
+          const typename D::A a0 = D::row4(Tp + 16 * bb * C + offT[kb]);
+          const typename D::A a1 = D::row4(Tp + 16 * bb * C + offT[kb + 1]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) vt[c] = D::mma2(a0, a1, Yb[c][kb], Yb[c][kb + 1], vt[c]);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb <= bb; ++kb) {
+          const typename D::A a0 = D::row4(Tp + 16 * bb * C + offT[kb]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) vt[c] = D::mma1(a0, Yb[c][kb], vt[c]);
+        }
+      }
+      const floatx4 ed4 = *reinterpret_cast<const floatx4*>(edp + 16 * bb + 4 * g4);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        Vb[c][bb] = D::cvt(vt[c]);
+        DVb[c][bb] = D::cvt(vt[c] * ed4);
+      }
+    }
+
+    // ---- outputs: O = scale (gamma_p Q S + A V~), S still the chunk-start state.  A is zero
+    // past each token's causal reach, so the product runs over all position blocks.
+    if constexpr (!SUM) {
+      constexpr int KSTEPA = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
+      // Output addresses depend only on the lane and the chunk; hiding the lane index keeps the
+      // optimiser from hoisting one register per row block and tile out of the chunk loop.
+      int lo = lane;
+      asm volatile("" : "+v"(lo));
+      const int mo = lo & 15, go = lo >> 4;
+#pragma unroll
+      for (int tq = 0; tq < NB; ++tq) {
+        if (tq < NQT) {
+          floatx4 o1[CT], o2[CT];
+#pragma unroll
+          for (int c = 0; c < CT; ++c) o1[c] = o2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < NTS; t += TSTEP) {
+            const typename D::A a0 = D::row4(Qp + 16 * tq * DK + offK[t]);
+            if constexpr (TSTEP == 2) {
+              const typename D::A a1 = D::row4(Qp + 16 * tq * DK + offK[t + 1]);
+#pragma unroll
+              for (int c = 0; c < CT; ++c) o1[c] = D::mma2(a0, a1, Sb[c][t], Sb[c][t + 1], o1[c]);
+            } else {
+#pragma unroll
+              for (int c = 0; c < CT; ++c) o1[c] = D::mma1(a0, Sb[c][t], o1[c]);
+            }
+          }
+#pragma unroll
+          for (int kb = 0; kb < NB; kb += KSTEPA) {
+            const typename D::A a0 = D::row4(Ap + 16 * tq * C + offT[kb]);
+            if constexpr (KSTEPA == 2) {
+              const typename D::A a1 = D::row4(Ap + 16 * tq * C + offT[kb + 1]);
+#pragma unroll
+              for (int c = 0; c < CT; ++c) o2[c] = D::mma2(a0, a1, Vb[c][kb], Vb[c][kb + 1], o2[c]);
+            } else {
+#pragma unroll
+              for (int c = 0; c < CT; ++c) o2[c] = D::mma1(a0, Vb[c][kb], o2[c]);
+            }
+          }
+          // gamma of each token's last sub-step, times scale (rows past the chunk's tokens: 0)
+          floatx4 gq;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int trow = 16 * tq + 4 * go + j;
+            const float e = egp[min(trow, QR - 1) * nh + nh - 1];
+            gq[j] = trow < QR ? e * p.scale : 0.f;
+          }
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            const floatx4 o = gq * o1[c] + p.scale * o2[c];
+            if constexpr (Cfg::OSTAGE) {
+              *reinterpret_cast<bf16x4*>(Ost.at(16 * c + mo, 16 * tq + 4 * go)) = DOp<bf16>::cvt(o);
+            } else if (isv[c]) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int trow = 16 * tq + 4 * go + j;
+                const long tok = (long)n * QR + trow;
+                if (trow < QR && tok < p.L)
+                  Og[(((long)b * p.L + tok) * p.H + h) * p.DV + 16 * tile[c] + mo] = to_elem<E>(o[j]);
+              }
+            }
+          }
+          if constexpr (Cfg::OSTAGE) {
+            // back from the staging tile: lane (g4, m) gets columns 16 c + 4 g4 .. +3 of token
+            // 16 tq + m (this wave's own LDS area: no barrier)
+            const int trow = 16 * tq + mo;
+            const long tok = (long)n * QR + trow;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+              const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Ost.at(16 * c + 4 * go + (mo >> 2), 16 * tq + 4 * (mo & 3))));
+              if (isv[c] && trow < QR && tok < p.L)
+                *reinterpret_cast<bf16x4*>(Og + (((long)b * p.L + tok) * p.H + h) * p.DV + 16 * tile[c] + 4 * go) = r;
+            }
+          }
+        }
+      }
+    }
+
+    // ---- S <- gamma_C S + K^T (gamma_C / gamma V~)
+    {
+      const float gC = egp[C - 1];
+      constexpr int BSTEP = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) {
+        floatx4 acc[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[c] = S[c][t] * gC;
+#pragma unroll
+        for (int bb = 0; bb < NB; bb += BSTEP) {
+          typename D::A a0, a1;
+          if constexpr (sizeof(E) == 2) {
+            a0 = read_tr4(reinterpret_cast<const bf16*>(Kp) + 16 * bb * DK + offKT[t]);
+            if constexpr (BSTEP == 2) a1 = read_tr4(reinterpret_cast<const bf16*>(Kp) + 16 * (bb + 1) * DK + offKT[t]);
+          } else {
+            const Tile<E> K = make_packed_tile<E, DK>(const_cast<E*>(Kp));
+            a0 = D::col4(K, 16 * bb, 16 * t, lane);
+            if constexpr (BSTEP == 2) a1 = D::col4(K, 16 * bb + 16, 16 * t, lane);
+          }
+          if constexpr (BSTEP == 2) {
+#pragma unroll
+            for (int c = 0; c < CT; ++c) acc[c] = D::mma2(a0, a1, DVb[c][bb], DVb[c][bb + 1], acc[c]);
+          } else {
+#pragma unroll
+            for (int c = 0; c < CT; ++c) acc[c] = D::mma1(a0, DVb[c][bb], acc[c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c) S[c][t] = acc[c];
+      }
+    }
+    barrier_lds();  // chunk done (and, with one stage, the stage may be reloaded)
+  }
+
+  // ---------------- segment results
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    if (!live[c]) continue;
+#pragma unroll
+    for (int t = 0; t < NTS; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * t + 4 * g4 + j;
+        if constexpr (SUM) {
+          const int W = p.DV + DK;
+          const int col = isv[c] ? 16 * tile[c] + m : p.DV + 16 * (tile[c] - NCT) + m;
+          p.SM[(((long)head * p.P + seg) * DK + row) * W + col] = S[c][t][j];
+        } else if (seg == p.P - 1 && p.S_final) {
+          p.S_final[((long)head * DK + row) * p.DV + 16 * tile[c] + m] = S[c][t][j];
+        }
+      }
+  }
+}
+
+// Start states of the segments, in order: S_start(1) = S_end(0) and
+// S_start(q+1) = M(q) S_start(q) + S_loc(q).  One workgroup per (head, 16 state columns), one
+// wavefront per 16 state rows; fp32 MFMA.
+template <int DK>
+__global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
+  __shared__ float Sl[DK][17];
+  const int NCT = p.DV / 16;
+  const int head = blockIdx.x / NCT, ct = blockIdx.x % NCT;
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6, m = lane & 15, g4 = lane >> 4;
+  const int W = p.DV + DK;
+  const float* SMh = p.SM + (long)head * p.P * DK * W;
+  float* Sst = p.Sst + (long)head * p.P * DK * p.DV;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * t + 4 * g4 + j;
+    const float x = SMh[(long)row * W + 16 * ct + m];
+    Sl[row][m] = x;
+    Sst[((long)1 * DK + row) * p.DV + 16 * ct + m] = x;
+  }
+  __syncthreads();
+  for (int q = 1; q + 1 < p.P; ++q) {
+    const float* SMq = SMh + (long)q * DK * W;
+    floatx4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[0][j] = SMq[(long)(16 * t + 4 * g4 + j) * W + 16 * ct + m];
+    acc[1] = acc[2] = acc[3] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 4) {
+      const float a = SMq[(long)(16 * t + m) * W + p.DV + k0 + g4];
+      const float bb = Sl[k0 + g4][m];
+      acc[(k0 / 4) & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc[(k0 / 4) & 3], 0, 0, 0);
+    }
+    const floatx4 s = acc[0] + acc[1] + acc[2] + acc[3];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * t + 4 * g4 + j;
+      Sl[row][m] = s[j];
+      Sst[((long)(q + 1) * DK + row) * p.DV + 16 * ct + m] = s[j];
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <typename E, int DK, int C, int CT, bool SUM>
+static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
+  constexpr int TPG = 4 * CT;
+  const int NCT = p.DV / 16, MCT = SUM ? DK / 16 : 0;
+  const int G = (NCT + MCT + TPG - 1) / TPG;
+  const int nseg = SUM ? p.P - 1 : p.P;
+  const long blocks = (long)nseg * p.B * p.H * G;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, SUM>), dim3((unsigned)blocks), dim3(SEG_THREADS), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename E, int DK, int C>
+static hipError_t inter_run(const FwdParams& p, hipStream_t st) {
+  hipError_t e;
+  if (p.P > 1) {
+    if ((e = launch_seg<E, DK, C, 2, true>(p, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((combine_kernel<DK>), dim3((unsigned)(p.B * p.H * (p.DV / 16))), dim3(DK / 16 * WAVE), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return p.DV / 16 <= 4 ? launch_seg<E, DK, C, 1, false>(p, st) : launch_seg<E, DK, C, 2, false>(p, st);
+}
+
+template <typename E, int DK>
+static hipError_t inter_by_c(const FwdParams& p, hipStream_t st) {
+  switch (p.C) {
+    case 16: return inter_run<E, DK, 16>(p, st);
+    case 32: return inter_run<E, DK, 32>(p, st);
+    case 48: return inter_run<E, DK, 48>(p, st);
+    case 64: return inter_run<E, DK, 64>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename E>
+static hipError_t inter_by_dk(const FwdParams& p, hipStream_t st) {
+  switch (p.DK) {
+    case 16: return inter_by_c<E, 16>(p, st);
+    case 32: return inter_by_c<E, 32>(p, st);
+    case 64: return inter_by_c<E, 64>(p, st);
+    case 128: return inter_by_c<E, 128>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_inter_chunk(const FwdParams& p, bool bf16_in, hipStream_t st) {
+  return bf16_in ? inter_by_dk<bf16>(p, st) : inter_by_dk<float>(p, st);
+}
+
+}  // namespace delta

@@ -87,6 +87,84 @@ __device__ inline Tile<E> make_tile(E* p) {
   return Tile<E>{p, TileLayout<E, L>::LD, TileLayout<E, L>::MASK};
 }
 
+// Unpadded layout for tiles filled by direct-to-LDS loads (each such load writes 64 consecutive
+// 16-byte chunks, so rows must be contiguous).  Chunks are XOR-swizzled with the row number
+// within the largest power-of-two group of chunks that divides the row (at most 16), which keeps
+// every swizzled chunk inside its row.
+constexpr int pow2_part(int x) { return (x & -x) > 16 ? 16 : (x & -x); }
+template <typename E, int L>
+struct PackedLayout {
+  static constexpr int CPR = L * (int)sizeof(E) / 16;  // 16-byte chunks per row
+  static constexpr int LD = L;
+  static constexpr int MASK = pow2_part(CPR) - 1;
+};
+
+template <typename E, int L>
+__device__ inline Tile<E> make_packed_tile(E* p) {
+  return Tile<E>{p, PackedLayout<E, L>::LD, PackedLayout<E, L>::MASK};
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).  The LDS address is
+// wave-uniform: lane l writes lds_base + 16 l.  Completion is tracked by vmcnt.
+__device__ inline void copy16_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds_base, 16, 0, 0);
+}
+
+// Wait until every vector memory operation of this wave has completed (vmcnt = 0).
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Copies rows [0, nrows) of a row-major global matrix (rows of L elements, row stride gstride
+// elements) into a PackedLayout tile with direct-to-LDS loads issued by wave w of nw waves.
+// Rows at or past `valid` read row 0 instead (finite data that the caller's products cancel).
+template <typename E, int L>
+__device__ inline void copy_rows_to_lds(E* tile, const E* g, int gstride, int nrows, int valid, int w, int nw,
+                                        int lane) {
+  constexpr int CPR = PackedLayout<E, L>::CPR, MASK = PackedLayout<E, L>::MASK, VEC = 16 / sizeof(E);
+  const int total = nrows * CPR;
+  for (int i = w; i * WAVE < total; i += nw) {
+    const int q = i * WAVE + lane;
+    const int r = q / CPR, pc = q % CPR;
+    const int src = r < valid ? r : 0;
+    if (q < total) copy16_to_lds(g + src * gstride + (pc ^ (r & MASK)) * VEC, tile + i * WAVE * VEC);
+  }
+}
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives element i % 4 of
+// the 4-element (8-byte) pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 of its
+// group, in that order.  (Lane semantics measured on the device.)
+__device__ inline bf16x4 read_tr4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+// C(16x16) += M^T(16 x K) * B(K x 16) for bf16, where M is a row-major [K][.] tile (here the
+// key tile, K = positions) and the A operand is M^T[d0 .. d0+16)[0 .. K): transpose reads give
+// each lane its column run of M directly.  B^T rows b_r0.. of tile b are K-contiguous.
+// One instruction shape per chain, as in mma_tile.
+template <int K>
+__device__ inline floatx4 mma_tn(floatx4 acc, const Tile<bf16>& m, int d0, const Tile<bf16>& b, int b_r0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int e = d0 + 4 * (i & 3);  // column of the 8-byte piece this lane addresses
+  if constexpr (K % 32 == 0) {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      const int r = k0 + 8 * g + (i >> 2);
+      const bf16x4 lo = read_tr4(m.at(r, e)), hi = read_tr4(m.at(r + 4, e));
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc = Mfma<bf16>::mma(a, *reinterpret_cast<const bf16x8*>(b.at(b_r0 + i, k0 + 8 * g)), acc);
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const bf16x4 a = read_tr4(m.at(k0 + 4 * g + (i >> 2), e));
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, *reinterpret_cast<const bf16x4*>(b.at(b_r0 + i, k0 + 4 * g)),
+                                                      acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
 // C(16x16) += A(16 x K) * B(K x 16): A rows a_r0.. of tile a (K along the row), B^T rows
 // b_r0.. of tile b (the B operand stored transposed, K along the row).  K must be a multiple
 // of 16 (of 4 for float).  One accumulation chain uses one instruction shape: a contraction

@@ -66,11 +66,23 @@ FwdParams make_params(const delta_shape* s) {
   p.Lx = s->L * s->n_h;
   p.NT = (p.Lx + p.C - 1) / p.C;
   p.scale = s->scale;
+  // Sequence split of the inter-chunk pass: enough segments per head that the output launch
+  // has about 256 workgroups (one per compute unit), each segment at least one chunk.  A
+  // function of the shape alone, so results do not depend on the device.
+  const long long units = (long long)p.B * p.H * ((p.DV / 16 + (p.DV <= 64 ? 4 : 8) - 1) / (p.DV <= 64 ? 4 : 8));
+  long long P = units > 0 && p.NT > 1 ? 256 / units : 1;
+  if (P < 1) P = 1;
+  if (P > p.NT) P = p.NT > 0 ? p.NT : 1;
+  p.NS = p.NT > 0 ? (int)((p.NT + P - 1) / P) : 1;
+  p.P = p.NT > 0 ? (p.NT + p.NS - 1) / p.NS : 1;
   return p;
 }
 
 size_t t_bytes(const FwdParams& p, size_t es) { return (size_t)p.B * p.H * p.NT * p.C * p.C * es; }
 size_t gc_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.C * 4; }
+// segment summaries and start states (only with a sequence split)
+size_t sm_bytes(const FwdParams& p) { return p.P > 1 ? (size_t)p.B * p.H * p.P * p.DK * (p.DV + p.DK) * 4 : 0; }
+size_t sst_bytes(const FwdParams& p) { return p.P > 1 ? (size_t)p.B * p.H * p.P * p.DK * p.DV * 4 : 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DELTA_OK : DELTA_ERR_HIP; }
 
@@ -84,8 +96,10 @@ int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
   if ((rc = check_chunk(s))) return rc;
   if (!bytes) return DELTA_ERR_NULL_ARG;
   const FwdParams p = make_params(s);
-  // T and A (element type of the inputs), then the gate prefix
-  *bytes = 2 * align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p));
+  // T and A (element type of the inputs), the gate prefix, then the segment summaries and
+  // segment start states of the inter-chunk pass
+  *bytes = 2 * align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p)) + align_up(sm_bytes(p)) +
+           align_up(sst_bytes(p));
   return DELTA_OK;
 }
 
@@ -145,7 +159,13 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
   p.S_final = S_final;
   p.T = workspace;
   p.A = static_cast<char*>(workspace) + align_up(t_bytes(p, es));
-  p.gc = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * align_up(t_bytes(p, es)));
+  char* ws = static_cast<char*>(workspace);
+  size_t off = 2 * align_up(t_bytes(p, es));
+  p.gc = reinterpret_cast<float*>(ws + off);
+  off += align_up(gc_bytes(p));
+  p.SM = p.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
+  off += align_up(sm_bytes(p));
+  p.Sst = p.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
   return DELTA_OK;
 }
 

@@ -24,6 +24,10 @@ struct FwdParams {
   float* gc;            // [B, H, NT, C] cumulative in-chunk log gate
   float* W;             // chunk_wy only: [B, H, NT, C, DK]
   float* U;             // chunk_wy only: [B, H, NT, C, DV]
+  // sequence split of the inter-chunk pass: P segments of NS chunks (P = 1: no split)
+  int P, NS;
+  float* SM;            // [B*H, P, DK, DV + DK]: per segment S_loc (value columns) and M
+  float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
 };
 
 struct DecodeParams {

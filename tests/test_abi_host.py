@@ -46,15 +46,40 @@ def ws(sh):
     return rc, n.value
 
 
+def segments(B, H, dv, NT):
+    """Sequence split of the inter-chunk pass: about 256 output workgroups in total (4 or 8
+    state column tiles per workgroup), each segment at least one chunk."""
+    tiles = 4 if dv <= 64 else 8
+    units = B * H * (-(-(dv // 16) // tiles))
+    P = 256 // units if units > 0 and NT > 1 else 1
+    P = max(1, min(P, NT if NT > 0 else 1))
+    NS = -(-NT // P) if NT > 0 else 1
+    return (-(-NT // NS) if NT > 0 else 1), NS
+
+
+def test_segments_rule():
+    assert segments(2, 16, 128, 128) == (8, 16)     # 32 heads: 8 segments of 16 chunks
+    assert segments(1, 16, 128, 1024) == (16, 64)
+    assert segments(4, 8, 128, 32) == (8, 4)
+    assert segments(64, 16, 128, 4) == (1, 4)       # enough heads: no split
+    assert segments(1, 1, 16, 4) == (4, 1)
+    assert segments(1, 1, 16, 5) == (5, 1)
+    assert segments(2, 1, 16, 300) == (100, 3)      # 128 wanted; segments of 3 chunks -> 100
+    assert segments(2, 1, 16, 300)[0] * segments(2, 1, 16, 300)[1] >= 300
+
+
 def test_workspace_bytes(lib):
-    rc, n = ws(shape())
-    NT = (100 + 31) // 32
-    t_bytes = 2 * 3 * NT * 32 * 32 * 2
-    gc_bytes = 2 * 3 * NT * 32 * 4
     up = lambda x: (x + 255) // 256 * 256
-    assert rc == 0 and n == 2 * up(t_bytes) + up(gc_bytes)
-    rc, n32 = ws(shape(dtype=D.F32))
-    assert rc == 0 and n32 == 2 * up(t_bytes * 2) + up(gc_bytes)
+    for B, H, L, dk, dv, C, dt, es in [(2, 3, 100, 64, 32, 32, D.BF16, 2), (2, 3, 100, 64, 32, 32, D.F32, 4),
+                                       (2, 16, 8192, 128, 128, 64, D.BF16, 2), (64, 16, 64, 128, 128, 64, D.BF16, 2),
+                                       (1, 1, 50, 16, 256, 16, D.F32, 4)]:
+        rc, n = ws(shape(B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, dtype=dt))
+        NT = (L + C - 1) // C
+        P, _ = segments(B, H, dv, NT)
+        t_bytes = B * H * NT * C * C * es
+        gc_bytes = B * H * NT * C * 4
+        seg = up(B * H * P * dk * (dv + dk) * 4) + up(B * H * P * dk * dv * 4) if P > 1 else 0
+        assert rc == 0 and n == 2 * up(t_bytes) + up(gc_bytes) + seg, (B, H, L, dk, dv, C)
     assert ws(shape(L=0)) == (0, 0)
 
 
