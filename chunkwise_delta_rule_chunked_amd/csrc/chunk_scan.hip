@@ -110,27 +110,14 @@ __device__ inline void barrier_all() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// Runtime-width variant of copy_rows_to_lds: rows of `cpr` 16-byte chunks, swizzle `mask`.
-template <typename E>
-__device__ inline void copy_rows_rt(E* tile, const E* g, int gstride, int nrows, int valid, int cpr, int mask, int w,
-                                    int nw, int lane) {
-  constexpr int VEC = 16 / sizeof(E);
-  const int total = nrows * cpr;
-  for (int i = w; i * WAVE < total; i += nw) {
-    const int q = i * WAVE + lane;
-    const int r = q / cpr, pc = q % cpr;
-    const int src = r < valid ? r : 0;
-    if (q < total) copy16_to_lds(g + src * gstride + (pc ^ (r & mask)) * VEC, tile + i * WAVE * VEC);
-  }
-}
-
-constexpr int SEG_THREADS = 8 * WAVE;  // 4 chain + 4 loading wavefronts
+constexpr int SEG_LOADERS = 4;  // loading wavefronts per workgroup
 constexpr int LDS_BUDGET = 160 * 1024;
 
-template <typename E, int DK, int C, int CT, bool SUM>
+template <typename E, int DK, int C, int CT, int NCW, bool SUM>
 struct SegCfg {
   static constexpr int ES = sizeof(E);
-  static constexpr int TPG = 4 * CT;        // state column tiles per workgroup
+  static constexpr int TPG = NCW * CT;      // state column tiles per workgroup
+  static constexpr int THREADS = (NCW + SEG_LOADERS) * WAVE;
   static constexpr int VWMAX = 16 * TPG;    // value columns staged per chunk
   static constexpr int KS = C * DK, QS = SUM ? 0 : C * DK, TS = C * C, AS = SUM ? 0 : C * C, VS = C * VWMAX;
   static constexpr int GS = 3 * C * 4 / ES;              // gc, exp(gc), exp(gc_last - gc)
@@ -138,15 +125,15 @@ struct SegCfg {
   // bf16 outputs go through a per-wave staging tile O^T [16 CT][C]
   static constexpr bool OSTAGE = !SUM && ES == 2;
   static constexpr int OSW = 16 * CT * C;                  // per wave (elements)
-  static constexpr int OS = OSTAGE ? 4 * OSW : 0;
+  static constexpr int OS = OSTAGE ? NCW * OSW : 0;
   static constexpr int NSTAGE = (2 * IN + OS) * ES <= LDS_BUDGET ? 2 : 1;
   static constexpr int ELEMS = NSTAGE * IN + OS;
   static_assert(ELEMS * ES <= LDS_BUDGET, "LDS budget");
 };
 
-template <typename E, int DK, int C, int CT, bool SUM>
-__global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
-  using Cfg = SegCfg<E, DK, C, CT, SUM>;
+template <typename E, int DK, int C, int CT, int NCW, bool SUM>
+__global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdParams p) {
+  using Cfg = SegCfg<E, DK, C, CT, NCW, SUM>;
   using D = DOp<E>;
   constexpr int NB = C / 16;     // position blocks per chunk
   constexpr int NTS = DK / 16;   // state row tiles
@@ -189,36 +176,50 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
   // segment 0 of the summary needs only the value columns
   if (SUM && seg == 0 && vcnt == 0) return;
 
-  if (wave >= 4) {
+  if (wave >= NCW) {
     // ---------------- loading wavefronts
-    const int dw = wave - 4;
+    const int dw = wave - NCW;
     const E* qg = reinterpret_cast<const E*>(p.q);
     const E* kg = reinterpret_cast<const E*>(p.k);
     const E* vg = reinterpret_cast<const E*>(p.v);
     const E* Tg = reinterpret_cast<const E*>(p.T);
     const E* Ag = reinterpret_cast<const E*>(p.A);
     const int HDK = p.H * DK, HDV = p.H * p.DV;
-    const int vcpr = VW * (int)sizeof(E) / 16, vmask = vcpr > 0 ? pow2_part(vcpr) - 1 : 0;
+    // copy plans of the whole-chunk case; a chunk cut short by the end of the sequence takes the
+    // general copy
+    CopyPlan<E, DK, C, SEG_LOADERS> pk, pq;
+    CopyPlan<E, C, C, SEG_LOADERS> pt;
+    CopyPlan<E, Cfg::VWMAX, C, SEG_LOADERS> pv;
+    CopyPlan<float, 4, C / 4, SEG_LOADERS> pg;
+    pk.init(HDK, C, dw, lane);
+    pq.init(HDK, QR, dw, lane);
+    pt.init(C, C, dw, lane);
+    pv.init(HDV, VW > 0 ? C : 0, dw, lane, VW * (int)sizeof(E) / 16);
+    pg.init(4, C / 4, dw, lane);
     auto issue = [&](int n, int stage) {
       E* st = smem + stage * Cfg::IN;
       const long P0 = (long)n * C;
       const int krows = (int)min((long)C, p.Lx - P0);                  // valid positions
       const long tok0 = (long)n * QR;
       const int qrows = (int)min((long)QR, (long)p.L - tok0);           // valid tokens
-      copy_rows_to_lds<E, DK>(st, kg + ((long)b * p.Lx + P0) * HDK + (long)h * DK, HDK, C, krows, dw, 4, lane);
-      if (!SUM)
-        copy_rows_to_lds<E, DK>(st + Cfg::KS, qg + ((long)b * p.L + tok0) * HDK + (long)h * DK, HDK, QR, qrows, dw,
-                                4, lane);
-      copy_rows_to_lds<E, C>(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, C, C, C, dw, 4, lane);
-      if (!SUM)
-        copy_rows_to_lds<E, C>(st + Cfg::KS + Cfg::QS + Cfg::TS, Ag + ((long)head * p.NT + n) * C * C, C, C, C, dw, 4,
-                               lane);
-      if (VW > 0)
-        copy_rows_rt<E>(st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS,
-                        vg + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0, HDV, C, krows, vcpr, vmask, dw,
-                        4, lane);
-      copy_rows_to_lds<float, 4>(reinterpret_cast<float*>(st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS + Cfg::VS),
-                                 p.gc + ((long)head * p.NT + n) * C, 4, C / 4, C / 4, dw, 4, lane);
+      const E* kc = kg + ((long)b * p.Lx + P0) * HDK + (long)h * DK;
+      const E* qc = qg + ((long)b * p.L + tok0) * HDK + (long)h * DK;
+      const E* vc = vg + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0;
+      E* sv = st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS;
+      if (krows == C && (SUM || qrows == QR)) {
+        pk.issue(st, kc, dw);
+        if (!SUM) pq.issue(st + Cfg::KS, qc, dw);
+        if (VW > 0) pv.issue(sv, vc, dw);
+      } else {
+        copy_rows_to_lds<E, DK>(st, kc, HDK, C, krows, dw, SEG_LOADERS, lane);
+        if (!SUM) copy_rows_to_lds<E, DK>(st + Cfg::KS, qc, HDK, QR, qrows, dw, SEG_LOADERS, lane);
+        // the group's value columns, at the fixed row pitch VWMAX (columns past them repeat its first)
+        if (VW > 0)
+          copy_rows_to_lds<E, Cfg::VWMAX>(sv, vc, HDV, C, krows, dw, SEG_LOADERS, lane, VW * (int)sizeof(E) / 16);
+      }
+      pt.issue(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, dw);
+      if (!SUM) pt.issue(st + Cfg::KS + Cfg::QS + Cfg::TS, Ag + ((long)head * p.NT + n) * C * C, dw);
+      pg.issue(reinterpret_cast<float*>(sv + Cfg::VS), p.gc + ((long)head * p.NT + n) * C, dw);
     };
     // exp(gc) and exp(gc_last - gc) of a staged chunk, once for all chain wavefronts
     auto exps = [&](int stage) {
@@ -295,19 +296,7 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
   constexpr int CH = 16 / sizeof(E);
   constexpr int MK = PackedLayout<E, DK>::MASK, MC = PackedLayout<E, C>::MASK;
   auto swz = [](int r, int e, int ld, int mask) { return r * ld + ((e / CH) ^ (r & mask)) * CH + e % CH; };
-  const int vmask = VW > 0 ? pow2_part(VW * (int)sizeof(E) / 16) - 1 : 0;
-  int offK[NTS], offKT[NTS], offT[NB], offV[CT];
-#pragma unroll
-  for (int t = 0; t < NTS; ++t) {
-    offK[t] = swz(m, 16 * t + 4 * g4, DK, MK);                          // K, Q rows
-    offKT[t] = swz(4 * g4 + (m >> 2), 16 * t + 4 * (m & 3), DK, MK);   // K^T transpose reads
-  }
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb) offT[kb] = swz(m, 16 * kb + 4 * g4, C, MC);  // T, A rows
-#pragma unroll
-  for (int c = 0; c < CT; ++c)   // V transpose reads (D layout of the tile's 16 columns)
-    offV[c] = isv[c] ? swz(4 * g4 + (m >> 2), 16 * (tile[c] - vt0) + 4 * (m & 3), VW, vmask) : 0;
-
+  constexpr int MV = PackedLayout<E, Cfg::VWMAX>::MASK;
   if constexpr (Cfg::NSTAGE == 2) barrier_lds();
 
   E* Og = reinterpret_cast<E*>(p.O);
@@ -325,6 +314,22 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
     const float* gcp = reinterpret_cast<const float*>(Vp + Cfg::VS);
     const float* egp = gcp + C;        // exp(gc)
     const float* edp = gcp + 2 * C;    // exp(gc_last - gc)
+    // Per-lane LDS element offsets of this chunk's fragment reads, recomputed every chunk from
+    // a lane index the optimiser cannot see through (hoisted, they would pin ~20 registers).
+    int lnL = lane;
+    asm volatile("" : "+v"(lnL));
+    const int mL = lnL & 15, gL = lnL >> 4;
+    int offK[NTS], offKT[NTS], offT[NB], offV[CT];
+#pragma unroll
+    for (int t = 0; t < NTS; ++t) {
+      offK[t] = swz(mL, 16 * t + 4 * gL, DK, MK);                          // K, Q rows
+      offKT[t] = swz(4 * gL + (mL >> 2), 16 * t + 4 * (mL & 3), DK, MK);   // K^T transpose reads
+    }
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) offT[kb] = swz(mL, 16 * kb + 4 * gL, C, MC);  // T, A rows
+#pragma unroll
+    for (int c = 0; c < CT; ++c)   // V transpose reads (D layout of the tile's 16 columns)
+      offV[c] = isv[c] ? swz(4 * gL + (mL >> 2), 16 * (tile[c] - vt0) + 4 * (mL & 3), Cfg::VWMAX, MV) : 0;
 
     // chunk-start state as a B operand
     typename D::B Sb[CT][NTS];
@@ -365,10 +370,10 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
         floatx4 v4 = {0.f, 0.f, 0.f, 0.f};
         if (isv[c]) {
           if constexpr (sizeof(E) == 2) {
-            const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Vp) + 16 * bb * VW + offV[c]);
+            const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Vp) + 16 * bb * Cfg::VWMAX + offV[c]);
             v4 = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
           } else {
-            const Tile<E> V{const_cast<E*>(Vp), VW, vmask};
+            const Tile<E> V = make_packed_tile<E, Cfg::VWMAX>(const_cast<E*>(Vp));
 #pragma unroll
             for (int j = 0; j < 4; ++j) v4[j] = to_float(*V.at(16 * bb + 4 * g4 + j, 16 * (tile[c] - vt0) + m));
           }
@@ -417,6 +422,10 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
       int lo = lane;
       asm volatile("" : "+v"(lo));
       const int mo = lo & 15, go = lo >> 4;
+      // this chunk's first token row of O (uniform) and the number of its rows inside the sequence
+      const int HDV = p.H * p.DV;
+      E* Ochunk = Og + (((long)b * p.L + (long)n * QR) * p.H + h) * p.DV;
+      const int orows = min(QR, (int)((long)p.L - (long)n * QR));
 #pragma unroll
       for (int tq = 0; tq < NB; ++tq) {
         if (tq < NQT) {
@@ -464,9 +473,7 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int trow = 16 * tq + 4 * go + j;
-                const long tok = (long)n * QR + trow;
-                if (trow < QR && tok < p.L)
-                  Og[(((long)b * p.L + tok) * p.H + h) * p.DV + 16 * tile[c] + mo] = to_elem<E>(o[j]);
+                if (trow < orows) Ochunk[trow * HDV + 16 * tile[c] + mo] = to_elem<E>(o[j]);
               }
             }
           }
@@ -474,12 +481,11 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
             // back from the staging tile: lane (g4, m) gets columns 16 c + 4 g4 .. +3 of token
             // 16 tq + m (this wave's own LDS area: no barrier)
             const int trow = 16 * tq + mo;
-            const long tok = (long)n * QR + trow;
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
               const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Ost.at(16 * c + 4 * go + (mo >> 2), 16 * tq + 4 * (mo & 3))));
-              if (isv[c] && trow < QR && tok < p.L)
-                *reinterpret_cast<bf16x4*>(Og + (((long)b * p.L + tok) * p.H + h) * p.DV + 16 * tile[c] + 4 * go) = r;
+              if (isv[c] && trow < orows)
+                *reinterpret_cast<bf16x4*>(Ochunk + trow * HDV + 16 * tile[c] + 4 * go) = r;
             }
           }
         }
@@ -492,9 +498,8 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
       constexpr int BSTEP = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
 #pragma unroll
       for (int t = 0; t < NTS; ++t) {
-        floatx4 acc[CT];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) acc[c] = S[c][t] * gC;
+        for (int c = 0; c < CT; ++c) S[c][t] *= gC;
 #pragma unroll
         for (int bb = 0; bb < NB; bb += BSTEP) {
           typename D::A a0, a1;
@@ -508,14 +513,12 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
           }
           if constexpr (BSTEP == 2) {
 #pragma unroll
-            for (int c = 0; c < CT; ++c) acc[c] = D::mma2(a0, a1, DVb[c][bb], DVb[c][bb + 1], acc[c]);
+            for (int c = 0; c < CT; ++c) S[c][t] = D::mma2(a0, a1, DVb[c][bb], DVb[c][bb + 1], S[c][t]);
           } else {
 #pragma unroll
-            for (int c = 0; c < CT; ++c) acc[c] = D::mma1(a0, DVb[c][bb], acc[c]);
+            for (int c = 0; c < CT; ++c) S[c][t] = D::mma1(a0, DVb[c][bb], S[c][t]);
           }
         }
-#pragma unroll
-        for (int c = 0; c < CT; ++c) S[c][t] = acc[c];
       }
     }
     barrier_lds();  // chunk done (and, with one stage, the stage may be reloaded)
@@ -543,9 +546,12 @@ __global__ __launch_bounds__(SEG_THREADS) void seg_kernel(FwdParams p) {
 
 // Start states of the segments, in order: S_start(1) = S_end(0) and
 // S_start(q+1) = M(q) S_start(q) + S_loc(q).  One workgroup per (head, 16 state columns), one
-// wavefront per 16 state rows; fp32 MFMA.
+// wavefront per 16 state rows; fp32 MFMA.  The contraction index is permuted so that lane group
+// g takes k = 32 g + s at step s (consistently in both operands): each lane's run of M is then
+// 128 contiguous bytes, loaded as 8 vectors, two segments ahead of the step that uses it.
 template <int DK>
 __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
+  constexpr int KPL = DK / 4;  // contraction indices per lane group
   __shared__ float Sl[DK][17];
   const int NCT = p.DV / 16;
   const int head = blockIdx.x / NCT, ct = blockIdx.x % NCT;
@@ -560,53 +566,78 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
     Sl[row][m] = x;
     Sst[((long)1 * DK + row) * p.DV + 16 * ct + m] = x;
   }
+  // this lane's A run of segment q: M(q)[16t + m][KPL g4 .. KPL g4 + KPL), and its S_loc values
+  auto load = [&](int q, floatx4* a, floatx4& sl) {
+    const float* SMq = SMh + (long)q * DK * W;
+    const floatx4* src = reinterpret_cast<const floatx4*>(SMq + (long)(16 * t + m) * W + p.DV + KPL * g4);
+#pragma unroll
+    for (int i = 0; i < KPL / 4; ++i) a[i] = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sl[j] = SMq[(long)(16 * t + 4 * g4 + j) * W + 16 * ct + m];
+  };
+  // two segments of lead: loads stay in flight across a whole step
+  floatx4 a[KPL / 4], sl, a1[KPL / 4], sl1;
+  if (p.P > 2) load(1, a, sl);
+  if (p.P > 3) load(2, a1, sl1);
   __syncthreads();
   for (int q = 1; q + 1 < p.P; ++q) {
-    const float* SMq = SMh + (long)q * DK * W;
-    floatx4 acc[4];
+    floatx4 a2[KPL / 4], sl2;
+    if (q + 3 < p.P) load(q + 2, a2, sl2);
+    floatx4 acc[4] = {sl, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[0][j] = SMq[(long)(16 * t + 4 * g4 + j) * W + 16 * ct + m];
-    acc[1] = acc[2] = acc[3] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k0 = 0; k0 < DK; k0 += 4) {
-      const float a = SMq[(long)(16 * t + m) * W + p.DV + k0 + g4];
-      const float bb = Sl[k0 + g4][m];
-      acc[(k0 / 4) & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc[(k0 / 4) & 3], 0, 0, 0);
-    }
-    const floatx4 s = acc[0] + acc[1] + acc[2] + acc[3];
+    for (int s = 0; s < KPL; ++s)
+      acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s / 4][s % 4], Sl[KPL * g4 + s][m], acc[s & 3], 0, 0, 0);
+    const floatx4 st = acc[0] + acc[1] + acc[2] + acc[3];
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * t + 4 * g4 + j;
-      Sl[row][m] = s[j];
-      Sst[((long)(q + 1) * DK + row) * p.DV + 16 * ct + m] = s[j];
+      Sl[row][m] = st[j];
+      Sst[((long)(q + 1) * DK + row) * p.DV + 16 * ct + m] = st[j];
     }
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPL / 4; ++i) {
+      a[i] = a1[i];
+      a1[i] = a2[i];
+    }
+    sl = sl1;
+    sl1 = sl2;
   }
 }
 
 // ------------------------------------------------------------------ launch
-template <typename E, int DK, int C, int CT, bool SUM>
+template <typename E, int DK, int C, int CT, int NCW, bool SUM>
 static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
-  constexpr int TPG = 4 * CT;
+  using Cfg = SegCfg<E, DK, C, CT, NCW, SUM>;
+  constexpr int TPG = Cfg::TPG;
   const int NCT = p.DV / 16, MCT = SUM ? DK / 16 : 0;
   const int G = (NCT + MCT + TPG - 1) / TPG;
   const int nseg = SUM ? p.P - 1 : p.P;
   const long blocks = (long)nseg * p.B * p.H * G;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, SUM>), dim3((unsigned)blocks), dim3(SEG_THREADS), 0, st, p);
+  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, NCW, SUM>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0, st, p);
   return hipGetLastError();
 }
 
+#ifndef OUT_NCW
+#define OUT_NCW 4
+#endif
+#ifndef SUM_NCW
+#define SUM_NCW 4
+#endif
+#ifndef SUM_CT
+#define SUM_CT 2
+#endif
 template <typename E, int DK, int C>
 static hipError_t inter_run(const FwdParams& p, hipStream_t st) {
   hipError_t e;
   if (p.P > 1) {
-    if ((e = launch_seg<E, DK, C, 2, true>(p, st)) != hipSuccess) return e;
+    if ((e = launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((combine_kernel<DK>), dim3((unsigned)(p.B * p.H * (p.DV / 16))), dim3(DK / 16 * WAVE), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return p.DV / 16 <= 4 ? launch_seg<E, DK, C, 1, false>(p, st) : launch_seg<E, DK, C, 2, false>(p, st);
+  return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, false>(p, st) : launch_seg<E, DK, C, 2, 4, false>(p, st);
 }
 
 template <typename E, int DK>

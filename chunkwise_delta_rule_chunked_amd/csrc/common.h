@@ -118,18 +118,49 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Copies rows [0, nrows) of a row-major global matrix (rows of L elements, row stride gstride
 // elements) into a PackedLayout tile with direct-to-LDS loads issued by wave w of nw waves.
 // Rows at or past `valid` read row 0 instead (finite data that the caller's products cancel).
+// Chunks of a row at or past `cvalid` (16-byte chunks) read the row's first chunk instead.
 template <typename E, int L>
 __device__ inline void copy_rows_to_lds(E* tile, const E* g, int gstride, int nrows, int valid, int w, int nw,
-                                        int lane) {
+                                        int lane, int cvalid = PackedLayout<E, L>::CPR) {
   constexpr int CPR = PackedLayout<E, L>::CPR, MASK = PackedLayout<E, L>::MASK, VEC = 16 / sizeof(E);
   const int total = nrows * CPR;
   for (int i = w; i * WAVE < total; i += nw) {
     const int q = i * WAVE + lane;
     const int r = q / CPR, pc = q % CPR;
     const int src = r < valid ? r : 0;
-    if (q < total) copy16_to_lds(g + src * gstride + (pc ^ (r & MASK)) * VEC, tile + i * WAVE * VEC);
+    const int lc = pc ^ (r & MASK);
+    if (q < total) copy16_to_lds(g + src * gstride + (lc < cvalid ? lc : 0) * VEC, tile + i * WAVE * VEC);
   }
 }
+
+// The direct-to-LDS copies of one tile that one of `nw` waves issues, with the per-lane source
+// byte offsets worked out once: copy instruction i = w + nw s (s < NS) moves LDS chunks
+// [64 i, 64 i + 64) of the tile; rows are assumed valid (a partial tile takes copy_rows_to_lds).
+// Issuing then costs no vector ALU work: a uniform base plus a 32-bit lane offset per copy.
+template <typename E, int L, int ROWS, int NW>
+struct CopyPlan {
+  static constexpr int CPR = PackedLayout<E, L>::CPR, MASK = PackedLayout<E, L>::MASK, VEC = 16 / sizeof(E);
+  static constexpr int NS = ((ROWS * CPR + WAVE - 1) / WAVE + NW - 1) / NW;
+  unsigned off[NS];
+  int n;  // copies this wave issues
+  __device__ inline void init(int gstride, int nrows, int w, int lane, int cvalid = CPR) {
+    const int total = nrows * CPR;
+    n = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int q = (w + NW * s) * WAVE + lane;
+      const int r = q / CPR, lc = (q % CPR) ^ (r & MASK);
+      off[s] = q < total ? (unsigned)((r * gstride + (lc < cvalid ? lc : 0) * VEC) * (int)sizeof(E)) : ~0u;
+      if ((w + NW * s) * WAVE < total) n = s + 1;
+    }
+  }
+  __device__ inline void issue(E* tile, const E* g, int w) const {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s < n && off[s] != ~0u)
+        copy16_to_lds(reinterpret_cast<const char*>(g) + off[s], tile + (w + NW * s) * WAVE * VEC);
+  }
+};
 
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives element i % 4 of
 // the 4-element (8-byte) pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 of its

@@ -57,6 +57,25 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   const int NQT = (QR + 15) / 16;      // token row blocks
   const bool want_a = p.A != nullptr;
 
+  // stage the key tile [C][DK] and the query tile (token rows, zero past the sequence)
+  constexpr int VEC = 16 / sizeof(E);
+  constexpr int PER_ROW = DK / VEC;
+  const E* kbase = reinterpret_cast<const E*>(p.k);
+  const E* qbase = reinterpret_cast<const E*>(p.q);
+  // every thread issues all of its loads before its first LDS store, so their latencies overlap
+  constexpr int NLD = (C * PER_ROW + 255) / 256;
+  u32x4 kv[NLD], qv[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int idx = tid + 256 * u;
+    const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
+    const long pos = P0 + r, tok = (long)n * QR + r;
+    kv[u] = qv[u] = u32x4{0u, 0u, 0u, 0u};
+    if (idx < C * PER_ROW && pos < p.Lx)
+      kv[u] = *reinterpret_cast<const u32x4*>(kbase + (((long)b * p.Lx + pos) * p.H + h) * DK + c);
+    if (want_a && idx < C * PER_ROW && r < QR && tok < p.L)
+      qv[u] = *reinterpret_cast<const u32x4*>(qbase + (((long)b * p.L + tok) * p.H + h) * DK + c);
+  }
   // beta and log gate of position `lane` (wave 0); padded positions carry beta = 0, log g = 0
   if (wave == 0) {
     float beta_i = 0.f, lg = 0.f;
@@ -75,22 +94,13 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
     }
   }
 
-  // stage the key tile [C][DK] and the query tile (token rows, zero past the sequence)
-  constexpr int VEC = 16 / sizeof(E);
-  constexpr int PER_ROW = DK / VEC;
-  const E* kbase = reinterpret_cast<const E*>(p.k);
-  const E* qbase = reinterpret_cast<const E*>(p.q);
-  for (int idx = tid; idx < C * PER_ROW; idx += 256) {
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int idx = tid + 256 * u;
     const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-    const long pos = P0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (pos < p.Lx) val = *reinterpret_cast<const u32x4*>(kbase + (((long)b * p.Lx + pos) * p.H + h) * DK + c);
-    *reinterpret_cast<u32x4*>(Kt.at(r, c)) = val;
-    if (want_a) {
-      const long tok = (long)n * QR + r;
-      u32x4 qv = {0u, 0u, 0u, 0u};
-      if (r < QR && tok < p.L) qv = *reinterpret_cast<const u32x4*>(qbase + (((long)b * p.L + tok) * p.H + h) * DK + c);
-      *reinterpret_cast<u32x4*>(Qt.at(r, c)) = qv;
+    if (idx < C * PER_ROW) {
+      *reinterpret_cast<u32x4*>(Kt.at(r, c)) = kv[u];
+      if (want_a) *reinterpret_cast<u32x4*>(Qt.at(r, c)) = qv[u];
     }
   }
   __syncthreads();
@@ -207,11 +217,14 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  // T = N diag(beta), row-major, zero above the diagonal
+  // T = N diag(beta), row-major, zero above the diagonal; 4 consecutive elements per store
   TO* Tout = reinterpret_cast<TO*>(p.T) + ((long)bh * p.NT + n) * C * C;
-  for (int idx = tid; idx < C * C; idx += 256) {
+  for (int idx = 4 * tid; idx < C * C; idx += 4 * 256) {
     const int r = idx / C, c = idx % C;
-    Tout[idx] = to_elem<TO>(c <= r ? Ns[r * LDA + c] * bs[c] : 0.f);
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = c + e <= r ? Ns[r * LDA + c + e] * bs[c + e] : 0.f;
+    store4<TO>(Tout + idx, x[0], x[1], x[2], x[3]);
   }
 }
 
