@@ -61,6 +61,10 @@ def load_library():
     lib.delta_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_inter.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_segments.argtypes = [SP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.delta_fwd_scan_summary.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_scan_combine.argtypes = [SP, P, ctypes.c_size_t, P]
+    lib.delta_fwd_scan_outputs.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_chunk_wy.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_strerror.argtypes = [ctypes.c_int]
@@ -190,6 +194,49 @@ def fwd_inter(q, k, v, S0, workspace, *, n_h: int = 1, chunk: int = 64, scale: f
                                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                         _stream(stream))
     _check(rc, "delta_fwd_inter")
+    return O, S_final
+
+
+def segments(B, L, H, dk, dv, n_h=1, chunk=64, dtype=BF16):
+    """(segments, chunks per segment) of the inter-chunk phase's sequence split."""
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, dtype)
+    P, NS = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().delta_fwd_segments(ctypes.byref(sh), ctypes.byref(P), ctypes.byref(NS)),
+           "delta_fwd_segments")
+    return P.value, NS.value
+
+
+def scan_summary(k, v, S0, workspace, *, n_h: int = 1, chunk: int = 64, stream=None):
+    """First launch of fwd_inter: per-segment summaries into the workspace."""
+    torch = _torch()
+    B, Lx, H, dk = k.shape
+    sh = make_shape(B, Lx // n_h, H, dk, v.shape[-1], n_h, chunk, _dtype_code(k))
+    rc = load_library().delta_fwd_scan_summary(ctypes.byref(sh), _dev(k, "k", k.dtype), _dev(v, "v", k.dtype),
+                                               _dev(S0, "S0", torch.float32), _dev(workspace, "workspace"),
+                                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "delta_fwd_scan_summary")
+
+
+def scan_combine(workspace, *, B, L, H, dk, dv, n_h: int = 1, chunk: int = 64, dtype=BF16, stream=None):
+    """Second launch of fwd_inter: segment start states from the summaries."""
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, dtype)
+    rc = load_library().delta_fwd_scan_combine(ctypes.byref(sh), _dev(workspace, "workspace"),
+                                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "delta_fwd_scan_combine")
+
+
+def scan_outputs(q, k, v, S0, workspace, *, n_h: int = 1, chunk: int = 64, scale: float = 1.0, O=None,
+                 S_final=None, stream=None):
+    """Third launch of fwd_inter: every segment from its start state, writing O and S_final."""
+    torch = _torch()
+    B, L, H, dk = q.shape
+    sh = make_shape(B, L, H, dk, v.shape[-1], n_h, chunk, _dtype_code(q), scale)
+    rc = load_library().delta_fwd_scan_outputs(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype),
+                                               _dev(v, "v", q.dtype), _dev(S0, "S0", torch.float32),
+                                               _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32),
+                                               _dev(workspace, "workspace"),
+                                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "delta_fwd_scan_outputs")
     return O, S_final
 
 

@@ -630,40 +630,47 @@ static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
 #define SUM_CT 2
 #endif
 template <typename E, int DK, int C>
-static hipError_t inter_run(const FwdParams& p, hipStream_t st) {
-  hipError_t e;
-  if (p.P > 1) {
-    if ((e = launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<DK>), dim3((unsigned)(p.B * p.H * (p.DV / 16))), dim3(DK / 16 * WAVE), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
+  switch (phase) {
+    case SCAN_SUMMARY:
+      return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st) : hipSuccess;
+    case SCAN_COMBINE:
+      if (p.P <= 1 || p.B * p.H == 0) return hipSuccess;
+      hipLaunchKernelGGL((combine_kernel<DK>), dim3((unsigned)(p.B * p.H * (p.DV / 16))), dim3(DK / 16 * WAVE), 0, st,
+                         p);
+      return hipGetLastError();
+    case SCAN_OUTPUTS:
+      return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, false>(p, st)
+                                  : launch_seg<E, DK, C, 2, 4, false>(p, st);
+    default:
+      return hipErrorInvalidValue;
   }
-  return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, false>(p, st) : launch_seg<E, DK, C, 2, 4, false>(p, st);
 }
 
 template <typename E, int DK>
-static hipError_t inter_by_c(const FwdParams& p, hipStream_t st) {
+static hipError_t phase_by_c(const FwdParams& p, int phase, hipStream_t st) {
   switch (p.C) {
-    case 16: return inter_run<E, DK, 16>(p, st);
-    case 32: return inter_run<E, DK, 32>(p, st);
-    case 48: return inter_run<E, DK, 48>(p, st);
-    case 64: return inter_run<E, DK, 64>(p, st);
+    case 16: return scan_phase<E, DK, 16>(p, phase, st);
+    case 32: return scan_phase<E, DK, 32>(p, phase, st);
+    case 48: return scan_phase<E, DK, 48>(p, phase, st);
+    case 64: return scan_phase<E, DK, 64>(p, phase, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename E>
-static hipError_t inter_by_dk(const FwdParams& p, hipStream_t st) {
+static hipError_t phase_by_dk(const FwdParams& p, int phase, hipStream_t st) {
   switch (p.DK) {
-    case 16: return inter_by_c<E, 16>(p, st);
-    case 32: return inter_by_c<E, 32>(p, st);
-    case 64: return inter_by_c<E, 64>(p, st);
-    case 128: return inter_by_c<E, 128>(p, st);
+    case 16: return phase_by_c<E, 16>(p, phase, st);
+    case 32: return phase_by_c<E, 32>(p, phase, st);
+    case 64: return phase_by_c<E, 64>(p, phase, st);
+    case 128: return phase_by_c<E, 128>(p, phase, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_inter_chunk(const FwdParams& p, bool bf16_in, hipStream_t st) {
-  return bf16_in ? inter_by_dk<bf16>(p, st) : inter_by_dk<float>(p, st);
+hipError_t launch_scan_phase(const FwdParams& p, bool bf16_in, int phase, hipStream_t st) {
+  return bf16_in ? phase_by_dk<bf16>(p, phase, st) : phase_by_dk<float>(p, phase, st);
 }
 
 }  // namespace delta

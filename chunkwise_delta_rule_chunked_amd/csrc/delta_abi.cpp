@@ -107,9 +107,17 @@ int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
 
 namespace {
 
-// Validates a forward call and fills p.  `phase`: 0 = whole pass, 1 = intra-chunk phase only
-// (needs q, k, beta, g_log, workspace), 2 = inter-chunk phase only (needs q, k, v, S0, O,
-// S_final, workspace).  Pointers a phase does not use are ignored.
+// Phases a forward call may cover; each names the tensors it reads or writes.
+enum Phase {
+  PH_ALL = 0,      // the whole pass: q, k, v, beta, g_log, S0, O, S_final
+  PH_INTRA = 1,    // q, k, beta, g_log
+  PH_INTER = 2,    // q, k, v, S0, O, S_final
+  PH_SUMMARY = 3,  // k, v, S0
+  PH_COMBINE = 4,  // workspace only
+  PH_OUTPUTS = 5   // q, k, v, S0, O, S_final
+};
+
+// Validates a forward call and fills p.  Pointers the phase does not use are ignored.
 int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, const void* v,
                 const float* beta, const float* g_log, const float* S0, void* O, float* S_final,
                 void* workspace, size_t workspace_bytes, FwdParams& p) {
@@ -117,16 +125,22 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
   if (rc) return rc;
   if ((rc = check_chunk(s))) return rc;
   p = make_params(s);
-  const bool use_intra = phase != 2, use_inter = phase != 1;
+  const bool use_intra = phase == PH_ALL || phase == PH_INTRA;
+  const bool use_q = phase != PH_SUMMARY && phase != PH_COMBINE, use_k = phase != PH_COMBINE;
+  const bool use_vs = phase == PH_ALL || phase == PH_INTER || phase == PH_SUMMARY || phase == PH_OUTPUTS;
+  const bool use_out = phase == PH_ALL || phase == PH_INTER || phase == PH_OUTPUTS;
   if (!use_intra) beta = nullptr, g_log = nullptr;
-  if (!use_inter) v = nullptr, S0 = nullptr, O = nullptr, S_final = nullptr;
+  if (!use_q) q = nullptr;
+  if (!use_k) k = nullptr;
+  if (!use_vs) v = nullptr, S0 = nullptr;
+  if (!use_out) O = nullptr, S_final = nullptr;
   const size_t es = esize(s->dtype);
   const size_t sz_q = (size_t)p.B * p.L * p.H * p.DK * es, sz_k = (size_t)p.B * p.Lx * p.H * p.DK * es,
                sz_v = (size_t)p.B * p.Lx * p.H * p.DV * es, sz_b = (size_t)p.B * p.Lx * p.H * 4,
                sz_g = (size_t)p.B * p.L * p.H * 4, sz_S = (size_t)p.B * p.H * p.DK * p.DV * 4,
                sz_o = (size_t)p.B * p.L * p.H * p.DV * es;
   // a pointer is required when its tensor is not empty
-  if ((sz_k && !k) || (sz_q && !q) || (use_inter && ((sz_v && !v) || (sz_o && !O))) ||
+  if ((use_k && sz_k && !k) || (use_q && sz_q && !q) || (use_vs && sz_v && !v) || (use_out && sz_o && !O) ||
       (use_intra && sz_b && !beta))
     return DELTA_ERR_NULL_ARG;
   size_t need = 0;
@@ -139,7 +153,7 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
     if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
   if (!aligned(beta, 4) || !aligned(g_log, 4)) return DELTA_ERR_MISALIGNED;
 
-  const Range in[] = {range(q, q ? sz_q : 0), range(k, sz_k), range(v, v ? sz_v : 0),
+  const Range in[] = {range(q, q ? sz_q : 0), range(k, k ? sz_k : 0), range(v, v ? sz_v : 0),
                       range(beta, beta ? sz_b : 0), range(g_log, g_log ? sz_g : 0), range(S0, S0 ? sz_S : 0)};
   const Range ro = range(O, O ? sz_o : 0), rs = range(S_final, S_final ? sz_S : 0), rw = range(workspace, need);
   for (const Range& r : in) {
@@ -174,11 +188,18 @@ int run_intra(const FwdParams& p, bool bf, hipStream_t st) {
   return hip_status(delta::launch_intra_chunk(p, bf, false, st));
 }
 
-int run_inter(const FwdParams& p, bool bf, hipStream_t st) {
+int run_scan(const FwdParams& p, bool bf, int phase, hipStream_t st) {
   if (p.B * p.H == 0) return DELTA_OK;
-  // L == 0: no chunks; the inter-chunk kernel still writes S_final = S0 (or zeros)
-  if (p.NT == 0 && !p.S_final) return DELTA_OK;
-  return hip_status(delta::launch_inter_chunk(p, bf, st));
+  // L == 0: no chunks; the output launch still writes S_final = S0 (or zeros)
+  if (p.NT == 0 && (phase != delta::SCAN_OUTPUTS || !p.S_final)) return DELTA_OK;
+  return hip_status(delta::launch_scan_phase(p, bf, phase, st));
+}
+
+int run_inter(const FwdParams& p, bool bf, hipStream_t st) {
+  int rc;
+  if ((rc = run_scan(p, bf, delta::SCAN_SUMMARY, st))) return rc;
+  if ((rc = run_scan(p, bf, delta::SCAN_COMBINE, st))) return rc;
+  return run_scan(p, bf, delta::SCAN_OUTPUTS, st);
 }
 
 }  // namespace
@@ -189,7 +210,7 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
               const float* g_log, const float* S0, void* O, float* S_final, void* workspace,
               size_t workspace_bytes, void* stream) {
   FwdParams p;
-  int rc = prepare_fwd(s, 0, q, k, v, beta, g_log, S0, O, S_final, workspace, workspace_bytes, p);
+  int rc = prepare_fwd(s, PH_ALL, q, k, v, beta, g_log, S0, O, S_final, workspace, workspace_bytes, p);
   if (rc) return rc;
   const bool bf = s->dtype == DELTA_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -200,7 +221,7 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
 int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const float* beta,
                     const float* g_log, void* workspace, size_t workspace_bytes, void* stream) {
   FwdParams p;
-  int rc = prepare_fwd(s, 1, q, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
+  int rc = prepare_fwd(s, PH_INTRA, q, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
                        workspace_bytes, p);
   if (rc) return rc;
   return run_intra(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream));
@@ -209,9 +230,47 @@ int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const fl
 int delta_fwd_inter(const delta_shape* s, const void* q, const void* k, const void* v, const float* S0,
                     void* O, float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
   FwdParams p;
-  int rc = prepare_fwd(s, 2, q, k, v, nullptr, nullptr, S0, O, S_final, workspace, workspace_bytes, p);
+  int rc = prepare_fwd(s, PH_INTER, q, k, v, nullptr, nullptr, S0, O, S_final, workspace, workspace_bytes, p);
   if (rc) return rc;
   return run_inter(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream));
+}
+
+int delta_fwd_segments(const delta_shape* s, int32_t* segments, int32_t* chunks_per_segment) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_chunk(s))) return rc;
+  if (!segments || !chunks_per_segment) return DELTA_ERR_NULL_ARG;
+  const FwdParams p = make_params(s);
+  *segments = p.P;
+  *chunks_per_segment = p.NS;
+  return DELTA_OK;
+}
+
+int delta_fwd_scan_summary(const delta_shape* s, const void* k, const void* v, const float* S0,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  FwdParams p;
+  int rc = prepare_fwd(s, PH_SUMMARY, nullptr, k, v, nullptr, nullptr, S0, nullptr, nullptr, workspace,
+                       workspace_bytes, p);
+  if (rc) return rc;
+  return run_scan(p, s->dtype == DELTA_BF16, delta::SCAN_SUMMARY, static_cast<hipStream_t>(stream));
+}
+
+int delta_fwd_scan_combine(const delta_shape* s, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdParams p;
+  int rc = prepare_fwd(s, PH_COMBINE, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       workspace, workspace_bytes, p);
+  if (rc) return rc;
+  return run_scan(p, s->dtype == DELTA_BF16, delta::SCAN_COMBINE, static_cast<hipStream_t>(stream));
+}
+
+int delta_fwd_scan_outputs(const delta_shape* s, const void* q, const void* k, const void* v,
+                           const float* S0, void* O, float* S_final, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  FwdParams p;
+  int rc = prepare_fwd(s, PH_OUTPUTS, q, k, v, nullptr, nullptr, S0, O, S_final, workspace, workspace_bytes,
+                       p);
+  if (rc) return rc;
+  return run_scan(p, s->dtype == DELTA_BF16, delta::SCAN_OUTPUTS, static_cast<hipStream_t>(stream));
 }
 
 int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const float* beta,

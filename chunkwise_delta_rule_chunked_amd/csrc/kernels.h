@@ -46,7 +46,10 @@ struct DecodeParams {
 // q/k/v/O (true: bfloat16, false: float32).
 hipError_t launch_intra_chunk(const FwdParams& p, bool bf16, bool t_as_float, hipStream_t st);
 hipError_t launch_wy_factors(const FwdParams& p, bool bf16, hipStream_t st);
-hipError_t launch_inter_chunk(const FwdParams& p, bool bf16, hipStream_t st);
+// The three launches of the inter-chunk pass (see chunk_scan.hip): segment summaries,
+// segment start states, outputs.  The first two do nothing when P == 1.
+enum { SCAN_SUMMARY = 0, SCAN_COMBINE = 1, SCAN_OUTPUTS = 2 };
+hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
 
 }  // namespace delta

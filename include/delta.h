@@ -70,9 +70,11 @@ typedef struct delta_shape {
 } delta_shape;
 
 /*
- * Bytes of device workspace delta_fwd needs for this shape (a function of B, H, L,
- * n_h, chunk and dtype only).  Holds, per chunk, the UT-transform matrix T, the gated
- * causal Q K^T (both C x C in the input dtype) and the in-chunk cumulative log gate.
+ * Bytes of device workspace delta_fwd needs for this shape (a function of the shape only).
+ * Holds, per chunk, the UT-transform matrix T, the gated causal Q K^T (both C x C in the
+ * input dtype) and the in-chunk cumulative log gate; and, when the sequence is split into
+ * segments (see delta_fwd_segments), each segment's summary (float32 d_k x (d_v + d_k): its
+ * state run from zero and its d_k x d_k transition) and start state (float32 d_k x d_v).
  * Returns DELTA_OK and sets *bytes, or an error code.
  */
 int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes);
@@ -118,6 +120,31 @@ int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const fl
 int delta_fwd_inter(const delta_shape* s, const void* q, const void* k, const void* v,
                     const float* S0, void* O, float* S_final, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * How the inter-chunk phase splits each sequence: *segments segments of *chunks_per_segment
+ * chunks (the last may be shorter), a function of the shape alone.  The per-step maps of the
+ * recurrence are affine in the state (DeltaProduct notes, section 3), so segments run in
+ * parallel: each is summarised from a zero state, the summaries are chained into segment
+ * start states, and every segment is then re-run from its start state to produce outputs.
+ * With one segment the first two launches do nothing.
+ */
+int delta_fwd_segments(const delta_shape* s, int32_t* segments, int32_t* chunks_per_segment);
+
+/*
+ * The three launches of delta_fwd_inter, for per-kernel timing; called in this order on one
+ * stream after delta_fwd_intra, with the same workspace, they compute what delta_fwd_inter
+ * computes.  Arguments as for delta_fwd; each reads only the tensors it lists.
+ *   delta_fwd_scan_summary  k, v, S0 (segment 0 starts from S0) -> segment summaries
+ *   delta_fwd_scan_combine  segment summaries -> segment start states (sequential, float32)
+ *   delta_fwd_scan_outputs  q, k, v, S0 and start states -> O, S_final
+ */
+int delta_fwd_scan_summary(const delta_shape* s, const void* k, const void* v, const float* S0,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int delta_fwd_scan_combine(const delta_shape* s, void* workspace, size_t workspace_bytes, void* stream);
+int delta_fwd_scan_outputs(const delta_shape* s, const void* q, const void* k, const void* v,
+                           const float* S0, void* O, float* S_final, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Intra-chunk factors only, for inspection and testing ("08 linear delta rule & DPLR",

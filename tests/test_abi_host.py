@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_header_function(lib):
     names = D.header_functions()
     assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_intra", "delta_fwd_inter",
-                          "delta_chunk_wy", "delta_decode", "delta_strerror"}
+                          "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
+                          "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -66,6 +67,13 @@ def test_segments_rule():
     assert segments(1, 1, 16, 5) == (5, 1)
     assert segments(2, 1, 16, 300) == (100, 3)      # 128 wanted; segments of 3 chunks -> 100
     assert segments(2, 1, 16, 300)[0] * segments(2, 1, 16, 300)[1] >= 300
+
+
+def test_segments_reported(lib):
+    for B, H, L, dv, C in [(2, 16, 8192, 128, 64), (1, 16, 65536, 128, 64), (4, 8, 2048, 128, 64),
+                           (64, 16, 64, 128, 64), (1, 1, 64, 16, 16), (2, 3, 100, 32, 32), (1, 1, 0, 16, 16)]:
+        NT = (L + C - 1) // C
+        assert D.segments(B, L, H, 128 if dv == 128 else 64, dv, 1, C) == segments(B, H, dv, NT), (B, H, L, dv, C)
 
 
 def test_workspace_bytes(lib):

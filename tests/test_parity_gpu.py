@@ -187,6 +187,43 @@ def test_segment_split():
     assert head_rel_err(to_np(Sb), Sr, (0, 1)) <= TOL["bf16"]
 
 
+def test_phase_calls_match_fwd():
+    """intra, then the three scan launches called one by one, reproduce fwd bitwise."""
+    w = wl("phases", B=1, H=2, L=400, dk=64, dv=96, chunk=32, gate="weak", s0=0.1)
+    P, NS = D.segments(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk)
+    assert P > 1
+    inp = W.make_inputs(w)
+    d = inputs_to_dev(inp, "bf16")
+    O1, S1 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=w.chunk)
+    ws = torch.empty(D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk), dtype=torch.uint8, device="cuda")
+    O2, S2 = torch.empty_like(O1), torch.empty_like(S1)
+    D.fwd_intra(d["q"], d["k"], d["beta"], d["g_log"], ws, chunk=w.chunk)
+    D.scan_summary(d["k"], d["v"], d["S0"], ws, chunk=w.chunk)
+    D.scan_combine(ws, B=w.B, L=w.L, H=w.H, dk=w.dk, dv=w.dv, chunk=w.chunk)
+    D.scan_outputs(d["q"], d["k"], d["v"], d["S0"], ws, chunk=w.chunk, O=O2, S_final=S2)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dt,chunk", [("bf16", 16), ("f32", 64), ("bf16", 48)])
+def test_many_segments_weak_gate(dt, chunk):
+    """One head, a long sequence and a weak gate: the state carries across ~100 segments, so
+    every segment's transition and the chained start states matter."""
+    L = {16: 1500, 64: 3000, 48: 2400}[chunk]
+    w = wl("many_seg", B=1, H=1, L=L, dk=128, dv=128, chunk=chunk, dtype=dt, gate="weak", s0=0.1)
+    P, NS = D.segments(w.B, w.L, w.H, w.dk, w.dv, 1, chunk, D.BF16 if dt == "bf16" else D.F32)
+    say("segments", P, "x", NS, "chunks")
+    assert P >= 40
+    check(w, W.make_inputs(w))
+
+
+def test_unsplit_many_heads():
+    """Enough heads to fill the GPU: one segment per sequence (no summary or combine launch)."""
+    w = wl("unsplit", B=32, H=8, L=130, dk=32, dv=32, chunk=32, gate="cfg3", s0=0.1)
+    assert D.segments(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk) == (1, 5)
+    check(w, W.make_inputs(w), heads=[(0, 0), (7, 3), (31, 7)])
+
+
 def test_scale():
     w = wl("scale", B=1, H=2, L=70, dk=32, dv=32, chunk=32, dtype="f32", gate="cfg3")
     inp = W.make_inputs(w)
