@@ -4,8 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-others]
 
-One step = one full forward pass (intra-chunk kernel, then inter-chunk kernel) over one batch of
-synthetic inputs already resident in HBM.  W untimed warm-up steps, then K timed steps bracketed
+One step = one full forward pass (the intra-chunk kernel, then the segment summary, combine and
+output launches of the inter-chunk pass) over one batch of synthetic inputs already resident in HBM.  W untimed warm-up steps, then K timed steps bracketed
 by device synchronisation.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 Default workload: Gated DeltaNet, B=2, H=16, L=8192, d_k=d_v=128, bf16 inputs, fp32 state,
@@ -39,10 +39,25 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ algorithmic work per launch
+#
+# One prefill step is four launches: intra (T, A, gate prefix per chunk), summary (per segment:
+# the state run from zero and the d_k x d_k transition), combine (segment start states) and
+# outputs.  Bytes count every tensor a launch must read or write once; flops count the products
+# the method computes (causal / triangular counts).
+
+
+def _es(w):
+    return 2 if w.dtype == "bf16" else 4
+
+
+def _segments(w):
+    import chunkwise_delta_rule_chunked_amd as D
+    return D.segments(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk, D.BF16 if w.dtype == "bf16" else D.F32)
+
 
 def intra_bytes(w) -> int:
-    """Kernel (a): reads q, k, beta, log g; writes T and A (input dtype) and the gate prefix."""
-    es = 2 if w.dtype == "bf16" else 4
+    """Reads q, k, beta, log g; writes T and A (input dtype) and the gate prefix."""
+    es = _es(w)
     NT = -(-w.Lx // w.chunk)
     b = w.B * w.Lx * w.H * (w.dk * es + 4) + w.B * w.L * w.H * w.dk * es
     if w.gate:
@@ -51,37 +66,83 @@ def intra_bytes(w) -> int:
     return b
 
 
-def inter_bytes(w) -> int:
-    """Kernel (b): reads q, k, v, T, A, gate prefix, S0; writes O, S_final."""
-    es = 2 if w.dtype == "bf16" else 4
+def intra_flops(w) -> int:
+    """Strictly-lower Gram, the triangular inverse, causal Q K^T."""
+    C, dk, nh = w.chunk, w.dk, w.n_h
+    NT = -(-w.Lx // C)
+    reach = sum(t * nh + nh for t in range(C // nh))
+    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3 + 2 * reach * dk)
+
+
+def _chain_flops(w, cols) -> int:
+    """One chunk of the state chain on `cols` state columns: K S, T Y, K^T (D V~)."""
+    C, dk = w.chunk, w.dk
+    return 2 * C * dk * cols + C * (C + 1) * cols + 2 * C * dk * cols
+
+
+def summary_bytes(w) -> int:
+    """Segments 0..P-2: reads k, v, T, gate prefix, S0; writes each segment's summary."""
+    P, NS = _segments(w)
+    if P <= 1:
+        return 0
+    es = _es(w)
+    nch = min(-(-w.Lx // w.chunk), (P - 1) * NS)
+    pos = min(w.Lx, nch * w.chunk)
+    b = w.B * pos * w.H * (w.dk + w.dv) * es + w.B * w.H * nch * w.chunk * (w.chunk * es + 4)
+    b += w.B * w.H * w.dk * w.dv * 4 if w.s0 is not None else 0
+    b += w.B * w.H * (P - 1) * w.dk * (w.dv + w.dk) * 4
+    return b
+
+
+def summary_flops(w) -> int:
+    P, NS = _segments(w)
+    if P <= 1:
+        return 0
+    NT = -(-w.Lx // w.chunk)
+    seg0 = min(NS, NT)
+    rest = min(NT, (P - 1) * NS) - seg0
+    return w.B * w.H * (seg0 * _chain_flops(w, w.dv) + rest * _chain_flops(w, w.dv + w.dk))
+
+
+def combine_bytes(w) -> int:
+    P, _ = _segments(w)
+    if P <= 1:
+        return 0
+    return w.B * w.H * ((P - 1) * w.dk * (w.dv + w.dk) * 4 + (P - 1) * w.dk * w.dv * 4)
+
+
+def combine_flops(w) -> int:
+    P, _ = _segments(w)
+    return w.B * w.H * max(0, P - 2) * 2 * w.dk * w.dk * w.dv
+
+
+def outputs_bytes(w) -> int:
+    """Reads q, k, v, T, A, gate prefix, S0 and segment start states; writes O, S_final."""
+    es = _es(w)
+    P, _ = _segments(w)
     NT = -(-w.Lx // w.chunk)
     b = w.B * w.L * w.H * (w.dk + w.dv) * es           # q, O
     b += w.B * w.Lx * w.H * (w.dk + w.dv) * es         # k, v
     b += w.B * w.H * NT * w.chunk * (2 * w.chunk * es + 4)  # T, A, gate prefix
     b += w.B * w.H * w.dk * w.dv * 4 * (2 if w.s0 is not None else 1)
+    b += w.B * w.H * (P - 1) * w.dk * w.dv * 4
     return b
 
 
-def inter_flops(w) -> int:
-    """Kernel (b) algorithmic flops (causal/triangular counts) per launch."""
+def outputs_flops(w) -> int:
     C, dk, dv, nh = w.chunk, w.dk, w.dv, w.n_h
     QR = C // nh
-    per_chunk = (2 * C * dk * dv          # K S
-                 + C * (C + 1) * dv       # T Y (lower triangular incl. diagonal)
-                 + 2 * QR * dk * dv       # Q S
-                 + 2 * C * dk * dv)       # K^T V~
     reach = sum(t * nh + nh for t in range(QR))   # positions each token row reads
-    per_chunk += 2 * reach * dv                   # A V~ (causal)
-    NT = -(-w.Lx // C)
-    return w.B * w.H * NT * per_chunk
+    per_chunk = _chain_flops(w, dv) + 2 * QR * dk * dv + 2 * reach * dv
+    return w.B * w.H * (-(-w.Lx // C)) * per_chunk
 
 
-def intra_flops(w) -> int:
-    """Kernel (a): strictly-lower Gram, the triangular inverse, causal Q K^T."""
-    C, dk, nh = w.chunk, w.dk, w.n_h
-    NT = -(-w.Lx // C)
-    reach = sum(t * nh + nh for t in range(C // nh))
-    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3 + 2 * reach * dk)
+KERNELS = {  # phase -> (kernel symbol substring, bytes, flops)
+    "intra": ("intra_chunk_kernel", intra_bytes, intra_flops),
+    "summary": ("seg_kernel", summary_bytes, summary_flops),
+    "combine": ("combine_kernel", combine_bytes, combine_flops),
+    "outputs": ("seg_kernel", outputs_bytes, outputs_flops),
+}
 
 
 def decode_bytes(w) -> int:
@@ -92,7 +153,7 @@ def decode_bytes(w) -> int:
 
 # ------------------------------------------------------------------ timing
 
-def time_prefill(w, steps, warmup):
+def time_prefill(w, steps, warmup, copy_calibration_mib=0):
     import torch
     import chunkwise_delta_rule_chunked_amd as D
     import workloads as W
@@ -108,45 +169,85 @@ def time_prefill(w, steps, warmup):
     del inp
     O = torch.empty((w.B, w.L, w.H, w.dv), dtype=dt, device="cuda")
     SF = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    nbytes = D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk, D.BF16 if w.dtype == "bf16" else D.F32)
+    code = D.BF16 if w.dtype == "bf16" else D.F32
+    nbytes = D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk, code)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-
-    def step():
-        D.fwd_intra(q, k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
-        D.fwd_inter(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)
-
+    if copy_calibration_mib:
+        # a plain device copy of known size, for scaling the HBM byte counters of a profile run
+        src = torch.ones(copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    # the calls of one step, in order, each timed by its own event pair on the launch stream
+    calls = [
+        ("intra", lambda: D.fwd_intra(q, k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)),
+        ("summary", lambda: D.scan_summary(k, v, S0, ws, n_h=w.n_h, chunk=w.chunk)),
+        ("combine", lambda: D.scan_combine(ws, B=w.B, L=w.L, H=w.H, dk=w.dk, dv=w.dv, n_h=w.n_h, chunk=w.chunk,
+                                           dtype=code)),
+        ("outputs", lambda: D.scan_outputs(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)),
+    ]
     for _ in range(warmup):
-        step()
+        for _, c in calls:
+            c()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        D.fwd_intra(q, k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)
-        ev[i][1].record()
-        D.fwd_inter(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)
-        ev[i][2].record()
+        for j, (_, c) in enumerate(calls):
+            c()
+            ev[i][j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    intra_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    inter_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "intra_ms": intra_ms, "inter_ms": inter_ms,
+    ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j, (name, _) in enumerate(calls)}
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ms,
             "tokens_per_s": w.B * w.L * steps / wall}
+
+
+def kernel_sources_sha():
+    """Hash of the HIP sources, recorded with measured traffic so a stale figure is dropped."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "chunkwise_delta_rule_chunked_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(src, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(w, phase):
+    """HBM bytes per launch of `phase` from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when there is
+    none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % w.name)
+    if not os.path.exists(path):
+        return None
+    sha, val = None, None
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) >= 2 and parts[0] == "sources:":
+                sha = parts[1]
+            if len(parts) >= 3 and parts[0] == "traffic:" and parts[1] == phase:
+                val = int(parts[2])
+    return val if sha == kernel_sources_sha() else None
 
 
 def roofline_of(w, r):
     """Roofline record for the dominant (longest) kernel of one prefill step."""
-    if r["inter_ms"] >= r["intra_ms"]:
-        name, ms, nb, nf = "inter_chunk", r["inter_ms"], inter_bytes(w), inter_flops(w)
-    else:
-        name, ms, nb, nf = "intra_chunk", r["intra_ms"], intra_bytes(w), intra_flops(w)
+    phase = max(r["kernel_ms"], key=r["kernel_ms"].get)
+    ms = r["kernel_ms"][phase]
+    _, fb, ff = KERNELS[phase]
+    nb, nf = fb(w), ff(w)
     gbs = nb / (ms * 1e-3) / 1e9
     tflops = nf / (ms * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": name, "kernel_ms": round(ms, 5), "bytes_per_launch": nb, "flops_per_launch": nf,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w, phase),
+            "kernel": phase, "kernel_ms": round(ms, 5), "bytes_per_launch": nb, "flops_per_launch": nf,
             "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / mfma_peak, 4)}
 
 
@@ -228,6 +329,8 @@ def main():
     ap.add_argument("--workload", default="gdn_b2h16_l8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (one (b, h) shard of the work); "
@@ -243,9 +346,9 @@ def main():
         sys.exit(1)
 
     w = W.get(args.workload)
-    r = time_prefill(w, args.steps, args.warmup)
-    log("[bench] %s: %.3f ms/step (intra %.4f ms, inter %.4f ms), %.3e tokens/s" % (
-        w.name, r["ms_per_step"], r["intra_ms"], r["inter_ms"], r["tokens_per_s"]))
+    r = time_prefill(w, args.steps, args.warmup, args.copy_calibration_mib)
+    log("[bench] %s: %.3f ms/step (%s), %.3e tokens/s" % (
+        w.name, r["ms_per_step"], ", ".join("%s %.4f ms" % kv for kv in r["kernel_ms"].items()), r["tokens_per_s"]))
     line = {
         "metric": "tokens/s of chunkwise delta-rule fwd (H=16,d=128,L=8K) + % MFMA/HBM roofline",
         "value": round(r["tokens_per_s"], 1),
@@ -263,7 +366,8 @@ def main():
                    "n_h": w.n_h, "chunk": w.chunk, "gate": w.gate, "state": "fp32",
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
         "roofline": roofline_of(w, r),
-        "kernels_ms": {"intra_chunk": round(r["intra_ms"], 5), "inter_chunk": round(r["inter_ms"], 5)},
+        "kernels_ms": {k: round(v, 5) for k, v in r["kernel_ms"].items()},
+        "segments": list(_segments(w)),
     }
     if not args.no_others:
         others = {}
