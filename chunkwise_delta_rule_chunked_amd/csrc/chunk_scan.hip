@@ -546,19 +546,85 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 
 // Start states of the segments, in order: S_start(1) = S_end(0) and
 // S_start(q+1) = M(q) S_start(q) + S_loc(q).  One workgroup per (head, 16 state columns), one
-// wavefront per 16 state rows; fp32 MFMA.  The contraction index is permuted so that lane group
-// g takes k = 32 g + s at step s (consistently in both operands): each lane's run of M is then
-// 128 contiguous bytes, loaded as 8 vectors, two segments ahead of the step that uses it.
-template <int DK>
+// wavefront per 16 state rows; fp32 accumulation.  The contraction index is permuted so that lane
+// group g takes the contiguous run k in [KPL g, KPL g + KPL) (consistently in both operands):
+// each lane's run of M is then 128 contiguous bytes, loaded as vectors two segments ahead of the
+// step that uses it.  BF: products on bf16 MFMA (operands rounded to bf16, as the chunk chain
+// rounds the state every chunk), else fp32 MFMA.
+template <int DK, bool BF>
 __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
   constexpr int KPL = DK / 4;  // contraction indices per lane group
+  static_assert(!BF || KPL % 8 == 0, "bf16 steps take 8 indices per lane group");
   __shared__ float Sl[DK][17];
   const int NCT = p.DV / 16;
-  const int head = blockIdx.x / NCT, ct = blockIdx.x % NCT;
+  // workgroups are dealt round-robin over the 8 XCDs: keep the column tiles of one head on one
+  // XCD so that its transitions are fetched into one L2 once
+  int head, ct;
+  if ((p.B * p.H) % 8 == 0) {
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+    head = x + 8 * (j / NCT);
+    ct = j % NCT;
+  } else {
+    head = blockIdx.x / NCT;
+    ct = blockIdx.x % NCT;
+  }
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6, m = lane & 15, g4 = lane >> 4;
   const int W = p.DV + DK;
   const float* SMh = p.SM + (long)head * p.P * DK * W;
   float* Sst = p.Sst + (long)head * p.P * DK * p.DV;
+  // this lane's A run of segment q: M(q)[16t + m][KPL g4 .. KPL g4 + KPL), and its S_loc values
+  struct Run {
+    floatx4 a[KPL / 4];
+    floatx4 sl;
+  };
+  auto load = [&](int q, Run& r) {
+    const float* SMq = SMh + (long)q * DK * W;
+    const floatx4* src = reinterpret_cast<const floatx4*>(SMq + (long)(16 * t + m) * W + p.DV + KPL * g4);
+#pragma unroll
+    for (int i = 0; i < KPL / 4; ++i) r.a[i] = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.sl[j] = SMq[(long)(16 * t + 4 * g4 + j) * W + 16 * ct + m];
+  };
+  // one step: S_start(q+1) from the run of segment q, while the run of segment q+2 loads
+  auto step = [&](int q, const Run& cur, Run& next) {
+    if (q + 3 < p.P) load(q + 2, next);
+    floatx4 acc[4] = {cur.sl, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (BF) {
+      // 16x16x32: k slot 8 g + j of step s is k = KPL g + 8 s + j in both operands
+#pragma unroll
+      for (int s = 0; s < KPL / 8; ++s) {
+        const floatx4 x0 = cur.a[2 * s], x1 = cur.a[2 * s + 1];
+        const bf16x8 av = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
+                           (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
+        bf16x8 bv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = (bf16)Sl[KPL * g4 + 8 * s + j][m];
+        acc[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[s & 1], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KPL; ++s)
+        acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.a[s / 4][s % 4], Sl[KPL * g4 + s][m], acc[s & 3], 0, 0, 0);
+    }
+    const floatx4 st = acc[0] + acc[1] + acc[2] + acc[3];
+    // waves exchange the state only through LDS: a barrier that waits for LDS alone, so the
+    // loads in flight are not drained
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * t + 4 * g4 + j;
+      Sl[row][m] = st[j];
+      Sst[((long)(q + 1) * DK + row) * p.DV + 16 * ct + m] = st[j];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // three register sets in fixed roles (a loop with copies between them would wait for each
+  // load one step after issuing it): two segments of lead
+  Run r0, r1, r2;
+  if (p.P > 2) load(1, r0);
+  if (p.P > 3) load(2, r1);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * t + 4 * g4 + j;
@@ -566,43 +632,14 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
     Sl[row][m] = x;
     Sst[((long)1 * DK + row) * p.DV + 16 * ct + m] = x;
   }
-  // this lane's A run of segment q: M(q)[16t + m][KPL g4 .. KPL g4 + KPL), and its S_loc values
-  auto load = [&](int q, floatx4* a, floatx4& sl) {
-    const float* SMq = SMh + (long)q * DK * W;
-    const floatx4* src = reinterpret_cast<const floatx4*>(SMq + (long)(16 * t + m) * W + p.DV + KPL * g4);
-#pragma unroll
-    for (int i = 0; i < KPL / 4; ++i) a[i] = src[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sl[j] = SMq[(long)(16 * t + 4 * g4 + j) * W + 16 * ct + m];
-  };
-  // two segments of lead: loads stay in flight across a whole step
-  floatx4 a[KPL / 4], sl, a1[KPL / 4], sl1;
-  if (p.P > 2) load(1, a, sl);
-  if (p.P > 3) load(2, a1, sl1);
-  __syncthreads();
-  for (int q = 1; q + 1 < p.P; ++q) {
-    floatx4 a2[KPL / 4], sl2;
-    if (q + 3 < p.P) load(q + 2, a2, sl2);
-    floatx4 acc[4] = {sl, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < KPL; ++s)
-      acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s / 4][s % 4], Sl[KPL * g4 + s][m], acc[s & 3], 0, 0, 0);
-    const floatx4 st = acc[0] + acc[1] + acc[2] + acc[3];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * t + 4 * g4 + j;
-      Sl[row][m] = st[j];
-      Sst[((long)(q + 1) * DK + row) * p.DV + 16 * ct + m] = st[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPL / 4; ++i) {
-      a[i] = a1[i];
-      a1[i] = a2[i];
-    }
-    sl = sl1;
-    sl1 = sl2;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+  for (int q = 1; q + 1 < p.P; q += 3) {
+    step(q, r0, r2);
+    if (q + 2 >= p.P) break;
+    step(q + 1, r1, r0);
+    if (q + 3 >= p.P) break;
+    step(q + 2, r2, r1);
   }
 }
 
@@ -636,8 +673,8 @@ static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
       return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st) : hipSuccess;
     case SCAN_COMBINE:
       if (p.P <= 1 || p.B * p.H == 0) return hipSuccess;
-      hipLaunchKernelGGL((combine_kernel<DK>), dim3((unsigned)(p.B * p.H * (p.DV / 16))), dim3(DK / 16 * WAVE), 0, st,
-                         p);
+      hipLaunchKernelGGL((combine_kernel<DK, sizeof(E) == 2 && DK >= 32>), dim3((unsigned)(p.B * p.H * (p.DV / 16))),
+                         dim3(DK / 16 * WAVE), 0, st, p);
       return hipGetLastError();
     case SCAN_OUTPUTS:
       return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, false>(p, st)
