@@ -75,6 +75,11 @@ struct DOp<bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
                                                    __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
   }
+  // A fragment of a 32-deep step read as one 16-byte piece (8 consecutive elements)
+  __device__ static inline bf16x8 row8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ static inline floatx4 mma8(bf16x8 a, B b0, B b1, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
+  }
   static constexpr bool PAIRS = true;  // mma2 is one instruction (a chain must not mix shapes)
 };
 
@@ -265,7 +270,15 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     live[c] = tile[c] < NCT + ((SUM && seg == 0) ? 0 : MCT);
   }
 
-  // state init: rows 16t + 4 g4 + j, column m of tile c
+  // State rows.  With pairs of 32-deep steps (DP), the two row tiles 2u, 2u+1 of a pair interleave
+  // their d_k indices so that lane group g's k slots 8g .. 8g+7 of the pair are d_k indices
+  // 32u + 8g .. 32u + 8g + 7: the A fragment of K S and Q S is then one contiguous 16-byte read.
+  // Accumulator row 4g + j of tile t holds d_k index dkrow(t, 4g + j).
+  constexpr bool DP = D::PAIRS && NTS % 2 == 0;
+  auto dkrow = [](int t, int r) {
+    return DP ? 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3) : 16 * t + r;
+  };
+  // state init: column m of tile c
   floatx4 S[CT][NTS];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
@@ -273,7 +286,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     for (int t = 0; t < NTS; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = 16 * t + 4 * g4 + j;
+        const int row = dkrow(t, 4 * g4 + j);
         float x = 0.f;
         if (live[c]) {
           if (isv[c]) {
@@ -292,10 +305,10 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     }
 
   // Per-lane LDS element offsets of the fragments this lane reads.  A block of 16 rows further
-  // down a tile adds a constant: for r = 16 bb + x, r & mask == x & mask (every mask < 16).
+  // down a tile adds a constant: for r = 16 bb + x the key depends on x alone (every mask < 16).
   constexpr int CH = 16 / sizeof(E);
   constexpr int MK = PackedLayout<E, DK>::MASK, MC = PackedLayout<E, C>::MASK;
-  auto swz = [](int r, int e, int ld, int mask) { return r * ld + ((e / CH) ^ (r & mask)) * CH + e % CH; };
+  auto swz = [](int r, int e, int ld, int mask) { return r * ld + ((e / CH) ^ swz_key(r, mask)) * CH + e % CH; };
   constexpr int MV = PackedLayout<E, Cfg::VWMAX>::MASK;
   if constexpr (Cfg::NSTAGE == 2) barrier_lds();
 
@@ -322,8 +335,14 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     int offK[NTS], offKT[NTS], offT[NB], offV[CT];
 #pragma unroll
     for (int t = 0; t < NTS; ++t) {
-      offK[t] = swz(mL, 16 * t + 4 * gL, DK, MK);                          // K, Q rows
-      offKT[t] = swz(4 * gL + (mL >> 2), 16 * t + 4 * (mL & 3), DK, MK);   // K^T transpose reads
+      if constexpr (DP) {
+        offK[t] = swz(mL, 32 * (t >> 1) + 8 * gL, DK, MK);   // K, Q rows: 16-byte pieces (t even)
+        // K^T transpose reads: the lane addresses d_k columns dkrow(t, 4i .. 4i + 3), i = lane % 4
+        offKT[t] = swz(4 * gL + (mL >> 2), 32 * (t >> 1) + 4 * (t & 1) + 8 * (mL & 3), DK, MK);
+      } else {
+        offK[t] = swz(mL, 16 * t + 4 * gL, DK, MK);                          // K, Q rows
+        offKT[t] = swz(4 * gL + (mL >> 2), 16 * t + 4 * (mL & 3), DK, MK);   // K^T transpose reads
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) offT[kb] = swz(mL, 16 * kb + 4 * gL, C, MC);  // T, A rows
@@ -349,12 +368,12 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     for (int t = 0; t < NTS; t += TSTEP)
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        const typename D::A a0 = D::row4(Kp + 16 * bb * DK + offK[t]);
-        if constexpr (TSTEP == 2) {
-          const typename D::A a1 = D::row4(Kp + 16 * bb * DK + offK[t + 1]);
+        if constexpr (DP) {
+          const bf16x8 a = DOp<bf16>::row8(reinterpret_cast<const bf16*>(Kp) + 16 * bb * DK + offK[t]);
 #pragma unroll
-          for (int c = 0; c < CT; ++c) X[c][bb] = D::mma2(a0, a1, Sb[c][t], Sb[c][t + 1], X[c][bb]);
+          for (int c = 0; c < CT; ++c) X[c][bb] = DOp<bf16>::mma8(a, Sb[c][t], Sb[c][t + 1], X[c][bb]);
         } else {
+          const typename D::A a0 = D::row4(Kp + 16 * bb * DK + offK[t]);
 #pragma unroll
           for (int c = 0; c < CT; ++c) X[c][bb] = D::mma1(a0, Sb[c][t], X[c][bb]);
         }
@@ -434,12 +453,12 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
           for (int c = 0; c < CT; ++c) o1[c] = o2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < NTS; t += TSTEP) {
-            const typename D::A a0 = D::row4(Qp + 16 * tq * DK + offK[t]);
-            if constexpr (TSTEP == 2) {
-              const typename D::A a1 = D::row4(Qp + 16 * tq * DK + offK[t + 1]);
+            if constexpr (DP) {
+              const bf16x8 a = DOp<bf16>::row8(reinterpret_cast<const bf16*>(Qp) + 16 * tq * DK + offK[t]);
 #pragma unroll
-              for (int c = 0; c < CT; ++c) o1[c] = D::mma2(a0, a1, Sb[c][t], Sb[c][t + 1], o1[c]);
+              for (int c = 0; c < CT; ++c) o1[c] = DOp<bf16>::mma8(a, Sb[c][t], Sb[c][t + 1], o1[c]);
             } else {
+              const typename D::A a0 = D::row4(Qp + 16 * tq * DK + offK[t]);
 #pragma unroll
               for (int c = 0; c < CT; ++c) o1[c] = D::mma1(a0, Sb[c][t], o1[c]);
             }
@@ -532,7 +551,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     for (int t = 0; t < NTS; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = 16 * t + 4 * g4 + j;
+        const int row = dkrow(t, 4 * g4 + j);
         if constexpr (SUM) {
           const int W = p.DV + DK;
           const int col = isv[c] ? 16 * tile[c] + m : p.DV + 16 * (tile[c] - NCT) + m;

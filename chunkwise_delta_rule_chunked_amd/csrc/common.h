@@ -50,8 +50,15 @@ struct Mfma<float> {
   __device__ static inline floatx4 mma_tail(const float* a, const float* b, floatx4 c) { return mma(*a, *b, c); }
 };
 
+// XOR key of row r for a swizzle mask.  With 16 chunks per row (mask 15) the two 2-bit fields of
+// r & 15 are swapped: still a bijection on 16 consecutive rows, and it also spreads 4 consecutive
+// rows read at 4 different chunks each (transpose reads of column runs) over 16 chunks.
+__host__ __device__ constexpr int swz_key(int r, int mask) {
+  return mask == 15 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (r & mask);
+}
+
 // A matrix tile in LDS.  Element (r, e) lives at p + r * ld + swizzled column, where the
-// 16-byte chunks of a row are permuted by XOR with (r & mask).  With bf16 operands each lane
+// 16-byte chunks of a row are permuted by XOR with swz_key(r, mask).  With bf16 operands each lane
 // of an MFMA fragment read takes one 16-byte chunk of one of 16 rows; on gfx950 such a read
 // is free of bank conflicts when the rows are 128 or 256 bytes long and chunks are swizzled
 // (mask = chunks per row - 1), or when the row stride is an odd multiple of 32 bytes
@@ -63,7 +70,7 @@ struct Tile {
   int mask;  // chunk swizzle mask (0 = none)
   __device__ inline E* at(int r, int e) const {
     constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
-    return p + r * ld + ((((e / CH) ^ (r & mask))) * CH) + (e % CH);
+    return p + r * ld + ((((e / CH) ^ swz_key(r, mask))) * CH) + (e % CH);
   }
 };
 
@@ -128,7 +135,7 @@ __device__ inline void copy_rows_to_lds(E* tile, const E* g, int gstride, int nr
     const int q = i * WAVE + lane;
     const int r = q / CPR, pc = q % CPR;
     const int src = r < valid ? r : 0;
-    const int lc = pc ^ (r & MASK);
+    const int lc = pc ^ swz_key(r, MASK);
     if (q < total) copy16_to_lds(g + src * gstride + (lc < cvalid ? lc : 0) * VEC, tile + i * WAVE * VEC);
   }
 }
@@ -149,7 +156,7 @@ struct CopyPlan {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int q = (w + NW * s) * WAVE + lane;
-      const int r = q / CPR, lc = (q % CPR) ^ (r & MASK);
+      const int r = q / CPR, lc = (q % CPR) ^ swz_key(r, MASK);
       off[s] = q < total ? (unsigned)((r * gstride + (lc < cvalid ? lc : 0) * VEC) * (int)sizeof(E)) : ~0u;
       if ((w + NW * s) * WAVE < total) n = s + 1;
     }
