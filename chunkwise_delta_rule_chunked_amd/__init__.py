@@ -167,13 +167,13 @@ def fwd(q, k, v, beta, g_log=None, S0=None, *, n_h: int = 1, chunk: int = 64, sc
 
 
 def fwd_intra(q, k, beta, g_log, workspace, *, n_h: int = 1, chunk: int = 64, dv: int = None,
-              stream=None):
-    """Intra-chunk phase of fwd: T, the gated causal Q K^T and the gate prefix into `workspace`
-    (a uint8 GPU tensor of at least workspace_bytes(...)).  dv is only used for validation
-    (defaults to dk)."""
+              scale: float = 1.0, stream=None):
+    """Intra-chunk phase of fwd: T, the gated causal Q K^T (times `scale`, which must match the
+    later fwd_inter / scan_outputs call) and the gate prefix into `workspace` (a uint8 GPU tensor
+    of at least workspace_bytes(...)).  dv (default dk) sizes the workspace check."""
     torch = _torch()
     B, L, H, dk = q.shape
-    sh = make_shape(B, L, H, dk, dv or dk, n_h, chunk, _dtype_code(k))
+    sh = make_shape(B, L, H, dk, dv or dk, n_h, chunk, _dtype_code(k), scale)
     rc = load_library().delta_fwd_intra(ctypes.byref(sh), _dev(q, "q", k.dtype), _dev(k, "k", k.dtype),
                                         _dev(beta, "beta", torch.float32),
                                         _dev(g_log, "g_log", torch.float32), _dev(workspace, "workspace"),

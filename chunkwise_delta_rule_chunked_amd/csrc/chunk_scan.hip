@@ -125,7 +125,7 @@ struct SegCfg {
   static constexpr int THREADS = (NCW + SEG_LOADERS) * WAVE;
   static constexpr int VWMAX = 16 * TPG;    // value columns staged per chunk
   static constexpr int KS = C * DK, QS = SUM ? 0 : C * DK, TS = C * C, AS = SUM ? 0 : C * C, VS = C * VWMAX;
-  static constexpr int GS = 3 * C * 4 / ES;              // gc, exp(gc), exp(gc_last - gc)
+  static constexpr int GS = 4 * C * 4 / ES;  // gc, exp(gc), exp(gc_last - gc), token output gates
   static constexpr int IN = KS + QS + TS + AS + VS + GS;   // one staged chunk (elements)
   // bf16 outputs go through a per-wave staging tile O^T [16 CT][C]
   static constexpr bool OSTAGE = !SUM && ES == 2;
@@ -226,13 +226,15 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       if (!SUM) pt.issue(st + Cfg::KS + Cfg::QS + Cfg::TS, Ag + ((long)head * p.NT + n) * C * C, dw);
       pg.issue(reinterpret_cast<float*>(sv + Cfg::VS), p.gc + ((long)head * p.NT + n) * C, dw);
     };
-    // exp(gc) and exp(gc_last - gc) of a staged chunk, once for all chain wavefronts
+    // exp(gc), exp(gc_last - gc) and, per token row, scale * exp(gc) at the token's last
+    // sub-step (0 past the chunk's tokens) of a staged chunk, once for all chain wavefronts
     auto exps = [&](int stage) {
       if (dw == 0 && lane < C) {
         float* gcs = reinterpret_cast<float*>(smem + stage * Cfg::IN + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS + Cfg::VS);
         const float x = gcs[lane], xl = gcs[C - 1];
         gcs[C + lane] = expf(x);
         gcs[2 * C + lane] = expf(xl - x);
+        gcs[3 * C + lane] = lane < QR ? p.scale * expf(gcs[min(lane, QR - 1) * nh + nh - 1]) : 0.f;
       }
     };
     if constexpr (Cfg::NSTAGE == 2) {
@@ -327,6 +329,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     const float* gcp = reinterpret_cast<const float*>(Vp + Cfg::VS);
     const float* egp = gcp + C;        // exp(gc)
     const float* edp = gcp + 2 * C;    // exp(gc_last - gc)
+    const float* eqp = gcp + 3 * C;    // scale * exp(gc) of each token row's last sub-step
     // Per-lane LDS element offsets of this chunk's fragment reads, recomputed every chunk from
     // a lane index the optimiser cannot see through (hoisted, they would pin ~20 registers).
     int lnL = lane;
@@ -475,17 +478,12 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
               for (int c = 0; c < CT; ++c) o2[c] = D::mma1(a0, Vb[c][kb], o2[c]);
             }
           }
-          // gamma of each token's last sub-step, times scale (rows past the chunk's tokens: 0)
-          floatx4 gq;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int trow = 16 * tq + 4 * go + j;
-            const float e = egp[min(trow, QR - 1) * nh + nh - 1];
-            gq[j] = trow < QR ? e * p.scale : 0.f;
-          }
+          // scale * gamma of each token's last sub-step (rows past the chunk's tokens: 0); the
+          // stored A_qk already carries the scale
+          const floatx4 gq = *reinterpret_cast<const floatx4*>(eqp + 16 * tq + 4 * go);
 #pragma unroll
           for (int c = 0; c < CT; ++c) {
-            const floatx4 o = gq * o1[c] + p.scale * o2[c];
+            const floatx4 o = gq * o1[c] + o2[c];
             if constexpr (Cfg::OSTAGE) {
               *reinterpret_cast<bf16x4*>(Ost.at(16 * c + mo, 16 * tq + 4 * go)) = DOp<bf16>::cvt(o);
             } else if (isv[c]) {

@@ -119,9 +119,9 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
     }
   }
 
-  // Gated causal Q K^T of the chunk, stored row-major [C][C] with zeros wherever a token
-  // row may not read a position (the inter-chunk kernel reads whole rows):
-  //   A[t][j] = q_t . k_j * exp(gc_p - gc_j) for j <= p = t*n_h + n_h - 1, else 0.
+  // Gated causal Q K^T of the chunk times the readout scale, stored row-major [C][C] with zeros
+  // wherever a token row may not read a position (the inter-chunk kernel reads whole rows):
+  //   A[t][j] = scale * q_t . k_j * exp(gc_p - gc_j) for j <= p = t*n_h + n_h - 1, else 0.
   // The block (j, t) of K Q^T holds A^T: lane's D[m][n] = A[16 t + n][16 j + m], i.e. four
   // consecutive columns of one row.  Blocks are dealt round-robin to waves.
   if (want_a) {
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pc = 16 * j + rq + r;
-          if (trow < QR && pc <= ptok) a[r] = d[r] * expf(gcs[ptok] - gcs[pc]);
+          if (trow < QR && pc <= ptok) a[r] = p.scale * d[r] * expf(gcs[ptok] - gcs[pc]);
         }
       }
       store4<E>(Ag + trow * C + 16 * j + rq, a[0], a[1], a[2], a[3]);

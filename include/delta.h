@@ -109,7 +109,8 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
 /*
  * The two phases of delta_fwd, for callers that schedule them separately (and for per-kernel
  * timing).  delta_fwd_intra computes, per chunk, the UT-transform matrix T, the gated causal
- * Q K^T and the in-chunk cumulative log gate into the workspace (from q, k, beta, g_log only);
+ * Q K^T times s->scale and the in-chunk cumulative log gate into the workspace (from q, k,
+ * beta, g_log only);
  * delta_fwd_inter then runs the state recurrence and the outputs from q, k, v, S0 and that
  * workspace.  Calling
  * delta_fwd_intra then delta_fwd_inter on one stream with the same arguments and workspace

@@ -188,19 +188,20 @@ def test_segment_split():
 
 
 def test_phase_calls_match_fwd():
-    """intra, then the three scan launches called one by one, reproduce fwd bitwise."""
+    """intra, then the three scan launches called one by one, reproduce fwd bitwise (with a
+    readout scale, which the intra phase folds into the stored Q K^T)."""
     w = wl("phases", B=1, H=2, L=400, dk=64, dv=96, chunk=32, gate="weak", s0=0.1)
     P, NS = D.segments(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk)
     assert P > 1
     inp = W.make_inputs(w)
     d = inputs_to_dev(inp, "bf16")
-    O1, S1 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=w.chunk)
+    O1, S1 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=w.chunk, scale=0.5)
     ws = torch.empty(D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk), dtype=torch.uint8, device="cuda")
     O2, S2 = torch.empty_like(O1), torch.empty_like(S1)
-    D.fwd_intra(d["q"], d["k"], d["beta"], d["g_log"], ws, chunk=w.chunk)
+    D.fwd_intra(d["q"], d["k"], d["beta"], d["g_log"], ws, chunk=w.chunk, dv=w.dv, scale=0.5)
     D.scan_summary(d["k"], d["v"], d["S0"], ws, chunk=w.chunk)
     D.scan_combine(ws, B=w.B, L=w.L, H=w.H, dk=w.dk, dv=w.dv, chunk=w.chunk)
-    D.scan_outputs(d["q"], d["k"], d["v"], d["S0"], ws, chunk=w.chunk, O=O2, S_final=S2)
+    D.scan_outputs(d["q"], d["k"], d["v"], d["S0"], ws, chunk=w.chunk, scale=0.5, O=O2, S_final=S2)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(S1, S2)
 
