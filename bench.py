@@ -56,22 +56,21 @@ def _segments(w):
 
 
 def intra_bytes(w) -> int:
-    """Reads q, k, beta, log g; writes T and A (input dtype) and the gate prefix."""
+    """Reads k, beta, log g; writes T (input dtype) and the gate prefix."""
     es = _es(w)
     NT = -(-w.Lx // w.chunk)
-    b = w.B * w.Lx * w.H * (w.dk * es + 4) + w.B * w.L * w.H * w.dk * es
+    b = w.B * w.Lx * w.H * (w.dk * es + 4)
     if w.gate:
         b += w.B * w.L * w.H * 4
-    b += w.B * w.H * NT * w.chunk * (2 * w.chunk * es + 4)
+    b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)
     return b
 
 
 def intra_flops(w) -> int:
-    """Strictly-lower Gram, the triangular inverse, causal Q K^T."""
-    C, dk, nh = w.chunk, w.dk, w.n_h
+    """Strictly-lower Gram and the triangular inverse."""
+    C, dk = w.chunk, w.dk
     NT = -(-w.Lx // C)
-    reach = sum(t * nh + nh for t in range(C // nh))
-    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3 + 2 * reach * dk)
+    return w.B * w.H * NT * (C * (C - 1) * dk + C ** 3 // 3)
 
 
 def _chain_flops(w, cols) -> int:
@@ -117,13 +116,13 @@ def combine_flops(w) -> int:
 
 
 def outputs_bytes(w) -> int:
-    """Reads q, k, v, T, A, gate prefix, S0 and segment start states; writes O, S_final."""
+    """Reads q, k, v, T, gate prefix, S0 and segment start states; writes O, S_final."""
     es = _es(w)
     P, _ = _segments(w)
     NT = -(-w.Lx // w.chunk)
     b = w.B * w.L * w.H * (w.dk + w.dv) * es           # q, O
     b += w.B * w.Lx * w.H * (w.dk + w.dv) * es         # k, v
-    b += w.B * w.H * NT * w.chunk * (2 * w.chunk * es + 4)  # T, A, gate prefix
+    b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)  # T, gate prefix
     b += w.B * w.H * w.dk * w.dv * 4 * (2 if w.s0 is not None else 1)
     b += w.B * w.H * (P - 1) * w.dk * w.dv * 4
     return b
@@ -133,7 +132,8 @@ def outputs_flops(w) -> int:
     C, dk, dv, nh = w.chunk, w.dk, w.dv, w.n_h
     QR = C // nh
     reach = sum(t * nh + nh for t in range(QR))   # positions each token row reads
-    per_chunk = _chain_flops(w, dv) + 2 * QR * dk * dv + 2 * reach * dv
+    # chain, Q S, A V~ and the causal Q K^T itself
+    per_chunk = _chain_flops(w, dv) + 2 * QR * dk * dv + 2 * reach * dv + 2 * reach * dk
     return w.B * w.H * (-(-w.Lx // C)) * per_chunk
 
 
@@ -181,7 +181,7 @@ def time_prefill(w, steps, warmup, copy_calibration_mib=0):
         del src, dst
     # the calls of one step, in order, each timed by its own event pair on the launch stream
     calls = [
-        ("intra", lambda: D.fwd_intra(q, k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)),
+        ("intra", lambda: D.fwd_intra(k, beta, g, ws, n_h=w.n_h, chunk=w.chunk, dv=w.dv)),
         ("summary", lambda: D.scan_summary(k, v, S0, ws, n_h=w.n_h, chunk=w.chunk)),
         ("combine", lambda: D.scan_combine(ws, B=w.B, L=w.L, H=w.H, dk=w.dk, dv=w.dv, n_h=w.n_h, chunk=w.chunk,
                                            dtype=code)),

@@ -59,7 +59,7 @@ def load_library():
     P, SP = ctypes.c_void_p, ctypes.POINTER(Shape)
     lib.delta_fwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.delta_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-    lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_inter.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_segments.argtypes = [SP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.delta_fwd_scan_summary.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P]
@@ -166,15 +166,13 @@ def fwd(q, k, v, beta, g_log=None, S0=None, *, n_h: int = 1, chunk: int = 64, sc
     return O, S_final
 
 
-def fwd_intra(q, k, beta, g_log, workspace, *, n_h: int = 1, chunk: int = 64, dv: int = None,
-              scale: float = 1.0, stream=None):
-    """Intra-chunk phase of fwd: T, the gated causal Q K^T (times `scale`, which must match the
-    later fwd_inter / scan_outputs call) and the gate prefix into `workspace` (a uint8 GPU tensor
-    of at least workspace_bytes(...)).  dv (default dk) sizes the workspace check."""
+def fwd_intra(k, beta, g_log, workspace, *, n_h: int = 1, chunk: int = 64, dv: int = None, stream=None):
+    """Intra-chunk phase of fwd: T and the gate prefix into `workspace` (a uint8 GPU tensor of at
+    least workspace_bytes(...)).  dv (default dk) sizes the workspace check."""
     torch = _torch()
-    B, L, H, dk = q.shape
-    sh = make_shape(B, L, H, dk, dv or dk, n_h, chunk, _dtype_code(k), scale)
-    rc = load_library().delta_fwd_intra(ctypes.byref(sh), _dev(q, "q", k.dtype), _dev(k, "k", k.dtype),
+    B, Lx, H, dk = k.shape
+    sh = make_shape(B, Lx // n_h, H, dk, dv or dk, n_h, chunk, _dtype_code(k))
+    rc = load_library().delta_fwd_intra(ctypes.byref(sh), _dev(k, "k", k.dtype),
                                         _dev(beta, "beta", torch.float32),
                                         _dev(g_log, "g_log", torch.float32), _dev(workspace, "workspace"),
                                         workspace.numel() * workspace.element_size(), _stream(stream))

@@ -9,7 +9,7 @@
 // Parallel scan over the sequence: DeltaProduct notes, section 3 (the per-step maps are
 // affine in S, so they compose associatively).
 //
-// Per chunk, with T and A from the intra-chunk kernel and gamma_r = exp(gc_r):
+// Per chunk, with T from the intra-chunk kernel and gamma_r = exp(gc_r):
 //   Y   = V - gamma * (K S)                    (the residual the writes must correct)
 //   V~  = T Y                                  (= U - W S with U = T V, W = T (gamma K))
 //   O   = scale * (gamma_p * (Q S) + A V~),    A = Q K^T weighted by Gamma, causal
@@ -28,6 +28,10 @@
 //            the last segment).
 // With one segment (enough heads to fill the GPU) only the outputs launch runs, from S0.
 //
+// A (section 3's Gamma-weighted causal Q K^T) is formed in the outputs launch itself, by the
+// loading wavefronts from the staged Q and K of the next chunk while the chain works on the
+// current one: it never travels through HBM.
+//
 // Work split inside a workgroup: each of the 4 chain wavefronts owns CT 16-column tiles of
 // the state for the whole segment, so the chain needs no exchange between wavefronts.  The
 // state stays in MFMA accumulators: on gfx950 the accumulator layout of a 16x16 tile (lane l
@@ -41,9 +45,10 @@
 // workgroup fence, which would otherwise wait for the loaders' in-flight loads.
 //
 // Padded positions of the last chunk: the intra-chunk kernel leaves T's padded rows and
-// columns and A's padded columns at exactly zero, so padded key, value and query rows may
-// hold any finite data -- they are loaded from row 0 of the sequence -- without reaching an
-// output (padded rows of V~ are 0 and add nothing to the state).
+// columns at exactly zero, so padded key, value and query rows may hold any finite data --
+// they are loaded from row 0 of the sequence -- without reaching an output (padded rows of V~
+// are 0, so whatever A holds in their columns multiplies zeros, and they add nothing to the
+// state).
 #include "common.h"
 #include "kernels.h"
 
@@ -115,6 +120,15 @@ __device__ inline void barrier_all() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Rendezvous of the loading wavefronts only (the chain wavefronts are mid-chunk): each arrives
+// once per call, `target` = (calls so far) x (loading wavefronts).  Every loading wavefront runs
+// the same number of calls, so the wait always ends.  The release orders this wave's completed
+// LDS writes (its direct-to-LDS loads were waited for) before the count.
+__device__ inline void loader_rendezvous(unsigned* ctr, unsigned target, int lane) {
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+}
+
 constexpr int SEG_LOADERS = 4;  // loading wavefronts per workgroup
 constexpr int LDS_BUDGET = 160 * 1024;
 
@@ -131,8 +145,9 @@ struct SegCfg {
   static constexpr bool OSTAGE = !SUM && ES == 2;
   static constexpr int OSW = 16 * CT * C;                  // per wave (elements)
   static constexpr int OS = OSTAGE ? NCW * OSW : 0;
-  static constexpr int NSTAGE = (2 * IN + OS) * ES <= LDS_BUDGET ? 2 : 1;
-  static constexpr int ELEMS = NSTAGE * IN + OS;
+  static constexpr int SYNC = SUM ? 0 : 16 / ES;              // loader rendezvous counter
+  static constexpr int NSTAGE = (2 * IN + OS + SYNC) * ES <= LDS_BUDGET ? 2 : 1;
+  static constexpr int ELEMS = NSTAGE * IN + OS + SYNC;
   static_assert(ELEMS * ES <= LDS_BUDGET, "LDS budget");
 };
 
@@ -180,6 +195,11 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
   const int VW = 16 * vcnt;
   // segment 0 of the summary needs only the value columns
   if (SUM && seg == 0 && vcnt == 0) return;
+  unsigned* rdv = reinterpret_cast<unsigned*>(smem + Cfg::NSTAGE * Cfg::IN + Cfg::OS);
+  if constexpr (!SUM) {
+    if (tid == 0) *rdv = 0u;
+    barrier_lds();
+  }
 
   if (wave >= NCW) {
     // ---------------- loading wavefronts
@@ -188,7 +208,6 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     const E* kg = reinterpret_cast<const E*>(p.k);
     const E* vg = reinterpret_cast<const E*>(p.v);
     const E* Tg = reinterpret_cast<const E*>(p.T);
-    const E* Ag = reinterpret_cast<const E*>(p.A);
     const int HDK = p.H * DK, HDV = p.H * p.DV;
     // copy plans of the whole-chunk case; a chunk cut short by the end of the sequence takes the
     // general copy
@@ -201,7 +220,11 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     pt.init(C, C, dw, lane);
     pv.init(HDV, VW > 0 ? C : 0, dw, lane, VW * (int)sizeof(E) / 16);
     pg.init(4, C / 4, dw, lane);
-    auto issue = [&](int n, int stage) {
+    // Issues the copies of chunk n into `stage`: gate prefix, keys and queries first, then T and
+    // the values.  Returns how many of this wave's copies were issued after the first three
+    // (the outputs launch forms A from those three while the rest is in flight), or 0 when the
+    // caller must wait for everything (a chunk cut short by the end of the sequence).
+    auto issue = [&](int n, int stage) -> int {
       E* st = smem + stage * Cfg::IN;
       const long P0 = (long)n * C;
       const int krows = (int)min((long)C, p.Lx - P0);                  // valid positions
@@ -211,20 +234,21 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       const E* qc = qg + ((long)b * p.L + tok0) * HDK + (long)h * DK;
       const E* vc = vg + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0;
       E* sv = st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS;
+      pg.issue(reinterpret_cast<float*>(sv + Cfg::VS), p.gc + ((long)head * p.NT + n) * C, dw);
       if (krows == C && (SUM || qrows == QR)) {
         pk.issue(st, kc, dw);
         if (!SUM) pq.issue(st + Cfg::KS, qc, dw);
+        pt.issue(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, dw);
         if (VW > 0) pv.issue(sv, vc, dw);
-      } else {
-        copy_rows_to_lds<E, DK>(st, kc, HDK, C, krows, dw, SEG_LOADERS, lane);
-        if (!SUM) copy_rows_to_lds<E, DK>(st + Cfg::KS, qc, HDK, QR, qrows, dw, SEG_LOADERS, lane);
-        // the group's value columns, at the fixed row pitch VWMAX (columns past them repeat its first)
-        if (VW > 0)
-          copy_rows_to_lds<E, Cfg::VWMAX>(sv, vc, HDV, C, krows, dw, SEG_LOADERS, lane, VW * (int)sizeof(E) / 16);
+        return pt.n + (VW > 0 ? pv.n : 0);
       }
+      copy_rows_to_lds<E, DK>(st, kc, HDK, C, krows, dw, SEG_LOADERS, lane);
+      if (!SUM) copy_rows_to_lds<E, DK>(st + Cfg::KS, qc, HDK, QR, qrows, dw, SEG_LOADERS, lane);
       pt.issue(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, dw);
-      if (!SUM) pt.issue(st + Cfg::KS + Cfg::QS + Cfg::TS, Ag + ((long)head * p.NT + n) * C * C, dw);
-      pg.issue(reinterpret_cast<float*>(sv + Cfg::VS), p.gc + ((long)head * p.NT + n) * C, dw);
+      // the group's value columns, at the fixed row pitch VWMAX (columns past them repeat its first)
+      if (VW > 0)
+        copy_rows_to_lds<E, Cfg::VWMAX>(sv, vc, HDV, C, krows, dw, SEG_LOADERS, lane, VW * (int)sizeof(E) / 16);
+      return 0;
     };
     // exp(gc), exp(gc_last - gc) and, per token row, scale * exp(gc) at the token's last
     // sub-step (0 past the chunk's tokens) of a staged chunk, once for all chain wavefronts
@@ -237,23 +261,73 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
         gcs[3 * C + lane] = lane < QR ? p.scale * expf(gcs[min(lane, QR - 1) * nh + nh - 1]) : 0.f;
       }
     };
+    // Outputs launch: A[t][j] = scale q_t . k_j exp(gc_p - gc_j) for positions j <= p, the
+    // token's last sub-step p = t n_h + n_h - 1, else 0 (rows past the chunk's tokens: 0), from
+    // the staged Q and K once every loading wavefront's copies have landed.  Block (t, j) of
+    // K Q^T on MFMA holds A^T: lane (g, m) gets A[16 t + m][16 j + 4 g .. + 3], one row run.
+    // Every block is formed, those past the causal reach (or past the tokens: Q rows there are
+    // stale, and the select drops whatever they give) as zeros, so each wave's blocks are
+    // independent straight-line work.
+    unsigned arrivals = 0;
+    auto build_a = [&](int stage) {
+      if constexpr (!SUM) {
+        arrivals += SEG_LOADERS;
+        loader_rendezvous(rdv, arrivals, lane);
+        E* st = smem + stage * Cfg::IN;
+        const Tile<E> Kt = make_packed_tile<E, DK>(st), Qt = make_packed_tile<E, DK>(st + Cfg::KS);
+        const Tile<E> At = make_packed_tile<E, C>(st + Cfg::KS + Cfg::QS + Cfg::TS);
+        const float* gcs = reinterpret_cast<const float*>(st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS + Cfg::VS);
+        constexpr int NBLK = NB * NB, PER = (NBLK + SEG_LOADERS - 1) / SEG_LOADERS;
+        floatx4 d[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int blk = dw + SEG_LOADERS * u;
+          d[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (NBLK % SEG_LOADERS == 0 || blk < NBLK)
+            d[u] = mma_tile<E>(d[u], Kt, 16 * (blk % NB), Qt, 16 * (blk / NB), DK, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int blk = dw + SEG_LOADERS * u;
+          if (NBLK % SEG_LOADERS != 0 && blk >= NBLK) continue;
+          const int t = blk / NB, j = blk % NB;
+          const int trow = 16 * t + m, ptok = min(trow, QR - 1) * nh + nh - 1;
+          const float gp = gcs[ptok];
+          float a[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int pc = 16 * j + 4 * g4 + r;
+            const float x = p.scale * d[u][r] * gate_exp(gp - gcs[pc]);
+            a[r] = (trow < QR && pc <= ptok) ? x : 0.f;
+          }
+          store4<E>(At.at(trow, 16 * j + 4 * g4), a[0], a[1], a[2], a[3]);
+        }
+      }
+    };
+    // stage a chunk: copies, gate tables and (outputs launch) A, which needs only the first
+    // copies; everything has landed when the function returns
+    auto stage_chunk = [&](int n, int stage) {
+      const int late = issue(n, stage);
+      if constexpr (SUM) {
+        wait_vmem();
+        exps(stage);
+      } else {
+        wait_vmem_upto(late);
+        exps(stage);
+        build_a(stage);
+        wait_vmem();
+      }
+    };
     if constexpr (Cfg::NSTAGE == 2) {
-      if (n0 < n1) issue(n0, 0);
-      wait_vmem();
-      if (n0 < n1) exps(0);
+      if (n0 < n1) stage_chunk(n0, 0);
       barrier_all();  // first chunk staged
       for (int n = n0; n < n1; ++n) {
-        const int s1 = (n + 1 - n0) & 1;
-        if (n + 1 < n1) issue(n + 1, s1);
-        wait_vmem();
-        if (n + 1 < n1) exps(s1);
+        if (n + 1 < n1) stage_chunk(n + 1, (n + 1 - n0) & 1);
         barrier_all();  // chunk n done, chunk n+1 staged
       }
     } else {
       for (int n = n0; n < n1; ++n) {
-        issue(n, 0);
-        wait_vmem();
-        exps(0);
+        stage_chunk(n, 0);
         barrier_all();  // chunk n staged
         barrier_all();  // chunk n done
       }
@@ -308,16 +382,19 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 
   // Per-lane LDS element offsets of the fragments this lane reads.  A block of 16 rows further
   // down a tile adds a constant: for r = 16 bb + x the key depends on x alone (every mask < 16).
-  constexpr int CH = 16 / sizeof(E);
+  constexpr unsigned CH = 16 / sizeof(E);
   constexpr int MK = PackedLayout<E, DK>::MASK, MC = PackedLayout<E, C>::MASK;
-  auto swz = [](int r, int e, int ld, int mask) { return r * ld + ((e / CH) ^ swz_key(r, mask)) * CH + e % CH; };
+  // (column indices are never negative: unsigned chunk arithmetic is shifts and masks)
+  auto swz = [](int r, int e, int ld, int mask) {
+    const unsigned u = e;
+    return r * ld + (int)(((u / CH) ^ (unsigned)swz_key(r, mask)) * CH + u % CH);
+  };
   constexpr int MV = PackedLayout<E, Cfg::VWMAX>::MASK;
   if constexpr (Cfg::NSTAGE == 2) barrier_lds();
 
   E* Og = reinterpret_cast<E*>(p.O);
   // bf16 outputs: per-wave staging of O^T [16 CT][C], written back with transpose reads
   const Tile<E> Ost = make_packed_tile<E, C>(smem + Cfg::NSTAGE * Cfg::IN + (Cfg::OSTAGE ? wave * Cfg::OSW : 0));
-  const int NQT = (QR + 15) / 16;
 
   for (int n = n0; n < n1; ++n) {
     if constexpr (Cfg::NSTAGE == 1) barrier_lds();
@@ -351,7 +428,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     for (int kb = 0; kb < NB; ++kb) offT[kb] = swz(mL, 16 * kb + 4 * gL, C, MC);  // T, A rows
 #pragma unroll
     for (int c = 0; c < CT; ++c)   // V transpose reads (D layout of the tile's 16 columns)
-      offV[c] = isv[c] ? swz(4 * gL + (mL >> 2), 16 * (tile[c] - vt0) + 4 * (mL & 3), Cfg::VWMAX, MV) : 0;
+      offV[c] = swz(4 * gL + (mL >> 2), 16 * (isv[c] ? tile[c] - vt0 : 0) + 4 * (mL & 3), Cfg::VWMAX, MV);
 
     // chunk-start state as a B operand
     typename D::B Sb[CT][NTS];
@@ -389,15 +466,24 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       const floatx4 eg4 = *reinterpret_cast<const floatx4*>(egp + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        floatx4 v4 = {0.f, 0.f, 0.f, 0.f};
-        if (isv[c]) {
-          if constexpr (sizeof(E) == 2) {
-            const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Vp) + 16 * bb * Cfg::VWMAX + offV[c]);
-            v4 = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
-          } else {
-            const Tile<E> V = make_packed_tile<E, Cfg::VWMAX>(const_cast<E*>(Vp));
+        // read unconditionally (offV of a transition tile addresses the stage's first value
+        // columns, which may never have been loaded) and select, so the chunk body stays one
+        // straight-line block
+        floatx4 v4;
+        if constexpr (sizeof(E) == 2) {
+          const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Vp) + 16 * bb * Cfg::VWMAX + offV[c]);
+          u32x2 u = __builtin_bit_cast(u32x2, r);
+          u[0] = isv[c] ? u[0] : 0u;
+          u[1] = isv[c] ? u[1] : 0u;
+          const bf16x4 rs = __builtin_bit_cast(bf16x4, u);
+          v4 = floatx4{(float)rs[0], (float)rs[1], (float)rs[2], (float)rs[3]};
+        } else {
+          const Tile<E> V = make_packed_tile<E, Cfg::VWMAX>(const_cast<E*>(Vp));
+          const int vc = isv[c] ? 16 * (tile[c] - vt0) : 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v4[j] = to_float(*V.at(16 * bb + 4 * g4 + j, 16 * (tile[c] - vt0) + m));
+          for (int j = 0; j < 4; ++j) {
+            const float x = to_float(*V.at(16 * bb + 4 * g4 + j, vc + m));
+            v4[j] = isv[c] ? x : 0.f;
           }
         }
         Yb[c][bb] = D::cvt(v4 - eg4 * X[c][bb]);
@@ -436,7 +522,11 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     }
 
     // ---- outputs: O = scale (gamma_p Q S + A V~), S still the chunk-start state.  A is zero
-    // past each token's causal reach, so the product runs over all position blocks.
+    // past each token's causal reach, so the product runs over all position blocks.  Every row
+    // block is computed (with several sub-steps per token the blocks past the chunk's tokens read
+    // stale but in-bounds LDS and are never stored) and the stores are masked by the buffer
+    // range check: no branch splits the chunk body, so the row blocks' LDS reads, products and
+    // stores can overlap.
     if constexpr (!SUM) {
       constexpr int KSTEPA = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
       // Output addresses depend only on the lane and the chunk; hiding the lane index keeps the
@@ -448,9 +538,14 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       const int HDV = p.H * p.DV;
       E* Ochunk = Og + (((long)b * p.L + (long)n * QR) * p.H + h) * p.DV;
       const int orows = min(QR, (int)((long)p.L - (long)n * QR));
+      const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(Ochunk, orows * HDV * (int)sizeof(E));
+      // element column of each tile in O; a tile past the value columns stores out of range
+      int ocol[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) ocol[c] = isv[c] ? 16 * tile[c] : orows * HDV;
 #pragma unroll
       for (int tq = 0; tq < NB; ++tq) {
-        if (tq < NQT) {
+        {
           floatx4 o1[CT], o2[CT];
 #pragma unroll
           for (int c = 0; c < CT; ++c) o1[c] = o2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -486,12 +581,10 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
             const floatx4 o = gq * o1[c] + o2[c];
             if constexpr (Cfg::OSTAGE) {
               *reinterpret_cast<bf16x4*>(Ost.at(16 * c + mo, 16 * tq + 4 * go)) = DOp<bf16>::cvt(o);
-            } else if (isv[c]) {
+            } else {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int trow = 16 * tq + 4 * go + j;
-                if (trow < orows) Ochunk[trow * HDV + 16 * tile[c] + mo] = to_elem<E>(o[j]);
-              }
+              for (int j = 0; j < 4; ++j)
+                buffer_store4(orsrc, ((16 * tq + 4 * go + j) * HDV + ocol[c] + mo) * 4, o[j]);
             }
           }
           if constexpr (Cfg::OSTAGE) {
@@ -501,8 +594,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
               const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Ost.at(16 * c + 4 * go + (mo >> 2), 16 * tq + 4 * (mo & 3))));
-              if (isv[c] && trow < orows)
-                *reinterpret_cast<bf16x4*>(Ochunk + trow * HDV + 16 * tile[c] + 4 * go) = r;
+              buffer_store8(orsrc, (trow * HDV + ocol[c] + 4 * go) * 2, r);
             }
           }
         }
@@ -677,8 +769,12 @@ static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
 #ifndef OUT_NCW
 #define OUT_NCW 4
 #endif
+// Summary: 2 state tiles per chain wavefront; with bf16 inputs 8 chain wavefronts, so that one
+// workgroup covers 16 tiles (the d_v value and d_k transition columns of a segment together when
+// d_v + d_k <= 256: K and T are then staged once per segment, and a segment's workgroups fit the
+// GPU in one round); fp32 state fragments need twice the registers, so fp32 takes 4.
 #ifndef SUM_NCW
-#define SUM_NCW 4
+#define SUM_NCW (sizeof(E) == 2 ? 8 : 4)
 #endif
 #ifndef SUM_CT
 #define SUM_CT 2

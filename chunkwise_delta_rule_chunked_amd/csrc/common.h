@@ -69,8 +69,9 @@ struct Tile {
   int ld;    // row stride in elements
   int mask;  // chunk swizzle mask (0 = none)
   __device__ inline E* at(int r, int e) const {
-    constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
-    return p + r * ld + ((((e / CH) ^ swz_key(r, mask))) * CH) + (e % CH);
+    constexpr unsigned CH = 16 / sizeof(E);  // elements per 16-byte chunk
+    const unsigned u = e;                      // column indices are never negative: shifts, not divides
+    return p + r * ld + (int)((((u / CH) ^ (unsigned)swz_key(r, mask))) * CH + u % CH);
   }
 };
 
@@ -121,6 +122,17 @@ __device__ inline void copy16_to_lds(const void* g, void* lds_base) {
 
 // Wait until every vector memory operation of this wave has completed (vmcnt = 0).
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits until at most k (wave-uniform, clamped to [0, 15]) of this wave's vector memory loads are
+// outstanding: loads complete in issue order, so all but the k most recent have landed.
+template <int K = 15>
+__device__ inline void wait_vmem_upto(int k) {
+  if constexpr (K == 0) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  } else {
+    if (k >= K) __builtin_amdgcn_s_waitcnt(0x0F70 | K);
+    else wait_vmem_upto<K - 1>(k);
+  }
+}
 
 // Copies rows [0, nrows) of a row-major global matrix (rows of L elements, row stride gstride
 // elements) into a PackedLayout tile with direct-to-LDS loads issued by wave w of nw waves.
@@ -249,6 +261,24 @@ __device__ inline void store4<bf16>(bf16* dst, float a, float b, float c, float 
 
 // 16-byte vector type for global<->LDS copies.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over [base, base + bytes) (stride 0; descriptor word 3 = 32-bit data
+// format, the raw-buffer setting of gfx9-family parts).  A buffer access whose byte offset lies
+// outside the range is dropped by the hardware's range check, so rows past the end of a
+// sequence can be masked with no branch and no per-lane exec mask.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+__device__ inline void buffer_store8(__amdgpu_buffer_rsrc_t r, int off, bf16x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
+}
+__device__ inline void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);  // data operand is a u32
+}
+
+// exp(x) of a gate ratio (x <= 0: a decay) as the hardware base-2 exponential of x log2(e).
+__device__ inline float gate_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ inline float wave_inclusive_scan(float x, int lane) {

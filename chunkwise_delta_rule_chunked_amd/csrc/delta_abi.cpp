@@ -96,9 +96,9 @@ int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
   if ((rc = check_chunk(s))) return rc;
   if (!bytes) return DELTA_ERR_NULL_ARG;
   const FwdParams p = make_params(s);
-  // T and A (element type of the inputs), the gate prefix, then the segment summaries and
-  // segment start states of the inter-chunk pass
-  *bytes = 2 * align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p)) + align_up(sm_bytes(p)) +
+  // T (element type of the inputs), the gate prefix, then the segment summaries and segment
+  // start states of the inter-chunk pass
+  *bytes = align_up(t_bytes(p, esize(s->dtype))) + align_up(gc_bytes(p)) + align_up(sm_bytes(p)) +
            align_up(sst_bytes(p));
   return DELTA_OK;
 }
@@ -110,7 +110,7 @@ namespace {
 // Phases a forward call may cover; each names the tensors it reads or writes.
 enum Phase {
   PH_ALL = 0,      // the whole pass: q, k, v, beta, g_log, S0, O, S_final
-  PH_INTRA = 1,    // q, k, beta, g_log
+  PH_INTRA = 1,    // k, beta, g_log
   PH_INTER = 2,    // q, k, v, S0, O, S_final
   PH_SUMMARY = 3,  // k, v, S0
   PH_COMBINE = 4,  // workspace only
@@ -126,7 +126,7 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
   if ((rc = check_chunk(s))) return rc;
   p = make_params(s);
   const bool use_intra = phase == PH_ALL || phase == PH_INTRA;
-  const bool use_q = phase != PH_SUMMARY && phase != PH_COMBINE, use_k = phase != PH_COMBINE;
+  const bool use_q = phase == PH_ALL || phase == PH_INTER || phase == PH_OUTPUTS, use_k = phase != PH_COMBINE;
   const bool use_vs = phase == PH_ALL || phase == PH_INTER || phase == PH_SUMMARY || phase == PH_OUTPUTS;
   const bool use_out = phase == PH_ALL || phase == PH_INTER || phase == PH_OUTPUTS;
   if (!use_intra) beta = nullptr, g_log = nullptr;
@@ -172,9 +172,8 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
   p.O = O;
   p.S_final = S_final;
   p.T = workspace;
-  p.A = static_cast<char*>(workspace) + align_up(t_bytes(p, es));
   char* ws = static_cast<char*>(workspace);
-  size_t off = 2 * align_up(t_bytes(p, es));
+  size_t off = align_up(t_bytes(p, es));
   p.gc = reinterpret_cast<float*>(ws + off);
   off += align_up(gc_bytes(p));
   p.SM = p.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
@@ -218,10 +217,10 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
   return run_inter(p, bf, st);
 }
 
-int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const float* beta,
-                    const float* g_log, void* workspace, size_t workspace_bytes, void* stream) {
+int delta_fwd_intra(const delta_shape* s, const void* k, const float* beta, const float* g_log,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   FwdParams p;
-  int rc = prepare_fwd(s, PH_INTRA, q, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
+  int rc = prepare_fwd(s, PH_INTRA, nullptr, k, nullptr, beta, g_log, nullptr, nullptr, nullptr, workspace,
                        workspace_bytes, p);
   if (rc) return rc;
   return run_intra(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream));

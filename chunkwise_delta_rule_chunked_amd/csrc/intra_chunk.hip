@@ -1,6 +1,5 @@
 // Intra-chunk kernel: per (b, h, chunk) tile, the gate prefix, the Gram matrix K K^T on
-// MFMA, the UT transform T = (I + strictLower(diag(beta) (Gamma * K K^T)))^-1 diag(beta),
-// and the gated causal Q K^T of the chunk.
+// MFMA and the UT transform T = (I + strictLower(diag(beta) (Gamma * K K^T)))^-1 diag(beta).
 //
 // Sources: "08 linear delta rule & DPLR" page, section 2.2 (UT transform; the triangular
 // inverse by forward substitution fits on chip at C = 64; prior art blocks it as 16 x 16
@@ -9,10 +8,9 @@
 // DeltaProduct notes, section 4.1: on the expanded sequence the token's log gate sits at its
 // first sub-step, 0 at the others.
 //
-// One workgroup of 4 wavefronts per tile.  Keys and queries are staged in LDS; the lower
-// 16 x 16 blocks of K K^T and of K Q^T come from MFMA (fp32 accumulation).  Q K^T depends
-// only on the chunk's own inputs, so it is formed here once per chunk (the inter-chunk
-// kernel would otherwise form it once per value slab).
+// One workgroup of 4 wavefronts per tile.  Keys are staged in LDS; the lower 16 x 16 blocks
+// of K K^T come from MFMA (fp32 accumulation).  (The gated causal Q K^T is formed where it is
+// used, in the outputs launch of the inter-chunk pass.)
 //
 // The unit-lower-triangular inverse N = (I + A)^-1 (A strictly lower, fp32) is blocked in
 // 16 x 16 tiles: each diagonal tile is inverted by forward substitution (lane c owns column
@@ -28,7 +26,7 @@ template <typename E, int DK, int C>
 struct IntraLds {
   static constexpr int LDK = TileLayout<E, DK>::LD;  // key / query row stride (elements)
   static constexpr int LDA = C + 4;                  // fp32 row stride of A and N
-  static constexpr int KQBYTES = 2 * C * LDK * (int)sizeof(E);
+  static constexpr int KQBYTES = C * LDK * (int)sizeof(E);
   static constexpr int ANBYTES = 2 * C * LDA * 4 + 4 * 16 * 20 * 4;  // A, N, one 16x16 tile per wave
   static constexpr int BYTES = KQBYTES > ANBYTES ? KQBYTES : ANBYTES;
 };
@@ -41,8 +39,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::BYTES];
   __shared__ float gcs[C], bs[C];
   const Tile<E> Kt = make_tile<E, DK>(reinterpret_cast<E*>(smem));
-  const Tile<E> Qt = make_tile<E, DK>(reinterpret_cast<E*>(smem) + C * LDK);
-  float* As = reinterpret_cast<float*>(smem);   // after the tiles are dead
+  float* As = reinterpret_cast<float*>(smem);   // after the key tile is dead
   float* Ns = As + C * LDA;
   float* Ps = Ns + C * LDA;                     // 4 x [16][20] per-wave product tiles
 
@@ -53,28 +50,22 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   const int b = bh / p.H, h = bh % p.H;
   const long P0 = (long)n * C;
   const int nh = p.nh;
-  const int QR = C / nh;               // tokens in a chunk
-  const int NQT = (QR + 15) / 16;      // token row blocks
-  const bool want_a = p.A != nullptr;
 
-  // stage the key tile [C][DK] and the query tile (token rows, zero past the sequence)
+  // stage the key tile [C][DK] (zero past the sequence)
   constexpr int VEC = 16 / sizeof(E);
   constexpr int PER_ROW = DK / VEC;
   const E* kbase = reinterpret_cast<const E*>(p.k);
-  const E* qbase = reinterpret_cast<const E*>(p.q);
   // every thread issues all of its loads before its first LDS store, so their latencies overlap
   constexpr int NLD = (C * PER_ROW + 255) / 256;
-  u32x4 kv[NLD], qv[NLD];
+  u32x4 kv[NLD];
 #pragma unroll
   for (int u = 0; u < NLD; ++u) {
     const int idx = tid + 256 * u;
     const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-    const long pos = P0 + r, tok = (long)n * QR + r;
-    kv[u] = qv[u] = u32x4{0u, 0u, 0u, 0u};
+    const long pos = P0 + r;
+    kv[u] = u32x4{0u, 0u, 0u, 0u};
     if (idx < C * PER_ROW && pos < p.Lx)
       kv[u] = *reinterpret_cast<const u32x4*>(kbase + (((long)b * p.Lx + pos) * p.H + h) * DK + c);
-    if (want_a && idx < C * PER_ROW && r < QR && tok < p.L)
-      qv[u] = *reinterpret_cast<const u32x4*>(qbase + (((long)b * p.L + tok) * p.H + h) * DK + c);
   }
   // beta and log gate of position `lane` (wave 0); padded positions carry beta = 0, log g = 0
   if (wave == 0) {
@@ -98,10 +89,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   for (int u = 0; u < NLD; ++u) {
     const int idx = tid + 256 * u;
     const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-    if (idx < C * PER_ROW) {
-      *reinterpret_cast<u32x4*>(Kt.at(r, c)) = kv[u];
-      if (want_a) *reinterpret_cast<u32x4*>(Qt.at(r, c)) = qv[u];
-    }
+    if (idx < C * PER_ROW) *reinterpret_cast<u32x4*>(Kt.at(r, c)) = kv[u];
   }
   __syncthreads();
 
@@ -119,31 +107,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
     }
   }
 
-  // Gated causal Q K^T of the chunk times the readout scale, stored row-major [C][C] with zeros
-  // wherever a token row may not read a position (the inter-chunk kernel reads whole rows):
-  //   A[t][j] = scale * q_t . k_j * exp(gc_p - gc_j) for j <= p = t*n_h + n_h - 1, else 0.
-  // The block (j, t) of K Q^T holds A^T: lane's D[m][n] = A[16 t + n][16 j + m], i.e. four
-  // consecutive columns of one row.  Blocks are dealt round-robin to waves.
-  if (want_a) {
-    E* Ag = reinterpret_cast<E*>(p.A) + ((long)bh * p.NT + n) * C * C;
-    for (int blk = wave; blk < NB * NB; blk += 4) {
-      const int t = blk / NB, j = blk % NB;
-      const int trow = 16 * t + col;
-      const int ptok = trow * nh + nh - 1;
-      float a[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < NQT && 16 * j <= (min(16 * t + 15, QR - 1) * nh + nh - 1)) {
-        floatx4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma_tile<E>(d, Kt, 16 * j, Qt, 16 * t, DK, lane);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pc = 16 * j + rq + r;
-          if (trow < QR && pc <= ptok) a[r] = p.scale * d[r] * expf(gcs[ptok] - gcs[pc]);
-        }
-      }
-      store4<E>(Ag + trow * C + 16 * j + rq, a[0], a[1], a[2], a[3]);
-    }
-  }
-  __syncthreads();  // the key/query tiles are dead: A and N overwrite them
+  __syncthreads();  // the key tile is dead: A and N overwrite it
 
   // A_rc = beta_r exp(gc_r - gc_c) (K K^T)_rc for r > c (0 on and above the diagonal)
 #pragma unroll
@@ -157,7 +121,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * i + rq + r;
-        As[row * LDA + c] = (row > c) ? bs[row] * expf(gcs[row] - gcs[c]) * G[u][r] : 0.f;
+        As[row * LDA + c] = (row > c) ? bs[row] * gate_exp(gcs[row] - gcs[c]) * G[u][r] : 0.f;
       }
     }
   }

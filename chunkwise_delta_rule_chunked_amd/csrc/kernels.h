@@ -19,8 +19,6 @@ struct FwdParams {
   void* O;              // [B, L, H, DV]
   float* S_final;       // [B, H, DK, DV] or nullptr
   void* T;              // [B, H, NT, C, C]: element type of the inputs, or float for chunk_wy
-  void* A;              // [B, H, NT, C, C] element type of the inputs: gated causal Q K^T per
-                        // chunk (token rows, position columns); nullptr = not computed
   float* gc;            // [B, H, NT, C] cumulative in-chunk log gate
   float* W;             // chunk_wy only: [B, H, NT, C, DK]
   float* U;             // chunk_wy only: [B, H, NT, C, DV]

@@ -71,8 +71,8 @@ typedef struct delta_shape {
 
 /*
  * Bytes of device workspace delta_fwd needs for this shape (a function of the shape only).
- * Holds, per chunk, the UT-transform matrix T, the gated causal Q K^T (both C x C in the
- * input dtype) and the in-chunk cumulative log gate; and, when the sequence is split into
+ * Holds, per chunk, the UT-transform matrix T (C x C in the input dtype) and the in-chunk
+ * cumulative log gate; and, when the sequence is split into
  * segments (see delta_fwd_segments), each segment's summary (float32 d_k x (d_v + d_k): its
  * state run from zero and its d_k x d_k transition) and start state (float32 d_k x d_v).
  * Returns DELTA_OK and sets *bytes, or an error code.
@@ -108,16 +108,15 @@ int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
 
 /*
  * The two phases of delta_fwd, for callers that schedule them separately (and for per-kernel
- * timing).  delta_fwd_intra computes, per chunk, the UT-transform matrix T, the gated causal
- * Q K^T times s->scale and the in-chunk cumulative log gate into the workspace (from q, k,
- * beta, g_log only);
+ * timing).  delta_fwd_intra computes, per chunk, the UT-transform matrix T and the in-chunk
+ * cumulative log gate into the workspace (from k, beta, g_log only);
  * delta_fwd_inter then runs the state recurrence and the outputs from q, k, v, S0 and that
- * workspace.  Calling
+ * workspace (the gated causal Q K^T of each chunk is formed on chip there).  Calling
  * delta_fwd_intra then delta_fwd_inter on one stream with the same arguments and workspace
  * computes exactly what delta_fwd computes.  Arguments as for delta_fwd.
  */
-int delta_fwd_intra(const delta_shape* s, const void* q, const void* k, const float* beta,
-                    const float* g_log, void* workspace, size_t workspace_bytes, void* stream);
+int delta_fwd_intra(const delta_shape* s, const void* k, const float* beta, const float* g_log,
+                    void* workspace, size_t workspace_bytes, void* stream);
 int delta_fwd_inter(const delta_shape* s, const void* q, const void* k, const void* v,
                     const float* S0, void* O, float* S_final, void* workspace,
                     size_t workspace_bytes, void* stream);

@@ -87,7 +87,7 @@ def test_workspace_bytes(lib):
         t_bytes = B * H * NT * C * C * es
         gc_bytes = B * H * NT * C * 4
         seg = up(B * H * P * dk * (dv + dk) * 4) + up(B * H * P * dk * dv * 4) if P > 1 else 0
-        assert rc == 0 and n == 2 * up(t_bytes) + up(gc_bytes) + seg, (B, H, L, dk, dv, C)
+        assert rc == 0 and n == up(t_bytes) + up(gc_bytes) + seg, (B, H, L, dk, dv, C)
     assert ws(shape(L=0)) == (0, 0)
 
 

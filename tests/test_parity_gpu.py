@@ -189,7 +189,7 @@ def test_segment_split():
 
 def test_phase_calls_match_fwd():
     """intra, then the three scan launches called one by one, reproduce fwd bitwise (with a
-    readout scale, which the intra phase folds into the stored Q K^T)."""
+    readout scale, which the outputs launch folds into its on-chip Q K^T)."""
     w = wl("phases", B=1, H=2, L=400, dk=64, dv=96, chunk=32, gate="weak", s0=0.1)
     P, NS = D.segments(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk)
     assert P > 1
@@ -198,7 +198,7 @@ def test_phase_calls_match_fwd():
     O1, S1 = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], chunk=w.chunk, scale=0.5)
     ws = torch.empty(D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, 1, w.chunk), dtype=torch.uint8, device="cuda")
     O2, S2 = torch.empty_like(O1), torch.empty_like(S1)
-    D.fwd_intra(d["q"], d["k"], d["beta"], d["g_log"], ws, chunk=w.chunk, dv=w.dv, scale=0.5)
+    D.fwd_intra(d["k"], d["beta"], d["g_log"], ws, chunk=w.chunk, dv=w.dv)
     D.scan_summary(d["k"], d["v"], d["S0"], ws, chunk=w.chunk)
     D.scan_combine(ws, B=w.B, L=w.L, H=w.H, dk=w.dk, dv=w.dv, chunk=w.chunk)
     D.scan_outputs(d["q"], d["k"], d["v"], d["S0"], ws, chunk=w.chunk, scale=0.5, O=O2, S_final=S2)
