@@ -22,26 +22,33 @@
 
 namespace delta {
 
+// A and N are lower triangular: only their NB (NB + 1) / 2 blocks of 16 x 16 on and below the
+// diagonal are stored, block (i, j) at index i (i + 1) / 2 + j, rows padded to LDB floats.
 template <typename E, int DK, int C>
 struct IntraLds {
-  static constexpr int LDK = TileLayout<E, DK>::LD;  // key / query row stride (elements)
-  static constexpr int LDA = C + 4;                  // fp32 row stride of A and N
-  static constexpr int KQBYTES = C * LDK * (int)sizeof(E);
-  static constexpr int ANBYTES = 2 * C * LDA * 4 + 4 * 16 * 20 * 4;  // A, N, one 16x16 tile per wave
-  static constexpr int BYTES = KQBYTES > ANBYTES ? KQBYTES : ANBYTES;
+  static constexpr int NB = C / 16;
+  static constexpr int LDK = TileLayout<E, DK>::LD;  // key row stride (elements)
+  static constexpr int LDB = 20;                      // fp32 row stride inside a 16 x 16 block
+  static constexpr int BLK = 16 * LDB;                // floats per block
+  static constexpr int NBLK = NB * (NB + 1) / 2;
+  static constexpr int KBYTES = C * LDK * (int)sizeof(E);
+  static constexpr int ANBYTES = (2 * NBLK + 4) * BLK * 4;  // A, N, one 16x16 tile per wave
+  static constexpr int BYTES = KBYTES > ANBYTES ? KBYTES : ANBYTES;
 };
+__host__ __device__ constexpr int lower_block(int i, int j) { return i * (i + 1) / 2 + j; }
 
 template <typename E, typename TO, int DK, int C>
 __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   using Lds = IntraLds<E, DK, C>;
-  constexpr int LDK = Lds::LDK, LDA = Lds::LDA, NB = C / 16;
-  constexpr int NBLK = NB * (NB + 1) / 2;  // lower blocks of K K^T
+  constexpr int NB = C / 16, LDB = Lds::LDB, BLK = Lds::BLK;
+  constexpr int NBLK = Lds::NBLK;  // lower blocks of K K^T
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::BYTES];
   __shared__ float gcs[C], bs[C];
   const Tile<E> Kt = make_tile<E, DK>(reinterpret_cast<E*>(smem));
   float* As = reinterpret_cast<float*>(smem);   // after the key tile is dead
-  float* Ns = As + C * LDA;
-  float* Ps = Ns + C * LDA;                     // 4 x [16][20] per-wave product tiles
+  float* Ns = As + NBLK * BLK;
+  float* Ps = Ns + NBLK * BLK;                  // 4 x [16][LDB] per-wave product tiles
+  auto blk = [](float* base, int i, int j) { return base + lower_block(i, j) * BLK; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, rq = 4 * (lane >> 4);
@@ -50,34 +57,40 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   const int b = bh / p.H, h = bh % p.H;
   const long P0 = (long)n * C;
   const int nh = p.nh;
+  const int valid = (int)min((long)C, p.Lx - P0);   // positions of this chunk inside the sequence
 
-  // stage the key tile [C][DK] (zero past the sequence)
+  // stage the key tile [C][DK]: rows past the sequence fall outside the buffer range and read 0
   constexpr int VEC = 16 / sizeof(E);
   constexpr int PER_ROW = DK / VEC;
-  const E* kbase = reinterpret_cast<const E*>(p.k);
+  const int HDK = p.H * DK;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(
+      const_cast<E*>(reinterpret_cast<const E*>(p.k)) + (((long)b * p.Lx + P0) * p.H + h) * DK,
+      valid * HDK * (int)sizeof(E));
   // every thread issues all of its loads before its first LDS store, so their latencies overlap
   constexpr int NLD = (C * PER_ROW + 255) / 256;
+  constexpr bool WHOLE = (C * PER_ROW) % 256 == 0;   // every thread's copies fall inside the tile
   u32x4 kv[NLD];
 #pragma unroll
   for (int u = 0; u < NLD; ++u) {
     const int idx = tid + 256 * u;
     const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-    const long pos = P0 + r;
-    kv[u] = u32x4{0u, 0u, 0u, 0u};
-    if (idx < C * PER_ROW && pos < p.Lx)
-      kv[u] = *reinterpret_cast<const u32x4*>(kbase + (((long)b * p.Lx + pos) * p.H + h) * DK + c);
+    kv[u] = buffer_load16(krs, (r * HDK + c) * (int)sizeof(E));
   }
   // beta and log gate of position `lane` (wave 0); padded positions carry beta = 0, log g = 0
   if (wave == 0) {
-    float beta_i = 0.f, lg = 0.f;
-    if (lane < C) {
-      const long pos = P0 + lane;
-      if (pos < p.Lx) {
-        beta_i = p.beta[((long)b * p.Lx + pos) * p.H + h];
-        if (p.g_log && (pos % nh) == 0) lg = p.g_log[((long)b * p.L + pos / nh) * p.H + h];
-      }
+    const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(const_cast<float*>(p.beta) + ((long)b * p.Lx + P0) * p.H + h,
+                                                   valid * p.H * 4);
+    const float beta_i = buffer_load4(brs, lane < C ? lane * p.H * 4 : valid * p.H * 4);
+    float lg = 0.f;
+    if (p.g_log) {
+      // the token's log gate sits at its first sub-step (P0 is a multiple of n_h)
+      const int tok0 = (int)(P0 / nh), ntok = (valid + nh - 1) / nh;
+      const __amdgpu_buffer_rsrc_t grs = buffer_rsrc(const_cast<float*>(p.g_log) + ((long)b * p.L + tok0) * p.H + h,
+                                                     ntok * p.H * 4);
+      const bool first = lane < C && lane % nh == 0;
+      lg = buffer_load4(grs, first ? (lane / nh) * p.H * 4 : ntok * p.H * 4);
     }
-    const float gc = wave_inclusive_scan(lane < C ? lg : 0.f, lane);
+    const float gc = wave_inclusive_scan(lg, lane);
     if (lane < C) {
       gcs[lane] = gc;
       bs[lane] = beta_i;
@@ -89,7 +102,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   for (int u = 0; u < NLD; ++u) {
     const int idx = tid + 256 * u;
     const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-    if (idx < C * PER_ROW) *reinterpret_cast<u32x4*>(Kt.at(r, c)) = kv[u];
+    if (WHOLE || idx < C * PER_ROW) *reinterpret_cast<u32x4*>(Kt.at(r, c)) = kv[u];
   }
   __syncthreads();
 
@@ -117,41 +130,49 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
       int i = 0;
       while ((i + 1) * (i + 2) / 2 <= t) ++i;
       const int j = t - i * (i + 1) / 2;
-      const int c = 16 * j + col;
+      const int c = 16 * j + col, row0 = 16 * i + rq;
+      const floatx4 br = *reinterpret_cast<const floatx4*>(bs + row0);
+      const floatx4 gr = *reinterpret_cast<const floatx4*>(gcs + row0);
+      const float gcc = gcs[c];
+      float* Ab = blk(As, i, j) + rq * LDB + col;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * i + rq + r;
-        As[row * LDA + c] = (row > c) ? bs[row] * gate_exp(gcs[row] - gcs[c]) * G[u][r] : 0.f;
-      }
+      for (int r = 0; r < 4; ++r)
+        Ab[r * LDB] = (row0 + r > c) ? br[r] * gate_exp(gr[r] - gcc) * G[u][r] : 0.f;
     }
   }
   // N starts as zero above the block diagonal (never read there) -- only the computed tiles
   // are read, so no clearing is needed.
   __syncthreads();
 
-  // diagonal tiles: wave w inverts tile w by forward substitution, lane c < 16 owns column c
-  if (wave < NB && lane < 16) {
-    const int o = 16 * wave;
+  // diagonal tiles by forward substitution, all in wave 0: lane 16 t + c owns column c of tile t
+  // (x_i = e_i - sum_{j<i} A_ij x_j), rows of A read 4 at a time
+  if (wave == 0 && lane < 16 * NB) {
+    const int t = lane >> 4;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float a0 = (i == lane) ? 1.f : 0.f, a1 = 0.f;
-      const float* Ai = As + (o + i) * LDA + o;
+      float a0 = (i == col) ? 1.f : 0.f, a1 = 0.f;
+      const float* Ai = blk(As, t, t) + i * LDB;
 #pragma unroll
-      for (int j = 0; j < i; j += 2) {
-        a0 -= Ai[j] * x[j];
-        if (j + 1 < i) a1 -= Ai[j + 1] * x[j + 1];
+      for (int j4 = 0; j4 < i; j4 += 4) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(Ai + j4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j4 + e < i) {
+            if (e & 1) a1 -= a[e] * x[j4 + e];
+            else a0 -= a[e] * x[j4 + e];
+          }
       }
       x[i] = a0 + a1;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Ns[(o + i) * LDA + o + lane] = x[i];
+    for (int i = 0; i < 16; ++i) blk(Ns, t, t)[i * LDB + col] = x[i];
   }
   __syncthreads();
 
   // tiles below the diagonal, one block diagonal d at a time:
   //   P = sum_{k=j}^{i-1} A_ik N_kj  (then through LDS),  N_ij = -N_ii P
-  float* Pw = Ps + wave * 16 * 20;
+  float* Pw = Ps + wave * BLK;
   for (int d = 1; d < NB; ++d) {
     const int i = wave + d, j = wave;   // wave w owns tile (w + d, w)
     if (i < NB) {
@@ -161,11 +182,11 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
         for (int k0 = 0; k0 < 16; k0 += 4) {
           const int kk = k0 + (lane >> 4);
-          acc = Mfma<float>::mma(As[(16 * i + col) * LDA + 16 * k + kk], Ns[(16 * k + kk) * LDA + 16 * j + col], acc);
+          acc = Mfma<float>::mma(blk(As, i, k)[col * LDB + kk], blk(Ns, k, j)[kk * LDB + col], acc);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Pw[(rq + r) * 20 + col] = acc[r];
+      for (int r = 0; r < 4; ++r) Pw[(rq + r) * LDB + col] = acc[r];
     }
     __syncthreads();
     if (i < NB) {
@@ -173,21 +194,25 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
       for (int k0 = 0; k0 < 16; k0 += 4) {
         const int kk = k0 + (lane >> 4);
-        acc = Mfma<float>::mma(Ns[(16 * i + col) * LDA + 16 * i + kk], Pw[kk * 20 + col], acc);
+        acc = Mfma<float>::mma(blk(Ns, i, i)[col * LDB + kk], Pw[kk * LDB + col], acc);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ns[(16 * i + rq + r) * LDA + 16 * j + col] = -acc[r];
+      for (int r = 0; r < 4; ++r) blk(Ns, i, j)[(rq + r) * LDB + col] = -acc[r];
     }
     __syncthreads();
   }
 
   // T = N diag(beta), row-major, zero above the diagonal; 4 consecutive elements per store
   TO* Tout = reinterpret_cast<TO*>(p.T) + ((long)bh * p.NT + n) * C * C;
+#pragma unroll
   for (int idx = 4 * tid; idx < C * C; idx += 4 * 256) {
     const int r = idx / C, c = idx % C;
+    // blocks above the diagonal are not stored: the index stays inside N, the select drops it
+    const floatx4 nv = *reinterpret_cast<const floatx4*>(blk(Ns, r >> 4, c >> 4) + (r & 15) * LDB + (c & 15));
+    const floatx4 bv = *reinterpret_cast<const floatx4*>(bs + c);
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = c + e <= r ? Ns[r * LDA + c + e] * bs[c + e] : 0.f;
+    for (int e = 0; e < 4; ++e) x[e] = c + e <= r ? nv[e] * bv[e] : 0.f;
     store4<TO>(Tout + idx, x[0], x[1], x[2], x[3]);
   }
 }
