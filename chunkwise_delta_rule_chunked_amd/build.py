@@ -16,7 +16,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdelta.so")
-SOURCES = ["intra_chunk.hip", "chunk_scan.hip", "decode.hip", "delta_abi.cpp"]
+SOURCES = ["intra_chunk.hip", "chunk_scan.hip", "scan_summary.hip", "decode.hip", "delta_abi.cpp"]
+# per-file flags: the summary kernel keeps MFMA accumulators in VGPRs (its state is also worked on
+# by vector instructions, and in AGPRs every such step copies it through VGPRs)
+EXTRA = {"scan_summary.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed fp32 VALU ops are disabled for all device code (-packed-fp32-ops); the kernels move
@@ -29,7 +32,7 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-fno-strict-a
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -319,11 +319,87 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       }
     };
     if constexpr (Cfg::NSTAGE == 2) {
-      if (n0 < n1) stage_chunk(n0, 0);
-      barrier_all();  // first chunk staged
+      // Double-buffered stage, with the next chunk prefetched into registers: the copies of
+      // chunk n+2 are loaded while chunk n is processed and written to LDS at the start of
+      // chunk n+1, so neither the gate tables nor A ever wait for HBM.  Loads go through
+      // buffer resources over the chunk's valid rows (rows past the sequence read 0).
+      u32x4 rk[decltype(pk)::NS], rq[SUM ? 1 : decltype(pq)::NS], rt[decltype(pt)::NS], rv[decltype(pv)::NS],
+          rg[decltype(pg)::NS];
+      auto load = [&](int n) {
+        const long P0 = (long)n * C;
+        const int krows = (int)min((long)C, p.Lx - P0);
+        const long tok0 = (long)n * QR;
+        const int qrows = (int)min((long)QR, (long)p.L - tok0);
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<E*>(kg) + ((long)b * p.Lx + P0) * HDK + (long)h * DK,
+                                                      krows * HDK * (int)sizeof(E));
+        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(
+            const_cast<E*>(vg) + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0, krows * HDV * (int)sizeof(E));
+        const __amdgpu_buffer_rsrc_t tr =
+            buffer_rsrc(const_cast<E*>(Tg) + ((long)head * p.NT + n) * C * C, C * C * (int)sizeof(E));
+        const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(p.gc + ((long)head * p.NT + n) * C, C * 4);
+#pragma unroll
+        for (int s = 0; s < decltype(pg)::NS; ++s)
+          if (s < pg.n && pg.off[s] != ~0u) rg[s] = buffer_load16(gr, (int)pg.off[s]);
+#pragma unroll
+        for (int s = 0; s < decltype(pk)::NS; ++s)
+          if (s < pk.n && pk.off[s] != ~0u) rk[s] = buffer_load16(kr, (int)pk.off[s]);
+        if constexpr (!SUM) {
+          const __amdgpu_buffer_rsrc_t qr =
+              buffer_rsrc(const_cast<E*>(qg) + ((long)b * p.L + tok0) * HDK + (long)h * DK, qrows * HDK * (int)sizeof(E));
+#pragma unroll
+          for (int s = 0; s < decltype(pq)::NS; ++s)
+            if (s < pq.n && pq.off[s] != ~0u) rq[s] = buffer_load16(qr, (int)pq.off[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < decltype(pt)::NS; ++s)
+          if (s < pt.n && pt.off[s] != ~0u) rt[s] = buffer_load16(tr, (int)pt.off[s]);
+#pragma unroll
+        for (int s = 0; s < decltype(pv)::NS; ++s)
+          if (s < pv.n && pv.off[s] != ~0u) rv[s] = buffer_load16(vr, (int)pv.off[s]);
+      };
+      // the registers into stage `stage`: each piece where its direct-to-LDS copy would land
+      auto store = [&](int stage) {
+        E* st = smem + stage * Cfg::IN;
+        E* sv = st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS;
+        auto put = [&](E* tile, int s, const u32x4& x) {
+          *reinterpret_cast<u32x4*>(tile + ((dw + SEG_LOADERS * s) * WAVE + lane) * (16 / (int)sizeof(E))) = x;
+        };
+#pragma unroll
+        for (int s = 0; s < decltype(pg)::NS; ++s)
+          if (s < pg.n && pg.off[s] != ~0u)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(sv + Cfg::VS) + ((dw + SEG_LOADERS * s) * WAVE + lane) * 4) = rg[s];
+#pragma unroll
+        for (int s = 0; s < decltype(pk)::NS; ++s)
+          if (s < pk.n && pk.off[s] != ~0u) put(st, s, rk[s]);
+        if constexpr (!SUM) {
+#pragma unroll
+          for (int s = 0; s < decltype(pq)::NS; ++s)
+            if (s < pq.n && pq.off[s] != ~0u) put(st + Cfg::KS, s, rq[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < decltype(pt)::NS; ++s)
+          if (s < pt.n && pt.off[s] != ~0u) put(st + Cfg::KS + Cfg::QS, s, rt[s]);
+#pragma unroll
+        for (int s = 0; s < decltype(pv)::NS; ++s)
+          if (s < pv.n && pv.off[s] != ~0u) put(sv, s, rv[s]);
+      };
+      if (n0 < n1) {
+        load(n0);
+        store(0);
+        exps(0);
+        build_a(0);
+        if (n0 + 1 < n1) load(n0 + 1);
+      }
+      barrier_lds();  // first chunk staged
       for (int n = n0; n < n1; ++n) {
-        if (n + 1 < n1) stage_chunk(n + 1, (n + 1 - n0) & 1);
-        barrier_all();  // chunk n done, chunk n+1 staged
+        if (n + 1 < n1) {
+          const int stage = (n + 1 - n0) & 1;
+          store(stage);  // chunk n+1, loaded during chunk n-1
+          if (n + 2 < n1) load(n + 2);
+          exps(stage);
+          build_a(stage);
+        }
+        barrier_lds();  // chunk n done, chunk n+1 staged (the loads in flight are not waited for)
       }
     } else {
       for (int n = n0; n < n1; ++n) {
@@ -820,6 +896,7 @@ static hipError_t phase_by_dk(const FwdParams& p, int phase, hipStream_t st) {
 }
 
 hipError_t launch_scan_phase(const FwdParams& p, bool bf16_in, int phase, hipStream_t st) {
+  if (phase == SCAN_SUMMARY && scan_summary_fast_applies(p, bf16_in)) return launch_scan_summary_fast(p, st);
   return bf16_in ? phase_by_dk<bf16>(p, phase, st) : phase_by_dk<float>(p, phase, st);
 }
 

@@ -48,6 +48,9 @@ hipError_t launch_wy_factors(const FwdParams& p, bool bf16, hipStream_t st);
 // segment start states, outputs.  The first two do nothing when P == 1.
 enum { SCAN_SUMMARY = 0, SCAN_COMBINE = 1, SCAN_OUTPUTS = 2 };
 hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream_t st);
+// Summary launch for bf16 inputs, d_k = d_v = 128, chunk 64 (scan_summary.hip).
+bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
+hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
 
 }  // namespace delta
