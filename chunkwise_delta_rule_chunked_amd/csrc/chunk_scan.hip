@@ -49,6 +49,8 @@
 // they are loaded from row 0 of the sequence -- without reaching an output (padded rows of V~
 // are 0, so whatever A holds in their columns multiplies zeros, and they add nothing to the
 // state).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -730,92 +732,131 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 }
 
 // Start states of the segments, in order: S_start(1) = S_end(0) and
-// S_start(q+1) = M(q) S_start(q) + S_loc(q).  One workgroup per (head, 16 state columns), one
-// wavefront per 16 state rows; fp32 accumulation.  The contraction index is permuted so that lane
-// group g takes the contiguous run k in [KPL g, KPL g + KPL) (consistently in both operands):
-// each lane's run of M is then 128 contiguous bytes, loaded as vectors two segments ahead of the
-// step that uses it.  BF: products on bf16 MFMA (operands rounded to bf16, as the chunk chain
-// rounds the state every chunk), else fp32 MFMA.
-template <int DK, bool BF>
+// S_start(q+1) = M(q) S_start(q) + S_loc(q).  One workgroup per (head, CTW tiles of 16 state
+// columns), one wavefront per 16 state rows; fp32 accumulation.  The contraction index is permuted (consistently in both operands) so that lane
+// group g takes k = 16 i + 4 g + e (i < KPL / 4, e < 4): load i of the four lane groups of a row
+// then covers 64 contiguous bytes of M, where a contiguous run per lane would make every load
+// touch 64 cache lines and saturate the address unit.  Runs are loaded two segments ahead of the
+// step that uses them, and one A fragment serves all CTW column tiles.
+// BF: products on bf16 MFMA (operands rounded to bf16, as the chunk chain rounds the state every
+// chunk), else fp32 MFMA.
+template <int DK, bool BF, int CTW>
 __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
   constexpr int KPL = DK / 4;  // contraction indices per lane group
   static_assert(!BF || KPL % 8 == 0, "bf16 steps take 8 indices per lane group");
-  __shared__ float Sl[DK][17];
-  const int NCT = p.DV / 16;
-  // workgroups are dealt round-robin over the 8 XCDs: keep the column tiles of one head on one
+  typedef typename std::conditional<BF, bf16, float>::type SE;
+  // the current start state, transposed: state column 16 c + m of the group at row 16 c + m, so
+  // each lane's operand run (8 or 4 consecutive k) is one 16-byte read; rows padded by 16 bytes
+  constexpr int LDT = DK + 16 / (int)sizeof(SE);
+  __shared__ __attribute__((aligned(16))) SE SlT[16 * CTW * LDT];
+  const int NG = p.DV / 16 / CTW;  // column groups per head
+  // workgroups are dealt round-robin over the 8 XCDs: keep the column groups of one head on one
   // XCD so that its transitions are fetched into one L2 once
-  int head, ct;
+  int head, cg;
   if ((p.B * p.H) % 8 == 0) {
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
-    head = x + 8 * (j / NCT);
-    ct = j % NCT;
+    head = x + 8 * (j / NG);
+    cg = j % NG;
   } else {
-    head = blockIdx.x / NCT;
-    ct = blockIdx.x % NCT;
+    head = blockIdx.x / NG;
+    cg = blockIdx.x % NG;
   }
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6, m = lane & 15, g4 = lane >> 4;
   const int W = p.DV + DK;
+  const int col0 = 16 * CTW * cg;  // first state column of the group
   const float* SMh = p.SM + (long)head * p.P * DK * W;
   float* Sst = p.Sst + (long)head * p.P * DK * p.DV;
-  // this lane's A run of segment q: M(q)[16t + m][KPL g4 .. KPL g4 + KPL), and its S_loc values
+  // this lane's A run of segment q: M(q)[16t + m][16 i + 4 g4 + e], and its S_loc values
+  // (rows 16 t + 4 g4 + j of column col0 + 16 c + m)
   struct Run {
     floatx4 a[KPL / 4];
-    floatx4 sl;
+    floatx4 sl[CTW];
   };
   auto load = [&](int q, Run& r) {
     const float* SMq = SMh + (long)q * DK * W;
-    const floatx4* src = reinterpret_cast<const floatx4*>(SMq + (long)(16 * t + m) * W + p.DV + KPL * g4);
+    const floatx4* src = reinterpret_cast<const floatx4*>(SMq + (long)(16 * t + m) * W + p.DV + 4 * g4);
 #pragma unroll
-    for (int i = 0; i < KPL / 4; ++i) r.a[i] = src[i];
+    for (int i = 0; i < KPL / 4; ++i) r.a[i] = src[4 * i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.sl[j] = SMq[(long)(16 * t + 4 * g4 + j) * W + 16 * ct + m];
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.sl[c][j] = SMq[(long)(16 * t + 4 * g4 + j) * W + col0 + 16 * c + m];
   };
-  // one step: S_start(q+1) from the run of segment q, while the run of segment q+2 loads
+  auto put = [&](int c, floatx4 x) {
+    SE* d = SlT + (16 * c + m) * LDT + 16 * t + 4 * g4;
+    if constexpr (BF) *reinterpret_cast<bf16x4*>(d) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    else *reinterpret_cast<floatx4*>(d) = x;
+  };
+  // one step: S_start(q+1) from the run of segment q, while the run of segment q+2 loads.  The
+  // load is unconditional (past the last segment it repeats it): with a conditional one the
+  // compiler's wait before the products has to assume the load was skipped, and then waits for
+  // the loads just issued as well.
   auto step = [&](int q, const Run& cur, Run& next) {
-    if (q + 3 < p.P) load(q + 2, next);
-    floatx4 acc[4] = {cur.sl, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    load(min(q + 2, p.P - 2), next);
+    floatx4 acc[CTW][2];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+      acc[c][0] = cur.sl[c];
+      acc[c][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     if constexpr (BF) {
-      // 16x16x32: k slot 8 g + j of step s is k = KPL g + 8 s + j in both operands
+      // 16x16x32: k slot 8 g + 4 h + e of step s is k = 16 (2 s + h) + 4 g + e in both operands
 #pragma unroll
       for (int s = 0; s < KPL / 8; ++s) {
         const floatx4 x0 = cur.a[2 * s], x1 = cur.a[2 * s + 1];
         const bf16x8 av = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
                            (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
-        bf16x8 bv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = (bf16)Sl[KPL * g4 + 8 * s + j][m];
-        acc[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[s & 1], 0, 0, 0);
+        for (int c = 0; c < CTW; ++c) {
+          const SE* row = SlT + (16 * c + m) * LDT + 32 * s + 4 * g4;
+          const bf16x8 bv = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(row),
+                                                    *reinterpret_cast<const bf16x4*>(row + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[c][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[c][s & 1], 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KPL; ++s)
-        acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.a[s / 4][s % 4], Sl[KPL * g4 + s][m], acc[s & 3], 0, 0, 0);
+      for (int s4 = 0; s4 < KPL / 4; ++s4)
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+          const floatx4 y = *reinterpret_cast<const floatx4*>(SlT + (16 * c + m) * LDT + 16 * s4 + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[c][i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.a[s4][i], y[i], acc[c][i & 1], 0, 0, 0);
+        }
     }
-    const floatx4 st = acc[0] + acc[1] + acc[2] + acc[3];
     // waves exchange the state only through LDS: a barrier that waits for LDS alone, so the
     // loads in flight are not drained
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * t + 4 * g4 + j;
-      Sl[row][m] = st[j];
-      Sst[((long)(q + 1) * DK + row) * p.DV + 16 * ct + m] = st[j];
+    for (int c = 0; c < CTW; ++c) {
+      const floatx4 st = acc[c][0] + acc[c][1];
+      put(c, st);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Sst[((long)(q + 1) * DK + 16 * t + 4 * g4 + j) * p.DV + col0 + 16 * c + m] = st[j];
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
   };
+  // S_start(1) = S_end(0), loaded before the runs so waiting for it does not wait for them
+  floatx4 x[CTW];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[c][j] = SMh[(long)(16 * t + 4 * g4 + j) * W + col0 + 16 * c + m];
   // three register sets in fixed roles (a loop with copies between them would wait for each
   // load one step after issuing it): two segments of lead
   Run r0, r1, r2;
-  if (p.P > 2) load(1, r0);
-  if (p.P > 3) load(2, r1);
+  if (p.P > 2) {
+    load(1, r0);
+    load(min(2, p.P - 2), r1);
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * t + 4 * g4 + j;
-    const float x = SMh[(long)row * W + 16 * ct + m];
-    Sl[row][m] = x;
-    Sst[((long)1 * DK + row) * p.DV + 16 * ct + m] = x;
+  for (int c = 0; c < CTW; ++c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Sst[((long)1 * DK + 16 * t + 4 * g4 + j) * p.DV + col0 + 16 * c + m] = x[c][j];
+    put(c, x[c]);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");
@@ -862,7 +903,8 @@ static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
       return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st) : hipSuccess;
     case SCAN_COMBINE:
       if (p.P <= 1 || p.B * p.H == 0) return hipSuccess;
-      hipLaunchKernelGGL((combine_kernel<DK, sizeof(E) == 2 && DK >= 32>), dim3((unsigned)(p.B * p.H * (p.DV / 16))),
+      // one column tile per workgroup (several per workgroup measured slower)
+      hipLaunchKernelGGL((combine_kernel<DK, sizeof(E) == 2 && DK >= 32, 1>), dim3((unsigned)(p.B * p.H * (p.DV / 16))),
                          dim3(DK / 16 * WAVE), 0, st, p);
       return hipGetLastError();
     case SCAN_OUTPUTS:
