@@ -62,25 +62,9 @@ __device__ inline floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The prefetch loads and the LDS writes of the loaded pieces are inline assembly: the compiler
-// would otherwise wait for every outstanding load before the first use of any of them, that is,
-// for the next chunk's loads too.  Their completion is awaited explicitly: loads return in issue
-// order, so at most N outstanding vector memory operations, N being the number of loads issued
-// after the needed ones, means those have landed (stores in flight only make the wait longer).
-__device__ inline u32x4 make_desc(const void* base, unsigned bytes) {
-  const unsigned long a = reinterpret_cast<unsigned long>(base);
-  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-__device__ inline void load16(u32x4& dst, u32x4 desc, int off) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(desc));
-}
-__device__ inline void load4(unsigned& dst, u32x4 desc, int off) {
-  asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(desc));
-}
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+// The LDS writes of the prefetched pieces are inline assembly too (see asm_load16 in
+// common.h): the compiler would otherwise wait for every outstanding load before the first of
+// them, that is, for the next chunk's loads as well.
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)reinterpret_cast<unsigned long>((const __attribute__((address_space(3))) void*)p);
 }
@@ -144,12 +128,12 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     const u32x4 vd = make_desc(vg + ((long)b * p.Lx + P0) * HDV, krows * HDV * 2);
     const u32x4 td = make_desc(Tg + (long)n * C * C, C * C * 2);
 #pragma unroll
-    for (int i = 0; i < NKP; ++i) load16(R.k[i], kd, offG_k[i]);
+    for (int i = 0; i < NKP; ++i) asm_load16(R.k[i], kd, offG_k[i]);
 #pragma unroll
-    for (int i = 0; i < NTP; ++i) load16(R.t[i], td, ((NTP * wave + i) * WAVE + lane) * 16);
+    for (int i = 0; i < NTP; ++i) asm_load16(R.t[i], td, ((NTP * wave + i) * WAVE + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < NKP; ++i) load16(R.v[i], vd, offG_v[i]);
-    load4(R.gc, make_desc(gcg + (long)n * C, C * 4), lane * 4);
+    for (int i = 0; i < NKP; ++i) asm_load16(R.v[i], vd, offG_v[i]);
+    asm_load4(R.gc, make_desc(gcg + (long)n * C, C * 4), lane * 4);
   };
 
   // registers -> LDS stage; wavefront 0 also writes the gate tables
