@@ -139,7 +139,7 @@ def outputs_flops(w) -> int:
 
 KERNELS = {  # phase -> (kernel symbol substring, bytes, flops)
     "intra": ("intra_chunk_kernel", intra_bytes, intra_flops),
-    "summary": ("seg_kernel", summary_bytes, summary_flops),
+    "summary": ("summary_kernel", summary_bytes, summary_flops),
     "combine": ("combine_kernel", combine_bytes, combine_flops),
     "outputs": ("seg_kernel", outputs_bytes, outputs_flops),
 }
