@@ -50,11 +50,19 @@ struct Mfma<float> {
   __device__ static inline floatx4 mma_tail(const float* a, const float* b, floatx4 c) { return mma(*a, *b, c); }
 };
 
-// XOR key of row r for a swizzle mask.  With 16 chunks per row (mask 15) the two 2-bit fields of
-// r & 15 are swapped: still a bijection on 16 consecutive rows, and it also spreads 4 consecutive
-// rows read at 4 different chunks each (transpose reads of column runs) over 16 chunks.
+// XOR key of row r for a swizzle mask: the 16-byte chunks of row r are permuted by chunk ^ key.
+// With 16 chunks per row (256-byte rows, mask 15) the key is the linear map over GF(2) that
+// takes row bits 0, 1, 2, 3 to 0x2, 0x6, 0xd, 0xe.  It was chosen by timing all 20160 invertible
+// 4-bit linear keys on gfx950 for the three reads of such tiles in the chain kernels: 16-byte
+// fragment reads of 16 rows at one logical chunk (238 B/cycle/CU, conflict-free), and transpose
+// reads of column runs of the key tile (122, the ds_read_b64_tr_b16 rate) and of the value tile
+// (189); swapping the two 2-bit fields of the row, the previous key, gave 124 / 121 / 121.  With 8
+// chunks per row (128-byte rows, mask 7) two consecutive rows share one 256-byte bank sweep, so
+// the key is (r / 2) % 8: 16 rows read at one chunk fall on 16 distinct bank groups.
 __host__ __device__ constexpr int swz_key(int r, int mask) {
-  return mask == 15 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (r & mask);
+  return mask == 15 ? (((r & 1) ? 0x2 : 0) ^ ((r & 2) ? 0x6 : 0) ^ ((r & 4) ? 0xd : 0) ^ ((r & 8) ? 0xe : 0))
+       : mask == 7 ? ((r >> 1) & 7)
+                   : (r & mask);
 }
 
 // A matrix tile in LDS.  Element (r, e) lives at p + r * ld + swizzled column, where the

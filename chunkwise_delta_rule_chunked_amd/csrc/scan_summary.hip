@@ -115,7 +115,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
   for (int i = 0; i < NTP; ++i) {
     const int q = (NTP * wave + i) * WAVE + lane, r = q >> 3, c = q & 7;
-    offL_t[i] = (T_OFF + r * C + ((c ^ (r & 7)) << 3)) * 2;
+    offL_t[i] = (T_OFF + r * C + ((c ^ swz_key(r, 7)) << 3)) * 2;
   }
 
   // loads of chunk n (clamped to the segment's last chunk: past the end they repeat it) into
