@@ -298,3 +298,67 @@ def test_decode_steps(dt, n_h, dk, dv, gate):
     eo, es = head_rel_err(O, Or, (0, 2)), head_rel_err(S, Sr, (0, 1))
     say("  err O %.3e S %.3e" % (eo, es))
     assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+# ---------------------------------------------------------------- HIP graph capture
+
+def test_decode_graph_replay():
+    """Decode steps captured in a HIP graph: every replay (with eager work and synchronisation
+    between replays) matches the same steps run eagerly."""
+    w = W.Workload("dec_graph", B=4, H=2, L=1, dk=128, dv=128, dtype="bf16", gate="cfg3", s0=0.1, cfg_id=93)
+    steps = [inputs_to_dev(dict(W.make_decode_inputs(w, t), S0=None), w.dtype) for t in range(3)]
+    S0 = torch.from_numpy(W.make_decode_state(w)).cuda()
+    Sg, Se = S0.clone(), S0.clone()
+    Og = torch.empty((w.B, 1, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    Oe = torch.empty_like(Og)
+
+    def run(S, O):
+        for d in steps:
+            D.decode(d["q"], d["k"], d["v"], d["beta"], d["g_log"], S, O=O)
+
+    # warm the library up outside the capture, on a scratch state
+    run(S0.clone(), torch.empty_like(Og))
+    torch.cuda.synchronize()
+    Sg.copy_(S0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(Sg, Og)
+    Sg.copy_(S0)  # capture does not execute; start the replays from S0
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        run(Se, Oe)
+        torch.cuda.synchronize()
+        es = (Sg - Se).abs().max().item()
+        eo = (Og.float() - Oe.float()).abs().max().item()
+        say("  replay %d: |S - S_eager| %.3e, |O - O_eager| %.3e" % (rep, es, eo))
+        assert es == 0.0 and eo == 0.0, (rep, es, eo)
+
+
+def test_fwd_graph_replay():
+    """A whole forward pass (intra-chunk, summary, combine and output launches) captured in a HIP
+    graph: every replay matches the eager call exactly."""
+    w = wl("fwd_graph", B=1, H=2, L=1000, dk=128, dv=128, chunk=64, gate="cfg3", s0=0.1, cfg_id=94)
+    d = inputs_to_dev(W.make_inputs(w), w.dtype)
+    code = D.BF16
+    ws = torch.empty(D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk, code), dtype=torch.uint8, device="cuda")
+    Og = torch.empty((w.B, w.L, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    Sg = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    call = lambda O, S: D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], n_h=w.n_h, chunk=w.chunk,
+                              O=O, S_final=S, workspace=ws)
+    Oe, Se = D.fwd(d["q"], d["k"], d["v"], d["beta"], d["g_log"], d["S0"], n_h=w.n_h, chunk=w.chunk)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(Og, Sg)
+    for rep in range(3):
+        Og.zero_()
+        Sg.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eo = (Og.float() - Oe.float()).abs().max().item()
+        es = (Sg - Se).abs().max().item()
+        say("  replay %d: |O - O_eager| %.3e, |S - S_eager| %.3e" % (rep, eo, es))
+        assert eo == 0.0 and es == 0.0, (rep, eo, es)
