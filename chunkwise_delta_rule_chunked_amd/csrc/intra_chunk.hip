@@ -32,7 +32,7 @@ struct IntraLds {
   static constexpr int BLK = 16 * LDB;                // floats per block
   static constexpr int NBLK = NB * (NB + 1) / 2;
   static constexpr int KBYTES = C * LDK * (int)sizeof(E);
-  static constexpr int ANBYTES = (2 * NBLK + 4) * BLK * 4;  // A, N, one 16x16 tile per wave
+  static constexpr int ANBYTES = 2 * NBLK * BLK * 4;  // A and N
   static constexpr int BYTES = KBYTES > ANBYTES ? KBYTES : ANBYTES;
 };
 __host__ __device__ constexpr int lower_block(int i, int j) { return i * (i + 1) / 2 + j; }
@@ -47,7 +47,6 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   const Tile<E> Kt = make_tile<E, DK>(reinterpret_cast<E*>(smem));
   float* As = reinterpret_cast<float*>(smem);   // after the key tile is dead
   float* Ns = As + NBLK * BLK;
-  float* Ps = Ns + NBLK * BLK;                  // 4 x [16][LDB] per-wave product tiles
   auto blk = [](float* base, int i, int j) { return base + lower_block(i, j) * BLK; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -171,8 +170,11 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   __syncthreads();
 
   // tiles below the diagonal, one block diagonal d at a time:
-  //   P = sum_{k=j}^{i-1} A_ik N_kj  (then through LDS),  N_ij = -N_ii P
-  float* Pw = Ps + wave * BLK;
+  //   P = sum_{k=j}^{i-1} A_ik N_kj,  N_ij = -N_ii P
+  // P stays in the accumulator registers: lane (g, n) holds P[4g + r][n], r < 4, which is the B
+  // operand of step r of the second product when its contraction index is taken as 4g + r (the
+  // A operand N_ii[m][4g + r] is read to match).  P being the wave's own, one barrier per block
+  // diagonal orders the N tiles between the waves.
   for (int d = 1; d < NB; ++d) {
     const int i = wave + d, j = wave;   // wave w owns tile (w + d, w)
     if (i < NB) {
@@ -185,19 +187,12 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
           acc = Mfma<float>::mma(blk(As, i, k)[col * LDB + kk], blk(Ns, k, j)[kk * LDB + col], acc);
         }
       }
+      floatx4 nij = {0.f, 0.f, 0.f, 0.f};
+      const float* Nii = blk(Ns, i, i) + col * LDB + rq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Pw[(rq + r) * LDB + col] = acc[r];
-    }
-    __syncthreads();
-    if (i < NB) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) nij = Mfma<float>::mma(Nii[r], acc[r], nij);
 #pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4) {
-        const int kk = k0 + (lane >> 4);
-        acc = Mfma<float>::mma(blk(Ns, i, i)[col * LDB + kk], Pw[kk * LDB + col], acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) blk(Ns, i, j)[(rq + r) * LDB + col] = -acc[r];
+      for (int r = 0; r < 4; ++r) blk(Ns, i, j)[(rq + r) * LDB + col] = -nij[r];
     }
     __syncthreads();
   }
