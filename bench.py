@@ -89,7 +89,8 @@ def summary_bytes(w) -> int:
     pos = min(w.Lx, nch * w.chunk)
     b = w.B * pos * w.H * (w.dk + w.dv) * es + w.B * w.H * nch * w.chunk * (w.chunk * es + 4)
     b += w.B * w.H * w.dk * w.dv * 4 if w.s0 is not None else 0
-    b += w.B * w.H * (P - 1) * w.dk * (w.dv + w.dk) * 4
+    # S_loc (fp32) of segments 0..P-2, M (element type) of segments 1..P-2
+    b += w.B * w.H * ((P - 1) * w.dk * w.dv * 4 + (P - 2) * w.dk * w.dk * es)
     return b
 
 
@@ -104,10 +105,11 @@ def summary_flops(w) -> int:
 
 
 def combine_bytes(w) -> int:
+    """Reads S_loc of segments 0..P-2 and M of 1..P-2; writes the start states of 1..P-1."""
     P, _ = _segments(w)
     if P <= 1:
         return 0
-    return w.B * w.H * ((P - 1) * w.dk * (w.dv + w.dk) * 4 + (P - 1) * w.dk * w.dv * 4)
+    return w.B * w.H * ((P - 1) * w.dk * w.dv * 4 + (P - 2) * w.dk * w.dk * _es(w) + (P - 1) * w.dk * w.dv * 4)
 
 
 def combine_flops(w) -> int:

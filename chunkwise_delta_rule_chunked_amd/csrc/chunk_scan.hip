@@ -159,7 +159,6 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
   using D = DOp<E>;
   constexpr int NB = C / 16;     // position blocks per chunk
   constexpr int NTS = DK / 16;   // state row tiles
-  constexpr int VEC = 16 / sizeof(E);
   constexpr int TPG = Cfg::TPG;
 
   __shared__ __attribute__((aligned(16))) E smem[Cfg::ELEMS];
@@ -711,7 +710,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     barrier_lds();  // chunk done (and, with one stage, the stage may be reloaded)
   }
 
-  // ---------------- segment results
+  // ---------------- segment results (a summary: S_loc, and M as E, in the combine's order)
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     if (!live[c]) continue;
@@ -721,9 +720,9 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       for (int j = 0; j < 4; ++j) {
         const int row = dkrow(t, 4 * g4 + j);
         if constexpr (SUM) {
-          const int W = p.DV + DK;
-          const int col = isv[c] ? 16 * tile[c] + m : p.DV + 16 * (tile[c] - NCT) + m;
-          p.SM[(((long)head * p.P + seg) * DK + row) * W + col] = S[c][t][j];
+          float* SMs = p.SM + ((long)head * p.P + seg) * DK * (p.DV + DK);
+          if (isv[c]) SMs[sloc_index(row, 16 * tile[c] + m, DK)] = S[c][t][j];
+          else reinterpret_cast<E*>(SMs + (long)p.DV * DK)[mfrag_index<mfrag_width<E, DK>()>(row, 16 * (tile[c] - NCT) + m, DK)] = to_elem<E>(S[c][t][j]);
         } else if (seg == p.P - 1 && p.S_final) {
           p.S_final[((long)head * DK + row) * p.DV + 16 * tile[c] + m] = S[c][t][j];
         }
@@ -733,23 +732,36 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 
 // Start states of the segments, in order: S_start(1) = S_end(0) and
 // S_start(q+1) = M(q) S_start(q) + S_loc(q).  One workgroup per (head, CTW tiles of 16 state
-// columns), one wavefront per 16 state rows; fp32 accumulation.  The contraction index is permuted (consistently in both operands) so that lane
-// group g takes k = 16 i + 4 g + e (i < KPL / 4, e < 4): load i of the four lane groups of a row
-// then covers 64 contiguous bytes of M, where a contiguous run per lane would make every load
-// touch 64 cache lines and saturate the address unit.  Runs are loaded two segments ahead of the
-// step that uses them, and one A fragment serves all CTW column tiles.
-// BF: products on bf16 MFMA (operands rounded to bf16, as the chunk chain rounds the state every
-// chunk), else fp32 MFMA.
-template <int DK, bool BF, int CTW>
+// columns), one wavefront per 16 state rows; fp32 accumulation.  The chain is short and each
+// step is a few MFMAs: the time goes into fetching the summaries, M(q) once per workgroup (so
+// several column tiles share each A fragment) and S_loc(q) for the workgroup's columns.  The
+// loads of up to DEPTH segments are issued together into DEPTH register sets; the current start
+// state is exchanged between the wavefronts through two LDS buffers, one barrier per step.
+// BF: bf16 products (M is stored in bf16; the state is rounded to bf16 as the chunk chain
+// rounds it every chunk) on the 32-deep MFMA, k in natural order: the lane's A fragment is 16
+// contiguous bytes of its row of M.  Otherwise fp32 products on the 4-deep MFMA with the
+// contraction index permuted (consistently in both operands): lane group g takes
+// k = 16 i + 4 g + e, so one load of the four lane groups of a row covers 16 contiguous elements.
+template <typename E, int DK, bool BF, int CTW>
+struct CombineCfg {
+  static constexpr int NA = BF ? DK / 32 : DK / 16;  // A pieces per lane and segment
+  static constexpr int RUNREGS = NA * (BF ? 4 : (int)sizeof(E)) + 4 * CTW;
+  static constexpr int DEPTH = 192 / RUNREGS < 8 ? 192 / RUNREGS : 8;
+};
+
+template <typename E, int DK, bool BF, int CTW>
 __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
-  constexpr int KPL = DK / 4;  // contraction indices per lane group
-  static_assert(!BF || KPL % 8 == 0, "bf16 steps take 8 indices per lane group");
+  using Cfg = CombineCfg<E, DK, BF, CTW>;
+  constexpr int NA = Cfg::NA, DEPTH = Cfg::DEPTH;
+  static_assert(!BF || (sizeof(E) == 2 && DK % 32 == 0), "bf16 products take bf16 M, 32 indices a step");
   typedef typename std::conditional<BF, bf16, float>::type SE;
-  // the current start state, transposed: state column 16 c + m of the group at row 16 c + m, so
-  // each lane's operand run (8 or 4 consecutive k) is one 16-byte read; rows padded by 16 bytes
+  // A piece as loaded: 8 bf16 (BF), 4 E otherwise
+  typedef typename std::conditional<BF, bf16x8, typename std::conditional<sizeof(E) == 2, bf16x4, floatx4>::type>::type Piece;
+  // the current start state, transposed: column 16 c + m at row 16 c + m, padded by 16 bytes;
+  // two buffers
   constexpr int LDT = DK + 16 / (int)sizeof(SE);
-  __shared__ __attribute__((aligned(16))) SE SlT[16 * CTW * LDT];
-  const int NG = p.DV / 16 / CTW;  // column groups per head
+  __shared__ __attribute__((aligned(16))) SE SlT[2][16 * CTW * LDT];
+  const int NG = p.DV / (16 * CTW);  // column groups per head
   // workgroups are dealt round-robin over the 8 XCDs: keep the column groups of one head on one
   // XCD so that its transitions are fetched into one L2 once
   int head, cg;
@@ -762,110 +774,96 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
     cg = blockIdx.x % NG;
   }
   const int lane = threadIdx.x & 63, t = threadIdx.x >> 6, m = lane & 15, g4 = lane >> 4;
-  const int W = p.DV + DK;
-  const int col0 = 16 * CTW * cg;  // first state column of the group
-  const float* SMh = p.SM + (long)head * p.P * DK * W;
+  const int col0 = 16 * CTW * cg + m;        // the lane's column of tile 0 (tile c: + 16 c)
+  const long SLOT = (long)DK * (p.DV + DK);  // floats per segment summary
+  const float* SMh = p.SM + (long)head * p.P * SLOT;
   float* Sst = p.Sst + (long)head * p.P * DK * p.DV;
-  // this lane's A run of segment q: M(q)[16t + m][16 i + 4 g4 + e], and its S_loc values
-  // (rows 16 t + 4 g4 + j of column col0 + 16 c + m)
+  // Loads go through a buffer resource per segment summary, so a lane keeps two offsets: its
+  // S_loc values (rows 16 t + 4 g4 .. + 3 of its column of tile 0) and its first A piece (row
+  // 16 t + m of M); both layouts put a wavefront's 64 pieces of one load side by side.
+  constexpr int PW = mfrag_width<E, DK>();
+  static_assert(PW == (BF ? 8 : 4), "M piece width");
+  const int offS = sloc_index(16 * t + 4 * g4, col0, DK) * 4;
+  const int offM = p.DV * DK * 4 + mfrag_index<PW>(16 * t + m, PW * g4, DK) * (int)sizeof(E);
+  constexpr int STEPM = 64 * PW * (int)sizeof(E);  // bytes between a lane's A pieces
+  constexpr int STEPS = DK / 16 * 64 * 16;         // bytes between a lane's S_loc column tiles
+  auto rsrc = [&](int q) { return buffer_rsrc(const_cast<float*>(SMh) + q * SLOT, (int)SLOT * 4); };
   struct Run {
-    floatx4 a[KPL / 4];
+    Piece a[NA];
     floatx4 sl[CTW];
   };
   auto load = [&](int q, Run& r) {
-    const float* SMq = SMh + (long)q * DK * W;
-    const floatx4* src = reinterpret_cast<const floatx4*>(SMq + (long)(16 * t + m) * W + p.DV + 4 * g4);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(q);
 #pragma unroll
-    for (int i = 0; i < KPL / 4; ++i) r.a[i] = src[4 * i];
+    for (int i = 0; i < NA; ++i) {
+      if constexpr (sizeof(Piece) == 16) r.a[i] = __builtin_bit_cast(Piece, buffer_load16(rs, offM + STEPM * i));
+      else r.a[i] = __builtin_bit_cast(Piece, buffer_load8(rs, offM + STEPM * i));
+    }
 #pragma unroll
-    for (int c = 0; c < CTW; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r.sl[c][j] = SMq[(long)(16 * t + 4 * g4 + j) * W + col0 + 16 * c + m];
+    for (int c = 0; c < CTW; ++c) r.sl[c] = __builtin_bit_cast(floatx4, buffer_load16(rs, offS + STEPS * c));
   };
-  auto put = [&](int c, floatx4 x) {
-    SE* d = SlT + (16 * c + m) * LDT + 16 * t + 4 * g4;
+  // the new start state of q1, tile c: into LDS buffer q1 & 1 and to the start-state output
+  auto put = [&](int q1, int c, floatx4 x) {
+    SE* d = SlT[q1 & 1] + (16 * c + m) * LDT + 16 * t + 4 * g4;
     if constexpr (BF) *reinterpret_cast<bf16x4*>(d) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
     else *reinterpret_cast<floatx4*>(d) = x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Sst[((long)q1 * DK + 16 * t + 4 * g4 + j) * p.DV + col0 + 16 * c] = x[j];
   };
-  // one step: S_start(q+1) from the run of segment q, while the run of segment q+2 loads.  The
-  // load is unconditional (past the last segment it repeats it): with a conditional one the
-  // compiler's wait before the products has to assume the load was skipped, and then waits for
-  // the loads just issued as well.
-  auto step = [&](int q, const Run& cur, Run& next) {
-    load(min(q + 2, p.P - 2), next);
-    floatx4 acc[CTW][2];
+  // waves exchange the state only through LDS: a barrier that waits for LDS alone, so the loads
+  // in flight are not drained
+  auto lds_barrier = [] {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // S_start(q+1) from the run of segment q and S_start(q) in buffer q & 1
+  auto step = [&](int q, const Run& r) {
+    floatx4 acc0[CTW], acc1[CTW];
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
-      acc[c][0] = cur.sl[c];
-      acc[c][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc0[c] = r.sl[c];
+      acc1[c] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    if constexpr (BF) {
-      // 16x16x32: k slot 8 g + 4 h + e of step s is k = 16 (2 s + h) + 4 g + e in both operands
 #pragma unroll
-      for (int s = 0; s < KPL / 8; ++s) {
-        const floatx4 x0 = cur.a[2 * s], x1 = cur.a[2 * s + 1];
-        const bf16x8 av = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
-                           (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
+    for (int i = 0; i < NA; ++i) {
 #pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-          const SE* row = SlT + (16 * c + m) * LDT + 32 * s + 4 * g4;
-          const bf16x8 bv = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(row),
-                                                    *reinterpret_cast<const bf16x4*>(row + 16), 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[c][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[c][s & 1], 0, 0, 0);
+      for (int c = 0; c < CTW; ++c) {
+        const SE* y = SlT[q & 1] + (16 * c + m) * LDT;
+        floatx4& acc = (i & 1) ? acc1[c] : acc0[c];
+        if constexpr (BF) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(y + 32 * i + 8 * g4);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[i], b, acc, 0, 0, 0);
+        } else {
+          const floatx4 b = *reinterpret_cast<const floatx4*>(y + 16 * i + 4 * g4);
+          floatx4 a;
+          if constexpr (sizeof(E) == 2) a = floatx4{(float)r.a[i][0], (float)r.a[i][1], (float)r.a[i][2], (float)r.a[i][3]};
+          else a = r.a[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
         }
       }
-    } else {
-#pragma unroll
-      for (int s4 = 0; s4 < KPL / 4; ++s4)
-#pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-          const floatx4 y = *reinterpret_cast<const floatx4*>(SlT + (16 * c + m) * LDT + 16 * s4 + 4 * g4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[c][i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.a[s4][i], y[i], acc[c][i & 1], 0, 0, 0);
-        }
     }
-    // waves exchange the state only through LDS: a barrier that waits for LDS alone, so the
-    // loads in flight are not drained
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) {
-      const floatx4 st = acc[c][0] + acc[c][1];
-      put(c, st);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Sst[((long)(q + 1) * DK + 16 * t + 4 * g4 + j) * p.DV + col0 + 16 * c + m] = st[j];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    asm volatile("s_barrier" ::: "memory");
+    for (int c = 0; c < CTW; ++c) put(q + 1, c, acc0[c] + acc1[c]);
+    lds_barrier();
   };
-  // S_start(1) = S_end(0), loaded before the runs so waiting for it does not wait for them
-  floatx4 x[CTW];
+  // S_start(1) = S_end(0)
+  {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(0);
 #pragma unroll
-  for (int c = 0; c < CTW; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[c][j] = SMh[(long)(16 * t + 4 * g4 + j) * W + col0 + 16 * c + m];
-  // three register sets in fixed roles (a loop with copies between them would wait for each
-  // load one step after issuing it): two segments of lead
-  Run r0, r1, r2;
-  if (p.P > 2) {
-    load(1, r0);
-    load(min(2, p.P - 2), r1);
+    for (int c = 0; c < CTW; ++c) put(1, c, __builtin_bit_cast(floatx4, buffer_load16(rs, offS + STEPS * c)));
   }
+  lds_barrier();
+  // rounds of DEPTH segments: all of a round's loads are issued together, then its steps run
+  const int last = p.P - 2;  // last segment with a transition
+  for (int q0 = 1; q0 <= last; q0 += DEPTH) {
+    Run r[DEPTH];
 #pragma unroll
-  for (int c = 0; c < CTW; ++c) {
+    for (int d = 0; d < DEPTH; ++d)
+      if (q0 + d <= last) load(q0 + d, r[d]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Sst[((long)1 * DK + 16 * t + 4 * g4 + j) * p.DV + col0 + 16 * c + m] = x[c][j];
-    put(c, x[c]);
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("s_barrier" ::: "memory");
-  for (int q = 1; q + 1 < p.P; q += 3) {
-    step(q, r0, r2);
-    if (q + 2 >= p.P) break;
-    step(q + 1, r1, r0);
-    if (q + 3 >= p.P) break;
-    step(q + 2, r2, r1);
+    for (int d = 0; d < DEPTH; ++d)
+      if (q0 + d <= last) step(q0 + d, r[d]);
   }
 }
 
@@ -903,10 +901,14 @@ static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
       return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st) : hipSuccess;
     case SCAN_COMBINE:
       if (p.P <= 1 || p.B * p.H == 0) return hipSuccess;
-      // one column tile per workgroup (several per workgroup measured slower)
-      hipLaunchKernelGGL((combine_kernel<DK, sizeof(E) == 2 && DK >= 32, 1>), dim3((unsigned)(p.B * p.H * (p.DV / 16))),
-                         dim3(DK / 16 * WAVE), 0, st, p);
+    {
+      // one column tile per workgroup: the workgroup's loads are what takes the time, and with
+      // 2 or 4 tiles (M fetched once for more columns) the launch measured 9.8 / 13.5 us against
+      // 8.2 us on the 8K-token workload
+      constexpr bool BF = sizeof(E) == 2 && DK >= 32;
+      hipLaunchKernelGGL((combine_kernel<E, DK, BF, 1>), dim3((unsigned)(p.B * p.H * (p.DV / 16))), dim3(DK / 16 * WAVE), 0, st, p);
       return hipGetLastError();
+    }
     case SCAN_OUTPUTS:
       return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, false>(p, st)
                                   : launch_seg<E, DK, C, 2, 4, false>(p, st);

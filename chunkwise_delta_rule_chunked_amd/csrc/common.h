@@ -50,6 +50,27 @@ struct Mfma<float> {
   __device__ static inline floatx4 mma_tail(const float* a, const float* b, floatx4 c) { return mma(*a, *b, c); }
 };
 
+// Layout of a segment summary (S_loc, M) in the order the start-state combine reads it: every
+// wavefront load there is 64 lanes x one contiguous 16-byte piece (or 8 bytes), so a load covers
+// whole cache lines.  Lane (g, m) of the wavefront for rows 16 t .. 16 t + 15 takes:
+//   S_loc, column tile ct: rows 16 t + 4 g .. + 3 of column 16 ct + m (fp32), at
+//     sloc_index(r, c) = ((c / 16 * (DK / 16) + r / 16) * 64 + (r % 16) / 4 * 16 + c % 16) * 4 + r % 4;
+//   M, contraction block i: its A fragment, row 16 t + m, k = i KB + g PW .. + PW - 1, at
+//     mfrag_index(r, k) = ((r / 16 * (DK / KB) + k / KB) * 64 + (k % KB) / PW * 16 + r % 16) * PW + k % PW
+//   with PW = 8 elements (bf16 products on the 32-deep MFMA, KB = 32) or 4 (KB = 16).
+__host__ __device__ constexpr int sloc_index(int r, int c, int DK) {
+  return ((c / 16 * (DK / 16) + r / 16) * 64 + (r % 16) / 4 * 16 + c % 16) * 4 + r % 4;
+}
+template <int PW>
+__host__ __device__ constexpr int mfrag_index(int r, int k, int DK) {
+  return ((r / 16 * (DK / (4 * PW)) + k / (4 * PW)) * 64 + (k % (4 * PW)) / PW * 16 + r % 16) * PW + k % PW;
+}
+// piece width of M for element type E and key width DK (bf16 products need DK >= 32)
+template <typename E, int DK>
+__host__ __device__ constexpr int mfrag_width() {
+  return sizeof(E) == 2 && DK >= 32 ? 8 : 4;
+}
+
 // XOR key of row r for a swizzle mask: the 16-byte chunks of row r are permuted by chunk ^ key.
 // With 16 chunks per row (256-byte rows, mask 15) the key is the linear map over GF(2) that
 // takes row bits 0, 1, 2, 3 to 0x2, 0x6, 0xd, 0xe.  It was chosen by timing all 20160 invertible
@@ -283,6 +304,9 @@ __device__ inline void buffer_store8(__amdgpu_buffer_rsrc_t r, int off, bf16x4 x
 }
 __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {  // 0 outside the range
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {   // 0 outside the range
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 __device__ inline float buffer_load4(__amdgpu_buffer_rsrc_t r, int off) {   // 0 outside the range
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));

@@ -24,7 +24,10 @@ struct FwdParams {
   float* U;             // chunk_wy only: [B, H, NT, C, DV]
   // sequence split of the inter-chunk pass: P segments of NS chunks (P = 1: no split)
   int P, NS;
-  float* SM;            // [B*H, P, DK, DV + DK]: per segment S_loc (value columns) and M
+  // [B*H, P] segment summaries, each in a slot of DK * (DV + DK) floats: S_loc as float at
+  // sloc_index, then, from float offset DV * DK, M in the element type of the inputs at
+  // mfrag_index (common.h)
+  float* SM;
   float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
 };
 

@@ -291,16 +291,23 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   lds_barrier();
   for (int i = 0; i < cnt; ++i) body(i, R);
 
-  // segment 0 starts from S0 and needs no transition map
+  // the summary (S_loc: a lane's four consecutive rows are one 16-byte store; M in bf16, which
+  // its consumer rounds it to for its products); segment 0 starts from S0 and needs no
+  // transition map
+  float* SMs = p.SM + ((long)head * p.P + seg) * DK * (DV + DK);
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int t = 0; t < NTS; ++t)
+    for (int t = 0; t < NTS; ++t) {
+      const int row = dkrow(t, 4 * g4), col = 16 * (tile0 + c) + m;
+      if (isv) {
+        *reinterpret_cast<floatx4*>(SMs + sloc_index(row, col, DK)) = S[c][t];
+      } else if (seg > 0) {
+        bf16* Ms = reinterpret_cast<bf16*>(SMs + DV * DK);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = dkrow(t, 4 * g4 + j), col = 16 * (tile0 + c) + m;
-        if (isv || seg > 0) p.SM[(((long)head * p.P + seg) * DK + row) * (DV + DK) + col] = S[c][t][j];
+        for (int j = 0; j < 4; ++j) Ms[mfrag_index<mfrag_width<bf16, DK>()>(row + j, col - DV, DK)] = (bf16)S[c][t][j];
       }
+    }
 }
 
 }  // namespace summary
