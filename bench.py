@@ -4,16 +4,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-others]
 
-One step = one full forward pass (the intra-chunk kernel, then the segment summary, combine and
-output launches of the inter-chunk pass) over one batch of synthetic inputs already resident in HBM.  W untimed warm-up steps, then K timed steps bracketed
-by device synchronisation.  Prints ONE JSON line on stdout; progress goes to stderr.
+One step = one full forward pass (one delta_fwd call: the intra-chunk kernel, then the segment
+summary, combine and output launches of the inter-chunk pass) over one batch of synthetic inputs
+already resident in HBM.  W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation; `value` and `ms_per_step` come from them.  The same K steps are then run as
+their four launches with HIP events between them (per-kernel durations: `kernels_ms`, the
+roofline) and replayed K times from a HIP graph of one step (`graph`).  Prints ONE JSON line on
+stdout; progress goes to stderr.
 
 Default workload: Gated DeltaNet, B=2, H=16, L=8192, d_k=d_v=128, bf16 inputs, fp32 state,
 chunk 64 (the H=16, d=128, L=8K shape the tokens/s metric is quoted on).  tokens = B * L.
 
 The line carries:
   roofline      for the dominant kernel: algorithmic bytes per launch / its mean launch time
-                (HIP events on the launch stream over the timed steps), against 8 TB/s HBM
+                (HIP events on the launch stream over the event-timed steps), against 8 TB/s HBM
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the same workload
   others        the other workloads (DeltaNet 4x8x2K, DeltaProduct n_h=2, GDN 64K, and the
                 batch-64 decode step), measured the same way, unless --no-others
@@ -189,23 +193,48 @@ def time_prefill(w, steps, warmup, copy_calibration_mib=0):
                                            dtype=code)),
         ("outputs", lambda: D.scan_outputs(q, k, v, S0, ws, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF)),
     ]
+    def step():  # one forward pass as a caller runs it: one delta_fwd call
+        D.fwd(q, k, v, beta, g, S0, n_h=w.n_h, chunk=w.chunk, O=O, S_final=SF, workspace=ws)
+
     for _ in range(warmup):
+        step()
         for _, c in calls:
             c()
     torch.cuda.synchronize()
+    # timed region 1: whole steps back to back (the throughput reported as `value`)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # timed region 2: the same steps as their four launches, each bracketed by events on the
+    # launch stream (the per-kernel durations of the roofline; the events add their own gaps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
         for j, (_, c) in enumerate(calls):
             c()
             ev[i][j + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_ev = time.perf_counter() - t1
     ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j, (name, _) in enumerate(calls)}
+    # timed region 3: one step captured as a HIP graph and replayed (launch gaps removed)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall_g = time.perf_counter() - t2
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ms,
-            "tokens_per_s": w.B * w.L * steps / wall}
+            "tokens_per_s": w.B * w.L * steps / wall, "ms_per_step_with_events": wall_ev * 1e3 / steps,
+            "graph_ms_per_step": wall_g * 1e3 / steps, "graph_tokens_per_s": w.B * w.L * steps / wall_g}
 
 
 def kernel_sources_sha():
@@ -402,6 +431,8 @@ def main():
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
         "roofline": roofline_of(w, r),
         "kernels_ms": {k: round(v, 5) for k, v in r["kernel_ms"].items()},
+        "ms_per_step_with_events": round(r["ms_per_step_with_events"], 5),
+        "graph": {"ms_per_step": round(r["graph_ms_per_step"], 5), "tokens_per_s": round(r["graph_tokens_per_s"], 1)},
         "segments": list(_segments(w)),
     }
     if not args.no_others:
@@ -413,7 +444,7 @@ def main():
                 wo = W.get(name)
                 ro = time_prefill(wo, max(5, args.steps // 5), 2)
                 others[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1), "ms_per_step": round(ro["ms_per_step"], 5),
-                                "roofline": roofline_of(wo, ro)}
+                                "graph_tokens_per_s": round(ro["graph_tokens_per_s"], 1), "roofline": roofline_of(wo, ro)}
                 log("[bench] %s: %.3f ms/step, %.3e tokens/s" % (name, ro["ms_per_step"], ro["tokens_per_s"]))
             except Exception as e:  # an auxiliary line must not hide the main one
                 others[name] = {"error": repr(e)}
