@@ -315,29 +315,6 @@ __device__ inline void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, float x)
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);  // data operand is a u32
 }
 
-// Loads issued through inline assembly, for prefetches that must stay in flight across code that
-// the compiler would otherwise precede with a wait for every outstanding load (it waits for all
-// loads it knows of before the first use of any of them).  The compiler does not track these, so
-// their completion is awaited explicitly with wait_vm<N>(): loads return in issue order, so at
-// most N outstanding vector memory operations, N being the number of loads issued after the
-// needed ones or fewer, means those have landed (stores in flight only make the wait longer).
-// Buffer resource over [base, base + bytes): accesses outside the range read 0.
-__device__ inline u32x4 make_desc(const void* base, unsigned bytes) {
-  const unsigned long a = reinterpret_cast<unsigned long>(base);
-  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-__device__ inline void asm_load16(u32x4& dst, u32x4 desc, int off) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(desc));
-}
-__device__ inline void asm_load4(unsigned& dst, u32x4 desc, int off) {
-  asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(desc));
-}
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// exp(x) of a gate ratio (x <= 0: a decay) as the hardware base-2 exponential of x log2(e).
 __device__ inline float gate_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // Inclusive prefix sum across the 64 lanes of a wave.

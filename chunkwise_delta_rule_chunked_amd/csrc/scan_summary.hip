@@ -27,6 +27,8 @@
 // Fragment layouts (16x16x32 bf16): lane (g, m) (g = lane / 16, m = lane % 16) holds
 // A[m][8g .. 8g+7], B[8g .. 8g+7][m] and D[4g .. 4g+3][m].  State row tiles 2u, 2u+1 interleave
 // their d_k indices so that the K S A-fragment is one 16-byte LDS read.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -62,9 +64,8 @@ __device__ inline floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The LDS writes of the prefetched pieces are inline assembly too (see asm_load16 in
-// common.h): the compiler would otherwise wait for every outstanding load before the first of
-// them, that is, for the next chunk's loads as well.
+// The LDS writes of the prefetched pieces, with the stage offset as the instruction's immediate
+// (the compiler waits for each piece's load before its write).
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)reinterpret_cast<unsigned long>((const __attribute__((address_space(3))) void*)p);
 }
@@ -124,16 +125,16 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     n = min(n, n1 - 1);
     const long P0 = (long)n * C;
     const unsigned krows = (unsigned)min((long)C, p.Lx - P0);
-    const u32x4 kd = make_desc(kg + ((long)b * p.Lx + P0) * HDK, krows * HDK * 2);
-    const u32x4 vd = make_desc(vg + ((long)b * p.Lx + P0) * HDV, krows * HDV * 2);
-    const u32x4 td = make_desc(Tg + (long)n * C * C, C * C * 2);
+    const __amdgpu_buffer_rsrc_t kd = buffer_rsrc(const_cast<bf16*>(kg) + ((long)b * p.Lx + P0) * HDK, krows * HDK * 2);
+    const __amdgpu_buffer_rsrc_t vd = buffer_rsrc(const_cast<bf16*>(vg) + ((long)b * p.Lx + P0) * HDV, krows * HDV * 2);
+    const __amdgpu_buffer_rsrc_t td = buffer_rsrc(const_cast<bf16*>(Tg) + (long)n * C * C, C * C * 2);
 #pragma unroll
-    for (int i = 0; i < NKP; ++i) asm_load16(R.k[i], kd, offG_k[i]);
+    for (int i = 0; i < NKP; ++i) R.k[i] = buffer_load16(kd, offG_k[i]);
 #pragma unroll
-    for (int i = 0; i < NTP; ++i) asm_load16(R.t[i], td, ((NTP * wave + i) * WAVE + lane) * 16);
+    for (int i = 0; i < NTP; ++i) R.t[i] = buffer_load16(td, ((NTP * wave + i) * WAVE + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < NKP; ++i) asm_load16(R.v[i], vd, offG_v[i]);
-    asm_load4(R.gc, make_desc(gcg + (long)n * C, C * 4), lane * 4);
+    for (int i = 0; i < NKP; ++i) R.v[i] = buffer_load16(vd, offG_v[i]);
+    R.gc = __builtin_bit_cast(unsigned, buffer_load4(buffer_rsrc(const_cast<float*>(gcg) + (long)n * C, C * 4), lane * 4));
   };
 
   // registers -> LDS stage; wavefront 0 also writes the gate tables
@@ -198,11 +199,12 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   for (int c = 0; c < CT; ++c) offV[c] = swz(4 * g4 + (m >> 2), 16 * (isv ? tile0 + c : c) + 4 * (m & 3), DV, 15);
 
   // one chunk on stage st; Rw (chunk n+1) goes to the other stage, then takes chunk n+2
-  auto body = [&](int i, Regs& Rw) __attribute__((always_inline)) {
+  // (ISV: this wavefront's tiles are value columns; transition columns see V = 0 and read no V)
+  auto body = [&](int i, Regs& Rw, auto isv_tag) __attribute__((always_inline)) {
+    constexpr bool ISV = decltype(isv_tag)::value;
     bf16* st = smem + (i & 1) * STAGE;
     bf16* sn = smem + ((i & 1) ^ 1) * STAGE;
-    wait_vm<0>();  // Rw (chunk n+1) has landed
-    write_stage(sn, Rw);
+    write_stage(sn, Rw);  // chunk n+1 (the compiler waits for its loads)
     load(n0 + i + 2, Rw);
     __builtin_amdgcn_iglp_opt(1);
 
@@ -237,10 +239,13 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       const floatx4 eg = *reinterpret_cast<const floatx4*>(G + C + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const bf16x4 r = read_tr4(V + 16 * bb * DV + offV[c]);
-        floatx4 v4 = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
-        v4 = isv ? v4 : floatx4{0.f, 0.f, 0.f, 0.f};
-        Yb[c][bb] = cvt4(v4 - eg * X[c][bb]);
+        if constexpr (ISV) {
+          const bf16x4 r = read_tr4(V + 16 * bb * DV + offV[c]);
+          const floatx4 v4 = floatx4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+          Yb[c][bb] = cvt4(v4 - eg * X[c][bb]);
+        } else {
+          Yb[c][bb] = cvt4(-(eg * X[c][bb]));
+        }
       }
     }
     // V~ = T Y (T lower triangular: block pairs at or left of the diagonal), weighted by
@@ -285,11 +290,14 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   // prologue: chunk n0 staged, chunk n0+1 in flight
   Regs R;
   load(n0, R);
-  wait_vm<0>();
   write_stage(smem, R);
   load(n0 + 1, R);
   lds_barrier();
-  for (int i = 0; i < cnt; ++i) body(i, R);
+  if (isv) {
+    for (int i = 0; i < cnt; ++i) body(i, R, std::true_type{});
+  } else {
+    for (int i = 0; i < cnt; ++i) body(i, R, std::false_type{});
+  }
 
   // the summary (S_loc: a lane's four consecutive rows are one 16-byte store; M in bf16, which
   // its consumer rounds it to for its products); segment 0 starts from S0 and needs no
