@@ -22,8 +22,25 @@
 
 namespace delta {
 
-// A and N are lower triangular: only their NB (NB + 1) / 2 blocks of 16 x 16 on and below the
-// diagonal are stored, block (i, j) at index i (i + 1) / 2 + j, rows padded to LDB floats.
+// A and N are lower triangular: only their blocks of 16 x 16 on and below the diagonal are
+// stored, rows padded to LDB floats, in slots of one array.  A block (i, j) is in slot
+// lower_block(i, j).  N's diagonal blocks take the slots of A's (a diagonal A block is read only
+// by the substitution that turns it into the N block, in the same wavefront); N's blocks below
+// the diagonal follow A's, except at C = 64, where N_20 and N_30 take the slots of A_10 and A_21,
+// which are no longer read once those are formed (A_10 only feeds N_10, A_21 only N_21 and
+// N_20).  Fewer LDS bytes per tile let more workgroups share a compute unit (8 at C = 64, d = 128).
+__host__ __device__ constexpr int lower_block(int i, int j) { return i * (i + 1) / 2 + j; }
+template <int NB>
+__host__ __device__ constexpr int n_slot(int i, int j) {
+  constexpr int NBLK = NB * (NB + 1) / 2;
+  if (i == j) return lower_block(i, i);
+  if (NB == 4) {
+    if (i == 2 && j == 0) return lower_block(1, 0);
+    if (i == 3 && j == 0) return lower_block(2, 1);
+    return NBLK + (i == 1 ? 0 : i == 2 ? 1 : j + 1);  // N_10, N_21, N_31, N_32
+  }
+  return NBLK + i * (i - 1) / 2 + j;
+}
 template <typename E, int DK, int C>
 struct IntraLds {
   static constexpr int NB = C / 16;
@@ -31,11 +48,11 @@ struct IntraLds {
   static constexpr int LDB = 20;                      // fp32 row stride inside a 16 x 16 block
   static constexpr int BLK = 16 * LDB;                // floats per block
   static constexpr int NBLK = NB * (NB + 1) / 2;
+  static constexpr int NSLOT = NBLK + (NB == 4 ? 4 : NB * (NB - 1) / 2);
   static constexpr int KBYTES = C * LDK * (int)sizeof(E);
-  static constexpr int ANBYTES = 2 * NBLK * BLK * 4;  // A and N
+  static constexpr int ANBYTES = NSLOT * BLK * 4;     // A and N
   static constexpr int BYTES = KBYTES > ANBYTES ? KBYTES : ANBYTES;
 };
-__host__ __device__ constexpr int lower_block(int i, int j) { return i * (i + 1) / 2 + j; }
 
 template <typename E, typename TO, int DK, int C>
 __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
@@ -46,8 +63,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   __shared__ float gcs[C], bs[C];
   const Tile<E> Kt = make_tile<E, DK>(reinterpret_cast<E*>(smem));
   float* As = reinterpret_cast<float*>(smem);   // after the key tile is dead
-  float* Ns = As + NBLK * BLK;
-  auto blk = [](float* base, int i, int j) { return base + lower_block(i, j) * BLK; };
+  auto ablk = [&](int i, int j) { return As + lower_block(i, j) * BLK; };
+  auto nblk = [&](int i, int j) { return As + n_slot<NB>(i, j) * BLK; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, rq = 4 * (lane >> 4);
@@ -133,7 +150,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
       const floatx4 br = *reinterpret_cast<const floatx4*>(bs + row0);
       const floatx4 gr = *reinterpret_cast<const floatx4*>(gcs + row0);
       const float gcc = gcs[c];
-      float* Ab = blk(As, i, j) + rq * LDB + col;
+      float* Ab = ablk(i, j) + rq * LDB + col;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         Ab[r * LDB] = (row0 + r > c) ? br[r] * gate_exp(gr[r] - gcc) * G[u][r] : 0.f;
@@ -151,7 +168,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float a0 = (i == col) ? 1.f : 0.f, a1 = 0.f;
-      const float* Ai = blk(As, t, t) + i * LDB;
+      const float* Ai = ablk(t, t) + i * LDB;
 #pragma unroll
       for (int j4 = 0; j4 < i; j4 += 4) {
         const floatx4 a = *reinterpret_cast<const floatx4*>(Ai + j4);
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
       x[i] = a0 + a1;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) blk(Ns, t, t)[i * LDB + col] = x[i];
+    for (int i = 0; i < 16; ++i) nblk(t, t)[i * LDB + col] = x[i];
   }
   __syncthreads();
 
@@ -184,15 +201,15 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
         for (int k0 = 0; k0 < 16; k0 += 4) {
           const int kk = k0 + (lane >> 4);
-          acc = Mfma<float>::mma(blk(As, i, k)[col * LDB + kk], blk(Ns, k, j)[kk * LDB + col], acc);
+          acc = Mfma<float>::mma(ablk(i, k)[col * LDB + kk], nblk(k, j)[kk * LDB + col], acc);
         }
       }
       floatx4 nij = {0.f, 0.f, 0.f, 0.f};
-      const float* Nii = blk(Ns, i, i) + col * LDB + rq;
+      const float* Nii = nblk(i, i) + col * LDB + rq;
 #pragma unroll
       for (int r = 0; r < 4; ++r) nij = Mfma<float>::mma(Nii[r], acc[r], nij);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) blk(Ns, i, j)[(rq + r) * LDB + col] = -nij[r];
+      for (int r = 0; r < 4; ++r) nblk(i, j)[(rq + r) * LDB + col] = -nij[r];
     }
     __syncthreads();
   }
@@ -202,8 +219,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
   for (int idx = 4 * tid; idx < C * C; idx += 4 * 256) {
     const int r = idx / C, c = idx % C;
-    // blocks above the diagonal are not stored: the index stays inside N, the select drops it
-    const floatx4 nv = *reinterpret_cast<const floatx4*>(blk(Ns, r >> 4, c >> 4) + (r & 15) * LDB + (c & 15));
+    // blocks above the diagonal are not stored: read the row's diagonal block, the select drops it
+    const floatx4 nv = *reinterpret_cast<const floatx4*>(nblk(r >> 4, min(c >> 4, r >> 4)) + (r & 15) * LDB + (c & 15));
     const floatx4 bv = *reinterpret_cast<const floatx4*>(bs + c);
     float x[4];
 #pragma unroll
