@@ -143,13 +143,9 @@ struct SegCfg {
   static constexpr int KS = C * DK, QS = SUM ? 0 : C * DK, TS = C * C, AS = SUM ? 0 : C * C, VS = C * VWMAX;
   static constexpr int GS = 4 * C * 4 / ES;  // gc, exp(gc), exp(gc_last - gc), token output gates
   static constexpr int IN = KS + QS + TS + AS + VS + GS;   // one staged chunk (elements)
-  // bf16 outputs go through a per-wave staging tile O^T [16 CT][C]
-  static constexpr bool OSTAGE = !SUM && ES == 2;
-  static constexpr int OSW = 16 * CT * C;                  // per wave (elements)
-  static constexpr int OS = OSTAGE ? NCW * OSW : 0;
   static constexpr int SYNC = SUM ? 0 : 16 / ES;              // loader rendezvous counter
-  static constexpr int NSTAGE = (2 * IN + OS + SYNC) * ES <= LDS_BUDGET ? 2 : 1;
-  static constexpr int ELEMS = NSTAGE * IN + OS + SYNC;
+  static constexpr int NSTAGE = (2 * IN + SYNC) * ES <= LDS_BUDGET ? 2 : 1;
+  static constexpr int ELEMS = NSTAGE * IN + SYNC;
   static_assert(ELEMS * ES <= LDS_BUDGET, "LDS budget");
 };
 
@@ -196,7 +192,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
   const int VW = 16 * vcnt;
   // segment 0 of the summary needs only the value columns
   if (SUM && seg == 0 && vcnt == 0) return;
-  unsigned* rdv = reinterpret_cast<unsigned*>(smem + Cfg::NSTAGE * Cfg::IN + Cfg::OS);
+  unsigned* rdv = reinterpret_cast<unsigned*>(smem + Cfg::NSTAGE * Cfg::IN);
   if constexpr (!SUM) {
     if (tid == 0) *rdv = 0u;
     barrier_lds();
@@ -470,8 +466,6 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
   if constexpr (Cfg::NSTAGE == 2) barrier_lds();
 
   E* Og = reinterpret_cast<E*>(p.O);
-  // bf16 outputs: per-wave staging of O^T [16 CT][C], written back with transpose reads
-  const Tile<E> Ost = make_packed_tile<E, C>(smem + Cfg::NSTAGE * Cfg::IN + (Cfg::OSTAGE ? wave * Cfg::OSW : 0));
 
   for (int n = n0; n < n1; ++n) {
     if constexpr (Cfg::NSTAGE == 1) barrier_lds();
@@ -598,12 +592,15 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       }
     }
 
-    // ---- outputs: O = scale (gamma_p Q S + A V~), S still the chunk-start state.  A is zero
-    // past each token's causal reach, so the product runs over all position blocks.  Every row
-    // block is computed (with several sub-steps per token the blocks past the chunk's tokens read
-    // stale but in-bounds LDS and are never stored) and the stores are masked by the buffer
-    // range check: no branch splits the chunk body, so the row blocks' LDS reads, products and
-    // stores can overlap.
+    // ---- outputs: O = scale (gamma_p Q S + A V~), S still the chunk-start state, formed
+    // transposed: with the operands of each product swapped the MFMA yields the tile of O^T
+    // (O^T = S^T Q^T + V~^T A^T; the state and V~ registers serve as A operands and the Q and A
+    // row fragments as B operands unchanged), so lane (g, m) holds columns 4g .. 4g + 3 of token
+    // row m and stores them with one 8-byte (bf16) or 16-byte (fp32) write.  A is zero past each
+    // token's causal reach, so the product runs over all position blocks.  Every row block is
+    // computed (with several sub-steps per token the blocks past the chunk's tokens read stale
+    // but in-bounds LDS) and the stores are masked by the buffer range check: no branch splits
+    // the chunk body.
     if constexpr (!SUM) {
       constexpr int KSTEPA = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
       // Output addresses depend only on the lane and the chunk; hiding the lane index keeps the
@@ -616,64 +613,51 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       E* Ochunk = Og + (((long)b * p.L + (long)n * QR) * p.H + h) * p.DV;
       const int orows = min(QR, (int)((long)p.L - (long)n * QR));
       const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(Ochunk, orows * HDV * (int)sizeof(E));
-      // element column of each tile in O; a tile past the value columns stores out of range
+      // the lane's first element column of each tile in O; a tile past the value columns stores
+      // out of range
       int ocol[CT];
 #pragma unroll
-      for (int c = 0; c < CT; ++c) ocol[c] = isv[c] ? 16 * tile[c] : orows * HDV;
+      for (int c = 0; c < CT; ++c) ocol[c] = isv[c] ? 16 * tile[c] + 4 * go : orows * HDV;
 #pragma unroll
       for (int tq = 0; tq < NB; ++tq) {
-        {
-          floatx4 o1[CT], o2[CT];
+        floatx4 o1[CT], o2[CT];
 #pragma unroll
-          for (int c = 0; c < CT; ++c) o1[c] = o2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CT; ++c) o1[c] = o2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int t = 0; t < NTS; t += TSTEP) {
-            if constexpr (DP) {
-              const bf16x8 a = DOp<bf16>::row8(reinterpret_cast<const bf16*>(Qp) + 16 * tq * DK + offK[t]);
+        for (int t = 0; t < NTS; t += TSTEP) {
+          if constexpr (DP) {
+            const bf16x8 a = DOp<bf16>::row8(reinterpret_cast<const bf16*>(Qp) + 16 * tq * DK + offK[t]);
 #pragma unroll
-              for (int c = 0; c < CT; ++c) o1[c] = DOp<bf16>::mma8(a, Sb[c][t], Sb[c][t + 1], o1[c]);
-            } else {
-              const typename D::A a0 = D::row4(Qp + 16 * tq * DK + offK[t]);
+            for (int c = 0; c < CT; ++c)
+              o1[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_shufflevector(Sb[c][t], Sb[c][t + 1], 0, 1, 2, 3, 4, 5, 6, 7), a, o1[c], 0, 0, 0);
+          } else {
+            const typename D::A a0 = D::row4(Qp + 16 * tq * DK + offK[t]);
 #pragma unroll
-              for (int c = 0; c < CT; ++c) o1[c] = D::mma1(a0, Sb[c][t], o1[c]);
-            }
+            for (int c = 0; c < CT; ++c) o1[c] = D::mma1(Sb[c][t], a0, o1[c]);
           }
+        }
 #pragma unroll
-          for (int kb = 0; kb < NB; kb += KSTEPA) {
-            const typename D::A a0 = D::row4(Ap + 16 * tq * C + offT[kb]);
-            if constexpr (KSTEPA == 2) {
-              const typename D::A a1 = D::row4(Ap + 16 * tq * C + offT[kb + 1]);
+        for (int kb = 0; kb < NB; kb += KSTEPA) {
+          const typename D::A a0 = D::row4(Ap + 16 * tq * C + offT[kb]);
+          if constexpr (KSTEPA == 2) {
+            const typename D::A a1 = D::row4(Ap + 16 * tq * C + offT[kb + 1]);
 #pragma unroll
-              for (int c = 0; c < CT; ++c) o2[c] = D::mma2(a0, a1, Vb[c][kb], Vb[c][kb + 1], o2[c]);
-            } else {
+            for (int c = 0; c < CT; ++c) o2[c] = D::mma2(Vb[c][kb], Vb[c][kb + 1], a0, a1, o2[c]);
+          } else {
 #pragma unroll
-              for (int c = 0; c < CT; ++c) o2[c] = D::mma1(a0, Vb[c][kb], o2[c]);
-            }
+            for (int c = 0; c < CT; ++c) o2[c] = D::mma1(Vb[c][kb], a0, o2[c]);
           }
-          // scale * gamma of each token's last sub-step (rows past the chunk's tokens: 0); the
-          // stored A_qk already carries the scale
-          const floatx4 gq = *reinterpret_cast<const floatx4*>(eqp + 16 * tq + 4 * go);
+        }
+        // scale * gamma of the lane's token (its last sub-step; rows past the chunk's tokens: 0);
+        // the stored A_qk already carries the scale
+        const float gq = eqp[16 * tq + mo];
+        const int orow = (16 * tq + mo) * HDV;
 #pragma unroll
-          for (int c = 0; c < CT; ++c) {
-            const floatx4 o = gq * o1[c] + o2[c];
-            if constexpr (Cfg::OSTAGE) {
-              *reinterpret_cast<bf16x4*>(Ost.at(16 * c + mo, 16 * tq + 4 * go)) = DOp<bf16>::cvt(o);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                buffer_store4(orsrc, ((16 * tq + 4 * go + j) * HDV + ocol[c] + mo) * 4, o[j]);
-            }
-          }
-          if constexpr (Cfg::OSTAGE) {
-            // back from the staging tile: lane (g4, m) gets columns 16 c + 4 g4 .. +3 of token
-            // 16 tq + m (this wave's own LDS area: no barrier)
-            const int trow = 16 * tq + mo;
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-              const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Ost.at(16 * c + 4 * go + (mo >> 2), 16 * tq + 4 * (mo & 3))));
-              buffer_store8(orsrc, (trow * HDV + ocol[c] + 4 * go) * 2, r);
-            }
-          }
+        for (int c = 0; c < CT; ++c) {
+          const floatx4 o = gq * o1[c] + o2[c];
+          if constexpr (sizeof(E) == 2) buffer_store8(orsrc, (orow + ocol[c]) * 2, DOp<bf16>::cvt(o));
+          else buffer_store16(orsrc, (orow + ocol[c]) * 4, o);
         }
       }
     }

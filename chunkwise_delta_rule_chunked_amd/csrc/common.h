@@ -311,6 +311,9 @@ __device__ inline u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {   // 0
 __device__ inline float buffer_load4(__amdgpu_buffer_rsrc_t r, int off) {   // 0 outside the range
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+__device__ inline void buffer_store16(__amdgpu_buffer_rsrc_t r, int off, floatx4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
 __device__ inline void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);  // data operand is a u32
 }
