@@ -9,8 +9,9 @@ summary, combine and output launches of the inter-chunk pass) over one batch of 
 already resident in HBM.  W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation; `value` and `ms_per_step` come from them.  The same K steps are then run as
 their four launches with HIP events between them (per-kernel durations: `kernels_ms`, the
-roofline) and replayed K times from a HIP graph of one step (`graph`).  Prints ONE JSON line on
-stdout; progress goes to stderr.
+roofline), replayed K times from a HIP graph of one step (`graph`), and called K times singly
+between event pairs, warm and with the Infinity Cache flushed before each call
+(`median_call_ms`).  Prints ONE JSON line on stdout; progress goes to stderr.
 
 Default workload: Gated DeltaNet, B=2, H=16, L=8192, d_k=d_v=128, bf16 inputs, fp32 state,
 chunk 64 (the H=16, d=128, L=8K shape the tokens/s metric is quoted on).  tokens = B * L.
@@ -232,9 +233,27 @@ def time_prefill(w, steps, warmup, copy_calibration_mib=0):
         graph.replay()
     torch.cuda.synchronize()
     wall_g = time.perf_counter() - t2
+    # single calls, each bracketed by an event pair: warm (back to back) and cold (a 512 MiB
+    # scratch buffer written between calls, outside the pair, so no input or workspace byte is
+    # left in the 256 MB Infinity Cache); medians
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    single = {"warm": [], "cold": []}
+    for mode in ("warm", "cold"):
+        for i in range(steps):
+            if mode == "cold":
+                scratch.fill_(i & 255)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            single[mode].append((e0, e1))
+        torch.cuda.synchronize()
+    del scratch
+    med = {mode: sorted(a.elapsed_time(b) for a, b in pairs)[len(pairs) // 2] for mode, pairs in single.items()}
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms": ms,
             "tokens_per_s": w.B * w.L * steps / wall, "ms_per_step_with_events": wall_ev * 1e3 / steps,
-            "graph_ms_per_step": wall_g * 1e3 / steps, "graph_tokens_per_s": w.B * w.L * steps / wall_g}
+            "graph_ms_per_step": wall_g * 1e3 / steps, "graph_tokens_per_s": w.B * w.L * steps / wall_g,
+            "median_call_ms": med}
 
 
 def kernel_sources_sha():
@@ -433,6 +452,7 @@ def main():
         "kernels_ms": {k: round(v, 5) for k, v in r["kernel_ms"].items()},
         "ms_per_step_with_events": round(r["ms_per_step_with_events"], 5),
         "graph": {"ms_per_step": round(r["graph_ms_per_step"], 5), "tokens_per_s": round(r["graph_tokens_per_s"], 1)},
+        "median_call_ms": {k: round(v, 5) for k, v in r["median_call_ms"].items()},
         "segments": list(_segments(w)),
     }
     if not args.no_others:
@@ -444,7 +464,9 @@ def main():
                 wo = W.get(name)
                 ro = time_prefill(wo, max(5, args.steps // 5), 2)
                 others[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1), "ms_per_step": round(ro["ms_per_step"], 5),
-                                "graph_tokens_per_s": round(ro["graph_tokens_per_s"], 1), "roofline": roofline_of(wo, ro)}
+                                "graph_tokens_per_s": round(ro["graph_tokens_per_s"], 1),
+                                "median_call_ms": {k: round(v, 5) for k, v in ro["median_call_ms"].items()},
+                                "roofline": roofline_of(wo, ro)}
                 log("[bench] %s: %.3f ms/step, %.3e tokens/s" % (name, ro["ms_per_step"], ro["tokens_per_s"]))
             except Exception as e:  # an auxiliary line must not hide the main one
                 others[name] = {"error": repr(e)}
