@@ -9,13 +9,15 @@ Functions
 ---------
 fwd(...)        the token-by-token recurrence in fp64 (oracle.c); the definition
                 of what delta_fwd and delta_decode compute.
+bwd(...)        its gradients by reverse-mode differentiation of the same recurrence
+                (oracle.c), for the backward pass.
 ut_factors(...) the per-chunk UT transform T = (I + strictLower(diag(beta)
                 (Gamma * K K^T)))^-1 diag(beta) and the WY factors
                 W = T (gamma * K), U = T V, written from their definitions with a
                 library triangular solve (what delta_chunk_wy computes).
 
-Both are pinned in tests/test_oracle_pins.py (closed forms, brute force,
-independent formulations); neither is "parity unpinned".
+All three are pinned in tests/test_oracle_pins.py (closed forms, brute force,
+independent formulations, finite differences); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -51,6 +53,8 @@ def _load():
         lib.oracle_fwd.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [P] * 8 + [ctypes.c_int]
         lib.oracle_fwd.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [P] * 14 + [ctypes.c_int]
+        lib.oracle_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -90,6 +94,33 @@ def fwd(q, k, v, beta, g_log=None, S0=None, n_h: int = 1, scale: float = 1.0,
     if rc != 0:
         raise RuntimeError("oracle_fwd failed (%d)" % rc)
     return O, S_final
+
+
+def bwd(q, k, v, beta, g_log, S0, dO, dS_final=None, n_h: int = 1, scale: float = 1.0,
+        nthreads: int = 0):
+    """Gradients of fwd (oracle.c, oracle_bwd: reverse-mode differentiation of the same
+    recurrence in fp64) for the loss <O, dO> + <S_final, dS_final>.  Inputs as fwd, plus dO
+    [B,L,H,dv] and dS_final [B,H,dk,dv] or None (taken as float32).  Returns a dict of fp64
+    arrays dq, dk, dv, dbeta, dg_log (None when ungated), dS0."""
+    q, k, v, beta, g_log, S0, dO, dS_final = map(_f32, (q, k, v, beta, g_log, S0, dO, dS_final))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    Lx = L * n_h
+    assert k.shape == (B, Lx, H, dk) and v.shape == (B, Lx, H, dv) and beta.shape == (B, Lx, H)
+    assert g_log is None or g_log.shape == (B, L, H)
+    assert S0 is None or S0.shape == (B, H, dk, dv)
+    assert dO.shape == (B, L, H, dv)
+    assert dS_final is None or dS_final.shape == (B, H, dk, dv)
+    out = {"dq": np.empty((B, L, H, dk)), "dk": np.empty((B, Lx, H, dk)), "dv": np.empty((B, Lx, H, dv)),
+           "dbeta": np.empty((B, Lx, H)), "dg_log": np.empty((B, L, H)) if g_log is not None else None,
+           "dS0": np.empty((B, H, dk, dv))}
+    rc = _load().oracle_bwd(B, L, H, dk, dv, n_h, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                            _ptr(g_log), _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
+                            _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dg_log"]),
+                            _ptr(out["dS0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_bwd failed (%d)" % rc)
+    return out
 
 
 def decode(q, k, v, beta, g_log, S, n_h: int = 1, scale: float = 1.0):

@@ -117,6 +117,134 @@ int oracle_fwd(int B, int L, int H, int dk, int dv, int nh, double scale,
     return fail ? -1 : 0;
 }
 
+/*
+ * oracle_bwd -- gradients of the forward pass above, by reverse-mode differentiation of the
+ * same recurrence, in fp64, with every intermediate state stored (no chunking).
+ *
+ * The pages give no gradient formulas; these follow from the recurrence by the chain rule.
+ * With G = dLoss/dS for the state after a step (starting from dS_final, or 0):
+ *   read    o_i = scale S^T q_i:          dq_i = scale S do_i;   G += scale q_i do_i^T
+ *   write   S_a = S_b + beta k e^T, e = v - S_b^T k, u = G^T k:
+ *           dv_t = beta u;   dbeta_t = u . e;   dk_t = beta (G e - S_b u);   G <- G - beta k u^T
+ *   gate    S_{i,0} = g_i S_{i-1}:        dlog g_i = <G, S_{i,0}>;   G <- g_i G
+ *   dS0 = G after the first token.
+ * Steps are undone in reverse order: tokens from the last, and within a token its sub-steps
+ * from the last, then its gate.
+ *
+ * Inputs as oracle_fwd, plus dO [B, L, H, dv] (float32) and dS_final [B, H, dk, dv] (float32
+ * or NULL = 0).  Outputs fp64: dq [B, L, H, dk], dk [B, L*n_h, H, dk], dv [B, L*n_h, H, dv],
+ * dbeta [B, L*n_h, H], dg_log [B, L, H] (ignored when g_log is NULL; may be NULL then),
+ * dS0 [B, H, dk, dv].  Returns 0, or -1 on allocation failure or bad sizes.
+ *
+ * Pins: tests/test_oracle_pins.py compares every output with central finite differences of
+ * oracle_fwd and with the closed form of a one-token sequence.
+ */
+int oracle_bwd(int B, int L, int H, int dk, int dv, int nh, double scale,
+               const float* q, const float* k, const float* v, const float* beta,
+               const float* g_log, const float* S0, const float* dO, const float* dS_final,
+               double* dq, double* dkx, double* dvx, double* dbeta, double* dg_log, double* dS0,
+               int nthreads) {
+    if (B < 0 || L < 0 || H <= 0 || dk <= 0 || dv <= 0 || nh <= 0) return -1;
+    const long Lx = (long)L * nh;
+    const size_t SS = (size_t)dk * dv;
+    int fail = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+#endif
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        /* Sb[t]: state before sub-step t; So[i]: state after token i (read by o_i) */
+        double* Sb = (double*)malloc(sizeof(double) * SS * (size_t)(Lx > 0 ? Lx : 1));
+        double* So = (double*)malloc(sizeof(double) * SS * (size_t)(L > 0 ? L : 1));
+        double* S = (double*)malloc(sizeof(double) * SS);
+        double* G = (double*)malloc(sizeof(double) * SS);
+        double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!Sb || !So || !S || !G || !e || !u) {
+            free(Sb); free(So); free(S); free(G); free(e); free(u);
+            fail |= 1;
+            continue;
+        }
+        /* forward, keeping the states */
+        for (size_t x = 0; x < SS; ++x) S[x] = S0 ? (double)S0[((size_t)b * H + h) * SS + x] : 0.0;
+        for (long i = 0; i < L; ++i) {
+            if (g_log) {
+                const double g = exp((double)g_log[((size_t)b * L + i) * H + h]);
+                for (size_t x = 0; x < SS; ++x) S[x] *= g;
+            }
+            for (int j = 0; j < nh; ++j) {
+                const long t = i * nh + j;
+                const float* kt = k + (((size_t)b * Lx + t) * H + h) * dk;
+                const float* vt = v + (((size_t)b * Lx + t) * H + h) * dv;
+                const double bt = (double)beta[((size_t)b * Lx + t) * H + h];
+                memcpy(Sb + (size_t)t * SS, S, sizeof(double) * SS);
+                for (int c = 0; c < dv; ++c) e[c] = (double)vt[c];
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c) e[c] -= S[(size_t)r * dv + c] * (double)kt[r];
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] += bt * (double)kt[r] * e[c];
+            }
+            memcpy(So + (size_t)i * SS, S, sizeof(double) * SS);
+        }
+        /* backward */
+        for (size_t x = 0; x < SS; ++x) G[x] = dS_final ? (double)dS_final[((size_t)b * H + h) * SS + x] : 0.0;
+        for (long i = L - 1; i >= 0; --i) {
+            const float* qi = q + (((size_t)b * L + i) * H + h) * dk;
+            const float* doi = dO + (((size_t)b * L + i) * H + h) * dv;
+            double* dqi = dq + (((size_t)b * L + i) * H + h) * dk;
+            const double* Si = So + (size_t)i * SS;
+            for (int r = 0; r < dk; ++r) {
+                double a = 0.0;
+                for (int c = 0; c < dv; ++c) a += Si[(size_t)r * dv + c] * (double)doi[c];
+                dqi[r] = scale * a;
+            }
+            for (int r = 0; r < dk; ++r)
+                for (int c = 0; c < dv; ++c) G[(size_t)r * dv + c] += scale * (double)qi[r] * (double)doi[c];
+            for (int j = nh - 1; j >= 0; --j) {
+                const long t = i * nh + j;
+                const float* kt = k + (((size_t)b * Lx + t) * H + h) * dk;
+                const float* vt = v + (((size_t)b * Lx + t) * H + h) * dv;
+                const double bt = (double)beta[((size_t)b * Lx + t) * H + h];
+                const double* St = Sb + (size_t)t * SS;
+                double* dkt = dkx + (((size_t)b * Lx + t) * H + h) * dk;
+                double* dvt = dvx + (((size_t)b * Lx + t) * H + h) * dv;
+                for (int c = 0; c < dv; ++c) { e[c] = (double)vt[c]; u[c] = 0.0; }
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c) {
+                        e[c] -= St[(size_t)r * dv + c] * (double)kt[r];
+                        u[c] += G[(size_t)r * dv + c] * (double)kt[r];
+                    }
+                double db = 0.0;
+                for (int c = 0; c < dv; ++c) {
+                    dvt[c] = bt * u[c];
+                    db += u[c] * e[c];
+                }
+                dbeta[((size_t)b * Lx + t) * H + h] = db;
+                for (int r = 0; r < dk; ++r) {
+                    double a = 0.0;
+                    for (int c = 0; c < dv; ++c) a += G[(size_t)r * dv + c] * e[c] - St[(size_t)r * dv + c] * u[c];
+                    dkt[r] = bt * a;
+                }
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c) G[(size_t)r * dv + c] -= bt * (double)kt[r] * u[c];
+            }
+            if (g_log) {
+                /* the state right after the gate is the state before the token's first sub-step */
+                const double g = exp((double)g_log[((size_t)b * L + i) * H + h]);
+                const double* S0i = Sb + (size_t)(i * nh) * SS;
+                double a = 0.0;
+                for (size_t x = 0; x < SS; ++x) a += G[x] * S0i[x];
+                if (dg_log) dg_log[((size_t)b * L + i) * H + h] = a;
+                for (size_t x = 0; x < SS; ++x) G[x] *= g;
+            }
+        }
+        memcpy(dS0 + ((size_t)b * H + h) * SS, G, sizeof(double) * SS);
+        free(Sb); free(So); free(S); free(G); free(e); free(u);
+    }
+    return fail ? -1 : 0;
+}
+
 /* Number of threads OpenMP would use (for reporting the CPU baseline). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -52,3 +52,48 @@ def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught >= 1, name
+
+
+# slips in the backward pass (oracle_bwd), each caught by its pins
+BWD_MUTANTS = {
+    "bwd_dk_term_dropped": ("a += G[(size_t)r * dv + c] * e[c] - St[(size_t)r * dv + c] * u[c];",
+                            "a += G[(size_t)r * dv + c] * e[c];"),
+    "bwd_dbeta_uses_v": ("db += u[c] * e[c];", "db += u[c] * (double)vt[c];"),
+    "bwd_gate_grad_after_token": ("const double* S0i = Sb + (size_t)(i * nh) * SS;",
+                                  "const double* S0i = So + (size_t)i * SS;"),
+    "bwd_erase_not_propagated": ("G[(size_t)r * dv + c] -= bt * (double)kt[r] * u[c];",
+                                 "G[(size_t)r * dv + c] -= 0.0 * bt * (double)kt[r] * u[c];"),
+    "bwd_dq_unscaled": ("dqi[r] = scale * a;", "dqi[r] = a;"),
+    "bwd_gate_not_applied": ("for (size_t x = 0; x < SS; ++x) G[x] *= g;", ""),
+}
+
+BWD_PINS = [
+    lambda: P.test_bwd_matches_finite_differences(2, True, True),
+    lambda: P.test_bwd_matches_finite_differences(1, False, False),
+    P.test_bwd_one_token_closed_form,
+]
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_planted_backward_mistake_is_caught(name, tmp_path, monkeypatch):
+    a, b = BWD_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(a) == 1, name
+    (tmp_path / "m.c").write_text(src.replace(a, b))
+    so = tmp_path / "libm.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(tmp_path / "m.c"),
+                    "-lm"], check=True)
+    oracle._load()
+    import ctypes
+    lib = ctypes.CDLL(str(so))
+    for f in ("oracle_fwd", "oracle_bwd"):
+        getattr(lib, f).argtypes = getattr(oracle._lib, f).argtypes
+        getattr(lib, f).restype = ctypes.c_int
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = 0
+    for pin in BWD_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, name

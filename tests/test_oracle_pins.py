@@ -474,3 +474,79 @@ def test_ut_factors_drive_chunk_recurrence():
         Oc[pos] = (np.exp(gc)[:, None] * Q) @ Sc + ((Q @ K.T) * Gam) @ Vt
         Sc = np.exp(gc[-1]) * Sc + (np.exp(gc[-1] - gc)[:, None] * K).T @ Vt
     assert np.abs(Oc - O[0, :, 0]).max() < 1e-12 and np.abs(Sc - S[0, 0]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- backward (oracle.bwd)
+
+def _loss(inp, dO, dS, n_h, scale):
+    """<O, dO> + <S_final, dS> of the forward oracle, in fp64."""
+    q, k, v, beta, g, S0 = inp
+    O, S = oracle.fwd(q, k, v, beta, g, S0, n_h=n_h, scale=scale)
+    return float(np.sum(O * dO) + np.sum(S * dS))
+
+
+@pytest.mark.parametrize("n_h,gate,s0", [(1, False, False), (1, True, True), (2, True, True), (3, False, True)])
+def test_bwd_matches_finite_differences(n_h, gate, s0):
+    """Every gradient of oracle.bwd against central differences of oracle.fwd (an independent
+    function, itself pinned above).  Perturbations are float32-exact (h = 2^-11 on inputs of
+    magnitude < 8), so oracle.fwd sees exactly x +- h; the O(h^2) truncation error is ~1e-7."""
+    inp = list(rand_inputs(40 + 7 * n_h + gate, B=1, L=4, H=1, dk=3, dv=2, n_h=n_h, gate=gate, s0=s0,
+                           beta_hi=1.9))
+    r = rnd(5)
+    dO = r.standard_normal((1, 4, 1, 2)).astype(f32)
+    dS = r.standard_normal((1, 1, 3, 2)).astype(f32)
+    scale = 0.75
+    got = oracle.bwd(*inp, dO, dS, n_h=n_h, scale=scale)
+    h = 2.0 ** -11
+    names = [("dq", 0), ("dk", 1), ("dv", 2), ("dbeta", 3), ("dg_log", 4), ("dS0", 5)]
+    for name, idx in names:
+        x = inp[idx]
+        if x is None:
+            assert name in ("dg_log", "dS0") and (name != "dg_log" or got["dg_log"] is None)
+            continue
+        num = np.zeros(x.shape)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += f32(h)
+            xm[pos] -= f32(h)
+            assert float(xp[pos]) - float(x[pos]) == h  # exact perturbation
+            ip, im = list(inp), list(inp)
+            ip[idx], im[idx] = xp, xm
+            num[pos] = (_loss(ip, dO, dS, n_h, scale) - _loss(im, dO, dS, n_h, scale)) / (2 * h)
+        err = np.max(np.abs(num - got[name])) / max(1.0, np.max(np.abs(num)))
+        assert err < 1e-6, (name, err)
+
+
+def test_bwd_one_token_closed_form():
+    """One token, n_h = 1, gate g, state S0: S = g S0 + beta k (v - g S0^T k)^T, o = scale S^T q.
+    The gradients written out by hand for <o, do>:
+      dq = scale S do;  dv = scale beta (k.q) do;  dbeta = scale (k.q) (e.do), e = v - g S0^T k;
+      dk = scale beta [(e.do) q - (k.q) g S0 do];  dlog g = scale [<S0, q do^T> g - beta (k.q) g (S0^T k).do];
+      dS0 = scale g [q do^T - beta k (k.q) do^T]."""
+    r = rnd(77)
+    dk, dv = 4, 3
+    q = r.standard_normal((1, 1, 1, dk)).astype(f32)
+    k = r.standard_normal((1, 1, 1, dk)).astype(f32)
+    v = r.standard_normal((1, 1, 1, dv)).astype(f32)
+    beta = np.array([[[0.6]]], f32)
+    glog = np.array([[[-0.4]]], f32)
+    S0 = r.standard_normal((1, 1, dk, dv)).astype(f32)
+    do = r.standard_normal((1, 1, 1, dv)).astype(f32)
+    scale = 1.3
+    got = oracle.bwd(q, k, v, beta, glog, S0, do, None, n_h=1, scale=scale)
+    Q, K, V, D = (x.astype(np.float64).ravel() for x in (q, k, v, do))
+    Z = S0[0, 0].astype(np.float64)
+    g, b = np.exp(np.float64(glog.ravel()[0])), np.float64(beta.ravel()[0])
+    e = V - g * Z.T @ K
+    S = g * Z + b * np.outer(K, e)
+    kq = K @ Q
+    want = {
+        "dq": scale * S @ D,
+        "dv": scale * b * kq * D,
+        "dbeta": scale * kq * (e @ D),
+        "dk": scale * b * ((e @ D) * Q - kq * g * (Z @ D)),
+        "dg_log": scale * (g * (Q @ Z @ D) - b * kq * g * ((Z.T @ K) @ D)),
+        "dS0": scale * g * (np.outer(Q, D) - b * kq * np.outer(K, D)),
+    }
+    for name, w in want.items():
+        assert np.allclose(np.asarray(got[name]).ravel(), np.asarray(w).ravel(), rtol=1e-12, atol=1e-12), name
