@@ -190,3 +190,99 @@ def one_chunk_closed_form(q, k, v, beta):
     A = np.tril(bt[:, None] * (K @ K.T), -1)
     T = scipy.linalg.solve_triangular(np.eye(C) + A, np.diag(bt), lower=True, unit_diagonal=True)
     return np.tril(Q @ K.T) @ T @ V
+
+
+def chunked_bwd(q, k, v, beta, g_log=None, S0=None, dO=None, dS_final=None, n_h=1, C=16, scale=1.0):
+    """Gradients of `chunked` for <O, dO> + <S_final, dS_final>, chunk by chunk, in fp64: the
+    chunkwise backward the GPU kernels are to compute.  Per chunk, with the forward's
+    Y = V - gam K S, V~ = T Y, T = N diag(beta), N = (I + A)^-1, O = (gam Q) S + (Q K^T * Gam) V~
+    and S' = gam_C S + K^T (w V~), w = gam_C / gam, given G' = dS' and dO (Q and dO rows only
+    at each token's last sub-step):
+        dV~ = w K G' + (Q K^T * Gam)^T dO,   dY = T^T dV~,   dT = dV~ Y^T,   dN = dT diag(beta)
+        dA  = -strictLower(N^T dN N^T),      dG = diag(beta) (Gam * dA)   (A = diag(beta)(Gam * K K^T))
+        dS  = gam_C G' - K^T (gam dY) + (gam Q)^T dO                    (carried to the previous chunk)
+        dQ  = gam (dO S^T) + (Gam * dO V~^T) K
+        dK  = -gam (dY S^T) + w (V~ G'^T) + (Gam * dO V~^T)^T Q + (dG + dG^T) K
+        dbeta = diag(N^T dT) + rowsum(dA * Gam * K K^T),   dV = dY
+    and the log-gate prefix gc (gam = exp(gc)) collects every gamma-dependent factor; the log
+    gates are its reverse cumulative sum within the chunk (at each token's first sub-step)."""
+    q, k, v, beta, g_log, S0, dO, dS_final = map(_f64, (q, k, v, beta, g_log, S0, dO, dS_final))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    Lx = L * n_h
+    NT = -(-Lx // C)
+    out = {"dq": np.zeros((B, L, H, dk)), "dk": np.zeros((B, Lx, H, dk)), "dv": np.zeros((B, Lx, H, dv)),
+           "dbeta": np.zeros((B, Lx, H)), "dg_log": np.zeros((B, L, H)), "dS0": np.zeros((B, H, dk, dv))}
+    for b in range(B):
+        for h in range(H):
+            # forward, keeping each chunk's start state and pieces
+            S = np.zeros((dk, dv)) if S0 is None else S0[b, h].copy()
+            saved = []
+            for n in range(NT):
+                pos = np.arange(n * C, min((n + 1) * C, Lx))
+                c = len(pos)
+                K, V, bt = k[b, pos, h], v[b, pos, h], beta[b, pos, h]
+                lg = np.zeros(c)
+                first = (pos % n_h) == 0
+                if g_log is not None:
+                    lg[first] = g_log[b, pos[first] // n_h, h]
+                gc = np.cumsum(lg)
+                gam = np.exp(gc)
+                lower = np.tril(np.ones((c, c), dtype=bool))
+                Gam = np.exp(np.where(lower, gc[:, None] - gc[None, :], -np.inf))
+                Gm = K @ K.T
+                A = np.tril(bt[:, None] * Gam * Gm, -1)
+                N = _forward_substitution_inverse(A)
+                T = N * bt[None, :]
+                Y = V - gam[:, None] * (K @ S)
+                Vt = T @ Y
+                last = (pos % n_h) == n_h - 1
+                Qf = np.zeros((c, dk))
+                Qf[last] = q[b, pos[last] // n_h, h] * scale
+                w = np.exp(gc[-1] - gc)
+                saved.append((pos, K, V, bt, lg, gc, gam, Gam, Gm, N, T, Y, Vt, Qf, last, first, w, S.copy()))
+                S = gam[-1] * S + (w[:, None] * K).T @ Vt
+            # backward over chunks, last first
+            G = np.zeros((dk, dv)) if dS_final is None else dS_final[b, h].copy()
+            for n in range(NT - 1, -1, -1):
+                pos, K, V, bt, lg, gc, gam, Gam, Gm, N, T, Y, Vt, Qf, last, first, w, Sn = saved[n]
+                c = len(pos)
+                dOc = np.zeros((c, dv))
+                if dO is not None:
+                    dOc[last] = dO[b, pos[last] // n_h, h]
+                QK = (Qf @ K.T) * Gam
+                dVt = w[:, None] * (K @ G) + QK.T @ dOc
+                dY = T.T @ dVt
+                dT = dVt @ Y.T
+                dN = dT * bt[None, :]
+                dA = -np.tril(N.T @ dN @ N.T, -1)
+                dGm = bt[:, None] * Gam * dA
+                dOV = dOc @ Vt.T                                   # (dO V~^T)
+                dQf = gam[:, None] * (dOc @ Sn.T) + (Gam * dOV) @ K
+                dK = (-gam[:, None] * (dY @ Sn.T) + w[:, None] * (Vt @ G.T) + (Gam * dOV).T @ Qf
+                      + (dGm + dGm.T) @ K)
+                dbeta = np.diag(N.T @ dT) + np.sum(dA * Gam * Gm, axis=1)
+                # the log-gate prefix: every factor that depends on gc
+                dgc = np.zeros(c)
+                dgc += gam * np.sum(-(K @ Sn) * dY, axis=1)           # Y = V - gam K S
+                dgc += gam * np.sum((Qf @ Sn) * dOc, axis=1)          # O's gam Q S
+                dGam = np.where(np.tril(np.ones((c, c), dtype=bool), -1), bt[:, None] * Gm * dA, 0.0)
+                dGam += (Qf @ K.T) * dOV * np.tril(np.ones((c, c)))  # O's (Q K^T * Gam) V~
+                t = Gam * dGam
+                dgc += t.sum(axis=1) - t.sum(axis=0)
+                dw = np.sum((K @ G) * Vt, axis=1)                     # S' = gam_C S + K^T (w V~)
+                dgc[-1] += gam[-1] * np.sum(G * Sn) + np.sum(w * dw)
+                dgc -= w * dw
+                dlg = np.cumsum(dgc[::-1])[::-1]
+                # carry the state gradient to the previous chunk
+                G = gam[-1] * G - K.T @ (gam[:, None] * dY) + (gam[:, None] * Qf).T @ dOc
+                out["dk"][b, pos, h] = dK
+                out["dv"][b, pos, h] = dY
+                out["dbeta"][b, pos, h] = dbeta
+                out["dq"][b, pos[last] // n_h, h] = dQf[last] * scale
+                if g_log is not None:
+                    out["dg_log"][b, pos[first] // n_h, h] = dlg[first]
+            out["dS0"][b, h] = G
+    if g_log is None:
+        out["dg_log"] = None
+    return out
