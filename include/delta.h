@@ -73,8 +73,9 @@ typedef struct delta_shape {
  * Bytes of device workspace delta_fwd needs for this shape (a function of the shape only).
  * Holds, per chunk, the UT-transform matrix T (C x C in the input dtype) and the in-chunk
  * cumulative log gate; and, when the sequence is split into
- * segments (see delta_fwd_segments), each segment's summary (float32 d_k x (d_v + d_k): its
- * state run from zero and its d_k x d_k transition) and start state (float32 d_k x d_v).
+ * segments (see delta_fwd_segments), each segment's summary (a slot of d_k x (d_v + d_k)
+ * floats: its state run from zero in float32 and its d_k x d_k transition in the input dtype)
+ * and start state (float32 d_k x d_v).
  * Returns DELTA_OK and sets *bytes, or an error code.
  */
 int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes);
