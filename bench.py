@@ -462,7 +462,7 @@ def main():
                 continue
             try:
                 wo = W.get(name)
-                ro = time_prefill(wo, max(5, args.steps // 5), 2)
+                ro = time_prefill(wo, max(20, args.steps // 2), 3)
                 others[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1), "ms_per_step": round(ro["ms_per_step"], 5),
                                 "graph_tokens_per_s": round(ro["graph_tokens_per_s"], 1),
                                 "median_call_ms": {k: round(v, 5) for k, v in ro["median_call_ms"].items()},
