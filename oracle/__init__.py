@@ -11,12 +11,14 @@ fwd(...)        the token-by-token recurrence in fp64 (oracle.c); the definition
                 of what delta_fwd and delta_decode compute.
 bwd(...)        its gradients by reverse-mode differentiation of the same recurrence
                 (oracle.c), for the backward pass.
+fwd_kda(...)    the KDA recurrence (per-key-channel decay, then the delta-rule write),
+                in fp64 (oracle.c); decode_kda is its one-token step.
 ut_factors(...) the per-chunk UT transform T = (I + strictLower(diag(beta)
                 (Gamma * K K^T)))^-1 diag(beta) and the WY factors
                 W = T (gamma * K), U = T V, written from their definitions with a
                 library triangular solve (what delta_chunk_wy computes).
 
-All three are pinned in tests/test_oracle_pins.py (closed forms, brute force,
+All of them are pinned in tests/test_oracle_pins.py (closed forms, brute force,
 independent formulations, finite differences); none is "parity unpinned".
 """
 from __future__ import annotations
@@ -55,6 +57,8 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_bwd.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] + [P] * 14 + [ctypes.c_int]
         lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_fwd_kda.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double] + [P] * 8 + [ctypes.c_int]
+        lib.oracle_fwd_kda.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -121,6 +125,32 @@ def bwd(q, k, v, beta, g_log, S0, dO, dS_final=None, n_h: int = 1, scale: float 
     if rc != 0:
         raise RuntimeError("oracle_bwd failed (%d)" % rc)
     return out
+
+
+def fwd_kda(q, k, v, beta, a_log, S0=None, scale: float = 1.0, nthreads: int = 0):
+    """The KDA recurrence in fp64 (oracle.c, oracle_fwd_kda): per token, the state's key
+    channels decay by exp(a_log) (vector), then the delta-rule write, then the readout.
+    q, k [B,L,H,dk], v [B,L,H,dv], beta [B,L,H], a_log [B,L,H,dk], S0 [B,H,dk,dv] or None.
+    Returns (O, S_final) in fp64."""
+    q, k, v, beta, a_log, S0 = map(_f32, (q, k, v, beta, a_log, S0))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, L, H, dk) and v.shape == (B, L, H, dv) and beta.shape == (B, L, H)
+    assert a_log.shape == (B, L, H, dk)
+    assert S0 is None or S0.shape == (B, H, dk, dv)
+    O = np.empty((B, L, H, dv))
+    S_final = np.empty((B, H, dk, dv))
+    rc = _load().oracle_fwd_kda(B, L, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                _ptr(a_log), _ptr(S0), _ptr(O), _ptr(S_final), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_fwd_kda failed (%d)" % rc)
+    return O, S_final
+
+
+def decode_kda(q, k, v, beta, a_log, S, scale: float = 1.0):
+    """One KDA decode step per (b, h): q, k [B,1,H,dk], v [B,1,H,dv], beta [B,1,H],
+    a_log [B,1,H,dk], S [B,H,dk,dv].  Returns (O [B,1,H,dv], S_new) in fp64."""
+    return fwd_kda(q, k, v, beta, a_log, S, scale=scale)
 
 
 def decode(q, k, v, beta, g_log, S, n_h: int = 1, scale: float = 1.0):

@@ -118,6 +118,66 @@ int oracle_fwd(int B, int L, int H, int dk, int dv, int nh, double scale,
 }
 
 /*
+ * oracle_fwd_kda -- the KDA recurrence ("08 linear delta rule & DPLR" page, section 1.4 table
+ * and section 5: S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T with a
+ * decay per key channel, the diagonal applied first, then the Householder write), in fp64:
+ *
+ *   S <- S0 (or 0)
+ *   for each token i:
+ *       S[r][:] <- alpha_i[r] * S[r][:]                 (row r of S is key channel r)
+ *       e <- v_i - S^T k_i;   S <- S + beta_i k_i e^T
+ *       o_i <- scale * S^T q_i
+ *
+ * a_log [B, L, H, dk] float32 holds log alpha (exponentiated here in fp64).  One sub-step per
+ * token.  Other arguments and layouts as oracle_fwd (n_h = 1).  Returns 0, or -1.
+ * Pins: tests/test_oracle_pins.py (the page's DPLR reduction of KDA; equal channels give the
+ * scalar-gated oracle_fwd; a zero channel decay erases that row of the state).
+ */
+int oracle_fwd_kda(int B, int L, int H, int dk, int dv, double scale,
+                   const float* q, const float* k, const float* v, const float* beta,
+                   const float* a_log, const float* S0, double* O, double* S_final, int nthreads) {
+    if (B < 0 || L < 0 || H <= 0 || dk <= 0 || dv <= 0 || !a_log) return -1;
+    int fail = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+#endif
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !e) { free(S); free(e); fail |= 1; continue; }
+        for (size_t x = 0; x < (size_t)dk * dv; ++x) S[x] = S0 ? (double)S0[((size_t)b * H + h) * dk * dv + x] : 0.0;
+        for (long i = 0; i < L; ++i) {
+            const size_t row = ((size_t)b * L + i) * H + h;   /* token-head index */
+            for (int r = 0; r < dk; ++r) {
+                const double a = exp((double)a_log[row * dk + r]);
+                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= a;
+            }
+            const float* ki = k + row * dk;
+            const float* vi = v + row * dv;
+            const double bt = (double)beta[row];
+            for (int c = 0; c < dv; ++c) e[c] = (double)vi[c];
+            for (int r = 0; r < dk; ++r)
+                for (int c = 0; c < dv; ++c) e[c] -= S[(size_t)r * dv + c] * (double)ki[r];
+            for (int r = 0; r < dk; ++r)
+                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] += bt * (double)ki[r] * e[c];
+            const float* qi = q + row * dk;
+            double* oi = O + row * dv;
+            for (int c = 0; c < dv; ++c) {
+                double a = 0.0;
+                for (int r = 0; r < dk; ++r) a += S[(size_t)r * dv + c] * (double)qi[r];
+                oi[c] = scale * a;
+            }
+        }
+        if (S_final) memcpy(S_final + ((size_t)b * H + h) * (size_t)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+        free(S);
+        free(e);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
  * oracle_bwd -- gradients of the forward pass above, by reverse-mode differentiation of the
  * same recurrence, in fp64, with every intermediate state stored (no chunking).
  *

@@ -97,3 +97,40 @@ def test_planted_backward_mistake_is_caught(name, tmp_path, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught >= 1, name
+
+
+# slips in the KDA recurrence (oracle_fwd_kda), each caught by its pins
+KDA_MUTANTS = {
+    "kda_decay_on_columns": ("const double a = exp((double)a_log[row * dk + r]);\n                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= a;",
+                             "for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= exp((double)a_log[row * dk + c % dk]);"),
+    "kda_decay_twice": ("            const float* qi = q + row * dk;\n            double* oi = O + row * dv;",
+                              "            for (int r = 0; r < dk; ++r) for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= exp((double)a_log[row * dk + r]) / exp((double)a_log[row * dk + r]) * exp((double)a_log[row * dk + r]);\n            const float* qi = q + row * dk;\n            double* oi = O + row * dv;"),
+}
+
+KDA_PINS = [P.test_kda_dplr_reduction, P.test_kda_equal_channels_is_gated_deltanet,
+            P.test_kda_zero_channel_decay_erases_row]
+
+
+@pytest.mark.parametrize("name", sorted(KDA_MUTANTS))
+def test_planted_kda_mistake_is_caught(name, tmp_path, monkeypatch):
+    a, b = KDA_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(a) == 1, name
+    (tmp_path / "m.c").write_text(src.replace(a, b))
+    so = tmp_path / "libm.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(tmp_path / "m.c"),
+                    "-lm"], check=True)
+    oracle._load()
+    import ctypes
+    lib = ctypes.CDLL(str(so))
+    for f in ("oracle_fwd", "oracle_fwd_kda"):
+        getattr(lib, f).argtypes = getattr(oracle._lib, f).argtypes
+        getattr(lib, f).restype = ctypes.c_int
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = 0
+    for pin in KDA_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, name

@@ -572,3 +572,54 @@ def test_chunked_backward_matches_oracle_bwd(n_h, C, gate, s0):
             continue
         err = np.max(np.abs(got[name] - want[name])) / max(1.0, np.max(np.abs(want[name])))
         assert err < 1e-10, (name, err)
+
+
+# ---------------------------------------------------------------- KDA (oracle.fwd_kda)
+
+def _kda_inputs(seed, B=2, L=9, H=2, dk=6, dv=5, s0=True):
+    r = rnd(seed)
+    q = unit(r.standard_normal((B, L, H, dk))).astype(f32)
+    k = unit(r.standard_normal((B, L, H, dk))).astype(f32)
+    v = r.standard_normal((B, L, H, dv)).astype(f32)
+    beta = r.uniform(0.05, 1.0, (B, L, H)).astype(f32)
+    a = (-np.logaddexp(0, r.standard_normal((B, L, H, dk)) - 1.0)).astype(f32)
+    S0 = (0.5 * r.standard_normal((B, H, dk, dv))).astype(f32) if s0 else None
+    return q, k, v, beta, a, S0
+
+
+def test_kda_dplr_reduction():
+    """Delta-rule/DPLR page, section 5: KDA = DPLR(w = log alpha (vector), a = -beta k,
+    b = alpha * k, beta k v^T) — the diagonal decay applied before the low-rank erase (the page
+    reports <= 5.2e-16 for this reduction)."""
+    q, k, v, beta, a, S0 = _kda_inputs(120)
+    O, S = oracle.fwd_kda(q, k, v, beta, a, S0, scale=0.7)
+    bv = beta[..., None].astype(np.float64)
+    k64, a64 = k.astype(np.float64), a.astype(np.float64)
+    Od, Sd = F.dplr(q, a64, -bv * k64, k64 * np.exp(a64), bv * k64, v, S0, scale=0.7)
+    assert np.abs(O - Od).max() < 1e-12 and np.abs(S - Sd).max() < 1e-12
+
+
+def test_kda_equal_channels_is_gated_deltanet():
+    """With the same decay on every key channel KDA is Gated DeltaNet (same page, section 1.4
+    table): fwd_kda with a_log = g for all channels equals fwd with the scalar log gate g."""
+    q, k, v, beta, _, S0 = _kda_inputs(121)
+    g = (-np.logaddexp(0, rnd(122).standard_normal(beta.shape) - 1.0)).astype(f32)
+    a = np.repeat(g[..., None], q.shape[-1], axis=-1)
+    O1, S1 = oracle.fwd_kda(q, k, v, beta, a, S0)
+    O2, S2 = oracle.fwd(q, k, v, beta, g, S0)
+    assert np.abs(O1 - O2).max() < 1e-13 and np.abs(S1 - S2).max() < 1e-13
+
+
+def test_kda_zero_channel_decay_erases_row():
+    """alpha_r = 0 (log alpha = -inf) erases key channel r of the state before the write: after
+    one token S[r] = beta k_r e with e = v - (Diag(alpha) S0)^T k, and row r of S0 is gone."""
+    q, k, v, beta, a, S0 = _kda_inputs(123, B=1, L=1, H=1)
+    a = a.copy()
+    a[0, 0, 0, 2] = -np.inf
+    _, S = oracle.fwd_kda(q, k, v, beta, a, S0)
+    al = np.exp(a[0, 0, 0].astype(np.float64))
+    Sd = al[:, None] * S0[0, 0].astype(np.float64)
+    assert np.all(Sd[2] == 0.0)
+    e = v[0, 0, 0].astype(np.float64) - Sd.T @ k[0, 0, 0].astype(np.float64)
+    want = Sd + float(beta[0, 0, 0]) * np.outer(k[0, 0, 0].astype(np.float64), e)
+    assert np.allclose(S[0, 0], want, rtol=1e-13, atol=1e-14)
