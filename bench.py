@@ -152,10 +152,13 @@ KERNELS = {  # phase -> (kernel symbol substring, bytes, flops)
 }
 
 
-def decode_bytes(w) -> int:
+def decode_bytes(w, kda=False) -> int:
+    """State read and written once, q, k, v, O, beta, and the gate (a float per head, or per key
+    channel for KDA)."""
     es = 2 if w.dtype == "bf16" else 4
     BH = w.B * w.H
-    return BH * (2 * w.dk * w.dv * 4 + (w.dk + w.n_h * (w.dk + w.dv) + w.dv) * es + w.n_h * 4 + (4 if w.gate else 0))
+    gate = w.dk * 4 if kda else (4 if w.gate else 0)
+    return BH * (2 * w.dk * w.dv * 4 + (w.dk + w.n_h * (w.dk + w.dv) + w.dv) * es + w.n_h * 4 + gate)
 
 
 # ------------------------------------------------------------------ timing
@@ -301,11 +304,12 @@ def roofline_of(w, r):
             "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / mfma_peak, 4)}
 
 
-def time_decode(w, steps, n_states=8):
+def time_decode(w, steps, n_states=8, kda=False):
     """`steps` back-to-back decode calls cycling over n_states independent states (8 x 64 MiB
     exceeds the 256 MB Infinity Cache, so each step streams its state from HBM); the same loop on
     one state (warm); the cold loop replayed from a HIP graph; and, as the practical ceiling of a
-    step that reads and writes its state once, a plain device copy of the same volume."""
+    step that reads and writes its state once, a plain device copy of the same volume.  kda: the
+    KDA step (delta_decode_kda, a decay per key channel) instead."""
     import torch
     import chunkwise_delta_rule_chunked_amd as D
     import workloads as W
@@ -319,11 +323,16 @@ def time_decode(w, steps, n_states=8):
         steps_in.append({kk: (None if vv is None else torch.from_numpy(vv).to(torch.float32 if kk in ("beta", "g_log")
                                                                               else dt).cuda())
                          for kk, vv in x.items()})
+        if kda:
+            steps_in[-1]["a_log"] = torch.from_numpy(W.make_kda_decay(w, t)).cuda()
     O = torch.empty((w.B, 1, w.H, w.dv), dtype=dt, device="cuda")
 
     def run(i, S):
         x = steps_in[i]
-        D.decode(x["q"], x["k"], x["v"], x["beta"], x["g_log"], S, n_h=w.n_h, O=O)
+        if kda:
+            D.decode_kda(x["q"], x["k"], x["v"], x["beta"], x["a_log"], S, O=O)
+        else:
+            D.decode(x["q"], x["k"], x["v"], x["beta"], x["g_log"], S, n_h=w.n_h, O=O)
 
     for i in range(min(5, steps)):
         run(i, states[i % n_states])
@@ -338,7 +347,7 @@ def time_decode(w, steps, n_states=8):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1)
     per_step_us = ms * 1e3 / steps
-    gbs = decode_bytes(w) / (per_step_us * 1e-6) / 1e9
+    gbs = decode_bytes(w, kda) / (per_step_us * 1e-6) / 1e9
     # the same loop on one state (warm: it stays in the Infinity Cache)
     e0.record()
     for i in range(steps):
@@ -377,7 +386,7 @@ def time_decode(w, steps, n_states=8):
     return {"us_per_step": round(per_step_us, 3), "tokens_per_s": w.B * steps / (ms * 1e-3),
             "wall_tokens_per_s": w.B * steps / wall, "achieved_GBs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "warm_us_per_step": round(warm_us, 3),
-            "warm_GBs": round(decode_bytes(w) / (warm_us * 1e-6) / 1e9, 1),
+            "warm_GBs": round(decode_bytes(w, kda) / (warm_us * 1e-6) / 1e9, 1),
             "graph_us_per_step": round(graph_us, 3), "graph_tokens_per_s": round(w.B / (graph_us * 1e-6), 1),
             "state_copy_us": round(copy_us, 3),
             "state_copy_GBs": round(2 * nel * 4 / (copy_us * 1e-6) / 1e9, 1)}
@@ -474,6 +483,9 @@ def main():
             dec = time_decode(W.DECODE, W.DECODE_STEPS)
             others[W.DECODE.name] = dec
             log("[bench] decode: %s" % dec)
+            kd = time_decode(W.DECODE, W.DECODE_STEPS, kda=True)
+            others["kda_" + W.DECODE.name] = kd
+            log("[bench] kda decode: %s" % kd)
         except Exception as e:
             others[W.DECODE.name] = {"error": repr(e)}
         line["others"] = others

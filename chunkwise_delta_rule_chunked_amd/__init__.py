@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "fwd_intra", "fwd_inter", "decode", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -67,10 +67,11 @@ def load_library():
     lib.delta_fwd_scan_outputs.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_chunk_wy.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
+    lib.delta_decode_kda.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_strerror.argtypes = [ctypes.c_int]
     lib.delta_strerror.restype = ctypes.c_char_p
     for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_intra, lib.delta_fwd_inter,
-              lib.delta_chunk_wy, lib.delta_decode):
+              lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -278,4 +279,24 @@ def decode(q, k, v, beta, g_log, S, *, n_h: int = 1, scale: float = 1.0, O=None,
                           _dev(beta, "beta", torch.float32), _dev(g_log, "g_log", torch.float32),
                           _dev(S, "S", torch.float32), _dev(O, "O", q.dtype), _stream(stream))
     _check(rc, "delta_decode")
+    return O
+
+
+def decode_kda(q, k, v, beta, a_log, S, *, scale: float = 1.0, O=None, stream=None):
+    """One KDA step per (b, h) (per-key-channel decay exp(a_log) of the state's rows, then the
+    delta-rule write and the readout); a_log [B,1,H,dk] fp32, S [B,H,dk,dv] fp32 updated in
+    place.  Returns O [B,1,H,dv]."""
+    torch = _torch()
+    lib = load_library()
+    B, one, H, dk = q.shape
+    if one != 1:
+        raise ValueError("decode_kda takes one token: q must be [B, 1, H, dk]")
+    dv = v.shape[-1]
+    sh = make_shape(B, 1, H, dk, dv, 1, 64, _dtype_code(q), scale)
+    if O is None:
+        O = torch.empty((B, 1, H, dv), dtype=q.dtype, device=q.device)
+    rc = lib.delta_decode_kda(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+                              _dev(beta, "beta", torch.float32), _dev(a_log, "a_log", torch.float32),
+                              _dev(S, "S", torch.float32), _dev(O, "O", q.dtype), _stream(stream))
+    _check(rc, "delta_decode_kda")
     return O

@@ -1,9 +1,10 @@
 // Recurrent decode kernel: one token per (b, h), state updated in place.
 //
 // Sources: "08 linear delta rule & DPLR" page, recurrent reference after section 2.3
-// (read v_old = S^T k, write beta k (v - v_old)^T, output S^T q) and section 3 (scalar
-// gate applied to the state first); DeltaProduct notes, section 2.6 pseudocode (gate,
-// then n_h ordered residual writes, then the readout).
+// (read v_old = S^T k, write beta k (v - v_old)^T, output S^T q), section 3 (scalar
+// gate applied to the state first) and sections 1.4 / 5 (KDA: a decay per key channel,
+// Diag(alpha) applied to the state's rows before the write); DeltaProduct notes, section 2.6
+// pseudocode (gate, then n_h ordered residual writes, then the readout).
 //
 // The step is bound by HBM traffic: the d_k x d_v fp32 state is read once and written
 // once.  One workgroup owns a d_k x SW column slab of one head's state (columns are
@@ -70,6 +71,12 @@ __global__ __launch_bounds__(DK * SW / 16) void decode_kernel(DecodeParams p) {
     const float g = expf(p.g_log[(long)b * p.H + h]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] *= g;
+  }
+  if (p.a_log) {
+    // KDA: each key channel (row of S) decays by its own factor before the write
+    const float* ah = p.a_log + ((long)b * p.H + h) * DK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] *= expf(ah[rg + RG * i]);
   }
 
   float qr[4];

@@ -313,8 +313,10 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
   return DELTA_OK;
 }
 
-int delta_decode(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
-                 const float* g_log, float* S, void* O, void* stream) {
+namespace {
+// A decode step with a scalar gate (g_log) or a per-key-channel one (a_log, KDA).
+int run_decode(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+               const float* g_log, const float* a_log, float* S, void* O, void* stream) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (s->L != 1) return DELTA_ERR_BAD_SHAPE;
@@ -322,12 +324,12 @@ int delta_decode(const delta_shape* s, const void* q, const void* k, const void*
   const void* ptrs[] = {q, k, v, S, O};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
-  if (!aligned(beta, 4) || !aligned(g_log, 4)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4) || !aligned(g_log, 4) || !aligned(a_log, 4)) return DELTA_ERR_MISALIGNED;
   const size_t es = esize(s->dtype);
   const size_t BH = (size_t)s->B * s->H;
   const Range in[] = {range(q, BH * s->dk * es), range(k, BH * s->n_h * s->dk * es),
                       range(v, BH * s->n_h * s->dv * es), range(beta, BH * s->n_h * 4),
-                      range(g_log, g_log ? BH * 4 : 0)};
+                      range(g_log, g_log ? BH * 4 : 0), range(a_log, a_log ? BH * s->dk * 4 : 0)};
   const Range rS = range(S, BH * s->dk * s->dv * 4), rO = range(O, BH * s->dv * es);
   for (const Range& r : in)
     if (overlap(rS, r) || overlap(rO, r)) return DELTA_ERR_ALIAS;
@@ -346,9 +348,25 @@ int delta_decode(const delta_shape* s, const void* q, const void* k, const void*
   p.v = v;
   p.beta = beta;
   p.g_log = g_log;
+  p.a_log = a_log;
   p.S = S;
   p.O = O;
   return hip_status(delta::launch_decode(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int delta_decode(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+                 const float* g_log, float* S, void* O, void* stream) {
+  return run_decode(s, q, k, v, beta, g_log, nullptr, S, O, stream);
+}
+
+int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+                     const float* a_log, float* S, void* O, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->n_h != 1) return DELTA_ERR_BAD_SHAPE;
+  if ((size_t)s->B * s->H > 0 && !a_log) return DELTA_ERR_NULL_ARG;
+  return run_decode(s, q, k, v, beta, nullptr, a_log, S, O, stream);
 }
 
 const char* delta_strerror(int code) {

@@ -39,6 +39,7 @@ struct DecodeParams {
   const void* v;        // [B, nh, H, DV]
   const float* beta;    // [B, nh, H]
   const float* g_log;   // [B, 1, H] or nullptr
+  const float* a_log;   // [B, 1, H, DK] per-key-channel log decay (KDA) or nullptr
   float* S;             // [B, H, DK, DV], in place
   void* O;              // [B, 1, H, DV]
 };

@@ -173,6 +173,19 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
 int delta_decode(const delta_shape* s, const void* q, const void* k, const void* v,
                  const float* beta, const float* g_log, float* S, void* O, void* stream);
 
+/*
+ * KDA decode step: the delta rule with a decay per key channel ("08 linear delta rule & DPLR",
+ * section 1.4 table and section 5: S <- (I - beta k k^T) Diag(alpha) S + beta k v^T, the
+ * diagonal applied first), one token per (b, h), the state updated in place.  As delta_decode
+ * with n_h = 1 (s->n_h must be 1), the scalar gate replaced by
+ *   a_log [B, 1, H, dk] float32: log alpha per key channel (row r of S decays by
+ *                                exp(a_log[.., r])), finite or -inf, <= 0; not NULL.
+ * Same argument checks and error codes as delta_decode; a_log must be 4-byte aligned and may
+ * not overlap S or O.
+ */
+int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const void* v,
+                     const float* beta, const float* a_log, float* S, void* O, void* stream);
+
 /* Static description of a return code. */
 const char* delta_strerror(int code);
 

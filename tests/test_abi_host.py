@@ -23,7 +23,8 @@ def test_exports_every_header_function(lib):
     names = D.header_functions()
     assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_intra", "delta_fwd_inter",
                           "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
-                          "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_strerror"}
+                          "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_decode_kda",
+                          "delta_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,6 +153,18 @@ def test_decode_argument_errors(lib, no_gpu):
     assert L.delta_decode(ctypes.byref(sh), None, *f[1:5], f[5], f[6], None) == -1   # q NULL
     assert L.delta_decode(ctypes.byref(sh), *f[:5], f[0], f[6], None) == -6          # S aliases q
     assert L.delta_decode(ctypes.byref(sh), *f[:5], ctypes.c_void_p(A * 6 + 4), f[6], None) == -4
+
+
+def test_decode_kda_argument_errors(lib, no_gpu):
+    L = D.load_library()
+    f = [fake(i) for i in range(7)]
+    sh = shape(L=1)
+    assert L.delta_decode_kda(ctypes.byref(sh), *f[:4], None, f[5], f[6], None) == -1    # a_log NULL
+    assert L.delta_decode_kda(ctypes.byref(shape(L=1, n_h=2, chunk=64)), *f[:5], f[5], f[6], None) == -2
+    assert L.delta_decode_kda(ctypes.byref(shape(L=2)), *f[:5], f[5], f[6], None) == -2   # L != 1
+    assert L.delta_decode_kda(ctypes.byref(sh), *f[:4], f[5], f[5], f[6], None) == -6     # a_log aliases S
+    assert L.delta_decode_kda(ctypes.byref(sh), *f[:4], ctypes.c_void_p(A * 4 + 2), f[5], f[6], None) == -4
+    assert L.delta_decode_kda(ctypes.byref(shape(B=0, L=1)), *[None] * 7, None) == 0       # empty
 
 
 def test_chunk_wy_argument_errors(lib, no_gpu):

@@ -362,3 +362,49 @@ def test_fwd_graph_replay():
         es = (Sg - Se).abs().max().item()
         say("  replay %d: |O - O_eager| %.3e, |S - S_eager| %.3e" % (rep, eo, es))
         assert eo == 0.0 and es == 0.0, (rep, eo, es)
+
+
+# ---------------------------------------------------------------- KDA decode (per-channel decay)
+
+def kda_sequence(w, S, steps):
+    """`steps` KDA decode calls on the GPU from state S; returns per-step O and the final S, and
+    the KDA oracle's O and S_final for the same tokens as one sequence."""
+    Sd = torch.from_numpy(S).cuda()
+    Os, stack, decays = [], [], []
+    for step in range(steps):
+        inp = W.make_decode_inputs(w, step)
+        a = W.make_kda_decay(w, step)
+        d = inputs_to_dev(dict(inp, S0=None), w.dtype)
+        Os.append(to_np(D.decode_kda(d["q"], d["k"], d["v"], d["beta"], torch.from_numpy(a).cuda(), Sd, scale=0.9)))
+        stack.append(inp)
+        decays.append(a)
+    torch.cuda.synchronize()
+    cat = lambda key: np.concatenate([x[key] for x in stack], axis=1)
+    Or, Sr = oracle.fwd_kda(cat("q"), cat("k"), cat("v"), cat("beta"), np.concatenate(decays, axis=1), S, scale=0.9)
+    return np.concatenate(Os, axis=1), Sd.cpu().numpy(), Or, Sr
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 128, 128), ("bf16", 128, 128), ("bf16", 16, 16), ("f32", 64, 48),
+                                      ("bf16", 32, 256)])
+def test_decode_kda_steps(dt, dk, dv):
+    w = W.Workload("kda", B=3, H=2, L=1, dk=dk, dv=dv, dtype=dt, gate="cfg3", s0=0.1, cfg_id=95)
+    say("case kda decode", w)
+    O, S, Or, Sr = kda_sequence(w, W.make_decode_state(w), steps=6)
+    eo, es = head_rel_err(O, Or, (0, 2)), head_rel_err(S, Sr, (0, 1))
+    say("  err O %.3e S %.3e" % (eo, es))
+    assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+def test_decode_kda_equal_channels_is_gated_decode():
+    """The same decay on every key channel is the scalar gate: delta_decode_kda with a_log = g
+    for all channels gives exactly what delta_decode gives with log gate g."""
+    w = W.Workload("kda_eq", B=2, H=3, L=1, dk=64, dv=64, dtype="bf16", gate="cfg3", s0=0.1, cfg_id=96)
+    S0 = torch.from_numpy(W.make_decode_state(w)).cuda()
+    S1, S2 = S0.clone(), S0.clone()
+    for step in range(3):
+        d = inputs_to_dev(dict(W.make_decode_inputs(w, step), S0=None), w.dtype)
+        a = d["g_log"][..., None].expand(w.B, 1, w.H, w.dk).contiguous()
+        O1 = D.decode(d["q"], d["k"], d["v"], d["beta"], d["g_log"], S1)
+        O2 = D.decode_kda(d["q"], d["k"], d["v"], d["beta"], a, S2)
+        torch.cuda.synchronize()
+        assert torch.equal(O1, O2) and torch.equal(S1, S2), step

@@ -176,6 +176,15 @@ def make_decode_inputs(w: Workload, step: int) -> dict:
             "beta": beta.astype(np.float32), "g_log": g_log}
 
 
+def make_kda_decay(w: Workload, step: int) -> np.ndarray:
+    """Per-key-channel log decay of decode step `step` for the KDA recurrence, [B, 1, H, dk]
+    float32: -softplus(N(0,1) + shift) per channel (the scalar gate's distribution, drawn for
+    every channel; shift as the workload's gate, cfg3 when it has none)."""
+    rng = _rng(w.cfg_id, 300 + step)
+    shift = {"cfg3": 2.0, "weak": -4.0}[w.gate or "cfg3"]
+    return (-_softplus(rng.standard_normal((w.B, 1, w.H, w.dk)) + shift)).astype(np.float32)
+
+
 def make_decode_state(w: Workload) -> np.ndarray:
     """Initial decode state S ~ s0 * N(0,1), [B, H, dk, dv] float32."""
     return (w.s0 * _rng(w.cfg_id, 5).standard_normal((w.B, w.H, w.dk, w.dv))).astype(np.float32)
