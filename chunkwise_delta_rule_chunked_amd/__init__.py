@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -68,10 +68,13 @@ def load_library():
     lib.delta_chunk_wy.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_decode_kda.argtypes = [SP, P, P, P, P, P, P, P, P]
+    lib.delta_bwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.delta_bwd.argtypes = [SP] + [P] * 15 + [ctypes.c_size_t, P]
     lib.delta_strerror.argtypes = [ctypes.c_int]
     lib.delta_strerror.restype = ctypes.c_char_p
     for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_intra, lib.delta_fwd_inter,
-              lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda):
+              lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda, lib.delta_bwd_workspace_bytes,
+              lib.delta_bwd):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -165,6 +168,52 @@ def fwd(q, k, v, beta, g_log=None, S0=None, *, n_h: int = 1, chunk: int = 64, sc
                        _stream(stream))
     _check(rc, "delta_fwd")
     return O, S_final
+
+
+def bwd_workspace_bytes(B, L, H, dk, dv, n_h=1, chunk=64, dtype=BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().delta_bwd_workspace_bytes(ctypes.byref(make_shape(B, L, H, dk, dv, n_h, chunk, dtype)),
+                                                    ctypes.byref(n)), "delta_bwd_workspace_bytes")
+    return n.value
+
+
+def bwd(q, k, v, beta, g_log=None, S0=None, dO=None, dS_final=None, *, n_h: int = 1, chunk: int = 64,
+        scale: float = 1.0, want_dS0: bool = True, grads=None, workspace=None, stream=None):
+    """Backward pass of fwd for the same arguments: returns a dict of float32 gradients dq, dk,
+    dv, dbeta, dg_log (None when g_log is None) and dS0 (None unless want_dS0).  dO (same dtype
+    as q) is required; dS_final (float32) may be None for zero.  `grads` may hold preallocated
+    outputs under the same names."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, L, H, d]")
+    if dO is None:
+        raise ValueError("dO is required")
+    B, L, H, dk = q.shape
+    Lx, dv = k.shape[1], v.shape[-1]
+    dt = _dtype_code(q)
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, dt, scale)
+    g = dict(grads or {})
+    f32, dev = torch.float32, q.device
+    shapes = {"dq": (B, L, H, dk), "dk": (B, Lx, H, dk), "dv": (B, Lx, H, dv), "dbeta": (B, Lx, H),
+              "dg_log": (B, L, H) if g_log is not None else None, "dS0": (B, H, dk, dv) if want_dS0 else None}
+    for name, shp in shapes.items():
+        if g.get(name) is None and shp is not None:
+            g[name] = torch.empty(shp, dtype=f32, device=dev)
+        g.setdefault(name, None)
+    if g_log is None:
+        g["dg_log"] = None
+    need = bwd_workspace_bytes(B, L, H, dk, dv, n_h, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.delta_bwd(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+                       _dev(beta, "beta", f32), _dev(g_log, "g_log", f32), _dev(S0, "S0", f32),
+                       _dev(dO, "dO", q.dtype), _dev(dS_final, "dS_final", f32), _dev(g["dq"], "dq", f32),
+                       _dev(g["dk"], "dk", f32), _dev(g["dv"], "dv", f32), _dev(g["dbeta"], "dbeta", f32),
+                       _dev(g["dg_log"], "dg_log", f32), _dev(g["dS0"], "dS0", f32), _dev(workspace, "workspace"),
+                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "delta_bwd")
+    return g
 
 
 def fwd_intra(k, beta, g_log, workspace, *, n_h: int = 1, chunk: int = 64, dv: int = None, stream=None):

@@ -1,0 +1,585 @@
+// Backward pass of the chunkwise delta rule: gradients of <O, dO> + <S_final, dS_final> with
+// respect to q, k, v, beta, the log gates and S0.
+//
+// The pages give the forward only ("08 linear delta rule & DPLR", sections 2.2-2.3 and 3:
+// per chunk Y = V - gam K S, V~ = T Y, O = (gam Q) S + (Q K^T * Gam) V~,
+// S' = gam_C S + K^T (w V~), w = gam_C / gam, T = (I + A)^-1 diag(beta),
+// A = strictLower(diag(beta) (Gam * K K^T))).  The gradients below are that forward
+// differentiated by hand, chunk by chunk; with N = (I + A)^-1 and G' the state gradient
+// after a chunk:
+//   dV~ = w (K G') + (Q K^T * Gam)^T dO            dY = T^T dV~ = dV
+//   G   = gam_C G' - K^T (gam dY) + (gam Q)^T dO   (state gradient before the chunk)
+//   dT  = dV~ Y^T,  dA = -strictLower(N^T dT T^T),  dGm = diag(beta) (Gam * dA)
+//   dQ  = gam (dO S^T) + (Gam * dO V~^T) K
+//   dK  = -gam (dY S^T) + w (V~ G'^T) + (Gam * dO V~^T)^T Q + (dGm + dGm^T) K
+//   dbeta = diag(N^T dT) + rowsum(dA * Gam * K K^T)
+// and every factor that depends on the in-chunk log-gate prefix gc adds to dgc, whose reverse
+// cumulative sum within the chunk is the log-gate gradient (taken at each token's first
+// sub-step).  Q and dO rows exist only at a token's last sub-step (DeltaProduct notes,
+// section 4.1); the readout scale is folded into Q.
+//
+// Three launches follow the intra-chunk launch (which leaves T in float32 and gc in the
+// workspace):
+//   bwd_states_kernel    one workgroup per (head, 16 state columns), chunks in order: stores
+//                        each chunk's start state S_n
+//   bwd_dstates_kernel   same split, chunks in reverse: stores each chunk's end-state gradient
+//                        G'_n, writes dV and dS0
+//   bwd_chunk_kernel     one workgroup per (head, chunk): everything that sums over the value
+//                        dimension (streamed in 16-column tiles of S_n and G'_n), then the
+//                        chunk-local C x C algebra, writes dq, dk, dbeta, dlog g
+// All arithmetic is float32 on the vector ALUs.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace delta {
+namespace {
+
+constexpr int CM = 64;   // largest chunk
+constexpr int NTH = 256; // threads per workgroup
+
+template <typename E>
+__device__ inline float ld(const void* p, long i) {
+  return to_float(static_cast<const E*>(p)[i]);
+}
+
+// Chunk rows i of a 16-column tile are owned by threads with (tid >> 4) == i % 16, column tid & 15.
+
+template <typename E, int DK>
+__global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
+  __shared__ float Kl[CM][DK + 1];
+  __shared__ float Tl[CM][CM + 1];
+  __shared__ float Sl[DK][17];
+  __shared__ float Yl[CM][17];
+  __shared__ float Vt[CM][17];
+  __shared__ float gam[CM], wl[CM];
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
+  const int ntile = p.DV / 16, c0 = (int)(blockIdx.x % ntile) * 16, bh = (int)(blockIdx.x / ntile);
+  const int b = bh / p.H, h = bh % p.H;
+  const int C = p.C, DV = p.DV;
+  constexpr int RD = DK / 16;
+  float S[RD];
+#pragma unroll
+  for (int u = 0; u < RD; ++u) S[u] = p.S0 ? p.S0[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] : 0.f;
+
+  for (int n = 0; n < p.NT; ++n) {
+    const long P0 = (long)n * C;
+    const int valid = (int)min((long)C, (long)p.Lx - P0);
+    const long chunk = (long)bh * p.NT + n;
+#pragma unroll
+    for (int u = 0; u < RD; ++u) {
+      p.Sn[(chunk * DK + r0 + 16 * u) * DV + c0 + c] = S[u];
+      Sl[r0 + 16 * u][c] = S[u];
+    }
+    for (int idx = tid; idx < C * DK; idx += NTH) {
+      const int i = idx / DK, d = idx % DK;
+      Kl[i][d] = i < valid ? ld<E>(p.k, ((b * (long)p.Lx + P0 + i) * p.H + h) * DK + d) : 0.f;
+    }
+    for (int idx = tid; idx < C * C; idx += NTH) Tl[idx / C][idx % C] = p.T[chunk * C * C + idx];
+    const float gC = p.gc[chunk * C + C - 1];
+    if (tid < C) {
+      const float g = p.gc[chunk * C + tid];
+      gam[tid] = expf(g);
+      wl[tid] = expf(gC - g);
+    }
+    __syncthreads();
+    // Y = V - gam K S
+    for (int i = r0; i < C; i += 16) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < DK; ++d) acc += Kl[i][d] * Sl[d][c];
+      const float vv = i < valid ? ld<E>(p.v, ((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c) : 0.f;
+      Yl[i][c] = vv - gam[i] * acc;
+    }
+    __syncthreads();
+    // V~ = T Y (T lower triangular)
+    for (int i = r0; i < C; i += 16) {
+      float acc = 0.f;
+      for (int j = 0; j <= i; ++j) acc += Tl[i][j] * Yl[j][c];
+      Vt[i][c] = acc;
+    }
+    __syncthreads();
+    // S <- gam_C S + K^T (w V~)
+    const float eC = expf(gC);
+#pragma unroll
+    for (int u = 0; u < RD; ++u) {
+      const int d = r0 + 16 * u;
+      float acc = 0.f;
+      for (int i = 0; i < C; ++i) acc += wl[i] * Kl[i][d] * Vt[i][c];
+      S[u] = eC * S[u] + acc;
+    }
+    __syncthreads();
+  }
+}
+
+template <typename E, int DK>
+__global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
+  __shared__ float Kl[CM][DK + 1];
+  __shared__ float Ql[CM][DK + 1];
+  __shared__ float Tl[CM][CM + 1];
+  __shared__ float Pl[CM][CM + 1];
+  __shared__ float Gl[DK][17];
+  __shared__ float dOl[CM][17];
+  __shared__ float dVt[CM][17];
+  __shared__ float dYl[CM][17];
+  __shared__ float gcl[CM], gam[CM], wl[CM];
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
+  const int ntile = p.DV / 16, c0 = (int)(blockIdx.x % ntile) * 16, bh = (int)(blockIdx.x / ntile);
+  const int b = bh / p.H, h = bh % p.H;
+  const int C = p.C, DV = p.DV, nh = p.nh;
+  constexpr int RD = DK / 16;
+  float G[RD];
+#pragma unroll
+  for (int u = 0; u < RD; ++u) G[u] = p.dS_final ? p.dS_final[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] : 0.f;
+
+  for (int n = p.NT - 1; n >= 0; --n) {
+    const long P0 = (long)n * C;
+    const int valid = (int)min((long)C, (long)p.Lx - P0);
+    const long chunk = (long)bh * p.NT + n;
+#pragma unroll
+    for (int u = 0; u < RD; ++u) {
+      p.Gn[(chunk * DK + r0 + 16 * u) * DV + c0 + c] = G[u];
+      Gl[r0 + 16 * u][c] = G[u];
+    }
+    for (int idx = tid; idx < C * DK; idx += NTH) {
+      const int i = idx / DK, d = idx % DK;
+      const long pos = P0 + i;
+      const bool last = i < valid && pos % nh == nh - 1;
+      Kl[i][d] = i < valid ? ld<E>(p.k, ((b * (long)p.Lx + pos) * p.H + h) * DK + d) : 0.f;
+      Ql[i][d] = last ? p.scale * ld<E>(p.q, ((b * (long)p.L + pos / nh) * p.H + h) * DK + d) : 0.f;
+    }
+    for (int idx = tid; idx < C * C; idx += NTH) Tl[idx / C][idx % C] = p.T[chunk * C * C + idx];
+    const float gC = p.gc[chunk * C + C - 1];
+    if (tid < C) {
+      const float g = p.gc[chunk * C + tid];
+      gcl[tid] = g;
+      gam[tid] = expf(g);
+      wl[tid] = expf(gC - g);
+    }
+    for (int i = r0; i < C; i += 16) {
+      const long pos = P0 + i;
+      const bool last = i < valid && pos % nh == nh - 1;
+      dOl[i][c] = last ? ld<E>(p.dO, ((b * (long)p.L + pos / nh) * p.H + h) * DV + c0 + c) : 0.f;
+    }
+    __syncthreads();
+    // P = Q K^T * Gam on and below the diagonal
+    for (int idx = tid; idx < C * C; idx += NTH) {
+      const int i = idx / C, j = idx % C;
+      float acc = 0.f;
+      if (j <= i) {
+#pragma unroll 8
+        for (int d = 0; d < DK; ++d) acc += Ql[i][d] * Kl[j][d];
+        acc *= expf(gcl[i] - gcl[j]);
+      }
+      Pl[i][j] = acc;
+    }
+    __syncthreads();
+    // dV~ = w (K G') + P^T dO
+    for (int i = r0; i < C; i += 16) {
+      float kg = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < DK; ++d) kg += Kl[i][d] * Gl[d][c];
+      float acc = wl[i] * kg;
+      for (int j = i; j < C; ++j) acc += Pl[j][i] * dOl[j][c];
+      dVt[i][c] = acc;
+    }
+    __syncthreads();
+    // dY = T^T dV~, which is dV
+    for (int i = r0; i < C; i += 16) {
+      float acc = 0.f;
+      for (int j = i; j < C; ++j) acc += Tl[j][i] * dVt[j][c];
+      dYl[i][c] = acc;
+      if (i < valid) p.dv[((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c] = acc;
+    }
+    __syncthreads();
+    // G <- gam_C G' - K^T (gam dY) + (gam Q)^T dO
+    const float eC = expf(gC);
+#pragma unroll
+    for (int u = 0; u < RD; ++u) {
+      const int d = r0 + 16 * u;
+      float acc = 0.f;
+      for (int i = 0; i < C; ++i) acc += gam[i] * (Ql[i][d] * dOl[i][c] - Kl[i][d] * dYl[i][c]);
+      G[u] = eC * G[u] + acc;
+    }
+    __syncthreads();
+  }
+  if (p.dS0) {
+#pragma unroll
+    for (int u = 0; u < RD; ++u) p.dS0[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] = G[u];
+  }
+}
+
+// Sum over the 16 lanes of a row group (lanes that share tid >> 4 within the wave).
+__device__ inline float sum16(float x) {
+  x += __shfl_xor(x, 8, 16);
+  x += __shfl_xor(x, 4, 16);
+  x += __shfl_xor(x, 2, 16);
+  x += __shfl_xor(x, 1, 16);
+  return x;
+}
+
+template <int DK>
+struct ChunkLds {
+  float K[CM][DK + 1];
+  float Q[CM][DK + 1];
+  float N[CM][CM + 1];  // (I + A)^-1
+  float P[CM][CM + 1];  // Q K^T * Gam, on and below the diagonal
+  union {
+    struct {  // one 16-column tile of the value dimension
+      float St[DK][17], Gt[DK][17];
+      float Y[CM][17], dO[CM][17], Vt[CM][17], dVt[CM][17], dY[CM][17];
+    } t;
+    struct {  // chunk-local C x C algebra
+      float R0[CM][CM + 1], R1[CM][CM + 1], R2[CM][CM + 1];
+    } m;
+  } u;
+  float gc[CM], gam[CM], w[CM], beta[CM], dbd[CM], dgc[CM], dw[CM], rsum[CM];
+  float sgs[NTH / WAVE];
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
+  __shared__ ChunkLds<DK> s;
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
+  const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
+  const int C = p.C, DV = p.DV, nh = p.nh, CU = C / 16;
+  constexpr int SD = DK / 16;
+  const long P0 = (long)n * C;
+  const int valid = (int)min((long)C, (long)p.Lx - P0);
+  const long chunk = (long)bh * p.NT + n;
+
+  for (int idx = tid; idx < C * DK; idx += NTH) {
+    const int i = idx / DK, d = idx % DK;
+    const long pos = P0 + i;
+    const bool last = i < valid && pos % nh == nh - 1;
+    s.K[i][d] = i < valid ? ld<E>(p.k, ((b * (long)p.Lx + pos) * p.H + h) * DK + d) : 0.f;
+    s.Q[i][d] = last ? p.scale * ld<E>(p.q, ((b * (long)p.L + pos / nh) * p.H + h) * DK + d) : 0.f;
+  }
+  const float gC = p.gc[chunk * C + C - 1];
+  if (tid < C) {
+    const float g = p.gc[chunk * C + tid];
+    s.gc[tid] = g;
+    s.gam[tid] = expf(g);
+    s.w[tid] = expf(gC - g);
+    s.beta[tid] = tid < valid ? p.beta[(b * (long)p.Lx + P0 + tid) * p.H + h] : 0.f;
+  }
+  __syncthreads();
+  // A = strictLower(diag(beta) (Gam * K K^T)) into R0, P into s.P
+  for (int idx = tid; idx < C * C; idx += NTH) {
+    const int i = idx / C, j = idx % C;
+    float kk = 0.f, qk = 0.f;
+    if (j <= i) {
+#pragma unroll 8
+      for (int d = 0; d < DK; ++d) {
+        kk += s.K[i][d] * s.K[j][d];
+        qk += s.Q[i][d] * s.K[j][d];
+      }
+    }
+    const float gm = j <= i ? expf(s.gc[i] - s.gc[j]) : 0.f;
+    s.u.m.R0[i][j] = j < i ? s.beta[i] * gm * kk : 0.f;
+    s.P[i][j] = gm * qk;
+  }
+  __syncthreads();
+  // N = (I + A)^-1 by forward substitution, one row per step
+  for (int i = 0; i < C; ++i) {
+    if (tid < C) {
+      const int m = tid;
+      float acc = m == i ? 1.f : 0.f;
+      for (int j = m; j < i; ++j) acc -= s.u.m.R0[i][j] * s.N[j][m];
+      s.N[i][m] = m <= i ? acc : 0.f;
+    }
+    __syncthreads();
+  }
+
+  // ---- value-dimension tiles
+  float dT[4][4] = {}, dOV[4][4] = {}, dQa[4][SD] = {}, dKa[4][SD] = {};
+  float dgcr[4] = {}, dwr[4] = {}, sgs = 0.f;
+  for (int c0 = 0; c0 < DV; c0 += 16) {
+#pragma unroll
+    for (int v = 0; v < SD; ++v) {
+      const int d = r0 + 16 * v;
+      s.u.t.St[d][c] = p.Sn[(chunk * DK + d) * DV + c0 + c];
+      s.u.t.Gt[d][c] = p.Gn[(chunk * DK + d) * DV + c0 + c];
+      sgs += s.u.t.St[d][c] * s.u.t.Gt[d][c];
+    }
+    for (int i = r0; i < C; i += 16) {
+      const long pos = P0 + i;
+      const bool last = i < valid && pos % nh == nh - 1;
+      s.u.t.dO[i][c] = last ? ld<E>(p.dO, ((b * (long)p.L + pos / nh) * p.H + h) * DV + c0 + c) : 0.f;
+    }
+    __syncthreads();
+    float ks[4], qs[4], kg[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = r0 + 16 * u;
+      ks[u] = qs[u] = kg[u] = 0.f;
+      if (u < CU) {
+#pragma unroll 8
+        for (int d = 0; d < DK; ++d) {
+          const float kv = s.K[i][d], sv = s.u.t.St[d][c];
+          ks[u] += kv * sv;
+          qs[u] += s.Q[i][d] * sv;
+          kg[u] += kv * s.u.t.Gt[d][c];
+        }
+        const float vv = i < valid ? ld<E>(p.v, ((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c) : 0.f;
+        s.u.t.Y[i][c] = vv - s.gam[i] * ks[u];
+      }
+    }
+    __syncthreads();
+    float vt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = r0 + 16 * u;
+      vt[u] = 0.f;
+      if (u < CU) {
+        for (int j = 0; j <= i; ++j) vt[u] += s.N[i][j] * s.beta[j] * s.u.t.Y[j][c];
+        s.u.t.Vt[i][c] = vt[u];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = r0 + 16 * u;
+      if (u < CU) {
+        float acc = s.w[i] * kg[u];
+        for (int j = i; j < C; ++j) acc += s.P[j][i] * s.u.t.dO[j][c];
+        s.u.t.dVt[i][c] = acc;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = r0 + 16 * u;
+      if (u < CU) {
+        float acc = 0.f;
+        for (int j = i; j < C; ++j) acc += s.N[j][i] * s.u.t.dVt[j][c];
+        acc *= s.beta[i];
+        s.u.t.dY[i][c] = acc;
+        dgcr[u] += sum16(s.gam[i] * (qs[u] * s.u.t.dO[i][c] - ks[u] * acc));
+        dwr[u] += sum16(kg[u] * vt[u]);
+      }
+    }
+    __syncthreads();
+    // dT += dV~ Y^T, dOV += dO V~^T
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u >= CU) continue;
+      const int i = r0 + 16 * u;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (v >= CU) continue;
+        const int j = c + 16 * v;
+        float a = 0.f, o = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          a += s.u.t.dVt[i][e] * s.u.t.Y[j][e];
+          o += s.u.t.dO[i][e] * s.u.t.Vt[j][e];
+        }
+        dT[u][v] += a;
+        dOV[u][v] += o;
+      }
+    }
+    // dQa += gam dO S^T, dKa += -gam dY S^T + w V~ G'^T
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u >= CU) continue;
+      const int i = r0 + 16 * u;
+      const float gi = s.gam[i], wi = s.w[i];
+#pragma unroll
+      for (int v = 0; v < SD; ++v) {
+        const int d = c + 16 * v;
+        float q = 0.f, k = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float sv = s.u.t.St[d][e];
+          q += s.u.t.dO[i][e] * sv;
+          k += wi * s.u.t.Vt[i][e] * s.u.t.Gt[d][e] - gi * s.u.t.dY[i][e] * sv;
+        }
+        dQa[u][v] += gi * q;
+        dKa[u][v] += k;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- chunk-local algebra
+  // sum of S_n * G'_n over the whole state: per-wave partial sums, then one total
+  {
+    float x = sgs;
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
+    if ((tid & (WAVE - 1)) == 0) s.sgs[tid / WAVE] = x;
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < CU) {
+        s.dgc[r0 + 16 * u] = dgcr[u];
+        s.dw[r0 + 16 * u] = dwr[u];
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (u < CU && v < CU) {
+        s.u.m.R0[r0 + 16 * u][c + 16 * v] = dT[u][v];
+        s.u.m.R1[r0 + 16 * u][c + 16 * v] = dOV[u][v];
+      }
+  __syncthreads();
+  // diag(N^T dT), and X = dT diag(beta) N^T (= dT T^T) into registers
+  if (tid < C) {
+    float acc = 0.f;
+    for (int i = tid; i < C; ++i) acc += s.N[i][tid] * s.u.m.R0[i][tid];
+    s.dbd[tid] = acc;
+  }
+  float X[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      X[u][v] = 0.f;
+      if (u < CU && v < CU) {
+        const int i = r0 + 16 * u, j = c + 16 * v;
+        for (int k = 0; k <= j; ++k) X[u][v] += s.u.m.R0[i][k] * s.beta[k] * s.N[j][k];
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (u < CU && v < CU) s.u.m.R0[r0 + 16 * u][c + 16 * v] = X[u][v];
+  __syncthreads();
+  // dA = -strictLower(N^T X); K K^T recomputed into R2
+  float dA[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      dA[u][v] = 0.f;
+      const int i = r0 + 16 * u, j = c + 16 * v;
+      if (u < CU && v < CU) {
+        if (j < i) {
+          float acc = 0.f;
+          for (int k = i; k < C; ++k) acc += s.N[k][i] * s.u.m.R0[k][j];
+          dA[u][v] = -acc;
+        }
+        float kk = 0.f;
+        if (j < i) {
+#pragma unroll 8
+          for (int d = 0; d < DK; ++d) kk += s.K[i][d] * s.K[j][d];
+        }
+        s.u.m.R2[i][j] = kk;
+      }
+    }
+  __syncthreads();
+  // per entry: the gate-prefix term t, dbeta's row term, dGm and E1 = Gam * dOV (lower)
+  float t[4][4], dGm[4][4], E1[4][4], rb[4] = {}, rt[4] = {};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      t[u][v] = dGm[u][v] = E1[u][v] = 0.f;
+      const int i = r0 + 16 * u, j = c + 16 * v;
+      if (u < CU && v < CU && j <= i) {
+        const float gm = expf(s.gc[i] - s.gc[j]);
+        const float kk = s.u.m.R2[i][j], dov = s.u.m.R1[i][j];
+        const float ta = dA[u][v] * gm * kk;  // zero on the diagonal
+        rb[u] += ta;
+        t[u][v] = s.beta[i] * ta + s.P[i][j] * dov;
+        dGm[u][v] = s.beta[i] * gm * dA[u][v];
+        E1[u][v] = gm * dov;
+        rt[u] += t[u][v];
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    rb[u] = sum16(rb[u]);
+    rt[u] = sum16(rt[u]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (u < CU && v < CU) {
+        const int i = r0 + 16 * u, j = c + 16 * v;
+        s.u.m.R0[i][j] = dGm[u][v];
+        s.u.m.R1[i][j] = E1[u][v];
+        s.u.m.R2[i][j] = t[u][v];
+      }
+    if (c == 0 && u < CU) {
+      const int i = r0 + 16 * u;
+      s.dbd[i] += rb[u];
+      s.rsum[i] = rt[u];
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    const int i = tid;
+    float col = 0.f;
+    for (int r = i; r < C; ++r) col += s.u.m.R2[r][i];
+    s.dgc[i] += s.rsum[i] - col - s.w[i] * s.dw[i];
+    if (i < valid) p.dbeta[(b * (long)p.Lx + P0 + i) * p.H + h] = s.dbd[i];
+  }
+  __syncthreads();
+  if (tid == 0 && p.dg_log) {
+    float tot = 0.f;
+    for (int i = 0; i < C; ++i) tot += s.w[i] * s.dw[i];
+    for (int o = 0; o < NTH / WAVE; ++o) tot += expf(gC) * s.sgs[o];
+    // reverse cumulative sum over the chunk; the last position also collects the total above
+    float run = tot;
+    for (int i = C - 1; i >= 0; --i) {
+      run += s.dgc[i];
+      const long pos = P0 + i;
+      if (i < valid && pos % nh == 0) p.dg_log[(b * (long)p.L + pos / nh) * p.H + h] = run;
+    }
+  }
+  // dQ = dQa + E1 K,  dK = dKa + E1^T Q + (dGm + dGm^T) K
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u >= CU) continue;
+    const int i = r0 + 16 * u;
+    const long pos = P0 + i;
+    if (i >= valid) continue;
+    const bool last = pos % nh == nh - 1;
+#pragma unroll
+    for (int v = 0; v < SD; ++v) {
+      const int d = c + 16 * v;
+      float dq = dQa[u][v], dk = dKa[u][v];
+      for (int j = 0; j <= i; ++j) dq += s.u.m.R1[i][j] * s.K[j][d];
+      for (int j = i; j < C; ++j) dk += s.u.m.R1[j][i] * s.Q[j][d];
+      for (int j = 0; j < C; ++j) dk += (s.u.m.R0[i][j] + s.u.m.R0[j][i]) * s.K[j][d];
+      p.dk[((b * (long)p.Lx + pos) * p.H + h) * DK + d] = dk;
+      if (last) p.dq[((b * (long)p.L + pos / nh) * p.H + h) * DK + d] = p.scale * dq;
+    }
+  }
+}
+
+template <typename E>
+hipError_t launch_by_dk(const BwdParams& p, int which, hipStream_t st) {
+  const dim3 block(NTH);
+  // one-dimensional grids: (head, column tile) and (head, chunk), tile or chunk fastest
+  const dim3 gs((unsigned)((long)p.DV / 16 * p.B * p.H)), gc((unsigned)((long)p.NT * p.B * p.H));
+#define DELTA_BWD_CASE(D)                                                                        \
+  case D:                                                                                        \
+    if (which == 0) hipLaunchKernelGGL((bwd_states_kernel<E, D>), gs, block, 0, st, p);         \
+    else if (which == 1) hipLaunchKernelGGL((bwd_dstates_kernel<E, D>), gs, block, 0, st, p);   \
+    else hipLaunchKernelGGL((bwd_chunk_kernel<E, D>), gc, block, 0, st, p);                      \
+    break;
+  switch (p.DK) {
+    DELTA_BWD_CASE(16)
+    DELTA_BWD_CASE(32)
+    DELTA_BWD_CASE(64)
+    DELTA_BWD_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef DELTA_BWD_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_phase(const BwdParams& p, bool bf16_in, int phase, hipStream_t st) {
+  return bf16_in ? launch_by_dk<bf16>(p, phase, st) : launch_by_dk<float>(p, phase, st);
+}
+
+}  // namespace delta

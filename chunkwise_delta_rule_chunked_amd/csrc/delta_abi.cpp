@@ -8,6 +8,7 @@
 #include "../../include/delta.h"
 #include "kernels.h"
 
+using delta::BwdParams;
 using delta::DecodeParams;
 using delta::FwdParams;
 
@@ -310,6 +311,90 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
   if (p.B * p.H * p.NT == 0) return DELTA_OK;
   if ((rc = hip_status(delta::launch_intra_chunk(p, bf, true, st)))) return rc;
   if (W || U) return hip_status(delta::launch_wy_factors(p, bf, st));
+  return DELTA_OK;
+}
+
+namespace {
+// Workspace of the backward pass: T (float32), the gate prefix, and per chunk the start state
+// and the end-of-chunk state gradient.
+size_t states_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.DK * p.DV * 4; }
+size_t bwd_workspace(const FwdParams& p) {
+  return align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
+}
+}  // namespace
+
+int delta_bwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_chunk(s))) return rc;
+  if (!bytes) return DELTA_ERR_NULL_ARG;
+  *bytes = bwd_workspace(make_params(s));
+  return DELTA_OK;
+}
+
+int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+              const float* g_log, const float* S0, const void* dO, const float* dS_final, float* dq,
+              float* dk, float* dv, float* dbeta, float* dg_log, float* dS0, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_chunk(s))) return rc;
+  const FwdParams f = make_params(s);
+  if (!g_log) dg_log = nullptr;
+  const size_t es = esize(s->dtype);
+  const size_t nq = (size_t)f.B * f.L * f.H, nx = (size_t)f.B * f.Lx * f.H, nS = (size_t)f.B * f.H * f.DK * f.DV;
+  const size_t sz_q = nq * f.DK * es, sz_k = nx * f.DK * es, sz_v = nx * f.DV * es, sz_o = nq * f.DV * es;
+  if (nx > 0 && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta)) return DELTA_ERR_NULL_ARG;
+  const size_t need = bwd_workspace(f);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DELTA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, S0, dO, dS_final, dq, dk, dv, dS0, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4) || !aligned(g_log, 4) || !aligned(dbeta, 4) || !aligned(dg_log, 4))
+    return DELTA_ERR_MISALIGNED;
+  const Range in[] = {range(q, q ? sz_q : 0),          range(k, k ? sz_k : 0),
+                      range(v, v ? sz_v : 0),          range(beta, beta ? nx * 4 : 0),
+                      range(g_log, g_log ? nq * 4 : 0), range(S0, S0 ? nS * 4 : 0),
+                      range(dO, dO ? sz_o : 0),         range(dS_final, dS_final ? nS * 4 : 0)};
+  const Range out[] = {range(dq, dq ? nq * f.DK * 4 : 0), range(dk, dk ? nx * f.DK * 4 : 0),
+                       range(dv, dv ? nx * f.DV * 4 : 0), range(dbeta, dbeta ? nx * 4 : 0),
+                       range(dg_log, dg_log ? nq * 4 : 0), range(dS0, dS0 ? nS * 4 : 0),
+                       range(workspace, need)};
+  constexpr int NO = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < NO; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return DELTA_ERR_ALIAS;
+    for (int j = i + 1; j < NO; ++j)
+      if (overlap(out[i], out[j])) return DELTA_ERR_ALIAS;
+  }
+  if ((size_t)f.B * f.H == 0) return DELTA_OK;
+
+  const bool bf = s->dtype == DELTA_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  FwdParams fi = f;  // the intra-chunk launch: T (float32) and the gate prefix
+  fi.k = k;
+  fi.beta = beta;
+  fi.g_log = g_log;
+  fi.T = ws;
+  fi.gc = reinterpret_cast<float*>(ws + align_up(t_bytes(f, 4)));
+  BwdParams p;
+  p.B = f.B, p.L = f.L, p.H = f.H, p.DK = f.DK, p.DV = f.DV, p.nh = f.nh, p.C = f.C, p.Lx = f.Lx, p.NT = f.NT;
+  p.scale = f.scale;
+  p.q = q, p.k = k, p.v = v, p.beta = beta, p.S0 = S0, p.dO = dO, p.dS_final = dS_final;
+  p.dq = dq, p.dk = dk, p.dv = dv, p.dbeta = dbeta, p.dg_log = dg_log, p.dS0 = dS0;
+  p.T = static_cast<const float*>(fi.T);
+  p.gc = fi.gc;
+  const size_t off = align_up(t_bytes(f, 4)) + align_up(gc_bytes(f));
+  p.Sn = reinterpret_cast<float*>(ws + off);
+  p.Gn = reinterpret_cast<float*>(ws + off + align_up(states_bytes(f)));
+  if (f.NT > 0) {
+    if ((rc = hip_status(delta::launch_intra_chunk(fi, bf, true, st)))) return rc;
+    if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 0, st)))) return rc;
+  }
+  // the reverse pass also writes dS0, so it runs when there are no chunks too
+  if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 1, st)))) return rc;
+  if (f.NT > 0) return hip_status(delta::launch_bwd_phase(p, bf, 2, st));
   return DELTA_OK;
 }
 

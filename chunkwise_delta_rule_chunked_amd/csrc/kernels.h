@@ -44,6 +44,29 @@ struct DecodeParams {
   void* O;              // [B, 1, H, DV]
 };
 
+// One backward problem after validation (shape fields as in FwdParams).
+struct BwdParams {
+  int B, L, H, DK, DV, nh, C, Lx, NT;
+  float scale;
+  const void* q;          // [B, L, H, DK]
+  const void* k;          // [B, Lx, H, DK]
+  const void* v;          // [B, Lx, H, DV]
+  const float* beta;      // [B, Lx, H]
+  const float* S0;        // [B, H, DK, DV] or nullptr
+  const void* dO;         // [B, L, H, DV], element type of the inputs
+  const float* dS_final;  // [B, H, DK, DV] or nullptr (zero)
+  float* dq;              // [B, L, H, DK]
+  float* dk;              // [B, Lx, H, DK]
+  float* dv;              // [B, Lx, H, DV]
+  float* dbeta;           // [B, Lx, H]
+  float* dg_log;          // [B, L, H] or nullptr (ungated)
+  float* dS0;             // [B, H, DK, DV] or nullptr
+  const float* T;         // [B*H, NT, C, C] float32, from the intra-chunk launch
+  const float* gc;        // [B*H, NT, C]
+  float* Sn;              // [B*H, NT, DK, DV] start state of each chunk
+  float* Gn;              // [B*H, NT, DK, DV] state gradient at the end of each chunk
+};
+
 // Each returns hipSuccess or the launch error.  `bf16` selects the element type of
 // q/k/v/O (true: bfloat16, false: float32).
 hipError_t launch_intra_chunk(const FwdParams& p, bool bf16, bool t_as_float, hipStream_t st);
@@ -55,6 +78,9 @@ hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream
 // Summary launch for bf16 inputs, d_k = d_v = 128, chunk 64 (scan_summary.hip).
 bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
+// Backward launches (backward.hip), in order after launch_intra_chunk with float T:
+// 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0), 2 per-chunk gradients.
+hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
 
 }  // namespace delta

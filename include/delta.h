@@ -186,6 +186,37 @@ int delta_decode(const delta_shape* s, const void* q, const void* k, const void*
 int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const void* v,
                      const float* beta, const float* a_log, float* S, void* O, void* stream);
 
+/*
+ * Bytes of device workspace delta_bwd needs for this shape: T in float32 and the gate prefix
+ * per chunk, and per chunk its start state and the gradient of its end state (float32
+ * d_k x d_v each).  Returns DELTA_OK and sets *bytes, or an error code.
+ */
+int delta_bwd_workspace_bytes(const delta_shape* s, size_t* bytes);
+
+/*
+ * Backward pass of delta_fwd: the gradients of <O, dO> + <S_final, dS_final> with respect to
+ * every input.  The pages define only the forward ("08 linear delta rule & DPLR", sections
+ * 2.2-2.3 and 3; DeltaProduct notes, section 4.1); these are its exact derivatives, evaluated
+ * chunkwise with the forward's T, gate prefix and chunk states recomputed from the inputs.
+ *   q, k, v, beta, g_log, S0   as passed to delta_fwd (g_log NULL: ungated, S0 NULL: zeros)
+ *   dO       [B, L, H, dv]        dtype     gradient of O
+ *   dS_final [B, H, dk, dv]       float32   gradient of S_final, or NULL for zero
+ *   dq       [B, L, H, dk]        float32   written
+ *   dk       [B, L*n_h, H, dk]    float32   written
+ *   dv       [B, L*n_h, H, dv]    float32   written
+ *   dbeta    [B, L*n_h, H]        float32   written
+ *   dg_log   [B, L, H]            float32   written; may be NULL (not computed); ignored when
+ *                                           g_log is NULL
+ *   dS0      [B, H, dk, dv]       float32   written, or NULL (not computed)
+ *   workspace                     at least delta_bwd_workspace_bytes bytes, 16-byte aligned
+ * Outputs may not overlap the inputs, each other or the workspace.  Alignment as for
+ * delta_fwd (dbeta and dg_log: 4-byte).  Error codes as for delta_fwd.
+ */
+int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+              const float* g_log, const float* S0, const void* dO, const float* dS_final, float* dq,
+              float* dk, float* dv, float* dbeta, float* dg_log, float* dS0, void* workspace,
+              size_t workspace_bytes, void* stream);
+
 /* Static description of a return code. */
 const char* delta_strerror(int code);
 

@@ -24,7 +24,7 @@ def test_exports_every_header_function(lib):
     assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_intra", "delta_fwd_inter",
                           "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
                           "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_decode_kda",
-                          "delta_strerror"}
+                          "delta_bwd_workspace_bytes", "delta_bwd", "delta_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -165,6 +165,44 @@ def test_decode_kda_argument_errors(lib, no_gpu):
     assert L.delta_decode_kda(ctypes.byref(sh), *f[:4], f[5], f[5], f[6], None) == -6     # a_log aliases S
     assert L.delta_decode_kda(ctypes.byref(sh), *f[:4], ctypes.c_void_p(A * 4 + 2), f[5], f[6], None) == -4
     assert L.delta_decode_kda(ctypes.byref(shape(B=0, L=1)), *[None] * 7, None) == 0       # empty
+
+
+def bwd_ws(sh):
+    n = ctypes.c_size_t(0)
+    rc = D.load_library().delta_bwd_workspace_bytes(ctypes.byref(sh), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_bwd_workspace_bytes(lib):
+    up = lambda x: (x + 255) // 256 * 256
+    for B, H, L, dk, dv, C, nh in [(2, 3, 100, 64, 32, 32, 1), (2, 16, 8192, 128, 128, 64, 1), (1, 2, 50, 16, 256, 48, 3)]:
+        NT = (L * nh + C - 1) // C
+        rc, n = bwd_ws(shape(B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, n_h=nh))
+        assert rc == 0 and n == up(B * H * NT * C * C * 4) + up(B * H * NT * C * 4) + 2 * up(B * H * NT * dk * dv * 4)
+    assert bwd_ws(shape(L=0)) == (0, 0)
+    assert bwd_ws(shape(dk=48))[0] == -3
+
+
+def call_bwd(sh, **kw):
+    names = ["q", "k", "v", "beta", "g", "S0", "dO", "dSF", "dq", "dk", "dv", "dbeta", "dg", "dS0", "w"]
+    defaults = {"q": 0, "k": 1, "v": 2, "beta": 3, "dO": 4, "dq": 5, "dk": 6, "dv": 7, "dbeta": 8, "w": 9}
+    args = [kw[n] if n in kw else (fake(defaults[n]) if n in defaults else None) for n in names]
+    wbytes = kw.get("wbytes", bwd_ws(sh)[1])
+    return D.load_library().delta_bwd(ctypes.byref(sh), *args, ctypes.c_size_t(wbytes), None)
+
+
+def test_bwd_argument_errors(lib, no_gpu):
+    sh = shape()
+    assert call_bwd(sh, dO=None) == -1                      # dO NULL
+    assert call_bwd(sh, dbeta=None) == -1                   # dbeta NULL
+    assert call_bwd(sh, w=None) == -5                       # workspace NULL
+    assert call_bwd(sh, wbytes=bwd_ws(sh)[1] - 1) == -5     # workspace too small
+    assert call_bwd(sh, dk=ctypes.c_void_p(A * 7 + 8)) == -4  # misaligned
+    assert call_bwd(sh, dq=fake(0)) == -6                   # dq aliases q
+    assert call_bwd(sh, dv=fake(6)) == -6                   # dv aliases dk
+    assert call_bwd(sh, dS0=fake(9)) == -6                  # dS0 inside the workspace
+    assert call_bwd(shape(chunk=24)) == -3
+    assert D.load_library().delta_bwd(ctypes.byref(shape(B=0)), *[None] * 15, ctypes.c_size_t(0), None) == 0
 
 
 def test_chunk_wy_argument_errors(lib, no_gpu):

@@ -17,7 +17,8 @@ Distributions (per the pages' model descriptions):
     cross-chunk state alive.
 
 Seeds: numpy PCG64 streams from SeedSequence([2026, cfg_id, stream]) with
-streams q=0, k=1, v=2, beta=3, g=4, S0=5, decode step t -> 100 + t.  Values are
+streams q=0, k=1, v=2, beta=3, g=4, S0=5, dO=6, dS_final=7, decode step t -> 100 + t,
+KDA decay of decode step t -> 300 + t.  Values are
 drawn in fp64, cast to fp32, and for bf16 workloads rounded to the nearest bf16
 (ties to even); both the oracle and the GPU consume exactly those values.
 """
@@ -156,6 +157,14 @@ def make_inputs(w: Workload, salt: int = 0) -> dict:
         "q": _cast(q, w.dtype), "k": _cast(k, w.dtype), "v": _cast(v, w.dtype),
         "beta": beta.astype(np.float32), "g_log": g_log, "S0": S0,
     }
+
+
+def make_cotangents(w: Workload, salt: int = 0) -> dict:
+    """Gradients fed to a backward call: dO [B, L, H, dv] ~ N(0,1) in the workload's dtype
+    (bf16-exact for bf16) and dS_final [B, H, dk, dv] ~ N(0,1) float32 (streams 6 and 7)."""
+    dO = _draw(w, 6, (w.B, w.L, w.H, w.dv), salt)
+    dS = _draw(w, 7, (w.B, w.H, w.dk, w.dv), salt).astype(np.float32)
+    return {"dO": _cast(dO, w.dtype), "dS_final": dS}
 
 
 def make_decode_inputs(w: Workload, step: int) -> dict:
