@@ -304,6 +304,40 @@ def roofline_of(w, r):
             "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / mfma_peak, 4)}
 
 
+def time_backward(w, steps, warmup=2):
+    """delta_bwd on the prefill workload with its seeded cotangents (dO, dS_final): `steps`
+    back-to-back calls with preallocated gradients and workspace, timed with HIP events."""
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    import workloads as W
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp, cot = W.make_inputs(w), W.make_cotangents(w)
+    dev = {kk: (None if vv is None else torch.from_numpy(vv).to(torch.float32 if kk in ("beta", "g_log", "S0")
+                                                            else dt).cuda()) for kk, vv in inp.items()}
+    dO = torch.from_numpy(cot["dO"]).to(dt).cuda()
+    dS = torch.from_numpy(cot["dS_final"]).cuda()
+    ws = torch.empty(D.bwd_workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk,
+                                           D.BF16 if w.dtype == "bf16" else D.F32), dtype=torch.uint8, device="cuda")
+
+    def run(grads=None):
+        return D.bwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g_log"], dev["S0"], dO, dS, n_h=w.n_h,
+                     chunk=w.chunk, grads=grads, workspace=ws)
+
+    grads = run()
+    for _ in range(warmup):
+        run(grads)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run(grads)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "steps": steps,
+            "workspace_mib": round(ws.numel() / 2**20, 1)}
+
+
 def time_decode(w, steps, n_states=8, kda=False):
     """`steps` back-to-back decode calls cycling over n_states independent states (8 x 64 MiB
     exceeds the 256 MB Infinity Cache, so each step streams its state from HBM); the same loop on
@@ -421,6 +455,8 @@ def main():
     ap.add_argument("--workload", default="gdn_b2h16_l8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only delta_bwd on the workload (--steps calls) and print its line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -438,6 +474,10 @@ def main():
         sys.exit(1)
 
     w = W.get(args.workload)
+    if args.backward_only:
+        bw = time_backward(w, args.steps, args.warmup)
+        print(json.dumps({"workload": w.name, "backward": bw}), flush=True)
+        return
     r = time_prefill(w, args.steps, args.warmup, args.copy_calibration_mib)
     log("[bench] %s: %.3f ms/step (%s), %.3e tokens/s" % (
         w.name, r["ms_per_step"], ", ".join("%s %.4f ms" % kv for kv in r["kernel_ms"].items()), r["tokens_per_s"]))
@@ -488,6 +528,12 @@ def main():
             log("[bench] kda decode: %s" % kd)
         except Exception as e:
             others[W.DECODE.name] = {"error": repr(e)}
+        try:
+            bw = time_backward(w, max(5, args.steps // 10))
+            others["bwd_" + w.name] = bw
+            log("[bench] backward %s: %s" % (w.name, bw))
+        except Exception as e:
+            others["bwd_" + w.name] = {"error": repr(e)}
         line["others"] = others
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w)
     print(json.dumps(line), flush=True)

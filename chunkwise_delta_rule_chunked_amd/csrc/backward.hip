@@ -18,8 +18,10 @@
 // sub-step).  Q and dO rows exist only at a token's last sub-step (DeltaProduct notes,
 // section 4.1); the readout scale is folded into Q.
 //
-// Three launches follow the intra-chunk launch (which leaves T in float32 and gc in the
+// Four launches follow the intra-chunk launch (which leaves T in float32 and gc in the
 // workspace):
+//   bwd_qk_kernel        one workgroup per (head, chunk): P = Q K^T * Gam (lower) into the
+//                        workspace
 //   bwd_states_kernel    one workgroup per (head, 16 state columns), chunks in order: stores
 //                        each chunk's start state S_n
 //   bwd_dstates_kernel   same split, chunks in reverse: stores each chunk's end-state gradient
@@ -39,10 +41,81 @@ namespace {
 constexpr int CM = 64;   // largest chunk
 constexpr int NTH = 256; // threads per workgroup
 
+// Eight bf16 or four floats of a 16-byte vector, as floats.
 template <typename E>
-__device__ inline float ld(const void* p, long i) {
-  return to_float(static_cast<const E*>(p)[i]);
+__device__ inline void unpack16(u32x4 r, float* x);
+template <>
+__device__ inline void unpack16<bf16>(u32x4 r, float* x) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(r[e] << 16);
+    x[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+  }
 }
+template <>
+__device__ inline void unpack16<float>(u32x4 r, float* x) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(r[e]);
+}
+
+// A tile of up to MAXR rows x WIDTH elements of E, moved in 16-byte vectors: issue() fetches
+// every vector of the calling thread into registers (all loads in flight together), commit()
+// later unpacks them into a float LDS tile.  rowptr(i) gives row i's first element, or nullptr
+// for a row of zeros.
+template <typename E, int WIDTH, int MAXR>
+struct RowTile {
+  static constexpr int VE = 16 / (int)sizeof(E), VPR = WIDTH / VE;
+  static constexpr int NV = (MAXR * VPR + NTH - 1) / NTH;
+  u32x4 r[NV];
+  template <typename F>
+  __device__ inline void issue(F rowptr, int tid) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + NTH * u, i = idx / VPR, j = (idx % VPR) * VE;
+      const E* q = i < MAXR ? rowptr(i) : nullptr;
+      r[u] = q ? *reinterpret_cast<const u32x4*>(q + j) : u32x4{0, 0, 0, 0};
+    }
+  }
+  template <int PITCH>
+  __device__ inline void commit(float (*dst)[PITCH], int rows, int tid, float mul = 1.f) const {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + NTH * u, i = idx / VPR, j = (idx % VPR) * VE;
+      if (i < rows) {
+        float x[VE];
+        unpack16<E>(r[u], x);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) dst[i][j + e] = mul * x[e];
+      }
+    }
+  }
+};
+
+// A C x C float matrix stored contiguously (C <= CM), moved the same way.
+struct SquareTile {
+  static constexpr int NV = CM * CM / 4 / NTH;
+  u32x4 r[NV];
+  __device__ inline void issue(const float* src, int C, int tid) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + NTH * u;
+      r[u] = idx < C * C / 4 ? *reinterpret_cast<const u32x4*>(src + 4 * idx) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ inline void commit(float (*dst)[CM + 1], int C, int tid) const {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int idx = tid + NTH * u;
+      if (idx < C * C / 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * idx + e;
+          dst[x / C][x % C] = __uint_as_float(r[u][e]);
+        }
+      }
+    }
+  }
+};
 
 // Chunk rows i of a 16-column tile are owned by threads with (tid >> 4) == i % 16, column tid & 15.
 
@@ -51,46 +124,59 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
   __shared__ float Kl[CM][DK + 1];
   __shared__ float Tl[CM][CM + 1];
   __shared__ float Sl[DK][17];
-  __shared__ float Yl[CM][17];
+  __shared__ float Yl[CM][17];  // V, then Y in place
   __shared__ float Vt[CM][17];
-  __shared__ float gam[CM], wl[CM];
+  __shared__ float gcl[CM], gam[CM], wl[CM];
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
   const int ntile = p.DV / 16, c0 = (int)(blockIdx.x % ntile) * 16, bh = (int)(blockIdx.x / ntile);
   const int b = bh / p.H, h = bh % p.H;
-  const int C = p.C, DV = p.DV;
+  const int C = p.C, DV = p.DV, NT = p.NT;
+  const long HDK = (long)p.H * DK, HDV = (long)p.H * DV;
+  const E* kb = static_cast<const E*>(p.k) + (long)b * p.Lx * HDK + (long)h * DK;
+  const E* vb = static_cast<const E*>(p.v) + (long)b * p.Lx * HDV + (long)h * DV + c0;
   constexpr int RD = DK / 16;
   float S[RD];
 #pragma unroll
   for (int u = 0; u < RD; ++u) S[u] = p.S0 ? p.S0[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] : 0.f;
 
-  for (int n = 0; n < p.NT; ++n) {
+  RowTile<E, DK, CM> kt;
+  RowTile<E, 16, CM> vt;
+  SquareTile tt;
+  float gv = 0.f;
+  auto issue = [&](int n) {
     const long P0 = (long)n * C;
     const int valid = (int)min((long)C, (long)p.Lx - P0);
-    const long chunk = (long)bh * p.NT + n;
+    kt.issue([&](int i) -> const E* { return i < valid ? kb + (P0 + i) * HDK : nullptr; }, tid);
+    vt.issue([&](int i) -> const E* { return i < valid ? vb + (P0 + i) * HDV : nullptr; }, tid);
+    tt.issue(p.T + ((long)bh * NT + n) * C * C, C, tid);
+    gv = tid < C ? p.gc[((long)bh * NT + n) * C + tid] : 0.f;
+  };
+  if (NT > 0) issue(0);
+  for (int n = 0; n < NT; ++n) {
+    const long chunk = (long)bh * NT + n;
+    kt.commit(Kl, C, tid);
+    vt.commit(Yl, C, tid);
+    tt.commit(Tl, C, tid);
+    if (tid < C) gcl[tid] = gv;
 #pragma unroll
     for (int u = 0; u < RD; ++u) {
       p.Sn[(chunk * DK + r0 + 16 * u) * DV + c0 + c] = S[u];
       Sl[r0 + 16 * u][c] = S[u];
     }
-    for (int idx = tid; idx < C * DK; idx += NTH) {
-      const int i = idx / DK, d = idx % DK;
-      Kl[i][d] = i < valid ? ld<E>(p.k, ((b * (long)p.Lx + P0 + i) * p.H + h) * DK + d) : 0.f;
-    }
-    for (int idx = tid; idx < C * C; idx += NTH) Tl[idx / C][idx % C] = p.T[chunk * C * C + idx];
-    const float gC = p.gc[chunk * C + C - 1];
+    __syncthreads();
+    const float gC = gcl[C - 1];
     if (tid < C) {
-      const float g = p.gc[chunk * C + tid];
-      gam[tid] = expf(g);
-      wl[tid] = expf(gC - g);
+      gam[tid] = expf(gcl[tid]);
+      wl[tid] = expf(gC - gcl[tid]);
     }
+    if (n + 1 < NT) issue(n + 1);  // the next chunk's loads fly while this one computes
     __syncthreads();
     // Y = V - gam K S
     for (int i = r0; i < C; i += 16) {
       float acc = 0.f;
 #pragma unroll 8
       for (int d = 0; d < DK; ++d) acc += Kl[i][d] * Sl[d][c];
-      const float vv = i < valid ? ld<E>(p.v, ((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c) : 0.f;
-      Yl[i][c] = vv - gam[i] * acc;
+      Yl[i][c] -= gam[i] * acc;
     }
     __syncthreads();
     // V~ = T Y (T lower triangular)
@@ -113,6 +199,42 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
   }
 }
 
+// P = Q K^T * Gam on and below the diagonal, per chunk (Q scaled, zero rows where a token has
+// no readout), for the reverse scan and the per-chunk gradients.
+template <typename E, int DK>
+__global__ __launch_bounds__(NTH) void bwd_qk_kernel(BwdParams p) {
+  __shared__ float Kl[CM][DK + 1];
+  __shared__ float Ql[CM][DK + 1];
+  __shared__ float gcl[CM];
+  const int tid = threadIdx.x;
+  const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
+  const int C = p.C, nh = p.nh;
+  const long HDK = (long)p.H * DK, P0 = (long)n * C, chunk = (long)bh * p.NT + n;
+  const int valid = (int)min((long)C, (long)p.Lx - P0);
+  const E* kb = static_cast<const E*>(p.k) + (long)b * p.Lx * HDK + (long)h * DK;
+  const E* qb = static_cast<const E*>(p.q) + (long)b * p.L * HDK + (long)h * DK;
+  RowTile<E, DK, CM> kt, qt;
+  kt.issue([&](int i) -> const E* { return i < valid ? kb + (P0 + i) * HDK : nullptr; }, tid);
+  qt.issue([&](int i) -> const E* {
+    return i < valid && (P0 + i) % nh == nh - 1 ? qb + (P0 + i) / nh * HDK : nullptr;
+  }, tid);
+  if (tid < C) gcl[tid] = p.gc[chunk * C + tid];
+  kt.commit(Kl, C, tid);
+  qt.commit(Ql, C, tid, p.scale);
+  __syncthreads();
+  float* out = p.Pm + chunk * C * C;
+  for (int idx = tid; idx < C * C; idx += NTH) {
+    const int i = idx / C, j = idx % C;
+    float acc = 0.f;
+    if (j <= i) {
+#pragma unroll 8
+      for (int d = 0; d < DK; ++d) acc += Ql[i][d] * Kl[j][d];
+      acc *= expf(gcl[i] - gcl[j]);
+    }
+    out[idx] = acc;
+  }
+}
+
 template <typename E, int DK>
 __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
   __shared__ float Kl[CM][DK + 1];
@@ -127,53 +249,54 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
   const int ntile = p.DV / 16, c0 = (int)(blockIdx.x % ntile) * 16, bh = (int)(blockIdx.x / ntile);
   const int b = bh / p.H, h = bh % p.H;
-  const int C = p.C, DV = p.DV, nh = p.nh;
+  const int C = p.C, DV = p.DV, nh = p.nh, NT = p.NT;
+  const long HDK = (long)p.H * DK, HDV = (long)p.H * DV;
+  const E* kb = static_cast<const E*>(p.k) + (long)b * p.Lx * HDK + (long)h * DK;
+  const E* qb = static_cast<const E*>(p.q) + (long)b * p.L * HDK + (long)h * DK;
+  const E* ob = static_cast<const E*>(p.dO) + (long)b * p.L * HDV + (long)h * DV + c0;
   constexpr int RD = DK / 16;
   float G[RD];
 #pragma unroll
   for (int u = 0; u < RD; ++u) G[u] = p.dS_final ? p.dS_final[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] : 0.f;
 
-  for (int n = p.NT - 1; n >= 0; --n) {
+  RowTile<E, DK, CM> kt, qt;
+  RowTile<E, 16, CM> ot;
+  SquareTile tt, pt;
+  float gv = 0.f;
+  auto issue = [&](int n) {
+    const long P0 = (long)n * C, chunk = (long)bh * NT + n;
+    const int valid = (int)min((long)C, (long)p.Lx - P0);
+    auto last = [&](int i) { return i < valid && (P0 + i) % nh == nh - 1; };
+    kt.issue([&](int i) -> const E* { return i < valid ? kb + (P0 + i) * HDK : nullptr; }, tid);
+    qt.issue([&](int i) -> const E* { return last(i) ? qb + (P0 + i) / nh * HDK : nullptr; }, tid);
+    ot.issue([&](int i) -> const E* { return last(i) ? ob + (P0 + i) / nh * HDV : nullptr; }, tid);
+    tt.issue(p.T + chunk * C * C, C, tid);
+    pt.issue(p.Pm + chunk * C * C, C, tid);
+    gv = tid < C ? p.gc[chunk * C + tid] : 0.f;
+  };
+  if (NT > 0) issue(NT - 1);
+  for (int n = NT - 1; n >= 0; --n) {
     const long P0 = (long)n * C;
     const int valid = (int)min((long)C, (long)p.Lx - P0);
-    const long chunk = (long)bh * p.NT + n;
+    const long chunk = (long)bh * NT + n;
+    kt.commit(Kl, C, tid);
+    qt.commit(Ql, C, tid, p.scale);
+    ot.commit(dOl, C, tid);
+    tt.commit(Tl, C, tid);
+    pt.commit(Pl, C, tid);
+    if (tid < C) gcl[tid] = gv;
 #pragma unroll
     for (int u = 0; u < RD; ++u) {
       p.Gn[(chunk * DK + r0 + 16 * u) * DV + c0 + c] = G[u];
       Gl[r0 + 16 * u][c] = G[u];
     }
-    for (int idx = tid; idx < C * DK; idx += NTH) {
-      const int i = idx / DK, d = idx % DK;
-      const long pos = P0 + i;
-      const bool last = i < valid && pos % nh == nh - 1;
-      Kl[i][d] = i < valid ? ld<E>(p.k, ((b * (long)p.Lx + pos) * p.H + h) * DK + d) : 0.f;
-      Ql[i][d] = last ? p.scale * ld<E>(p.q, ((b * (long)p.L + pos / nh) * p.H + h) * DK + d) : 0.f;
-    }
-    for (int idx = tid; idx < C * C; idx += NTH) Tl[idx / C][idx % C] = p.T[chunk * C * C + idx];
-    const float gC = p.gc[chunk * C + C - 1];
-    if (tid < C) {
-      const float g = p.gc[chunk * C + tid];
-      gcl[tid] = g;
-      gam[tid] = expf(g);
-      wl[tid] = expf(gC - g);
-    }
-    for (int i = r0; i < C; i += 16) {
-      const long pos = P0 + i;
-      const bool last = i < valid && pos % nh == nh - 1;
-      dOl[i][c] = last ? ld<E>(p.dO, ((b * (long)p.L + pos / nh) * p.H + h) * DV + c0 + c) : 0.f;
-    }
     __syncthreads();
-    // P = Q K^T * Gam on and below the diagonal
-    for (int idx = tid; idx < C * C; idx += NTH) {
-      const int i = idx / C, j = idx % C;
-      float acc = 0.f;
-      if (j <= i) {
-#pragma unroll 8
-        for (int d = 0; d < DK; ++d) acc += Ql[i][d] * Kl[j][d];
-        acc *= expf(gcl[i] - gcl[j]);
-      }
-      Pl[i][j] = acc;
+    const float gC = gcl[C - 1];
+    if (tid < C) {
+      gam[tid] = expf(gcl[tid]);
+      wl[tid] = expf(gC - gcl[tid]);
     }
+    if (n > 0) issue(n - 1);
     __syncthreads();
     // dV~ = w (K G') + P^T dO
     for (int i = r0; i < C; i += 16) {
@@ -249,12 +372,21 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
   const int valid = (int)min((long)C, (long)p.Lx - P0);
   const long chunk = (long)bh * p.NT + n;
 
-  for (int idx = tid; idx < C * DK; idx += NTH) {
-    const int i = idx / DK, d = idx % DK;
-    const long pos = P0 + i;
-    const bool last = i < valid && pos % nh == nh - 1;
-    s.K[i][d] = i < valid ? ld<E>(p.k, ((b * (long)p.Lx + pos) * p.H + h) * DK + d) : 0.f;
-    s.Q[i][d] = last ? p.scale * ld<E>(p.q, ((b * (long)p.L + pos / nh) * p.H + h) * DK + d) : 0.f;
+  const long HDK = (long)p.H * DK, HDV = (long)p.H * DV;
+  const E* kb = static_cast<const E*>(p.k) + (long)b * p.Lx * HDK + (long)h * DK;
+  const E* qb = static_cast<const E*>(p.q) + (long)b * p.L * HDK + (long)h * DK;
+  const E* vb = static_cast<const E*>(p.v) + (long)b * p.Lx * HDV + (long)h * DV;
+  const E* ob = static_cast<const E*>(p.dO) + (long)b * p.L * HDV + (long)h * DV;
+  auto last = [&](int i) { return i < valid && (P0 + i) % nh == nh - 1; };
+  {
+    RowTile<E, DK, CM> kt, qt;
+    SquareTile pt;
+    kt.issue([&](int i) -> const E* { return i < valid ? kb + (P0 + i) * HDK : nullptr; }, tid);
+    qt.issue([&](int i) -> const E* { return last(i) ? qb + (P0 + i) / nh * HDK : nullptr; }, tid);
+    pt.issue(p.Pm + chunk * C * C, C, tid);
+    kt.commit(s.K, C, tid);
+    qt.commit(s.Q, C, tid, p.scale);
+    pt.commit(s.P, C, tid);
   }
   const float gC = p.gc[chunk * C + C - 1];
   if (tid < C) {
@@ -265,20 +397,16 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
     s.beta[tid] = tid < valid ? p.beta[(b * (long)p.Lx + P0 + tid) * p.H + h] : 0.f;
   }
   __syncthreads();
-  // A = strictLower(diag(beta) (Gam * K K^T)) into R0, P into s.P
+  // A = strictLower(diag(beta) (Gam * K K^T)) into R0
   for (int idx = tid; idx < C * C; idx += NTH) {
     const int i = idx / C, j = idx % C;
-    float kk = 0.f, qk = 0.f;
-    if (j <= i) {
+    float kk = 0.f;
+    if (j < i) {
 #pragma unroll 8
-      for (int d = 0; d < DK; ++d) {
-        kk += s.K[i][d] * s.K[j][d];
-        qk += s.Q[i][d] * s.K[j][d];
-      }
+      for (int d = 0; d < DK; ++d) kk += s.K[i][d] * s.K[j][d];
+      kk *= s.beta[i] * expf(s.gc[i] - s.gc[j]);
     }
-    const float gm = j <= i ? expf(s.gc[i] - s.gc[j]) : 0.f;
-    s.u.m.R0[i][j] = j < i ? s.beta[i] * gm * kk : 0.f;
-    s.P[i][j] = gm * qk;
+    s.u.m.R0[i][j] = kk;
   }
   __syncthreads();
   // N = (I + A)^-1 by forward substitution, one row per step
@@ -292,23 +420,29 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  // ---- value-dimension tiles
+  // ---- value-dimension tiles; each tile's loads are issued one tile ahead
   float dT[4][4] = {}, dOV[4][4] = {}, dQa[4][SD] = {}, dKa[4][SD] = {};
   float dgcr[4] = {}, dwr[4] = {}, sgs = 0.f;
+  RowTile<float, 16, DK> st, gt;
+  RowTile<E, 16, CM> vt, ot;
+  auto issue = [&](int c0) {
+    const float* sb = p.Sn + chunk * DK * DV + c0;
+    const float* gb = p.Gn + chunk * DK * DV + c0;
+    st.issue([&](int d) -> const float* { return sb + (long)d * DV; }, tid);
+    gt.issue([&](int d) -> const float* { return gb + (long)d * DV; }, tid);
+    vt.issue([&](int i) -> const E* { return i < valid ? vb + (P0 + i) * HDV + c0 : nullptr; }, tid);
+    ot.issue([&](int i) -> const E* { return last(i) ? ob + (P0 + i) / nh * HDV + c0 : nullptr; }, tid);
+  };
+  issue(0);
   for (int c0 = 0; c0 < DV; c0 += 16) {
-#pragma unroll
-    for (int v = 0; v < SD; ++v) {
-      const int d = r0 + 16 * v;
-      s.u.t.St[d][c] = p.Sn[(chunk * DK + d) * DV + c0 + c];
-      s.u.t.Gt[d][c] = p.Gn[(chunk * DK + d) * DV + c0 + c];
-      sgs += s.u.t.St[d][c] * s.u.t.Gt[d][c];
-    }
-    for (int i = r0; i < C; i += 16) {
-      const long pos = P0 + i;
-      const bool last = i < valid && pos % nh == nh - 1;
-      s.u.t.dO[i][c] = last ? ld<E>(p.dO, ((b * (long)p.L + pos / nh) * p.H + h) * DV + c0 + c) : 0.f;
-    }
+    st.commit(s.u.t.St, DK, tid);
+    gt.commit(s.u.t.Gt, DK, tid);
+    vt.commit(s.u.t.Y, C, tid);
+    ot.commit(s.u.t.dO, C, tid);
     __syncthreads();
+    if (c0 + 16 < DV) issue(c0 + 16);
+#pragma unroll
+    for (int v = 0; v < SD; ++v) sgs += s.u.t.St[r0 + 16 * v][c] * s.u.t.Gt[r0 + 16 * v][c];
     float ks[4], qs[4], kg[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -322,8 +456,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
           qs[u] += s.Q[i][d] * sv;
           kg[u] += kv * s.u.t.Gt[d][c];
         }
-        const float vv = i < valid ? ld<E>(p.v, ((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c) : 0.f;
-        s.u.t.Y[i][c] = vv - s.gam[i] * ks[u];
+        s.u.t.Y[i][c] -= s.gam[i] * ks[u];
       }
     }
     __syncthreads();
@@ -563,7 +696,8 @@ hipError_t launch_by_dk(const BwdParams& p, int which, hipStream_t st) {
   case D:                                                                                        \
     if (which == 0) hipLaunchKernelGGL((bwd_states_kernel<E, D>), gs, block, 0, st, p);         \
     else if (which == 1) hipLaunchKernelGGL((bwd_dstates_kernel<E, D>), gs, block, 0, st, p);   \
-    else hipLaunchKernelGGL((bwd_chunk_kernel<E, D>), gc, block, 0, st, p);                      \
+    else if (which == 2) hipLaunchKernelGGL((bwd_chunk_kernel<E, D>), gc, block, 0, st, p);     \
+    else hipLaunchKernelGGL((bwd_qk_kernel<E, D>), gc, block, 0, st, p);                         \
     break;
   switch (p.DK) {
     DELTA_BWD_CASE(16)

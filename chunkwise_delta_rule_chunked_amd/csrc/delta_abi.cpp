@@ -315,11 +315,11 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
 }
 
 namespace {
-// Workspace of the backward pass: T (float32), the gate prefix, and per chunk the start state
-// and the end-of-chunk state gradient.
+// Workspace of the backward pass: T (float32), the gate prefix, Q K^T * Gam (float32, C x C
+// per chunk), and per chunk the start state and the end-of-chunk state gradient.
 size_t states_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.DK * p.DV * 4; }
 size_t bwd_workspace(const FwdParams& p) {
-  return align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
+  return 2 * align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
 }
 }  // namespace
 
@@ -385,11 +385,14 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   p.dq = dq, p.dk = dk, p.dv = dv, p.dbeta = dbeta, p.dg_log = dg_log, p.dS0 = dS0;
   p.T = static_cast<const float*>(fi.T);
   p.gc = fi.gc;
-  const size_t off = align_up(t_bytes(f, 4)) + align_up(gc_bytes(f));
+  size_t off = align_up(t_bytes(f, 4)) + align_up(gc_bytes(f));
+  p.Pm = reinterpret_cast<float*>(ws + off);
+  off += align_up(t_bytes(f, 4));
   p.Sn = reinterpret_cast<float*>(ws + off);
   p.Gn = reinterpret_cast<float*>(ws + off + align_up(states_bytes(f)));
   if (f.NT > 0) {
     if ((rc = hip_status(delta::launch_intra_chunk(fi, bf, true, st)))) return rc;
+    if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 3, st)))) return rc;
     if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 0, st)))) return rc;
   }
   // the reverse pass also writes dS0, so it runs when there are no chunks too

@@ -63,6 +63,7 @@ struct BwdParams {
   float* dS0;             // [B, H, DK, DV] or nullptr
   const float* T;         // [B*H, NT, C, C] float32, from the intra-chunk launch
   const float* gc;        // [B*H, NT, C]
+  float* Pm;              // [B*H, NT, C, C] Q K^T * Gam on and below the diagonal (Q scaled)
   float* Sn;              // [B*H, NT, DK, DV] start state of each chunk
   float* Gn;              // [B*H, NT, DK, DV] state gradient at the end of each chunk
 };
@@ -79,7 +80,8 @@ hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream
 bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 // Backward launches (backward.hip), in order after launch_intra_chunk with float T:
-// 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0), 2 per-chunk gradients.
+// 3 Q K^T * Gam per chunk, 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0),
+// 2 per-chunk gradients.
 hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
 

@@ -187,8 +187,8 @@ int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const v
                      const float* beta, const float* a_log, float* S, void* O, void* stream);
 
 /*
- * Bytes of device workspace delta_bwd needs for this shape: T in float32 and the gate prefix
- * per chunk, and per chunk its start state and the gradient of its end state (float32
+ * Bytes of device workspace delta_bwd needs for this shape: T in float32, the gate prefix and
+ * Q K^T weighted by the gate ratios (C x C float32) per chunk, and per chunk its start state and the gradient of its end state (float32
  * d_k x d_v each).  Returns DELTA_OK and sets *bytes, or an error code.
  */
 int delta_bwd_workspace_bytes(const delta_shape* s, size_t* bytes);
