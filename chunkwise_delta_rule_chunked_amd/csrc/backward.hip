@@ -40,6 +40,7 @@ namespace {
 
 constexpr int CM = 64;   // largest chunk
 constexpr int NTH = 256; // threads per workgroup
+constexpr int NTC = 512; // threads per workgroup of the per-chunk gradient kernel
 
 // Eight bf16 or four floats of a 16-byte vector, as floats.
 template <typename E>
@@ -62,16 +63,16 @@ __device__ inline void unpack16<float>(u32x4 r, float* x) {
 // every vector of the calling thread into registers (all loads in flight together), commit()
 // later unpacks them into a float LDS tile.  rowptr(i) gives row i's first element, or nullptr
 // for a row of zeros.
-template <typename E, int WIDTH, int MAXR>
+template <typename E, int WIDTH, int MAXR, int NTHR = NTH>
 struct RowTile {
   static constexpr int VE = 16 / (int)sizeof(E), VPR = WIDTH / VE;
-  static constexpr int NV = (MAXR * VPR + NTH - 1) / NTH;
+  static constexpr int NV = (MAXR * VPR + NTHR - 1) / NTHR;
   u32x4 r[NV];
   template <typename F>
   __device__ inline void issue(F rowptr, int tid) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int idx = tid + NTH * u, i = idx / VPR, j = (idx % VPR) * VE;
+      const int idx = tid + NTHR * u, i = idx / VPR, j = (idx % VPR) * VE;
       const E* q = i < MAXR ? rowptr(i) : nullptr;
       r[u] = q ? *reinterpret_cast<const u32x4*>(q + j) : u32x4{0, 0, 0, 0};
     }
@@ -80,7 +81,7 @@ struct RowTile {
   __device__ inline void commit(float (*dst)[PITCH], int rows, int tid, float mul = 1.f) const {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int idx = tid + NTH * u, i = idx / VPR, j = (idx % VPR) * VE;
+      const int idx = tid + NTHR * u, i = idx / VPR, j = (idx % VPR) * VE;
       if (i < rows) {
         float x[VE];
         unpack16<E>(r[u], x);
@@ -92,30 +93,39 @@ struct RowTile {
 };
 
 // A C x C float matrix stored contiguously (C <= CM), moved the same way.
+template <int NTHR = NTH>
 struct SquareTile {
-  static constexpr int NV = CM * CM / 4 / NTH;
+  static constexpr int NV = CM * CM / 4 / NTHR;
   u32x4 r[NV];
   __device__ inline void issue(const float* src, int C, int tid) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int idx = tid + NTH * u;
+      const int idx = tid + NTHR * u;
       r[u] = idx < C * C / 4 ? *reinterpret_cast<const u32x4*>(src + 4 * idx) : u32x4{0, 0, 0, 0};
     }
   }
-  __device__ inline void commit(float (*dst)[CM + 1], int C, int tid) const {
+  template <int PITCH, bool TRANSPOSE = false>
+  __device__ inline void commit(float (*dst)[PITCH], int C, int tid) const {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int idx = tid + NTH * u;
+      const int idx = tid + NTHR * u;
       if (idx < C * C / 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int x = 4 * idx + e;
-          dst[x / C][x % C] = __uint_as_float(r[u][e]);
+          if (TRANSPOSE)
+            dst[x % C][x / C] = __uint_as_float(r[u][e]);
+          else
+            dst[x / C][x % C] = __uint_as_float(r[u][e]);
         }
       }
     }
   }
 };
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+__device__ inline f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ inline float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 
 // Chunk rows i of a 16-column tile are owned by threads with (tid >> 4) == i % 16, column tid & 15.
 
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
 
   RowTile<E, DK, CM> kt;
   RowTile<E, 16, CM> vt;
-  SquareTile tt;
+  SquareTile<> tt;
   float gv = 0.f;
   auto issue = [&](int n) {
     const long P0 = (long)n * C;
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
 
   RowTile<E, DK, CM> kt, qt;
   RowTile<E, 16, CM> ot;
-  SquareTile tt, pt;
+  SquareTile<> tt, pt;
   float gv = 0.f;
   auto issue = [&](int n) {
     const long P0 = (long)n * C, chunk = (long)bh * NT + n;
@@ -342,28 +352,31 @@ __device__ inline float sum16(float x) {
   return x;
 }
 
+// Rows padded to a multiple of 4 floats so that 16-byte LDS reads stay aligned.
 template <int DK>
-struct ChunkLds {
-  float K[CM][DK + 1];
-  float Q[CM][DK + 1];
-  float N[CM][CM + 1];  // (I + A)^-1
-  float P[CM][CM + 1];  // Q K^T * Gam, on and below the diagonal
+struct __attribute__((aligned(16))) ChunkLds {
+  float K[CM][DK + 4];
+  float Q[CM][DK + 4];
+  float N[CM][CM + 4];   // (I + A)^-1
+  float Pt[CM][CM + 4];  // P^T, P = Q K^T * Gam on and below the diagonal
   union {
     struct {  // one 16-column tile of the value dimension
-      float St[DK][17], Gt[DK][17];
-      float Y[CM][17], dO[CM][17], Vt[CM][17], dVt[CM][17], dY[CM][17];
+      float St[DK][20], Gt[DK][20];
+      float Y[CM][20], dO[CM][20], Vt[CM][20], dVt[CM][20], dY[CM][20];
     } t;
     struct {  // chunk-local C x C algebra
-      float R0[CM][CM + 1], R1[CM][CM + 1], R2[CM][CM + 1];
+      float R0[CM][CM + 4], R1[CM][CM + 4], R2[CM][CM + 4];
     } m;
   } u;
   float gc[CM], gam[CM], w[CM], beta[CM], dbd[CM], dgc[CM], dw[CM], rsum[CM];
-  float sgs[NTH / WAVE];
+  float sgs[NTC / WAVE];
 };
 
 template <typename E, int DK>
-__global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
+__global__ __launch_bounds__(NTC) void bwd_chunk_kernel(BwdParams p) {
   __shared__ ChunkLds<DK> s;
+  // 512 threads: chunk rows r0 + 32 u (u < 2) of column c, two waves per SIMD
+  constexpr int RS = NTC / 16, NU = CM / RS;
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
   const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
   const int C = p.C, DV = p.DV, nh = p.nh, CU = C / 16;
@@ -379,14 +392,14 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
   const E* ob = static_cast<const E*>(p.dO) + (long)b * p.L * HDV + (long)h * DV;
   auto last = [&](int i) { return i < valid && (P0 + i) % nh == nh - 1; };
   {
-    RowTile<E, DK, CM> kt, qt;
-    SquareTile pt;
+    RowTile<E, DK, CM, NTC> kt, qt;
+    SquareTile<NTC> pt;
     kt.issue([&](int i) -> const E* { return i < valid ? kb + (P0 + i) * HDK : nullptr; }, tid);
     qt.issue([&](int i) -> const E* { return last(i) ? qb + (P0 + i) / nh * HDK : nullptr; }, tid);
     pt.issue(p.Pm + chunk * C * C, C, tid);
     kt.commit(s.K, C, tid);
     qt.commit(s.Q, C, tid, p.scale);
-    pt.commit(s.P, C, tid);
+    pt.commit<CM + 4, true>(s.Pt, C, tid);
   }
   const float gC = p.gc[chunk * C + C - 1];
   if (tid < C) {
@@ -398,12 +411,12 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
   }
   __syncthreads();
   // A = strictLower(diag(beta) (Gam * K K^T)) into R0
-  for (int idx = tid; idx < C * C; idx += NTH) {
+  for (int idx = tid; idx < C * C; idx += NTC) {
     const int i = idx / C, j = idx % C;
     float kk = 0.f;
     if (j < i) {
 #pragma unroll 8
-      for (int d = 0; d < DK; ++d) kk += s.K[i][d] * s.K[j][d];
+      for (int d = 0; d < DK; d += 4) kk += dot4(ld4(&s.K[i][d]), ld4(&s.K[j][d]));
       kk *= s.beta[i] * expf(s.gc[i] - s.gc[j]);
     }
     s.u.m.R0[i][j] = kk;
@@ -421,10 +434,10 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
   }
 
   // ---- value-dimension tiles; each tile's loads are issued one tile ahead
-  float dT[4][4] = {}, dOV[4][4] = {}, dQa[4][SD] = {}, dKa[4][SD] = {};
-  float dgcr[4] = {}, dwr[4] = {}, sgs = 0.f;
-  RowTile<float, 16, DK> st, gt;
-  RowTile<E, 16, CM> vt, ot;
+  float dT[NU][4] = {}, dOV[NU][4] = {}, dQa[NU][SD] = {}, dKa[NU][SD] = {};
+  float dgcr[NU] = {}, dwr[NU] = {}, sgs = 0.f;
+  RowTile<float, 16, DK, NTC> st, gt;
+  RowTile<E, 16, CM, NTC> vt, ot;
   auto issue = [&](int c0) {
     const float* sb = p.Sn + chunk * DK * DV + c0;
     const float* gb = p.Gn + chunk * DK * DV + c0;
@@ -441,96 +454,124 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
     ot.commit(s.u.t.dO, C, tid);
     __syncthreads();
     if (c0 + 16 < DV) issue(c0 + 16);
+    for (int d = r0; d < DK; d += RS) sgs += s.u.t.St[d][c] * s.u.t.Gt[d][c];
+    // K S, Q S and K G' on the thread's rows (four key dimensions per step)
+    float ks[NU] = {}, qs[NU] = {}, kg[NU] = {};
+#pragma unroll 2
+    for (int d = 0; d < DK; d += 4) {
+      f4 sv, gv;
 #pragma unroll
-    for (int v = 0; v < SD; ++v) sgs += s.u.t.St[r0 + 16 * v][c] * s.u.t.Gt[r0 + 16 * v][c];
-    float ks[4], qs[4], kg[4];
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = s.u.t.St[d + e][c];
+        gv[e] = s.u.t.Gt[d + e][c];
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = r0 + 16 * u;
-      ks[u] = qs[u] = kg[u] = 0.f;
-      if (u < CU) {
-#pragma unroll 8
-        for (int d = 0; d < DK; ++d) {
-          const float kv = s.K[i][d], sv = s.u.t.St[d][c];
-          ks[u] += kv * sv;
-          qs[u] += s.Q[i][d] * sv;
-          kg[u] += kv * s.u.t.Gt[d][c];
+      for (int u = 0; u < NU; ++u)
+        if (r0 + RS * u < C) {
+          const f4 kv = ld4(&s.K[r0 + RS * u][d]);
+          ks[u] += dot4(kv, sv);
+          qs[u] += dot4(ld4(&s.Q[r0 + RS * u][d]), sv);
+          kg[u] += dot4(kv, gv);
         }
-        s.u.t.Y[i][c] -= s.gam[i] * ks[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      if (r0 + RS * u < C) s.u.t.Y[r0 + RS * u][c] -= s.gam[r0 + RS * u] * ks[u];
+    __syncthreads();
+    // V~ = N diag(beta) Y; N is zero above the diagonal
+    float vt[NU] = {};
+    {
+      // up to the thread's last row, rounded up to 4
+      const int jend = r0 < C ? (r0 + RS * ((C - 1 - r0) / RS) + 4) & ~3 : 0;
+      for (int j = 0; j < jend; j += 4) {
+        const f4 bj = ld4(&s.beta[j]);
+        f4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = s.u.t.Y[j + e][c] * bj[e];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RS * u < C) vt[u] += dot4(ld4(&s.N[r0 + RS * u][j]), y);
       }
     }
-    __syncthreads();
-    float vt[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = r0 + 16 * u;
-      vt[u] = 0.f;
-      if (u < CU) {
-        for (int j = 0; j <= i; ++j) vt[u] += s.N[i][j] * s.beta[j] * s.u.t.Y[j][c];
-        s.u.t.Vt[i][c] = vt[u];
+    for (int u = 0; u < NU; ++u)
+      if (r0 + RS * u < C) s.u.t.Vt[r0 + RS * u][c] = vt[u];
+    __syncthreads();
+    // dV~ = w (K G') + P^T dO; P^T is zero below the diagonal
+    {
+      float dvt[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) dvt[u] = r0 + RS * u < C ? s.w[r0 + RS * u] * kg[u] : 0.f;
+      for (int j = r0 & ~3; j < C; j += 4) {
+        f4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = s.u.t.dO[j + e][c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RS * u < C) dvt[u] += dot4(ld4(&s.Pt[r0 + RS * u][j]), o);
       }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (r0 + RS * u < C) s.u.t.dVt[r0 + RS * u][c] = dvt[u];
     }
     __syncthreads();
+    // dY = diag(beta) N^T dV~
+    {
+      float dy[NU] = {};
+      for (int j = r0; j < C; ++j) {
+        const float x = s.u.t.dVt[j][c];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = r0 + 16 * u;
-      if (u < CU) {
-        float acc = s.w[i] * kg[u];
-        for (int j = i; j < C; ++j) acc += s.P[j][i] * s.u.t.dO[j][c];
-        s.u.t.dVt[i][c] = acc;
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RS * u < C) dy[u] += s.N[j][r0 + RS * u] * x;
       }
-    }
-    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = r0 + 16 * u;
-      if (u < CU) {
-        float acc = 0.f;
-        for (int j = i; j < C; ++j) acc += s.N[j][i] * s.u.t.dVt[j][c];
-        acc *= s.beta[i];
-        s.u.t.dY[i][c] = acc;
-        dgcr[u] += sum16(s.gam[i] * (qs[u] * s.u.t.dO[i][c] - ks[u] * acc));
-        dwr[u] += sum16(kg[u] * vt[u]);
-      }
-    }
-    __syncthreads();
-    // dT += dV~ Y^T, dOV += dO V~^T
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u >= CU) continue;
-      const int i = r0 + 16 * u;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (v >= CU) continue;
-        const int j = c + 16 * v;
-        float a = 0.f, o = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          a += s.u.t.dVt[i][e] * s.u.t.Y[j][e];
-          o += s.u.t.dO[i][e] * s.u.t.Vt[j][e];
+      for (int u = 0; u < NU; ++u) {
+        const int i = r0 + RS * u;
+        if (r0 + RS * u < C) {
+          const float acc = dy[u] * s.beta[i];
+          s.u.t.dY[i][c] = acc;
+          dgcr[u] += sum16(s.gam[i] * (qs[u] * s.u.t.dO[i][c] - ks[u] * acc));
+          dwr[u] += sum16(kg[u] * vt[u]);
         }
-        dT[u][v] += a;
-        dOV[u][v] += o;
       }
     }
-    // dQa += gam dO S^T, dKa += -gam dY S^T + w V~ G'^T
+    __syncthreads();
+    // dT += dV~ Y^T, dOV += dO V~^T; dQa += gam dO S^T, dKa += -gam dY S^T + w V~ G'^T
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u >= CU) continue;
-      const int i = r0 + 16 * u;
-      const float gi = s.gam[i], wi = s.w[i];
+    for (int e = 0; e < 16; e += 4) {
+      f4 a[NU], o[NU], dy4[NU], vt4[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (r0 + RS * u < C) {
+          const int i = r0 + RS * u;
+          a[u] = ld4(&s.u.t.dVt[i][e]);
+          o[u] = ld4(&s.u.t.dO[i][e]);
+          dy4[u] = ld4(&s.u.t.dY[i][e]);
+          vt4[u] = ld4(&s.u.t.Vt[i][e]);
+        }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (v < CU) {
+          const int j = c + 16 * v;
+          const f4 yv = ld4(&s.u.t.Y[j][e]), vv = ld4(&s.u.t.Vt[j][e]);
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            if (r0 + RS * u < C) {
+              dT[u][v] += dot4(a[u], yv);
+              dOV[u][v] += dot4(o[u], vv);
+            }
+        }
 #pragma unroll
       for (int v = 0; v < SD; ++v) {
         const int d = c + 16 * v;
-        float q = 0.f, k = 0.f;
+        const f4 sv = ld4(&s.u.t.St[d][e]), gv = ld4(&s.u.t.Gt[d][e]);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float sv = s.u.t.St[d][e];
-          q += s.u.t.dO[i][e] * sv;
-          k += wi * s.u.t.Vt[i][e] * s.u.t.Gt[d][e] - gi * s.u.t.dY[i][e] * sv;
-        }
-        dQa[u][v] += gi * q;
-        dKa[u][v] += k;
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RS * u < C) {
+            const int i = r0 + RS * u;
+            dQa[u][v] += s.gam[i] * dot4(o[u], sv);
+            dKa[u][v] += s.w[i] * dot4(vt4[u], gv) - s.gam[i] * dot4(dy4[u], sv);
+          }
       }
     }
     __syncthreads();
@@ -545,19 +586,19 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
   }
   if (c == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (u < CU) {
-        s.dgc[r0 + 16 * u] = dgcr[u];
-        s.dw[r0 + 16 * u] = dwr[u];
+    for (int u = 0; u < NU; ++u)
+      if (r0 + RS * u < C) {
+        s.dgc[r0 + RS * u] = dgcr[u];
+        s.dw[r0 + RS * u] = dwr[u];
       }
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (u < CU && v < CU) {
-        s.u.m.R0[r0 + 16 * u][c + 16 * v] = dT[u][v];
-        s.u.m.R1[r0 + 16 * u][c + 16 * v] = dOV[u][v];
+      if (r0 + RS * u < C && v < CU) {
+        s.u.m.R0[r0 + RS * u][c + 16 * v] = dT[u][v];
+        s.u.m.R1[r0 + RS * u][c + 16 * v] = dOV[u][v];
       }
   __syncthreads();
   // diag(N^T dT), and X = dT diag(beta) N^T (= dT T^T) into registers
@@ -566,33 +607,35 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
     for (int i = tid; i < C; ++i) acc += s.N[i][tid] * s.u.m.R0[i][tid];
     s.dbd[tid] = acc;
   }
-  float X[4][4];
+  float X[NU][4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       X[u][v] = 0.f;
-      if (u < CU && v < CU) {
-        const int i = r0 + 16 * u, j = c + 16 * v;
-        for (int k = 0; k <= j; ++k) X[u][v] += s.u.m.R0[i][k] * s.beta[k] * s.N[j][k];
+      if (r0 + RS * u < C && v < CU) {
+        const int i = r0 + RS * u, j = c + 16 * v;
+        // N is zero above the diagonal: k runs to j rounded up to 4
+        for (int k = 0; k <= j; k += 4)
+          X[u][v] += dot4(ld4(&s.u.m.R0[i][k]) * ld4(&s.beta[k]), ld4(&s.N[j][k]));
       }
     }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (u < CU && v < CU) s.u.m.R0[r0 + 16 * u][c + 16 * v] = X[u][v];
+      if (r0 + RS * u < C && v < CU) s.u.m.R0[r0 + RS * u][c + 16 * v] = X[u][v];
   __syncthreads();
   // dA = -strictLower(N^T X); K K^T recomputed into R2
-  float dA[4][4];
+  float dA[NU][4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       dA[u][v] = 0.f;
-      const int i = r0 + 16 * u, j = c + 16 * v;
-      if (u < CU && v < CU) {
+      const int i = r0 + RS * u, j = c + 16 * v;
+      if (r0 + RS * u < C && v < CU) {
         if (j < i) {
           float acc = 0.f;
           for (int k = i; k < C; ++k) acc += s.N[k][i] * s.u.m.R0[k][j];
@@ -601,26 +644,26 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
         float kk = 0.f;
         if (j < i) {
 #pragma unroll 8
-          for (int d = 0; d < DK; ++d) kk += s.K[i][d] * s.K[j][d];
+          for (int d = 0; d < DK; d += 4) kk += dot4(ld4(&s.K[i][d]), ld4(&s.K[j][d]));
         }
         s.u.m.R2[i][j] = kk;
       }
     }
   __syncthreads();
   // per entry: the gate-prefix term t, dbeta's row term, dGm and E1 = Gam * dOV (lower)
-  float t[4][4], dGm[4][4], E1[4][4], rb[4] = {}, rt[4] = {};
+  float t[NU][4], dGm[NU][4], E1[NU][4], rb[NU] = {}, rt[NU] = {};
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       t[u][v] = dGm[u][v] = E1[u][v] = 0.f;
-      const int i = r0 + 16 * u, j = c + 16 * v;
-      if (u < CU && v < CU && j <= i) {
+      const int i = r0 + RS * u, j = c + 16 * v;
+      if (r0 + RS * u < C && v < CU && j <= i) {
         const float gm = expf(s.gc[i] - s.gc[j]);
         const float kk = s.u.m.R2[i][j], dov = s.u.m.R1[i][j];
         const float ta = dA[u][v] * gm * kk;  // zero on the diagonal
         rb[u] += ta;
-        t[u][v] = s.beta[i] * ta + s.P[i][j] * dov;
+        t[u][v] = s.beta[i] * ta + s.Pt[j][i] * dov;
         dGm[u][v] = s.beta[i] * gm * dA[u][v];
         E1[u][v] = gm * dov;
         rt[u] += t[u][v];
@@ -628,19 +671,19 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
     }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NU; ++u) {
     rb[u] = sum16(rb[u]);
     rt[u] = sum16(rt[u]);
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (u < CU && v < CU) {
-        const int i = r0 + 16 * u, j = c + 16 * v;
+      if (r0 + RS * u < C && v < CU) {
+        const int i = r0 + RS * u, j = c + 16 * v;
         s.u.m.R0[i][j] = dGm[u][v];
         s.u.m.R1[i][j] = E1[u][v];
         s.u.m.R2[i][j] = t[u][v];
       }
-    if (c == 0 && u < CU) {
-      const int i = r0 + 16 * u;
+    if (c == 0 && r0 + RS * u < C) {
+      const int i = r0 + RS * u;
       s.dbd[i] += rb[u];
       s.rsum[i] = rt[u];
     }
@@ -657,7 +700,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
   if (tid == 0 && p.dg_log) {
     float tot = 0.f;
     for (int i = 0; i < C; ++i) tot += s.w[i] * s.dw[i];
-    for (int o = 0; o < NTH / WAVE; ++o) tot += expf(gC) * s.sgs[o];
+    for (int o = 0; o < NTC / WAVE; ++o) tot += expf(gC) * s.sgs[o];
     // reverse cumulative sum over the chunk; the last position also collects the total above
     float run = tot;
     for (int i = C - 1; i >= 0; --i) {
@@ -666,23 +709,37 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_kernel(BwdParams p) {
       if (i < valid && pos % nh == 0) p.dg_log[(b * (long)p.L + pos / nh) * p.H + h] = run;
     }
   }
-  // dQ = dQa + E1 K,  dK = dKa + E1^T Q + (dGm + dGm^T) K
+  // dQ = dQa + E1 K,  dK = dKa + E1^T Q + (dGm + dGm^T) K  (E1 lower, dGm strictly lower)
+  for (int j = 0; j < C; ++j) {
+    float kj[SD], qj[SD];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if (u >= CU) continue;
-    const int i = r0 + 16 * u;
+    for (int v = 0; v < SD; ++v) {
+      kj[v] = s.K[j][c + 16 * v];
+      qj[v] = s.Q[j][c + 16 * v];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      if (r0 + RS * u < C) {
+        const int i = r0 + RS * u;
+        const float e1 = s.u.m.R1[i][j], e1t = s.u.m.R1[j][i], gs = s.u.m.R0[i][j] + s.u.m.R0[j][i];
+#pragma unroll
+        for (int v = 0; v < SD; ++v) {
+          dQa[u][v] += e1 * kj[v];
+          dKa[u][v] += e1t * qj[v] + gs * kj[v];
+        }
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int i = r0 + RS * u;
+    if (i >= C || i >= valid) continue;
     const long pos = P0 + i;
-    if (i >= valid) continue;
-    const bool last = pos % nh == nh - 1;
+    const bool is_last = pos % nh == nh - 1;
 #pragma unroll
     for (int v = 0; v < SD; ++v) {
       const int d = c + 16 * v;
-      float dq = dQa[u][v], dk = dKa[u][v];
-      for (int j = 0; j <= i; ++j) dq += s.u.m.R1[i][j] * s.K[j][d];
-      for (int j = i; j < C; ++j) dk += s.u.m.R1[j][i] * s.Q[j][d];
-      for (int j = 0; j < C; ++j) dk += (s.u.m.R0[i][j] + s.u.m.R0[j][i]) * s.K[j][d];
-      p.dk[((b * (long)p.Lx + pos) * p.H + h) * DK + d] = dk;
-      if (last) p.dq[((b * (long)p.L + pos / nh) * p.H + h) * DK + d] = p.scale * dq;
+      p.dk[((b * (long)p.Lx + pos) * p.H + h) * DK + d] = dKa[u][v];
+      if (is_last) p.dq[((b * (long)p.L + pos / nh) * p.H + h) * DK + d] = p.scale * dQa[u][v];
     }
   }
 }
@@ -696,7 +753,7 @@ hipError_t launch_by_dk(const BwdParams& p, int which, hipStream_t st) {
   case D:                                                                                        \
     if (which == 0) hipLaunchKernelGGL((bwd_states_kernel<E, D>), gs, block, 0, st, p);         \
     else if (which == 1) hipLaunchKernelGGL((bwd_dstates_kernel<E, D>), gs, block, 0, st, p);   \
-    else if (which == 2) hipLaunchKernelGGL((bwd_chunk_kernel<E, D>), gc, block, 0, st, p);     \
+    else if (which == 2) hipLaunchKernelGGL((bwd_chunk_kernel<E, D>), gc, dim3(NTC), 0, st, p); \
     else hipLaunchKernelGGL((bwd_qk_kernel<E, D>), gc, block, 0, st, p);                         \
     break;
   switch (p.DK) {
