@@ -77,7 +77,7 @@ struct RowTile {
       r[u] = q ? *reinterpret_cast<const u32x4*>(q + j) : u32x4{0, 0, 0, 0};
     }
   }
-  template <int PITCH>
+  template <int PITCH, bool TRANSPOSE = false>
   __device__ inline void commit(float (*dst)[PITCH], int rows, int tid, float mul = 1.f) const {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -86,7 +86,12 @@ struct RowTile {
         float x[VE];
         unpack16<E>(r[u], x);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) dst[i][j + e] = mul * x[e];
+        for (int e = 0; e < VE; ++e) {
+          if (TRANSPOSE)
+            dst[j + e][i] = mul * x[e];
+          else
+            dst[i][j + e] = mul * x[e];
+        }
       }
     }
   }
@@ -129,13 +134,21 @@ __device__ inline float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * 
 
 // Chunk rows i of a 16-column tile are owned by threads with (tid >> 4) == i % 16, column tid & 15.
 
+// The two scans run 512 threads per (head, 16 state columns): thread (r0, c) = (tid >> 4,
+// tid & 15) owns state rows r0 + 32 u and chunk rows r0 + 32 u of column c.  K (and Q, T, P)
+// sit in LDS both as loaded and transposed, so that every product reads 16-byte vectors along
+// its summed index.
+constexpr int NTS = 512, RSS = NTS / 16;
+
 template <typename E, int DK>
-__global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
-  __shared__ float Kl[CM][DK + 1];
-  __shared__ float Tl[CM][CM + 1];
+__global__ __launch_bounds__(NTS) void bwd_states_kernel(BwdParams p) {
+  constexpr int RD = (DK + RSS - 1) / RSS, NU = CM / RSS;
+  __shared__ __attribute__((aligned(16))) float Kl[CM][DK + 4];
+  __shared__ __attribute__((aligned(16))) float Kt[DK][CM + 4];
+  __shared__ __attribute__((aligned(16))) float Tl[CM][CM + 4];
   __shared__ float Sl[DK][17];
   __shared__ float Yl[CM][17];  // V, then Y in place
-  __shared__ float Vt[CM][17];
+  __shared__ float Wv[CM][17];  // w * V~
   __shared__ float gcl[CM], gam[CM], wl[CM];
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
   const int ntile = p.DV / 16, c0 = (int)(blockIdx.x % ntile) * 16, bh = (int)(blockIdx.x / ntile);
@@ -144,14 +157,16 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
   const long HDK = (long)p.H * DK, HDV = (long)p.H * DV;
   const E* kb = static_cast<const E*>(p.k) + (long)b * p.Lx * HDK + (long)h * DK;
   const E* vb = static_cast<const E*>(p.v) + (long)b * p.Lx * HDV + (long)h * DV + c0;
-  constexpr int RD = DK / 16;
   float S[RD];
 #pragma unroll
-  for (int u = 0; u < RD; ++u) S[u] = p.S0 ? p.S0[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] : 0.f;
+  for (int u = 0; u < RD; ++u) {
+    const int d = r0 + RSS * u;
+    S[u] = p.S0 && d < DK ? p.S0[((long)bh * DK + d) * DV + c0 + c] : 0.f;
+  }
 
-  RowTile<E, DK, CM> kt;
-  RowTile<E, 16, CM> vt;
-  SquareTile<> tt;
+  RowTile<E, DK, CM, NTS> kt;
+  RowTile<E, 16, CM, NTS> vt;
+  SquareTile<NTS> tt;
   float gv = 0.f;
   auto issue = [&](int n) {
     const long P0 = (long)n * C;
@@ -165,13 +180,17 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
   for (int n = 0; n < NT; ++n) {
     const long chunk = (long)bh * NT + n;
     kt.commit(Kl, C, tid);
+    kt.template commit<CM + 4, true>(Kt, C, tid);
     vt.commit(Yl, C, tid);
-    tt.commit(Tl, C, tid);
+    tt.template commit<CM + 4>(Tl, C, tid);
     if (tid < C) gcl[tid] = gv;
 #pragma unroll
     for (int u = 0; u < RD; ++u) {
-      p.Sn[(chunk * DK + r0 + 16 * u) * DV + c0 + c] = S[u];
-      Sl[r0 + 16 * u][c] = S[u];
+      const int d = r0 + RSS * u;
+      if (d < DK) {
+        p.Sn[(chunk * DK + d) * DV + c0 + c] = S[u];
+        Sl[d][c] = S[u];
+      }
     }
     __syncthreads();
     const float gC = gcl[C - 1];
@@ -182,28 +201,52 @@ __global__ __launch_bounds__(NTH) void bwd_states_kernel(BwdParams p) {
     if (n + 1 < NT) issue(n + 1);  // the next chunk's loads fly while this one computes
     __syncthreads();
     // Y = V - gam K S
-    for (int i = r0; i < C; i += 16) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < DK; ++d) acc += Kl[i][d] * Sl[d][c];
-      Yl[i][c] -= gam[i] * acc;
+    {
+      float acc[NU] = {};
+      for (int d = 0; d < DK; d += 4) {
+        f4 sv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[e] = Sl[d + e][c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RSS * u < C) acc[u] += dot4(ld4(&Kl[r0 + RSS * u][d]), sv);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (r0 + RSS * u < C) Yl[r0 + RSS * u][c] -= gam[r0 + RSS * u] * acc[u];
     }
     __syncthreads();
-    // V~ = T Y (T lower triangular)
-    for (int i = r0; i < C; i += 16) {
-      float acc = 0.f;
-      for (int j = 0; j <= i; ++j) acc += Tl[i][j] * Yl[j][c];
-      Vt[i][c] = acc;
+    // w * V~ with V~ = T Y (T zero above the diagonal: j up to the thread's last row)
+    {
+      float acc[NU] = {};
+      const int jend = r0 < C ? (r0 + RSS * ((C - 1 - r0) / RSS) + 4) & ~3 : 0;
+      for (int j = 0; j < jend; j += 4) {
+        f4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = Yl[j + e][c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RSS * u < C) acc[u] += dot4(ld4(&Tl[r0 + RSS * u][j]), y);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (r0 + RSS * u < C) Wv[r0 + RSS * u][c] = wl[r0 + RSS * u] * acc[u];
     }
     __syncthreads();
     // S <- gam_C S + K^T (w V~)
-    const float eC = expf(gC);
+    {
+      const float eC = expf(gC);
+      float acc[RD] = {};
+      for (int i = 0; i < C; i += 4) {
+        f4 x;
 #pragma unroll
-    for (int u = 0; u < RD; ++u) {
-      const int d = r0 + 16 * u;
-      float acc = 0.f;
-      for (int i = 0; i < C; ++i) acc += wl[i] * Kl[i][d] * Vt[i][c];
-      S[u] = eC * S[u] + acc;
+        for (int e = 0; e < 4; ++e) x[e] = Wv[i + e][c];
+#pragma unroll
+        for (int u = 0; u < RD; ++u)
+          if (r0 + RSS * u < DK) acc[u] += dot4(ld4(&Kt[r0 + RSS * u][i]), x);
+      }
+#pragma unroll
+      for (int u = 0; u < RD; ++u) S[u] = eC * S[u] + acc[u];
     }
     __syncthreads();
   }
@@ -246,16 +289,19 @@ __global__ __launch_bounds__(NTH) void bwd_qk_kernel(BwdParams p) {
 }
 
 template <typename E, int DK>
-__global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
-  __shared__ float Kl[CM][DK + 1];
-  __shared__ float Ql[CM][DK + 1];
-  __shared__ float Tl[CM][CM + 1];
-  __shared__ float Pl[CM][CM + 1];
+__global__ __launch_bounds__(NTS) void bwd_dstates_kernel(BwdParams p) {
+  constexpr int RD = (DK + RSS - 1) / RSS, NU = CM / RSS;
+  __shared__ __attribute__((aligned(16))) float Kl[CM][DK + 4];
+  __shared__ __attribute__((aligned(16))) float Kt[DK][CM + 4];
+  __shared__ __attribute__((aligned(16))) float Qt[DK][CM + 4];
+  __shared__ __attribute__((aligned(16))) float Tt[CM][CM + 4];  // T^T
+  __shared__ __attribute__((aligned(16))) float Pt[CM][CM + 4];  // P^T
   __shared__ float Gl[DK][17];
   __shared__ float dOl[CM][17];
   __shared__ float dVt[CM][17];
   __shared__ float dYl[CM][17];
-  __shared__ float gcl[CM], gam[CM], wl[CM];
+  __shared__ __attribute__((aligned(16))) float gam[CM];
+  __shared__ float gcl[CM], wl[CM];
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
   const int ntile = p.DV / 16, c0 = (int)(blockIdx.x % ntile) * 16, bh = (int)(blockIdx.x / ntile);
   const int b = bh / p.H, h = bh % p.H;
@@ -264,14 +310,16 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
   const E* kb = static_cast<const E*>(p.k) + (long)b * p.Lx * HDK + (long)h * DK;
   const E* qb = static_cast<const E*>(p.q) + (long)b * p.L * HDK + (long)h * DK;
   const E* ob = static_cast<const E*>(p.dO) + (long)b * p.L * HDV + (long)h * DV + c0;
-  constexpr int RD = DK / 16;
   float G[RD];
 #pragma unroll
-  for (int u = 0; u < RD; ++u) G[u] = p.dS_final ? p.dS_final[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] : 0.f;
+  for (int u = 0; u < RD; ++u) {
+    const int d = r0 + RSS * u;
+    G[u] = p.dS_final && d < DK ? p.dS_final[((long)bh * DK + d) * DV + c0 + c] : 0.f;
+  }
 
-  RowTile<E, DK, CM> kt, qt;
-  RowTile<E, 16, CM> ot;
-  SquareTile<> tt, pt;
+  RowTile<E, DK, CM, NTS> kt, qt;
+  RowTile<E, 16, CM, NTS> ot;
+  SquareTile<NTS> tt, pt;
   float gv = 0.f;
   auto issue = [&](int n) {
     const long P0 = (long)n * C, chunk = (long)bh * NT + n;
@@ -290,15 +338,19 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
     const int valid = (int)min((long)C, (long)p.Lx - P0);
     const long chunk = (long)bh * NT + n;
     kt.commit(Kl, C, tid);
-    qt.commit(Ql, C, tid, p.scale);
+    kt.template commit<CM + 4, true>(Kt, C, tid);
+    qt.template commit<CM + 4, true>(Qt, C, tid, p.scale);
     ot.commit(dOl, C, tid);
-    tt.commit(Tl, C, tid);
-    pt.commit(Pl, C, tid);
+    tt.template commit<CM + 4, true>(Tt, C, tid);
+    pt.template commit<CM + 4, true>(Pt, C, tid);
     if (tid < C) gcl[tid] = gv;
 #pragma unroll
     for (int u = 0; u < RD; ++u) {
-      p.Gn[(chunk * DK + r0 + 16 * u) * DV + c0 + c] = G[u];
-      Gl[r0 + 16 * u][c] = G[u];
+      const int d = r0 + RSS * u;
+      if (d < DK) {
+        p.Gn[(chunk * DK + d) * DV + c0 + c] = G[u];
+        Gl[d][c] = G[u];
+      }
     }
     __syncthreads();
     const float gC = gcl[C - 1];
@@ -308,38 +360,79 @@ __global__ __launch_bounds__(NTH) void bwd_dstates_kernel(BwdParams p) {
     }
     if (n > 0) issue(n - 1);
     __syncthreads();
-    // dV~ = w (K G') + P^T dO
-    for (int i = r0; i < C; i += 16) {
-      float kg = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < DK; ++d) kg += Kl[i][d] * Gl[d][c];
-      float acc = wl[i] * kg;
-      for (int j = i; j < C; ++j) acc += Pl[j][i] * dOl[j][c];
-      dVt[i][c] = acc;
+    // dV~ = w (K G') + P^T dO  (P^T zero below the diagonal: j from the thread's first row)
+    {
+      float kg[NU] = {}, acc[NU] = {};
+      for (int d = 0; d < DK; d += 4) {
+        f4 gv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gv4[e] = Gl[d + e][c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RSS * u < C) kg[u] += dot4(ld4(&Kl[r0 + RSS * u][d]), gv4);
+      }
+      for (int j = r0 & ~3; j < C; j += 4) {
+        f4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = dOl[j + e][c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RSS * u < C) acc[u] += dot4(ld4(&Pt[r0 + RSS * u][j]), o);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (r0 + RSS * u < C) dVt[r0 + RSS * u][c] = wl[r0 + RSS * u] * kg[u] + acc[u];
     }
     __syncthreads();
-    // dY = T^T dV~, which is dV
-    for (int i = r0; i < C; i += 16) {
-      float acc = 0.f;
-      for (int j = i; j < C; ++j) acc += Tl[j][i] * dVt[j][c];
-      dYl[i][c] = acc;
-      if (i < valid) p.dv[((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c] = acc;
+    // dY = T^T dV~, which is dV  (T^T zero below the diagonal)
+    {
+      float acc[NU] = {};
+      for (int j = r0 & ~3; j < C; j += 4) {
+        f4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dVt[j + e][c];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (r0 + RSS * u < C) acc[u] += dot4(ld4(&Tt[r0 + RSS * u][j]), x);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int i = r0 + RSS * u;
+        if (i < C) {
+          dYl[i][c] = acc[u];
+          if (i < valid) p.dv[((b * (long)p.Lx + P0 + i) * p.H + h) * DV + c0 + c] = acc[u];
+        }
+      }
     }
     __syncthreads();
     // G <- gam_C G' - K^T (gam dY) + (gam Q)^T dO
-    const float eC = expf(gC);
+    {
+      const float eC = expf(gC);
+      float acc[RD] = {};
+      for (int i = 0; i < C; i += 4) {
+        const f4 g4 = ld4(&gam[i]);
+        f4 o, y;
 #pragma unroll
-    for (int u = 0; u < RD; ++u) {
-      const int d = r0 + 16 * u;
-      float acc = 0.f;
-      for (int i = 0; i < C; ++i) acc += gam[i] * (Ql[i][d] * dOl[i][c] - Kl[i][d] * dYl[i][c]);
-      G[u] = eC * G[u] + acc;
+        for (int e = 0; e < 4; ++e) {
+          o[e] = g4[e] * dOl[i + e][c];
+          y[e] = g4[e] * dYl[i + e][c];
+        }
+#pragma unroll
+        for (int u = 0; u < RD; ++u)
+          if (r0 + RSS * u < DK)
+            acc[u] += dot4(ld4(&Qt[r0 + RSS * u][i]), o) - dot4(ld4(&Kt[r0 + RSS * u][i]), y);
+      }
+#pragma unroll
+      for (int u = 0; u < RD; ++u) G[u] = eC * G[u] + acc[u];
     }
     __syncthreads();
   }
   if (p.dS0) {
 #pragma unroll
-    for (int u = 0; u < RD; ++u) p.dS0[((long)bh * DK + r0 + 16 * u) * DV + c0 + c] = G[u];
+    for (int u = 0; u < RD; ++u) {
+      const int d = r0 + RSS * u;
+      if (d < DK) p.dS0[((long)bh * DK + d) * DV + c0 + c] = G[u];
+    }
   }
 }
 
@@ -399,7 +492,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_kernel(BwdParams p) {
     pt.issue(p.Pm + chunk * C * C, C, tid);
     kt.commit(s.K, C, tid);
     qt.commit(s.Q, C, tid, p.scale);
-    pt.commit<CM + 4, true>(s.Pt, C, tid);
+    pt.template commit<CM + 4, true>(s.Pt, C, tid);
   }
   const float gC = p.gc[chunk * C + C - 1];
   if (tid < C) {
@@ -751,8 +844,8 @@ hipError_t launch_by_dk(const BwdParams& p, int which, hipStream_t st) {
   const dim3 gs((unsigned)((long)p.DV / 16 * p.B * p.H)), gc((unsigned)((long)p.NT * p.B * p.H));
 #define DELTA_BWD_CASE(D)                                                                        \
   case D:                                                                                        \
-    if (which == 0) hipLaunchKernelGGL((bwd_states_kernel<E, D>), gs, block, 0, st, p);         \
-    else if (which == 1) hipLaunchKernelGGL((bwd_dstates_kernel<E, D>), gs, block, 0, st, p);   \
+    if (which == 0) hipLaunchKernelGGL((bwd_states_kernel<E, D>), gs, dim3(NTS), 0, st, p);     \
+    else if (which == 1) hipLaunchKernelGGL((bwd_dstates_kernel<E, D>), gs, dim3(NTS), 0, st, p); \
     else if (which == 2) hipLaunchKernelGGL((bwd_chunk_kernel<E, D>), gc, dim3(NTC), 0, st, p); \
     else hipLaunchKernelGGL((bwd_qk_kernel<E, D>), gc, block, 0, st, p);                         \
     break;
