@@ -18,6 +18,10 @@ ut_factors(...) the per-chunk UT transform T = (I + strictLower(diag(beta)
                 W = T (gamma * K), U = T V, written from their definitions with a
                 library triangular solve (what delta_chunk_wy computes).
 
+layer (module)  the layer steps around the token mixer: causal depthwise ShortConv, SiLU,
+                per-head L2 norm (prologue), RMS norm times a SiLU gate (epilogue), in
+                numpy fp64; pinned in tests/test_oracle_layer.py.
+
 All of them are pinned in tests/test_oracle_pins.py (closed forms, brute force,
 independent formulations, finite differences); none is "parity unpinned".
 """
