@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -70,11 +70,13 @@ def load_library():
     lib.delta_decode_kda.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_bwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.delta_bwd.argtypes = [SP] + [P] * 15 + [ctypes.c_size_t, P]
+    lib.delta_layer_prologue.argtypes = [SP, ctypes.c_int32, ctypes.c_float] + [P] * 9 + [P]
+    lib.delta_layer_epilogue.argtypes = [SP, ctypes.c_float, P, P, P, P, P]
     lib.delta_strerror.argtypes = [ctypes.c_int]
     lib.delta_strerror.restype = ctypes.c_char_p
     for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_intra, lib.delta_fwd_inter,
               lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda, lib.delta_bwd_workspace_bytes,
-              lib.delta_bwd):
+              lib.delta_bwd, lib.delta_layer_prologue, lib.delta_layer_epilogue):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -214,6 +216,39 @@ def bwd(q, k, v, beta, g_log=None, S0=None, dO=None, dS_final=None, *, n_h: int 
                        workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "delta_bwd")
     return g
+
+
+def layer_prologue(xq, xk, xv, wq, wk, wv, *, n_h: int = 1, eps: float = 1e-6, q=None, k=None, v=None,
+                   stream=None):
+    """q, k = L2norm(SiLU(ShortConv(xq | xk))), v = SiLU(ShortConv(xv)) (delta_layer_prologue).
+    xq [B, L, H, dk], xk [B, L*n_h, H, dk], xv [B, L*n_h, H, dv]; w* float32 [H*d, width]."""
+    torch = _torch()
+    B, L, H, dk = xq.shape
+    dv, width = xv.shape[-1], wq.shape[-1]
+    sh = make_shape(B, L, H, dk, dv, n_h, 64 if 64 % n_h == 0 else n_h, _dtype_code(xq))
+    q = torch.empty_like(xq) if q is None else q
+    k = torch.empty_like(xk) if k is None else k
+    v = torch.empty_like(xv) if v is None else v
+    f32 = torch.float32
+    rc = load_library().delta_layer_prologue(ctypes.byref(sh), int(width), float(eps), _dev(xq, "xq", xq.dtype),
+                                             _dev(xk, "xk", xq.dtype), _dev(xv, "xv", xq.dtype), _dev(wq, "wq", f32),
+                                             _dev(wk, "wk", f32), _dev(wv, "wv", f32), _dev(q, "q", xq.dtype),
+                                             _dev(k, "k", xq.dtype), _dev(v, "v", xq.dtype), _stream(stream))
+    _check(rc, "delta_layer_prologue")
+    return q, k, v
+
+
+def layer_epilogue(o, g, weight, *, eps: float = 1e-6, y=None, stream=None):
+    """y = RMSNorm(o) * weight * SiLU(g) per head (delta_layer_epilogue); o, g [B, L, H, dv]."""
+    torch = _torch()
+    B, L, H, dv = o.shape
+    sh = make_shape(B, L, H, 16, dv, 1, 64, _dtype_code(o))
+    y = torch.empty_like(o) if y is None else y
+    rc = load_library().delta_layer_epilogue(ctypes.byref(sh), float(eps), _dev(o, "o", o.dtype), _dev(g, "g", o.dtype),
+                                             _dev(weight, "weight", torch.float32), _dev(y, "y", o.dtype),
+                                             _stream(stream))
+    _check(rc, "delta_layer_epilogue")
+    return y
 
 
 def fwd_intra(k, beta, g_log, workspace, *, n_h: int = 1, chunk: int = 64, dv: int = None, stream=None):

@@ -11,6 +11,7 @@
 using delta::BwdParams;
 using delta::DecodeParams;
 using delta::FwdParams;
+using delta::LayerParams;
 
 namespace {
 
@@ -455,6 +456,65 @@ int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const v
   if (s->n_h != 1) return DELTA_ERR_BAD_SHAPE;
   if ((size_t)s->B * s->H > 0 && !a_log) return DELTA_ERR_NULL_ARG;
   return run_decode(s, q, k, v, beta, nullptr, a_log, S, O, stream);
+}
+
+int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const void* xq, const void* xk,
+                         const void* xv, const float* wq, const float* wk, const float* wv, void* q, void* k,
+                         void* v, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (width < 1 || width > 4) return DELTA_ERR_UNSUPPORTED_DIM;
+  if (!(eps >= 0.f)) return DELTA_ERR_BAD_SHAPE;
+  const size_t es = esize(s->dtype);
+  const size_t rq = (size_t)s->B * s->L * s->H, rkv = rq * s->n_h;
+  if ((rkv + 3) / 4 > 0x7fffffffu) return DELTA_ERR_BAD_SHAPE;
+  if ((rq > 0 && (!xq || !wq || !q)) || (rkv > 0 && (!xk || !xv || !wk || !wv || !k || !v)))
+    return DELTA_ERR_NULL_ARG;
+  const void* ptrs[] = {xq, xk, xv, wq, wk, wv, q, k, v};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  const Range in[] = {range(xq, rq * s->dk * es), range(xk, rkv * s->dk * es), range(xv, rkv * s->dv * es),
+                      range(wq, (size_t)s->H * s->dk * width * 4), range(wk, (size_t)s->H * s->dk * width * 4),
+                      range(wv, (size_t)s->H * s->dv * width * 4)};
+  const Range out[] = {range(q, rq * s->dk * es), range(k, rkv * s->dk * es), range(v, rkv * s->dv * es)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return DELTA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], out[j])) return DELTA_ERR_ALIAS;
+  }
+  if (rkv == 0) return DELTA_OK;  // nothing to do (rq <= rkv)
+  LayerParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = s->B, p.L = s->L, p.H = s->H, p.DK = s->dk, p.DV = s->dv, p.Lx = s->L * s->n_h, p.width = width;
+  p.eps = eps;
+  p.xq = xq, p.xk = xk, p.xv = xv, p.wq = wq, p.wk = wk, p.wv = wv, p.q = q, p.k = k, p.v = v;
+  return hip_status(delta::launch_layer_prologue(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int delta_layer_epilogue(const delta_shape* s, float eps, const void* o, const void* g, const float* weight,
+                         void* y, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!(eps >= 0.f)) return DELTA_ERR_BAD_SHAPE;
+  const size_t es = esize(s->dtype);
+  const size_t rows = (size_t)s->B * s->L * s->H;
+  if ((rows + 3) / 4 > 0x7fffffffu) return DELTA_ERR_BAD_SHAPE;
+  if (rows > 0 && (!o || !g || !weight || !y)) return DELTA_ERR_NULL_ARG;
+  const void* ptrs[] = {o, g, weight, y};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  const Range ro = range(o, rows * s->dv * es), rg = range(g, rows * s->dv * es), rw = range(weight, (size_t)s->dv * 4),
+              ry = range(y, rows * s->dv * es);
+  // y may be o itself (each row is read whole before it is written); no other overlap
+  if ((overlap(ry, ro) && y != o) || overlap(ry, rg) || overlap(ry, rw)) return DELTA_ERR_ALIAS;
+  if (rows == 0) return DELTA_OK;
+  LayerParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = s->B, p.L = s->L, p.H = s->H, p.DK = s->dk, p.DV = s->dv, p.Lx = s->L * s->n_h;
+  p.eps = eps;
+  p.o = o, p.g = g, p.weight = weight, p.y = y;
+  return hip_status(delta::launch_layer_epilogue(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 const char* delta_strerror(int code) {

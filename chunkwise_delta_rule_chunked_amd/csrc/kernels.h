@@ -68,6 +68,19 @@ struct BwdParams {
   float* Gn;              // [B*H, NT, DK, DV] state gradient at the end of each chunk
 };
 
+// The layer steps around the mixer (layer.hip).
+struct LayerParams {
+  int B, L, H, DK, DV, Lx, width;
+  float eps;
+  const void *xq, *xk, *xv;       // prologue inputs [B, L, H, DK], [B, Lx, H, DK], [B, Lx, H, DV]
+  const float *wq, *wk, *wv;      // [H * d, width] conv filters
+  void *q, *k, *v;                // prologue outputs, shapes as the inputs
+  const void* o;                  // epilogue: mixer output [B, L, H, DV]
+  const void* g;                  // gate projection [B, L, H, DV]
+  const float* weight;            // [DV]
+  void* y;                        // [B, L, H, DV]
+};
+
 // Each returns hipSuccess or the launch error.  `bf16` selects the element type of
 // q/k/v/O (true: bfloat16, false: float32).
 hipError_t launch_intra_chunk(const FwdParams& p, bool bf16, bool t_as_float, hipStream_t st);
@@ -83,6 +96,8 @@ hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 // 3 Q K^T * Gam per chunk, 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0),
 // 2 per-chunk gradients.
 hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_t st);
+hipError_t launch_layer_prologue(const LayerParams& p, bool bf16, hipStream_t st);
+hipError_t launch_layer_epilogue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
 
 }  // namespace delta

@@ -217,6 +217,33 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
               float* dk, float* dv, float* dbeta, float* dg_log, float* dS0, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/*
+ * Layer prologue ("08 linear delta rule & DPLR" page, Gated DeltaNet layer-design figure after
+ * section 3: q/k through ShortConv, SiLU and L2 norm, v through ShortConv and SiLU), applied to
+ * the projections before delta_fwd.  Per channel c = head * d + i, a causal depthwise filter of
+ * `width` taps (1..4; tap width-1 multiplies the current token, earlier tokens of the same
+ * sequence before it, zeros before the first token), then SiLU(x) = x / (1 + exp(-x)); q and k
+ * rows (one head of one token) are then divided by sqrt(sum of squares + eps).
+ *   xq [B, L, H, dk], xk [B, L*n_h, H, dk], xv [B, L*n_h, H, dv]     dtype    inputs
+ *   wq, wk [H*dk, width], wv [H*dv, width]                           float32  filters
+ *   q, k, v                                  shapes of xq, xk, xv   dtype    outputs (written)
+ * k and v are filtered along their L*n_h rows in order.  Outputs may not overlap any input or
+ * each other.  16-byte aligned pointers.  s->chunk and s->scale are ignored.  Error codes as
+ * delta_fwd (width outside 1..4: DELTA_ERR_UNSUPPORTED_DIM; eps < 0: DELTA_ERR_BAD_SHAPE).
+ */
+int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const void* xq, const void* xk,
+                         const void* xv, const float* wq, const float* wk, const float* wv, void* q, void* k,
+                         void* v, void* stream);
+
+/*
+ * Layer epilogue (same figure: Norm, then the output gate): per head of each token,
+ *   y = o / sqrt(mean(o^2) + eps) * weight * SiLU(g)
+ *   o, g, y [B, L, H, dv] dtype; weight [dv] float32 (shared by the heads).
+ * y may be o itself (in place); no other overlap.  16-byte aligned pointers.
+ */
+int delta_layer_epilogue(const delta_shape* s, float eps, const void* o, const void* g, const float* weight,
+                         void* y, void* stream);
+
 /* Static description of a return code. */
 const char* delta_strerror(int code);
 

@@ -24,7 +24,8 @@ def test_exports_every_header_function(lib):
     assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_intra", "delta_fwd_inter",
                           "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
                           "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_decode_kda",
-                          "delta_bwd_workspace_bytes", "delta_bwd", "delta_strerror"}
+                          "delta_bwd_workspace_bytes", "delta_bwd", "delta_layer_prologue",
+                          "delta_layer_epilogue", "delta_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -203,6 +204,20 @@ def test_bwd_argument_errors(lib, no_gpu):
     assert call_bwd(sh, dS0=fake(9)) == -6                  # dS0 inside the workspace
     assert call_bwd(shape(chunk=24)) == -3
     assert D.load_library().delta_bwd(ctypes.byref(shape(B=0)), *[None] * 15, ctypes.c_size_t(0), None) == 0
+
+
+def test_layer_argument_errors(lib, no_gpu):
+    L = D.load_library()
+    sh = shape()
+    f = [fake(i) for i in range(9)]
+    assert L.delta_layer_prologue(ctypes.byref(sh), 5, ctypes.c_float(1e-6), *f, None) == -3     # width
+    assert L.delta_layer_prologue(ctypes.byref(sh), 4, ctypes.c_float(-1.0), *f, None) == -2     # eps < 0
+    assert L.delta_layer_prologue(ctypes.byref(sh), 4, ctypes.c_float(1e-6), None, *f[1:], None) == -1
+    assert L.delta_layer_prologue(ctypes.byref(sh), 4, ctypes.c_float(1e-6), *f[:6], f[0], f[7], f[8], None) == -6
+    assert L.delta_layer_prologue(ctypes.byref(sh), 4, ctypes.c_float(1e-6), *f[:8], ctypes.c_void_p(A * 9 + 4), None) == -4
+    assert L.delta_layer_epilogue(ctypes.byref(sh), ctypes.c_float(1e-6), f[0], f[1], f[2], f[1], None) == -6  # y aliases g
+    assert L.delta_layer_epilogue(ctypes.byref(sh), ctypes.c_float(1e-6), f[0], None, f[2], f[3], None) == -1
+    assert L.delta_layer_epilogue(ctypes.byref(shape(B=0)), ctypes.c_float(1e-6), None, None, None, None, None) == 0
 
 
 def test_chunk_wy_argument_errors(lib, no_gpu):
