@@ -339,6 +339,43 @@ def time_backward(w, steps, warmup=2):
             "workspace_mib": round(ws.numel() / 2**20, 1)}
 
 
+def time_layer(w, steps, width=4):
+    """delta_layer_prologue and delta_layer_epilogue on the workload's shapes (seeded inputs),
+    `steps` calls each timed with HIP events; GB/s from the bytes each must move (inputs read
+    once, outputs written once, filters and weights)."""
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
+    g = torch.Generator(device="cpu").manual_seed(2026)
+    mk = lambda *shape: torch.randn(*shape, generator=g).to(dt).cuda()
+    Lx = w.L * w.n_h
+    xq, xk, xv = mk(w.B, w.L, w.H, w.dk), mk(w.B, Lx, w.H, w.dk), mk(w.B, Lx, w.H, w.dv)
+    wq, wk, wv = (torch.randn(w.H * d, width, generator=g).cuda() for d in (w.dk, w.dk, w.dv))
+    o, gate = mk(w.B, w.L, w.H, w.dv), mk(w.B, w.L, w.H, w.dv)
+    nw = torch.ones(w.dv, device="cuda")
+    q, k, v = D.layer_prologue(xq, xk, xv, wq, wk, wv, n_h=w.n_h)
+    y = D.layer_epilogue(o, gate, nw)
+    out = {}
+    for name, fn, nbytes in (
+            ("prologue", lambda: D.layer_prologue(xq, xk, xv, wq, wk, wv, n_h=w.n_h, q=q, k=k, v=v),
+             2 * es * (w.B * w.L * w.H * w.dk + w.B * Lx * w.H * (w.dk + w.dv)) + 4 * width * w.H * (2 * w.dk + w.dv)),
+            ("epilogue", lambda: D.layer_epilogue(o, gate, nw, y=y), 3 * es * w.B * w.L * w.H * w.dv + 4 * w.dv)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us_per_call": round(us, 2), "bytes": nbytes, "GB_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def time_decode(w, steps, n_states=8, kda=False):
     """`steps` back-to-back decode calls cycling over n_states independent states (8 x 64 MiB
     exceeds the 256 MB Infinity Cache, so each step streams its state from HBM); the same loop on
@@ -456,6 +493,8 @@ def main():
     ap.add_argument("--workload", default="gdn_b2h16_l8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the layer prologue/epilogue on the workload's shapes")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only delta_bwd on the workload (--steps calls) and print its line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -475,6 +514,9 @@ def main():
         sys.exit(1)
 
     w = W.get(args.workload)
+    if args.layer_only:
+        print(json.dumps({"workload": w.name, "layer": time_layer(w, args.steps)}), flush=True)
+        return
     if args.backward_only:
         bw = time_backward(w, args.steps, args.warmup)
         print(json.dumps({"workload": w.name, "backward": bw}), flush=True)
@@ -529,6 +571,12 @@ def main():
             log("[bench] kda decode: %s" % kd)
         except Exception as e:
             others[W.DECODE.name] = {"error": repr(e)}
+        try:
+            ly = time_layer(w, max(20, args.steps))
+            others["layer_" + w.name] = ly
+            log("[bench] layer steps %s: %s" % (w.name, ly))
+        except Exception as e:
+            others["layer_" + w.name] = {"error": repr(e)}
         try:
             bw = time_backward(w, max(5, args.steps // 10))
             others["bwd_" + w.name] = bw

@@ -4,7 +4,9 @@
 // channels; after the mixer an RMS norm over each head's d_v channels scaled by a per-channel
 // weight and multiplied by SiLU of the gate projection.
 //
-// One wave per (token, head) row; lane l owns channels l, l + 64, ... of the row.  The row's
+// Rows of d elements whose 16-byte vectors number a power of two are split over that many
+// lanes (conv_act_vec_kernel, norm_gate_vec_kernel); other widths take one wave per
+// (token, head) row, lane l owning channels l, l + 64, ... .  The row's
 // earlier taps are the same channels of the preceding tokens' rows, which neighbouring waves
 // read too, so HBM sees each input about once.  Arithmetic in float32; outputs rounded to the
 // element type.
@@ -91,19 +93,149 @@ __global__ __launch_bounds__(WAVE * ROWS_PER_WG) void norm_gate_kernel(const E* 
   }
 }
 
+// 16-byte vectors of E as floats, and back (rounded to nearest even for bf16).
+template <typename E>
+__device__ inline void unpack(u32x4 r, float* x) {
+  const E* e = reinterpret_cast<const E*>(&r);
+#pragma unroll
+  for (int i = 0; i < 16 / (int)sizeof(E); ++i) x[i] = to_float(e[i]);
+}
+template <typename E>
+__device__ inline u32x4 pack(const float* x) {
+  E e[16 / sizeof(E)];
+#pragma unroll
+  for (int i = 0; i < 16 / (int)sizeof(E); ++i) e[i] = to_elem<E>(x[i]);
+  u32x4 r;
+  __builtin_memcpy(&r, e, 16);
+  return r;
+}
+
+// Vector form of conv_act_kernel for four-tap filters and rows of LPR 16-byte vectors (LPR a
+// power of two): LPR lanes share a row, each owning VE consecutive channels; all of a lane's
+// tap and filter loads are in flight together.
+template <typename E, bool NORM, int LPR>
+__global__ __launch_bounds__(256) void conv_act_vec_kernel(const E* __restrict__ x, const float* __restrict__ w,
+                                                          E* __restrict__ y, int T, int H, int d, float eps) {
+  // a workgroup takes RPB consecutive tokens of one (sequence, head): the earlier taps of its
+  // rows are rows it reads itself, so they come from this compute unit's caches
+  constexpr int VE = 16 / (int)sizeof(E), RPW = WAVE / LPR, RPB = 256 / LPR;
+  const int lane = threadIdx.x % WAVE;
+  const int TB = (T + RPB - 1) / RPB;
+  const long bh = (long)blockIdx.x / TB;
+  const int t = (int)(blockIdx.x % TB) * RPB + (int)(threadIdx.x / WAVE) * RPW + lane / LPR;
+  const long row = ((bh / H) * T + t) * H + bh % H;
+  const int i0 = (lane % LPR) * VE;
+  const bool ok = t < T;
+  float a[VE];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) a[e] = 0.f;
+  if (ok) {
+    const int h = (int)(bh % H);
+    const long base = row * d + i0, step = (long)H * d;
+    // four taps: each channel's filter is one 16-byte vector
+    u32x4 xs[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int lag = 3 - s;
+      xs[s] = lag <= t ? *reinterpret_cast<const u32x4*>(x + base - lag * step) : u32x4{0, 0, 0, 0};
+    }
+    const float* wc = w + ((long)h * d + i0) * 4;
+    float4 wv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) wv[e] = *reinterpret_cast<const float4*>(wc + 4 * e);
+    float xv[4][VE];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) unpack<E>(xs[s], xv[s]);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) a[e] = wv[e].x * xv[0][e] + wv[e].y * xv[1][e] + wv[e].z * xv[2][e] + wv[e].w * xv[3][e];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      a[e] = silu(a[e]);
+      ss += a[e] * a[e];
+    }
+  }
+  float scale = 1.f;
+  if (NORM) {
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+    scale = rsqrtf(ss + eps);
+  }
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) a[e] *= scale;
+    *reinterpret_cast<u32x4*>(y + row * d + i0) = pack<E>(a);
+  }
+}
+
+// Vector form of norm_gate_kernel, same row split.
+template <typename E, int LPR>
+__global__ __launch_bounds__(256) void norm_gate_vec_kernel(const E* o, const E* __restrict__ g,
+                                                           const float* __restrict__ weight, E* y, long rows,
+                                                           int d, float eps) {
+  constexpr int VE = 16 / (int)sizeof(E), RPW = WAVE / LPR;
+  const int lane = threadIdx.x % WAVE;
+  const long row = ((long)blockIdx.x * (256 / WAVE) + threadIdx.x / WAVE) * RPW + lane / LPR;
+  const int i0 = (lane % LPR) * VE;
+  const bool ok = row < rows;
+  float a[VE], gv[VE], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) a[e] = gv[e] = 0.f;
+  if (ok) {
+    unpack<E>(*reinterpret_cast<const u32x4*>(o + row * d + i0), a);
+    unpack<E>(*reinterpret_cast<const u32x4*>(g + row * d + i0), gv);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss += a[e] * a[e];
+  }
+#pragma unroll
+  for (int s = LPR / 2; s > 0; s >>= 1) ss += __shfl_xor(ss, s, WAVE);
+  const float r = rsqrtf(ss / d + eps);
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) a[e] = a[e] * r * weight[i0 + e] * silu(gv[e]);
+    *reinterpret_cast<u32x4*>(y + row * d + i0) = pack<E>(a);
+  }
+}
+
+// Rows of d elements as 16-byte vectors: lanes per row when that is a power of two, else 0.
+template <typename E>
+int lanes_per_row(int d) {
+  const int l = d * (int)sizeof(E) / 16;
+  return (l & (l - 1)) == 0 && l >= 1 && l <= WAVE ? l : 0;
+}
+
+template <typename E, bool NORM>
+void launch_conv(const E* x, const float* w, E* y, long rows, int T, int H, int d, int width, float eps,
+                 hipStream_t st) {
+  int lpr = width == 4 ? lanes_per_row<E>(d) : 0;
+  const long rpb = lpr ? 256 / lpr : 1, nblk = rows / T * ((T + rpb - 1) / rpb);  // rows / T sequence-heads
+  if (nblk > 0x7fffffffL) lpr = 0;
+  if (lpr == 0) {
+    hipLaunchKernelGGL((conv_act_kernel<E, NORM>), dim3((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)),
+                       dim3(WAVE * ROWS_PER_WG), 0, st, x, w, y, rows, T, H, d, width, eps);
+    return;
+  }
+  const dim3 grid((unsigned)nblk), block(256);
+  switch (lpr) {
+#define DELTA_CONV_CASE(N) \
+  case N: hipLaunchKernelGGL((conv_act_vec_kernel<E, NORM, N>), grid, block, 0, st, x, w, y, T, H, d, eps); break;
+    DELTA_CONV_CASE(1) DELTA_CONV_CASE(2) DELTA_CONV_CASE(4) DELTA_CONV_CASE(8) DELTA_CONV_CASE(16)
+    DELTA_CONV_CASE(32) DELTA_CONV_CASE(64)
+#undef DELTA_CONV_CASE
+  }
+}
+
 template <typename E>
 hipError_t prologue_t(const LayerParams& p, hipStream_t st) {
-  const dim3 block(WAVE * ROWS_PER_WG);
   const long rq = (long)p.B * p.L * p.H, rkv = (long)p.B * p.Lx * p.H;
-  auto blocks = [](long rows) { return dim3((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)); };
   if (rq > 0)
-    hipLaunchKernelGGL((conv_act_kernel<E, true>), blocks(rq), block, 0, st, static_cast<const E*>(p.xq), p.wq,
-                       static_cast<E*>(p.q), rq, p.L, p.H, p.DK, p.width, p.eps);
+    launch_conv<E, true>(static_cast<const E*>(p.xq), p.wq, static_cast<E*>(p.q), rq, p.L, p.H, p.DK, p.width,
+                         p.eps, st);
   if (rkv > 0) {
-    hipLaunchKernelGGL((conv_act_kernel<E, true>), blocks(rkv), block, 0, st, static_cast<const E*>(p.xk), p.wk,
-                       static_cast<E*>(p.k), rkv, p.Lx, p.H, p.DK, p.width, p.eps);
-    hipLaunchKernelGGL((conv_act_kernel<E, false>), blocks(rkv), block, 0, st, static_cast<const E*>(p.xv), p.wv,
-                       static_cast<E*>(p.v), rkv, p.Lx, p.H, p.DV, p.width, p.eps);
+    launch_conv<E, true>(static_cast<const E*>(p.xk), p.wk, static_cast<E*>(p.k), rkv, p.Lx, p.H, p.DK, p.width,
+                         p.eps, st);
+    launch_conv<E, false>(static_cast<const E*>(p.xv), p.wv, static_cast<E*>(p.v), rkv, p.Lx, p.H, p.DV, p.width,
+                          p.eps, st);
   }
   return hipGetLastError();
 }
@@ -111,10 +243,25 @@ hipError_t prologue_t(const LayerParams& p, hipStream_t st) {
 template <typename E>
 hipError_t epilogue_t(const LayerParams& p, hipStream_t st) {
   const long rows = (long)p.B * p.L * p.H;
-  if (rows > 0)
+  if (rows == 0) return hipSuccess;
+  const E* o = static_cast<const E*>(p.o);
+  const E* g = static_cast<const E*>(p.g);
+  E* y = static_cast<E*>(p.y);
+  const int lpr = lanes_per_row<E>(p.DV);
+  if (lpr == 0) {
     hipLaunchKernelGGL((norm_gate_kernel<E>), dim3((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)),
-                       dim3(WAVE * ROWS_PER_WG), 0, st, static_cast<const E*>(p.o), static_cast<const E*>(p.g),
-                       p.weight, static_cast<E*>(p.y), rows, p.DV, p.eps);
+                       dim3(WAVE * ROWS_PER_WG), 0, st, o, g, p.weight, y, rows, p.DV, p.eps);
+    return hipGetLastError();
+  }
+  const long per_block = 256 / lpr;
+  const dim3 grid((unsigned)((rows + per_block - 1) / per_block)), block(256);
+  switch (lpr) {
+#define DELTA_NG_CASE(N) \
+  case N: hipLaunchKernelGGL((norm_gate_vec_kernel<E, N>), grid, block, 0, st, o, g, p.weight, y, rows, p.DV, p.eps); break;
+    DELTA_NG_CASE(1) DELTA_NG_CASE(2) DELTA_NG_CASE(4) DELTA_NG_CASE(8) DELTA_NG_CASE(16)
+    DELTA_NG_CASE(32) DELTA_NG_CASE(64)
+#undef DELTA_NG_CASE
+  }
   return hipGetLastError();
 }
 
