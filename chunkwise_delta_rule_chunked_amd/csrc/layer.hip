@@ -111,60 +111,60 @@ __device__ inline u32x4 pack(const float* x) {
 }
 
 // Vector form of conv_act_kernel for four-tap filters and rows of LPR 16-byte vectors (LPR a
-// power of two): LPR lanes share a row, each owning VE consecutive channels; all of a lane's
-// tap and filter loads are in flight together.
+// power of two): LPR lanes share a row, each owning VE consecutive channels.  A workgroup takes
+// NR runs of RPB consecutive tokens of one (sequence, head); each lane has its NR rows' tap
+// loads (and its channels' filters, loaded once) in flight together, and the earlier taps of
+// the workgroup's rows are rows it reads itself, so they come from this compute unit's caches.
+constexpr int NR = 4;
+
 template <typename E, bool NORM, int LPR>
 __global__ __launch_bounds__(256) void conv_act_vec_kernel(const E* __restrict__ x, const float* __restrict__ w,
                                                           E* __restrict__ y, int T, int H, int d, float eps) {
-  // a workgroup takes RPB consecutive tokens of one (sequence, head): the earlier taps of its
-  // rows are rows it reads itself, so they come from this compute unit's caches
   constexpr int VE = 16 / (int)sizeof(E), RPW = WAVE / LPR, RPB = 256 / LPR;
   const int lane = threadIdx.x % WAVE;
-  const int TB = (T + RPB - 1) / RPB;
+  const int TB = (T + RPB * NR - 1) / (RPB * NR);
   const long bh = (long)blockIdx.x / TB;
-  const int t = (int)(blockIdx.x % TB) * RPB + (int)(threadIdx.x / WAVE) * RPW + lane / LPR;
-  const long row = ((bh / H) * T + t) * H + bh % H;
+  const int h = (int)(bh % H);
+  const int t0 = (int)(blockIdx.x % TB) * RPB * NR + (int)(threadIdx.x / WAVE) * RPW + lane / LPR;
   const int i0 = (lane % LPR) * VE;
-  const bool ok = t < T;
-  float a[VE];
-  float ss = 0.f;
+  const long step = (long)H * d;
+  const long row0 = ((bh / H) * T + t0) * H + h;  // row of token t0; token t0 + j is j * H rows on
+  u32x4 xs[NR][4];
 #pragma unroll
-  for (int e = 0; e < VE; ++e) a[e] = 0.f;
-  if (ok) {
-    const int h = (int)(bh % H);
-    const long base = row * d + i0, step = (long)H * d;
-    // four taps: each channel's filter is one 16-byte vector
-    u32x4 xs[4];
+  for (int r = 0; r < NR; ++r) {
+    const int t = t0 + r * RPB;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int lag = 3 - s;
-      xs[s] = lag <= t ? *reinterpret_cast<const u32x4*>(x + base - lag * step) : u32x4{0, 0, 0, 0};
+      xs[r][s] = t < T && lag <= t ? *reinterpret_cast<const u32x4*>(x + (row0 + (long)(r * RPB - lag) * H) * d + i0)
+                                   : u32x4{0, 0, 0, 0};
     }
-    const float* wc = w + ((long)h * d + i0) * 4;
-    float4 wv[VE];
+  }
+  const float* wc = w + ((long)h * d + i0) * 4;  // each channel's four taps: one 16-byte vector
+  float4 wv[VE];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) wv[e] = *reinterpret_cast<const float4*>(wc + 4 * e);
-    float xv[4][VE];
+  for (int e = 0; e < VE; ++e) wv[e] = *reinterpret_cast<const float4*>(wc + 4 * e);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) unpack<E>(xs[s], xv[s]);
+  for (int r = 0; r < NR; ++r) {
+    float xv[4][VE], a[VE], ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) a[e] = wv[e].x * xv[0][e] + wv[e].y * xv[1][e] + wv[e].z * xv[2][e] + wv[e].w * xv[3][e];
+    for (int s = 0; s < 4; ++s) unpack<E>(xs[r][s], xv[s]);
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
-      a[e] = silu(a[e]);
+      a[e] = silu(wv[e].x * xv[0][e] + wv[e].y * xv[1][e] + wv[e].z * xv[2][e] + wv[e].w * xv[3][e]);
       ss += a[e] * a[e];
     }
-  }
-  float scale = 1.f;
-  if (NORM) {
+    float scale = 1.f;
+    if (NORM) {
 #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
-    scale = rsqrtf(ss + eps);
-  }
-  if (ok) {
+      for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+      scale = rsqrtf(ss + eps);
+    }
+    if (t0 + r * RPB < T) {
 #pragma unroll
-    for (int e = 0; e < VE; ++e) a[e] *= scale;
-    *reinterpret_cast<u32x4*>(y + row * d + i0) = pack<E>(a);
+      for (int e = 0; e < VE; ++e) a[e] *= scale;
+      *reinterpret_cast<u32x4*>(y + (row0 + (long)r * RPB * H) * d + i0) = pack<E>(a);
+    }
   }
 }
 
@@ -208,7 +208,7 @@ template <typename E, bool NORM>
 void launch_conv(const E* x, const float* w, E* y, long rows, int T, int H, int d, int width, float eps,
                  hipStream_t st) {
   int lpr = width == 4 ? lanes_per_row<E>(d) : 0;
-  const long rpb = lpr ? 256 / lpr : 1, nblk = rows / T * ((T + rpb - 1) / rpb);  // rows / T sequence-heads
+  const long run = lpr ? 256 / lpr * NR : 1, nblk = rows / T * ((T + run - 1) / run);  // rows / T sequence-heads
   if (nblk > 0x7fffffffL) lpr = 0;
   if (lpr == 0) {
     hipLaunchKernelGGL((conv_act_kernel<E, NORM>), dim3((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)),
