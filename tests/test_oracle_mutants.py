@@ -134,3 +134,50 @@ def test_planted_kda_mistake_is_caught(name, tmp_path, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught >= 1, name
+
+
+# ---- the layer prologue/epilogue oracle (numpy): slips planted by swapping in a wrong function
+
+def _conv_taps_reversed(x, w):
+    return _REAL_CONV(x, w[:, ::-1])
+
+
+def _l2_over_heads(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-2, keepdims=True) + eps)
+
+
+def _silu_sigmoid_only(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def _epilogue_sum_not_mean(o, g, weight, eps=1e-6):
+    o = np.asarray(o, dtype=np.float64)
+    return o / np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps) * weight * _REAL_SILU(g)
+
+
+import numpy as np  # noqa: E402
+from oracle import layer as _L  # noqa: E402
+import test_oracle_layer as LP  # noqa: E402
+
+_REAL_CONV, _REAL_SILU = _L.short_conv, _L.silu
+LAYER_MUTANTS = {"conv_taps_reversed": ("short_conv", _conv_taps_reversed),
+                 "l2_over_heads": ("l2_norm", _l2_over_heads),
+                 "silu_is_sigmoid": ("silu", _silu_sigmoid_only),
+                 "rms_sum_not_mean": ("epilogue", _epilogue_sum_not_mean)}
+LAYER_PINS = [LP.test_silu_closed_forms, lambda: LP.test_conv_matches_numpy_convolve(4),
+              LP.test_conv_current_tap_is_identity_and_causal, LP.test_prologue_unit_norm_and_direction,
+              LP.test_epilogue_rms_gate_and_scale_invariance]
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_MUTANTS))
+def test_planted_layer_mistake_is_caught(name, monkeypatch):
+    attr, fn = LAYER_MUTANTS[name]
+    monkeypatch.setattr(_L, attr, fn)
+    failed = 0
+    for pin in LAYER_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, name
