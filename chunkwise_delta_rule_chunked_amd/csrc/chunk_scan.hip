@@ -440,10 +440,14 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
         if (live[c]) {
           if (isv[c]) {
             const long col = 16 * tile[c] + m;
-            if (seg == 0) {
-              if (p.S0) x = p.S0[((long)head * DK + row) * p.DV + col];
-            } else if (!SUM) {
+            if (!SUM && p.P > 1) {
+              // with a split every segment, the first too, starts from the start state the
+              // summary and combine launches wrote: this launch then reads no caller tensor that
+              // it also writes (S_final may be S0 itself, written by the last segment)
               x = p.Sst[(((long)head * p.P + seg) * DK + row) * p.DV + col];
+            } else if (seg == 0) {
+              if (p.S0) x = p.S0[((long)head * DK + row) * p.DV + col];
+              if (SUM) p.Sst[((long)head * p.P * DK + row) * p.DV + col] = x;  // segment 0's start
             }
           } else {
             x = (row == 16 * (tile[c] - NCT) + m) ? 1.f : 0.f;  // identity columns of M

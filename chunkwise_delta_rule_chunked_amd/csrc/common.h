@@ -320,6 +320,11 @@ __device__ inline void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, float x)
 
 __device__ inline float gate_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Lower bound applied to each token's log gate on the chunkwise path.  exp(-150) ~ 7e-66 is far
+// below the smallest float32 subnormal (1.4e-45), so any decay spanning a clamped position is
+// exactly 0; a true log gate below the floor differs from it by a factor under 1e-65.
+constexpr float LOG_GATE_FLOOR = -150.f;
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ inline float wave_inclusive_scan(float x, int lane) {
 #pragma unroll

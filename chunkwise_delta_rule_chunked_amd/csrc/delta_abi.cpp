@@ -3,7 +3,10 @@
 // never allocates device memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include "../../include/delta.h"
 #include "kernels.h"
@@ -87,6 +90,47 @@ size_t sm_bytes(const FwdParams& p) { return p.P > 1 ? (size_t)p.B * p.H * p.P *
 size_t sst_bytes(const FwdParams& p) { return p.P > 1 ? (size_t)p.B * p.H * p.P * p.DK * p.DV * 4 : 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DELTA_OK : DELTA_ERR_HIP; }
+
+// Opt-in switches, read from the environment at every call:
+//   DELTA_VALIDATE=1    check beta and the log gates before enqueuing work (validate.hip); a
+//                       value outside the contract returns DELTA_ERR_BAD_VALUE with nothing
+//                       written.  The check waits for the stream, so the call is synchronous.
+//   DELTA_FAULT=launch  every entry point that has work to enqueue fails as if its first launch
+//                       had failed: DELTA_ERR_HIP, nothing enqueued (for testing error paths).
+bool env_is(const char* name, const char* value) {
+  const char* e = getenv(name);
+  return e && strcmp(e, value) == 0;
+}
+bool validate_on() { return env_is("DELTA_VALIDATE", "1"); }
+int launch_guard() { return env_is("DELTA_FAULT", "launch") ? DELTA_ERR_HIP : DELTA_OK; }
+
+// The validation pass on the device: the flag words go to `flags` (VALIDATE_BLOCKS words of the
+// caller's workspace, overwritten afterwards by the pass itself), then are read back.
+int validate_device(const float* beta, size_t nbeta, const float* glog, size_t ngate, void* flags, hipStream_t st) {
+  if (nbeta + ngate == 0) return DELTA_OK;
+  unsigned* f = static_cast<unsigned*>(flags);
+  if (delta::launch_validate(beta, (long)nbeta, glog, (long)ngate, f, st) != hipSuccess) return DELTA_ERR_HIP;
+  unsigned h[delta::VALIDATE_BLOCKS];
+  if (hipMemcpyAsync(h, f, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess) return DELTA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return DELTA_ERR_HIP;
+  for (unsigned x : h)
+    if (x) return DELTA_ERR_BAD_VALUE;
+  return DELTA_OK;
+}
+
+// The same check for the decode steps, which take no workspace: their beta and gate arrays are
+// one value per (sequence, head) or per key channel, read back and checked on the host.
+int validate_small(const float* beta, size_t nbeta, const float* glog, size_t ngate, hipStream_t st) {
+  std::vector<float> hb(nbeta), hg(ngate);
+  if (nbeta && hipMemcpyAsync(hb.data(), beta, nbeta * 4, hipMemcpyDeviceToHost, st) != hipSuccess) return DELTA_ERR_HIP;
+  if (ngate && hipMemcpyAsync(hg.data(), glog, ngate * 4, hipMemcpyDeviceToHost, st) != hipSuccess) return DELTA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return DELTA_ERR_HIP;
+  for (float x : hb)
+    if (!__builtin_isfinite(x)) return DELTA_ERR_BAD_VALUE;
+  for (float x : hg)
+    if (x != x || x == __builtin_inff()) return DELTA_ERR_BAD_VALUE;
+  return DELTA_OK;
+}
 
 }  // namespace
 
@@ -186,6 +230,11 @@ int prepare_fwd(const delta_shape* s, int phase, const void* q, const void* k, c
 
 int run_intra(const FwdParams& p, bool bf, hipStream_t st) {
   if (p.B * p.H * p.NT == 0) return DELTA_OK;
+  int rc = launch_guard();
+  if (rc) return rc;
+  if (validate_on() &&
+      (rc = validate_device(p.beta, (size_t)p.B * p.Lx * p.H, p.g_log, p.g_log ? (size_t)p.B * p.L * p.H : 0, p.T, st)))
+    return rc;
   return hip_status(delta::launch_intra_chunk(p, bf, false, st));
 }
 
@@ -193,6 +242,8 @@ int run_scan(const FwdParams& p, bool bf, int phase, hipStream_t st) {
   if (p.B * p.H == 0) return DELTA_OK;
   // L == 0: no chunks; the output launch still writes S_final = S0 (or zeros)
   if (p.NT == 0 && (phase != delta::SCAN_OUTPUTS || !p.S_final)) return DELTA_OK;
+  int rc = launch_guard();
+  if (rc) return rc;
   return hip_status(delta::launch_scan_phase(p, bf, phase, st));
 }
 
@@ -310,6 +361,7 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
   const bool bf = s->dtype == DELTA_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (p.B * p.H * p.NT == 0) return DELTA_OK;
+  if ((rc = launch_guard())) return rc;
   if ((rc = hip_status(delta::launch_intra_chunk(p, bf, true, st)))) return rc;
   if (W || U) return hip_status(delta::launch_wy_factors(p, bf, st));
   return DELTA_OK;
@@ -373,6 +425,9 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   const bool bf = s->dtype == DELTA_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if ((rc = launch_guard())) return rc;
+  // the check's flag words take the start of the T region, which the first launch rewrites
+  if (validate_on() && f.NT > 0 && (rc = validate_device(beta, nx, g_log, g_log ? nq : 0, ws, st))) return rc;
   FwdParams fi = f;  // the intra-chunk launch: T (float32) and the gate prefix
   fi.k = k;
   fi.beta = beta;
@@ -425,6 +480,11 @@ int run_decode(const delta_shape* s, const void* q, const void* k, const void* v
   if (overlap(rS, rO)) return DELTA_ERR_ALIAS;
 
   if (BH == 0) return DELTA_OK;
+  if ((rc = launch_guard())) return rc;
+  if (validate_on() &&
+      (rc = validate_small(beta, BH * s->n_h, g_log ? g_log : a_log, g_log ? BH : a_log ? BH * s->dk : 0,
+                           static_cast<hipStream_t>(stream))))
+    return rc;
   DecodeParams p;
   p.B = s->B;
   p.H = s->H;
@@ -484,6 +544,7 @@ int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const v
       if (overlap(out[i], out[j])) return DELTA_ERR_ALIAS;
   }
   if (rkv == 0) return DELTA_OK;  // nothing to do (rq <= rkv)
+  if ((rc = launch_guard())) return rc;
   LayerParams p;
   memset(&p, 0, sizeof(p));
   p.B = s->B, p.L = s->L, p.H = s->H, p.DK = s->dk, p.DV = s->dv, p.Lx = s->L * s->n_h, p.width = width;
@@ -509,6 +570,7 @@ int delta_layer_epilogue(const delta_shape* s, float eps, const void* o, const v
   // y may be o itself (each row is read whole before it is written); no other overlap
   if ((overlap(ry, ro) && y != o) || overlap(ry, rg) || overlap(ry, rw)) return DELTA_ERR_ALIAS;
   if (rows == 0) return DELTA_OK;
+  if ((rc = launch_guard())) return rc;
   LayerParams p;
   memset(&p, 0, sizeof(p));
   p.B = s->B, p.L = s->L, p.H = s->H, p.DK = s->dk, p.DV = s->dv, p.Lx = s->L * s->n_h;
@@ -529,6 +591,9 @@ const char* delta_strerror(int code) {
     case DELTA_ERR_WORKSPACE: return "workspace missing or smaller than delta_fwd_workspace_bytes";
     case DELTA_ERR_ALIAS: return "an output overlaps an input or another output";
     case DELTA_ERR_HIP: return "HIP launch or runtime error";
+    case DELTA_ERR_BAD_VALUE:
+      return "input value outside the contract (non-finite beta, or a NaN or +inf log gate); reported only "
+             "with DELTA_VALIDATE=1";
     default: return "unknown error code";
   }
 }

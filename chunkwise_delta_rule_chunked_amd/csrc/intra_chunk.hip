@@ -105,6 +105,12 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
                                                      ntok * p.H * 4);
       const bool first = lane < C && lane % nh == 0;
       lg = buffer_load4(grs, first ? (lane / nh) * p.H * 4 : ntok * p.H * 4);
+      // g = 0 (log g = -inf) is a hard reset (DeltaProduct notes, section 3.3).  Taken as the
+      // finite LOG_GATE_FLOOR it makes every decay that spans the position underflow to exactly 0
+      // in float32 (gamma, Gamma_ij, gamma_C / gamma), which erases the state as g = 0 does,
+      // while differences of prefix sums on one side of it stay finite (-inf - (-inf) would be
+      // NaN).  NaN fails the comparison and passes through.
+      lg = lg < LOG_GATE_FLOOR ? LOG_GATE_FLOOR : lg;
     }
     const float gc = wave_inclusive_scan(lg, lane);
     if (lane < C) {

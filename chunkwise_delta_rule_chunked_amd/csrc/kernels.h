@@ -99,5 +99,10 @@ hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_
 hipError_t launch_layer_prologue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_layer_epilogue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
+// Opt-in input check (validate.hip): beta finite, log gates finite or -inf.  Writes one flag word
+// per workgroup (VALIDATE_BLOCKS words) at `flags`.
+constexpr int VALIDATE_BLOCKS = 128;
+hipError_t launch_validate(const float* beta, long nbeta, const float* glog, long ngate, unsigned* flags,
+                           hipStream_t st);
 
 }  // namespace delta

@@ -181,8 +181,13 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       for (int j = 0; j < 4; ++j) {
         const int row = dkrow(t, 4 * g4 + j), col = 16 * (tile0 + c) + m;
         float x;
-        if (isv) x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
-        else x = (row == col - DV) ? 1.f : 0.f;  // identity columns of the transition map
+        if (isv) {
+          x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
+          // segment 0's start state, which the outputs launch reads instead of S0
+          if (seg == 0) p.Sst[((long)head * p.P * DK + row) * DV + col] = x;
+        } else {
+          x = (row == col - DV) ? 1.f : 0.f;  // identity columns of the transition map
+        }
         S[c][t][j] = x;
       }
   // the compiler waits for these loads at their first use: use them here, before any prefetch

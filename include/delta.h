@@ -19,14 +19,29 @@
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never
  *     allocates, frees or retains them.  All tensors are contiguous, row-major.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
- *     default stream); no entry point synchronises the host.
+ *     default stream); no entry point synchronises the host (unless DELTA_VALIDATE=1,
+ *     below).
  *   - Argument errors are detected before anything is enqueued: the call returns
  *     a negative code and writes nothing.  Launch failures return DELTA_ERR_HIP.
  *   - The library keeps no state between calls and may be called from several
  *     host threads at once.
  *   - Keys are used as given: L2 normalisation belongs to the caller.
- *   - g_log is the LOG of the gate (finite, <= 0 expected; a positive value is
- *     computed as given but the chunk form's decay ratios may overflow).
+ *   - g_log is the LOG of the gate: finite and <= 0 expected (a positive value is
+ *     computed as given but the chunk form's decay ratios may overflow), or -inf for
+ *     g = 0, the hard reset of the DeltaProduct notes (section 3.3), which clears the
+ *     state.  On the chunkwise path each log gate is raised to at least -150 first:
+ *     every decay across such a position is then exactly 0 in float32, as for g = 0.
+ *   - NaN or infinite inputs are not masked: they propagate to the outputs they reach.
+ *
+ * Environment switches, read at every call:
+ *   - DELTA_VALIDATE=1: delta_fwd, delta_fwd_intra, delta_bwd, delta_decode and
+ *     delta_decode_kda first check beta (must be finite) and the log gates (finite or
+ *     -inf) and return DELTA_ERR_BAD_VALUE, having written nothing but the start of the
+ *     workspace, if one is not.  The check waits for the stream (the call is then
+ *     synchronous) and must not be used while the stream is being captured into a graph.
+ *   - DELTA_FAULT=launch: every entry point with work to enqueue returns DELTA_ERR_HIP
+ *     in place of its first launch and enqueues nothing (for testing callers' error
+ *     handling).
  */
 #ifndef DELTA_H
 #define DELTA_H
@@ -51,7 +66,9 @@ enum {
   DELTA_ERR_MISALIGNED = -4,      /* a tensor pointer is not 16-byte aligned (beta, g_log: 4-byte) */
   DELTA_ERR_WORKSPACE = -5,       /* workspace NULL or smaller than delta_fwd_workspace_bytes */
   DELTA_ERR_ALIAS = -6,           /* S_final partially overlaps S0, or an output overlaps an input */
-  DELTA_ERR_HIP = -7              /* a HIP launch or runtime call failed */
+  DELTA_ERR_HIP = -7,             /* a HIP launch or runtime call failed */
+  DELTA_ERR_BAD_VALUE = -8        /* beta not finite, or a log gate NaN or +inf; reported only when
+                                     the environment sets DELTA_VALIDATE=1 (see below) */
 };
 
 /* Problem description shared by all entry points. */
@@ -136,9 +153,13 @@ int delta_fwd_segments(const delta_shape* s, int32_t* segments, int32_t* chunks_
  * The three launches of delta_fwd_inter, for per-kernel timing; called in this order on one
  * stream after delta_fwd_intra, with the same workspace, they compute what delta_fwd_inter
  * computes.  Arguments as for delta_fwd; each reads only the tensors it lists.
- *   delta_fwd_scan_summary  k, v, S0 (segment 0 starts from S0) -> segment summaries
- *   delta_fwd_scan_combine  segment summaries -> segment start states (sequential, float32)
- *   delta_fwd_scan_outputs  q, k, v, S0 and start states -> O, S_final
+ *   delta_fwd_scan_summary  k, v, S0 (segment 0 starts from S0) -> segment summaries, and
+ *                           segment 0's start state (a copy of S0)
+ *   delta_fwd_scan_combine  segment summaries -> the other segments' start states (sequential,
+ *                           float32)
+ *   delta_fwd_scan_outputs  q, k, v and the start states (S0 itself when the sequence is not
+ *                           split) -> O, S_final.  With a split this launch does not read S0,
+ *                           so S_final == S0 (in place) cannot race with it.
  */
 int delta_fwd_scan_summary(const delta_shape* s, const void* k, const void* v, const float* S0,
                            void* workspace, size_t workspace_bytes, void* stream);

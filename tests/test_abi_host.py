@@ -31,7 +31,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_strerror(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         msg = D.strerror(code)
         assert msg and msg != "unknown error code", code
     assert D.strerror(-99) == "unknown error code"
@@ -242,3 +242,24 @@ def test_binding_rejects_cpu_tensors(lib):
     q = torch.zeros(1, 16, 1, 16)
     with pytest.raises(ValueError):
         D.fwd(q, q, q, torch.zeros(1, 16, 1), chunk=16)
+
+
+def test_fault_injection_returns_hip_error(lib, no_gpu, monkeypatch):
+    """DELTA_FAULT=launch: a call that passes every argument check returns DELTA_ERR_HIP (-7) in
+    place of its first launch, so callers' error paths can be tested without a GPU; calls with
+    nothing to enqueue still succeed and argument errors keep their own codes."""
+    monkeypatch.setenv("DELTA_FAULT", "launch")
+    Lb = D.load_library()
+    assert call_fwd(shape()) == -7
+    assert call_fwd(shape(L=0), w=ctypes.c_void_p(0), wbytes=0, O=ctypes.c_void_p(0), SF=fake(6)) == -7  # S_final = S0
+    assert call_fwd(shape(), q=ctypes.c_void_p(0)) == -1
+    f = [fake(i) for i in range(9)]
+    assert Lb.delta_decode(ctypes.byref(shape(L=1)), *f[:5], f[5], f[6], None) == -7
+    assert Lb.delta_decode_kda(ctypes.byref(shape(L=1)), *f[:5], f[5], f[6], None) == -7
+    assert Lb.delta_layer_prologue(ctypes.byref(shape()), 4, ctypes.c_float(1e-6), *f, None) == -7
+    assert Lb.delta_layer_epilogue(ctypes.byref(shape()), ctypes.c_float(1e-6), f[0], f[1], f[2], f[3], None) == -7
+    assert call_bwd(shape()) == -7
+    assert Lb.delta_fwd(ctypes.byref(shape(B=0)), *[None] * 9, ctypes.c_size_t(0), None) == 0
+    with pytest.raises(D.DeltaError) as e:
+        D._check(-7, "delta_fwd")
+    assert e.value.code == -7 and "HIP" in str(e.value)
