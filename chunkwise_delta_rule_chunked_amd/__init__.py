@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -59,6 +59,7 @@ def load_library():
     P, SP = ctypes.c_void_p, ctypes.POINTER(Shape)
     lib.delta_fwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.delta_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.delta_fwd_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_fwd_intra.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_inter.argtypes = [SP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_fwd_segments.argtypes = [SP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
@@ -74,7 +75,7 @@ def load_library():
     lib.delta_layer_epilogue.argtypes = [SP, ctypes.c_float, P, P, P, P, P]
     lib.delta_strerror.argtypes = [ctypes.c_int]
     lib.delta_strerror.restype = ctypes.c_char_p
-    for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_intra, lib.delta_fwd_inter,
+    for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_noalloc, lib.delta_fwd_intra, lib.delta_fwd_inter,
               lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda, lib.delta_bwd_workspace_bytes,
               lib.delta_bwd, lib.delta_layer_prologue, lib.delta_layer_epilogue):
         f.restype = ctypes.c_int
@@ -169,6 +170,27 @@ def fwd(q, k, v, beta, g_log=None, S0=None, *, n_h: int = 1, chunk: int = 64, sc
                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                        _stream(stream))
     _check(rc, "delta_fwd")
+    return O, S_final
+
+
+# include/delta.h: DELTA_NOALLOC_MAX_BYTES, the fixed device workspace of delta_fwd_noalloc
+NOALLOC_MAX_BYTES = 96 << 20
+
+
+def fwd_noalloc(q, k, v, beta, g_log, S0, O, S_final, *, n_h: int = 1, chunk: int = 64, scale: float = 1.0,
+                stream=None):
+    """fwd through delta_fwd_noalloc: the workspace is the library's fixed device array, and the
+    caller provides O (and S_final, or None), so nothing is allocated.  Calls that overlap on one
+    device race (they share that array)."""
+    torch = _torch()
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    sh = make_shape(B, L, H, dk, dv, n_h, chunk, _dtype_code(q), scale)
+    rc = load_library().delta_fwd_noalloc(
+        ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(beta, "beta", torch.float32), _dev(g_log, "g_log", torch.float32), _dev(S0, "S0", torch.float32),
+        _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32), _stream(stream))
+    _check(rc, "delta_fwd_noalloc")
     return O, S_final
 
 

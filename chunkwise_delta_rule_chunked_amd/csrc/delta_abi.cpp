@@ -591,6 +591,9 @@ const char* delta_strerror(int code) {
     case DELTA_ERR_WORKSPACE: return "workspace missing or smaller than delta_fwd_workspace_bytes";
     case DELTA_ERR_ALIAS: return "an output overlaps an input or another output";
     case DELTA_ERR_HIP: return "HIP launch or runtime error";
+    case DELTA_ERR_NOALLOC_TOO_LARGE:
+      return "delta_fwd_noalloc: the shape needs more workspace than the library's fixed device array "
+             "(DELTA_NOALLOC_MAX_BYTES)";
     case DELTA_ERR_BAD_VALUE:
       return "input value outside the contract (non-finite beta, or a NaN or +inf log gate); reported only "
              "with DELTA_VALIDATE=1";

@@ -67,8 +67,10 @@ enum {
   DELTA_ERR_WORKSPACE = -5,       /* workspace NULL or smaller than delta_fwd_workspace_bytes */
   DELTA_ERR_ALIAS = -6,           /* S_final partially overlaps S0, or an output overlaps an input */
   DELTA_ERR_HIP = -7,             /* a HIP launch or runtime call failed */
-  DELTA_ERR_BAD_VALUE = -8        /* beta not finite, or a log gate NaN or +inf; reported only when
+  DELTA_ERR_BAD_VALUE = -8,       /* beta not finite, or a log gate NaN or +inf; reported only when
                                      the environment sets DELTA_VALIDATE=1 (see below) */
+  DELTA_ERR_NOALLOC_TOO_LARGE = -9 /* delta_fwd_noalloc: the shape needs more workspace than the
+                                     library's fixed device array (DELTA_NOALLOC_MAX_BYTES) */
 };
 
 /* Problem description shared by all entry points. */
@@ -123,6 +125,24 @@ int delta_fwd_workspace_bytes(const delta_shape* s, size_t* bytes);
 int delta_fwd(const delta_shape* s, const void* q, const void* k, const void* v,
               const float* beta, const float* g_log, const float* S0, void* O,
               float* S_final, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * delta_fwd for callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same computation, with the workspace
+ * taken from a fixed device array inside the library instead of a caller buffer.  It calls no
+ * allocating routine.
+ *   - Arguments, results and error codes as delta_fwd (no workspace arguments); shapes whose
+ *     delta_fwd_workspace_bytes exceeds DELTA_NOALLOC_MAX_BYTES return
+ *     DELTA_ERR_NOALLOC_TOO_LARGE before anything is enqueued.
+ *   - The array holds DELTA_NOALLOC_MAX_BYTES on every device the library is used on, from the
+ *     first call there until the process ends; its device address is looked up once per device.
+ *   - All calls on one device share it: calls that overlap on one device (several streams or
+ *     threads) race and must be serialised by the caller.  Its contents on entry do not matter.
+ */
+#define DELTA_NOALLOC_MAX_BYTES (96u << 20)
+int delta_fwd_noalloc(const delta_shape* s, const void* q, const void* k, const void* v,
+                      const float* beta, const float* g_log, const float* S0, void* O,
+                      float* S_final, void* stream);
 
 /*
  * The two phases of delta_fwd, for callers that schedule them separately (and for per-kernel

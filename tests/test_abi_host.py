@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = D.header_functions()
-    assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_intra", "delta_fwd_inter",
+    assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_noalloc", "delta_fwd_intra", "delta_fwd_inter",
                           "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
                           "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_decode_kda",
                           "delta_bwd_workspace_bytes", "delta_bwd", "delta_layer_prologue",
@@ -31,7 +31,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_strerror(lib):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         msg = D.strerror(code)
         assert msg and msg != "unknown error code", code
     assert D.strerror(-99) == "unknown error code"
@@ -263,3 +263,16 @@ def test_fault_injection_returns_hip_error(lib, no_gpu, monkeypatch):
     with pytest.raises(D.DeltaError) as e:
         D._check(-7, "delta_fwd")
     assert e.value.code == -7 and "HIP" in str(e.value)
+
+
+def test_noalloc_limit(lib):
+    """The binding's copy of DELTA_NOALLOC_MAX_BYTES matches the header, and a shape needing more
+    workspace than that is rejected (-9) before any device call; shape errors keep their codes."""
+    import re
+    txt = open(os.path.join(ROOT, "include", "delta.h")).read()
+    m = re.search(r"#define DELTA_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", txt)
+    assert m and D.NOALLOC_MAX_BYTES == int(m.group(1)) << int(m.group(2))
+    sh = shape(B=1, H=16, L=65536, dk=128, dv=128, chunk=64)
+    assert ws(sh)[1] > D.NOALLOC_MAX_BYTES
+    assert D.load_library().delta_fwd_noalloc(ctypes.byref(sh), *[None] * 8, None) == -9
+    assert D.load_library().delta_fwd_noalloc(ctypes.byref(shape(dk=48)), *[None] * 8, None) == -3
