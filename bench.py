@@ -17,11 +17,20 @@ Default workload: Gated DeltaNet, B=2, H=16, L=8192, d_k=d_v=128, bf16 inputs, f
 chunk 64 (the H=16, d=128, L=8K shape the tokens/s metric is quoted on).  tokens = B * L.
 
 The line carries:
-  roofline      for the dominant kernel: algorithmic bytes per launch / its mean launch time
-                (HIP events on the launch stream over the event-timed steps), against 8 TB/s HBM
+  roofline      for the dominant (longest) launch: the forward pass's compulsory HBM bytes (q, k,
+                v, O in the input dtype, beta and log g in fp32, S0 and S_final in fp32: 1032 B per
+                token-head at d = 128 bf16) over that launch's mean duration (HIP events on the
+                launch stream), against 8 TB/s.  `launch_bytes` is what that launch itself must
+                move, `traffic` its HBM bytes from the committed rocprofv3 counters, and
+                `traffic_step` / `traffic_ratio` the counter bytes of all four launches and their
+                ratio to the compulsory bytes.
+  step          the same compulsory bytes and the algorithmic flops (causal counts; `dense_flops`
+                with full C x C tiles) over ms_per_step: % of HBM, % of bf16 MFMA peak, and the
+                roofline fraction achieved FLOP/s / min(MFMA peak, 8 TB/s x intensity)
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the same workload
   others        the other workloads (DeltaNet 4x8x2K, DeltaProduct n_h=2, GDN 64K, and the
-                batch-64 decode step), measured the same way, unless --no-others
+                batch-64 decode step), measured the same way, each with its own oracle baseline,
+                unless --no-others
 """
 from __future__ import annotations
 
@@ -183,10 +192,11 @@ def time_prefill(w, steps, warmup, copy_calibration_mib=0):
     nbytes = D.workspace_bytes(w.B, w.L, w.H, w.dk, w.dv, w.n_h, w.chunk, code)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     if copy_calibration_mib:
-        # a plain device copy of known size, for scaling the HBM byte counters of a profile run
+        # the library's streaming copy (delta_measure_copy) over a known size, for scaling the HBM
+        # byte counters of a profile run
         src = torch.ones(copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        D.measure_copy(src, dst, unroll=4, blocks=4096)
         torch.cuda.synchronize()
         del src, dst
     # the calls of one step, in order, each timed by its own event pair on the launch stream
@@ -290,19 +300,62 @@ def measured_traffic(w, phase):
     return val if sha == kernel_sources_sha() else None
 
 
+def compulsory_bytes(w) -> int:
+    """HBM bytes one forward pass cannot avoid: q, k, v and O in the input dtype, beta and log g
+    in fp32, S0 (when given) and S_final in fp32, each touched once (1032 B per token-head at
+    d = 128, bf16, with S0)."""
+    es = _es(w)
+    b = w.B * w.L * w.H * (w.dk + w.dv) * es + w.B * w.Lx * w.H * ((w.dk + w.dv) * es + 4)
+    if w.gate:
+        b += w.B * w.L * w.H * 4
+    b += w.B * w.H * w.dk * w.dv * 4 * (2 if w.s0 is not None else 1)
+    return b
+
+
+def method_flops(w, dense=False) -> float:
+    """Flops of the chunkwise method: per expanded position 4 d_k d_v (W S and K^T V~),
+    C (2 d_k + d_v) (K K^T, W = T K, U = T V, causal halves) and C^2 / 3 (the triangular solve); per
+    output 2 d_k d_v (Q S) and C (d_k + d_v) (the causal Q K^T and its product with V~).  dense:
+    the C-terms over full C x C tiles (twice the causal count)."""
+    C, dk, dv = w.chunk, w.dk, w.dv
+    m = 2 if dense else 1
+    npos, nout = w.B * w.H * w.Lx, w.B * w.H * w.L
+    return npos * (4 * dk * dv + m * C * (2 * dk + dv) + C * C / 3) + nout * (2 * dk * dv + m * C * (dk + dv))
+
+
+def _mfma_peak(w):
+    return (MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS) * 1e12
+
+
 def roofline_of(w, r):
-    """Roofline record for the dominant (longest) kernel of one prefill step."""
+    """Roofline record of the dominant (longest) launch of one forward pass: the pass's
+    compulsory bytes over that launch's mean duration."""
     phase = max(r["kernel_ms"], key=r["kernel_ms"].get)
     ms = r["kernel_ms"][phase]
-    _, fb, ff = KERNELS[phase]
-    nb, nf = fb(w), ff(w)
+    nb = compulsory_bytes(w)
     gbs = nb / (ms * 1e-3) / 1e9
-    tflops = nf / (ms * 1e-3) / 1e12
-    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    traffic = {ph: measured_traffic(w, ph) for ph in KERNELS}
+    step_traffic = sum(traffic.values()) if all(v is not None for v in traffic.values()) else None
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w, phase),
-            "kernel": phase, "kernel_ms": round(ms, 5), "bytes_per_launch": nb, "flops_per_launch": nf,
-            "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / mfma_peak, 4)}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic[phase],
+            "kernel": phase, "kernel_ms": round(ms, 5), "bytes_per_launch": nb,
+            "launch_bytes": KERNELS[phase][1](w), "traffic_step": step_traffic,
+            "traffic_ratio": None if step_traffic is None else round(step_traffic / nb, 3)}
+
+
+def step_roofline(w, ms_per_step):
+    """The whole forward pass against the roofline: compulsory bytes and method flops over the
+    measured time per step."""
+    t = ms_per_step * 1e-3
+    nb, F, Fd = compulsory_bytes(w), method_flops(w), method_flops(w, dense=True)
+    peak = _mfma_peak(w)
+    I = F / nb
+    ceiling = min(peak, HBM_PEAK_GBS * 1e9 * I)
+    return {"ms": round(ms_per_step, 5), "compulsory_bytes": nb, "alg_flops": round(F), "dense_flops": round(Fd),
+            "intensity_flop_per_B": round(I, 1), "bound": "hbm" if ceiling < peak else "mfma",
+            "hbm_GBs": round(nb / t / 1e9, 1), "hbm_frac": round(nb / t / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_frac_alg": round(F / t / peak, 4), "mfma_frac_dense": round(Fd / t / peak, 4),
+            "roofline_frac": round(F / t / ceiling, 4), "floor_us": round(nb / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
 
 
 def time_backward(w, steps, warmup=2):
@@ -455,13 +508,64 @@ def time_decode(w, steps, n_states=8, kda=False):
     torch.cuda.synchronize()
     copy_us = e0.elapsed_time(e1) * 1e3 / steps
     del src, dst
+    ceil = stream_ceiling(nel * 4, n_buf=n_states)
     return {"us_per_step": round(per_step_us, 3), "tokens_per_s": w.B * steps / (ms * 1e-3),
+            "stream_ceiling": {k: v for k, v in ceil.items() if k != "sweep_us"},
+            "frac_of_stream_ceiling": round(ceil["us"] / per_step_us, 4),
             "wall_tokens_per_s": w.B * steps / wall, "achieved_GBs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "warm_us_per_step": round(warm_us, 3),
             "warm_GBs": round(decode_bytes(w, kda) / (warm_us * 1e-6) / 1e9, 1),
             "graph_us_per_step": round(graph_us, 3), "graph_tokens_per_s": round(w.B / (graph_us * 1e-6), 1),
             "state_copy_us": round(copy_us, 3),
             "state_copy_GBs": round(2 * nel * 4 / (copy_us * 1e-6) / 1e9, 1)}
+
+
+def stream_ceiling(nbytes, n_buf=8, reps=32):
+    """The best rate of the library's plain streaming copy (delta_measure_copy) reading nbytes and
+    writing nbytes, cycling n_buf buffer pairs so that nothing stays in the 256 MB Infinity Cache,
+    over a sweep of its launch shapes: the practical ceiling of a kernel that moves each byte once."""
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    src = [torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(n_buf)]
+    dst = [torch.empty_like(x) for x in src]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best, sweep = None, {}
+    for unroll in (1, 2, 4, 8):
+        for blocks in (1024, 2048, 4096, 8192):
+            for nt in (0, 1):
+                for i in range(n_buf):
+                    D.measure_copy(src[i], dst[i], unroll=unroll, blocks=blocks, nontemporal=nt)
+                e0.record()
+                for i in range(reps):
+                    D.measure_copy(src[i % n_buf], dst[i % n_buf], unroll=unroll, blocks=blocks, nontemporal=nt)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                sweep["u%d_b%d_nt%d" % (unroll, blocks, nt)] = round(us, 2)
+                if best is None or us < best[0]:
+                    best = (us, unroll, blocks, nt)
+    del src, dst
+    us, unroll, blocks, nt = best
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 3), "bytes": 2 * nbytes, "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "unroll": unroll, "blocks": blocks, "nontemporal": bool(nt), "sweep_us": sweep}
+
+
+def cpu_baseline_decode(w, steps):
+    """The fp64 oracle on the decode workload: every (b, h) runs its `steps` tokens as one
+    sequence from the same start state (the decode step is the recurrence's token step)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    xs = [W.make_decode_inputs(w, t) for t in range(steps)]
+    cat = lambda key: None if xs[0][key] is None else np.concatenate([x[key] for x in xs], axis=1)
+    S0 = W.make_decode_state(w)
+    args = [cat(k) for k in ("q", "k", "v", "beta", "g_log")]
+    t0 = time.perf_counter()
+    oracle.fwd(*args, S0, n_h=w.n_h)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.B * steps / dt, 1), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "all %d (b,h) sequences x %d steps (whole workload), fp64, %.2f s" % (w.B * w.H, steps, dt)}
 
 
 def cpu_baseline(w, budget_s=15.0):
@@ -499,6 +603,8 @@ def main():
                     help="time only delta_bwd on the workload (--steps calls) and print its line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (for HBM counter scaling)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the batch-64 decode step (scalar gate, then KDA) and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (one (b, h) shard of the work); "
@@ -514,6 +620,16 @@ def main():
         sys.exit(1)
 
     w = W.get(args.workload)
+    if args.decode_only:
+        if args.copy_calibration_mib:
+            src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
+            D.measure_copy(src, torch.empty_like(src), unroll=4, blocks=4096)
+            torch.cuda.synchronize()
+            del src
+        dec = time_decode(W.DECODE, W.DECODE_STEPS)
+        kd = time_decode(W.DECODE, W.DECODE_STEPS, kda=True)
+        print(json.dumps({"workload": W.DECODE.name, "decode": dec, "kda_decode": kd}), flush=True)
+        return
     if args.layer_only:
         print(json.dumps({"workload": w.name, "layer": time_layer(w, args.steps)}), flush=True)
         return
@@ -541,6 +657,7 @@ def main():
                    "n_h": w.n_h, "chunk": w.chunk, "gate": w.gate, "state": "fp32",
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
         "roofline": roofline_of(w, r),
+        "step": step_roofline(w, r["ms_per_step"]),
         "kernels_ms": {k: round(v, 5) for k, v in r["kernel_ms"].items()},
         "ms_per_step_with_events": round(r["ms_per_step_with_events"], 5),
         "graph": {"ms_per_step": round(r["graph_ms_per_step"], 5), "tokens_per_s": round(r["graph_tokens_per_s"], 1)},
@@ -558,12 +675,19 @@ def main():
                 others[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1), "ms_per_step": round(ro["ms_per_step"], 5),
                                 "graph_tokens_per_s": round(ro["graph_tokens_per_s"], 1),
                                 "median_call_ms": {k: round(v, 5) for k, v in ro["median_call_ms"].items()},
-                                "roofline": roofline_of(wo, ro)}
+                                "kernels_ms": {k: round(v, 5) for k, v in ro["kernel_ms"].items()},
+                                "roofline": roofline_of(wo, ro), "step": step_roofline(wo, ro["ms_per_step"])}
+                if wo.n_h > 1:  # DeltaProduct: expanded positions (L * n_h per sequence) per second
+                    others[name]["positions_per_s"] = round(ro["tokens_per_s"] * wo.n_h, 1)
+                if not args.no_cpu_baseline:
+                    others[name]["cpu_baseline"] = cpu_baseline(wo, budget_s=5.0)
                 log("[bench] %s: %.3f ms/step, %.3e tokens/s" % (name, ro["ms_per_step"], ro["tokens_per_s"]))
             except Exception as e:  # an auxiliary line must not hide the main one
                 others[name] = {"error": repr(e)}
         try:
             dec = time_decode(W.DECODE, W.DECODE_STEPS)
+            if not args.no_cpu_baseline:
+                dec["cpu_baseline"] = cpu_baseline_decode(W.DECODE, W.DECODE_STEPS)
             others[W.DECODE.name] = dec
             log("[bench] decode: %s" % dec)
             kd = time_decode(W.DECODE, W.DECODE_STEPS, kda=True)

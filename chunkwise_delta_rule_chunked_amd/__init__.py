@@ -73,6 +73,8 @@ def load_library():
     lib.delta_bwd.argtypes = [SP] + [P] * 15 + [ctypes.c_size_t, P]
     lib.delta_layer_prologue.argtypes = [SP, ctypes.c_int32, ctypes.c_float] + [P] * 9 + [P]
     lib.delta_layer_epilogue.argtypes = [SP, ctypes.c_float, P, P, P, P, P]
+    lib.delta_measure_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+    lib.delta_measure_copy.restype = ctypes.c_int
     lib.delta_strerror.argtypes = [ctypes.c_int]
     lib.delta_strerror.restype = ctypes.c_char_p
     for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_noalloc, lib.delta_fwd_intra, lib.delta_fwd_inter,
@@ -83,9 +85,9 @@ def load_library():
     return lib
 
 
-def header_functions() -> list:
-    """Names of the functions include/delta.h declares."""
-    txt = open(_HEADER).read()
+def header_functions(header: str = _HEADER) -> list:
+    """Names of the functions a header of include/ declares (default include/delta.h)."""
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(delta_\w+)\s*\(", txt, flags=re.M)
 
@@ -192,6 +194,16 @@ def fwd_noalloc(q, k, v, beta, g_log, S0, O, S_final, *, n_h: int = 1, chunk: in
         _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32), _stream(stream))
     _check(rc, "delta_fwd_noalloc")
     return O, S_final
+
+
+def measure_copy(src, dst, *, unroll: int = 4, blocks: int = 4096, nontemporal: bool = False, stream=None):
+    """delta_measure_copy (include/delta_measure.h): a plain streaming copy of src into dst (GPU
+    tensors of equal byte size), the measured ceiling of a kernel that moves each byte once."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _check(load_library().delta_measure_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, int(unroll), int(blocks),
+                                             int(bool(nontemporal)), _stream(stream)), "delta_measure_copy")
 
 
 def bwd_workspace_bytes(B, L, H, dk, dv, n_h=1, chunk=64, dtype=BF16) -> int:

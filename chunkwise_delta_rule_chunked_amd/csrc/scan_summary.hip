@@ -181,13 +181,8 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       for (int j = 0; j < 4; ++j) {
         const int row = dkrow(t, 4 * g4 + j), col = 16 * (tile0 + c) + m;
         float x;
-        if (isv) {
-          x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
-          // segment 0's start state, which the outputs launch reads instead of S0
-          if (seg == 0) p.Sst[((long)head * p.P * DK + row) * DV + col] = x;
-        } else {
-          x = (row == col - DV) ? 1.f : 0.f;  // identity columns of the transition map
-        }
+        if (isv) x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
+        else x = (row == col - DV) ? 1.f : 0.f;  // identity columns of the transition map
         S[c][t][j] = x;
       }
   // the compiler waits for these loads at their first use: use them here, before any prefetch
@@ -308,6 +303,15 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   // its consumer rounds it to for its products); segment 0 starts from S0 and needs no
   // transition map
   float* SMs = p.SM + ((long)head * p.P + seg) * DK * (DV + DK);
+  // segment 0's start state, which the outputs launch reads instead of S0 (copied here, after the
+  // chunk loop, so that the loop's schedule is not disturbed by these stores)
+  if (seg == 0 && isv) {
+    for (int i = lane + WAVE * (wave & 3); i < DK * DV / 4; i += 4 * WAVE) {
+      const long off = (long)head * DK * DV + 4L * i;
+      const floatx4 x = p.S0 ? *reinterpret_cast<const floatx4*>(p.S0 + off) : floatx4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<floatx4*>(p.Sst + (long)head * p.P * DK * DV + 4L * i) = x;
+    }
+  }
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll

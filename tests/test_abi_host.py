@@ -30,6 +30,17 @@ def test_exports_every_header_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_measure_header_exported(lib):
+    names = D.header_functions(os.path.join(ROOT, "include", "delta_measure.h"))
+    assert names == ["delta_measure_copy"] and hasattr(lib, "delta_measure_copy")
+    # argument checks come before any device call
+    assert lib.delta_measure_copy(None, None, 0, 4, 16, 0, None) == 0
+    assert lib.delta_measure_copy(None, fake(1), 64, 4, 16, 0, None) == -1
+    assert lib.delta_measure_copy(fake(0), fake(1), 40, 4, 16, 0, None) == -4
+    assert lib.delta_measure_copy(fake(0), fake(1), 64, 3, 16, 0, None) == -3
+    assert lib.delta_measure_copy(fake(0), ctypes.c_void_p(A + 32), 64, 4, 16, 0, None) == -6
+
+
 def test_strerror(lib):
     for code in range(0, -10, -1):
         msg = D.strerror(code)
