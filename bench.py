@@ -392,6 +392,48 @@ def time_backward(w, steps, warmup=2):
             "workspace_mib": round(ws.numel() / 2**20, 1)}
 
 
+KDA_WORKLOAD = "kda_b2h16_l8k"   # the Gated DeltaNet workload's shape and inputs, decays per key channel
+F32_VALU_PEAK_TFLOPS = 157.3
+
+
+def time_kda(steps, warmup=2):
+    """delta_fwd_kda (the token recurrence with a decay per key channel) on the 32-head, 8K-token
+    shape: `steps` back-to-back calls timed with HIP events.  Its bound is the fp32 vector ALU (a
+    chain of L dependent steps of ~7 d_k d_v flops per sequence), so the roofline is that
+    arithmetic against the fp32 vector peak, with the compulsory bytes beside it."""
+    import torch
+    import chunkwise_delta_rule_chunked_amd as D
+    import workloads as W
+    w = W.CONFIGS["gdn_b2h16_l8k"].replace(name=KDA_WORKLOAD)
+    inp = W.make_inputs(w)
+    a = torch.from_numpy(W.make_kda_decays(w)).cuda()
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda x, d: torch.from_numpy(x).to(d).cuda()
+    q, k, v = dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt)
+    beta, S0 = dev(inp["beta"], torch.float32), dev(inp["S0"], torch.float32)
+    O = torch.empty((w.B, w.L, w.H, w.dv), dtype=dt, device="cuda")
+    SF = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    run = lambda: D.fwd_kda(q, k, v, beta, a, S0, O=O, S_final=SF)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    th = w.B * w.L * w.H
+    flops = th * 7 * w.dk * w.dv
+    nb = compulsory_bytes(w) - w.B * w.L * w.H * 4 + th * w.dk * 4   # a per-channel log decay in place of g
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "steps": steps,
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / F32_VALU_PEAK_TFLOPS, 4), "flops": flops, "compulsory_bytes": nb,
+                         "hbm_frac": round(nb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}}
+
+
 def time_layer(w, steps, width=4):
     """delta_layer_prologue and delta_layer_epilogue on the workload's shapes (seeded inputs),
     `steps` calls each timed with HIP events; GB/s from the bytes each must move (inputs read
@@ -603,6 +645,8 @@ def main():
                     help="time only delta_bwd on the workload (--steps calls) and print its line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (for HBM counter scaling)")
+    ap.add_argument("--kda-only", action="store_true",
+                    help="time only delta_fwd_kda on the 32-head 8K-token shape and print its line")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the batch-64 decode step (scalar gate, then KDA) and print its line")
     args = ap.parse_args()
@@ -620,6 +664,9 @@ def main():
         sys.exit(1)
 
     w = W.get(args.workload)
+    if args.kda_only:
+        print(json.dumps({"workload": KDA_WORKLOAD, "kda": time_kda(args.steps, args.warmup)}), flush=True)
+        return
     if args.decode_only:
         if args.copy_calibration_mib:
             src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
@@ -695,6 +742,12 @@ def main():
             log("[bench] kda decode: %s" % kd)
         except Exception as e:
             others[W.DECODE.name] = {"error": repr(e)}
+        try:
+            kd = time_kda(max(5, args.steps // 10))
+            others[KDA_WORKLOAD] = kd
+            log("[bench] kda prefill: %s" % kd)
+        except Exception as e:
+            others[KDA_WORKLOAD] = {"error": repr(e)}
         try:
             ly = time_layer(w, max(20, args.steps))
             others["layer_" + w.name] = ly

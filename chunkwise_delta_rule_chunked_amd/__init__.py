@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "fwd_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -69,6 +69,7 @@ def load_library():
     lib.delta_chunk_wy.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_decode_kda.argtypes = [SP, P, P, P, P, P, P, P, P]
+    lib.delta_fwd_kda.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     lib.delta_bwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.delta_bwd.argtypes = [SP] + [P] * 15 + [ctypes.c_size_t, P]
     lib.delta_layer_prologue.argtypes = [SP, ctypes.c_int32, ctypes.c_float] + [P] * 9 + [P]
@@ -78,7 +79,7 @@ def load_library():
     lib.delta_strerror.argtypes = [ctypes.c_int]
     lib.delta_strerror.restype = ctypes.c_char_p
     for f in (lib.delta_fwd_workspace_bytes, lib.delta_fwd, lib.delta_fwd_noalloc, lib.delta_fwd_intra, lib.delta_fwd_inter,
-              lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda, lib.delta_bwd_workspace_bytes,
+              lib.delta_chunk_wy, lib.delta_decode, lib.delta_decode_kda, lib.delta_fwd_kda, lib.delta_bwd_workspace_bytes,
               lib.delta_bwd, lib.delta_layer_prologue, lib.delta_layer_epilogue):
         f.restype = ctypes.c_int
     _lib = lib
@@ -398,6 +399,27 @@ def decode(q, k, v, beta, g_log, S, *, n_h: int = 1, scale: float = 1.0, O=None,
                           _dev(S, "S", torch.float32), _dev(O, "O", q.dtype), _stream(stream))
     _check(rc, "delta_decode")
     return O
+
+
+def fwd_kda(q, k, v, beta, a_log, S0=None, *, scale: float = 1.0, O=None, S_final=None, want_state: bool = True,
+            stream=None):
+    """KDA over a sequence (delta_fwd_kda): q, k [B,L,H,dk], v [B,L,H,dv] (bf16 or fp32), beta
+    [B,L,H] and a_log [B,L,H,dk] (log of the per-channel decay) fp32, S0 [B,H,dk,dv] fp32 or None.
+    Returns (O, S_final); pass S_final=S0 to update the state in place."""
+    torch = _torch()
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    sh = make_shape(B, L, H, dk, dv, 1, 64, _dtype_code(q), scale)
+    if O is None:
+        O = torch.empty((B, L, H, dv), dtype=q.dtype, device=q.device)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    rc = load_library().delta_fwd_kda(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype),
+                                      _dev(v, "v", q.dtype), _dev(beta, "beta", torch.float32),
+                                      _dev(a_log, "a_log", torch.float32), _dev(S0, "S0", torch.float32),
+                                      _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32), _stream(stream))
+    _check(rc, "delta_fwd_kda")
+    return O, S_final
 
 
 def decode_kda(q, k, v, beta, a_log, S, *, scale: float = 1.0, O=None, stream=None):

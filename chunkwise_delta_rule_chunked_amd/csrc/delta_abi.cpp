@@ -518,6 +518,38 @@ int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const v
   return run_decode(s, q, k, v, beta, nullptr, a_log, S, O, stream);
 }
 
+int delta_fwd_kda(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+                  const float* a_log, const float* S0, void* O, float* S_final, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->n_h != 1) return DELTA_ERR_BAD_SHAPE;
+  const size_t es = esize(s->dtype);
+  const size_t nt = (size_t)s->B * s->L * s->H, BH = (size_t)s->B * s->H;
+  if (nt > 0 && (!q || !k || !v || !beta || !a_log || !O)) return DELTA_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, a_log, S0, O, S_final};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4)) return DELTA_ERR_MISALIGNED;
+  const Range in[] = {range(q, q ? nt * s->dk * es : 0), range(k, k ? nt * s->dk * es : 0),
+                      range(v, v ? nt * s->dv * es : 0), range(beta, beta ? nt * 4 : 0),
+                      range(a_log, a_log ? nt * s->dk * 4 : 0), range(S0, S0 ? BH * s->dk * s->dv * 4 : 0)};
+  const Range ro = range(O, O ? nt * s->dv * es : 0), rs = range(S_final, S_final ? BH * s->dk * s->dv * 4 : 0);
+  for (const Range& r : in) {
+    if (overlap(ro, r)) return DELTA_ERR_ALIAS;
+    if (overlap(rs, r) && !(S0 && S_final == S0 && r.lo == reinterpret_cast<uintptr_t>(S0))) return DELTA_ERR_ALIAS;
+  }
+  if (overlap(ro, rs)) return DELTA_ERR_ALIAS;
+  if (BH == 0 || (s->L == 0 && !S_final)) return DELTA_OK;
+  if ((rc = launch_guard())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (validate_on() && (rc = validate_small(beta, nt, a_log, nt * s->dk, st))) return rc;
+  delta::KdaParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = s->B, p.L = s->L, p.H = s->H, p.DK = s->dk, p.DV = s->dv, p.scale = s->scale;
+  p.q = q, p.k = k, p.v = v, p.beta = beta, p.a_log = a_log, p.S0 = S0, p.O = O, p.S_final = S_final;
+  return hip_status(delta::launch_kda_fwd(p, s->dtype == DELTA_BF16, st));
+}
+
 int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const void* xq, const void* xk,
                          const void* xv, const float* wq, const float* wk, const float* wv, void* q, void* k,
                          void* v, void* stream) {

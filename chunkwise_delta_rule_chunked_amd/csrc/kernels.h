@@ -44,6 +44,20 @@ struct DecodeParams {
   void* O;              // [B, 1, H, DV]
 };
 
+// KDA forward over a sequence (kda.hip): n_h = 1, a decay per key channel.
+struct KdaParams {
+  int B, L, H, DK, DV;
+  float scale;
+  const void* q;        // [B, L, H, DK]
+  const void* k;        // [B, L, H, DK]
+  const void* v;        // [B, L, H, DV]
+  const float* beta;    // [B, L, H]
+  const float* a_log;   // [B, L, H, DK] log alpha per key channel
+  const float* S0;      // [B, H, DK, DV] or nullptr
+  void* O;              // [B, L, H, DV]
+  float* S_final;       // [B, H, DK, DV] or nullptr; may be S0
+};
+
 // One backward problem after validation (shape fields as in FwdParams).
 struct BwdParams {
   int B, L, H, DK, DV, nh, C, Lx, NT;
@@ -99,6 +113,7 @@ hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_
 hipError_t launch_layer_prologue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_layer_epilogue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
+hipError_t launch_kda_fwd(const KdaParams& p, bool bf16, hipStream_t st);
 // Opt-in input check (validate.hip): beta finite, log gates finite or -inf.  Writes one flag word
 // per workgroup (VALIDATE_BLOCKS words) at `flags`.
 constexpr int VALIDATE_BLOCKS = 128;

@@ -34,8 +34,8 @@
  *   - NaN or infinite inputs are not masked: they propagate to the outputs they reach.
  *
  * Environment switches, read at every call:
- *   - DELTA_VALIDATE=1: delta_fwd, delta_fwd_intra, delta_bwd, delta_decode and
- *     delta_decode_kda first check beta (must be finite) and the log gates (finite or
+ *   - DELTA_VALIDATE=1: delta_fwd, delta_fwd_intra, delta_bwd, delta_decode,
+ *     delta_decode_kda and delta_fwd_kda first check beta (must be finite) and the log gates (finite or
  *     -inf) and return DELTA_ERR_BAD_VALUE, having written nothing but the start of the
  *     workspace, if one is not.  The check waits for the stream (the call is then
  *     synchronous) and must not be used while the stream is being captured into a graph.
@@ -226,6 +226,24 @@ int delta_decode(const delta_shape* s, const void* q, const void* k, const void*
  */
 int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const void* v,
                      const float* beta, const float* a_log, float* S, void* O, void* stream);
+
+/*
+ * KDA forward over a sequence: the delta rule with a decay per key channel ("08 linear delta rule
+ * & DPLR", section 1.4 table, KDA row, and section 5:
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = scale S_t^T q_t),
+ * run token by token with the state held on chip (the recurrence, not a chunked form).
+ * s->n_h must be 1; s->chunk is ignored.
+ *   q, k [B, L, H, dk], v [B, L, H, dv]      dtype
+ *   beta [B, L, H]                            float32
+ *   a_log [B, L, H, dk]                       float32   log alpha per key channel (finite or -inf,
+ *                                                       <= 0); not NULL; 16-byte aligned
+ *   S0 [B, H, dk, dv] float32 or NULL (zeros); O [B, L, H, dv] dtype (written);
+ *   S_final [B, H, dk, dv] float32 or NULL; may equal S0 (in place).
+ * Alignment, aliasing and error codes as delta_fwd (no workspace).
+ */
+int delta_fwd_kda(const delta_shape* s, const void* q, const void* k, const void* v,
+                  const float* beta, const float* a_log, const float* S0, void* O,
+                  float* S_final, void* stream);
 
 /*
  * Bytes of device workspace delta_bwd needs for this shape: T in float32, the gate prefix and

@@ -20,6 +20,9 @@ oracle's token loop (oracle/oracle.c) or its UT-factor routine
   one_chunk_closed_form
                 the fully parallel form O = (Q K^T * M) T V of section 2.4
                 (S0 = 0, ungated, one chunk)
+  chunked_kda   a chunkwise form of KDA (a decay per key channel), derived below
+                from the recurrence of the page's section 1.4 table and section 5;
+                it pins oracle.fwd_kda
 """
 from __future__ import annotations
 
@@ -125,6 +128,49 @@ def chunked(q, k, v, beta, g_log=None, S0=None, n_h=1, C=16, scale=1.0):
                     O[b, pos[r] // n_h, h] = Oc[r]
                 gC = gam[-1]
                 S = gC * S + (np.exp(gc[-1] - gc)[:, None] * K).T @ Vt
+            SF[b, h] = S
+    return O, SF
+
+
+def chunked_kda(q, k, v, beta, a_log, S0=None, C=16, scale=1.0):
+    """Chunkwise KDA in fp64.  The pages give KDA's recurrence, S_t = (I - b_t k_t k_t^T) D_t
+    S_{t-1} + b_t k_t v_t^T with D_t = Diag(alpha_t) ("08 linear delta rule & DPLR", section 1.4
+    table and section 5), but not a chunk algorithm; this one follows from it.
+
+    Write the update as S_t = D_t S_{t-1} + k_t u_t^T with u_t = b_t (v_t - S_{t-1}^T D_t k_t).
+    Inside a chunk that starts from S, with G_r = D_1 ... D_r (cumulative, restarting each chunk),
+    S_r = G_r S + sum_{j<=r} G_r G_j^-1 k_j u_j^T, so
+        u_r + b_r sum_{j<r} (k_r^T G_r G_j^-1 k_j) u_j = b_r (v_r - S^T G_r k_r),
+    i.e. U = T (V - (K G) S) with T = (I + A)^-1 diag(b), A_rj = b_r k_r^T G_r G_j^-1 k_j (j < r):
+    the UT transform of section 2.2 with the Gram matrix decayed per channel.  The readout
+    o_r = S_r^T q_r gives O = scale ((Q G) S + Aqk U), Aqk_rj = q_r^T G_r G_j^-1 k_j (j <= r), and
+    the chunk ends at S' = G_C S + (K G_C G^-1)^T U.  The ratios G_r G_j^-1 are formed only for
+    j <= r, where they are products of decays (no overflow).  A log decay of -inf (alpha = 0) is
+    taken as -800, whose exponential is exactly 0 in fp64 (so a reset stays exact)."""
+    q, k, v, beta, a_log, S0 = map(_f64, (q, k, v, beta, a_log, S0))
+    a_log = np.maximum(a_log, -800.0)
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    NT = -(-L // C)
+    O = np.zeros((B, L, H, dv))
+    SF = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else S0[b, h].copy()
+            for n in range(NT):
+                pos = np.arange(n * C, min((n + 1) * C, L))
+                c = len(pos)
+                K, V, Q, bt = k[b, pos, h], v[b, pos, h], q[b, pos, h] * scale, beta[b, pos, h]
+                Gc = np.cumsum(a_log[b, pos, h], axis=0)                       # [c, dk]
+                lower = np.tril(np.ones((c, c), dtype=bool))
+                diff = np.where(lower[:, :, None], Gc[:, None, :] - Gc[None, :, :], -np.inf)
+                R = np.exp(diff)                                              # [r, j, dk], j <= r
+                A = np.tril(bt[:, None] * np.einsum("rc,jc,rjc->rj", K, K, R), -1)
+                T = _forward_substitution_inverse(A) * bt[None, :]
+                U = T @ (V - (K * np.exp(Gc)) @ S)
+                Aqk = np.einsum("rc,jc,rjc->rj", Q, K, R)
+                O[b, pos, h] = (Q * np.exp(Gc)) @ S + Aqk @ U
+                S = np.exp(Gc[-1])[:, None] * S + (K * np.exp(Gc[-1][None, :] - Gc)).T @ U
             SF[b, h] = S
     return O, SF
 

@@ -623,3 +623,20 @@ def test_kda_zero_channel_decay_erases_row():
     e = v[0, 0, 0].astype(np.float64) - Sd.T @ k[0, 0, 0].astype(np.float64)
     want = Sd + float(beta[0, 0, 0]) * np.outer(k[0, 0, 0].astype(np.float64), e)
     assert np.allclose(S[0, 0], want, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("C,L,s0,reset", [(4, 9, True, False), (16, 37, True, False), (8, 30, False, True),
+                                          (32, 70, True, True), (1, 5, True, False)])
+def test_kda_chunked_form_matches_oracle(C, L, s0, reset):
+    """The chunkwise KDA form (tests/formulations.py, derived from the page's recurrence) and the
+    oracle's token loop agree to fp64 rounding, for chunks of 1..32 positions, ragged tails,
+    strong per-channel decays and channel resets (log alpha = -inf)."""
+    q, k, v, beta, a, S0 = _kda_inputs(130 + C, L=L, dk=8, dv=5, s0=s0)
+    a = (a * 3.0).astype(f32)                       # stronger decays: cumulative logs reach ~-60
+    if reset:
+        a[0, L // 3, 1, 2] = -np.inf
+        a[1, L // 2, 0, :] = -np.inf
+    O, S = oracle.fwd_kda(q, k, v, beta, a, S0, scale=0.8)
+    Oc, Sc = F.chunked_kda(q, k, v, beta, a, S0, C=C, scale=0.8)
+    assert np.abs(O - Oc).max() <= 1e-10 * max(1.0, np.abs(O).max())
+    assert np.abs(S - Sc).max() <= 1e-10 * max(1.0, np.abs(S).max())

@@ -17,7 +17,7 @@ Distributions (per the pages' model descriptions):
     cross-chunk state alive.
 
 Seeds: numpy PCG64 streams from SeedSequence([2026, cfg_id, stream]) with
-streams q=0, k=1, v=2, beta=3, g=4, S0=5, dO=6, dS_final=7, decode step t -> 100 + t,
+streams q=0, k=1, v=2, beta=3, g=4, S0=5, dO=6, dS_final=7, KDA decays=8, decode step t -> 100 + t,
 KDA decay of decode step t -> 300 + t.  Values are
 drawn in fp64, cast to fp32, and for bf16 workloads rounded to the nearest bf16
 (ties to even); both the oracle and the GPU consume exactly those values.
@@ -192,6 +192,14 @@ def make_kda_decay(w: Workload, step: int) -> np.ndarray:
     rng = _rng(w.cfg_id, 300 + step)
     shift = {"cfg3": 2.0, "weak": -4.0}[w.gate or "cfg3"]
     return (-_softplus(rng.standard_normal((w.B, 1, w.H, w.dk)) + shift)).astype(np.float32)
+
+
+def make_kda_decays(w: Workload, salt: int = 0) -> np.ndarray:
+    """Per-key-channel log decays of a whole sequence for the KDA recurrence, [B, L, H, dk]
+    float32 (stream 8): -softplus(N(0,1) + shift) per channel and token, shift as the workload's
+    gate (cfg3 when it has none)."""
+    shift = {"cfg3": 2.0, "weak": -4.0}[w.gate or "cfg3"]
+    return (-_softplus(_draw(w, 8, (w.B, w.L, w.H, w.dk), salt) + shift)).astype(np.float32)
 
 
 def make_decode_state(w: Workload) -> np.ndarray:
