@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "fwd_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_prologue_step", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "fwd_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -74,6 +74,8 @@ def load_library():
     lib.delta_bwd.argtypes = [SP] + [P] * 15 + [ctypes.c_size_t, P]
     lib.delta_layer_prologue.argtypes = [SP, ctypes.c_int32, ctypes.c_float] + [P] * 9 + [P]
     lib.delta_layer_epilogue.argtypes = [SP, ctypes.c_float, P, P, P, P, P]
+    lib.delta_layer_prologue_step.argtypes = [SP, ctypes.c_int32, ctypes.c_float] + [P] * 12 + [P]
+    lib.delta_layer_prologue_step.restype = ctypes.c_int
     lib.delta_measure_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
     lib.delta_measure_copy.restype = ctypes.c_int
     lib.delta_strerror.argtypes = [ctypes.c_int]
@@ -270,6 +272,29 @@ def layer_prologue(xq, xk, xv, wq, wk, wv, *, n_h: int = 1, eps: float = 1e-6, q
                                              _dev(wk, "wk", f32), _dev(wv, "wv", f32), _dev(q, "q", xq.dtype),
                                              _dev(k, "k", xq.dtype), _dev(v, "v", xq.dtype), _stream(stream))
     _check(rc, "delta_layer_prologue")
+    return q, k, v
+
+
+def layer_prologue_step(xq, xk, xv, wq, wk, wv, conv_q, conv_k, conv_v, *, n_h: int = 1, eps: float = 1e-6,
+                        q=None, k=None, v=None, stream=None):
+    """One decode token through the layer prologue (delta_layer_prologue_step): xq [B,1,H,dk],
+    xk [B,n_h,H,dk], xv [B,n_h,H,dv]; conv_* [B,width-1,H,d] (the filters' recent inputs, updated
+    in place; None when width = 1).  Returns (q, k, v)."""
+    torch = _torch()
+    B, _, H, dk = xq.shape
+    dv = xv.shape[-1]
+    width = wq.shape[1]
+    sh = make_shape(B, 1, H, dk, dv, n_h, 64, _dtype_code(xq))
+    q = torch.empty_like(xq) if q is None else q
+    k = torch.empty_like(xk) if k is None else k
+    v = torch.empty_like(xv) if v is None else v
+    f32 = torch.float32
+    rc = load_library().delta_layer_prologue_step(
+        ctypes.byref(sh), int(width), float(eps), _dev(xq, "xq", xq.dtype), _dev(xk, "xk", xq.dtype),
+        _dev(xv, "xv", xq.dtype), _dev(wq, "wq", f32), _dev(wk, "wk", f32), _dev(wv, "wv", f32),
+        _dev(conv_q, "conv_q", xq.dtype), _dev(conv_k, "conv_k", xq.dtype), _dev(conv_v, "conv_v", xq.dtype),
+        _dev(q, "q", xq.dtype), _dev(k, "k", xq.dtype), _dev(v, "v", xq.dtype), _stream(stream))
+    _check(rc, "delta_layer_prologue_step")
     return q, k, v
 
 

@@ -585,6 +585,45 @@ int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const v
   return hip_status(delta::launch_layer_prologue(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+int delta_layer_prologue_step(const delta_shape* s, int32_t width, float eps, const void* xq, const void* xk,
+                              const void* xv, const float* wq, const float* wk, const float* wv, void* conv_q,
+                              void* conv_k, void* conv_v, void* q, void* k, void* v, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->L != 1) return DELTA_ERR_BAD_SHAPE;
+  if (width < 1 || width > 4) return DELTA_ERR_UNSUPPORTED_DIM;
+  if (!(eps >= 0.f)) return DELTA_ERR_BAD_SHAPE;
+  const size_t es = esize(s->dtype);
+  const size_t BH = (size_t)s->B * s->H, nkv = BH * s->n_h, W1 = (size_t)width - 1;
+  if (BH > 0 && (!xq || !xk || !xv || !wq || !wk || !wv || !q || !k || !v)) return DELTA_ERR_NULL_ARG;
+  if (BH > 0 && W1 > 0 && (!conv_q || !conv_k || !conv_v)) return DELTA_ERR_NULL_ARG;
+  const void* ptrs[] = {xq, xk, xv, wq, wk, wv, conv_q, conv_k, conv_v, q, k, v};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  const Range in[] = {range(xq, BH * s->dk * es), range(xk, nkv * s->dk * es), range(xv, nkv * s->dv * es),
+                      range(wq, (size_t)s->H * s->dk * width * 4), range(wk, (size_t)s->H * s->dk * width * 4),
+                      range(wv, (size_t)s->H * s->dv * width * 4)};
+  const Range out[] = {range(q, BH * s->dk * es), range(k, nkv * s->dk * es), range(v, nkv * s->dv * es),
+                       range(conv_q, W1 * BH * s->dk * es), range(conv_k, W1 * BH * s->dk * es),
+                       range(conv_v, W1 * BH * s->dv * es)};
+  constexpr int NO = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < NO; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return DELTA_ERR_ALIAS;
+    for (int j = i + 1; j < NO; ++j)
+      if (overlap(out[i], out[j])) return DELTA_ERR_ALIAS;
+  }
+  if (BH == 0) return DELTA_OK;
+  if ((rc = launch_guard())) return rc;
+  LayerParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = s->B, p.L = 1, p.H = s->H, p.DK = s->dk, p.DV = s->dv, p.Lx = s->n_h, p.width = width;
+  p.eps = eps;
+  p.xq = xq, p.xk = xk, p.xv = xv, p.wq = wq, p.wk = wk, p.wv = wv, p.q = q, p.k = k, p.v = v;
+  p.cq = conv_q, p.ck = conv_k, p.cv = conv_v;
+  return hip_status(delta::launch_layer_prologue_step(p, s->dtype == DELTA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 int delta_layer_epilogue(const delta_shape* s, float eps, const void* o, const void* g, const float* weight,
                          void* y, void* stream) {
   int rc = check_shape(s);

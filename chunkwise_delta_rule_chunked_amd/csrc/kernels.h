@@ -89,6 +89,7 @@ struct LayerParams {
   const void *xq, *xk, *xv;       // prologue inputs [B, L, H, DK], [B, Lx, H, DK], [B, Lx, H, DV]
   const float *wq, *wk, *wv;      // [H * d, width] conv filters
   void *q, *k, *v;                // prologue outputs, shapes as the inputs
+  void *cq, *ck, *cv;             // decode step: filter states [B, width - 1, H, d], in/out
   const void* o;                  // epilogue: mixer output [B, L, H, DV]
   const void* g;                  // gate projection [B, L, H, DV]
   const float* weight;            // [DV]
@@ -112,6 +113,7 @@ hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_t st);
 hipError_t launch_layer_prologue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_layer_epilogue(const LayerParams& p, bool bf16, hipStream_t st);
+hipError_t launch_layer_prologue_step(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t st);
 hipError_t launch_kda_fwd(const KdaParams& p, bool bf16, hipStream_t st);
 // Opt-in input check (validate.hip): beta finite, log gates finite or -inf.  Writes one flag word

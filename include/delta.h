@@ -295,6 +295,25 @@ int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const v
                          void* v, void* stream);
 
 /*
+ * Layer prologue for one decode token (the same steps as delta_layer_prologue), the filters'
+ * recent inputs carried between calls.  s->L must be 1; s->chunk and s->scale are ignored.
+ *   xq [B, 1, H, dk], xk [B, n_h, H, dk], xv [B, n_h, H, dv]   dtype    this token's projections
+ *   wq, wk [H*dk, width], wv [H*dv, width]                      float32  filters
+ *   conv_q [B, width-1, H, dk], conv_k [B, width-1, H, dk], conv_v [B, width-1, H, dv]
+ *                                        dtype, read and updated: the width-1 most recent input
+ *                                        rows of each filter, oldest first (NULL when width = 1)
+ *   q [B, 1, H, dk], k [B, n_h, H, dk], v [B, n_h, H, dv]      dtype    outputs (written)
+ * k and v take their n_h rows in order, each a step of the filter.  After a prefill over L
+ * inputs, the state is the last width-1 input rows of xq (of xk, xv: along their L*n_h rows),
+ * zeros where the sequence is shorter.  No overlap between outputs, states and inputs.
+ * 16-byte aligned pointers.  Error codes as delta_layer_prologue (L != 1: DELTA_ERR_BAD_SHAPE).
+ */
+int delta_layer_prologue_step(const delta_shape* s, int32_t width, float eps, const void* xq,
+                              const void* xk, const void* xv, const float* wq, const float* wk,
+                              const float* wv, void* conv_q, void* conv_k, void* conv_v, void* q,
+                              void* k, void* v, void* stream);
+
+/*
  * Layer epilogue (same figure: Norm, then the output gate): per head of each token,
  *   y = o / sqrt(mean(o^2) + eps) * weight * SiLU(g)
  *   o, g, y [B, L, H, dv] dtype; weight [dv] float32 (shared by the heads).

@@ -24,7 +24,7 @@ def test_exports_every_header_function(lib):
     assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_noalloc", "delta_fwd_intra", "delta_fwd_inter",
                           "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
                           "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_decode_kda", "delta_fwd_kda",
-                          "delta_bwd_workspace_bytes", "delta_bwd", "delta_layer_prologue",
+                          "delta_bwd_workspace_bytes", "delta_bwd", "delta_layer_prologue", "delta_layer_prologue_step",
                           "delta_layer_epilogue", "delta_strerror"}
     for n in names:
         assert hasattr(lib, n), n
