@@ -465,10 +465,10 @@ int run_decode(const delta_shape* s, const void* q, const void* k, const void* v
   if (rc) return rc;
   if (s->L != 1) return DELTA_ERR_BAD_SHAPE;
   if ((size_t)s->B * s->H > 0 && (!q || !k || !v || !beta || !S || !O)) return DELTA_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, S, O};
+  const void* ptrs[] = {q, k, v, S, O, a_log};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
-  if (!aligned(beta, 4) || !aligned(g_log, 4) || !aligned(a_log, 4)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4) || !aligned(g_log, 4)) return DELTA_ERR_MISALIGNED;
   const size_t es = esize(s->dtype);
   const size_t BH = (size_t)s->B * s->H;
   const Range in[] = {range(q, BH * s->dk * es), range(k, BH * s->n_h * s->dk * es),

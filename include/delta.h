@@ -221,7 +221,7 @@ int delta_decode(const delta_shape* s, const void* q, const void* k, const void*
  * with n_h = 1 (s->n_h must be 1), the scalar gate replaced by
  *   a_log [B, 1, H, dk] float32: log alpha per key channel (row r of S decays by
  *                                exp(a_log[.., r])), finite or -inf, <= 0; not NULL.
- * Same argument checks and error codes as delta_decode; a_log must be 4-byte aligned and may
+ * Same argument checks and error codes as delta_decode; a_log must be 16-byte aligned and may
  * not overlap S or O.
  */
 int delta_decode_kda(const delta_shape* s, const void* q, const void* k, const void* v,
