@@ -102,7 +102,8 @@ def summary_bytes(w) -> int:
     nch = min(-(-w.Lx // w.chunk), (P - 1) * NS)
     pos = min(w.Lx, nch * w.chunk)
     b = w.B * pos * w.H * (w.dk + w.dv) * es + w.B * w.H * nch * w.chunk * (w.chunk * es + 4)
-    b += w.B * w.H * w.dk * w.dv * 4 if w.s0 is not None else 0
+    # S0 read for segment 0 (and once more for its copy), segment 0's start state written
+    b += w.B * w.H * w.dk * w.dv * 4 * (3 if w.s0 is not None else 1)
     # S_loc (fp32) of segments 0..P-2, M (element type) of segments 1..P-2
     b += w.B * w.H * ((P - 1) * w.dk * w.dv * 4 + (P - 2) * w.dk * w.dk * es)
     return b
@@ -132,15 +133,19 @@ def combine_flops(w) -> int:
 
 
 def outputs_bytes(w) -> int:
-    """Reads q, k, v, T, gate prefix, S0 and segment start states; writes O, S_final."""
+    """Reads q, k, v, T, gate prefix and the segments' start states (S0 itself when the sequence
+    is not split); writes O, S_final."""
     es = _es(w)
     P, _ = _segments(w)
     NT = -(-w.Lx // w.chunk)
     b = w.B * w.L * w.H * (w.dk + w.dv) * es           # q, O
     b += w.B * w.Lx * w.H * (w.dk + w.dv) * es         # k, v
     b += w.B * w.H * NT * w.chunk * (w.chunk * es + 4)  # T, gate prefix
-    b += w.B * w.H * w.dk * w.dv * 4 * (2 if w.s0 is not None else 1)
-    b += w.B * w.H * (P - 1) * w.dk * w.dv * 4
+    b += w.B * w.H * w.dk * w.dv * 4                    # S_final
+    if P > 1:
+        b += w.B * w.H * P * w.dk * w.dv * 4            # start states
+    elif w.s0 is not None:
+        b += w.B * w.H * w.dk * w.dv * 4                # S0
     return b
 
 
