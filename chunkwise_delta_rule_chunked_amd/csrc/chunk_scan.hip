@@ -869,24 +869,21 @@ static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-#ifndef OUT_NCW
-#define OUT_NCW 4
-#endif
-// Summary: 2 state tiles per chain wavefront; with bf16 inputs 8 chain wavefronts, so that one
-// workgroup covers 16 tiles (the d_v value and d_k transition columns of a segment together when
-// d_v + d_k <= 256: K and T are then staged once per segment, and a segment's workgroups fit the
-// GPU in one round); fp32 state fragments need twice the registers, so fp32 takes 4.
-#ifndef SUM_NCW
-#define SUM_NCW (sizeof(E) == 2 ? 8 : 4)
-#endif
-#ifndef SUM_CT
-#define SUM_CT 2
-#endif
+// Outputs: 4 chain wavefronts (plus the 4 loading ones), one 16-column tile each when d_v <= 64,
+// else two.  Summary: 2 state tiles per chain wavefront; with bf16 inputs 8 chain wavefronts, so
+// that one workgroup covers 16 tiles (the d_v value and d_k transition columns of a segment
+// together when d_v + d_k <= 256: K and T are then staged once per segment, and a segment's
+// workgroups fit the GPU in one round); fp32 state fragments need twice the registers, so fp32
+// takes 4.
+constexpr int OUT_NCW = 4, SUM_CT = 2;
+template <typename E>
+constexpr int sum_ncw() { return sizeof(E) == 2 ? 8 : 4; }
+
 template <typename E, int DK, int C>
 static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
   switch (phase) {
     case SCAN_SUMMARY:
-      return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, SUM_NCW, true>(p, st) : hipSuccess;
+      return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, sum_ncw<E>(), true>(p, st) : hipSuccess;
     case SCAN_COMBINE:
       if (p.P <= 1 || p.B * p.H == 0) return hipSuccess;
     {

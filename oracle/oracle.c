@@ -5,29 +5,22 @@
  * includes this file; only the tests, the smoke check and the benchmark's CPU
  * baseline leg load it.  It shares no source with the GPU path.
  *
- * What it computes is the plain token-by-token recurrence, in fp64, with no
- * chunking, blocking or reordering:
+ * What it computes is the definition of the recurrence, token by token, in fp64, with no
+ * chunking, blocking or reordering.  For each (b, h) the d_k x d_v state starts at S0 (or 0);
+ * token i multiplies the state by its gate g_i and then applies its n_h Householder steps in
+ * order, H_{i,j} = (I - beta_{i,j} k_{i,j} k_{i,j}^T) H_{i,j-1} + beta_{i,j} k_{i,j} v_{i,j}^T
+ * (each step computed as the rank-1 write of the residual v - H^T k, which is the same matrix);
+ * its output is scale * H_{i,n_h}^T q_i; the state after the last token is S_final.
  *
- *   S <- S0 (or 0)                                  S is d_k x d_v
- *   for each token i:
- *       S <- g_i * S                                (gate, once per token)
- *       for each sub-step j = 0 .. n_h-1, t = i*n_h + j:
- *           e <- v_t - S^T k_t                      (prediction residual)
- *           S <- S + beta_t * k_t e^T               (rank-1 write of the residual)
- *       o_i <- scale * S^T q_i                      (read after the last sub-step)
- *   S_final <- S
- *
- * Sources (cited by page title and section):
- *  - "08 linear delta rule & DPLR" page, section 1.2 (Householder form
- *    S_t = (I - beta k k^T) S_{t-1} + beta k v^T) and the recurrent reference
- *    routine after section 2.3 (read v_old = S^T k, write beta k (v - v_old)^T,
- *    output S^T (q*scale)).
- *  - same page, section 3 (Gated DeltaNet): S_t = (I - beta k k^T) alpha_t S_{t-1}
- *    + beta k v^T; alpha is a scalar, so the decay may be applied first.
- *  - DeltaProduct reading notes, sections 2.2 and 2.6 (n_h ordered Householder
- *    steps per token, H_{i,0} = g_i H_{i-1}, the pseudocode of the gated
- *    recurrence) and section 4.1 (keys/values/betas laid out as an expanded
- *    sequence, one output per token after its last sub-step).
+ * Sources (cited by page title and section; the equations, not any listing):
+ *  - "08 linear delta rule & DPLR" page, section 1.2: S_t = (I - beta k k^T) S_{t-1} + beta k v^T
+ *    (equal to the erase-write form of section 1.1), read out as o_t = S_t^T q_t.
+ *  - same page, section 3 (Gated DeltaNet): S_t = (I - beta k k^T) alpha_t S_{t-1} + beta k v^T
+ *    with a scalar alpha_t, which commutes with the Householder factor.
+ *  - DeltaProduct reading notes, section 2.2 (n_h Householder factors per token) and section 2.6
+ *    (the gated form H_{i,0} = g_i H_{i-1}, A_i = g_i F_{i,n_h} ... F_{i,1}), section 4.1 (keys,
+ *    values and betas of a token's sub-steps consecutive; one output per token after its last
+ *    sub-step).
  *
  * The gate enters as log g (fp32), exponentiated here in fp64; log g = -inf is
  * an exact reset (g = 0).  Inputs are float32 arrays holding exactly the values

@@ -176,7 +176,10 @@ def chunked_kda(q, k, v, beta, a_log, S0=None, C=16, scale=1.0):
 
 
 def dplr(q, w_log, a, bvec, kk, vv, S0=None, scale=1.0):
-    """S_t = (Diag(w_t) + a_t b_t^T) S_{t-1} + kk_t vv_t^T, o_t = S_t^T (q_t scale).
+    """The generic diagonal-plus-low-rank state transition of the "08 linear delta rule & DPLR"
+    page, section 5, applied token by token: S_t = (Diag(w_t) + a_t b_t^T) S_{t-1} + kk_t vv_t^T,
+    o_t = S_t^T (q_t scale), with the section's reductions (DeltaNet: w = 1, a = -beta k, b = k;
+    Gated DeltaNet: w = g, b = g k; KDA: w = alpha) supplied by the caller.
     w_log [B,T,H,dk] (log of the diagonal), a/bvec/kk [B,T,H,dk], vv [B,T,H,dv]."""
     q, w_log, a, bvec, kk, vv, S0 = map(_f64, (q, w_log, a, bvec, kk, vv, S0))
     B, T, H, dk = q.shape
