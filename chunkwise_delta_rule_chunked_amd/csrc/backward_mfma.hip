@@ -1,0 +1,481 @@
+// Per-chunk gradients of the backward pass on MFMA, for bf16 inputs with d_k = d_v = 128 and
+// chunk 64 (other shapes use bwd_chunk_kernel in backward.hip, whose header states the
+// gradients; this kernel evaluates the same formulas).  Per chunk, with N = (I + A)^-1,
+// T = N diag(beta), gamma = exp(gc), w = exp(gc_C - gc), Gam_ij = exp(gc_i - gc_j) (j <= i), the
+// chunk's start state S and the gradient G' of its end state:
+//   KS = K S, KG = K G';  Y = V - gamma KS;  V~ = T Y
+//   dV~ = w KG + P^T dO  (P = Q K^T * Gam, on and below the diagonal);  dY = T^T dV~
+//   dT = dV~ Y^T, dOV = dO V~^T                        (sums over the value dimension)
+//   dQ = gamma (dO S^T) + E1 K,  dK = w (V~ G'^T) - gamma (dY S^T) + E1^T Q + (dGm + dGm^T) K
+// with E1 = Gam * dOV and dGm from the chunk-local C x C algebra (dA = -strictLower(N^T dT T^T),
+// dGm = diag(beta) (Gam * dA)), and the gate-prefix and beta gradients from the same algebra.
+// Two row sums over the value dimension that the algebra needs follow from the accumulated
+// products: sum_c QS_ic dO_ic = Q_i . (dO S^T)_i, sum_c KS_ic dY_ic = K_i . (dY S^T)_i and
+// sum_c KG_ic V~_ic = K_i . (V~ G'^T)_i.
+//
+// One workgroup of 8 wavefronts per chunk.  K, Q, V, dO (bf16), N (float32), T and P (bf16)
+// are staged in LDS; the value dimension is taken in quarters of 32 columns, the next quarter's
+// S and G' loaded into registers while the current one is computed.  Per quarter wavefront w owns
+// the 16 x 16 tile (rows 16 (w / 2), columns 16 (w % 2)) of KS, KG, Y, V~, dV~ and dY, and
+// accumulates 16 output tiles of the products that sum over the value dimension (two of dT and
+// dOV, and the tiles of column block w of d_k for dO S^T, V~ G'^T, dY S^T) across the quarters.
+// Products on the 16x16x32 bf16 MFMA with float32 accumulation; the C x C algebra in float32
+// on the vector ALUs.
+#include "common.h"
+#include "kernels.h"
+
+namespace delta {
+namespace bwdm {
+
+constexpr int C = 64, DK = 128, DV = 128, QC = 32, NW = 8, NTH = NW * WAVE;
+constexpr int PC = C + 4;  // float row pitch of the C x C float32 matrices
+
+// A 16x16x32 fragment from a tile stored with the contraction index along its rows ([n][k] for
+// a B operand, [m][k] for an A operand): lane (g, i) takes row r0 + i, elements k0 + 8 g .. + 7.
+__device__ inline bf16x8 frag_rows(const Tile<bf16>& t, int r0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(t.at(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+// A 16x16x32 fragment from a tile stored with the contraction index down its columns ([k][n]
+// for a B operand; for an A operand the tile is the transpose, [k][m]): lane (g, i) takes
+// column c0 + i, elements k0 + 8 g .. + 7, by two transpose reads.
+__device__ inline bf16x8 frag_cols(const Tile<bf16>& t, int k0, int c0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int r = k0 + 8 * g + (i >> 2), e = c0 + 4 * (i & 3);
+  const bf16x4 lo = read_tr4(t.at(r, e)), hi = read_tr4(t.at(r + 4, e));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ inline floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// The accumulator tile (rows r0 + 4 g .. + 3 of column c0 + i) into a bf16 tile.
+__device__ inline void put_tile(const Tile<bf16>& t, int r0, int c0, floatx4 x, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *t.at(r0 + 4 * g + j, c0 + i) = (bf16)x[j];
+}
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of a DPP row (quad xor 1, xor 2, half-mirror, mirror)
+__device__ inline float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+
+using L128 = TileLayout<bf16, 128>;
+using L64 = TileLayout<bf16, 64>;
+using L32 = TileLayout<bf16, QC>;
+
+struct __attribute__((aligned(16))) Lds {
+  bf16 K[C * L128::LD], Q[C * L128::LD], V[C * L128::LD], dO[C * L128::LD];  // V, dO: then E1, Gs
+  bf16 T[C * L64::LD], P[C * L64::LD];
+  float N[C][PC];
+  union {
+    struct {
+      bf16 S[DK * L32::LD], G[DK * L32::LD];                              // this quarter of S, G'
+      bf16 Y[C * L32::LD], Vt[C * L32::LD], dVt[C * L32::LD], dY[C * L32::LD];
+    } q;
+    struct {
+      float R0[C][PC], R1[C][PC], R2[C][PC];
+    } m;
+  } u;
+  float gc[C], gam[C], w[C], beta[C], dbd[C], dgc[C], dw[C], rsum[C];
+  float part[3][NW][C];  // per-wave partial row sums: Q . dO S^T, K . dY S^T, K . V~ G'^T
+  float sgs[NW];
+};
+static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget");
+
+__global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
+  __shared__ Lds s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, m = lane & 15;
+  const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
+  const int nh = p.nh;
+  const long P0 = (long)n * C, chunk = (long)bh * p.NT + n;
+  const int valid = (int)min((long)C, (long)p.Lx - P0);
+  const long HD = (long)p.H * DK;  // d_k == d_v: one row stride for all four tensors
+
+  const Tile<bf16> Kt{s.K, L128::LD, L128::MASK}, Qt{s.Q, L128::LD, L128::MASK}, Vt{s.V, L128::LD, L128::MASK},
+      Ot{s.dO, L128::LD, L128::MASK};
+  const Tile<bf16> Tt{s.T, L64::LD, L64::MASK}, Pt{s.P, L64::LD, L64::MASK};
+  const Tile<bf16> Sq{s.u.q.S, L32::LD, L32::MASK}, Gq{s.u.q.G, L32::LD, L32::MASK};
+  const Tile<bf16> Yq{s.u.q.Y, L32::LD, L32::MASK}, Vq{s.u.q.Vt, L32::LD, L32::MASK},
+      dVq{s.u.q.dVt, L32::LD, L32::MASK}, dYq{s.u.q.dY, L32::LD, L32::MASK};
+  // E1 and Gs = dGm + dGm^T after the value loop, in the V and dO areas
+  const Tile<bf16> E1t{s.V, L64::LD, L64::MASK}, Gst{s.dO, L64::LD, L64::MASK};
+
+  // ---- stage K, Q (scaled, rows without a readout zero), V, dO, N and the per-position scalars
+  {
+    const bf16* kb = static_cast<const bf16*>(p.k) + ((long)b * p.Lx + P0) * HD + (long)h * DK;
+    const bf16* vb = static_cast<const bf16*>(p.v) + ((long)b * p.Lx + P0) * HD + (long)h * DV;
+    const bf16* qb = static_cast<const bf16*>(p.q) + (long)b * p.L * HD + (long)h * DK;
+    const bf16* ob = static_cast<const bf16*>(p.dO) + (long)b * p.L * HD + (long)h * DV;
+    u32x4 rk[2], rv[2], rq[2], ro[2];
+    floatx4 rn[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
+      const bool ok = r < valid, last = ok && (P0 + r) % nh == nh - 1;
+      const long tok = (P0 + r) / nh;
+      rk[u] = ok ? *reinterpret_cast<const u32x4*>(kb + r * HD + c) : u32x4{0, 0, 0, 0};
+      rv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + r * HD + c) : u32x4{0, 0, 0, 0};
+      rq[u] = last ? *reinterpret_cast<const u32x4*>(qb + tok * HD + c) : u32x4{0, 0, 0, 0};
+      ro[u] = last ? *reinterpret_cast<const u32x4*>(ob + tok * HD + c) : u32x4{0, 0, 0, 0};
+      const int rr = idx >> 4, cc = (idx & 15) * 4;  // N: 64 rows of 16 float4
+      rn[u] = *reinterpret_cast<const floatx4*>(p.N + chunk * C * C + rr * C + cc);
+    }
+    if (tid < C) {
+      const float g = p.gc[chunk * C + tid], gC = p.gc[chunk * C + C - 1];
+      s.gc[tid] = g;
+      s.gam[tid] = expf(g);
+      s.w[tid] = expf(gC - g);
+      s.beta[tid] = tid < valid ? p.beta[(b * (long)p.Lx + P0 + tid) * p.H + h] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
+      *reinterpret_cast<u32x4*>(Kt.at(r, c)) = rk[u];
+      *reinterpret_cast<u32x4*>(Vt.at(r, c)) = rv[u];
+      *reinterpret_cast<u32x4*>(Ot.at(r, c)) = ro[u];
+      // q scaled by the readout scale
+      bf16x8 qv = __builtin_bit_cast(bf16x8, rq[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = (bf16)((float)qv[e] * p.scale);
+      *reinterpret_cast<bf16x8*>(Qt.at(r, c)) = qv;
+      const int rr = idx >> 4, cc = (idx & 15) * 4;
+      *reinterpret_cast<floatx4*>(&s.N[rr][cc]) = rn[u];
+    }
+  }
+  __syncthreads();
+  // T = N diag(beta) in bf16, and P = (Q K^T) * Gam on and below the diagonal (bf16), on MFMA:
+  // wave w forms P blocks (w / 4 + 2 t, w % 4), t = 0, 1
+  for (int idx = tid; idx < C * C; idx += NTH) {
+    const int r = idx >> 6, c = idx & 63;
+    *Tt.at(r, c) = (bf16)(c <= r ? s.N[r][c] * s.beta[c] : 0.f);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int bi = wave / 4 + 2 * t, bj = wave % 4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 32) acc = mma(frag_rows(Qt, 16 * bi, k0, lane), frag_rows(Kt, 16 * bj, k0, lane), acc);
+    const int c = 16 * bj + m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * bi + 4 * g4 + j;
+      acc[j] = c <= r ? acc[j] * gate_exp(s.gc[r] - s.gc[c]) : 0.f;
+    }
+    put_tile(Pt, 16 * bi, 16 * bj, acc, lane);
+  }
+
+  // ---- the value dimension in quarters
+  // this wave's tile of the quarter: rows 16 rb, columns 16 ct of the quarter
+  const int rb = wave >> 1, ct = wave & 1;
+  // accumulators over the quarters: dT and dOV tiles (rows 16 (w / 4 + 2 t), columns 16 (w % 4)),
+  // and column block w of d_k for dQraw = dO S^T, A1 = V~ G'^T, A2 = dY S^T (all 4 row blocks)
+  floatx4 aT[2], aO[2], aQ[4], a1[4], a2[4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) aT[t] = aO[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) aQ[r] = a1[r] = a2[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float sgs = 0.f;
+  // S and G' quarters: 128 rows x 32 float columns each, 2 x 16-byte pieces per thread each
+  floatx4 ps[2], pg[2];
+  const float* Sn = p.Sn + chunk * DK * DV;
+  const float* Gn = p.Gn + chunk * DK * DV;
+  auto fetch = [&](int q) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + NTH * u, r = idx >> 3, c = QC * q + (idx & 7) * 4;
+      ps[u] = *reinterpret_cast<const floatx4*>(Sn + r * DV + c);
+      pg[u] = *reinterpret_cast<const floatx4*>(Gn + r * DV + c);
+    }
+  };
+  fetch(0);
+#pragma unroll 1
+  for (int q = 0; q < DV / QC; ++q) {
+    __syncthreads();  // the previous quarter's tiles are no longer read
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + NTH * u, r = idx >> 3, c = (idx & 7) * 4;
+      *reinterpret_cast<bf16x4*>(Sq.at(r, c)) = bf16x4{(bf16)ps[u][0], (bf16)ps[u][1], (bf16)ps[u][2], (bf16)ps[u][3]};
+      *reinterpret_cast<bf16x4*>(Gq.at(r, c)) = bf16x4{(bf16)pg[u][0], (bf16)pg[u][1], (bf16)pg[u][2], (bf16)pg[u][3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sgs += ps[u][e] * pg[u][e];
+    }
+    if (q + 1 < DV / QC) fetch(q + 1);  // in flight during this quarter
+    __syncthreads();
+    const int c0 = QC * q;
+    // KS and KG (contract d_k), then Y = V - gamma KS
+    floatx4 ks = {0.f, 0.f, 0.f, 0.f}, kg = ks;
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 32) {
+      const bf16x8 ka = frag_rows(Kt, 16 * rb, k0, lane);
+      ks = mma(ka, frag_cols(Sq, k0, 16 * ct, lane), ks);
+      kg = mma(ka, frag_cols(Gq, k0, 16 * ct, lane), kg);
+    }
+    floatx4 y;
+    {
+      const bf16x4 v4 = read_tr4(Vt.at(16 * rb + 4 * g4 + (m >> 2), c0 + 16 * ct + 4 * (m & 3)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (float)v4[j] - s.gam[16 * rb + 4 * g4 + j] * ks[j];
+    }
+    put_tile(Yq, 16 * rb, 16 * ct, y, lane);
+    __syncthreads();
+    // V~ = T Y (T zero above the diagonal), dV~ = w KG + P^T dO (P^T zero below it)
+    floatx4 vt = {0.f, 0.f, 0.f, 0.f}, dvt = vt;
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 32) {
+      if (k0 <= 16 * rb) vt = mma(frag_rows(Tt, 16 * rb, k0, lane), frag_cols(Yq, k0, 16 * ct, lane), vt);
+      if (k0 + 32 > 16 * rb)
+        dvt = mma(frag_cols(Pt, k0, 16 * rb, lane), frag_cols(Ot, k0, c0 + 16 * ct, lane), dvt);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dvt[j] += s.w[16 * rb + 4 * g4 + j] * kg[j];
+    put_tile(Vq, 16 * rb, 16 * ct, vt, lane);
+    put_tile(dVq, 16 * rb, 16 * ct, dvt, lane);
+    __syncthreads();
+    // dY = T^T dV~ (T^T zero below the diagonal)
+    {
+      floatx4 dy = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 32)
+        if (k0 + 32 > 16 * rb) dy = mma(frag_cols(Tt, k0, 16 * rb, lane), frag_cols(dVq, k0, 16 * ct, lane), dy);
+      put_tile(dYq, 16 * rb, 16 * ct, dy, lane);
+    }
+    __syncthreads();
+    // the products that sum over this quarter's 32 columns (one 32-deep step each)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int bi = wave / 4 + 2 * t, bj = wave % 4;
+      aT[t] = mma(frag_rows(dVq, 16 * bi, 0, lane), frag_rows(Yq, 16 * bj, 0, lane), aT[t]);
+      aO[t] = mma(frag_rows(Ot, 16 * bi, c0, lane), frag_rows(Vq, 16 * bj, 0, lane), aO[t]);
+    }
+    {
+      const bf16x8 sb = frag_rows(Sq, 16 * wave, 0, lane), gb = frag_rows(Gq, 16 * wave, 0, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        aQ[r] = mma(frag_rows(Ot, 16 * r, c0, lane), sb, aQ[r]);
+        a1[r] = mma(frag_rows(Vq, 16 * r, 0, lane), gb, a1[r]);
+        a2[r] = mma(frag_rows(dYq, 16 * r, 0, lane), sb, a2[r]);
+      }
+    }
+  }
+
+  // ---- row sums over the value dimension from the accumulated products (this wave: d_k block w)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float pq[4], pa2[4], pa1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * r + 4 * g4 + j, d = 16 * wave + m;
+      const float qv = (float)*Qt.at(row, d), kv = (float)*Kt.at(row, d);
+      pq[j] = row_sum16(qv * aQ[r][j]);
+      pa2[j] = row_sum16(kv * a2[r][j]);
+      pa1[j] = row_sum16(kv * a1[r][j]);
+    }
+    if (m == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * r + 4 * g4 + j;
+        s.part[0][wave][row] = pq[j];
+        s.part[1][wave][row] = pa2[j];
+        s.part[2][wave][row] = pa1[j];
+      }
+    }
+  }
+  {
+    float x = sgs;
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
+    if (lane == 0) s.sgs[wave] = x;
+  }
+  __syncthreads();  // the quarter tiles are dead: R0..R2 overwrite them
+  // dT -> R0, dOV -> R1; K K^T (strictly lower) -> R2; per-position row sums
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int bi = wave / 4 + 2 * t, bj = wave % 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s.u.m.R0[16 * bi + 4 * g4 + j][16 * bj + m] = aT[t][j];
+      s.u.m.R1[16 * bi + 4 * g4 + j][16 * bj + m] = aO[t][j];
+    }
+  }
+  for (int t = wave; t < 10; t += NW) {  // the 10 lower 16 x 16 blocks of K K^T
+    int bi = 0;
+    while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+    const int bj = t - bi * (bi + 1) / 2;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 32) acc = mma(frag_rows(Kt, 16 * bi, k0, lane), frag_rows(Kt, 16 * bj, k0, lane), acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.u.m.R2[16 * bi + 4 * g4 + j][16 * bj + m] = acc[j];
+  }
+  if (tid < C) {
+    float q = 0.f, k2 = 0.f, k1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      q += s.part[0][w][tid];
+      k2 += s.part[1][w][tid];
+      k1 += s.part[2][w][tid];
+    }
+    s.dgc[tid] = s.gam[tid] * (q - k2);  // gamma_i (sum_c QS dO - sum_c KS dY)
+    s.dw[tid] = k1;                      // sum_c KG V~
+  }
+  __syncthreads();
+
+  // ---- chunk-local C x C algebra (float32, vector ALUs): thread (r0, c) owns rows r0 + 32 u and
+  // columns c + 16 v
+  constexpr int RS = NTH / 16, NU = C / RS;
+  const int c = tid & 15, r0 = tid >> 4;
+  auto& N = s.N;
+  auto& R0 = s.u.m.R0;
+  auto& R1 = s.u.m.R1;
+  auto& R2 = s.u.m.R2;
+  // dbeta's diagonal term diag(N^T dT), and X = dT diag(beta) N^T (= dT T^T)
+  if (tid < C) {
+    float acc = 0.f;
+    for (int i = tid; i < C; ++i) acc += N[i][tid] * R0[i][tid];
+    s.dbd[tid] = acc;
+  }
+  float X[NU][4];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = r0 + RS * u, j = c + 16 * v;
+      float acc = 0.f;
+      for (int k = 0; k <= j; ++k) acc += R0[i][k] * s.beta[k] * N[j][k];
+      X[u][v] = acc;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) R0[r0 + RS * u][c + 16 * v] = X[u][v];
+  __syncthreads();
+  // dA = -strictLower(N^T X)
+  float dA[NU][4];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = r0 + RS * u, j = c + 16 * v;
+      float acc = 0.f;
+      if (j < i)
+        for (int k = i; k < C; ++k) acc += N[k][i] * R0[k][j];
+      dA[u][v] = -acc;
+    }
+  __syncthreads();
+  // per entry j <= i: the gate-prefix term t, dbeta's row term, dGm and E1 = Gam * dOV
+  float rbs[NU] = {}, rts[NU] = {};
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = r0 + RS * u, j = c + 16 * v;
+      float t = 0.f, dGm = 0.f, e1 = 0.f;
+      if (j <= i) {
+        const float gm = gate_exp(s.gc[i] - s.gc[j]);
+        const float kk = j < i ? R2[i][j] : 0.f, dov = R1[i][j];
+        const float ta = dA[u][v] * gm * kk;  // zero on the diagonal
+        rbs[u] += ta;
+        t = s.beta[i] * ta + (float)*Pt.at(i, j) * dov;
+        dGm = s.beta[i] * gm * dA[u][v];
+        e1 = gm * dov;
+        rts[u] += t;
+      }
+      X[u][v] = t;       // reused: t
+      dA[u][v] = dGm;    // reused: dGm
+      R1[i][j] = e1;     // each entry read above by its own thread only
+    }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    rbs[u] = row_sum16(rbs[u]);
+    rts[u] = row_sum16(rts[u]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      R0[r0 + RS * u][c + 16 * v] = dA[u][v];
+      R2[r0 + RS * u][c + 16 * v] = X[u][v];
+    }
+    if (c == 0) {
+      s.dbd[r0 + RS * u] += rbs[u];
+      s.rsum[r0 + RS * u] = rts[u];
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    const int i = tid;
+    float col = 0.f;
+    for (int r = i; r < C; ++r) col += R2[r][i];
+    s.dgc[i] += s.rsum[i] - col - s.w[i] * s.dw[i];
+    if (i < valid) p.dbeta[(b * (long)p.Lx + P0 + i) * p.H + h] = s.dbd[i];
+  }
+  // E1 and Gs = dGm + dGm^T in bf16 for the last products
+  for (int idx = tid; idx < C * C; idx += NTH) {
+    const int i = idx >> 6, j = idx & 63;
+    *E1t.at(i, j) = (bf16)R1[i][j];
+    *Gst.at(i, j) = (bf16)(R0[i][j] + R0[j][i]);
+  }
+  __syncthreads();
+  if (tid == 0 && p.dg_log) {
+    const float gC = s.gc[C - 1];
+    float tot = 0.f;
+    for (int i = 0; i < C; ++i) tot += s.w[i] * s.dw[i];
+    for (int o = 0; o < NW; ++o) tot += expf(gC) * s.sgs[o];
+    // reverse cumulative sum over the chunk; the last position also collects the total above
+    float run = tot;
+    for (int i = C - 1; i >= 0; --i) {
+      run += s.dgc[i];
+      const long pos = P0 + i;
+      if (i < valid && pos % nh == 0) p.dg_log[(b * (long)p.L + pos / nh) * p.H + h] = run;
+    }
+  }
+
+  // ---- dQ = gamma dQraw + E1 K, dK = w A1 - gamma A2 + E1^T Q + Gs K  (d_k block w)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    floatx4 dq, dk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * r + 4 * g4 + j;
+      dq[j] = s.gam[row] * aQ[r][j];
+      dk[j] = s.w[row] * a1[r][j] - s.gam[row] * a2[r][j];
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 32) {
+      const bf16x8 kb = frag_cols(Kt, k0, 16 * wave, lane);
+      dq = mma(frag_rows(E1t, 16 * r, k0, lane), kb, dq);
+      dk = mma(frag_cols(E1t, k0, 16 * r, lane), frag_cols(Qt, k0, 16 * wave, lane), dk);
+      dk = mma(frag_rows(Gst, 16 * r, k0, lane), kb, dk);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * r + 4 * g4 + j, d = 16 * wave + m;
+      if (row >= valid) continue;
+      const long pos = P0 + row;
+      p.dk[((b * (long)p.Lx + pos) * p.H + h) * DK + d] = dk[j];
+      if (pos % nh == nh - 1) p.dq[((b * (long)p.L + pos / nh) * p.H + h) * DK + d] = p.scale * dq[j];
+    }
+  }
+}
+
+}  // namespace bwdm
+
+bool bwd_chunk_mfma_applies(const BwdParams& p, bool bf16_in) {
+  return bf16_in && p.DK == bwdm::DK && p.DV == bwdm::DV && p.C == bwdm::C;
+}
+
+hipError_t launch_bwd_chunk_mfma(const BwdParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(bwdm::bwd_chunk_mfma_kernel, dim3((unsigned)((long)p.NT * p.B * p.H)), dim3(bwdm::NTH), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace delta

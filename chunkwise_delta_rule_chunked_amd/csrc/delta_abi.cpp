@@ -372,7 +372,7 @@ namespace {
 // per chunk), and per chunk the start state and the end-of-chunk state gradient.
 size_t states_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.DK * p.DV * 4; }
 size_t bwd_workspace(const FwdParams& p) {
-  return 2 * align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
+  return 3 * align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
 }
 }  // namespace
 
@@ -446,6 +446,10 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   off += align_up(t_bytes(f, 4));
   p.Sn = reinterpret_cast<float*>(ws + off);
   p.Gn = reinterpret_cast<float*>(ws + off + align_up(states_bytes(f)));
+  off += 2 * align_up(states_bytes(f));
+  fi.N = reinterpret_cast<float*>(ws + off);  // N = (I + A)^-1, for the MFMA per-chunk kernel
+  p.N = fi.N;
+  const bool mfma_chunk = delta::bwd_chunk_mfma_applies(p, bf);
   if (f.NT > 0) {
     if ((rc = hip_status(delta::launch_intra_chunk(fi, bf, true, st)))) return rc;
     if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 3, st)))) return rc;
@@ -453,7 +457,8 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   }
   // the reverse pass also writes dS0, so it runs when there are no chunks too
   if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 1, st)))) return rc;
-  if (f.NT > 0) return hip_status(delta::launch_bwd_phase(p, bf, 2, st));
+  if (f.NT > 0)
+    return hip_status(mfma_chunk ? delta::launch_bwd_chunk_mfma(p, st) : delta::launch_bwd_phase(p, bf, 2, st));
   return DELTA_OK;
 }
 

@@ -232,6 +232,11 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = c + e <= r ? nv[e] * bv[e] : 0.f;
     store4<TO>(Tout + idx, x[0], x[1], x[2], x[3]);
+    if (p.N) {  // the backward also takes N itself (beta may be 0, so T does not determine it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = c + e <= r ? nv[e] : 0.f;
+      store4<float>(p.N + ((long)bh * p.NT + n) * C * C + idx, x[0], x[1], x[2], x[3]);
+    }
   }
 }
 

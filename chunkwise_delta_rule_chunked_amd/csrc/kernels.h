@@ -22,6 +22,7 @@ struct FwdParams {
   float* gc;            // [B, H, NT, C] cumulative in-chunk log gate
   float* W;             // chunk_wy only: [B, H, NT, C, DK]
   float* U;             // chunk_wy only: [B, H, NT, C, DV]
+  float* N;             // backward only: [B, H, NT, C, C] (I + A)^-1 in float32, or nullptr
   // sequence split of the inter-chunk pass: P segments of NS chunks (P = 1: no split)
   int P, NS;
   // [B*H, P] segment summaries, each in a slot of DK * (DV + DK) floats: S_loc as float at
@@ -80,6 +81,7 @@ struct BwdParams {
   float* Pm;              // [B*H, NT, C, C] Q K^T * Gam on and below the diagonal (Q scaled)
   float* Sn;              // [B*H, NT, DK, DV] start state of each chunk
   float* Gn;              // [B*H, NT, DK, DV] state gradient at the end of each chunk
+  const float* N;         // [B*H, NT, C, C] (I + A)^-1 float32 (the MFMA per-chunk kernel)
 };
 
 // The layer steps around the mixer (layer.hip).
@@ -111,6 +113,10 @@ hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 // 3 Q K^T * Gam per chunk, 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0),
 // 2 per-chunk gradients.
 hipError_t launch_bwd_phase(const BwdParams& p, bool bf16, int phase, hipStream_t st);
+// Per-chunk gradients on MFMA for bf16 inputs, d_k = d_v = 128, chunk 64 (backward_mfma.hip), in
+// place of phase 2; reads N (float32, from the intra-chunk launch) instead of recomputing it.
+bool bwd_chunk_mfma_applies(const BwdParams& p, bool bf16);
+hipError_t launch_bwd_chunk_mfma(const BwdParams& p, hipStream_t st);
 hipError_t launch_layer_prologue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_layer_epilogue(const LayerParams& p, bool bf16, hipStream_t st);
 hipError_t launch_layer_prologue_step(const LayerParams& p, bool bf16, hipStream_t st);

@@ -190,7 +190,7 @@ def test_bwd_workspace_bytes(lib):
     for B, H, L, dk, dv, C, nh in [(2, 3, 100, 64, 32, 32, 1), (2, 16, 8192, 128, 128, 64, 1), (1, 2, 50, 16, 256, 48, 3)]:
         NT = (L * nh + C - 1) // C
         rc, n = bwd_ws(shape(B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, n_h=nh))
-        assert rc == 0 and n == 2 * up(B * H * NT * C * C * 4) + up(B * H * NT * C * 4) + 2 * up(B * H * NT * dk * dv * 4)
+        assert rc == 0 and n == 3 * up(B * H * NT * C * C * 4) + up(B * H * NT * C * 4) + 2 * up(B * H * NT * dk * dv * 4)
     assert bwd_ws(shape(L=0)) == (0, 0)
     assert bwd_ws(shape(dk=48))[0] == -3
 

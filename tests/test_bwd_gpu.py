@@ -1,8 +1,13 @@
 """GPU parity of the backward pass: delta_bwd (through the C ABI) against the fp64 oracle's
-reverse-mode gradients (oracle_bwd) on the same seeded inputs and cotangents.  Every gradient
-is computed in float32 from inputs both sides read identically (bf16-exact for bf16 cases), so
-one bar holds for both dtypes: per-head relative error (tests/parity.py) <= 1e-4, except the
-log-gate gradient, a sum of up to C * d_v products per token, held to 5e-4."""
+reverse-mode gradients (oracle_bwd) on the same seeded inputs and cotangents.
+
+Bars (per-head relative error, tests/parity.py):
+  - shapes whose per-chunk gradients run on the float32 vector ALUs (every float32 case, and bf16
+    outside d_k = d_v = 128, chunk 64): 1e-4, the log-gate gradient (a sum of up to C * d_v
+    products per token) 5e-4;
+  - bf16 inputs with d_k = d_v = 128 and chunk 64, whose per-chunk gradients run on the bf16
+    MFMA with float32 accumulation (states and intermediate tiles rounded to bf16 as operands):
+    2e-2, the bar the forward pass holds bf16 inputs to."""
 import numpy as np
 import pytest
 
@@ -50,6 +55,10 @@ def run(w, inp, cot, chunk=None, scale=1.0, with_dS=True):
     return {n: (None if t is None else t.cpu().numpy()) for n, t in g.items()}
 
 
+def mfma_path(w, chunk=None):
+    return w.dtype == "bf16" and w.dk == 128 and w.dv == 128 and (chunk or w.chunk) == 64
+
+
 def compare(got, want, tol=TOL, tol_g=TOL_G):
     errs = {}
     for n, ax in AXES.items():
@@ -71,7 +80,7 @@ def test_bwd_matches_oracle(w):
     got = run(w, inp, cot, scale=0.7)
     want = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g_log"], inp["S0"], cot["dO"],
                       cot["dS_final"], n_h=w.n_h, scale=0.7)
-    compare(got, want)
+    compare(got, want, *((2e-2, 2e-2) if mfma_path(w) else (TOL, TOL_G)))
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])
@@ -117,7 +126,7 @@ def test_bwd_empty_sequence():
     assert np.array_equal(got["dS0"], cot["dS_final"])
 
 
-@pytest.mark.parametrize("hb", [(0, 3), (1, 14)])
+@pytest.mark.parametrize("hb", [(0, 0), (0, 3), (1, 14), (1, 15)])
 def test_bwd_full_size_sampled_heads(hb):
     # the prefill workload at full size, one launch for all heads; the oracle on two sampled heads
     w = W.get("gdn_b2h16_l8k")
@@ -131,4 +140,4 @@ def test_bwd_full_size_sampled_heads(hb):
                       cot["dS_final"][b:b + 1, h:h + 1], n_h=w.n_h)
     sub = {n: (None if v is None else (v[b:b + 1, h:h + 1] if n == "dS0" else v[b:b + 1, :, h:h + 1]))
            for n, v in got.items()}
-    compare(sub, want)
+    compare(sub, want, *((2e-2, 2e-2) if mfma_path(w) else (TOL, TOL_G)))
