@@ -76,7 +76,7 @@ struct __attribute__((aligned(16))) Lds {
   float N[C][PC];
   union {
     struct {
-      bf16 S[DK * L32::LD], G[DK * L32::LD];                              // this quarter of S, G'
+      bf16 S[QC * L128::LD], G[QC * L128::LD], Gl[QC * L128::LD];  // this quarter of S^T, G'^T (hi, lo)
       bf16 Y[C * L32::LD], Vt[C * L32::LD], dVt[C * L32::LD], dY[C * L32::LD];
     } q;
     struct {
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
   const Tile<bf16> Kt{s.K, L128::LD, L128::MASK}, Qt{s.Q, L128::LD, L128::MASK}, Vt{s.V, L128::LD, L128::MASK},
       Ot{s.dO, L128::LD, L128::MASK};
   const Tile<bf16> Tt{s.T, L64::LD, L64::MASK}, Pt{s.P, L64::LD, L64::MASK};
-  const Tile<bf16> Sq{s.u.q.S, L32::LD, L32::MASK}, Gq{s.u.q.G, L32::LD, L32::MASK};
+  const Tile<bf16> Sq{s.u.q.S, L128::LD, L128::MASK}, Gq{s.u.q.G, L128::LD, L128::MASK},
+      Glq{s.u.q.Gl, L128::LD, L128::MASK};
   const Tile<bf16> Yq{s.u.q.Y, L32::LD, L32::MASK}, Vq{s.u.q.Vt, L32::LD, L32::MASK},
       dVq{s.u.q.dVt, L32::LD, L32::MASK}, dYq{s.u.q.dY, L32::LD, L32::MASK};
   // E1 and Gs = dGm + dGm^T after the value loop, in the V and dO areas
@@ -183,29 +184,30 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) aQ[r] = a1[r] = a2[r] = floatx4{0.f, 0.f, 0.f, 0.f};
   float sgs = 0.f;
-  // S and G' quarters: 128 rows x 32 float columns each, 2 x 16-byte pieces per thread each
-  floatx4 ps[2], pg[2];
-  const float* Sn = p.Sn + chunk * DK * DV;
-  const float* Gn = p.Gn + chunk * DK * DV;
+  // S^T and G'^T quarters (bf16, as the scans stored them, G' with its low part): 32 d_v rows x
+  // 128 d_k each, one 16-byte piece per thread each
+  u32x4 ps, pg, pgl;
+  const bf16* Sn = static_cast<const bf16*>(p.Snt) + chunk * DV * DK;
+  const bf16* Gn = static_cast<const bf16*>(p.Gnt) + chunk * DV * DK;
+  const bf16* Gnl = static_cast<const bf16*>(p.Gntl) + chunk * DV * DK;
+  const int fr = tid >> 4, fc = (tid & 15) * 8;
   auto fetch = [&](int q) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + NTH * u, r = idx >> 3, c = QC * q + (idx & 7) * 4;
-      ps[u] = *reinterpret_cast<const floatx4*>(Sn + r * DV + c);
-      pg[u] = *reinterpret_cast<const floatx4*>(Gn + r * DV + c);
-    }
+    ps = *reinterpret_cast<const u32x4*>(Sn + (QC * q + fr) * DK + fc);
+    pg = *reinterpret_cast<const u32x4*>(Gn + (QC * q + fr) * DK + fc);
   };
   fetch(0);
 #pragma unroll 1
   for (int q = 0; q < DV / QC; ++q) {
+    pgl = *reinterpret_cast<const u32x4*>(Gnl + (QC * q + fr) * DK + fc);  // (not prefetched: registers)
     __syncthreads();  // the previous quarter's tiles are no longer read
+    *reinterpret_cast<u32x4*>(Sq.at(fr, fc)) = ps;
+    *reinterpret_cast<u32x4*>(Gq.at(fr, fc)) = pg;
+    *reinterpret_cast<u32x4*>(Glq.at(fr, fc)) = pgl;
+    {
+      const bf16x8 sv = __builtin_bit_cast(bf16x8, ps), gv = __builtin_bit_cast(bf16x8, pg),
+                   gl = __builtin_bit_cast(bf16x8, pgl);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + NTH * u, r = idx >> 3, c = (idx & 7) * 4;
-      *reinterpret_cast<bf16x4*>(Sq.at(r, c)) = bf16x4{(bf16)ps[u][0], (bf16)ps[u][1], (bf16)ps[u][2], (bf16)ps[u][3]};
-      *reinterpret_cast<bf16x4*>(Gq.at(r, c)) = bf16x4{(bf16)pg[u][0], (bf16)pg[u][1], (bf16)pg[u][2], (bf16)pg[u][3]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sgs += ps[u][e] * pg[u][e];
+      for (int e = 0; e < 8; ++e) sgs += (float)sv[e] * ((float)gv[e] + (float)gl[e]);
     }
     if (q + 1 < DV / QC) fetch(q + 1);  // in flight during this quarter
     __syncthreads();
@@ -215,8 +217,9 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int k0 = 0; k0 < DK; k0 += 32) {
       const bf16x8 ka = frag_rows(Kt, 16 * rb, k0, lane);
-      ks = mma(ka, frag_cols(Sq, k0, 16 * ct, lane), ks);
-      kg = mma(ka, frag_cols(Gq, k0, 16 * ct, lane), kg);
+      ks = mma(ka, frag_rows(Sq, 16 * ct, k0, lane), ks);
+      kg = mma(ka, frag_rows(Gq, 16 * ct, k0, lane), kg);
+      kg = mma(ka, frag_rows(Glq, 16 * ct, k0, lane), kg);
     }
     floatx4 y;
     {
@@ -226,11 +229,29 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
     }
     put_tile(Yq, 16 * rb, 16 * ct, y, lane);
     __syncthreads();
-    // V~ = T Y (T zero above the diagonal), dV~ = w KG + P^T dO (P^T zero below it)
+    // V~ = T Y (T zero above the diagonal), dV~ = w KG + P^T dO (P^T zero below it).  T enters V~
+    // as a bf16 pair (high part and rounding residual, from N and beta): the log-gate gradient
+    // sums large terms that cancel between the V~ products and the N-based algebra, and a T
+    // rounded to 8 bits in one of them only leaves a residue of the size of those terms.
     floatx4 vt = {0.f, 0.f, 0.f, 0.f}, dvt = vt;
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 32) {
-      if (k0 <= 16 * rb) vt = mma(frag_rows(Tt, 16 * rb, k0, lane), frag_cols(Yq, k0, 16 * ct, lane), vt);
+      if (k0 <= 16 * rb) {
+        const int r = 16 * rb + m, kk = k0 + 8 * g4;
+        const floatx4 n0 = *reinterpret_cast<const floatx4*>(&s.N[r][kk]);
+        const floatx4 n1 = *reinterpret_cast<const floatx4*>(&s.N[r][kk + 4]);
+        const floatx4 b0 = *reinterpret_cast<const floatx4*>(&s.beta[kk]);
+        const floatx4 b1 = *reinterpret_cast<const floatx4*>(&s.beta[kk + 4]);
+        bf16x8 th, tl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = kk + e <= r ? (e < 4 ? n0[e] * b0[e] : n1[e - 4] * b1[e - 4]) : 0.f;
+          th[e] = (bf16)x;
+          tl[e] = (bf16)(x - (float)th[e]);
+        }
+        const bf16x8 yb = frag_cols(Yq, k0, 16 * ct, lane);
+        vt = mma(tl, yb, mma(th, yb, vt));
+      }
       if (k0 + 32 > 16 * rb)
         dvt = mma(frag_cols(Pt, k0, 16 * rb, lane), frag_cols(Ot, k0, c0 + 16 * ct, lane), dvt);
     }
@@ -246,6 +267,13 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
       for (int k0 = 0; k0 < C; k0 += 32)
         if (k0 + 32 > 16 * rb) dy = mma(frag_cols(Tt, k0, 16 * rb, lane), frag_cols(dVq, k0, 16 * ct, lane), dy);
       put_tile(dYq, 16 * rb, 16 * ct, dy, lane);
+      // dY is dv
+      float* dvp = p.dv + ((long)b * p.Lx + P0) * p.H * DV + (long)h * DV + c0 + 16 * ct + m;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * rb + 4 * g4 + j;
+        if (row < valid) dvp[(long)row * p.H * DV] = dy[j];
+      }
     }
     __syncthreads();
     // the products that sum over this quarter's 32 columns (one 32-deep step each)
@@ -256,11 +284,13 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
       aO[t] = mma(frag_rows(Ot, 16 * bi, c0, lane), frag_rows(Vq, 16 * bj, 0, lane), aO[t]);
     }
     {
-      const bf16x8 sb = frag_rows(Sq, 16 * wave, 0, lane), gb = frag_rows(Gq, 16 * wave, 0, lane);
+      const bf16x8 sb = frag_cols(Sq, 0, 16 * wave, lane), gb = frag_cols(Gq, 0, 16 * wave, lane),
+                   gbl = frag_cols(Glq, 0, 16 * wave, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         aQ[r] = mma(frag_rows(Ot, 16 * r, c0, lane), sb, aQ[r]);
-        a1[r] = mma(frag_rows(Vq, 16 * r, 0, lane), gb, a1[r]);
+        const bf16x8 vr = frag_rows(Vq, 16 * r, 0, lane);
+        a1[r] = mma(vr, gbl, mma(vr, gb, a1[r]));
         a2[r] = mma(frag_rows(dYq, 16 * r, 0, lane), sb, a2[r]);
       }
     }

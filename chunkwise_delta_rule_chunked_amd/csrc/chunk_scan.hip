@@ -134,24 +134,40 @@ __device__ inline void loader_rendezvous(unsigned* ctr, unsigned target, int lan
 constexpr int SEG_LOADERS = 4;  // loading wavefronts per workgroup
 constexpr int LDS_BUDGET = 160 * 1024;
 
-template <typename E, int DK, int C, int CT, int NCW, bool SUM>
+// What a launch of seg_kernel does with each segment:
+//   SEG_SUM     the segment summary (S_loc and the transition columns of M)
+//   SEG_OUT     the chain from the segment's start state, writing O (and S_final)
+//   SEG_STATES  the chain from the segment's start state, writing each chunk's start state
+//               (bf16 when the inputs are bf16) instead of O
+// and REV runs the adjoint chain of the backward pass instead (see the reverse chain below).
+enum SegMode { SEG_SUM = 0, SEG_OUT = 1, SEG_STATES = 2 };
+
+template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV>
 struct SegCfg {
+  static constexpr bool SUM = MODE == SEG_SUM;
+  static constexpr bool QA = MODE == SEG_OUT || REV;  // Q staged and A formed per chunk
   static constexpr int ES = sizeof(E);
   static constexpr int TPG = NCW * CT;      // state column tiles per workgroup
   static constexpr int THREADS = (NCW + SEG_LOADERS) * WAVE;
   static constexpr int VWMAX = 16 * TPG;    // value columns staged per chunk
-  static constexpr int KS = C * DK, QS = SUM ? 0 : C * DK, TS = C * C, AS = SUM ? 0 : C * C, VS = C * VWMAX;
+  static constexpr int KS = C * DK, QS = QA ? C * DK : 0, TS = C * C, AS = QA ? C * C : 0, VS = C * VWMAX;
   static constexpr int GS = 4 * C * 4 / ES;  // gc, exp(gc), exp(gc_last - gc), token output gates
   static constexpr int IN = KS + QS + TS + AS + VS + GS;   // one staged chunk (elements)
-  static constexpr int SYNC = SUM ? 0 : 16 / ES;              // loader rendezvous counter
+  static constexpr int SYNC = QA ? 16 / ES : 0;              // loader rendezvous counter
   static constexpr int NSTAGE = (2 * IN + SYNC) * ES <= LDS_BUDGET ? 2 : 1;
   static constexpr int ELEMS = NSTAGE * IN + SYNC;
   static_assert(ELEMS * ES <= LDS_BUDGET, "LDS budget");
 };
 
-template <typename E, int DK, int C, int CT, int NCW, bool SUM>
+template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV>
 __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdParams p) {
-  using Cfg = SegCfg<E, DK, C, CT, NCW, SUM>;
+  using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV>;
+  constexpr bool SUM = Cfg::SUM, QA = Cfg::QA, OUT = MODE == SEG_OUT, STATES = MODE == SEG_STATES;
+  static_assert(!REV || (sizeof(E) == 2 && MODE != SEG_OUT), "the reverse chain: bf16, summary or states");
+  // dO rows past the sequence must read as zeros (they meet A^T columns of padded tokens): the
+  // register-prefetched stages load through buffer ranges that give that, the one-stage copies
+  // repeat row 0 instead
+  static_assert(!REV || Cfg::NSTAGE == 2, "the reverse chain takes the double-buffered stage");
   using D = DOp<E>;
   constexpr int NB = C / 16;     // position blocks per chunk
   constexpr int NTS = DK / 16;   // state row tiles
@@ -181,9 +197,14 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       grp = i % G;
     }
   }
+  // the reverse chain numbers the segments from the end of the sequence (its segment 0 starts
+  // from the gradient of S_final) and walks each segment's chunks backwards
   const int seg = unit / BH, head = unit % BH;
   const int b = head / p.H, h = head % p.H;
-  const int n0 = seg * p.NS, n1 = min(p.NT, n0 + p.NS);  // chunks of this segment
+  const int fseg = REV ? p.P - 1 - seg : seg;              // the segment's place in the sequence
+  const int n0 = fseg * p.NS, n1 = min(p.NT, n0 + p.NS);  // chunks of this segment
+  const int cnt = max(0, n1 - n0);
+  auto chunk_at = [&](int i) { return REV ? n1 - 1 - i : n0 + i; };
   const int nh = p.nh;
   const int QR = C / nh;                                 // tokens per chunk
   // value columns staged for this group
@@ -193,7 +214,13 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
   // segment 0 of the summary needs only the value columns
   if (SUM && seg == 0 && vcnt == 0) return;
   unsigned* rdv = reinterpret_cast<unsigned*>(smem + Cfg::NSTAGE * Cfg::IN);
-  if constexpr (!SUM) {
+  if constexpr (QA) {
+    // The reverse chain contracts the staged Q and dO over all C rows, where only a chunk's
+    // QR token rows are ever loaded: with several sub-steps per token the rest must hold finite
+    // values (they meet zeros), so the stages start as zeros.
+    if (REV && nh > 1)
+      for (int i = tid; i < Cfg::NSTAGE * Cfg::IN * Cfg::ES / 16; i += Cfg::THREADS)
+        reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
     if (tid == 0) *rdv = 0u;
     barrier_lds();
   }
@@ -215,7 +242,8 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     pk.init(HDK, C, dw, lane);
     pq.init(HDK, QR, dw, lane);
     pt.init(C, C, dw, lane);
-    pv.init(HDV, VW > 0 ? C : 0, dw, lane, VW * (int)sizeof(E) / 16);
+    // values by position; the reverse chain's dO (in p.v) by token
+    pv.init(HDV, VW > 0 ? (REV ? QR : C) : 0, dw, lane, VW * (int)sizeof(E) / 16);
     pg.init(4, C / 4, dw, lane);
     // Issues the copies of chunk n into `stage`: gate prefix, keys and queries first, then T and
     // the values.  Returns how many of this wave's copies were issued after the first three
@@ -229,22 +257,23 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       const int qrows = (int)min((long)QR, (long)p.L - tok0);           // valid tokens
       const E* kc = kg + ((long)b * p.Lx + P0) * HDK + (long)h * DK;
       const E* qc = qg + ((long)b * p.L + tok0) * HDK + (long)h * DK;
-      const E* vc = vg + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0;
+      const E* vc = vg + (REV ? ((long)b * p.L + tok0) : ((long)b * p.Lx + P0)) * HDV + (long)h * p.DV + 16 * vt0;
       E* sv = st + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS;
       pg.issue(reinterpret_cast<float*>(sv + Cfg::VS), p.gc + ((long)head * p.NT + n) * C, dw);
-      if (krows == C && (SUM || qrows == QR)) {
+      if (krows == C && (!QA || qrows == QR)) {
         pk.issue(st, kc, dw);
-        if (!SUM) pq.issue(st + Cfg::KS, qc, dw);
+        if (QA) pq.issue(st + Cfg::KS, qc, dw);
         pt.issue(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, dw);
         if (VW > 0) pv.issue(sv, vc, dw);
         return pt.n + (VW > 0 ? pv.n : 0);
       }
       copy_rows_to_lds<E, DK>(st, kc, HDK, C, krows, dw, SEG_LOADERS, lane);
-      if (!SUM) copy_rows_to_lds<E, DK>(st + Cfg::KS, qc, HDK, QR, qrows, dw, SEG_LOADERS, lane);
+      if (QA) copy_rows_to_lds<E, DK>(st + Cfg::KS, qc, HDK, QR, qrows, dw, SEG_LOADERS, lane);
       pt.issue(st + Cfg::KS + Cfg::QS, Tg + ((long)head * p.NT + n) * C * C, dw);
       // the group's value columns, at the fixed row pitch VWMAX (columns past them repeat its first)
       if (VW > 0)
-        copy_rows_to_lds<E, Cfg::VWMAX>(sv, vc, HDV, C, krows, dw, SEG_LOADERS, lane, VW * (int)sizeof(E) / 16);
+        copy_rows_to_lds<E, Cfg::VWMAX>(sv, vc, HDV, REV ? QR : C, REV ? qrows : krows, dw, SEG_LOADERS, lane,
+                                         VW * (int)sizeof(E) / 16);
       return 0;
     };
     // exp(gc), exp(gc_last - gc) and, per token row, scale * exp(gc) at the token's last
@@ -265,9 +294,11 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     // Every block is formed, those past the causal reach (or past the tokens: Q rows there are
     // stale, and the select drops whatever they give) as zeros, so each wave's blocks are
     // independent straight-line work.
+    // The reverse chain takes A^T instead (rows: positions, columns: tokens), formed from the
+    // product Q K^T: lane (g, m) gets A[16 t + 4 g .. + 3][16 j + m], a row run of A^T.
     unsigned arrivals = 0;
     auto build_a = [&](int stage) {
-      if constexpr (!SUM) {
+      if constexpr (QA) {
         arrivals += SEG_LOADERS;
         loader_rendezvous(rdv, arrivals, lane);
         E* st = smem + stage * Cfg::IN;
@@ -281,23 +312,37 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
           const int blk = dw + SEG_LOADERS * u;
           d[u] = floatx4{0.f, 0.f, 0.f, 0.f};
           if (NBLK % SEG_LOADERS == 0 || blk < NBLK)
-            d[u] = mma_tile<E>(d[u], Kt, 16 * (blk % NB), Qt, 16 * (blk / NB), DK, lane);
+            d[u] = REV ? mma_tile<E>(d[u], Qt, 16 * (blk / NB), Kt, 16 * (blk % NB), DK, lane)
+                       : mma_tile<E>(d[u], Kt, 16 * (blk % NB), Qt, 16 * (blk / NB), DK, lane);
         }
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
           const int blk = dw + SEG_LOADERS * u;
           if (NBLK % SEG_LOADERS != 0 && blk >= NBLK) continue;
           const int t = blk / NB, j = blk % NB;
-          const int trow = 16 * t + m, ptok = min(trow, QR - 1) * nh + nh - 1;
-          const float gp = gcs[ptok];
-          float a[4];
+          if constexpr (REV) {
+            const int pc = 16 * j + m;  // the lane's position; tokens 16 t + 4 g4 + r
+            const float gj = gcs[pc];
+            float a[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int pc = 16 * j + 4 * g4 + r;
-            const float x = p.scale * d[u][r] * gate_exp(gp - gcs[pc]);
-            a[r] = (trow < QR && pc <= ptok) ? x : 0.f;
+            for (int r = 0; r < 4; ++r) {
+              const int trow = 16 * t + 4 * g4 + r, ptok = min(trow, QR - 1) * nh + nh - 1;
+              const float x = p.scale * d[u][r] * gate_exp(gcs[ptok] - gj);
+              a[r] = (trow < QR && pc <= ptok) ? x : 0.f;
+            }
+            store4<E>(At.at(pc, 16 * t + 4 * g4), a[0], a[1], a[2], a[3]);
+          } else {
+            const int trow = 16 * t + m, ptok = min(trow, QR - 1) * nh + nh - 1;
+            const float gp = gcs[ptok];
+            float a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int pc = 16 * j + 4 * g4 + r;
+              const float x = p.scale * d[u][r] * gate_exp(gp - gcs[pc]);
+              a[r] = (trow < QR && pc <= ptok) ? x : 0.f;
+            }
+            store4<E>(At.at(trow, 16 * j + 4 * g4), a[0], a[1], a[2], a[3]);
           }
-          store4<E>(At.at(trow, 16 * j + 4 * g4), a[0], a[1], a[2], a[3]);
         }
       }
     };
@@ -305,7 +350,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     // copies; everything has landed when the function returns
     auto stage_chunk = [&](int n, int stage) {
       const int late = issue(n, stage);
-      if constexpr (SUM) {
+      if constexpr (!QA) {
         wait_vmem();
         exps(stage);
       } else {
@@ -320,7 +365,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       // chunk n+2 are loaded while chunk n is processed and written to LDS at the start of
       // chunk n+1, so neither the gate tables nor A ever wait for HBM.  Loads go through
       // buffer resources over the chunk's valid rows (rows past the sequence read 0).
-      u32x4 rk[decltype(pk)::NS], rq[SUM ? 1 : decltype(pq)::NS], rt[decltype(pt)::NS], rv[decltype(pv)::NS],
+      u32x4 rk[decltype(pk)::NS], rq[QA ? decltype(pq)::NS : 1], rt[decltype(pt)::NS], rv[decltype(pv)::NS],
           rg[decltype(pg)::NS];
       auto load = [&](int n) {
         const long P0 = (long)n * C;
@@ -329,8 +374,11 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
         const int qrows = (int)min((long)QR, (long)p.L - tok0);
         const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(const_cast<E*>(kg) + ((long)b * p.Lx + P0) * HDK + (long)h * DK,
                                                       krows * HDK * (int)sizeof(E));
-        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(
-            const_cast<E*>(vg) + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0, krows * HDV * (int)sizeof(E));
+        const __amdgpu_buffer_rsrc_t vr =
+            REV ? buffer_rsrc(const_cast<E*>(vg) + ((long)b * p.L + tok0) * HDV + (long)h * p.DV + 16 * vt0,
+                              qrows * HDV * (int)sizeof(E))
+                : buffer_rsrc(const_cast<E*>(vg) + ((long)b * p.Lx + P0) * HDV + (long)h * p.DV + 16 * vt0,
+                              krows * HDV * (int)sizeof(E));
         const __amdgpu_buffer_rsrc_t tr =
             buffer_rsrc(const_cast<E*>(Tg) + ((long)head * p.NT + n) * C * C, C * C * (int)sizeof(E));
         const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(p.gc + ((long)head * p.NT + n) * C, C * 4);
@@ -340,7 +388,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 #pragma unroll
         for (int s = 0; s < decltype(pk)::NS; ++s)
           if (s < pk.n && pk.off[s] != ~0u) rk[s] = buffer_load16(kr, (int)pk.off[s]);
-        if constexpr (!SUM) {
+        if constexpr (QA) {
           const __amdgpu_buffer_rsrc_t qr =
               buffer_rsrc(const_cast<E*>(qg) + ((long)b * p.L + tok0) * HDK + (long)h * DK, qrows * HDK * (int)sizeof(E));
 #pragma unroll
@@ -368,7 +416,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 #pragma unroll
         for (int s = 0; s < decltype(pk)::NS; ++s)
           if (s < pk.n && pk.off[s] != ~0u) put(st, s, rk[s]);
-        if constexpr (!SUM) {
+        if constexpr (QA) {
 #pragma unroll
           for (int s = 0; s < decltype(pq)::NS; ++s)
             if (s < pq.n && pq.off[s] != ~0u) put(st + Cfg::KS, s, rq[s]);
@@ -380,27 +428,28 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
         for (int s = 0; s < decltype(pv)::NS; ++s)
           if (s < pv.n && pv.off[s] != ~0u) put(sv, s, rv[s]);
       };
-      if (n0 < n1) {
-        load(n0);
+      // (i counts the segment's chunks in processing order)
+      if (cnt > 0) {
+        load(chunk_at(0));
         store(0);
         exps(0);
         build_a(0);
-        if (n0 + 1 < n1) load(n0 + 1);
+        if (cnt > 1) load(chunk_at(1));
       }
       barrier_lds();  // first chunk staged
-      for (int n = n0; n < n1; ++n) {
-        if (n + 1 < n1) {
-          const int stage = (n + 1 - n0) & 1;
-          store(stage);  // chunk n+1, loaded during chunk n-1
-          if (n + 2 < n1) load(n + 2);
+      for (int i = 0; i < cnt; ++i) {
+        if (i + 1 < cnt) {
+          const int stage = (i + 1) & 1;
+          store(stage);  // chunk i+1, loaded during chunk i-1
+          if (i + 2 < cnt) load(chunk_at(i + 2));
           exps(stage);
           build_a(stage);
         }
-        barrier_lds();  // chunk n done, chunk n+1 staged (the loads in flight are not waited for)
+        barrier_lds();  // chunk i done, chunk i+1 staged (the loads in flight are not waited for)
       }
     } else {
-      for (int n = n0; n < n1; ++n) {
-        stage_chunk(n, 0);
+      for (int i = 0; i < cnt; ++i) {
+        stage_chunk(chunk_at(i), 0);
         barrier_all();  // chunk n staged
         barrier_all();  // chunk n done
       }
@@ -471,9 +520,10 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 
   E* Og = reinterpret_cast<E*>(p.O);
 
-  for (int n = n0; n < n1; ++n) {
+  for (int i = 0; i < cnt; ++i) {
+    const int n = chunk_at(i);
     if constexpr (Cfg::NSTAGE == 1) barrier_lds();
-    const E* Kp = smem + ((Cfg::NSTAGE == 2) ? ((n - n0) & 1) : 0) * Cfg::IN;
+    const E* Kp = smem + ((Cfg::NSTAGE == 2) ? (i & 1) : 0) * Cfg::IN;
     const E* Qp = Kp + Cfg::KS;
     const E* Tp = Qp + Cfg::QS;
     const E* Ap = Tp + Cfg::TS;
@@ -487,7 +537,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     int lnL = lane;
     asm volatile("" : "+v"(lnL));
     const int mL = lnL & 15, gL = lnL >> 4;
-    int offK[NTS], offKT[NTS], offT[NB], offV[CT];
+    int offK[NTS], offKT[NTS], offT[NB], offV[CT], offTT[NB];
 #pragma unroll
     for (int t = 0; t < NTS; ++t) {
       if constexpr (DP) {
@@ -500,7 +550,11 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) offT[kb] = swz(mL, 16 * kb + 4 * gL, C, MC);  // T, A rows
+    for (int kb = 0; kb < NB; ++kb) {
+      offT[kb] = swz(mL, 16 * kb + 4 * gL, C, MC);  // T, A rows
+      // T^T transpose reads (reverse chain): column block kb of T as rows, at row block 0
+      offTT[kb] = swz(4 * gL + (mL >> 2), 16 * kb + 4 * (mL & 3), C, MC);
+    }
 #pragma unroll
     for (int c = 0; c < CT; ++c)   // V transpose reads (D layout of the tile's 16 columns)
       offV[c] = swz(4 * gL + (mL >> 2), 16 * (isv[c] ? tile[c] - vt0 : 0) + 4 * (mL & 3), Cfg::VWMAX, MV);
@@ -511,6 +565,27 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int t = 0; t < NTS; ++t) Sb[c][t] = D::cvt(S[c][t]);
+
+    // ---- the chunk's start state as the chain holds it (rounded to the element type), into
+    // Sn [B*H, NT, d_v, d_k]: lane (g, m) holds 4 consecutive d_k rows of column 16 tile + m.  The
+    // reverse chain's gradients also leave their rounding residual in Snl: the gradient of the
+    // final state enters the last chunk unattenuated and can dwarf the rest of its products.
+    if constexpr (STATES) {
+      const long cofs = ((long)head * p.NT + n) * p.DV * DK;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        if (isv[c])
+#pragma unroll
+          for (int t = 0; t < NTS; ++t) {
+            const long e = cofs + (long)(16 * tile[c] + m) * DK + dkrow(t, 4 * g4);
+            *reinterpret_cast<typename D::B*>(reinterpret_cast<E*>(p.Sn) + e) = Sb[c][t];
+            if constexpr (REV) {
+              const bf16x4 hi = Sb[c][t];
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(p.Snl) + e) =
+                  DOp<bf16>::cvt(S[c][t] - floatx4{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]});
+            }
+          }
+    }
 
     // ---- X = K S, contracting over d_k
     constexpr int TSTEP = (D::PAIRS && NTS % 2 == 0) ? 2 : 1;
@@ -534,10 +609,42 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
         }
       }
 
-    // ---- Y = V - gamma X (transition columns see V = 0)
+    // ---- Y = V - gamma X (transition columns see V = 0); the reverse chain:
+    // dV~ = w X + A^T dO (dO tiles read once, D layout, zero on transition columns)
     typename D::B Yb[CT][NB];
+    [[maybe_unused]] typename D::B Ob[CT][NB];
+    if constexpr (REV) {
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const bf16x4 r = read_tr4(reinterpret_cast<const bf16*>(Vp) + 16 * kb * Cfg::VWMAX + offV[c]);
+          u32x2 u = __builtin_bit_cast(u32x2, r);
+          u[0] = isv[c] ? u[0] : 0u;
+          u[1] = isv[c] ? u[1] : 0u;
+          Ob[c][kb] = __builtin_bit_cast(bf16x4, u);
+        }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        floatx4 acc[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // A^T is zero past each position's causal reach; every token block is taken, so the
+        // chunk body stays straight-line
+#pragma unroll
+        for (int kb = 0; kb < NB; kb += 2) {
+          const typename D::A a0 = D::row4(Ap + 16 * bb * C + offT[kb]);
+          const typename D::A a1 = D::row4(Ap + 16 * bb * C + offT[kb + 1]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) acc[c] = D::mma2(a0, a1, Ob[c][kb], Ob[c][kb + 1], acc[c]);
+        }
+        const floatx4 ed4 = *reinterpret_cast<const floatx4*>(edp + 16 * bb + 4 * g4);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) Yb[c][bb] = D::cvt(acc[c] + ed4 * X[c][bb]);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB && !REV; ++bb) {
       const floatx4 eg4 = *reinterpret_cast<const floatx4*>(egp + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
@@ -565,10 +672,29 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       }
     }
 
-    // ---- V~ = T Y (T lower triangular; a zero block above the diagonal may pair in)
+    // ---- V~ = T Y (T lower triangular; a zero block above the diagonal may pair in); the
+    // reverse chain: dY = T^T dV~ (T^T upper triangular), kept as -gamma dY for the update
     typename D::B Vb[CT][NB], DVb[CT][NB];
+    if constexpr (REV) {
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
+      for (int bb = 0; bb < NB; ++bb) {
+        floatx4 vt[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) vt[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = bb & ~1; kb < NB; kb += 2) {
+          const bf16x4 a0 = read_tr4(reinterpret_cast<const bf16*>(Tp) + 16 * kb * C + offTT[bb]);
+          const bf16x4 a1 = read_tr4(reinterpret_cast<const bf16*>(Tp) + 16 * (kb + 1) * C + offTT[bb]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) vt[c] = D::mma2(a0, a1, Yb[c][kb], Yb[c][kb + 1], vt[c]);
+        }
+        const floatx4 eg4 = *reinterpret_cast<const floatx4*>(egp + 16 * bb + 4 * g4);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) DVb[c][bb] = D::cvt(-eg4 * vt[c]);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB && !REV; ++bb) {
       floatx4 vt[CT];
 #pragma unroll
       for (int c = 0; c < CT; ++c) vt[c] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -605,7 +731,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     // computed (with several sub-steps per token the blocks past the chunk's tokens read stale
     // but in-bounds LDS) and the stores are masked by the buffer range check: no branch splits
     // the chunk body.
-    if constexpr (!SUM) {
+    if constexpr (OUT) {
       constexpr int KSTEPA = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
       // Output addresses depend only on the lane and the chunk; hiding the lane index keeps the
       // optimiser from hoisting one register per row block and tile out of the chunk loop.
@@ -666,10 +792,24 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       }
     }
 
-    // ---- S <- gamma_C S + K^T (gamma_C / gamma V~)
+    // ---- S <- gamma_C S + K^T (gamma_C / gamma V~); the reverse chain:
+    // G <- gamma_C G + K^T (-gamma dY) + Q^T (gamma_q dO), gamma_q = scale exp(gc) at each token's
+    // last sub-step (0 past the chunk's tokens)
     {
       const float gC = egp[C - 1];
       constexpr int BSTEP = (D::PAIRS && NB % 2 == 0) ? 2 : 1;
+      [[maybe_unused]] typename D::B QOb[CT][NB];
+      if constexpr (REV) {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          const floatx4 eq4 = *reinterpret_cast<const floatx4*>(eqp + 16 * kb + 4 * g4);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            const bf16x4 o = Ob[c][kb];
+            QOb[c][kb] = D::cvt(eq4 * floatx4{(float)o[0], (float)o[1], (float)o[2], (float)o[3]});
+          }
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NTS; ++t) {
 #pragma unroll
@@ -691,6 +831,15 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
           } else {
 #pragma unroll
             for (int c = 0; c < CT; ++c) S[c][t] = D::mma1(a0, DVb[c][bb], S[c][t]);
+          }
+        }
+        if constexpr (REV) {
+#pragma unroll
+          for (int kb = 0; kb < NB; kb += 2) {
+            const bf16x4 a0 = read_tr4(reinterpret_cast<const bf16*>(Qp) + 16 * kb * DK + offKT[t]);
+            const bf16x4 a1 = read_tr4(reinterpret_cast<const bf16*>(Qp) + 16 * (kb + 1) * DK + offKT[t]);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) S[c][t] = D::mma2(a0, a1, QOb[c][kb], QOb[c][kb + 1], S[c][t]);
           }
         }
       }
@@ -856,16 +1005,16 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <typename E, int DK, int C, int CT, int NCW, bool SUM>
+template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV = false>
 static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
-  using Cfg = SegCfg<E, DK, C, CT, NCW, SUM>;
+  using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV>;
   constexpr int TPG = Cfg::TPG;
-  const int NCT = p.DV / 16, MCT = SUM ? DK / 16 : 0;
+  const int NCT = p.DV / 16, MCT = Cfg::SUM ? DK / 16 : 0;
   const int G = (NCT + MCT + TPG - 1) / TPG;
-  const int nseg = SUM ? p.P - 1 : p.P;
+  const int nseg = Cfg::SUM ? p.P - 1 : p.P;
   const long blocks = (long)nseg * p.B * p.H * G;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, NCW, SUM>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0, st, p);
+  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, NCW, MODE, REV>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0, st, p);
   return hipGetLastError();
 }
 
@@ -883,7 +1032,7 @@ template <typename E, int DK, int C>
 static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
   switch (phase) {
     case SCAN_SUMMARY:
-      return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, sum_ncw<E>(), true>(p, st) : hipSuccess;
+      return p.P > 1 ? launch_seg<E, DK, C, SUM_CT, sum_ncw<E>(), SEG_SUM>(p, st) : hipSuccess;
     case SCAN_COMBINE:
       if (p.P <= 1 || p.B * p.H == 0) return hipSuccess;
     {
@@ -895,8 +1044,8 @@ static hipError_t scan_phase(const FwdParams& p, int phase, hipStream_t st) {
       return hipGetLastError();
     }
     case SCAN_OUTPUTS:
-      return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, false>(p, st)
-                                  : launch_seg<E, DK, C, 2, 4, false>(p, st);
+      return p.DV / 16 <= OUT_NCW ? launch_seg<E, DK, C, 1, OUT_NCW, SEG_OUT>(p, st)
+                                  : launch_seg<E, DK, C, 2, 4, SEG_OUT>(p, st);
     default:
       return hipErrorInvalidValue;
   }
@@ -927,6 +1076,34 @@ static hipError_t phase_by_dk(const FwdParams& p, int phase, hipStream_t st) {
 hipError_t launch_scan_phase(const FwdParams& p, bool bf16_in, int phase, hipStream_t st) {
   if (phase == SCAN_SUMMARY && scan_summary_fast_applies(p, bf16_in)) return launch_scan_summary_fast(p, st);
   return bf16_in ? phase_by_dk<bf16>(p, phase, st) : phase_by_dk<float>(p, phase, st);
+}
+
+// The backward pass's two scans over chunk states, for bf16 inputs with d_k = d_v = 128 and
+// chunk 64 (bwd_scans_apply): the forward chain writing each chunk's start state, and the
+// adjoint chain (summary, combine, chain) writing each chunk's end-state gradient.  Both use
+// 4 chain wavefronts of 2 column tiles; the reverse summary covers the value and transition
+// columns in two workgroups per segment.
+bool bwd_scans_apply(const FwdParams& p, bool bf16_in) {
+  return bf16_in && p.DK == 128 && p.DV == 128 && p.C == 64;
+}
+
+hipError_t launch_scan_states(const FwdParams& p, hipStream_t st) {
+  if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
+  return launch_seg<bf16, 128, 64, 2, 4, SEG_STATES>(p, st);
+}
+
+hipError_t launch_rev_scan(const FwdParams& p, int phase, hipStream_t st) {
+  if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
+  switch (phase) {
+    case SCAN_SUMMARY:
+      return p.P > 1 ? launch_seg<bf16, 128, 64, 2, 4, SEG_SUM, true>(p, st) : hipSuccess;
+    case SCAN_COMBINE:
+      return scan_phase<bf16, 128, 64>(p, SCAN_COMBINE, st);
+    case SCAN_OUTPUTS:
+      return launch_seg<bf16, 128, 64, 2, 4, SEG_STATES, true>(p, st);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace delta

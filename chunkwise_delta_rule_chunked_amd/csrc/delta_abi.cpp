@@ -368,11 +368,19 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
 }
 
 namespace {
-// Workspace of the backward pass: T (float32), the gate prefix, Q K^T * Gam (float32, C x C
-// per chunk), and per chunk the start state and the end-of-chunk state gradient.
+// Workspace of the backward pass.  Where the state scans apply (bf16, d_k = d_v = 128, chunk 64):
+// T (bf16), the gate prefix, N = (I + A)^-1 (float32), the segment summaries and start states,
+// and per chunk the start state (bf16) and the end-of-chunk state gradient (bf16 and its bf16
+// rounding residual).  Otherwise:
+// T (float32), the gate prefix, Q K^T * Gam (float32, C x C per chunk) and the two per-chunk
+// state arrays in float32.
 size_t states_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.DK * p.DV * 4; }
-size_t bwd_workspace(const FwdParams& p) {
-  return 3 * align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
+bool bwd_scans(const FwdParams& p, bool bf) { return p.NT > 0 && delta::bwd_scans_apply(p, bf); }
+size_t bwd_workspace(const FwdParams& p, bool bf) {
+  if (bwd_scans(p, bf))
+    return align_up(t_bytes(p, 2)) + align_up(gc_bytes(p)) + align_up(t_bytes(p, 4)) + align_up(sm_bytes(p)) +
+           align_up(sst_bytes(p)) + 3 * align_up(states_bytes(p) / 2);
+  return 2 * align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
 }
 }  // namespace
 
@@ -381,7 +389,7 @@ int delta_bwd_workspace_bytes(const delta_shape* s, size_t* bytes) {
   if (rc) return rc;
   if ((rc = check_chunk(s))) return rc;
   if (!bytes) return DELTA_ERR_NULL_ARG;
-  *bytes = bwd_workspace(make_params(s));
+  *bytes = bwd_workspace(make_params(s), s->dtype == DELTA_BF16);
   return DELTA_OK;
 }
 
@@ -398,7 +406,7 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   const size_t nq = (size_t)f.B * f.L * f.H, nx = (size_t)f.B * f.Lx * f.H, nS = (size_t)f.B * f.H * f.DK * f.DV;
   const size_t sz_q = nq * f.DK * es, sz_k = nx * f.DK * es, sz_v = nx * f.DV * es, sz_o = nq * f.DV * es;
   if (nx > 0 && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta)) return DELTA_ERR_NULL_ARG;
-  const size_t need = bwd_workspace(f);
+  const size_t need = bwd_workspace(f, s->dtype == DELTA_BF16);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DELTA_ERR_WORKSPACE;
   const void* ptrs[] = {q, k, v, S0, dO, dS_final, dq, dk, dv, dS0, workspace};
   for (const void* ptr : ptrs)
@@ -428,6 +436,48 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   if ((rc = launch_guard())) return rc;
   // the check's flag words take the start of the T region, which the first launch rewrites
   if (validate_on() && f.NT > 0 && (rc = validate_device(beta, nx, g_log, g_log ? nq : 0, ws, st))) return rc;
+  if (bwd_scans(f, bf)) {
+    // T (bf16), the gate prefix and N; the chunk start states by the forward summary, combine and
+    // a chain that stores them; the end-state gradients (and dS0) by the reverse scan; then the
+    // per-chunk gradients (and dv) on MFMA
+    FwdParams fs = f;
+    fs.q = q, fs.k = k, fs.v = v, fs.beta = beta, fs.g_log = g_log, fs.S0 = S0;
+    size_t off = 0;
+    fs.T = ws;
+    off += align_up(t_bytes(f, 2));
+    fs.gc = reinterpret_cast<float*>(ws + off);
+    off += align_up(gc_bytes(f));
+    fs.N = reinterpret_cast<float*>(ws + off);
+    off += align_up(t_bytes(f, 4));
+    fs.SM = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
+    off += align_up(sm_bytes(f));
+    fs.Sst = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
+    off += align_up(sst_bytes(f));
+    void* Sn = ws + off;
+    void* Gn = ws + off + align_up(states_bytes(f) / 2);
+    void* Gnl = ws + off + 2 * align_up(states_bytes(f) / 2);
+    fs.Sn = Sn;
+    fs.Snl = nullptr;
+    if ((rc = hip_status(delta::launch_intra_chunk(fs, bf, false, st)))) return rc;
+    fs.N = nullptr;
+    if ((rc = hip_status(delta::launch_scan_phase(fs, bf, delta::SCAN_SUMMARY, st)))) return rc;
+    if ((rc = hip_status(delta::launch_scan_phase(fs, bf, delta::SCAN_COMBINE, st)))) return rc;
+    if ((rc = hip_status(delta::launch_scan_states(fs, st)))) return rc;
+    FwdParams fr = fs;  // the adjoint chain: dO for the values, dS_final in, dS0 out
+    fr.v = dO, fr.S0 = dS_final, fr.S_final = dS0, fr.Sn = Gn, fr.Snl = Gnl;
+    for (int ph : {delta::SCAN_SUMMARY, delta::SCAN_COMBINE, delta::SCAN_OUTPUTS})
+      if ((rc = hip_status(delta::launch_rev_scan(fr, ph, st)))) return rc;
+    BwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.B = f.B, p.L = f.L, p.H = f.H, p.DK = f.DK, p.DV = f.DV, p.nh = f.nh, p.C = f.C, p.Lx = f.Lx, p.NT = f.NT;
+    p.scale = f.scale;
+    p.q = q, p.k = k, p.v = v, p.beta = beta, p.S0 = S0, p.dO = dO, p.dS_final = dS_final;
+    p.dq = dq, p.dk = dk, p.dv = dv, p.dbeta = dbeta, p.dg_log = dg_log, p.dS0 = dS0;
+    p.gc = fs.gc;
+    p.N = reinterpret_cast<const float*>(ws + align_up(t_bytes(f, 2)) + align_up(gc_bytes(f)));
+    p.Snt = Sn, p.Gnt = Gn, p.Gntl = Gnl;
+    return hip_status(delta::launch_bwd_chunk_mfma(p, st));
+  }
   FwdParams fi = f;  // the intra-chunk launch: T (float32) and the gate prefix
   fi.k = k;
   fi.beta = beta;
@@ -435,6 +485,7 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   fi.T = ws;
   fi.gc = reinterpret_cast<float*>(ws + align_up(t_bytes(f, 4)));
   BwdParams p;
+  memset(&p, 0, sizeof(p));
   p.B = f.B, p.L = f.L, p.H = f.H, p.DK = f.DK, p.DV = f.DV, p.nh = f.nh, p.C = f.C, p.Lx = f.Lx, p.NT = f.NT;
   p.scale = f.scale;
   p.q = q, p.k = k, p.v = v, p.beta = beta, p.S0 = S0, p.dO = dO, p.dS_final = dS_final;
@@ -446,10 +497,6 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   off += align_up(t_bytes(f, 4));
   p.Sn = reinterpret_cast<float*>(ws + off);
   p.Gn = reinterpret_cast<float*>(ws + off + align_up(states_bytes(f)));
-  off += 2 * align_up(states_bytes(f));
-  fi.N = reinterpret_cast<float*>(ws + off);  // N = (I + A)^-1, for the MFMA per-chunk kernel
-  p.N = fi.N;
-  const bool mfma_chunk = delta::bwd_chunk_mfma_applies(p, bf);
   if (f.NT > 0) {
     if ((rc = hip_status(delta::launch_intra_chunk(fi, bf, true, st)))) return rc;
     if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 3, st)))) return rc;
@@ -457,8 +504,7 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
   }
   // the reverse pass also writes dS0, so it runs when there are no chunks too
   if ((rc = hip_status(delta::launch_bwd_phase(p, bf, 1, st)))) return rc;
-  if (f.NT > 0)
-    return hip_status(mfma_chunk ? delta::launch_bwd_chunk_mfma(p, st) : delta::launch_bwd_phase(p, bf, 2, st));
+  if (f.NT > 0) return hip_status(delta::launch_bwd_phase(p, bf, 2, st));
   return DELTA_OK;
 }
 

@@ -30,6 +30,11 @@ struct FwdParams {
   // mfrag_index (common.h)
   float* SM;
   float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
+  // backward scans only: [B*H, NT, DV, DK] in the element type of the inputs, each chunk's start
+  // state (forward chain) or end-state gradient (reverse chain), transposed; the reverse chain
+  // also stores the rounding residual of each gradient (G - Sn, rounded) at Snl
+  void* Sn;
+  void* Snl;
 };
 
 struct DecodeParams {
@@ -82,6 +87,11 @@ struct BwdParams {
   float* Sn;              // [B*H, NT, DK, DV] start state of each chunk
   float* Gn;              // [B*H, NT, DK, DV] state gradient at the end of each chunk
   const float* N;         // [B*H, NT, C, C] (I + A)^-1 float32 (the MFMA per-chunk kernel)
+  // the MFMA per-chunk kernel: Sn and Gn as bf16 [B*H, NT, DV, DK] (transposed), from the scans,
+  // and Gn's rounding residual (G' = Gnt + Gntl to about 16 bits)
+  const void* Snt;
+  const void* Gnt;
+  const void* Gntl;
 };
 
 // The layer steps around the mixer (layer.hip).
@@ -109,6 +119,14 @@ hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream
 // Summary launch for bf16 inputs, d_k = d_v = 128, chunk 64 (scan_summary.hip).
 bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
+// The backward pass's state scans on the inter-chunk machinery, for bf16 inputs with
+// d_k = d_v = 128 and chunk 64 (chunk_scan.hip).  After the forward summary and combine,
+// launch_scan_states runs the forward chain writing each chunk's start state to p.Sn.  The
+// reverse scan takes p.v = dO, p.S0 = dS_final, p.S_final = dS0, p.Sn = end-state gradients, and
+// runs the same three phases (the combine unchanged) with segments numbered from the end.
+bool bwd_scans_apply(const FwdParams& p, bool bf16);
+hipError_t launch_scan_states(const FwdParams& p, hipStream_t st);
+hipError_t launch_rev_scan(const FwdParams& p, int phase, hipStream_t st);
 // Backward launches (backward.hip), in order after launch_intra_chunk with float T:
 // 3 Q K^T * Gam per chunk, 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0),
 // 2 per-chunk gradients.

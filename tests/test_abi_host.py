@@ -186,11 +186,26 @@ def bwd_ws(sh):
 
 
 def test_bwd_workspace_bytes(lib):
+    """Vector-ALU scans: T and Q K^T * Gam (float32, C x C per chunk), the gate prefix and two
+    float32 states per chunk.  State scans on the inter-chunk machinery (bf16, d_k = d_v = 128,
+    chunk 64): T (bf16), the gate prefix, N (float32), the segment summaries and start states,
+    and per chunk the start state (bf16) and the end-state gradient (bf16 high and low parts)."""
     up = lambda x: (x + 255) // 256 * 256
-    for B, H, L, dk, dv, C, nh in [(2, 3, 100, 64, 32, 32, 1), (2, 16, 8192, 128, 128, 64, 1), (1, 2, 50, 16, 256, 48, 3)]:
+    for B, H, L, dk, dv, C, nh, dt in [(2, 3, 100, 64, 32, 32, 1, D.BF16), (2, 16, 8192, 128, 128, 64, 1, D.F32),
+                                       (1, 2, 50, 16, 256, 48, 3, D.BF16), (2, 16, 8192, 128, 128, 64, 1, D.BF16),
+                                       (1, 2, 300, 128, 128, 64, 2, D.BF16), (64, 16, 100, 128, 128, 64, 1, D.BF16)]:
         NT = (L * nh + C - 1) // C
-        rc, n = bwd_ws(shape(B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, n_h=nh))
-        assert rc == 0 and n == 3 * up(B * H * NT * C * C * 4) + up(B * H * NT * C * 4) + 2 * up(B * H * NT * dk * dv * 4)
+        rc, n = bwd_ws(shape(B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, n_h=nh, dtype=dt))
+        states = B * H * NT * dk * dv * 4
+        if dt == D.BF16 and dk == dv == 128 and C == 64:
+            P, _ = segments(B, H, dv, NT)
+            sm = B * H * P * dk * (dv + dk) * 4 if P > 1 else 0
+            sst = B * H * P * dk * dv * 4 if P > 1 else 0
+            want = (up(B * H * NT * C * C * 2) + up(B * H * NT * C * 4) + up(B * H * NT * C * C * 4) + up(sm) + up(sst)
+                    + 3 * up(states // 2))
+        else:
+            want = 2 * up(B * H * NT * C * C * 4) + up(B * H * NT * C * 4) + 2 * up(states)
+        assert rc == 0 and n == want, (B, H, L, dk, dv, C, nh, dt)
     assert bwd_ws(shape(L=0)) == (0, 0)
     assert bwd_ws(shape(dk=48))[0] == -3
 

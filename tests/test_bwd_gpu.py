@@ -42,6 +42,11 @@ CASES = [
     wl("bwd_bf16_gdp2_d128", B=1, H=2, L=300, dk=128, dv=128, chunk=64, n_h=2, gate="weak",
        key="silu_l2n", beta="2sigmoid"),
     wl("bwd_bf16_one_chunk", B=1, H=1, L=5, dk=64, dv=32, chunk=64, gate="cfg3"),
+    # the state scans' segment split: none (256 heads fill the GPU), one chunk per segment over
+    # 41 chunks (40 combine steps, a ragged last chunk), ungated with a start state
+    wl("bwd_bf16_d128_unsplit", B=2, H=128, L=70, dk=128, dv=128, chunk=64, gate="cfg3", s0=0.1),
+    wl("bwd_bf16_d128_41_segments", B=1, H=1, L=64 * 40 + 17, dk=128, dv=128, chunk=64, gate="weak", s0=0.1),
+    wl("bwd_bf16_d128_ungated", B=1, H=3, L=200, dk=128, dv=128, chunk=64, s0=0.1),
 ]
 
 
