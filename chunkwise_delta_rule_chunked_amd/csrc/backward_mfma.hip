@@ -94,7 +94,10 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, m = lane & 15;
   const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
+  // the chunk starts at a token boundary (C is a multiple of n_h): row r is sub-step r % n_h of
+  // the chunk's token r / n_h, token index tok0 + r / n_h
   const int nh = p.nh;
+  const long tok0 = (long)n * (C / nh);
   const long P0 = (long)n * C, chunk = (long)bh * p.NT + n;
   const int valid = (int)min((long)C, (long)p.Lx - P0);
   const long HD = (long)p.H * DK;  // d_k == d_v: one row stride for all four tensors
@@ -120,8 +123,9 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
-      const bool ok = r < valid, last = ok && (P0 + r) % nh == nh - 1;
-      const long tok = (P0 + r) / nh;
+      const int rt = r / nh;
+      const bool ok = r < valid, last = ok && r - rt * nh == nh - 1;
+      const long tok = tok0 + rt;
       rk[u] = ok ? *reinterpret_cast<const u32x4*>(kb + r * HD + c) : u32x4{0, 0, 0, 0};
       rv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + r * HD + c) : u32x4{0, 0, 0, 0};
       rq[u] = last ? *reinterpret_cast<const u32x4*>(qb + tok * HD + c) : u32x4{0, 0, 0, 0};
@@ -455,18 +459,19 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
     *Gst.at(i, j) = (bf16)(R0[i][j] + R0[j][i]);
   }
   __syncthreads();
-  if (tid == 0 && p.dg_log) {
-    const float gC = s.gc[C - 1];
-    float tot = 0.f;
-    for (int i = 0; i < C; ++i) tot += s.w[i] * s.dw[i];
-    for (int o = 0; o < NW; ++o) tot += expf(gC) * s.sgs[o];
-    // reverse cumulative sum over the chunk; the last position also collects the total above
-    float run = tot;
-    for (int i = C - 1; i >= 0; --i) {
-      run += s.dgc[i];
-      const long pos = P0 + i;
-      if (i < valid && pos % nh == 0) p.dg_log[(b * (long)p.L + pos / nh) * p.H + h] = run;
+  if (wave == 0 && p.dg_log) {
+    // lane i: sum over positions >= i of dgc, plus (every position) the chunk-end total
+    // sum_i w_i dw_i + gamma_C sum S G'; one position per lane (C == WAVE)
+    static_assert(C == WAVE, "one position per lane");
+    float tot = s.w[lane] * s.dw[lane] + (lane < NW ? expf(s.gc[C - 1]) * s.sgs[lane] : 0.f);
+    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, WAVE);
+    float run = s.dgc[lane];
+    for (int o = 1; o < WAVE; o <<= 1) {
+      const float x = __shfl_down(run, o, WAVE);
+      if (lane + o < WAVE) run += x;
     }
+    const int iq = lane / nh;
+    if (lane < valid && lane - iq * nh == 0) p.dg_log[(b * (long)p.L + tok0 + iq) * p.H + h] = tot + run;
   }
 
   // ---- dQ = gamma dQraw + E1 K, dK = w A1 - gamma A2 + E1^T Q + Gs K  (d_k block w)
@@ -488,11 +493,10 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = 16 * r + 4 * g4 + j, d = 16 * wave + m;
+      const int row = 16 * r + 4 * g4 + j, d = 16 * wave + m, rq = row / nh;
       if (row >= valid) continue;
-      const long pos = P0 + row;
-      p.dk[((b * (long)p.Lx + pos) * p.H + h) * DK + d] = dk[j];
-      if (pos % nh == nh - 1) p.dq[((b * (long)p.L + pos / nh) * p.H + h) * DK + d] = p.scale * dq[j];
+      p.dk[((b * (long)p.Lx + P0 + row) * p.H + h) * DK + d] = dk[j];
+      if (row - rq * nh == nh - 1) p.dq[((b * (long)p.L + tok0 + rq) * p.H + h) * DK + d] = p.scale * dq[j];
     }
   }
 }
