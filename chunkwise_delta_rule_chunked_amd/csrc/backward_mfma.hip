@@ -83,8 +83,10 @@ struct __attribute__((aligned(16))) Lds {
       float R0[C][PC], R1[C][PC], R2[C][PC];
     } m;
   } u;
-  float gc[C], gam[C], w[C], beta[C], dbd[C], dgc[C], dw[C], rsum[C];
-  float part[3][NW][C];  // per-wave partial row sums: Q . dO S^T, K . dY S^T, K . V~ G'^T
+  float gc[C], gam[C], w[C], beta[C], dgc[C], dw[C];
+  // per-wave partial row sums (Q . dO S^T, K . dY S^T, K . V~ G'^T), then the algebra's partial
+  // sums per tile and of dbeta's diagonal term per wave
+  float part[4][NW][C];
   float sgs[NW];
 };
 static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget");
@@ -361,102 +363,120 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // ---- chunk-local C x C algebra (float32, vector ALUs): thread (r0, c) owns rows r0 + 32 u and
-  // columns c + 16 v
-  constexpr int RS = NTH / 16, NU = C / RS;
-  const int c = tid & 15, r0 = tid >> 4;
+  // ---- chunk-local C x C algebra (float32).  The two C x C x C products, X = dT diag(beta) N^T
+  // (= dT T^T) and dA = -strictLower(N^T X), run on the fp32 MFMA (16x16x4: lane (g, m) supplies
+  // A[m][g] and B[g][m] of each 4-deep step and holds D[4 g .. 4 g + 3][m]).  The per-entry
+  // terms then work on each wave's lower dA tiles in that layout; their row and column sums are
+  // reduced across lanes, left per tile in LDS and summed in a fixed order.
   auto& N = s.N;
   auto& R0 = s.u.m.R0;
   auto& R1 = s.u.m.R1;
   auto& R2 = s.u.m.R2;
-  // dbeta's diagonal term diag(N^T dT), and X = dT diag(beta) N^T (= dT T^T)
-  if (tid < C) {
+  auto mma4 = [](float a, float b, floatx4 acc) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0); };
+  // dbeta's diagonal term diag(N^T dT), rows 8 w .. 8 w + 7 by wave w
+  {
+    const int i = lane;
     float acc = 0.f;
-    for (int i = tid; i < C; ++i) acc += N[i][tid] * R0[i][tid];
-    s.dbd[tid] = acc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * wave + e;
+      acc += r >= i ? N[r][i] * R0[r][i] : 0.f;
+    }
+    s.part[3][wave][i] = acc;
   }
-  float X[NU][4];
+  // X tiles (w / 2, w % 2) and (w / 2, 3 - w % 2), equal depth per wave (N[j][k] = 0 for k > j)
+  floatx4 xt[2];
 #pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = r0 + RS * u, j = c + 16 * v;
-      float acc = 0.f;
-      for (int k = 0; k <= j; ++k) acc += R0[i][k] * s.beta[k] * N[j][k];
-      X[u][v] = acc;
+  for (int t = 0; t < 2; ++t) {
+    const int bi = wave >> 1, bj = t == 0 ? (wave & 1) : 3 - (wave & 1);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < 16 * (bj + 1); k0 += 4) {
+      const int k = k0 + g4;
+      acc = mma4(R0[16 * bi + m][k], s.beta[k] * N[16 * bj + m][k], acc);
     }
+    xt[t] = acc;
+  }
+  __syncthreads();  // dT is no longer read
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int bi = wave >> 1, bj = t == 0 ? (wave & 1) : 3 - (wave & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R0[16 * bi + 4 * g4 + j][16 * bj + m] = xt[t][j];
+  }
   __syncthreads();
+  // The 10 lower tiles of dA, tile l = (bi, bj) with l = bi (bi + 1) / 2 + bj, dealt to the waves
+  // so that their depths (64 - 16 bi) even out: waves 0-6 take tile w, waves 3-5 also 12 - w.
+  int tbi[2], tbj[2];
+  floatx4 da[2];
 #pragma unroll
-  for (int u = 0; u < NU; ++u)
+  for (int t = 0; t < 2; ++t) {
+    const int l = t == 0 ? (wave < 7 ? wave : -1) : (wave >= 3 && wave <= 5 ? 12 - wave : -1);
+    const int bi = l >= 6 ? 3 : l >= 3 ? 2 : l >= 1 ? 1 : 0;
+    tbi[t] = l < 0 ? -1 : bi;
+    tbj[t] = l - bi * (bi + 1) / 2;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (l >= 0)
+      for (int k0 = 16 * bi; k0 < C; k0 += 4) {  // N[k][i] = 0 for k < i
+        const int k = k0 + g4;
+        acc = mma4(N[k][16 * bi + m], R0[k][16 * tbj[t] + m], acc);
+      }
+    da[t] = acc;
+  }
+  __syncthreads();  // X is no longer read
+  // per entry j <= i: the gate-prefix term tg, dbeta's row term ta, dGm and E1 = Gam * dOV
 #pragma unroll
-    for (int v = 0; v < 4; ++v) R0[r0 + RS * u][c + 16 * v] = X[u][v];
-  __syncthreads();
-  // dA = -strictLower(N^T X)
-  float dA[NU][4];
+  for (int t = 0; t < 2; ++t) {
+    if (tbi[t] < 0) continue;
+    const int bi = tbi[t], bj = tbj[t], j = 16 * bj + m;
+    float rb[4], rt[4], cs = 0.f;
 #pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = r0 + RS * u, j = c + 16 * v;
-      float acc = 0.f;
-      if (j < i)
-        for (int k = i; k < C; ++k) acc += N[k][i] * R0[k][j];
-      dA[u][v] = -acc;
-    }
-  __syncthreads();
-  // per entry j <= i: the gate-prefix term t, dbeta's row term, dGm and E1 = Gam * dOV
-  float rbs[NU] = {}, rts[NU] = {};
-#pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = r0 + RS * u, j = c + 16 * v;
-      float t = 0.f, dGm = 0.f, e1 = 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * bi + 4 * g4 + e;
+      float ta = 0.f, tg = 0.f, dGm = 0.f, e1 = 0.f;
       if (j <= i) {
         const float gm = gate_exp(s.gc[i] - s.gc[j]);
-        const float kk = j < i ? R2[i][j] : 0.f, dov = R1[i][j];
-        const float ta = dA[u][v] * gm * kk;  // zero on the diagonal
-        rbs[u] += ta;
-        t = s.beta[i] * ta + (float)*Pt.at(i, j) * dov;
-        dGm = s.beta[i] * gm * dA[u][v];
+        const float dA = j < i ? -da[t][e] : 0.f, dov = R1[i][j];
+        ta = dA * gm * (j < i ? R2[i][j] : 0.f);
+        tg = s.beta[i] * ta + (float)*Pt.at(i, j) * dov;
+        dGm = s.beta[i] * gm * dA;
         e1 = gm * dov;
-        rts[u] += t;
       }
-      X[u][v] = t;       // reused: t
-      dA[u][v] = dGm;    // reused: dGm
-      R1[i][j] = e1;     // each entry read above by its own thread only
+      R0[i][j] = dGm;  // each entry is this lane's alone
+      R1[i][j] = e1;
+      rb[e] = row_sum16(ta);
+      rt[e] = row_sum16(tg);
+      cs += tg;
     }
+    // column sums of tg over the tile's rows: the lane's 4, then its column's 4 lane groups
+    cs += __shfl_xor(cs, 16, WAVE);
+    cs += __shfl_xor(cs, 32, WAVE);
+    if (m == 0)
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    rbs[u] = row_sum16(rbs[u]);
-    rts[u] = row_sum16(rts[u]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      R0[r0 + RS * u][c + 16 * v] = dA[u][v];
-      R2[r0 + RS * u][c + 16 * v] = X[u][v];
-    }
-    if (c == 0) {
-      s.dbd[r0 + RS * u] += rbs[u];
-      s.rsum[r0 + RS * u] = rts[u];
-    }
+      for (int e = 0; e < 4; ++e) {
+        s.part[0][bj][16 * bi + 4 * g4 + e] = rb[e];
+        s.part[1][bj][16 * bi + 4 * g4 + e] = rt[e];
+      }
+    if (g4 == 0) s.part[2][bi][j] = cs;
   }
   __syncthreads();
   if (tid < C) {
-    const int i = tid;
-    float col = 0.f;
-    for (int r = i; r < C; ++r) col += R2[r][i];
-    s.dgc[i] += s.rsum[i] - col - s.w[i] * s.dw[i];
-    if (i < valid) p.dbeta[(b * (long)p.Lx + P0 + i) * p.H + h] = s.dbd[i];
+    const int i = tid, bi = i >> 4;
+    float dbd = 0.f, rs = 0.f, col = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) dbd += s.part[3][w][i];
+    for (int bj = 0; bj <= bi; ++bj) {
+      dbd += s.part[0][bj][i];
+      rs += s.part[1][bj][i];
+    }
+    for (int bk = bi; bk < C / 16; ++bk) col += s.part[2][bk][i];
+    s.dgc[i] += rs - col - s.w[i] * s.dw[i];
+    if (i < valid) p.dbeta[(b * (long)p.Lx + P0 + i) * p.H + h] = dbd;
   }
-  // E1 and Gs = dGm + dGm^T in bf16 for the last products
+  // E1 and Gs = dGm + dGm^T in bf16 for the last products (only the lower entries were written)
   for (int idx = tid; idx < C * C; idx += NTH) {
     const int i = idx >> 6, j = idx & 63;
-    *E1t.at(i, j) = (bf16)R1[i][j];
-    *Gst.at(i, j) = (bf16)(R0[i][j] + R0[j][i]);
+    *E1t.at(i, j) = (bf16)(j <= i ? R1[i][j] : 0.f);
+    *Gst.at(i, j) = (bf16)((j < i ? R0[i][j] : 0.f) + (i < j ? R0[j][i] : 0.f));
   }
   __syncthreads();
   if (wave == 0 && p.dg_log) {
