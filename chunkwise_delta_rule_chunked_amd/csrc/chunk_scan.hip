@@ -87,7 +87,9 @@ struct DOp<bf16> {
   __device__ static inline floatx4 mma8(bf16x8 a, B b0, B b1, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
   }
-  static constexpr bool PAIRS = true;  // mma2 is one instruction (a chain must not mix shapes)
+  // mma2 is one instruction: a chain must not mix shapes (a dependent pair of different shapes
+  // needs wait states the compiler does not insert on gfx950)
+  static constexpr bool PAIRS = true;
 };
 
 template <>

@@ -247,9 +247,11 @@ __device__ inline floatx4 mma_tn(floatx4 acc, const Tile<bf16>& m, int d0, const
 // C(16x16) += A(16 x K) * B(K x 16): A rows a_r0.. of tile a (K along the row), B^T rows
 // b_r0.. of tile b (the B operand stored transposed, K along the row).  K must be a multiple
 // of 16 (of 4 for float).  One accumulation chain uses one instruction shape: a contraction
-// whose K is not a multiple of the long step runs entirely on the 16-deep instruction (a
-// dependent 16x16x32 -> 16x16x16 pair on one accumulator gave intermittently wrong sums on
-// gfx950).
+// whose K is not a multiple of the long step runs entirely on the 16-deep instruction.  On
+// gfx950 an MFMA that reads the previous MFMA's result as its accumulator input needs wait
+// states when the two differ in shape (16x16x32 vs 16x16x16 bf16, either order), and the
+// compiler issues such a pair back to back: measured, about half the entries come out wrong.
+// Same-shape pairs, separate accumulators, or 16 wait states between give exact sums.
 template <typename E>
 __device__ inline floatx4 mma_tile(floatx4 acc, const Tile<E>& a, int a_r0, const Tile<E>& b, int b_r0, int K,
                                    int lane) {
