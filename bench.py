@@ -274,16 +274,18 @@ def time_prefill(w, steps, warmup, copy_calibration_mib=0):
             "median_call_ms": med}
 
 
+FORWARD_SOURCES = ("chunk_scan.hip", "common.h", "intra_chunk.hip", "kernels.h", "scan_summary.hip")
+
+
 def kernel_sources_sha():
     """Hash of the sources the forward step's kernels are built from, recorded with measured
-    traffic so a stale figure is dropped (the decode and backward kernels are not part of it)."""
+    traffic so that a stale figure is dropped."""
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "chunkwise_delta_rule_chunked_amd", "csrc")
-    for f in sorted(os.listdir(src)):
-        if f.endswith((".hip", ".h")) and f not in ("decode.hip", "backward.hip"):
-            with open(os.path.join(src, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    for f in FORWARD_SOURCES:
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
