@@ -365,6 +365,18 @@ def step_roofline(w, ms_per_step):
             "roofline_frac": round(F / t / ceiling, 4), "floor_us": round(nb / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
 
 
+def backward_flops(w) -> float:
+    """Flops of the chunkwise backward as the kernels evaluate it, causal halves counted once:
+    per expanded position 16 d_k d_v (the two state chains re-run: K S, K^T V~, K G', K^T dY; the
+    per-chunk products K S, K G', dY S^T, V~ G'^T), C (6 d_v + 5 d_k) (T Y, T^T dV~, P^T dO,
+    dV~ Y^T, dO V~^T, K K^T, Q K^T, E1 K, E1^T Q, Gs K, each over the causal half) and C^2 (the
+    two C x C x C products of the chunk-local algebra, triangular); per output 4 d_k d_v (Q^T dO
+    in the adjoint chain, dO S^T) and C (d_k + d_v)."""
+    C, dk, dv = w.chunk, w.dk, w.dv
+    npos, nout = w.B * w.H * w.Lx, w.B * w.H * w.L
+    return npos * (16 * dk * dv + C * (6 * dv + 5 * dk) + C * C) + nout * (4 * dk * dv + C * (dk + dv))
+
+
 def time_backward(w, steps, warmup=2):
     """delta_bwd on the prefill workload with its seeded cotangents (dO, dS_final): `steps`
     back-to-back calls with preallocated gradients and workspace, timed with HIP events."""
@@ -395,8 +407,12 @@ def time_backward(w, steps, warmup=2):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    F = backward_flops(w)
+    peak = _mfma_peak(w)
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "steps": steps,
-            "workspace_mib": round(ws.numel() / 2**20, 1)}
+            "workspace_mib": round(ws.numel() / 2**20, 1),
+            "roofline": {"bound": "mfma", "achieved": round(F / (ms * 1e-3) / 1e12, 2), "peak": round(peak / 1e12, 1),
+                         "unit": "TFLOP/s", "frac": round(F / (ms * 1e-3) / peak, 4), "flops": round(F)}}
 
 
 KDA_WORKLOAD = "kda_b2h16_l8k"   # the Gated DeltaNet workload's shape and inputs, decays per key channel
