@@ -246,9 +246,13 @@ int delta_fwd_kda(const delta_shape* s, const void* q, const void* k, const void
                   float* S_final, void* stream);
 
 /*
- * Bytes of device workspace delta_bwd needs for this shape: T in float32, the gate prefix and
- * Q K^T weighted by the gate ratios (C x C float32) per chunk, and per chunk its start state and the gradient of its end state (float32
- * d_k x d_v each).  Returns DELTA_OK and sets *bytes, or an error code.
+ * Bytes of device workspace delta_bwd needs for this shape.  bf16 inputs with dk = dv = 128 and
+ * chunk 64: per chunk T (bf16), the gate prefix and (I + A)^-1 (float32), the segment summaries
+ * and start states of the two state scans, and per chunk its start state (bf16) and the
+ * gradient of its end state (bf16 value and bf16 rounding residual), d_k x d_v each.  Other
+ * shapes: per chunk T and Q K^T weighted by the gate ratios (C x C float32 each), the gate
+ * prefix, and the start state and end-state gradient in float32.  The contents need no clearing
+ * between calls.  Returns DELTA_OK and sets *bytes, or an error code.
  */
 int delta_bwd_workspace_bytes(const delta_shape* s, size_t* bytes);
 
@@ -257,6 +261,9 @@ int delta_bwd_workspace_bytes(const delta_shape* s, size_t* bytes);
  * every input.  The pages define only the forward ("08 linear delta rule & DPLR", sections
  * 2.2-2.3 and 3; DeltaProduct notes, section 4.1); these are its exact derivatives, evaluated
  * chunkwise with the forward's T, gate prefix and chunk states recomputed from the inputs.
+ * For bf16 inputs with dk = dv = 128 and chunk 64 the chunk products run on the bf16 MFMA with
+ * float32 accumulation (the chunk states and most intermediate tiles rounded to bf16 as
+ * operands); otherwise all arithmetic is float32.
  *   q, k, v, beta, g_log, S0   as passed to delta_fwd (g_log NULL: ungated, S0 NULL: zeros)
  *   dO       [B, L, H, dv]        dtype     gradient of O
  *   dS_final [B, H, dk, dv]       float32   gradient of S_final, or NULL for zero
