@@ -181,7 +181,9 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
   const int m = lane & 15, g4 = lane >> 4;
   const int BH = p.B * p.H;
   const int NCT = p.DV / 16;
-  const int MCT = SUM ? DK / 16 : 0;
+  // transition columns: the forward summary's; the reverse chain takes its transition maps from
+  // the forward summary (transposed), so its summary runs the value columns only
+  const int MCT = (SUM && !REV) ? DK / 16 : 0;
   const int G = (NCT + MCT + TPG - 1) / TPG;            // column groups
   const int NSEG = SUM ? p.P - 1 : p.P;                 // segments this launch handles
 
@@ -1011,7 +1013,7 @@ template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV = false
 static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
   using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV>;
   constexpr int TPG = Cfg::TPG;
-  const int NCT = p.DV / 16, MCT = Cfg::SUM ? DK / 16 : 0;
+  const int NCT = p.DV / 16, MCT = (Cfg::SUM && !REV) ? DK / 16 : 0;
   const int G = (NCT + MCT + TPG - 1) / TPG;
   const int nseg = Cfg::SUM ? p.P - 1 : p.P;
   const long blocks = (long)nseg * p.B * p.H * G;

@@ -369,7 +369,8 @@ int delta_chunk_wy(const delta_shape* s, const void* k, const void* v, const flo
 
 namespace {
 // Workspace of the backward pass.  Where the state scans apply (bf16, d_k = d_v = 128, chunk 64):
-// T (bf16), the gate prefix, N = (I + A)^-1 (float32), the segment summaries and start states,
+// T (bf16), the gate prefix, N = (I + A)^-1 (float32), the segment summaries of the two scans
+// (the reverse scan's transition maps are the forward's, transposed) and their start states,
 // and per chunk the start state (bf16) and the end-of-chunk state gradient (bf16 and its bf16
 // rounding residual).  Otherwise:
 // T (float32), the gate prefix, Q K^T * Gam (float32, C x C per chunk) and the two per-chunk
@@ -378,7 +379,7 @@ size_t states_bytes(const FwdParams& p) { return (size_t)p.B * p.H * p.NT * p.DK
 bool bwd_scans(const FwdParams& p, bool bf) { return p.NT > 0 && delta::bwd_scans_apply(p, bf); }
 size_t bwd_workspace(const FwdParams& p, bool bf) {
   if (bwd_scans(p, bf))
-    return align_up(t_bytes(p, 2)) + align_up(gc_bytes(p)) + align_up(t_bytes(p, 4)) + align_up(sm_bytes(p)) +
+    return align_up(t_bytes(p, 2)) + align_up(gc_bytes(p)) + align_up(t_bytes(p, 4)) + 2 * align_up(sm_bytes(p)) +
            align_up(sst_bytes(p)) + 3 * align_up(states_bytes(p) / 2);
   return 2 * align_up(t_bytes(p, 4)) + align_up(gc_bytes(p)) + 2 * align_up(states_bytes(p));
 }
@@ -451,6 +452,8 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
     off += align_up(t_bytes(f, 4));
     fs.SM = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
     off += align_up(sm_bytes(f));
+    fs.SMr = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;  // the reverse scan's summaries
+    off += align_up(sm_bytes(f));
     fs.Sst = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
     off += align_up(sst_bytes(f));
     void* Sn = ws + off;
@@ -465,6 +468,7 @@ int delta_bwd(const delta_shape* s, const void* q, const void* k, const void* v,
     if ((rc = hip_status(delta::launch_scan_states(fs, st)))) return rc;
     FwdParams fr = fs;  // the adjoint chain: dO for the values, dS_final in, dS0 out
     fr.v = dO, fr.S0 = dS_final, fr.S_final = dS0, fr.Sn = Gn, fr.Snl = Gnl;
+    fr.SM = fs.SMr, fr.SMr = nullptr;
     for (int ph : {delta::SCAN_SUMMARY, delta::SCAN_COMBINE, delta::SCAN_OUTPUTS})
       if ((rc = hip_status(delta::launch_rev_scan(fr, ph, st)))) return rc;
     BwdParams p;

@@ -30,6 +30,10 @@ struct FwdParams {
   // mfrag_index (common.h)
   float* SM;
   float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
+  // backward only: the summary launch also writes each segment's transition map transposed, in
+  // the M part of slot P - 1 - seg of these summaries (the reverse scan's, whose segments are
+  // numbered from the end and whose transition maps are the forward's transposed)
+  float* SMr;
   // backward scans only: [B*H, NT, DV, DK] in the element type of the inputs, each chunk's start
   // state (forward chain) or end-state gradient (reverse chain), transposed; the reverse chain
   // also stores the rounding residual of each gradient (G - Sn, rounded) at Snl

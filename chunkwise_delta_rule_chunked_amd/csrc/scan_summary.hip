@@ -323,6 +323,11 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
         bf16* Ms = reinterpret_cast<bf16*>(SMs + DV * DK);
 #pragma unroll
         for (int j = 0; j < 4; ++j) Ms[mfrag_index<mfrag_width<bf16, DK>()>(row + j, col - DV, DK)] = (bf16)S[c][t][j];
+        if (p.SMr) {  // M^T: the lane's four rows are four consecutive k of one row of M^T
+          bf16* Mt = reinterpret_cast<bf16*>(p.SMr + ((long)head * p.P + p.P - 1 - seg) * DK * (DV + DK) + DV * DK);
+          *reinterpret_cast<bf16x4*>(Mt + mfrag_index<mfrag_width<bf16, DK>()>(col - DV, row, DK)) =
+              bf16x4{(bf16)S[c][t][0], (bf16)S[c][t][1], (bf16)S[c][t][2], (bf16)S[c][t][3]};
+        }
       }
     }
 }

@@ -201,7 +201,7 @@ def test_bwd_workspace_bytes(lib):
             P, _ = segments(B, H, dv, NT)
             sm = B * H * P * dk * (dv + dk) * 4 if P > 1 else 0
             sst = B * H * P * dk * dv * 4 if P > 1 else 0
-            want = (up(B * H * NT * C * C * 2) + up(B * H * NT * C * 4) + up(B * H * NT * C * C * 4) + up(sm) + up(sst)
+            want = (up(B * H * NT * C * C * 2) + up(B * H * NT * C * 4) + up(B * H * NT * C * C * 4) + 2 * up(sm) + up(sst)
                     + 3 * up(states // 2))
         else:
             want = 2 * up(B * H * NT * C * C * 4) + up(B * H * NT * C * 4) + 2 * up(states)
