@@ -420,10 +420,12 @@ F32_VALU_PEAK_TFLOPS = 157.3
 
 
 def time_kda(steps, warmup=2):
-    """delta_fwd_kda (the token recurrence with a decay per key channel) on the 32-head, 8K-token
-    shape: `steps` back-to-back calls timed with HIP events.  Its bound is the fp32 vector ALU (a
-    chain of L dependent steps of ~7 d_k d_v flops per sequence), so the roofline is that
-    arithmetic against the fp32 vector peak, with the compulsory bytes beside it."""
+    """KDA forward on the 32-head, 8K-token shape (the Gated DeltaNet workload's inputs, decays per
+    key channel), `steps` back-to-back calls of each form timed with HIP events:
+      - chunked (delta_fwd_kda_chunked): against HBM, its compulsory bytes (q, k, v, O, beta, the
+        per-channel log decays, S0 and S_final once each) over the time per call;
+      - recurrent (delta_fwd_kda, the token recurrence): bound by the fp32 vector ALU (a chain of L
+        dependent steps of ~7 d_k d_v flops per sequence), against the fp32 vector peak."""
     import torch
     import chunkwise_delta_rule_chunked_amd as D
     import workloads as W
@@ -436,25 +438,35 @@ def time_kda(steps, warmup=2):
     beta, S0 = dev(inp["beta"], torch.float32), dev(inp["S0"], torch.float32)
     O = torch.empty((w.B, w.L, w.H, w.dv), dtype=dt, device="cuda")
     SF = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    run = lambda: D.fwd_kda(q, k, v, beta, a, S0, O=O, S_final=SF)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ws = torch.empty(D.kda_chunked_workspace_bytes(w.B, w.L, w.H), dtype=torch.uint8, device="cuda")
+
+    def timed(run):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_c = timed(lambda: D.fwd_kda_chunked(q, k, v, beta, a, S0, O=O, S_final=SF, workspace=ws))
+    ms = timed(lambda: D.fwd_kda(q, k, v, beta, a, S0, O=O, S_final=SF))
     th = w.B * w.L * w.H
     flops = th * 7 * w.dk * w.dv
     nb = compulsory_bytes(w) - w.B * w.L * w.H * 4 + th * w.dk * 4   # a per-channel log decay in place of g
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1), "steps": steps,
-            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / F32_VALU_PEAK_TFLOPS, 4), "flops": flops, "compulsory_bytes": nb,
-                         "hbm_frac": round(nb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}}
+    gbs = nb / (ms_c * 1e-3) / 1e9
+    return {"ms_per_step": round(ms_c, 4), "tokens_per_s": round(w.B * w.L / (ms_c * 1e-3), 1), "steps": steps,
+            "form": "chunked", "workspace_mib": round(ws.numel() / 2**20, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "compulsory_bytes": nb},
+            "recurrent": {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+                          "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": F32_VALU_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / F32_VALU_PEAK_TFLOPS, 4), "flops": flops,
+                                       "hbm_frac": round(nb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}}}
 
 
 def time_layer(w, steps, width=4):
@@ -669,7 +681,7 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (for HBM counter scaling)")
     ap.add_argument("--kda-only", action="store_true",
-                    help="time only delta_fwd_kda on the 32-head 8K-token shape and print its line")
+                    help="time only the KDA forward (chunked and recurrent) on the 32-head 8K-token shape and print its line")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the batch-64 decode step (scalar gate, then KDA) and print its line")
     args = ap.parse_args()

@@ -21,7 +21,7 @@ import os
 import re
 from typing import Optional
 
-__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_prologue_step", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "fwd_kda", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
+__all__ = ["fwd", "fwd_noalloc", "NOALLOC_MAX_BYTES", "bwd", "bwd_workspace_bytes", "layer_prologue", "layer_prologue_step", "layer_epilogue", "fwd_intra", "fwd_inter", "decode", "decode_kda", "fwd_kda", "fwd_kda_chunked", "kda_chunked_workspace_bytes", "chunk_wy", "workspace_bytes", "strerror", "DeltaError", "lib_path",
            "load_library", "F32", "BF16"]
 
 F32, BF16 = 0, 1
@@ -70,6 +70,8 @@ def load_library():
     lib.delta_decode.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_decode_kda.argtypes = [SP, P, P, P, P, P, P, P, P]
     lib.delta_fwd_kda.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+    lib.delta_fwd_kda_chunked_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.delta_fwd_kda_chunked.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.delta_bwd_workspace_bytes.argtypes = [SP, ctypes.POINTER(ctypes.c_size_t)]
     lib.delta_bwd.argtypes = [SP] + [P] * 15 + [ctypes.c_size_t, P]
     lib.delta_layer_prologue.argtypes = [SP, ctypes.c_int32, ctypes.c_float] + [P] * 9 + [P]
@@ -444,6 +446,38 @@ def fwd_kda(q, k, v, beta, a_log, S0=None, *, scale: float = 1.0, O=None, S_fina
                                       _dev(a_log, "a_log", torch.float32), _dev(S0, "S0", torch.float32),
                                       _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32), _stream(stream))
     _check(rc, "delta_fwd_kda")
+    return O, S_final
+
+
+def kda_chunked_workspace_bytes(B, L, H, dk=128, dv=128, chunk=64, dtype=BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().delta_fwd_kda_chunked_workspace_bytes(ctypes.byref(make_shape(B, L, H, dk, dv, 1, chunk, dtype)),
+                                                                ctypes.byref(n)), "delta_fwd_kda_chunked_workspace_bytes")
+    return n.value
+
+
+def fwd_kda_chunked(q, k, v, beta, a_log, S0=None, *, scale: float = 1.0, chunk: int = 64, O=None, S_final=None,
+                    want_state: bool = True, workspace=None, stream=None):
+    """KDA over a sequence in chunks (delta_fwd_kda_chunked; bf16, dk = dv = 128, chunk 64): the
+    arguments and result of fwd_kda.  Returns (O, S_final)."""
+    torch = _torch()
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    sh = make_shape(B, L, H, dk, dv, 1, chunk, _dtype_code(q), scale)
+    if O is None:
+        O = torch.empty((B, L, H, dv), dtype=q.dtype, device=q.device)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = kda_chunked_workspace_bytes(B, L, H, dk, dv, chunk, _dtype_code(q))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = load_library().delta_fwd_kda_chunked(ctypes.byref(sh), _dev(q, "q", q.dtype), _dev(k, "k", q.dtype),
+                                              _dev(v, "v", q.dtype), _dev(beta, "beta", torch.float32),
+                                              _dev(a_log, "a_log", torch.float32), _dev(S0, "S0", torch.float32),
+                                              _dev(O, "O", q.dtype), _dev(S_final, "S_final", torch.float32),
+                                              _dev(workspace, "workspace"),
+                                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "delta_fwd_kda_chunked")
     return O, S_final
 
 

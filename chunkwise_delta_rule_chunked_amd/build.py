@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdelta.so")
-SOURCES = ["intra_chunk.hip", "chunk_scan.hip", "scan_summary.hip", "decode.hip", "kda.hip", "backward.hip", "backward_mfma.hip", "layer.hip", "validate.hip", "noalloc.hip", "measure.hip", "delta_abi.cpp"]
+SOURCES = ["intra_chunk.hip", "chunk_scan.hip", "scan_summary.hip", "decode.hip", "kda.hip", "kda_chunk.hip", "backward.hip", "backward_mfma.hip", "layer.hip", "validate.hip", "noalloc.hip", "measure.hip", "delta_abi.cpp"]
 # per-file flags: the summary kernel keeps MFMA accumulators in VGPRs (its state is also worked on
 # by vector instructions, and in AGPRs every such step copies it through VGPRs)
 EXTRA = {"scan_summary.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

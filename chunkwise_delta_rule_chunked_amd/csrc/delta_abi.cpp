@@ -605,6 +605,94 @@ int delta_fwd_kda(const delta_shape* s, const void* q, const void* k, const void
   return hip_status(delta::launch_kda_fwd(p, s->dtype == DELTA_BF16, st));
 }
 
+namespace {
+// KDA in chunks: bf16, d_k = d_v = 128, chunk 64, one step per token.  Workspace: T and Aqk (C x C
+// bf16 per chunk), K e^{Gc}, K e^{Gc_C - Gc} and Q e^{Gc} (bf16, the layout of k), e^{Gc_C}
+// (d_k float32 per chunk), the segment summaries and start states, and each chunk's start state
+// (bf16).
+bool kda_chunked_shape(const delta_shape* s) {
+  return s->dtype == DELTA_BF16 && s->dk == 128 && s->dv == 128 && s->chunk == 64 && s->n_h == 1;
+}
+size_t kda_tile_bytes(const FwdParams& f) { return (size_t)f.B * f.L * f.H * 128 * 2; }
+size_t kda_dc_bytes(const FwdParams& f) { return (size_t)f.B * f.H * f.NT * 128 * 4; }
+size_t kda_chunked_workspace(const FwdParams& f) {
+  return 2 * align_up(t_bytes(f, 2)) + 3 * align_up(kda_tile_bytes(f)) + align_up(kda_dc_bytes(f)) +
+         align_up(sm_bytes(f)) + align_up(sst_bytes(f)) + align_up(states_bytes(f) / 2);
+}
+}  // namespace
+
+int delta_fwd_kda_chunked_workspace_bytes(const delta_shape* s, size_t* bytes) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!kda_chunked_shape(s)) return DELTA_ERR_UNSUPPORTED_DIM;
+  if (!bytes) return DELTA_ERR_NULL_ARG;
+  *bytes = kda_chunked_workspace(make_params(s));
+  return DELTA_OK;
+}
+
+int delta_fwd_kda_chunked(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+                          const float* a_log, const float* S0, void* O, float* S_final, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!kda_chunked_shape(s)) return DELTA_ERR_UNSUPPORTED_DIM;
+  const size_t es = 2;
+  const size_t nt = (size_t)s->B * s->L * s->H, BH = (size_t)s->B * s->H;
+  if (nt > 0 && (!q || !k || !v || !beta || !a_log || !O)) return DELTA_ERR_NULL_ARG;
+  const FwdParams f = make_params(s);
+  const size_t need = kda_chunked_workspace(f);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DELTA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, a_log, S0, O, S_final, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DELTA_ERR_MISALIGNED;
+  if (!aligned(beta, 4)) return DELTA_ERR_MISALIGNED;
+  const Range in[] = {range(q, q ? nt * 128 * es : 0), range(k, k ? nt * 128 * es : 0),
+                      range(v, v ? nt * 128 * es : 0), range(beta, beta ? nt * 4 : 0),
+                      range(a_log, a_log ? nt * 128 * 4 : 0), range(S0, S0 ? BH * 128 * 128 * 4 : 0)};
+  const Range ro = range(O, O ? nt * 128 * es : 0), rs = range(S_final, S_final ? BH * 128 * 128 * 4 : 0),
+              rw = range(workspace, need);
+  for (const Range& r : in) {
+    if (overlap(ro, r) || overlap(rw, r)) return DELTA_ERR_ALIAS;
+    if (overlap(rs, r) && !(S0 && S_final == S0 && r.lo == reinterpret_cast<uintptr_t>(S0))) return DELTA_ERR_ALIAS;
+  }
+  if (overlap(ro, rs) || overlap(ro, rw) || overlap(rs, rw)) return DELTA_ERR_ALIAS;
+  if (BH == 0 || (s->L == 0 && !S_final)) return DELTA_OK;
+  if (s->L == 0) return delta_fwd_kda(s, q, k, v, beta, a_log, S0, O, S_final, stream);  // state passes through
+  if ((rc = launch_guard())) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (validate_on() && (rc = validate_small(beta, nt, a_log, nt * 128, st))) return rc;
+  char* ws = static_cast<char*>(workspace);
+  delta::KdaChunkParams kp;
+  memset(&kp, 0, sizeof(kp));
+  kp.B = f.B, kp.L = f.L, kp.H = f.H, kp.NT = f.NT, kp.scale = f.scale;
+  kp.q = q, kp.k = k, kp.v = v, kp.beta = beta, kp.a_log = a_log, kp.O = O;
+  size_t off = 0;
+  kp.T = ws + off;
+  off += align_up(t_bytes(f, 2));
+  kp.Aqk = ws + off;
+  off += align_up(t_bytes(f, 2));
+  kp.kp = ws + off;
+  off += align_up(kda_tile_bytes(f));
+  kp.kh = ws + off;
+  off += align_up(kda_tile_bytes(f));
+  kp.qp = ws + off;
+  off += align_up(kda_tile_bytes(f));
+  kp.dC = reinterpret_cast<float*>(ws + off);
+  off += align_up(kda_dc_bytes(f));
+  FwdParams fs = f;
+  fs.SM = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
+  off += align_up(sm_bytes(f));
+  fs.Sst = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
+  off += align_up(sst_bytes(f));
+  fs.Sn = ws + off;
+  kp.Sn = fs.Sn;
+  fs.k = kp.kp, fs.kh = kp.kh, fs.dC = kp.dC, fs.v = v, fs.T = kp.T, fs.beta = beta, fs.S0 = S0, fs.S_final = S_final;
+  if ((rc = hip_status(delta::launch_kda_intra(kp, st)))) return rc;
+  for (int ph : {delta::SCAN_SUMMARY, delta::SCAN_COMBINE, delta::SCAN_OUTPUTS})
+    if ((rc = hip_status(delta::launch_kda_scan(fs, ph, st)))) return rc;
+  return hip_status(delta::launch_kda_out(kp, st));
+}
+
 int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const void* xq, const void* xk,
                          const void* xv, const float* wq, const float* wk, const float* wv, void* q, void* k,
                          void* v, void* stream) {

@@ -30,6 +30,10 @@ struct FwdParams {
   // mfrag_index (common.h)
   float* SM;
   float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
+  // KDA chunks (kda_chunk.hip): k holds K e^{Gc}; kh K e^{Gc_C - Gc} (same layout) and dC
+  // e^{Gc_C} [B*H, NT, DK], the chunk's decay per key channel
+  const void* kh;
+  const float* dC;
   // backward only: the summary launch also writes each segment's transition map transposed, in
   // the M part of slot P - 1 - seg of these summaries (the reverse scan's, whose segments are
   // numbered from the end and whose transition maps are the forward's transposed)
@@ -66,6 +70,28 @@ struct KdaParams {
   const float* S0;      // [B, H, DK, DV] or nullptr
   void* O;              // [B, L, H, DV]
   float* S_final;       // [B, H, DK, DV] or nullptr; may be S0
+};
+
+// KDA forward in chunks (kda_chunk.hip): bf16, d_k = d_v = 128, chunk 64, one step per token.
+struct KdaChunkParams {
+  int B, L, H, NT;
+  float scale;
+  const void* q;        // [B, L, H, 128] bf16
+  const void* k;        // [B, L, H, 128] bf16
+  const void* v;        // [B, L, H, 128] bf16
+  const float* beta;    // [B, L, H]
+  const float* a_log;   // [B, L, H, 128] log alpha per key channel
+  // per chunk, written by the intra launch: T and Aqk [B*H, NT, C, C] bf16; K e^{Gc},
+  // K e^{Gc_C - Gc} and scale Q e^{Gc} in the layout of k [B, L, H, 128] bf16; e^{Gc_C}
+  // [B*H, NT, 128] float32
+  void* T;
+  void* Aqk;
+  void* kp;
+  void* kh;
+  void* qp;
+  float* dC;
+  const void* Sn;       // [B*H, NT, 128, 128] bf16: each chunk's start state, transposed (output launch)
+  void* O;              // [B, L, H, 128] bf16
 };
 
 // One backward problem after validation (shape fields as in FwdParams).
@@ -131,6 +157,11 @@ hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 bool bwd_scans_apply(const FwdParams& p, bool bf16);
 hipError_t launch_scan_states(const FwdParams& p, hipStream_t st);
 hipError_t launch_rev_scan(const FwdParams& p, int phase, hipStream_t st);
+// KDA in chunks: the intra launch (kda_chunk.hip), the scan's summary and state-storing chain in
+// KDA mode (chunk_scan.hip; the combine is the forward's), the output launch.
+hipError_t launch_kda_intra(const KdaChunkParams& p, hipStream_t st);
+hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st);
+hipError_t launch_kda_out(const KdaChunkParams& p, hipStream_t st);
 // Backward launches (backward.hip), in order after launch_intra_chunk with float T:
 // 3 Q K^T * Gam per chunk, 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0),
 // 2 per-chunk gradients.

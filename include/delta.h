@@ -246,6 +246,28 @@ int delta_fwd_kda(const delta_shape* s, const void* q, const void* k, const void
                   float* S_final, void* stream);
 
 /*
+ * Bytes of device workspace delta_fwd_kda_chunked needs for this shape (see below).  Shapes other
+ * than bf16, dk = dv = 128, chunk 64, n_h = 1: DELTA_ERR_UNSUPPORTED_DIM.
+ */
+int delta_fwd_kda_chunked_workspace_bytes(const delta_shape* s, size_t* bytes);
+
+/*
+ * KDA forward over a sequence in chunks: the same result as delta_fwd_kda (same arguments and
+ * meaning), computed chunkwise ("08 linear delta rule & DPLR", section 1.4 table, KDA row, and
+ * section 5 for the recurrence; the chunk form follows from it as sections 2.2-2.3 and 3 derive
+ * the scalar-gated one: inside a chunk the Gram matrix and the causal Q K^T carry the decay per
+ * key channel, e^{Gc_r - Gc_j} with Gc the in-chunk cumulative log decay, and the state decays
+ * row by row by e^{Gc_C}).  bf16 only, dk = dv = 128, s->chunk = 64, s->n_h = 1; other shapes
+ * return DELTA_ERR_UNSUPPORTED_DIM (delta_fwd_kda takes them).  Each log decay is raised to at
+ * least -150 first (a -inf reset then decays to exactly 0).  Workspace: at least
+ * delta_fwd_kda_chunked_workspace_bytes bytes, 16-byte aligned, overlapping no argument; its
+ * contents need no clearing.  Alignment, aliasing and error codes otherwise as delta_fwd_kda.
+ */
+int delta_fwd_kda_chunked(const delta_shape* s, const void* q, const void* k, const void* v, const float* beta,
+                          const float* a_log, const float* S0, void* O, float* S_final, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace delta_bwd needs for this shape.  bf16 inputs with dk = dv = 128 and
  * chunk 64: per chunk T (bf16), the gate prefix and (I + A)^-1 (float32), the segment summaries
  * and start states of the two state scans, and per chunk its start state (bf16) and the

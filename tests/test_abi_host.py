@@ -24,6 +24,7 @@ def test_exports_every_header_function(lib):
     assert set(names) == {"delta_fwd_workspace_bytes", "delta_fwd", "delta_fwd_noalloc", "delta_fwd_intra", "delta_fwd_inter",
                           "delta_fwd_segments", "delta_fwd_scan_summary", "delta_fwd_scan_combine",
                           "delta_fwd_scan_outputs", "delta_chunk_wy", "delta_decode", "delta_decode_kda", "delta_fwd_kda",
+                          "delta_fwd_kda_chunked", "delta_fwd_kda_chunked_workspace_bytes",
                           "delta_bwd_workspace_bytes", "delta_bwd", "delta_layer_prologue", "delta_layer_prologue_step",
                           "delta_layer_epilogue", "delta_strerror"}
     for n in names:
@@ -302,3 +303,37 @@ def test_noalloc_limit(lib):
     assert ws(sh)[1] > D.NOALLOC_MAX_BYTES
     assert D.load_library().delta_fwd_noalloc(ctypes.byref(sh), *[None] * 8, None) == -9
     assert D.load_library().delta_fwd_noalloc(ctypes.byref(shape(dk=48)), *[None] * 8, None) == -3
+
+
+def test_kda_chunked_workspace_and_argument_checks(lib):
+    """delta_fwd_kda_chunked takes bf16, dk = dv = 128, chunk 64, n_h = 1 only; its workspace holds T and
+    Aqk (C x C bf16 per chunk), three bf16 tiles in the layout of k, the chunk decay (128 floats per
+    chunk), the segment summaries and start states, and each chunk's start state (bf16)."""
+    up = lambda x: (x + 255) // 256 * 256
+    L = D.load_library()
+    for B, H, Ln in [(2, 16, 8192), (1, 2, 333), (2, 128, 70)]:
+        NT = -(-Ln // 64)
+        n = ctypes.c_size_t(0)
+        assert L.delta_fwd_kda_chunked_workspace_bytes(ctypes.byref(shape(B=B, H=H, L=Ln, dk=128, dv=128, chunk=64)),
+                                                       ctypes.byref(n)) == 0
+        P, _ = segments(B, H, 128, NT)
+        sm = B * H * P * 128 * 256 * 4 if P > 1 else 0
+        sst = B * H * P * 128 * 128 * 4 if P > 1 else 0
+        want = (2 * up(B * H * NT * 64 * 64 * 2) + 3 * up(B * Ln * H * 128 * 2) + up(B * H * NT * 128 * 4) + up(sm)
+                + up(sst) + up(B * H * NT * 128 * 128 * 2))
+        assert n.value == want, (B, H, Ln)
+    n = ctypes.c_size_t(0)
+    for bad in (dict(dk=64), dict(dv=64), dict(chunk=32), dict(n_h=2, chunk=64), dict(dtype=D.F32)):
+        kw = dict(B=1, H=2, L=100, dk=128, dv=128, chunk=64)
+        kw.update(bad)
+        assert L.delta_fwd_kda_chunked_workspace_bytes(ctypes.byref(shape(**kw)), ctypes.byref(n)) == -3, bad
+    sh = shape(B=1, H=2, L=100, dk=128, dv=128, chunk=64)
+    f = [ctypes.c_void_p(4096 * (i + 1) * 1024) for i in range(9)]
+    args = f[:5] + [None] + f[5:7]                        # q k v beta a_log S0 O S_final
+    assert L.delta_fwd_kda_chunked(ctypes.byref(sh), *args, f[8], ctypes.c_size_t(16), None) == -5   # workspace small
+    assert L.delta_fwd_kda_chunked(ctypes.byref(sh), *args, None, ctypes.c_size_t(0), None) == -5
+    big = ctypes.c_size_t(1 << 40)
+    assert L.delta_fwd_kda_chunked(ctypes.byref(sh), *args, f[0], big, None) == -6                     # aliases q
+    assert L.delta_fwd_kda_chunked(ctypes.byref(sh), f[0], None, *args[2:], f[8], big, None) == -1     # k NULL
+    assert L.delta_fwd_kda_chunked(ctypes.byref(shape(B=1, H=2, L=100, dk=64, dv=64, chunk=64)), *args, f[8], big,
+                                   None) == -3

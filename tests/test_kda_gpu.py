@@ -131,3 +131,64 @@ def test_kda_prefill_then_decode():
     Or, Sr = oracle.fwd_kda(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["S0"])
     assert head_rel_err(np.concatenate(outs, axis=1), Or, (0, 2)) <= TOL["f32"]
     assert head_rel_err(S.cpu().numpy(), Sr, (0, 1)) <= TOL["f32"]
+
+
+# ---------------------------------------------------------------- KDA in chunks
+def run_kda_chunked(w, inp, a, scale=1.0, S_final=None):
+    d = inputs_to_dev(inp, w.dtype)
+    ad = torch.from_numpy(a).cuda()
+    O, S = D.fwd_kda_chunked(d["q"], d["k"], d["v"], d["beta"], ad, d["S0"] if S_final is None else S_final,
+                             scale=scale, S_final=S_final)
+    torch.cuda.synchronize()
+    return to_np(O), to_np(S)
+
+
+def check_kda_chunked(w, inp=None, a=None, scale=1.0):
+    """delta_fwd_kda_chunked against the oracle (bar 2e-2, bf16 inputs) and against the token
+    recurrence delta_fwd_kda on the same inputs (same bar)."""
+    inp = inp if inp is not None else W.make_inputs(w)
+    a = a if a is not None else W.make_kda_decays(w)
+    say("case kda chunked", w, "segments", D.segments(w.B, w.L, w.H, w.dk, w.dv))
+    O, S = run_kda_chunked(w, inp, a, scale)
+    Or, Sr = oracle.fwd_kda(inp["q"], inp["k"], inp["v"], inp["beta"], a, inp["S0"], scale=scale)
+    eo, es = head_rel_err(O, Or, (0, 2)), head_rel_err(S, Sr, (0, 1))
+    Ot, St = run_kda(w, inp, a, scale)
+    et = head_rel_err(O, Ot.astype(np.float64), (0, 2))
+    say("  err O %.3e S %.3e; against the recurrence %.3e" % (eo, es, et))
+    assert np.isfinite(O).all() and np.isfinite(S).all()
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and et <= TOL["bf16"], (eo, es, et)
+
+
+CHUNKED = [
+    kda_case("kdac_bf16_333", B=2, L=333, dk=128, dv=128),
+    kda_case("kdac_weak_700", B=1, L=700, dk=128, dv=128, gate="weak"),
+    kda_case("kdac_one_chunk", B=2, H=3, L=64, dk=128, dv=128, s0=None),
+    kda_case("kdac_short", B=1, L=5, dk=128, dv=128),
+    # the scan's segment split: none (256 heads fill the GPU), and 41 one-chunk segments
+    kda_case("kdac_unsplit", B=2, H=128, L=70, dk=128, dv=128),
+    kda_case("kdac_41_segments", B=1, H=1, L=64 * 40 + 17, dk=128, dv=128, gate="weak"),
+]
+
+
+@pytest.mark.parametrize("w", CHUNKED, ids=lambda w: w.name)
+def test_kda_chunked(w):
+    check_kda_chunked(w, scale=0.9)
+
+
+def test_kda_chunked_full_shape_all_heads():
+    check_kda_chunked(kda_case("kda_b2h16_l8k", B=2, H=16, L=8192, dk=128, dv=128, cfg_id=3))
+
+
+def test_kda_chunked_resets_and_in_place():
+    """log alpha = -inf on one channel, on a whole token at a chunk start and mid-chunk: exact
+    erasure as in the oracle; then S_final = S0 in place gives the same O and state."""
+    w = kda_case("kdac_reset", B=1, H=2, L=300, dk=128, dv=128, gate="weak")
+    inp, a = W.make_inputs(w), W.make_kda_decays(w)
+    a[0, 50, 0, 7] = -np.inf
+    a[0, 128, 1, :] = -np.inf
+    a[0, 201, 0, :] = -np.inf
+    check_kda_chunked(w, inp=inp, a=a)
+    O1, S1 = run_kda_chunked(w, inp, a)
+    Sin = torch.from_numpy(inp["S0"]).cuda()
+    O2, S2 = run_kda_chunked(w, inp, a, S_final=Sin)
+    assert np.array_equal(O1, O2) and np.array_equal(S1, S2) and np.array_equal(Sin.cpu().numpy(), S1)
