@@ -58,15 +58,129 @@ __device__ inline u32x4 pack8(const float* x) {
   return __builtin_bit_cast(u32x4, v);
 }
 
+// Diagonal block I of A and Aqk entry by entry, with the exact per-channel factor e^{Gc_r - Gc_j}
+// (j <= r, never above 1), by one wave: 16-lane group g takes the block's rows g, 7 - g, 8 + g and
+// 15 - g (34 entries), lane l of the group channels 8 l .. 8 l + 7, each entry a DPP row sum.
+__device__ __noinline__ void diag_exact(const float (*Gc)[GP], const bf16 (*Kl)[KP], float* As, bf16 (*Aq)[C + 8],
+                                        const float* bs, const bf16* qb, long HD, int valid, float scale, int I,
+                                        int lane) {
+  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
+  const int grp = lane >> 4, gl = lane & 15, c = 8 * gl;
+  float* blk = As + lower_block(I, I) * BLK;
+  const int rl4[4] = {grp, 7 - grp, 8 + grp, 15 - grp};
+  for (int u = 0; u < 4; ++u) {
+    const int rl = rl4[u], r = 16 * I + rl;
+    float kr[8], qr[8], gr[8];
+    unpack8(*reinterpret_cast<const u32x4*>(&Kl[r][c]), kr);
+    unpack8(r < valid ? *reinterpret_cast<const u32x4*>(qb + r * HD + c) : u32x4{0, 0, 0, 0}, qr);
+    *reinterpret_cast<floatx4*>(gr) = *reinterpret_cast<const floatx4*>(&Gc[r][c]);
+    *reinterpret_cast<floatx4*>(gr + 4) = *reinterpret_cast<const floatx4*>(&Gc[r][c + 4]);
+    for (int jl = 0; jl <= rl; ++jl) {
+      const int j = 16 * I + jl;
+      float kj[8], gj[8];
+      unpack8(*reinterpret_cast<const u32x4*>(&Kl[j][c]), kj);
+      *reinterpret_cast<floatx4*>(gj) = *reinterpret_cast<const floatx4*>(&Gc[j][c]);
+      *reinterpret_cast<floatx4*>(gj + 4) = *reinterpret_cast<const floatx4*>(&Gc[j][c + 4]);
+      float sg = 0.f, sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kd = kj[e] * gate_exp(gr[e] - gj[e]);
+        sg += kr[e] * kd;
+        sq += qr[e] * kd;
+      }
+      sg = row_sum16(sg);
+      sq = row_sum16(sq);
+      if (gl == 0) {
+        if (jl < rl) blk[rl * LDB + jl] = bs[r] * sg;
+        Aq[r][j] = (bf16)(scale * sq);
+      }
+    }
+  }
+}
+
+// Largest per-channel decay span (Gc at the row before a 16-row block minus Gc at its last row) for
+// which the block's diagonal entries are taken on the MFMA: its B factors reach e^{span}, its A
+// factors e^{-span}, both far inside float32's normal range.
+constexpr float DIAG_SPAN = 64.f;
+
+// The entries of row block I of A and Aqk against column blocks J0 .. J0 + NJ - 1 (J <= I), each a
+// 16 x 16 product over d_k on the fp32 MFMA.  The reference is the row just before the block,
+// rho = 16 I - 1 (Gc_rho = 0 for I = 0): the A operand is k_r e^{Gc_r - Gc_rho} (scale q_r e^{...}
+// for Aqk), the B operand k_j e^{Gc_rho - Gc_j}.  Below the diagonal block (j <= rho) both factors
+// are decays (<= 1; a product that underflows is below either factor); on the diagonal block the
+// B factor is a growth bounded by e^{span}, so that block takes this route only when every
+// channel's span is within DIAG_SPAN (NaN is not), else diag_exact below.  The contraction over
+// d_k is permuted alike in both operands: lane group g takes channels 32 g .. 32 g + 31, one per
+// 4-deep step.  Results go to the A slots (times beta of the row; the diagonal block's entries
+// j < r) and to the Aqk tile (j <= r; above the diagonal it keeps its zeros).
+template <int NJ>
+__device__ __forceinline__ void block_row(const float (*Gc)[GP], const bf16 (*Kl)[KP], float* As, bf16 (*Aq)[C + 8],
+                                          const float* bs, const bf16* qb, long HD, int valid, float scale, int I,
+                                          int J0, int lane) {
+  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
+  const int g4 = lane >> 4, m = lane & 15, ra = 16 * I + m, rho = 16 * I - 1, c0 = 32 * g4;
+  const bool has_diag = J0 + NJ - 1 == I;
+  bool diag_ok = true;
+  if (has_diag) {
+    const int e = 16 * I + 15;
+    const float s0 = (rho >= 0 ? Gc[rho][lane] : 0.f) - Gc[e][lane];
+    const float s1 = (rho >= 0 ? Gc[rho][lane + 64] : 0.f) - Gc[e][lane + 64];
+    diag_ok = __all(s0 <= DIAG_SPAN && s1 <= DIAG_SPAN);
+  }
+  float qa[32];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u32x4 x = ra < valid ? *reinterpret_cast<const u32x4*>(qb + ra * HD + c0 + 8 * u) : u32x4{0, 0, 0, 0};
+    unpack8(x, qa + 8 * u);
+  }
+  floatx4 gram[NJ], aqk[NJ];
+#pragma unroll
+  for (int t = 0; t < NJ; ++t) gram[t] = aqk[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int s4 = 0; s4 < 32; s4 += 4) {
+    const int c = c0 + s4;
+    const floatx4 ga = *reinterpret_cast<const floatx4*>(&Gc[ra][c]);
+    const floatx4 gr = rho >= 0 ? *reinterpret_cast<const floatx4*>(&Gc[rho][c]) : floatx4{0.f, 0.f, 0.f, 0.f};
+    const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&Kl[ra][c]);
+    floatx4 gb[NJ];
+    bf16x4 kb[NJ];
+#pragma unroll
+    for (int t = 0; t < NJ; ++t) {
+      gb[t] = *reinterpret_cast<const floatx4*>(&Gc[16 * (J0 + t) + m][c]);
+      kb[t] = *reinterpret_cast<const bf16x4*>(&Kl[16 * (J0 + t) + m][c]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float ea = gate_exp(ga[s] - gr[s]), av = (float)ka[s] * ea, aq = scale * qa[s4 + s] * ea;
+#pragma unroll
+      for (int t = 0; t < NJ; ++t) {
+        const float bv = (float)kb[t][s] * gate_exp(gr[s] - gb[t][s]);
+        gram[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, gram[t], 0, 0, 0);
+        aqk[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, bv, aqk[t], 0, 0, 0);
+      }
+    }
+  }
+  // lane (g, m) holds rows 4 g .. 4 g + 3 of column m of each block
+#pragma unroll
+  for (int t = 0; t < NJ; ++t) {
+    const int J = J0 + t;
+    if (J == I && !diag_ok) continue;
+    float* blk = As + lower_block(I, J) * BLK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = 4 * g4 + j, r = 16 * I + rl;
+      if (J < I || m < rl) blk[rl * LDB + m] = bs[r] * gram[t][j];
+      if (J < I || m <= rl) Aq[r][16 * J + m] = (bf16)aqk[t][j];
+    }
+  }
+  if (has_diag && !diag_ok) diag_exact(Gc, Kl, As, Aq, bs, qb, HD, valid, scale, I, lane);
+}
+
 // One workgroup of 4 wavefronts per (sequence, head, chunk).
 //   1. keys to LDS (rows past the sequence: 0), beta, Gc per channel (two half-chunk scans)
-//   2. the 6 blocks of A and Aqk below the block diagonal on the fp32 MFMA: with e the last row of
-//      the column block, the A side carries e^{Gc_r - Gc_e} and the B side e^{Gc_e - Gc_j}, both
-//      decays; the contraction over d_k is permuted alike in both operands (lane group g takes
-//      channels 32 g .. 32 g + 31, one per 4-deep step)
-//   3. the 4 diagonal blocks entry by entry with the exact per-channel factor (16 lanes per
-//      entry, 8 channels each, a DPP row sum)
-//   4. T by ut_solve_store; Aqk, K+, Kh, Q+ and e^{Gc_C} stored
+//   2. the 10 blocks of A and Aqk on or below the block diagonal by row block (block_row), the
+//      diagonal blocks whose decay span is too large for it entry by entry (diag_exact)
+//   3. T by ut_solve_store; Aqk, K+, Kh, Q+ and e^{Gc_C} stored
 __global__ __launch_bounds__(NTH) void kda_intra_kernel(KdaChunkParams p) {
   __shared__ __attribute__((aligned(16))) float Gc[C][GP];
   __shared__ __attribute__((aligned(16))) bf16 Kl[C][KP];
@@ -74,10 +188,8 @@ __global__ __launch_bounds__(NTH) void kda_intra_kernel(KdaChunkParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char slots[UtSlots<C>::BYTES];
   __shared__ __attribute__((aligned(16))) float bs[C];
   float* As = reinterpret_cast<float*>(slots);
-  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
-  auto ablk = [&](int i, int j) { return As + lower_block(i, j) * BLK; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, m = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
   const long P0 = (long)n * C, chunk = (long)bh * p.NT + n;
   const int valid = (int)min((long)C, (long)p.L - P0);
@@ -129,95 +241,22 @@ __global__ __launch_bounds__(NTH) void kda_intra_kernel(KdaChunkParams p) {
   }
   __syncthreads();
 
-  // ---- 2. blocks (I, J), J < I: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); wave w takes w and w + 4
-  floatx4 gram[2], aqk[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    gram[t] = aqk[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int l = wave + 4 * t;
-    if (l >= 6) continue;
-    const int I = l >= 3 ? 3 : l >= 1 ? 2 : 1, J = l - (I - 1) * I / 2;
-    const int ra = 16 * I + m, rb = 16 * J + m, e = 16 * J + 15, c0 = 32 * g4;
-    float qa[32];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 x = ra < valid ? *reinterpret_cast<const u32x4*>(qb + ra * HD + c0 + 8 * u) : u32x4{0, 0, 0, 0};
-      unpack8(x, qa + 8 * u);
-    }
-#pragma unroll
-    for (int s4 = 0; s4 < 32; s4 += 4) {
-      const int c = c0 + s4;
-      const floatx4 ga = *reinterpret_cast<const floatx4*>(&Gc[ra][c]);
-      const floatx4 ge = *reinterpret_cast<const floatx4*>(&Gc[e][c]);
-      const floatx4 gb = *reinterpret_cast<const floatx4*>(&Gc[rb][c]);
-      const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&Kl[ra][c]);
-      const bf16x4 kv = *reinterpret_cast<const bf16x4*>(&Kl[rb][c]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float ea = gate_exp(ga[s] - ge[s]), bv = (float)kv[s] * gate_exp(ge[s] - gb[s]);
-        gram[t] = __builtin_amdgcn_mfma_f32_16x16x4f32((float)ka[s] * ea, bv, gram[t], 0, 0, 0);
-        aqk[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(p.scale * qa[s4 + s] * ea, bv, aqk[t], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- 3. diagonal blocks, row by row: 16-lane group g takes rows 16 d + g of blocks 0, 1 and
-  // 16 d + 15 - g of blocks 2, 3 (34 entries j <= r each), lane l of the group channels 8 l .. + 7;
-  // the group's query rows are loaded once, first
-  {
-    const int grp = tid >> 4, gl = tid & 15, c = 8 * gl;
-    int rows[4];
-    u32x4 qrow[4];
-#pragma unroll
-    for (int d = 0; d < NB; ++d) {
-      rows[d] = 16 * d + (d < 2 ? grp : 15 - grp);
-      qrow[d] = rows[d] < valid ? *reinterpret_cast<const u32x4*>(qb + rows[d] * HD + c) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int d = 0; d < NB; ++d) {
-      const int r = rows[d];
-      float kr[8], qr[8], gr[8];
-      unpack8(*reinterpret_cast<const u32x4*>(&Kl[r][c]), kr);
-      unpack8(qrow[d], qr);
-      *reinterpret_cast<floatx4*>(gr) = *reinterpret_cast<const floatx4*>(&Gc[r][c]);
-      *reinterpret_cast<floatx4*>(gr + 4) = *reinterpret_cast<const floatx4*>(&Gc[r][c + 4]);
-      for (int j = 16 * d; j <= r; ++j) {
-        float kj[8], gj[8];
-        unpack8(*reinterpret_cast<const u32x4*>(&Kl[j][c]), kj);
-        *reinterpret_cast<floatx4*>(gj) = *reinterpret_cast<const floatx4*>(&Gc[j][c]);
-        *reinterpret_cast<floatx4*>(gj + 4) = *reinterpret_cast<const floatx4*>(&Gc[j][c + 4]);
-        float sg = 0.f, sq = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kd = kj[e] * gate_exp(gr[e] - gj[e]);
-          sg += kr[e] * kd;
-          sq += qr[e] * kd;
-        }
-        sg = row_sum16(sg);
-        sq = row_sum16(sq);
-        if (gl == 0) {
-          ablk(d, d)[(r - 16 * d) * LDB + (j - 16 * d)] = j < r ? bs[r] * sg : 0.f;
-          Aq[r][j] = (bf16)(p.scale * sq);
-        }
-      }
-    }
-  }
-  // the blocks below the diagonal into A (times beta of the row) and Aqk
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int l = wave + 4 * t;
-    if (l >= 6) continue;
-    const int I = l >= 3 ? 3 : l >= 1 ? 2 : 1, J = l - (I - 1) * I / 2;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * I + 4 * g4 + j;
-      ablk(I, J)[(4 * g4 + j) * LDB + m] = bs[r] * gram[t][j];
-      Aq[r][16 * J + m] = (bf16)aqk[t][j];
-    }
+  // ---- 2. A and Aqk by 16-row blocks (block_row); wave w: w = 0 row block 3
+  // against column blocks 0, 1 and row block 0; w = 1 row block 3 against 2, 3; w = 2 row block 2;
+  // w = 3 row block 1 (3, 2, 3 and 2 blocks)
+  if (wave == 0) {
+    block_row<2>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 3, 0, lane);
+    block_row<1>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 0, 0, lane);
+  } else if (wave == 1) {
+    block_row<2>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 3, 2, lane);
+  } else if (wave == 2) {
+    block_row<3>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 2, 0, lane);
+  } else {
+    block_row<2>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 1, 0, lane);
   }
   __syncthreads();
 
-  // ---- 4. T, Aqk, K+, Kh, Q+, e^{Gc_C}
+  // ---- 3. T, Aqk, K+, Kh, Q+, e^{Gc_C}
   ut_solve_store<C>(As, bs, static_cast<bf16*>(p.T) + chunk * C * C, static_cast<float*>(nullptr), tid);
   bf16* aq = static_cast<bf16*>(p.Aqk) + chunk * C * C;
   for (int idx = tid; idx < C * C / 8; idx += NTH) {

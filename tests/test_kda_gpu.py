@@ -179,6 +179,14 @@ def test_kda_chunked_full_shape_all_heads():
     check_kda_chunked(kda_case("kda_b2h16_l8k", B=2, H=16, L=8192, dk=128, dv=128, cfg_id=3))
 
 
+def test_kda_chunked_decay_spans_around_the_diagonal_bound():
+    """Decays 1.9 times the default (about 65 nats over 16 tokens on average per channel): the
+    intra kernel's diagonal blocks take the MFMA route or the entry-by-entry one, block by block,
+    both against the oracle."""
+    w = kda_case("kdac_spans", B=1, H=4, L=500, dk=128, dv=128)
+    check_kda_chunked(w, a=W.make_kda_decays(w) * np.float32(1.9))
+
+
 def test_kda_chunked_resets_and_in_place():
     """log alpha = -inf on one channel, on a whole token at a chunk start and mid-chunk: exact
     erasure as in the oracle; then S_final = S0 in place gives the same O and state."""
