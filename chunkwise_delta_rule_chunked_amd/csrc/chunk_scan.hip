@@ -113,17 +113,6 @@ struct DOp<float> {
   static constexpr bool PAIRS = false;
 };
 
-// Barrier without the compiler's workgroup fence: waits for this wave's own LDS operations
-// (and, for loading waves, its vector memory operations) and then synchronises.
-__device__ inline void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-}
-__device__ inline void barrier_all() {
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-}
-
 // Rendezvous of the loading wavefronts only (the chain wavefronts are mid-chunk): each arrives
 // once per call, `target` = (calls so far) x (loading wavefronts).  Every loading wavefront runs
 // the same number of calls, so the wait always ends.  The release orders this wave's completed
@@ -1121,13 +1110,13 @@ hipError_t launch_scan_states(const FwdParams& p, hipStream_t st) {
   return launch_seg<bf16, 128, 64, 2, 4, SEG_STATES>(p, st);
 }
 
-// KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary with 8 chain wavefronts of 2
-// tiles (value and transition columns in one workgroup), the state-storing chain with 4.
+// KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary by the summary kernel's KDA form
+// (scan_summary.hip), the state-storing chain with 4 chain wavefronts.
 hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st) {
   if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
   switch (phase) {
     case SCAN_SUMMARY:
-      return p.P > 1 ? launch_seg<bf16, 128, 64, 2, 8, SEG_SUM, false, true>(p, st) : hipSuccess;
+      return launch_scan_summary_fast_kda(p, st);
     case SCAN_COMBINE:
       return scan_phase<bf16, 128, 64>(p, SCAN_COMBINE, st);
     case SCAN_OUTPUTS:

@@ -320,6 +320,18 @@ __device__ inline void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, float x)
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);  // data operand is a u32
 }
 
+// Barrier without the compiler's workgroup fence: waits for this wave's own LDS operations
+// (and, for barrier_all, its vector memory operations) and then synchronises.  Global loads
+// still in flight stay in flight (the compiler waits for them where their registers are used).
+__device__ inline void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+__device__ inline void barrier_all() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 __device__ inline float gate_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // Lower bound applied to each token's log gate on the chunkwise path.  exp(-150) ~ 7e-66 is far

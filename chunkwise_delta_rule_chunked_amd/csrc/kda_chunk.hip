@@ -58,136 +58,177 @@ __device__ inline u32x4 pack8(const float* x) {
   return __builtin_bit_cast(u32x4, v);
 }
 
-// Diagonal block I of A and Aqk entry by entry, with the exact per-channel factor e^{Gc_r - Gc_j}
-// (j <= r, never above 1), by one wave: 16-lane group g takes the block's rows g, 7 - g, 8 + g and
-// 15 - g (34 entries), lane l of the group channels 8 l .. 8 l + 7, each entry a DPP row sum.
-__device__ __noinline__ void diag_exact(const float (*Gc)[GP], const bf16 (*Kl)[KP], float* As, bf16 (*Aq)[C + 8],
-                                        const float* bs, const bf16* qb, long HD, int valid, float scale, int I,
-                                        int lane) {
-  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
-  const int grp = lane >> 4, gl = lane & 15, c = 8 * gl;
-  float* blk = As + lower_block(I, I) * BLK;
-  const int rl4[4] = {grp, 7 - grp, 8 + grp, 15 - grp};
-  for (int u = 0; u < 4; ++u) {
-    const int rl = rl4[u], r = 16 * I + rl;
-    float kr[8], qr[8], gr[8];
-    unpack8(*reinterpret_cast<const u32x4*>(&Kl[r][c]), kr);
-    unpack8(r < valid ? *reinterpret_cast<const u32x4*>(qb + r * HD + c) : u32x4{0, 0, 0, 0}, qr);
-    *reinterpret_cast<floatx4*>(gr) = *reinterpret_cast<const floatx4*>(&Gc[r][c]);
-    *reinterpret_cast<floatx4*>(gr + 4) = *reinterpret_cast<const floatx4*>(&Gc[r][c + 4]);
-    for (int jl = 0; jl <= rl; ++jl) {
-      const int j = 16 * I + jl;
-      float kj[8], gj[8];
-      unpack8(*reinterpret_cast<const u32x4*>(&Kl[j][c]), kj);
-      *reinterpret_cast<floatx4*>(gj) = *reinterpret_cast<const floatx4*>(&Gc[j][c]);
-      *reinterpret_cast<floatx4*>(gj + 4) = *reinterpret_cast<const floatx4*>(&Gc[j][c + 4]);
-      float sg = 0.f, sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kd = kj[e] * gate_exp(gr[e] - gj[e]);
-        sg += kr[e] * kd;
-        sq += qr[e] * kd;
-      }
-      sg = row_sum16(sg);
-      sq = row_sum16(sq);
-      if (gl == 0) {
-        if (jl < rl) blk[rl * LDB + jl] = bs[r] * sg;
-        Aq[r][j] = (bf16)(scale * sq);
-      }
-    }
-  }
-}
+// LDS of the intra kernel.  The Gc table is dead once the decayed tiles and the MFMA products are
+// done; A's slots and the Aqk staging tile then take its place.
+struct IntraLds {
+  static constexpr int GC_BYTES = C * GP * 4;
+  static constexpr int SLOT_BYTES = UtSlots<C>::BYTES;
+  static constexpr int AQ_LD = C + 8;  // bf16 row pitch of the Aqk tile
+  static constexpr int AQ_BYTES = C * AQ_LD * 2;
+  static_assert(SLOT_BYTES + AQ_BYTES <= GC_BYTES, "A's slots and Aqk must fit in the Gc table");
+  union {
+    float Gc[C][GP];
+    struct {
+      unsigned char slots[SLOT_BYTES];
+      bf16 Aq[C][AQ_LD];
+    } a;
+  } u;
+  bf16 Kl[C][KP];
+  float bs[C];
+};
 
-// Largest per-channel decay span (Gc at the row before a 16-row block minus Gc at its last row) for
-// which the block's diagonal entries are taken on the MFMA: its B factors reach e^{span}, its A
-// factors e^{-span}, both far inside float32's normal range.
+// Largest per-channel decay span (Gc at the row before a 16-row block minus Gc at its last row,
+// i.e. minus the sum of the block's log decays) for which the block's diagonal entries are taken
+// on the MFMA: its B factors reach e^{span}, its A factors e^{-span}, both far inside float32's
+// normal range.
 constexpr float DIAG_SPAN = 64.f;
 
-// The entries of row block I of A and Aqk against column blocks J0 .. J0 + NJ - 1 (J <= I), each a
-// 16 x 16 product over d_k on the fp32 MFMA.  The reference is the row just before the block,
-// rho = 16 I - 1 (Gc_rho = 0 for I = 0): the A operand is k_r e^{Gc_r - Gc_rho} (scale q_r e^{...}
-// for Aqk), the B operand k_j e^{Gc_rho - Gc_j}.  Below the diagonal block (j <= rho) both factors
-// are decays (<= 1; a product that underflows is below either factor); on the diagonal block the
-// B factor is a growth bounded by e^{span}, so that block takes this route only when every
-// channel's span is within DIAG_SPAN (NaN is not), else diag_exact below.  The contraction over
-// d_k is permuted alike in both operands: lane group g takes channels 32 g .. 32 g + 31, one per
-// 4-deep step.  Results go to the A slots (times beta of the row; the diagonal block's entries
-// j < r) and to the Aqk tile (j <= r; above the diagonal it keeps its zeros).
-template <int NJ>
-__device__ __forceinline__ void block_row(const float (*Gc)[GP], const bf16 (*Kl)[KP], float* As, bf16 (*Aq)[C + 8],
-                                          const float* bs, const bf16* qb, long HD, int valid, float scale, int I,
-                                          int J0, int lane) {
-  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
-  const int g4 = lane >> 4, m = lane & 15, ra = 16 * I + m, rho = 16 * I - 1, c0 = 32 * g4;
-  const bool has_diag = J0 + NJ - 1 == I;
-  bool diag_ok = true;
-  if (has_diag) {
-    const int e = 16 * I + 15;
-    const float s0 = (rho >= 0 ? Gc[rho][lane] : 0.f) - Gc[e][lane];
-    const float s1 = (rho >= 0 ? Gc[rho][lane + 64] : 0.f) - Gc[e][lane + 64];
-    diag_ok = __all(s0 <= DIAG_SPAN && s1 <= DIAG_SPAN);
-  }
-  float qa[32];
+// Entries of row block I of A and Aqk against column blocks J0 .. J0 + NJ - 1 (J <= I), each a
+// 16 x 16 product over d_k on the fp32 MFMA, into accumulators OFF .. OFF + NJ - 1.  The reference
+// is the row just before the block, rho = 16 I - 1 (Gc_rho = 0 for I = 0): the A operand is
+// k_r e^{Gc_r - Gc_rho} (scale q_r e^{...} for Aqk), the B operand k_j e^{Gc_rho - Gc_j}.  Below the
+// diagonal block (j <= rho) both factors are decays (<= 1; a product that underflows is below
+// either factor); on the diagonal block the B factor is a growth bounded by e^{span}, which
+// diag_span_ok checks.  The contraction over d_k is permuted alike in both operands: lane group g
+// takes channels 32 g .. 32 g + 31, one per 4-deep step.
+template <int I, int J0, int NJ, int OFF, int NA>
+__device__ __forceinline__ void block_row(const IntraLds& s, __amdgpu_buffer_rsrc_t qrs, long HD, float scale,
+                                          floatx4 (&gram)[NA], floatx4 (&aqk)[NA], int lane) {
+  const int g4 = lane >> 4, m = lane & 15, ra = 16 * I + m, c0 = 32 * g4;
+  constexpr int rho = 16 * I - 1;
+  u32x4 qa[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const u32x4 x = ra < valid ? *reinterpret_cast<const u32x4*>(qb + ra * HD + c0 + 8 * u) : u32x4{0, 0, 0, 0};
-    unpack8(x, qa + 8 * u);
-  }
-  floatx4 gram[NJ], aqk[NJ];
+  for (int u = 0; u < 4; ++u)
+    qa[u] = buffer_load16(qrs, (int)((ra * HD + c0 + 8 * u) * 2));  // 0 past the sequence
 #pragma unroll
-  for (int t = 0; t < NJ; ++t) gram[t] = aqk[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NJ; ++t) gram[OFF + t] = aqk[OFF + t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
   for (int s4 = 0; s4 < 32; s4 += 4) {
     const int c = c0 + s4;
-    const floatx4 ga = *reinterpret_cast<const floatx4*>(&Gc[ra][c]);
-    const floatx4 gr = rho >= 0 ? *reinterpret_cast<const floatx4*>(&Gc[rho][c]) : floatx4{0.f, 0.f, 0.f, 0.f};
-    const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&Kl[ra][c]);
+    const floatx4 ga = *reinterpret_cast<const floatx4*>(&s.u.Gc[ra][c]);
+    const floatx4 gr = rho >= 0 ? *reinterpret_cast<const floatx4*>(&s.u.Gc[rho][c]) : floatx4{0.f, 0.f, 0.f, 0.f};
+    const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&s.Kl[ra][c]);
+    const bf16x8 q8 = __builtin_bit_cast(bf16x8, qa[s4 >> 3]);
     floatx4 gb[NJ];
     bf16x4 kb[NJ];
 #pragma unroll
     for (int t = 0; t < NJ; ++t) {
-      gb[t] = *reinterpret_cast<const floatx4*>(&Gc[16 * (J0 + t) + m][c]);
-      kb[t] = *reinterpret_cast<const bf16x4*>(&Kl[16 * (J0 + t) + m][c]);
+      gb[t] = *reinterpret_cast<const floatx4*>(&s.u.Gc[16 * (J0 + t) + m][c]);
+      kb[t] = *reinterpret_cast<const bf16x4*>(&s.Kl[16 * (J0 + t) + m][c]);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float ea = gate_exp(ga[s] - gr[s]), av = (float)ka[s] * ea, aq = scale * qa[s4 + s] * ea;
+    for (int e = 0; e < 4; ++e) {
+      const float ea = gate_exp(ga[e] - gr[e]), av = (float)ka[e] * ea;
+      const float aq = scale * (float)q8[(s4 & 4) + e] * ea;
 #pragma unroll
       for (int t = 0; t < NJ; ++t) {
-        const float bv = (float)kb[t][s] * gate_exp(gr[s] - gb[t][s]);
-        gram[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, gram[t], 0, 0, 0);
-        aqk[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, bv, aqk[t], 0, 0, 0);
+        const float bv = (float)kb[t][e] * gate_exp(gr[e] - gb[t][e]);
+        gram[OFF + t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, gram[OFF + t], 0, 0, 0);
+        aqk[OFF + t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, bv, aqk[OFF + t], 0, 0, 0);
       }
     }
   }
-  // lane (g, m) holds rows 4 g .. 4 g + 3 of column m of each block
+}
+
+// Whether every channel's decay span over diagonal block I is within DIAG_SPAN (NaN is not), for
+// the whole wave.
+template <int I>
+__device__ __forceinline__ bool diag_span_ok(const IntraLds& s, int lane) {
+  constexpr int rho = 16 * I - 1, e = 16 * I + 15;
+  const float s0 = (rho >= 0 ? s.u.Gc[rho][lane] : 0.f) - s.u.Gc[e][lane];
+  const float s1 = (rho >= 0 ? s.u.Gc[rho][lane + 64] : 0.f) - s.u.Gc[e][lane + 64];
+  return __all(s0 <= DIAG_SPAN && s1 <= DIAG_SPAN);
+}
+
+// The accumulators of block_row into A's slots (times beta of the row; on the diagonal block the
+// entries j < r) and into the Aqk tile (j <= r; zeros above the diagonal, also when diag_exact
+// takes the diagonal block).  Lane (g, m) holds rows
+// 4 g .. 4 g + 3 of column m of each block.
+template <int I, int J0, int NJ, int OFF, int NA>
+__device__ __forceinline__ void store_row(IntraLds& s, const floatx4 (&gram)[NA], const floatx4 (&aqk)[NA], bool diag_ok,
+                                          int lane) {
+  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
+  const int g4 = lane >> 4, m = lane & 15;
+  float* As = reinterpret_cast<float*>(s.u.a.slots);
 #pragma unroll
   for (int t = 0; t < NJ; ++t) {
     const int J = J0 + t;
-    if (J == I && !diag_ok) continue;
+    const bool mf = J < I || diag_ok;  // else diag_exact writes the entries j <= r
     float* blk = As + lower_block(I, J) * BLK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rl = 4 * g4 + j, r = 16 * I + rl;
-      if (J < I || m < rl) blk[rl * LDB + m] = bs[r] * gram[t][j];
-      if (J < I || m <= rl) Aq[r][16 * J + m] = (bf16)aqk[t][j];
+      if (mf && (J < I || m < rl)) blk[rl * LDB + m] = s.bs[r] * gram[OFF + t][j];
+      if (J < I || m <= rl) {
+        if (mf) s.u.a.Aq[r][16 * J + m] = (bf16)aqk[OFF + t][j];
+      } else {
+        s.u.a.Aq[r][16 * J + m] = (bf16)0.f;
+      }
     }
   }
-  if (has_diag && !diag_ok) diag_exact(Gc, Kl, As, Aq, bs, qb, HD, valid, scale, I, lane);
+}
+
+// Diagonal block I of A and Aqk entry by entry with the exact per-channel factor e^{Gc_r - Gc_j}
+// (j <= r), for blocks whose span is beyond DIAG_SPAN (a reset, very strong decay, NaN), by one
+// wave from global memory (the Gc table is gone by then): 16-lane group g takes the block's rows
+// g, 7 - g, 8 + g and 15 - g (34 entries), lane l of the group channels 8 l .. 8 l + 7.  For a row
+// r the factor runs down from j = r as a product of the per-token decays (factor_{j-1} =
+// factor_j e^{log alpha_j}), each entry a DPP row sum.  Rows past the sequence have k = q = 0 and
+// decay by nothing.
+__device__ __noinline__ void diag_exact(IntraLds& s, const bf16* qb, const bf16* kb, const float* ab, long HD,
+                                        int valid, float scale, int I, int lane) {
+  constexpr int LDB = UtSlots<C>::LDB, BLK = UtSlots<C>::BLK;
+  const int grp = lane >> 4, gl = lane & 15, c = 8 * gl;
+  float* blk = reinterpret_cast<float*>(s.u.a.slots) + lower_block(I, I) * BLK;
+  const int rl4[4] = {grp, 7 - grp, 8 + grp, 15 - grp};
+  for (int u = 0; u < 4; ++u) {
+    const int rl = rl4[u], r = 16 * I + rl;
+    float kr[8], qr[8], f[8];
+    unpack8(r < valid ? *reinterpret_cast<const u32x4*>(kb + r * HD + c) : u32x4{0, 0, 0, 0}, kr);
+    unpack8(r < valid ? *reinterpret_cast<const u32x4*>(qb + r * HD + c) : u32x4{0, 0, 0, 0}, qr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 1.f;
+    for (int jl = rl; jl >= 0; --jl) {
+      const int j = 16 * I + jl;
+      float kj[8];
+      unpack8(j < valid ? *reinterpret_cast<const u32x4*>(kb + j * HD + c) : u32x4{0, 0, 0, 0}, kj);
+      float sg = 0.f, sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kd = kj[e] * f[e];
+        sg += kr[e] * kd;
+        sq += qr[e] * kd;
+      }
+      if (j < valid) {  // the factor for j - 1 takes in token j's decay
+        const floatx4 a0 = *reinterpret_cast<const floatx4*>(ab + j * HD + c);
+        const floatx4 a1 = *reinterpret_cast<const floatx4*>(ab + j * HD + c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] *= gate_exp(a0[e] < LOG_GATE_FLOOR ? LOG_GATE_FLOOR : a0[e]);
+          f[4 + e] *= gate_exp(a1[e] < LOG_GATE_FLOOR ? LOG_GATE_FLOOR : a1[e]);
+        }
+      }
+      sg = row_sum16(sg);
+      sq = row_sum16(sq);
+      if (gl == 0) {
+        if (jl < rl) blk[rl * LDB + jl] = s.bs[r] * sg;
+        s.u.a.Aq[r][j] = (bf16)(scale * sq);
+      }
+    }
+  }
 }
 
 // One workgroup of 4 wavefronts per (sequence, head, chunk).
 //   1. keys to LDS (rows past the sequence: 0), beta, Gc per channel (two half-chunk scans)
-//   2. the 10 blocks of A and Aqk on or below the block diagonal by row block (block_row), the
-//      diagonal blocks whose decay span is too large for it entry by entry (diag_exact)
-//   3. T by ut_solve_store; Aqk, K+, Kh, Q+ and e^{Gc_C} stored
-__global__ __launch_bounds__(NTH) void kda_intra_kernel(KdaChunkParams p) {
-  __shared__ __attribute__((aligned(16))) float Gc[C][GP];
-  __shared__ __attribute__((aligned(16))) bf16 Kl[C][KP];
-  __shared__ __attribute__((aligned(16))) bf16 Aq[C][C + 8];  // Aqk staged for 16-byte stores
-  __shared__ __attribute__((aligned(16))) unsigned char slots[UtSlots<C>::BYTES];
-  __shared__ __attribute__((aligned(16))) float bs[C];
-  float* As = reinterpret_cast<float*>(slots);
+//   2. the decayed tiles K+, Kh, Q+ and e^{Gc_C} stored
+//   3. the 10 blocks of A and Aqk on or below the block diagonal on the MFMA (block_row; wave 0:
+//      row block 3 against column blocks 0, 1 and row block 0; wave 1: row block 3 against 2, 3;
+//      wave 2: row block 2; wave 3: row block 1), held in registers
+//   4. with the Gc table dead, the products into A's slots and the Aqk tile; a diagonal block
+//      whose span is too large entry by entry (diag_exact)
+//   5. T by ut_solve_store; Aqk stored
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3))) void kda_intra_kernel(KdaChunkParams p) {
+  __shared__ IntraLds s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
@@ -198,14 +239,20 @@ __global__ __launch_bounds__(NTH) void kda_intra_kernel(KdaChunkParams p) {
   const bf16* kb = static_cast<const bf16*>(p.k) + row0 * DK;
   const bf16* qb = static_cast<const bf16*>(p.q) + row0 * DK;
   const float* ab = p.a_log + row0 * DK;
+  constexpr int PIECES = C * DK / 8 / NTH;  // 16-byte pieces of a 64 x 128 bf16 tile per thread
+  // rows past the sequence read 0 through the buffer range check (no select waits for a load)
+  const int span_rows = (int)((valid - 1) * HD + DK);
+  const auto krs = buffer_rsrc(const_cast<bf16*>(kb), span_rows * 2);
+  const auto qrs = buffer_rsrc(const_cast<bf16*>(qb), span_rows * 2);
+  const auto ars = buffer_rsrc(const_cast<float*>(ab), span_rows * 4);
 
   // ---- 1. keys, beta, Gc (every thread's loads issued before its first use)
   {
-    u32x4 kv[C * DK / 8 / NTH];
+    u32x4 kv[PIECES];
 #pragma unroll
-    for (int u = 0; u < C * DK / 8 / NTH; ++u) {
+    for (int u = 0; u < PIECES; ++u) {
       const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
-      kv[u] = r < valid ? *reinterpret_cast<const u32x4*>(kb + r * HD + c) : u32x4{0, 0, 0, 0};
+      kv[u] = buffer_load16(krs, (int)((r * HD + c) * 2));
     }
     // thread t scans channel t % 128 over rows 32 (t / 128) .. + 31; positions past the sequence
     // decay by nothing; each log decay is raised to the floor (a -inf reset then decays to
@@ -214,86 +261,111 @@ __global__ __launch_bounds__(NTH) void kda_intra_kernel(KdaChunkParams p) {
     float x[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const int r = r0 + i;
-      const float a = r < valid ? ab[r * HD + c] : 0.f;
+      const float a = buffer_load4(ars, (int)(((r0 + i) * HD + c) * 4));
       x[i] = a < LOG_GATE_FLOOR ? LOG_GATE_FLOOR : a;
     }
-    if (tid < C) bs[tid] = tid < valid ? p.beta[row0 + (long)tid * p.H] : 0.f;
+    if (tid < C) s.bs[tid] = tid < valid ? p.beta[row0 + (long)tid * p.H] : 0.f;
 #pragma unroll
-    for (int u = 0; u < C * DK / 8 / NTH; ++u) {
+    for (int u = 0; u < PIECES; ++u) {
       const int idx = tid + NTH * u, r = idx >> 4, cc = (idx & 15) * 8;
-      *reinterpret_cast<u32x4*>(&Kl[r][cc]) = kv[u];
-      *reinterpret_cast<u32x4*>(&Aq[r][cc & 63]) = u32x4{0, 0, 0, 0};  // Aqk starts as zeros
+      *reinterpret_cast<u32x4*>(&s.Kl[r][cc]) = kv[u];
     }
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       run += x[i];
       x[i] = run;
-      if (r0 == 0) Gc[i][c] = run;
+      if (r0 == 0) s.u.Gc[i][c] = run;
     }
     __syncthreads();
     if (r0 != 0) {  // the second half adds the first half's total
-      const float base = Gc[31][c];
+      const float base = s.u.Gc[31][c];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) Gc[32 + i][c] = x[i] + base;
+      for (int i = 0; i < 32; ++i) s.u.Gc[32 + i][c] = x[i] + base;
     }
   }
   __syncthreads();
 
-  // ---- 2. A and Aqk by 16-row blocks (block_row); wave w: w = 0 row block 3
-  // against column blocks 0, 1 and row block 0; w = 1 row block 3 against 2, 3; w = 2 row block 2;
-  // w = 3 row block 1 (3, 2, 3 and 2 blocks)
+  // ---- 2. K+, Kh, Q+, e^{Gc_C}
+  {
+    u32x4 qv[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
+      qv[u] = buffer_load16(qrs, (int)((r * HD + c) * 2));
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
+      if (r >= valid) continue;
+      float kx[8], qx[8], kp[8], kh[8], qp[8];
+      unpack8(*reinterpret_cast<const u32x4*>(&s.Kl[r][c]), kx);
+      unpack8(qv[u], qx);
+#pragma unroll
+      for (int e4 = 0; e4 < 8; e4 += 4) {
+        const floatx4 gr = *reinterpret_cast<const floatx4*>(&s.u.Gc[r][c + e4]);
+        const floatx4 gl = *reinterpret_cast<const floatx4*>(&s.u.Gc[C - 1][c + e4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = gate_exp(gr[e]);
+          kp[e4 + e] = kx[e4 + e] * d;
+          kh[e4 + e] = kx[e4 + e] * gate_exp(gl[e] - gr[e]);
+          qp[e4 + e] = p.scale * qx[e4 + e] * d;
+        }
+      }
+      const long off = r * HD + c;
+      *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.kp) + row0 * DK + off) = pack8(kp);
+      *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.kh) + row0 * DK + off) = pack8(kh);
+      *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.qp) + row0 * DK + off) = pack8(qp);
+    }
+    if (tid < DK) p.dC[chunk * DK + tid] = gate_exp(s.u.Gc[C - 1][tid]);
+  }
+
+  // ---- 3. A and Aqk on the MFMA, in registers (up to 3 blocks per wave)
+  floatx4 gram[3], aqk[3];
+  bool diag_ok;
   if (wave == 0) {
-    block_row<2>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 3, 0, lane);
-    block_row<1>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 0, 0, lane);
+    block_row<3, 0, 2, 0>(s, qrs, HD, p.scale, gram, aqk, lane);
+    block_row<0, 0, 1, 2>(s, qrs, HD, p.scale, gram, aqk, lane);
+    diag_ok = diag_span_ok<0>(s, lane);
   } else if (wave == 1) {
-    block_row<2>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 3, 2, lane);
+    block_row<3, 2, 2, 0>(s, qrs, HD, p.scale, gram, aqk, lane);
+    diag_ok = diag_span_ok<3>(s, lane);
   } else if (wave == 2) {
-    block_row<3>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 2, 0, lane);
+    block_row<2, 0, 3, 0>(s, qrs, HD, p.scale, gram, aqk, lane);
+    diag_ok = diag_span_ok<2>(s, lane);
   } else {
-    block_row<2>(Gc, Kl, As, Aq, bs, qb, HD, valid, p.scale, 1, 0, lane);
+    block_row<1, 0, 2, 0>(s, qrs, HD, p.scale, gram, aqk, lane);
+    diag_ok = diag_span_ok<1>(s, lane);
+  }
+  __syncthreads();  // the Gc table is dead
+
+  // ---- 4. A's slots and the Aqk tile (blocks above the diagonal are written as zeros at the store)
+  if (wave == 0) {
+    store_row<3, 0, 2, 0>(s, gram, aqk, true, lane);
+    store_row<0, 0, 1, 2>(s, gram, aqk, diag_ok, lane);
+  } else if (wave == 1) {
+    store_row<3, 2, 2, 0>(s, gram, aqk, diag_ok, lane);
+  } else if (wave == 2) {
+    store_row<2, 0, 3, 0>(s, gram, aqk, diag_ok, lane);
+  } else {
+    store_row<1, 0, 2, 0>(s, gram, aqk, diag_ok, lane);
+  }
+  if (!diag_ok) {
+    const int I = wave == 0 ? 0 : wave == 1 ? 3 : wave == 2 ? 2 : 1;
+    diag_exact(s, qb, kb, ab, HD, valid, p.scale, I, lane);
   }
   __syncthreads();
 
-  // ---- 3. T, Aqk, K+, Kh, Q+, e^{Gc_C}
-  ut_solve_store<C>(As, bs, static_cast<bf16*>(p.T) + chunk * C * C, static_cast<float*>(nullptr), tid);
+  // ---- 5. T, Aqk
+  ut_solve_store<C>(reinterpret_cast<float*>(s.u.a.slots), s.bs, static_cast<bf16*>(p.T) + chunk * C * C,
+                    static_cast<float*>(nullptr), tid);
   bf16* aq = static_cast<bf16*>(p.Aqk) + chunk * C * C;
   for (int idx = tid; idx < C * C / 8; idx += NTH) {
     const int r = idx >> 3, c = (idx & 7) * 8;
-    *reinterpret_cast<u32x4*>(aq + r * C + c) = *reinterpret_cast<const u32x4*>(&Aq[r][c]);
+    const u32x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(aq + r * C + c) = c >= 16 * (r / 16 + 1) ? z : *reinterpret_cast<const u32x4*>(&s.u.a.Aq[r][c]);
   }
-  u32x4 qv[C * DK / 8 / NTH];
-#pragma unroll
-  for (int u = 0; u < C * DK / 8 / NTH; ++u) {
-    const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
-    qv[u] = r < valid ? *reinterpret_cast<const u32x4*>(qb + r * HD + c) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int u = 0; u < C * DK / 8 / NTH; ++u) {
-    const int idx = tid + NTH * u, r = idx >> 4, c = (idx & 15) * 8;
-    if (r >= valid) continue;
-    float kx[8], qx[8], kp[8], kh[8], qp[8];
-    unpack8(*reinterpret_cast<const u32x4*>(&Kl[r][c]), kx);
-    unpack8(qv[u], qx);
-#pragma unroll
-    for (int e4 = 0; e4 < 8; e4 += 4) {
-      const floatx4 gr = *reinterpret_cast<const floatx4*>(&Gc[r][c + e4]);
-      const floatx4 gl = *reinterpret_cast<const floatx4*>(&Gc[C - 1][c + e4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float d = gate_exp(gr[e]);
-        kp[e4 + e] = kx[e4 + e] * d;
-        kh[e4 + e] = kx[e4 + e] * gate_exp(gl[e] - gr[e]);
-        qp[e4 + e] = p.scale * qx[e4 + e] * d;
-      }
-    }
-    const long off = r * HD + c;
-    *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.kp) + row0 * DK + off) = pack8(kp);
-    *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.kh) + row0 * DK + off) = pack8(kh);
-    *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.qp) + row0 * DK + off) = pack8(qp);
-  }
-  if (tid < DK) p.dC[chunk * DK + tid] = gate_exp(Gc[C - 1][tid]);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -345,37 +417,53 @@ __global__ __launch_bounds__(NTO) void kda_out_kernel(KdaChunkParams p) {
   const bf16* vb = static_cast<const bf16*>(p.v) + row0 * DV;
   const bf16* Sn = static_cast<const bf16*>(p.Sn) + chunk * DV * DK;
 
-  // Q+, K+ (rows past the sequence: 0), T, Aqk
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = tid + NTO * u, r = idx >> 4, c = (idx & 15) * 8;
-    const bool ok = r < valid;
-    *reinterpret_cast<u32x4*>(Qt.at(r, c)) = ok ? *reinterpret_cast<const u32x4*>(qp + r * HD + c) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(Kt.at(r, c)) = ok ? *reinterpret_cast<const u32x4*>(kp + r * HD + c) : u32x4{0, 0, 0, 0};
-  }
+  // Q+, K+ (rows past the sequence: 0), T, Aqk, and quarter 0 of S^T and V: every load issued
+  // before the first LDS write.  Thread t moves S^T row t / 16 (16-byte piece t % 16) of a
+  // quarter, and threads t < 256 V row t / 4 (piece t % 4).
+  const int rs = tid >> 4, cs = (tid & 15) * 8, rv = tid >> 2, cv = (tid & 3) * 8;
+  const bool vthr = tid < C * QC / 8;
+  // Rows past the sequence read 0 through the buffer range check (no select waits for a load
+  // before its LDS write); a thread t >= 256 addresses V past the range and reads 0 as well.
+  const auto qrs = buffer_rsrc(const_cast<bf16*>(qp), (int)(((valid - 1) * HD + DK) * 2));
+  const auto krs = buffer_rsrc(const_cast<bf16*>(kp), (int)(((valid - 1) * HD + DK) * 2));
+  const auto vrs = buffer_rsrc(const_cast<bf16*>(vb), (int)(((valid - 1) * (long)p.H * DV + DV) * 2));
+  auto load_s = [&](int q) { return *reinterpret_cast<const u32x4*>(Sn + (QC * q + rs) * DK + cs); };
+  auto load_v = [&](int q) { return buffer_load16(vrs, (int)((rv * (long)p.H * DV + QC * q + cv) * 2)); };
   {
+    u32x4 qk[4], ta[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + NTO * u, r = idx >> 4, c = (idx & 15) * 8;
+      qk[u] = buffer_load16(qrs, (int)((r * HD + c) * 2));
+      qk[2 + u] = buffer_load16(krs, (int)((r * HD + c) * 2));
+    }
     const int r = tid >> 3, c = (tid & 7) * 8;
-    *reinterpret_cast<u32x4*>(Tt.at(r, c)) =
-        *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.T) + chunk * C * C + r * C + c);
-    *reinterpret_cast<u32x4*>(At.at(r, c)) =
-        *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.Aqk) + chunk * C * C + r * C + c);
+    ta[0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.T) + chunk * C * C + r * C + c);
+    ta[1] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.Aqk) + chunk * C * C + r * C + c);
+    const u32x4 s0 = load_s(0), v0 = load_v(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + NTO * u, rr = idx >> 4, cc = (idx & 15) * 8;
+      *reinterpret_cast<u32x4*>(Qt.at(rr, cc)) = qk[u];
+      *reinterpret_cast<u32x4*>(Kt.at(rr, cc)) = qk[2 + u];
+    }
+    *reinterpret_cast<u32x4*>(Tt.at(r, c)) = ta[0];
+    *reinterpret_cast<u32x4*>(At.at(r, c)) = ta[1];
+    *reinterpret_cast<u32x4*>(St.at(rs, cs)) = s0;
+    if (vthr) *reinterpret_cast<u32x4*>(Vq.at(rv, cv)) = v0;
   }
   const int rb = wave >> 1, ct = wave & 1;
   bf16* Ob = static_cast<bf16*>(p.O) + row0 * DV;
-#pragma unroll 1
+#pragma unroll
   for (int q = 0; q < DV / QC; ++q) {
     const int c0 = QC * q;
-    // this quarter of S^T (32 d_v rows x 128 d_k) and of V (64 rows x 32 columns)
-    {
-      const int r = tid >> 4, c = (tid & 15) * 8;
-      *reinterpret_cast<u32x4*>(St.at(r, c)) = *reinterpret_cast<const u32x4*>(Sn + (c0 + r) * DK + c);
-      if (tid < C * QC / 8) {
-        const int rv = tid >> 2, cv = (tid & 3) * 8;
-        *reinterpret_cast<u32x4*>(Vq.at(rv, cv)) =
-            rv < valid ? *reinterpret_cast<const u32x4*>(vb + rv * p.H * DV + c0 + cv) : u32x4{0, 0, 0, 0};
-      }
+    barrier_lds();
+    // the next quarter's S^T and V in flight while this one is worked on
+    u32x4 sn, vn;
+    if (q + 1 < DV / QC) {
+      sn = load_s(q + 1);
+      vn = load_v(q + 1);
     }
-    __syncthreads();
     // Y = V - K+ S (contract d_k)
     {
       floatx4 ks = {0.f, 0.f, 0.f, 0.f};
@@ -385,7 +473,7 @@ __global__ __launch_bounds__(NTO) void kda_out_kernel(KdaChunkParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) *Yq.at(16 * rb + 4 * g4 + j, 16 * ct + m) = (bf16)((float)v4[j] - ks[j]);
     }
-    __syncthreads();
+    barrier_lds();
     // V~ = T Y (T zero above the diagonal)
     {
       floatx4 vt = {0.f, 0.f, 0.f, 0.f};
@@ -395,7 +483,7 @@ __global__ __launch_bounds__(NTO) void kda_out_kernel(KdaChunkParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) *Vtq.at(16 * rb + 4 * g4 + j, 16 * ct + m) = (bf16)vt[j];
     }
-    __syncthreads();
+    barrier_lds();
     // O^T tile (value columns 16 ct .., rows 16 rb ..) = S^T Q+^T + V~^T Aqk^T (Aqk zero above the diagonal)
     {
       floatx4 o = {0.f, 0.f, 0.f, 0.f};
@@ -409,7 +497,11 @@ __global__ __launch_bounds__(NTO) void kda_out_kernel(KdaChunkParams p) {
         *reinterpret_cast<bf16x4*>(Ob + (long)row * p.H * DV + c0 + 16 * ct + 4 * g4) =
             bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
     }
-    __syncthreads();  // the quarter's tiles are rewritten next
+    if (q + 1 < DV / QC) {
+      barrier_lds();  // the quarter's S^T and V are read no more
+      *reinterpret_cast<u32x4*>(St.at(rs, cs)) = sn;
+      if (vthr) *reinterpret_cast<u32x4*>(Vq.at(rv, cv)) = vn;
+    }
   }
 }
 

@@ -149,6 +149,7 @@ hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream
 // Summary launch for bf16 inputs, d_k = d_v = 128, chunk 64 (scan_summary.hip).
 bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
+hipError_t launch_scan_summary_fast_kda(const FwdParams& p, hipStream_t st);  // KDA in chunks
 // The backward pass's state scans on the inter-chunk machinery, for bf16 inputs with
 // d_k = d_v = 128 and chunk 64 (chunk_scan.hip).  After the forward summary and combine,
 // launch_scan_states runs the forward chain writing each chunk's start state to p.Sn.  The

@@ -24,6 +24,10 @@
 // compiler keeps the state in AGPRs, copies it through VGPRs for every vector operation, and
 // waits for each LDS operand read before issuing the next.
 //
+// KDA (kda_chunk.hip; a decay per key channel): K is K e^{Gc}, Y = V - K S with no row gate, V~
+// enters the update unweighted, the update's keys are K e^{Gc_C - Gc} (a fourth staged tile), and
+// row r of the state decays by its channel's e^{Gc_C} (staged in place of the gate tables).
+//
 // Fragment layouts (16x16x32 bf16): lane (g, m) (g = lane / 16, m = lane % 16) holds
 // A[m][8g .. 8g+7], B[8g .. 8g+7][m] and D[4g .. 4g+3][m].  State row tiles 2u, 2u+1 interleave
 // their d_k indices so that the K S A-fragment is one 16-byte LDS read.
@@ -44,16 +48,22 @@ constexpr int NTP = C * C / 8 / (NW * WAVE);   // of T
 
 // one stage (bf16 elements): K [C][DK], T [C][C], V [C][DV], then fp32 gc, exp(gc) and
 // exp(gc_last - gc) tables of C
+// (KDA: the tables hold e^{Gc_C} per channel, and K e^{Gc_C - Gc} [C][DK] follows them)
 constexpr int K_OFF = 0, T_OFF = K_OFF + C * DK, V_OFF = T_OFF + C * C, G_OFF = V_OFF + C * DV;
-constexpr int STAGE = G_OFF + 3 * C * 2;
-static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS budget");
+constexpr int K2_OFF = G_OFF + 3 * C * 2;
+template <bool KDA>
+constexpr int stage_elems() { return K2_OFF + (KDA ? C * DK : 0); }
+static_assert(2 * stage_elems<true>() * 2 <= 160 * 1024, "LDS budget");
+static_assert(3 * C * 2 >= DK * 2, "the tables hold d_k floats");
 
 // This lane's share of one chunk's input.
+template <bool KDA>
 struct Regs {
   u32x4 k[NKP];
   u32x4 t[NTP];
   u32x4 v[NKP];
-  unsigned gc;
+  u32x4 kh[KDA ? NKP : 1];
+  std::conditional_t<KDA, u32x2, unsigned> gc;  // gc of token `lane` (KDA: e^{Gc_C} of channels 2 lane, + 1)
 };
 
 __device__ inline bf16x8 lds8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -85,7 +95,9 @@ __device__ inline int swz(int r, int e, int ld, int mask) {
   return r * ld + (int)(((u >> 3) ^ (unsigned)swz_key(r, mask)) * 8 + (u & 7));
 }
 
+template <bool KDA>
 __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(FwdParams p) {
+  constexpr int STAGE = stage_elems<KDA>();
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -101,7 +113,8 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   const bf16* kg = reinterpret_cast<const bf16*>(p.k) + (long)h * DK;
   const bf16* vg = reinterpret_cast<const bf16*>(p.v) + (long)h * DV;
   const bf16* Tg = reinterpret_cast<const bf16*>(p.T) + (long)head * p.NT * C * C;
-  const float* gcg = p.gc + (long)head * p.NT * C;
+  const float* gcg = KDA ? p.dC + (long)head * p.NT * DK : p.gc + (long)head * p.NT * C;
+  const bf16* khg = KDA ? reinterpret_cast<const bf16*>(p.kh) + (long)h * DK : nullptr;
 
   // this lane's pieces of a chunk: piece 64 (NKP wave + i) + lane of the K (V) tile is row q / 16,
   // chunk q % 16; of the T tile, piece 64 (NTP wave + i) + lane
@@ -121,7 +134,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // loads of chunk n (clamped to the segment's last chunk: past the end they repeat it) into
   // registers; rows past the sequence read 0
-  auto load = [&](int n, Regs& R) __attribute__((always_inline)) {
+  auto load = [&](int n, Regs<KDA>& R) __attribute__((always_inline)) {
     n = min(n, n1 - 1);
     const long P0 = (long)n * C;
     const unsigned krows = (unsigned)min((long)C, p.Lx - P0);
@@ -134,11 +147,19 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int i = 0; i < NTP; ++i) R.t[i] = buffer_load16(td, ((NTP * wave + i) * WAVE + lane) * 16);
 #pragma unroll
     for (int i = 0; i < NKP; ++i) R.v[i] = buffer_load16(vd, offG_v[i]);
-    R.gc = __builtin_bit_cast(unsigned, buffer_load4(buffer_rsrc(const_cast<float*>(gcg) + (long)n * C, C * 4), lane * 4));
+    if constexpr (KDA) {
+      const __amdgpu_buffer_rsrc_t hd =
+          buffer_rsrc(const_cast<bf16*>(khg) + ((long)b * p.Lx + P0) * HDK, krows * HDK * 2);
+#pragma unroll
+      for (int i = 0; i < NKP; ++i) R.kh[i] = buffer_load16(hd, offG_k[i]);
+      R.gc = buffer_load8(buffer_rsrc(const_cast<float*>(gcg) + (long)n * DK, DK * 4), lane * 8);
+    } else {
+      R.gc = __builtin_bit_cast(unsigned, buffer_load4(buffer_rsrc(const_cast<float*>(gcg) + (long)n * C, C * 4), lane * 4));
+    }
   };
 
   // registers -> LDS stage; wavefront 0 also writes the gate tables
-  auto write_stage = [&](bf16* st, const Regs& R) __attribute__((always_inline)) {
+  auto write_stage = [&](bf16* st, const Regs<KDA>& R) __attribute__((always_inline)) {
     const unsigned base = lds_addr(st);
 #pragma unroll
     for (int i = 0; i < NKP; ++i) {
@@ -147,7 +168,11 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
 #pragma unroll
     for (int i = 0; i < NTP; ++i) write16<0>(base + offL_t[i], R.t[i]);
-    if (wave == 0) {
+    if constexpr (KDA) {
+#pragma unroll
+      for (int i = 0; i < NKP; ++i) write16<K2_OFF * 2>(base + offL_k[i], R.kh[i]);
+      if (wave == 0) *reinterpret_cast<u32x2*>(reinterpret_cast<float*>(st + G_OFF) + 2 * lane) = R.gc;
+    } else if (wave == 0) {
       float* G = reinterpret_cast<float*>(st + G_OFF);
       const float x = __builtin_bit_cast(float, R.gc), xl = __shfl(x, C - 1, WAVE);
       G[lane] = x;
@@ -200,7 +225,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // one chunk on stage st; Rw (chunk n+1) goes to the other stage, then takes chunk n+2
   // (ISV: this wavefront's tiles are value columns; transition columns see V = 0 and read no V)
-  auto body = [&](int i, Regs& Rw, auto isv_tag) __attribute__((always_inline)) {
+  auto body = [&](int i, Regs<KDA>& Rw, auto isv_tag) __attribute__((always_inline)) {
     constexpr bool ISV = decltype(isv_tag)::value;
     bf16* st = smem + (i & 1) * STAGE;
     bf16* sn = smem + ((i & 1) ^ 1) * STAGE;
@@ -212,6 +237,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     const bf16* T = st + T_OFF;
     const bf16* V = st + V_OFF;
     const float* G = reinterpret_cast<const float*>(st + G_OFF);
+    const bf16* K2 = st + K2_OFF;
 
     // X = K S, contracting over d_k in 4 steps of 32
     floatx4 X[CT][NB];
@@ -232,11 +258,11 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
     }
 
-    // Y = V - gamma X (transition columns see V = 0)
+    // Y = V - gamma X (KDA: V - X; transition columns see V = 0)
     bf16x4 Yb[CT][NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
-      const floatx4 eg = *reinterpret_cast<const floatx4*>(G + C + 16 * bb + 4 * g4);
+      const floatx4 eg = KDA ? floatx4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const floatx4*>(G + C + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         if constexpr (ISV) {
@@ -249,7 +275,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
     }
     // V~ = T Y (T lower triangular: block pairs at or left of the diagonal), weighted by
-    // gamma_C / gamma for the state update
+    // gamma_C / gamma for the state update (KDA: unweighted)
     bf16x8 DVb[CT][NB / 2];
     bf16x4 dlo[CT];
 #pragma unroll
@@ -263,7 +289,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int c = 0; c < CT; ++c) vt[c] = mma(a, cat8(Yb[c][kb], Yb[c][kb + 1]), vt[c]);
       }
-      const floatx4 ed = *reinterpret_cast<const floatx4*>(G + 2 * C + 16 * bb + 4 * g4);
+      const floatx4 ed = KDA ? floatx4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const floatx4*>(G + 2 * C + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         if (bb & 1) DVb[c][bb >> 1] = cat8(dlo[c], cvt4(vt[c] * ed));
@@ -271,15 +297,18 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
     }
 
-    // S <- gamma_C S + K^T (gamma_C / gamma V~)
-    const float gC = G[C + C - 1];
+    // S <- gamma_C S + K^T (gamma_C / gamma V~)  (KDA: e^{Gc_C} S + (K e^{Gc_C - Gc})^T V~, row r
+    // of S decayed by its channel's factor; a lane's four rows are consecutive channels)
+    const float gC = KDA ? 1.f : G[C + C - 1];
+    const bf16* Ku = KDA ? K2 : K;
 #pragma unroll
     for (int t = 0; t < NTS; ++t) {
+      const floatx4 d4 = KDA ? *reinterpret_cast<const floatx4*>(G + dkrow(t, 4 * g4)) : floatx4{gC, gC, gC, gC};
 #pragma unroll
-      for (int c = 0; c < CT; ++c) S[c][t] *= gC;
+      for (int c = 0; c < CT; ++c) S[c][t] *= d4;
 #pragma unroll
       for (int kp = 0; kp < NB / 2; ++kp) {
-        const bf16x8 a = cat8(read_tr4(K + 32 * kp * DK + offKT[t]), read_tr4(K + (32 * kp + 16) * DK + offKT[t]));
+        const bf16x8 a = cat8(read_tr4(Ku + 32 * kp * DK + offKT[t]), read_tr4(Ku + (32 * kp + 16) * DK + offKT[t]));
 #pragma unroll
         for (int c = 0; c < CT; ++c) S[c][t] = mma(a, DVb[c][kp], S[c][t]);
       }
@@ -288,7 +317,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   };
 
   // prologue: chunk n0 staged, chunk n0+1 in flight
-  Regs R;
+  Regs<KDA> R;
   load(n0, R);
   write_stage(smem, R);
   load(n0 + 1, R);
@@ -340,7 +369,14 @@ bool scan_summary_fast_applies(const FwdParams& p, bool bf16_in) {
 
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st) {
   if (p.P <= 1) return hipSuccess;
-  hipLaunchKernelGGL(summary::summary_kernel, dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
+  hipLaunchKernelGGL(summary::summary_kernel<false>, dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_summary_fast_kda(const FwdParams& p, hipStream_t st) {
+  if (p.P <= 1) return hipSuccess;
+  if (p.DK != summary::DK || p.DV != summary::DV || p.C != summary::C) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(summary::summary_kernel<true>, dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
   return hipGetLastError();
 }
 
