@@ -83,49 +83,76 @@ struct IntraLds {
 // normal range.
 constexpr float DIAG_SPAN = 64.f;
 
+// x = hi + lo in bf16 (hi the round-to-nearest of x, lo that of the remainder): a product of two
+// such pairs, hi hi + hi lo + lo hi on the bf16 MFMA, is the float32 product to about 2^-16.
+__device__ inline void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (bf16)x[e];
+    lo[e] = (bf16)(x[e] - (float)hi[e]);
+  }
+}
+__device__ inline floatx4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, floatx4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+}
+
 // Entries of row block I of A and Aqk against column blocks J0 .. J0 + NJ - 1 (J <= I), each a
-// 16 x 16 product over d_k on the fp32 MFMA, into accumulators OFF .. OFF + NJ - 1.  The reference
-// is the row just before the block, rho = 16 I - 1 (Gc_rho = 0 for I = 0): the A operand is
-// k_r e^{Gc_r - Gc_rho} (scale q_r e^{...} for Aqk), the B operand k_j e^{Gc_rho - Gc_j}.  Below the
-// diagonal block (j <= rho) both factors are decays (<= 1; a product that underflows is below
-// either factor); on the diagonal block the B factor is a growth bounded by e^{span}, which
-// diag_span_ok checks.  The contraction over d_k is permuted alike in both operands: lane group g
-// takes channels 32 g .. 32 g + 31, one per 4-deep step.
+// 16 x 16 product over d_k on the bf16 MFMA with split operands (split8), into accumulators
+// OFF .. OFF + NJ - 1.  The reference is the row just before the block, rho = 16 I - 1 (Gc_rho = 0
+// for I = 0): the A operand is k_r e^{Gc_r - Gc_rho} (scale q_r e^{...} for Aqk), the B operand
+// k_j e^{Gc_rho - Gc_j}.  Below the diagonal block (j <= rho) both factors are decays (<= 1; a
+// product that underflows is below either factor); on the diagonal block the B factor is a
+// growth bounded by e^{span}, which diag_span_ok checks.  Lane (g, m) of a 16x16x32 step takes
+// channels 32 u + 8 g .. + 7 of row m.
 template <int I, int J0, int NJ, int OFF, int NA>
 __device__ __forceinline__ void block_row(const IntraLds& s, __amdgpu_buffer_rsrc_t qrs, long HD, float scale,
                                           floatx4 (&gram)[NA], floatx4 (&aqk)[NA], int lane) {
-  const int g4 = lane >> 4, m = lane & 15, ra = 16 * I + m, c0 = 32 * g4;
+  const int g4 = lane >> 4, m = lane & 15, ra = 16 * I + m;
   constexpr int rho = 16 * I - 1;
   u32x4 qa[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    qa[u] = buffer_load16(qrs, (int)((ra * HD + c0 + 8 * u) * 2));  // 0 past the sequence
+  for (int u = 0; u < 4; ++u) qa[u] = buffer_load16(qrs, (int)((ra * HD + 32 * u + 8 * g4) * 2));  // 0 past the sequence
 #pragma unroll
   for (int t = 0; t < NJ; ++t) gram[OFF + t] = aqk[OFF + t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int s4 = 0; s4 < 32; s4 += 4) {
-    const int c = c0 + s4;
-    const floatx4 ga = *reinterpret_cast<const floatx4*>(&s.u.Gc[ra][c]);
-    const floatx4 gr = rho >= 0 ? *reinterpret_cast<const floatx4*>(&s.u.Gc[rho][c]) : floatx4{0.f, 0.f, 0.f, 0.f};
-    const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&s.Kl[ra][c]);
-    const bf16x8 q8 = __builtin_bit_cast(bf16x8, qa[s4 >> 3]);
-    floatx4 gb[NJ];
-    bf16x4 kb[NJ];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = 32 * u + 8 * g4;
+    float ga[8], gr[8], av[8], aq[8];
+    *reinterpret_cast<floatx4*>(ga) = *reinterpret_cast<const floatx4*>(&s.u.Gc[ra][c]);
+    *reinterpret_cast<floatx4*>(ga + 4) = *reinterpret_cast<const floatx4*>(&s.u.Gc[ra][c + 4]);
+    if (rho >= 0) {
+      *reinterpret_cast<floatx4*>(gr) = *reinterpret_cast<const floatx4*>(&s.u.Gc[rho][c]);
+      *reinterpret_cast<floatx4*>(gr + 4) = *reinterpret_cast<const floatx4*>(&s.u.Gc[rho][c + 4]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gr[e] = 0.f;
+    }
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&s.Kl[ra][c]);
+    const bf16x8 q8 = __builtin_bit_cast(bf16x8, qa[u]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ea = gate_exp(ga[e] - gr[e]);
+      av[e] = (float)ka[e] * ea;
+      aq[e] = scale * (float)q8[e] * ea;
+    }
+    bf16x8 ah, al, qh, ql;
+    split8(av, ah, al);
+    split8(aq, qh, ql);
 #pragma unroll
     for (int t = 0; t < NJ; ++t) {
-      gb[t] = *reinterpret_cast<const floatx4*>(&s.u.Gc[16 * (J0 + t) + m][c]);
-      kb[t] = *reinterpret_cast<const bf16x4*>(&s.Kl[16 * (J0 + t) + m][c]);
-    }
+      const int rb = 16 * (J0 + t) + m;
+      float gb[8], bv[8];
+      *reinterpret_cast<floatx4*>(gb) = *reinterpret_cast<const floatx4*>(&s.u.Gc[rb][c]);
+      *reinterpret_cast<floatx4*>(gb + 4) = *reinterpret_cast<const floatx4*>(&s.u.Gc[rb][c + 4]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&s.Kl[rb][c]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ea = gate_exp(ga[e] - gr[e]), av = (float)ka[e] * ea;
-      const float aq = scale * (float)q8[(s4 & 4) + e] * ea;
-#pragma unroll
-      for (int t = 0; t < NJ; ++t) {
-        const float bv = (float)kb[t][e] * gate_exp(gr[e] - gb[t][e]);
-        gram[OFF + t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, gram[OFF + t], 0, 0, 0);
-        aqk[OFF + t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, bv, aqk[OFF + t], 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e) bv[e] = (float)kb[e] * gate_exp(gr[e] - gb[e]);
+      bf16x8 bh, bl;
+      split8(bv, bh, bl);
+      gram[OFF + t] = mma3(ah, al, bh, bl, gram[OFF + t]);
+      aqk[OFF + t] = mma3(qh, ql, bh, bl, aqk[OFF + t]);
     }
   }
 }
