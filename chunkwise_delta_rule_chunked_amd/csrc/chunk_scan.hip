@@ -131,12 +131,9 @@ constexpr int LDS_BUDGET = 160 * 1024;
 //   SEG_STATES  the chain from the segment's start state, writing each chunk's start state
 //               (bf16 when the inputs are bf16) instead of O
 // and REV runs the adjoint chain of the backward pass instead (see the reverse chain below).
-// KDA runs the chain of KDA in chunks (kda_chunk.hip: K e^{Gc} in place of K, no scalar gates,
-// each state row decayed by its channel's e^{Gc_C}, and K e^{Gc_C - Gc} in the update), for the
-// summary and state-storing modes.
 enum SegMode { SEG_SUM = 0, SEG_OUT = 1, SEG_STATES = 2 };
 
-template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV, bool KDA = false>
+template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV>
 struct SegCfg {
   static constexpr bool SUM = MODE == SEG_SUM;
   static constexpr bool QA = MODE == SEG_OUT || REV;  // Q staged and A formed per chunk
@@ -145,27 +142,23 @@ struct SegCfg {
   static constexpr int THREADS = (NCW + SEG_LOADERS) * WAVE;
   static constexpr int VWMAX = 16 * TPG;    // value columns staged per chunk
   static constexpr int KS = C * DK, QS = QA ? C * DK : 0, TS = C * C, AS = QA ? C * C : 0, VS = C * VWMAX;
-  // gc, exp(gc), exp(gc_last - gc), token output gates (KDA: the chunk decay per key channel)
-  static constexpr int GS = 4 * C * 4 / ES;
-  static constexpr int K2S = KDA ? C * DK : 0;  // KDA: K e^{Gc_C - Gc}, after the tables
-  static constexpr int IN = KS + QS + TS + AS + VS + GS + K2S;   // one staged chunk (elements)
-  static_assert(!KDA || (GS * ES >= DK * 4 && !REV && MODE != SEG_OUT), "KDA: summary or states");
+  static constexpr int GS = 4 * C * 4 / ES;  // gc, exp(gc), exp(gc_last - gc), token output gates
+  static constexpr int IN = KS + QS + TS + AS + VS + GS;   // one staged chunk (elements)
   static constexpr int SYNC = QA ? 16 / ES : 0;              // loader rendezvous counter
   static constexpr int NSTAGE = (2 * IN + SYNC) * ES <= LDS_BUDGET ? 2 : 1;
   static constexpr int ELEMS = NSTAGE * IN + SYNC;
   static_assert(ELEMS * ES <= LDS_BUDGET, "LDS budget");
 };
 
-template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV, bool KDA = false>
+template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV>
 __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdParams p) {
-  using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV, KDA>;
+  using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV>;
   constexpr bool SUM = Cfg::SUM, QA = Cfg::QA, OUT = MODE == SEG_OUT, STATES = MODE == SEG_STATES;
   static_assert(!REV || (sizeof(E) == 2 && MODE != SEG_OUT), "the reverse chain: bf16, summary or states");
   // dO rows past the sequence must read as zeros (they meet A^T columns of padded tokens): the
   // register-prefetched stages load through buffer ranges that give that, the one-stage copies
   // repeat row 0 instead
   static_assert(!REV || Cfg::NSTAGE == 2, "the reverse chain takes the double-buffered stage");
-  static_assert(!KDA || Cfg::NSTAGE == 2, "the KDA chain takes the double-buffered stage");
   using D = DOp<E>;
   constexpr int NB = C / 16;     // position blocks per chunk
   constexpr int NTS = DK / 16;   // state row tiles
@@ -238,13 +231,13 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     CopyPlan<E, DK, C, SEG_LOADERS> pk, pq;
     CopyPlan<E, C, C, SEG_LOADERS> pt;
     CopyPlan<E, Cfg::VWMAX, C, SEG_LOADERS> pv;
-    CopyPlan<float, 4, (KDA ? DK : C) / 4, SEG_LOADERS> pg;
+    CopyPlan<float, 4, C / 4, SEG_LOADERS> pg;
     pk.init(HDK, C, dw, lane);
     pq.init(HDK, QR, dw, lane);
     pt.init(C, C, dw, lane);
     // values by position; the reverse chain's dO (in p.v) by token
     pv.init(HDV, VW > 0 ? (REV ? QR : C) : 0, dw, lane, VW * (int)sizeof(E) / 16);
-    pg.init(4, (KDA ? DK : C) / 4, dw, lane);
+    pg.init(4, C / 4, dw, lane);
     // Issues the copies of chunk n into `stage`: gate prefix, keys and queries first, then T and
     // the values.  Returns how many of this wave's copies were issued after the first three
     // (the outputs launch forms A from those three while the rest is in flight), or 0 when the
@@ -279,7 +272,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     // exp(gc), exp(gc_last - gc) and, per token row, scale * exp(gc) at the token's last
     // sub-step (0 past the chunk's tokens) of a staged chunk, once for all chain wavefronts
     auto exps = [&](int stage) {
-      if (!KDA && dw == 0 && lane < C) {
+      if (dw == 0 && lane < C) {
         float* gcs = reinterpret_cast<float*>(smem + stage * Cfg::IN + Cfg::KS + Cfg::QS + Cfg::TS + Cfg::AS + Cfg::VS);
         const float x = gcs[lane], xl = gcs[C - 1];
         gcs[C + lane] = expf(x);
@@ -366,7 +359,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       // chunk n+1, so neither the gate tables nor A ever wait for HBM.  Loads go through
       // buffer resources over the chunk's valid rows (rows past the sequence read 0).
       u32x4 rk[decltype(pk)::NS], rq[QA ? decltype(pq)::NS : 1], rt[decltype(pt)::NS], rv[decltype(pv)::NS],
-          rg[decltype(pg)::NS], rk2[KDA ? decltype(pk)::NS : 1];
+          rg[decltype(pg)::NS];
       auto load = [&](int n) {
         const long P0 = (long)n * C;
         const int krows = (int)min((long)C, p.Lx - P0);
@@ -381,22 +374,13 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
                               krows * HDV * (int)sizeof(E));
         const __amdgpu_buffer_rsrc_t tr =
             buffer_rsrc(const_cast<E*>(Tg) + ((long)head * p.NT + n) * C * C, C * C * (int)sizeof(E));
-        const __amdgpu_buffer_rsrc_t gr =
-            KDA ? buffer_rsrc(const_cast<float*>(p.dC) + ((long)head * p.NT + n) * DK, DK * 4)
-                : buffer_rsrc(p.gc + ((long)head * p.NT + n) * C, C * 4);
+        const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(p.gc + ((long)head * p.NT + n) * C, C * 4);
 #pragma unroll
         for (int s = 0; s < decltype(pg)::NS; ++s)
           if (s < pg.n && pg.off[s] != ~0u) rg[s] = buffer_load16(gr, (int)pg.off[s]);
 #pragma unroll
         for (int s = 0; s < decltype(pk)::NS; ++s)
           if (s < pk.n && pk.off[s] != ~0u) rk[s] = buffer_load16(kr, (int)pk.off[s]);
-        if constexpr (KDA) {
-          const __amdgpu_buffer_rsrc_t k2r = buffer_rsrc(
-              const_cast<E*>(static_cast<const E*>(p.kh)) + ((long)b * p.Lx + P0) * HDK + (long)h * DK, krows * HDK * (int)sizeof(E));
-#pragma unroll
-          for (int s = 0; s < decltype(pk)::NS; ++s)
-            if (s < pk.n && pk.off[s] != ~0u) rk2[s] = buffer_load16(k2r, (int)pk.off[s]);
-        }
         if constexpr (QA) {
           const __amdgpu_buffer_rsrc_t qr =
               buffer_rsrc(const_cast<E*>(qg) + ((long)b * p.L + tok0) * HDK + (long)h * DK, qrows * HDK * (int)sizeof(E));
@@ -425,11 +409,6 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
 #pragma unroll
         for (int s = 0; s < decltype(pk)::NS; ++s)
           if (s < pk.n && pk.off[s] != ~0u) put(st, s, rk[s]);
-        if constexpr (KDA) {
-#pragma unroll
-          for (int s = 0; s < decltype(pk)::NS; ++s)
-            if (s < pk.n && pk.off[s] != ~0u) put(sv + Cfg::VS + Cfg::GS, s, rk2[s]);
-        }
         if constexpr (QA) {
 #pragma unroll
           for (int s = 0; s < decltype(pq)::NS; ++s)
@@ -546,7 +525,6 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     const float* egp = gcp + C;        // exp(gc)
     const float* edp = gcp + 2 * C;    // exp(gc_last - gc)
     const float* eqp = gcp + 3 * C;    // scale * exp(gc) of each token row's last sub-step
-    const E* K2p = Vp + Cfg::VS + Cfg::GS;  // KDA: K e^{Gc_C - Gc}; gcp then holds e^{Gc_C} per channel
     // Per-lane LDS element offsets of this chunk's fragment reads, recomputed every chunk from
     // a lane index the optimiser cannot see through (hoisted, they would pin ~20 registers).
     int lnL = lane;
@@ -660,7 +638,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
     }
 #pragma unroll
     for (int bb = 0; bb < NB && !REV; ++bb) {
-      const floatx4 eg4 = KDA ? floatx4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const floatx4*>(egp + 16 * bb + 4 * g4);
+      const floatx4 eg4 = *reinterpret_cast<const floatx4*>(egp + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         // read unconditionally (offV of a transition tile addresses the stage's first value
@@ -729,7 +707,7 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
           for (int c = 0; c < CT; ++c) vt[c] = D::mma1(a0, Yb[c][kb], vt[c]);
         }
       }
-      const floatx4 ed4 = KDA ? floatx4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const floatx4*>(edp + 16 * bb + 4 * g4);
+      const floatx4 ed4 = *reinterpret_cast<const floatx4*>(edp + 16 * bb + 4 * g4);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         Vb[c][bb] = D::cvt(vt[c]);
@@ -827,17 +805,14 @@ __global__ __launch_bounds__((NCW + SEG_LOADERS) * WAVE) void seg_kernel(FwdPara
       }
 #pragma unroll
       for (int t = 0; t < NTS; ++t) {
-        // KDA: row r of the state decays by its channel's e^{Gc_C} (the lane's 4 rows are consecutive)
-        const floatx4 dc4 = KDA ? *reinterpret_cast<const floatx4*>(gcp + dkrow(t, 4 * g4)) : floatx4{gC, gC, gC, gC};
 #pragma unroll
-        for (int c = 0; c < CT; ++c) S[c][t] *= dc4;
+        for (int c = 0; c < CT; ++c) S[c][t] *= gC;
 #pragma unroll
         for (int bb = 0; bb < NB; bb += BSTEP) {
           typename D::A a0, a1;
           if constexpr (sizeof(E) == 2) {
-            const bf16* Ku = reinterpret_cast<const bf16*>(KDA ? K2p : Kp);  // the update's keys
-            a0 = read_tr4(Ku + 16 * bb * DK + offKT[t]);
-            if constexpr (BSTEP == 2) a1 = read_tr4(Ku + 16 * (bb + 1) * DK + offKT[t]);
+            a0 = read_tr4(reinterpret_cast<const bf16*>(Kp) + 16 * bb * DK + offKT[t]);
+            if constexpr (BSTEP == 2) a1 = read_tr4(reinterpret_cast<const bf16*>(Kp) + 16 * (bb + 1) * DK + offKT[t]);
           } else {
             const Tile<E> K = make_packed_tile<E, DK>(const_cast<E*>(Kp));
             a0 = D::col4(K, 16 * bb, 16 * t, lane);
@@ -1023,16 +998,16 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void combine_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV = false, bool KDA = false>
+template <typename E, int DK, int C, int CT, int NCW, int MODE, bool REV = false>
 static hipError_t launch_seg(const FwdParams& p, hipStream_t st) {
-  using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV, KDA>;
+  using Cfg = SegCfg<E, DK, C, CT, NCW, MODE, REV>;
   constexpr int TPG = Cfg::TPG;
   const int NCT = p.DV / 16, MCT = (Cfg::SUM && !REV) ? DK / 16 : 0;
   const int G = (NCT + MCT + TPG - 1) / TPG;
   const int nseg = Cfg::SUM ? p.P - 1 : p.P;
   const long blocks = (long)nseg * p.B * p.H * G;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, NCW, MODE, REV, KDA>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0, st, p);
+  hipLaunchKernelGGL((seg_kernel<E, DK, C, CT, NCW, MODE, REV>), dim3((unsigned)blocks), dim3(Cfg::THREADS), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1106,12 +1081,11 @@ bool bwd_scans_apply(const FwdParams& p, bool bf16_in) {
 }
 
 hipError_t launch_scan_states(const FwdParams& p, hipStream_t st) {
-  if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
-  return launch_seg<bf16, 128, 64, 2, 4, SEG_STATES>(p, st);
+  return launch_scan_states_fast(p, false, st);  // scan_summary.hip, its state-storing form
 }
 
-// KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary by the summary kernel's KDA form
-// (scan_summary.hip), the state-storing chain with 4 chain wavefronts.
+// KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary and the state-storing chain by the
+// summary kernel's KDA forms (scan_summary.hip), the start states by the combine launch.
 hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st) {
   if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
   switch (phase) {
@@ -1120,7 +1094,7 @@ hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st) {
     case SCAN_COMBINE:
       return scan_phase<bf16, 128, 64>(p, SCAN_COMBINE, st);
     case SCAN_OUTPUTS:
-      return launch_seg<bf16, 128, 64, 2, 4, SEG_STATES, false, true>(p, st);
+      return launch_scan_states_fast(p, true, st);
     default:
       return hipErrorInvalidValue;
   }

@@ -33,7 +33,7 @@ struct IntraLds {
 template <typename E, typename TO, int DK, int C>
 __global__ __launch_bounds__(256) void intra_chunk_kernel(FwdParams p) {
   using Lds = IntraLds<E, DK, C>;
-  constexpr int NB = C / 16, LDB = Lds::LDB, BLK = Lds::BLK;
+  constexpr int LDB = Lds::LDB, BLK = Lds::BLK;
   constexpr int NBLK = Lds::NBLK;  // lower blocks of K K^T
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::BYTES];
   __shared__ float gcs[C], bs[C];

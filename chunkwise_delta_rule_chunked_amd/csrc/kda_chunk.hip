@@ -29,7 +29,7 @@
 namespace delta {
 namespace kdac {
 
-constexpr int DK = 128, DV = 128, C = 64, NB = C / 16;
+constexpr int DK = 128, DV = 128, C = 64;
 constexpr int GP = DK + 4;  // float row pitch of the Gc table
 constexpr int KP = DK + 8;  // bf16 row pitch of the key tile
 constexpr int NTH = 256;

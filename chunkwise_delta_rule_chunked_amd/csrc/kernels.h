@@ -150,6 +150,9 @@ hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream
 bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 hipError_t launch_scan_summary_fast_kda(const FwdParams& p, hipStream_t st);  // KDA in chunks
+// the chain on the value columns from each segment's start state, storing every chunk's start
+// state to p.Sn (and S_final): bf16, d_k = d_v = 128, chunk 64; kda: KDA in chunks
+hipError_t launch_scan_states_fast(const FwdParams& p, bool kda, hipStream_t st);
 // The backward pass's state scans on the inter-chunk machinery, for bf16 inputs with
 // d_k = d_v = 128 and chunk 64 (chunk_scan.hip).  After the forward summary and combine,
 // launch_scan_states runs the forward chain writing each chunk's start state to p.Sn.  The

@@ -24,6 +24,11 @@
 // compiler keeps the state in AGPRs, copies it through VGPRs for every vector operation, and
 // waits for each LDS operand read before issuing the next.
 //
+// STATES: the same chain on the value columns alone, from each segment's start state (written by
+// the combine launch; S0 when the sequence is not split), one 16-column tile per wavefront,
+// storing every chunk's start state (bf16, [d_v][d_k] per chunk) and, for the last segment,
+// S_final.
+//
 // KDA (kda_chunk.hip; a decay per key channel): K is K e^{Gc}, Y = V - K S with no row gate, V~
 // enters the update unweighted, the update's keys are K e^{Gc_C - Gc} (a fourth staged tile), and
 // row r of the state decays by its channel's e^{Gc_C} (staged in place of the gate tables).
@@ -95,9 +100,10 @@ __device__ inline int swz(int r, int e, int ld, int mask) {
   return r * ld + (int)(((u >> 3) ^ (unsigned)swz_key(r, mask)) * 8 + (u & 7));
 }
 
-template <bool KDA>
+template <bool KDA, bool STATES = false>
 __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(FwdParams p) {
   constexpr int STAGE = stage_elems<KDA>();
+  constexpr int CT = STATES ? 1 : summary::CT;  // state tiles per wavefront
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   // state: tiles CT*wave + c (0..7 value, 8..15 transition); accumulator row 4g + j of tile t
   // holds d_k index dkrow(t, 4g + j)
   const int tile0 = CT * wave;
-  const bool isv = tile0 < NCT;  // wave-uniform
+  const bool isv = STATES || tile0 < NCT;  // wave-uniform
   auto dkrow = [](int t, int r) { return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3); };
   floatx4 S[CT][NTS];
 #pragma unroll
@@ -206,7 +212,8 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       for (int j = 0; j < 4; ++j) {
         const int row = dkrow(t, 4 * g4 + j), col = 16 * (tile0 + c) + m;
         float x;
-        if (isv) x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
+        if (STATES && p.P > 1) x = p.Sst[(((long)head * p.P + seg) * DK + row) * DV + col];
+        else if (isv) x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
         else x = (row == col - DV) ? 1.f : 0.f;  // identity columns of the transition map
         S[c][t][j] = x;
       }
@@ -238,6 +245,12 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     const bf16* V = st + V_OFF;
     const float* G = reinterpret_cast<const float*>(st + G_OFF);
     const bf16* K2 = st + K2_OFF;
+
+    if constexpr (STATES) {  // the chunk's start state as the chain holds it (rounded to bf16)
+      bf16* Sn = reinterpret_cast<bf16*>(p.Sn) + (((long)head * p.NT + n0 + i) * DV + 16 * tile0 + m) * DK;
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) *reinterpret_cast<bf16x4*>(Sn + dkrow(t, 4 * g4)) = cvt4(S[0][t]);
+    }
 
     // X = K S, contracting over d_k in 4 steps of 32
     floatx4 X[CT][NB];
@@ -327,6 +340,14 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   } else {
     for (int i = 0; i < cnt; ++i) body(i, R, std::false_type{});
   }
+  if constexpr (STATES) {
+    if (seg == p.P - 1 && p.S_final)
+#pragma unroll
+      for (int t = 0; t < NTS; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p.S_final[((long)head * DK + dkrow(t, 4 * g4 + j)) * DV + 16 * tile0 + m] = S[0][t][j];
+    return;
+  }
 
   // the summary (S_loc: a lane's four consecutive rows are one 16-byte store; M in bf16, which
   // its consumer rounds it to for its products); segment 0 starts from S0 and needs no
@@ -370,6 +391,14 @@ bool scan_summary_fast_applies(const FwdParams& p, bool bf16_in) {
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st) {
   if (p.P <= 1) return hipSuccess;
   hipLaunchKernelGGL(summary::summary_kernel<false>, dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_states_fast(const FwdParams& p, bool kda, hipStream_t st) {
+  if (p.DK != summary::DK || p.DV != summary::DV || p.C != summary::C) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.P * p.B * p.H)), block(summary::NW * WAVE);
+  if (kda) hipLaunchKernelGGL((summary::summary_kernel<true, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((summary::summary_kernel<false, true>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
