@@ -1081,11 +1081,11 @@ bool bwd_scans_apply(const FwdParams& p, bool bf16_in) {
 }
 
 hipError_t launch_scan_states(const FwdParams& p, hipStream_t st) {
-  return launch_scan_states_fast(p, false, st);  // scan_summary.hip, its state-storing form
+  return launch_scan_states_fast(p, st);  // scan_summary.hip, its state-storing form
 }
 
-// KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary and the state-storing chain by the
-// summary kernel's KDA forms (scan_summary.hip), the start states by the combine launch.
+// KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary and the chain forming the outputs by
+// the summary kernel's KDA forms (scan_summary.hip), the start states by the combine launch.
 hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st) {
   if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
   switch (phase) {
@@ -1094,7 +1094,7 @@ hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st) {
     case SCAN_COMBINE:
       return scan_phase<bf16, 128, 64>(p, SCAN_COMBINE, st);
     case SCAN_OUTPUTS:
-      return launch_scan_states_fast(p, true, st);
+      return launch_scan_outputs_kda(p, st);
     default:
       return hipErrorInvalidValue;
   }

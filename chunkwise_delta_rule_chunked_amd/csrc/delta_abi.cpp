@@ -617,7 +617,7 @@ size_t kda_tile_bytes(const FwdParams& f) { return (size_t)f.B * f.L * f.H * 128
 size_t kda_dc_bytes(const FwdParams& f) { return (size_t)f.B * f.H * f.NT * 128 * 4; }
 size_t kda_chunked_workspace(const FwdParams& f) {
   return 2 * align_up(t_bytes(f, 2)) + 3 * align_up(kda_tile_bytes(f)) + align_up(kda_dc_bytes(f)) +
-         align_up(sm_bytes(f)) + align_up(sst_bytes(f)) + align_up(states_bytes(f) / 2);
+         align_up(sm_bytes(f)) + align_up(sst_bytes(f));
 }
 }  // namespace
 
@@ -665,7 +665,7 @@ int delta_fwd_kda_chunked(const delta_shape* s, const void* q, const void* k, co
   delta::KdaChunkParams kp;
   memset(&kp, 0, sizeof(kp));
   kp.B = f.B, kp.L = f.L, kp.H = f.H, kp.NT = f.NT, kp.scale = f.scale;
-  kp.q = q, kp.k = k, kp.v = v, kp.beta = beta, kp.a_log = a_log, kp.O = O;
+  kp.q = q, kp.k = k, kp.beta = beta, kp.a_log = a_log;
   size_t off = 0;
   kp.T = ws + off;
   off += align_up(t_bytes(f, 2));
@@ -683,14 +683,12 @@ int delta_fwd_kda_chunked(const delta_shape* s, const void* q, const void* k, co
   fs.SM = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
   off += align_up(sm_bytes(f));
   fs.Sst = f.P > 1 ? reinterpret_cast<float*>(ws + off) : nullptr;
-  off += align_up(sst_bytes(f));
-  fs.Sn = ws + off;
-  kp.Sn = fs.Sn;
-  fs.k = kp.kp, fs.kh = kp.kh, fs.dC = kp.dC, fs.v = v, fs.T = kp.T, fs.beta = beta, fs.S0 = S0, fs.S_final = S_final;
+  fs.k = kp.kp, fs.kh = kp.kh, fs.dC = kp.dC, fs.q = kp.qp, fs.Aqk = kp.Aqk, fs.v = v, fs.T = kp.T;
+  fs.beta = beta, fs.S0 = S0, fs.S_final = S_final, fs.O = O;
   if ((rc = hip_status(delta::launch_kda_intra(kp, st)))) return rc;
   for (int ph : {delta::SCAN_SUMMARY, delta::SCAN_COMBINE, delta::SCAN_OUTPUTS})
     if ((rc = hip_status(delta::launch_kda_scan(fs, ph, st)))) return rc;
-  return hip_status(delta::launch_kda_out(kp, st));
+  return DELTA_OK;
 }
 
 int delta_layer_prologue(const delta_shape* s, int32_t width, float eps, const void* xq, const void* xk,

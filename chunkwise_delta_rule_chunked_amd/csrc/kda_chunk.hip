@@ -16,12 +16,12 @@
 // Every exponent above is a decay from a later position back to an earlier one (<= 0), so no
 // factor overflows.
 //
-// Four steps (delta_abi.cpp runs them):
+// Four launches (delta_abi.cpp runs them):
 //   kda_intra_kernel   per chunk: Gc, A and Aqk, T, and the decayed tiles K+, Kh, Q+ and the
 //                      chunk decay e^{Gc_C} into the workspace;
-//   the inter-chunk scan (chunk_scan.hip, KDA mode): summaries, combine, then the chain that
-//                      stores each chunk's start state;
-//   kda_out_kernel     per chunk, all in parallel: O from the start state.
+//   the inter-chunk scan in the summary kernel's KDA forms (scan_summary.hip): segment
+//                      summaries, the combine launch's start states, then the chain from each
+//                      segment's start state forming O and S_final.
 #include "common.h"
 #include "kernels.h"
 #include "ut_solve.h"
@@ -29,7 +29,7 @@
 namespace delta {
 namespace kdac {
 
-constexpr int DK = 128, DV = 128, C = 64;
+constexpr int DK = 128, C = 64;
 constexpr int GP = DK + 4;  // float row pitch of the Gc table
 constexpr int KP = DK + 8;  // bf16 row pitch of the key tile
 constexpr int NTH = 256;
@@ -395,143 +395,6 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3))) void k
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// Outputs, one workgroup of 8 wavefronts per chunk, from the chunk's start state S (bf16,
-// transposed [d_v][d_k], as the scan stored it): per quarter of 32 value columns
-//     Y = V - K+ S;  V~ = T Y;  O = Q+ S + Aqk V~,
-// wavefront w owning the 16 x 16 tile (rows 16 (w / 2), columns 16 (w % 2)) of each.  O is formed
-// transposed (the operands of both products swapped), so a lane holds 4 consecutive columns of
-// one row and stores them with one 8-byte write.  Fragment layouts (16x16x32 bf16): lane (g, i)
-// holds A[i][8g .. 8g+7], B[8g .. 8g+7][i], D[4g .. 4g+3][i].
-constexpr int QC = 32, NW = 8, NTO = NW * WAVE;
-using L128 = TileLayout<bf16, 128>;
-using L64 = TileLayout<bf16, 64>;
-using L32 = TileLayout<bf16, QC>;
-
-__device__ inline bf16x8 frag_rows(const Tile<bf16>& t, int r0, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(t.at(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
-}
-__device__ inline bf16x8 frag_cols(const Tile<bf16>& t, int k0, int c0, int lane) {
-  const int g = lane >> 4, i = lane & 15;
-  const int r = k0 + 8 * g + (i >> 2), e = c0 + 4 * (i & 3);
-  const bf16x4 lo = read_tr4(t.at(r, e)), hi = read_tr4(t.at(r + 4, e));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ inline floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-struct __attribute__((aligned(16))) OutLds {
-  bf16 Q[C * L128::LD], K[C * L128::LD];  // Q+, K+
-  bf16 T[C * L64::LD], A[C * L64::LD];    // T, Aqk
-  bf16 S[QC * L128::LD];                  // this quarter of S^T
-  bf16 V[C * L32::LD], Y[C * L32::LD], Vt[C * L32::LD];
-};
-
-__global__ __launch_bounds__(NTO) void kda_out_kernel(KdaChunkParams p) {
-  __shared__ OutLds s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, m = lane & 15;
-  const int n = (int)(blockIdx.x % p.NT), bh = (int)(blockIdx.x / p.NT), b = bh / p.H, h = bh % p.H;
-  const long P0 = (long)n * C, chunk = (long)bh * p.NT + n;
-  const int valid = (int)min((long)C, (long)p.L - P0);
-  const long HD = (long)p.H * DK;
-  const long row0 = ((long)b * p.L + P0) * p.H + h;
-  const Tile<bf16> Qt{s.Q, L128::LD, L128::MASK}, Kt{s.K, L128::LD, L128::MASK}, St{s.S, L128::LD, L128::MASK};
-  const Tile<bf16> Tt{s.T, L64::LD, L64::MASK}, At{s.A, L64::LD, L64::MASK};
-  const Tile<bf16> Vq{s.V, L32::LD, L32::MASK}, Yq{s.Y, L32::LD, L32::MASK}, Vtq{s.Vt, L32::LD, L32::MASK};
-  const bf16* qp = static_cast<const bf16*>(p.qp) + row0 * DK;
-  const bf16* kp = static_cast<const bf16*>(p.kp) + row0 * DK;
-  const bf16* vb = static_cast<const bf16*>(p.v) + row0 * DV;
-  const bf16* Sn = static_cast<const bf16*>(p.Sn) + chunk * DV * DK;
-
-  // Q+, K+ (rows past the sequence: 0), T, Aqk, and quarter 0 of S^T and V: every load issued
-  // before the first LDS write.  Thread t moves S^T row t / 16 (16-byte piece t % 16) of a
-  // quarter, and threads t < 256 V row t / 4 (piece t % 4).
-  const int rs = tid >> 4, cs = (tid & 15) * 8, rv = tid >> 2, cv = (tid & 3) * 8;
-  const bool vthr = tid < C * QC / 8;
-  // Rows past the sequence read 0 through the buffer range check (no select waits for a load
-  // before its LDS write); a thread t >= 256 addresses V past the range and reads 0 as well.
-  const auto qrs = buffer_rsrc(const_cast<bf16*>(qp), (int)(((valid - 1) * HD + DK) * 2));
-  const auto krs = buffer_rsrc(const_cast<bf16*>(kp), (int)(((valid - 1) * HD + DK) * 2));
-  const auto vrs = buffer_rsrc(const_cast<bf16*>(vb), (int)(((valid - 1) * (long)p.H * DV + DV) * 2));
-  auto load_s = [&](int q) { return *reinterpret_cast<const u32x4*>(Sn + (QC * q + rs) * DK + cs); };
-  auto load_v = [&](int q) { return buffer_load16(vrs, (int)((rv * (long)p.H * DV + QC * q + cv) * 2)); };
-  {
-    u32x4 qk[4], ta[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + NTO * u, r = idx >> 4, c = (idx & 15) * 8;
-      qk[u] = buffer_load16(qrs, (int)((r * HD + c) * 2));
-      qk[2 + u] = buffer_load16(krs, (int)((r * HD + c) * 2));
-    }
-    const int r = tid >> 3, c = (tid & 7) * 8;
-    ta[0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.T) + chunk * C * C + r * C + c);
-    ta[1] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.Aqk) + chunk * C * C + r * C + c);
-    const u32x4 s0 = load_s(0), v0 = load_v(0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + NTO * u, rr = idx >> 4, cc = (idx & 15) * 8;
-      *reinterpret_cast<u32x4*>(Qt.at(rr, cc)) = qk[u];
-      *reinterpret_cast<u32x4*>(Kt.at(rr, cc)) = qk[2 + u];
-    }
-    *reinterpret_cast<u32x4*>(Tt.at(r, c)) = ta[0];
-    *reinterpret_cast<u32x4*>(At.at(r, c)) = ta[1];
-    *reinterpret_cast<u32x4*>(St.at(rs, cs)) = s0;
-    if (vthr) *reinterpret_cast<u32x4*>(Vq.at(rv, cv)) = v0;
-  }
-  const int rb = wave >> 1, ct = wave & 1;
-  bf16* Ob = static_cast<bf16*>(p.O) + row0 * DV;
-#pragma unroll
-  for (int q = 0; q < DV / QC; ++q) {
-    const int c0 = QC * q;
-    barrier_lds();
-    // the next quarter's S^T and V in flight while this one is worked on
-    u32x4 sn, vn;
-    if (q + 1 < DV / QC) {
-      sn = load_s(q + 1);
-      vn = load_v(q + 1);
-    }
-    // Y = V - K+ S (contract d_k)
-    {
-      floatx4 ks = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < DK; k0 += 32) ks = mma(frag_rows(Kt, 16 * rb, k0, lane), frag_rows(St, 16 * ct, k0, lane), ks);
-      const bf16x4 v4 = read_tr4(Vq.at(16 * rb + 4 * g4 + (m >> 2), 16 * ct + 4 * (m & 3)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *Yq.at(16 * rb + 4 * g4 + j, 16 * ct + m) = (bf16)((float)v4[j] - ks[j]);
-    }
-    barrier_lds();
-    // V~ = T Y (T zero above the diagonal)
-    {
-      floatx4 vt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 32)
-        if (k0 <= 16 * rb) vt = mma(frag_rows(Tt, 16 * rb, k0, lane), frag_cols(Yq, k0, 16 * ct, lane), vt);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *Vtq.at(16 * rb + 4 * g4 + j, 16 * ct + m) = (bf16)vt[j];
-    }
-    barrier_lds();
-    // O^T tile (value columns 16 ct .., rows 16 rb ..) = S^T Q+^T + V~^T Aqk^T (Aqk zero above the diagonal)
-    {
-      floatx4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < DK; k0 += 32) o = mma(frag_rows(St, 16 * ct, k0, lane), frag_rows(Qt, 16 * rb, k0, lane), o);
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 32)
-        if (k0 <= 16 * rb) o = mma(frag_cols(Vtq, k0, 16 * ct, lane), frag_rows(At, 16 * rb, k0, lane), o);
-      const int row = 16 * rb + m;
-      if (row < valid)
-        *reinterpret_cast<bf16x4*>(Ob + (long)row * p.H * DV + c0 + 16 * ct + 4 * g4) =
-            bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
-    }
-    if (q + 1 < DV / QC) {
-      barrier_lds();  // the quarter's S^T and V are read no more
-      *reinterpret_cast<u32x4*>(St.at(rs, cs)) = sn;
-      if (vthr) *reinterpret_cast<u32x4*>(Vq.at(rv, cv)) = vn;
-    }
-  }
-}
-
 }  // namespace kdac
 
 
@@ -539,13 +402,6 @@ hipError_t launch_kda_intra(const KdaChunkParams& p, hipStream_t st) {
   const long blocks = (long)p.B * p.H * p.NT;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(kdac::kda_intra_kernel, dim3((unsigned)blocks), dim3(kdac::NTH), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_kda_out(const KdaChunkParams& p, hipStream_t st) {
-  const long blocks = (long)p.B * p.H * p.NT;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(kdac::kda_out_kernel, dim3((unsigned)blocks), dim3(kdac::NTO), 0, st, p);
   return hipGetLastError();
 }
 

@@ -31,9 +31,11 @@ struct FwdParams {
   float* SM;
   float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
   // KDA chunks (kda_chunk.hip): k holds K e^{Gc}; kh K e^{Gc_C - Gc} (same layout) and dC
-  // e^{Gc_C} [B*H, NT, DK], the chunk's decay per key channel
+  // e^{Gc_C} [B*H, NT, DK], the chunk's decay per key channel; for the outputs, q holds
+  // scale Q e^{Gc} and Aqk [B*H, NT, C, C] bf16 (zeros above the diagonal)
   const void* kh;
   const float* dC;
+  const void* Aqk;
   // backward only: the summary launch also writes each segment's transition map transposed, in
   // the M part of slot P - 1 - seg of these summaries (the reverse scan's, whose segments are
   // numbered from the end and whose transition maps are the forward's transposed)
@@ -78,7 +80,6 @@ struct KdaChunkParams {
   float scale;
   const void* q;        // [B, L, H, 128] bf16
   const void* k;        // [B, L, H, 128] bf16
-  const void* v;        // [B, L, H, 128] bf16
   const float* beta;    // [B, L, H]
   const float* a_log;   // [B, L, H, 128] log alpha per key channel
   // per chunk, written by the intra launch: T and Aqk [B*H, NT, C, C] bf16; K e^{Gc},
@@ -90,8 +91,6 @@ struct KdaChunkParams {
   void* kh;
   void* qp;
   float* dC;
-  const void* Sn;       // [B*H, NT, 128, 128] bf16: each chunk's start state, transposed (output launch)
-  void* O;              // [B, L, H, 128] bf16
 };
 
 // One backward problem after validation (shape fields as in FwdParams).
@@ -151,8 +150,11 @@ bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 hipError_t launch_scan_summary_fast_kda(const FwdParams& p, hipStream_t st);  // KDA in chunks
 // the chain on the value columns from each segment's start state, storing every chunk's start
-// state to p.Sn (and S_final): bf16, d_k = d_v = 128, chunk 64; kda: KDA in chunks
-hipError_t launch_scan_states_fast(const FwdParams& p, bool kda, hipStream_t st);
+// state to p.Sn (and S_final): bf16, d_k = d_v = 128, chunk 64
+hipError_t launch_scan_states_fast(const FwdParams& p, hipStream_t st);
+// KDA in chunks: the chain on the value columns from each segment's start state forming O (and
+// S_final), from the intra kernel's K+, Kh, Q+, T, Aqk and e^{Gc_C}
+hipError_t launch_scan_outputs_kda(const FwdParams& p, hipStream_t st);
 // The backward pass's state scans on the inter-chunk machinery, for bf16 inputs with
 // d_k = d_v = 128 and chunk 64 (chunk_scan.hip).  After the forward summary and combine,
 // launch_scan_states runs the forward chain writing each chunk's start state to p.Sn.  The
@@ -165,7 +167,6 @@ hipError_t launch_rev_scan(const FwdParams& p, int phase, hipStream_t st);
 // KDA mode (chunk_scan.hip; the combine is the forward's), the output launch.
 hipError_t launch_kda_intra(const KdaChunkParams& p, hipStream_t st);
 hipError_t launch_kda_scan(const FwdParams& p, int phase, hipStream_t st);
-hipError_t launch_kda_out(const KdaChunkParams& p, hipStream_t st);
 // Backward launches (backward.hip), in order after launch_intra_chunk with float T:
 // 3 Q K^T * Gam per chunk, 0 chunk start states, 1 end-of-chunk state gradients (and dv, dS0),
 // 2 per-chunk gradients.

@@ -24,10 +24,16 @@
 // compiler keeps the state in AGPRs, copies it through VGPRs for every vector operation, and
 // waits for each LDS operand read before issuing the next.
 //
-// STATES: the same chain on the value columns alone, from each segment's start state (written by
-// the combine launch; S0 when the sequence is not split), one 16-column tile per wavefront,
+// SM_STATES (the backward's chunk start states): the same chain on the value columns alone, from each segment's start state (written
+// by the combine launch; S0 when the sequence is not split), one 16-column tile per wavefront,
 // storing every chunk's start state (bf16, [d_v][d_k] per chunk) and, for the last segment,
-// S_final.
+// S_final.  SM_OUT (KDA): that chain forming each chunk's outputs instead,
+//     O = Q+ S + Aqk V~   (Q+ = scale Q e^{Gc} staged as a fifth tile, Aqk from the intra kernel),
+// transposed (O^T = S^T Q+^T + V~^T Aqk^T): the state's B-operand registers are the A operand of
+// the first product and V~'s of the second, so a lane's accumulator holds four consecutive value
+// columns of one token, stored with one 8-byte write.  Aqk's fragments are loaded per lane from
+// global memory into registers (two stages with Aqk staged would not fit the LDS), during the
+// chunk before.
 //
 // KDA (kda_chunk.hip; a decay per key channel): K is K e^{Gc}, Y = V - K S with no row gate, V~
 // enters the update unweighted, the update's keys are K e^{Gc_C - Gc} (a fourth staged tile), and
@@ -56,18 +62,21 @@ constexpr int NTP = C * C / 8 / (NW * WAVE);   // of T
 // (KDA: the tables hold e^{Gc_C} per channel, and K e^{Gc_C - Gc} [C][DK] follows them)
 constexpr int K_OFF = 0, T_OFF = K_OFF + C * DK, V_OFF = T_OFF + C * C, G_OFF = V_OFF + C * DV;
 constexpr int K2_OFF = G_OFF + 3 * C * 2;
-template <bool KDA>
-constexpr int stage_elems() { return K2_OFF + (KDA ? C * DK : 0); }
-static_assert(2 * stage_elems<true>() * 2 <= 160 * 1024, "LDS budget");
+constexpr int Q_OFF = K2_OFF + C * DK;  // KDA outputs: Q+ [C][DK]
+enum SumMode { SM_SUMMARY = 0, SM_STATES = 1, SM_OUT = 2 };
+template <bool KDA, int MODE>
+constexpr int stage_elems() { return K2_OFF + (KDA ? C * DK : 0) + (MODE == SM_OUT ? C * DK : 0); }
+static_assert(2 * stage_elems<true, SM_OUT>() * 2 <= 160 * 1024, "LDS budget");
 static_assert(3 * C * 2 >= DK * 2, "the tables hold d_k floats");
 
 // This lane's share of one chunk's input.
-template <bool KDA>
+template <bool KDA, int MODE>
 struct Regs {
   u32x4 k[NKP];
   u32x4 t[NTP];
   u32x4 v[NKP];
   u32x4 kh[KDA ? NKP : 1];
+  u32x4 q[MODE == SM_OUT ? NKP : 1];
   std::conditional_t<KDA, u32x2, unsigned> gc;  // gc of token `lane` (KDA: e^{Gc_C} of channels 2 lane, + 1)
 };
 
@@ -100,10 +109,13 @@ __device__ inline int swz(int r, int e, int ld, int mask) {
   return r * ld + (int)(((u >> 3) ^ (unsigned)swz_key(r, mask)) * 8 + (u & 7));
 }
 
-template <bool KDA, bool STATES = false>
+template <bool KDA, int MODE = SM_SUMMARY>
 __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(FwdParams p) {
-  constexpr int STAGE = stage_elems<KDA>();
-  constexpr int CT = STATES ? 1 : summary::CT;  // state tiles per wavefront
+  constexpr bool STATES = MODE == SM_STATES, OUT = MODE == SM_OUT, CHAIN = MODE != SM_SUMMARY;
+  static_assert(!OUT || KDA, "the outputs form is KDA's");
+  constexpr int STAGE = stage_elems<KDA, MODE>();
+  constexpr int CT = CHAIN ? 1 : summary::CT;  // state tiles per wavefront
+  using R_t = Regs<KDA, MODE>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -121,6 +133,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   const bf16* Tg = reinterpret_cast<const bf16*>(p.T) + (long)head * p.NT * C * C;
   const float* gcg = KDA ? p.dC + (long)head * p.NT * DK : p.gc + (long)head * p.NT * C;
   const bf16* khg = KDA ? reinterpret_cast<const bf16*>(p.kh) + (long)h * DK : nullptr;
+  const bf16* qg = reinterpret_cast<const bf16*>(p.q) + (long)h * DK;  // outputs: Q+
 
   // this lane's pieces of a chunk: piece 64 (NKP wave + i) + lane of the K (V) tile is row q / 16,
   // chunk q % 16; of the T tile, piece 64 (NTP wave + i) + lane
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // loads of chunk n (clamped to the segment's last chunk: past the end they repeat it) into
   // registers; rows past the sequence read 0
-  auto load = [&](int n, Regs<KDA>& R) __attribute__((always_inline)) {
+  auto load = [&](int n, R_t& R) __attribute__((always_inline)) {
     n = min(n, n1 - 1);
     const long P0 = (long)n * C;
     const unsigned krows = (unsigned)min((long)C, p.Lx - P0);
@@ -159,13 +172,19 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
       for (int i = 0; i < NKP; ++i) R.kh[i] = buffer_load16(hd, offG_k[i]);
       R.gc = buffer_load8(buffer_rsrc(const_cast<float*>(gcg) + (long)n * DK, DK * 4), lane * 8);
+      if constexpr (OUT) {
+        const __amdgpu_buffer_rsrc_t qd =
+            buffer_rsrc(const_cast<bf16*>(qg) + ((long)b * p.Lx + P0) * HDK, krows * HDK * 2);
+#pragma unroll
+        for (int i = 0; i < NKP; ++i) R.q[i] = buffer_load16(qd, offG_k[i]);
+      }
     } else {
       R.gc = __builtin_bit_cast(unsigned, buffer_load4(buffer_rsrc(const_cast<float*>(gcg) + (long)n * C, C * 4), lane * 4));
     }
   };
 
   // registers -> LDS stage; wavefront 0 also writes the gate tables
-  auto write_stage = [&](bf16* st, const Regs<KDA>& R) __attribute__((always_inline)) {
+  auto write_stage = [&](bf16* st, const R_t& R) __attribute__((always_inline)) {
     const unsigned base = lds_addr(st);
 #pragma unroll
     for (int i = 0; i < NKP; ++i) {
@@ -177,6 +196,10 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     if constexpr (KDA) {
 #pragma unroll
       for (int i = 0; i < NKP; ++i) write16<K2_OFF * 2>(base + offL_k[i], R.kh[i]);
+      if constexpr (OUT) {
+#pragma unroll
+        for (int i = 0; i < NKP; ++i) write16<Q_OFF * 2>(base + offL_k[i], R.q[i]);
+      }
       if (wave == 0) *reinterpret_cast<u32x2*>(reinterpret_cast<float*>(st + G_OFF) + 2 * lane) = R.gc;
     } else if (wave == 0) {
       float* G = reinterpret_cast<float*>(st + G_OFF);
@@ -201,7 +224,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   // state: tiles CT*wave + c (0..7 value, 8..15 transition); accumulator row 4g + j of tile t
   // holds d_k index dkrow(t, 4g + j)
   const int tile0 = CT * wave;
-  const bool isv = STATES || tile0 < NCT;  // wave-uniform
+  const bool isv = CHAIN || tile0 < NCT;  // wave-uniform
   auto dkrow = [](int t, int r) { return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3); };
   floatx4 S[CT][NTS];
 #pragma unroll
@@ -212,7 +235,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       for (int j = 0; j < 4; ++j) {
         const int row = dkrow(t, 4 * g4 + j), col = 16 * (tile0 + c) + m;
         float x;
-        if (STATES && p.P > 1) x = p.Sst[(((long)head * p.P + seg) * DK + row) * DV + col];
+        if (CHAIN && p.P > 1) x = p.Sst[(((long)head * p.P + seg) * DK + row) * DV + col];
         else if (isv) x = (seg == 0 && p.S0) ? p.S0[((long)head * DK + row) * DV + col] : 0.f;
         else x = (row == col - DV) ? 1.f : 0.f;  // identity columns of the transition map
         S[c][t][j] = x;
@@ -230,9 +253,31 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
   for (int c = 0; c < CT; ++c) offV[c] = swz(4 * g4 + (m >> 2), 16 * (isv ? tile0 + c : c) + 4 * (m & 3), DV, 15);
 
+  // outputs: this lane's fragments of chunk n's Aqk as the B operand of O^T += V~^T Aqk^T, for the
+  // token blocks bb and 32-token pairs kp <= bb / 2 at or left of the diagonal: Aqk row 16 bb + m,
+  // tokens 32 kp + 4 g .. + 3 and 32 kp + 16 + 4 g .. + 3 (the order of V~'s registers)
+  constexpr int NAQ = OUT ? 6 : 1;
+  u32x2 aqf[NAQ][2];
+  auto load_aq = [&](int n) __attribute__((always_inline)) {
+    if constexpr (OUT) {
+      n = min(n, n1 - 1);
+      const bf16* A = reinterpret_cast<const bf16*>(p.Aqk) + ((long)head * p.NT + n) * C * C;
+      const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(const_cast<bf16*>(A), C * C * 2);
+      int f = 0;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int kp = 0; kp <= bb / 2; ++kp, ++f) {
+          const int e = (16 * bb + m) * C + 32 * kp + 4 * g4;
+          aqf[f][0] = buffer_load8(ar, e * 2);
+          aqf[f][1] = buffer_load8(ar, (e + 16) * 2);
+        }
+    }
+  };
+
   // one chunk on stage st; Rw (chunk n+1) goes to the other stage, then takes chunk n+2
   // (ISV: this wavefront's tiles are value columns; transition columns see V = 0 and read no V)
-  auto body = [&](int i, Regs<KDA>& Rw, auto isv_tag) __attribute__((always_inline)) {
+  auto body = [&](int i, R_t& Rw, auto isv_tag) __attribute__((always_inline)) {
     constexpr bool ISV = decltype(isv_tag)::value;
     bf16* st = smem + (i & 1) * STAGE;
     bf16* sn = smem + ((i & 1) ^ 1) * STAGE;
@@ -310,6 +355,28 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
     }
 
+    // outputs, O^T = S^T Q+^T + V~^T Aqk^T per block of 16 tokens (S still the chunk's start state)
+    if constexpr (OUT) {
+      const bf16* Q = st + Q_OFF;
+      const long P0 = (long)(n0 + i) * C;
+      const int valid = (int)min((long)C, (long)p.L - P0);
+      bf16* Og = reinterpret_cast<bf16*>(p.O) + (((long)b * p.L + P0) * p.H + h) * DV + 16 * tile0 + 4 * g4;
+      int f = 0;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o = mma(cat8(cvt4(S[0][2 * u]), cvt4(S[0][2 * u + 1])), lds8(Q + 16 * bb * DK + offK[u]), o);
+#pragma unroll
+        for (int kp = 0; kp <= bb / 2; ++kp, ++f)
+          o = mma(DVb[0][kp], __builtin_bit_cast(bf16x8, u32x4{aqf[f][0][0], aqf[f][0][1], aqf[f][1][0], aqf[f][1][1]}), o);
+        const int row = 16 * bb + m;
+        if (row < valid) *reinterpret_cast<bf16x4*>(Og + (long)row * p.H * DV) = cvt4(o);
+      }
+      load_aq(n0 + i + 1);  // the next chunk's, into the registers just read
+    }
+
     // S <- gamma_C S + K^T (gamma_C / gamma V~)  (KDA: e^{Gc_C} S + (K e^{Gc_C - Gc})^T V~, row r
     // of S decayed by its channel's factor; a lane's four rows are consecutive channels)
     const float gC = KDA ? 1.f : G[C + C - 1];
@@ -330,7 +397,8 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   };
 
   // prologue: chunk n0 staged, chunk n0+1 in flight
-  Regs<KDA> R;
+  R_t R;
+  load_aq(n0);
   load(n0, R);
   write_stage(smem, R);
   load(n0 + 1, R);
@@ -340,7 +408,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
   } else {
     for (int i = 0; i < cnt; ++i) body(i, R, std::false_type{});
   }
-  if constexpr (STATES) {
+  if constexpr (CHAIN) {
     if (seg == p.P - 1 && p.S_final)
 #pragma unroll
       for (int t = 0; t < NTS; ++t)
@@ -390,22 +458,28 @@ bool scan_summary_fast_applies(const FwdParams& p, bool bf16_in) {
 
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st) {
   if (p.P <= 1) return hipSuccess;
-  hipLaunchKernelGGL(summary::summary_kernel<false>, dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
+  hipLaunchKernelGGL((summary::summary_kernel<false, summary::SM_SUMMARY>), dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_states_fast(const FwdParams& p, bool kda, hipStream_t st) {
+hipError_t launch_scan_states_fast(const FwdParams& p, hipStream_t st) {
   if (p.DK != summary::DK || p.DV != summary::DV || p.C != summary::C) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(p.P * p.B * p.H)), block(summary::NW * WAVE);
-  if (kda) hipLaunchKernelGGL((summary::summary_kernel<true, true>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((summary::summary_kernel<false, true>), grid, block, 0, st, p);
+  hipLaunchKernelGGL((summary::summary_kernel<false, summary::SM_STATES>), dim3((unsigned)(p.P * p.B * p.H)),
+                     dim3(summary::NW * WAVE), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_outputs_kda(const FwdParams& p, hipStream_t st) {
+  if (p.DK != summary::DK || p.DV != summary::DV || p.C != summary::C) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((summary::summary_kernel<true, summary::SM_OUT>), dim3((unsigned)(p.P * p.B * p.H)),
+                     dim3(summary::NW * WAVE), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_scan_summary_fast_kda(const FwdParams& p, hipStream_t st) {
   if (p.P <= 1) return hipSuccess;
   if (p.DK != summary::DK || p.DV != summary::DV || p.C != summary::C) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(summary::summary_kernel<true>, dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
+  hipLaunchKernelGGL((summary::summary_kernel<true, summary::SM_SUMMARY>), dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
   return hipGetLastError();
 }
 
