@@ -699,15 +699,16 @@ def main():
         sys.exit(1)
 
     w = W.get(args.workload)
+    if args.copy_calibration_mib and (args.kda_only or args.decode_only):
+        # the counter runs' reference: the library's streaming copy of a known size
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
+        D.measure_copy(src, torch.empty_like(src), unroll=4, blocks=4096)
+        torch.cuda.synchronize()
+        del src
     if args.kda_only:
         print(json.dumps({"workload": KDA_WORKLOAD, "kda": time_kda(args.steps, args.warmup)}), flush=True)
         return
     if args.decode_only:
-        if args.copy_calibration_mib:
-            src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
-            D.measure_copy(src, torch.empty_like(src), unroll=4, blocks=4096)
-            torch.cuda.synchronize()
-            del src
         dec = time_decode(W.DECODE, W.DECODE_STEPS)
         kd = time_decode(W.DECODE, W.DECODE_STEPS, kda=True)
         print(json.dumps({"workload": W.DECODE.name, "decode": dec, "kda_decode": kd}), flush=True)

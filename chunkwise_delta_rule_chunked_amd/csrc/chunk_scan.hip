@@ -1081,7 +1081,8 @@ bool bwd_scans_apply(const FwdParams& p, bool bf16_in) {
 }
 
 hipError_t launch_scan_states(const FwdParams& p, hipStream_t st) {
-  return launch_scan_states_fast(p, st);  // scan_summary.hip, its state-storing form
+  if (p.DK != 128 || p.DV != 128 || p.C != 64) return hipErrorInvalidValue;
+  return launch_seg<bf16, 128, 64, 2, 4, SEG_STATES>(p, st);
 }
 
 // KDA in chunks (bf16, d_k = d_v = 128, chunk 64): the summary and the chain forming the outputs by

@@ -149,9 +149,6 @@ hipError_t launch_scan_phase(const FwdParams& p, bool bf16, int phase, hipStream
 bool scan_summary_fast_applies(const FwdParams& p, bool bf16);
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st);
 hipError_t launch_scan_summary_fast_kda(const FwdParams& p, hipStream_t st);  // KDA in chunks
-// the chain on the value columns from each segment's start state, storing every chunk's start
-// state to p.Sn (and S_final): bf16, d_k = d_v = 128, chunk 64
-hipError_t launch_scan_states_fast(const FwdParams& p, hipStream_t st);
 // KDA in chunks: the chain on the value columns from each segment's start state forming O (and
 // S_final), from the intra kernel's K+, Kh, Q+, T, Aqk and e^{Gc_C}
 hipError_t launch_scan_outputs_kda(const FwdParams& p, hipStream_t st);

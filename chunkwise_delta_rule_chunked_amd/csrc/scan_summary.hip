@@ -24,10 +24,9 @@
 // compiler keeps the state in AGPRs, copies it through VGPRs for every vector operation, and
 // waits for each LDS operand read before issuing the next.
 //
-// SM_STATES (the backward's chunk start states): the same chain on the value columns alone, from each segment's start state (written
-// by the combine launch; S0 when the sequence is not split), one 16-column tile per wavefront,
-// storing every chunk's start state (bf16, [d_v][d_k] per chunk) and, for the last segment,
-// S_final.  SM_OUT (KDA): that chain forming each chunk's outputs instead,
+// SM_OUT (KDA): the same chain on the value columns alone, from each segment's start state
+// (written by the combine launch; S0 when the sequence is not split), one 16-column tile per
+// wavefront, forming each chunk's outputs and, for the last segment, S_final:
 //     O = Q+ S + Aqk V~   (Q+ = scale Q e^{Gc} staged as a fifth tile, Aqk from the intra kernel),
 // transposed (O^T = S^T Q+^T + V~^T Aqk^T): the state's B-operand registers are the A operand of
 // the first product and V~'s of the second, so a lane's accumulator holds four consecutive value
@@ -63,7 +62,7 @@ constexpr int NTP = C * C / 8 / (NW * WAVE);   // of T
 constexpr int K_OFF = 0, T_OFF = K_OFF + C * DK, V_OFF = T_OFF + C * C, G_OFF = V_OFF + C * DV;
 constexpr int K2_OFF = G_OFF + 3 * C * 2;
 constexpr int Q_OFF = K2_OFF + C * DK;  // KDA outputs: Q+ [C][DK]
-enum SumMode { SM_SUMMARY = 0, SM_STATES = 1, SM_OUT = 2 };
+enum SumMode { SM_SUMMARY = 0, SM_OUT = 2 };
 template <bool KDA, int MODE>
 constexpr int stage_elems() { return K2_OFF + (KDA ? C * DK : 0) + (MODE == SM_OUT ? C * DK : 0); }
 static_assert(2 * stage_elems<true, SM_OUT>() * 2 <= 160 * 1024, "LDS budget");
@@ -111,7 +110,7 @@ __device__ inline int swz(int r, int e, int ld, int mask) {
 
 template <bool KDA, int MODE = SM_SUMMARY>
 __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(FwdParams p) {
-  constexpr bool STATES = MODE == SM_STATES, OUT = MODE == SM_OUT, CHAIN = MODE != SM_SUMMARY;
+  constexpr bool OUT = MODE == SM_OUT, CHAIN = MODE != SM_SUMMARY;
   static_assert(!OUT || KDA, "the outputs form is KDA's");
   constexpr int STAGE = stage_elems<KDA, MODE>();
   constexpr int CT = CHAIN ? 1 : summary::CT;  // state tiles per wavefront
@@ -291,12 +290,6 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
     const float* G = reinterpret_cast<const float*>(st + G_OFF);
     const bf16* K2 = st + K2_OFF;
 
-    if constexpr (STATES) {  // the chunk's start state as the chain holds it (rounded to bf16)
-      bf16* Sn = reinterpret_cast<bf16*>(p.Sn) + (((long)head * p.NT + n0 + i) * DV + 16 * tile0 + m) * DK;
-#pragma unroll
-      for (int t = 0; t < NTS; ++t) *reinterpret_cast<bf16x4*>(Sn + dkrow(t, 4 * g4)) = cvt4(S[0][t]);
-    }
-
     // X = K S, contracting over d_k in 4 steps of 32
     floatx4 X[CT][NB];
 #pragma unroll
@@ -459,13 +452,6 @@ bool scan_summary_fast_applies(const FwdParams& p, bool bf16_in) {
 hipError_t launch_scan_summary_fast(const FwdParams& p, hipStream_t st) {
   if (p.P <= 1) return hipSuccess;
   hipLaunchKernelGGL((summary::summary_kernel<false, summary::SM_SUMMARY>), dim3((unsigned)((p.P - 1) * p.B * p.H)), dim3(summary::NW * WAVE), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_scan_states_fast(const FwdParams& p, hipStream_t st) {
-  if (p.DK != summary::DK || p.DV != summary::DV || p.C != summary::C) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((summary::summary_kernel<false, summary::SM_STATES>), dim3((unsigned)(p.P * p.B * p.H)),
-                     dim3(summary::NW * WAVE), 0, st, p);
   return hipGetLastError();
 }
 
