@@ -615,8 +615,9 @@ bool kda_chunked_shape(const delta_shape* s) {
 }
 size_t kda_tile_bytes(const FwdParams& f) { return (size_t)f.B * f.L * f.H * 128 * 2; }
 size_t kda_dc_bytes(const FwdParams& f) { return (size_t)f.B * f.H * f.NT * 128 * 4; }
+size_t kda_aqk_bytes(const FwdParams& f) { return (size_t)f.B * f.H * f.NT * delta::KDA_AQK_CHUNK_BYTES; }
 size_t kda_chunked_workspace(const FwdParams& f) {
-  return 2 * align_up(t_bytes(f, 2)) + 3 * align_up(kda_tile_bytes(f)) + align_up(kda_dc_bytes(f)) +
+  return align_up(t_bytes(f, 2)) + align_up(kda_aqk_bytes(f)) + 3 * align_up(kda_tile_bytes(f)) + align_up(kda_dc_bytes(f)) +
          align_up(sm_bytes(f)) + align_up(sst_bytes(f));
 }
 }  // namespace
@@ -670,7 +671,7 @@ int delta_fwd_kda_chunked(const delta_shape* s, const void* q, const void* k, co
   kp.T = ws + off;
   off += align_up(t_bytes(f, 2));
   kp.Aqk = ws + off;
-  off += align_up(t_bytes(f, 2));
+  off += align_up(kda_aqk_bytes(f));
   kp.kp = ws + off;
   off += align_up(kda_tile_bytes(f));
   kp.kh = ws + off;

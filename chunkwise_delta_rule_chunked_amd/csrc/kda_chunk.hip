@@ -253,7 +253,7 @@ __device__ __noinline__ void diag_exact(IntraLds& s, const bf16* qb, const bf16*
 //      wave 2: row block 2; wave 3: row block 1), held in registers
 //   4. with the Gc table dead, the products into A's slots and the Aqk tile; a diagonal block
 //      whose span is too large entry by entry (diag_exact)
-//   5. T by ut_solve_store; Aqk stored
+//   5. T by ut_solve_store; Aqk stored in the outputs chain's fragment order
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3))) void kda_intra_kernel(KdaChunkParams p) {
   __shared__ IntraLds s;
 
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3))) void k
   }
   __syncthreads();  // the Gc table is dead
 
-  // ---- 4. A's slots and the Aqk tile (blocks above the diagonal are written as zeros at the store)
+  // ---- 4. A's slots and the Aqk tile (blocks above the diagonal are never read)
   if (wave == 0) {
     store_row<3, 0, 2, 0>(s, gram, aqk, true, lane);
     store_row<0, 0, 1, 2>(s, gram, aqk, diag_ok, lane);
@@ -387,11 +387,14 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3))) void k
   // ---- 5. T, Aqk
   ut_solve_store<C>(reinterpret_cast<float*>(s.u.a.slots), s.bs, static_cast<bf16*>(p.T) + chunk * C * C,
                     static_cast<float*>(nullptr), tid);
-  bf16* aq = static_cast<bf16*>(p.Aqk) + chunk * C * C;
-  for (int idx = tid; idx < C * C / 8; idx += NTH) {
-    const int r = idx >> 3, c = (idx & 7) * 8;
-    const u32x4 z = {0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(aq + r * C + c) = c >= 16 * (r / 16 + 1) ? z : *reinterpret_cast<const u32x4*>(&s.u.a.Aq[r][c]);
+  // Aqk in the outputs chain's fragment order (KDA_AQK_FRAGS x 64 lanes x 16 bytes per chunk)
+  u32x4* aq = reinterpret_cast<u32x4*>(static_cast<char*>(p.Aqk) + chunk * KDA_AQK_CHUNK_BYTES);
+  for (int idx = tid; idx < KDA_AQK_FRAGS * 64; idx += NTH) {
+    const int f = idx >> 6, g = (idx >> 4) & 3, m = idx & 15;
+    const int bb = kda_aqk_block(f), kp = kda_aqk_pair(f), r = 16 * bb + m, c = 32 * kp + 4 * g;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(&s.u.a.Aq[r][c]);
+    const u32x2 hi = 2 * kp + 1 <= bb ? *reinterpret_cast<const u32x2*>(&s.u.a.Aq[r][c + 16]) : u32x2{0, 0};
+    aq[idx] = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 }
 

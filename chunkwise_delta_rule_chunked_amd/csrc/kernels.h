@@ -32,7 +32,8 @@ struct FwdParams {
   float* Sst;           // [B*H, P, DK, DV]: start state of each segment (segments >= 1)
   // KDA chunks (kda_chunk.hip): k holds K e^{Gc}; kh K e^{Gc_C - Gc} (same layout) and dC
   // e^{Gc_C} [B*H, NT, DK], the chunk's decay per key channel; for the outputs, q holds
-  // scale Q e^{Gc} and Aqk [B*H, NT, C, C] bf16 (zeros above the diagonal)
+  // scale Q e^{Gc} and Aqk the causal Q K^T per chunk in the outputs chain's fragment order
+  // (KDA_AQK_* below)
   const void* kh;
   const float* dC;
   const void* Aqk;
@@ -75,6 +76,16 @@ struct KdaParams {
 };
 
 // KDA forward in chunks (kda_chunk.hip): bf16, d_k = d_v = 128, chunk 64, one step per token.
+// KDA in chunks, chunk 64: Aqk's lower triangle as the outputs chain reads it, per chunk
+// KDA_AQK_FRAGS fragments of 64 lanes x 16 bytes.  Fragment f = (bb, kp) in the order (0,0) (1,0)
+// (2,0) (2,1) (3,0) (3,1) (token block bb of 16 rows, 32-token pair kp <= bb / 2); lane (g, m)
+// holds Aqk[16 bb + m][32 kp + 4 g .. + 3] and then Aqk[16 bb + m][32 kp + 16 + 4 g .. + 3] (zeros
+// past the diagonal), bf16.
+constexpr int KDA_AQK_FRAGS = 6;
+constexpr int KDA_AQK_CHUNK_BYTES = KDA_AQK_FRAGS * 64 * 16;
+__host__ __device__ constexpr int kda_aqk_block(int f) { return f == 0 ? 0 : f == 1 ? 1 : f < 4 ? 2 : 3; }
+__host__ __device__ constexpr int kda_aqk_pair(int f) { return (f == 3 || f == 5) ? 1 : 0; }
+
 struct KdaChunkParams {
   int B, L, H, NT;
   float scale;
@@ -82,7 +93,7 @@ struct KdaChunkParams {
   const void* k;        // [B, L, H, 128] bf16
   const float* beta;    // [B, L, H]
   const float* a_log;   // [B, L, H, 128] log alpha per key channel
-  // per chunk, written by the intra launch: T and Aqk [B*H, NT, C, C] bf16; K e^{Gc},
+  // per chunk, written by the intra launch: T [B*H, NT, C, C] bf16, Aqk (KDA_AQK_* below); K e^{Gc},
   // K e^{Gc_C - Gc} and scale Q e^{Gc} in the layout of k [B, L, H, 128] bf16; e^{Gc_C}
   // [B*H, NT, 128] float32
   void* T;

@@ -32,7 +32,8 @@
 // the first product and V~'s of the second, so a lane's accumulator holds four consecutive value
 // columns of one token, stored with one 8-byte write.  Aqk's fragments are loaded per lane from
 // global memory into registers (two stages with Aqk staged would not fit the LDS), during the
-// chunk before.
+// chunk before; the intra kernel stores them in that order (KDA_AQK_*, kernels.h), so each load
+// is 1 KB contiguous per wavefront.
 //
 // KDA (kda_chunk.hip; a decay per key channel): K is K e^{Gc}, Y = V - K S with no row gate, V~
 // enters the update unweighted, the update's keys are K e^{Gc_C - Gc} (a fourth staged tile), and
@@ -254,23 +255,17 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // outputs: this lane's fragments of chunk n's Aqk as the B operand of O^T += V~^T Aqk^T, for the
   // token blocks bb and 32-token pairs kp <= bb / 2 at or left of the diagonal: Aqk row 16 bb + m,
-  // tokens 32 kp + 4 g .. + 3 and 32 kp + 16 + 4 g .. + 3 (the order of V~'s registers)
-  constexpr int NAQ = OUT ? 6 : 1;
-  u32x2 aqf[NAQ][2];
+  // tokens 32 kp + 4 g .. + 3 and 32 kp + 16 + 4 g .. + 3 (the order of V~'s registers), stored
+  // so by the intra kernel
+  constexpr int NAQ = OUT ? KDA_AQK_FRAGS : 1;
+  u32x4 aqf[NAQ];
   auto load_aq = [&](int n) __attribute__((always_inline)) {
     if constexpr (OUT) {
       n = min(n, n1 - 1);
-      const bf16* A = reinterpret_cast<const bf16*>(p.Aqk) + ((long)head * p.NT + n) * C * C;
-      const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(const_cast<bf16*>(A), C * C * 2);
-      int f = 0;
+      const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(
+          static_cast<char*>(const_cast<void*>(p.Aqk)) + ((long)head * p.NT + n) * KDA_AQK_CHUNK_BYTES, KDA_AQK_CHUNK_BYTES);
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-        for (int kp = 0; kp <= bb / 2; ++kp, ++f) {
-          const int e = (16 * bb + m) * C + 32 * kp + 4 * g4;
-          aqf[f][0] = buffer_load8(ar, e * 2);
-          aqf[f][1] = buffer_load8(ar, (e + 16) * 2);
-        }
+      for (int f = 0; f < NAQ; ++f) aqf[f] = buffer_load16(ar, (f * WAVE + lane) * 16);
     }
   };
 
@@ -363,7 +358,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)
           o = mma(cat8(cvt4(S[0][2 * u]), cvt4(S[0][2 * u + 1])), lds8(Q + 16 * bb * DK + offK[u]), o);
 #pragma unroll
         for (int kp = 0; kp <= bb / 2; ++kp, ++f)
-          o = mma(DVb[0][kp], __builtin_bit_cast(bf16x8, u32x4{aqf[f][0][0], aqf[f][0][1], aqf[f][1][0], aqf[f][1][1]}), o);
+          o = mma(DVb[0][kp], __builtin_bit_cast(bf16x8, aqf[f]), o);
         const int row = 16 * bb + m;
         if (row < valid) *reinterpret_cast<bf16x4*>(Og + (long)row * p.H * DV) = cvt4(o);
       }

@@ -307,8 +307,9 @@ def test_noalloc_limit(lib):
 
 def test_kda_chunked_workspace_and_argument_checks(lib):
     """delta_fwd_kda_chunked takes bf16, dk = dv = 128, chunk 64, n_h = 1 only; its workspace holds T and
-    Aqk (C x C bf16 per chunk), three bf16 tiles in the layout of k, the chunk decay (128 floats per
-    chunk), and the segment summaries and start states."""
+    Aqk's lower triangle (6 fragments of 64 lanes x 16 bytes per chunk), three bf16 tiles in the
+    layout of k, the chunk decay (128 floats per chunk), and the segment summaries and start
+    states."""
     up = lambda x: (x + 255) // 256 * 256
     L = D.load_library()
     for B, H, Ln in [(2, 16, 8192), (1, 2, 333), (2, 128, 70)]:
@@ -319,8 +320,8 @@ def test_kda_chunked_workspace_and_argument_checks(lib):
         P, _ = segments(B, H, 128, NT)
         sm = B * H * P * 128 * 256 * 4 if P > 1 else 0
         sst = B * H * P * 128 * 128 * 4 if P > 1 else 0
-        want = (2 * up(B * H * NT * 64 * 64 * 2) + 3 * up(B * Ln * H * 128 * 2) + up(B * H * NT * 128 * 4) + up(sm)
-                + up(sst))
+        want = (up(B * H * NT * 64 * 64 * 2) + up(B * H * NT * 6 * 64 * 16) + 3 * up(B * Ln * H * 128 * 2)
+                + up(B * H * NT * 128 * 4) + up(sm) + up(sst))
         assert n.value == want, (B, H, Ln)
     n = ctypes.c_size_t(0)
     for bad in (dict(dk=64), dict(dv=64), dict(chunk=32), dict(n_h=2, chunk=64), dict(dtype=D.F32)):
