@@ -200,3 +200,42 @@ def test_kda_chunked_resets_and_in_place():
     Sin = torch.from_numpy(inp["S0"]).cuda()
     O2, S2 = run_kda_chunked(w, inp, a, S_final=Sin)
     assert np.array_equal(O1, O2) and np.array_equal(S1, S2) and np.array_equal(Sin.cpu().numpy(), S1)
+
+
+def test_kda_chunked_nan_workspace_is_ignored():
+    """A workspace filled with NaN gives the same result, bit for bit, as a zeroed one (every
+    workspace byte the launches read is written first in the same call)."""
+    w = kda_case("kdac_ws", B=1, H=4, L=700, dk=128, dv=128, gate="weak")
+    inp, a = W.make_inputs(w), W.make_kda_decays(w)
+    d = inputs_to_dev(inp, w.dtype)
+    ad = torch.from_numpy(a).cuda()
+    nbytes = D.kda_chunked_workspace_bytes(w.B, w.L, w.H)
+    res = []
+    for fill in (0.0, float("nan")):
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(fill)
+        res.append(D.fwd_kda_chunked(d["q"], d["k"], d["v"], d["beta"], ad, d["S0"], workspace=ws))
+    torch.cuda.synchronize()
+    (O0, S0), (O1, S1) = res
+    assert torch.isfinite(O1.float()).all() and torch.isfinite(S1).all()
+    assert torch.equal(O0, O1) and torch.equal(S0, S1)
+
+
+@pytest.mark.parametrize("where", ["v", "a_log"])
+def test_kda_chunked_nan_propagates(where):
+    """NaN in one value, or in one channel's log decay, of head 1 at token t reaches that head's
+    output at t and at the end, and its final state; head 0, and head 1's tokens before t's chunk,
+    stay finite (inside the chunk it may reach earlier tokens: the zeros above the diagonal of T
+    and Aqk multiply it)."""
+    w = kda_case("kdac_nan", B=1, H=2, L=300, dk=128, dv=128, gate="weak")
+    inp, a = W.make_inputs(w), W.make_kda_decays(w)
+    t = 150
+    if where == "v":
+        v = inp["v"].copy()
+        v[0, t, 1, 5] = np.nan
+        inp = dict(inp, v=v)
+    else:
+        a[0, t, 1, 7] = np.nan
+    O, S = run_kda_chunked(w, inp, a)
+    assert np.isfinite(O[0, :, 0]).all() and np.isfinite(S[0, 0]).all()
+    assert np.isfinite(O[0, :t // 64 * 64, 1]).all()
+    assert np.isnan(O[0, t, 1]).any() and np.isnan(O[0, -1, 1]).any() and np.isnan(S[0, 1]).any()
