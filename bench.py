@@ -686,7 +686,7 @@ def main():
                     help="time only the batch-64 decode step (scalar gate, then KDA) and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (one (b, h) shard of the work); "
+        print("bench.py: the library runs on exactly one GPU (one (b, h) shard of the work); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
