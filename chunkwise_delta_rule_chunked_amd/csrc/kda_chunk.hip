@@ -13,8 +13,10 @@
 //     V~    = T (V - K+ S),            K+ = K e^{Gc}
 //     O     = Q+ S + Aqk V~,           Q+ = scale Q e^{Gc},  Aqk_rj = scale q_r . (k_j e^{Gc_r - Gc_j}), j <= r
 //     S'    = e^{Gc_C} S + Kh^T V~,    Kh = K e^{Gc_C - Gc}     (e^{Gc_C} scales row c of S)
-// Every exponent above is a decay from a later position back to an earlier one (<= 0), so no
-// factor overflows.
+// Every exponent above is a decay from a later position back to an earlier one (<= 0).  The block
+// products below split e^{Gc_r - Gc_j} at a reference row between the two; below the block
+// diagonal both halves are decays, on it one half grows, and a bound on its span keeps it finite
+// (block_row, diag_span_ok).
 //
 // Four launches (delta_abi.cpp runs them):
 //   kda_intra_kernel   per chunk: Gc, A and Aqk, T, and the decayed tiles K+, Kh, Q+ and the
