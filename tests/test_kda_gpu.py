@@ -239,3 +239,35 @@ def test_kda_chunked_nan_propagates(where):
     assert np.isfinite(O[0, :, 0]).all() and np.isfinite(S[0, 0]).all()
     assert np.isfinite(O[0, :t // 64 * 64, 1]).all()
     assert np.isnan(O[0, t, 1]).any() and np.isnan(O[0, -1, 1]).any() and np.isnan(S[0, 1]).any()
+
+
+@pytest.mark.parametrize("what", ["nan_decay", "posinf_decay", "nan_beta", "ok_neginf_decay"])
+def test_kda_chunked_validate(monkeypatch, what):
+    """With DELTA_VALIDATE=1, a NaN or +inf log decay or a non-finite beta returns
+    DELTA_ERR_BAD_VALUE (-8) and leaves the outputs untouched; a -inf log decay (a reset) passes."""
+    w = kda_case("kdac_validate", B=1, H=2, L=300, dk=128, dv=128, gate="weak")
+    inp, a = W.make_inputs(w), W.make_kda_decays(w)
+    beta = inp["beta"].copy()
+    if what == "nan_decay":
+        a[0, 217, 1, 9] = np.nan
+    elif what == "posinf_decay":
+        a[0, 217, 1, 9] = np.inf
+    elif what == "nan_beta":
+        beta[0, 217, 1] = np.nan
+    else:
+        a[0, 217, 1, 9] = -np.inf
+    d = inputs_to_dev(dict(inp, beta=beta), w.dtype)
+    ad = torch.from_numpy(a).cuda()
+    O = torch.full((w.B, w.L, w.H, w.dv), 7.0, dtype=torch.bfloat16, device="cuda")
+    S = torch.full((w.B, w.H, w.dk, w.dv), 7.0, dtype=torch.float32, device="cuda")
+    monkeypatch.setenv("DELTA_VALIDATE", "1")
+    if what == "ok_neginf_decay":
+        D.fwd_kda_chunked(d["q"], d["k"], d["v"], d["beta"], ad, d["S0"], O=O, S_final=S)
+        torch.cuda.synchronize()
+        assert torch.isfinite(O.float()).all() and torch.isfinite(S).all()
+        return
+    with pytest.raises(D.DeltaError) as e:
+        D.fwd_kda_chunked(d["q"], d["k"], d["v"], d["beta"], ad, d["S0"], O=O, S_final=S)
+    torch.cuda.synchronize()
+    assert e.value.code == -8
+    assert bool((O.float() == 7.0).all()) and bool((S == 7.0).all())
