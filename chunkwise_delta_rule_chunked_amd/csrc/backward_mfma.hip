@@ -200,15 +200,20 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
   auto fetch = [&](int q) {
     ps = *reinterpret_cast<const u32x4*>(Sn + (QC * q + fr) * DK + fc);
     pg = *reinterpret_cast<const u32x4*>(Gn + (QC * q + fr) * DK + fc);
+    pgl = *reinterpret_cast<const u32x4*>(Gnl + (QC * q + fr) * DK + fc);
   };
   fetch(0);
 #pragma unroll 1
   for (int q = 0; q < DV / QC; ++q) {
-    pgl = *reinterpret_cast<const u32x4*>(Gnl + (QC * q + fr) * DK + fc);  // (not prefetched: registers)
+    // lane-derived offsets are formed again in every quarter from a lane index the optimiser
+    // cannot see through (kept live across the loop, they spill)
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    const int mq = lq & 15, gq = lq >> 4, frq = (lq + WAVE * wave) >> 4, fcq = (lq & 15) * 8;
     __syncthreads();  // the previous quarter's tiles are no longer read
-    *reinterpret_cast<u32x4*>(Sq.at(fr, fc)) = ps;
-    *reinterpret_cast<u32x4*>(Gq.at(fr, fc)) = pg;
-    *reinterpret_cast<u32x4*>(Glq.at(fr, fc)) = pgl;
+    *reinterpret_cast<u32x4*>(Sq.at(frq, fcq)) = ps;
+    *reinterpret_cast<u32x4*>(Gq.at(frq, fcq)) = pg;
+    *reinterpret_cast<u32x4*>(Glq.at(frq, fcq)) = pgl;
     {
       const bf16x8 sv = __builtin_bit_cast(bf16x8, ps), gv = __builtin_bit_cast(bf16x8, pg),
                    gl = __builtin_bit_cast(bf16x8, pgl);
@@ -222,18 +227,18 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
     floatx4 ks = {0.f, 0.f, 0.f, 0.f}, kg = ks;
 #pragma unroll
     for (int k0 = 0; k0 < DK; k0 += 32) {
-      const bf16x8 ka = frag_rows(Kt, 16 * rb, k0, lane);
-      ks = mma(ka, frag_rows(Sq, 16 * ct, k0, lane), ks);
-      kg = mma(ka, frag_rows(Gq, 16 * ct, k0, lane), kg);
-      kg = mma(ka, frag_rows(Glq, 16 * ct, k0, lane), kg);
+      const bf16x8 ka = frag_rows(Kt, 16 * rb, k0, lq);
+      ks = mma(ka, frag_rows(Sq, 16 * ct, k0, lq), ks);
+      kg = mma(ka, frag_rows(Gq, 16 * ct, k0, lq), kg);
+      kg = mma(ka, frag_rows(Glq, 16 * ct, k0, lq), kg);
     }
     floatx4 y;
     {
-      const bf16x4 v4 = read_tr4(Vt.at(16 * rb + 4 * g4 + (m >> 2), c0 + 16 * ct + 4 * (m & 3)));
+      const bf16x4 v4 = read_tr4(Vt.at(16 * rb + 4 * gq + (mq >> 2), c0 + 16 * ct + 4 * (mq & 3)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = (float)v4[j] - s.gam[16 * rb + 4 * g4 + j] * ks[j];
+      for (int j = 0; j < 4; ++j) y[j] = (float)v4[j] - s.gam[16 * rb + 4 * gq + j] * ks[j];
     }
-    put_tile(Yq, 16 * rb, 16 * ct, y, lane);
+    put_tile(Yq, 16 * rb, 16 * ct, y, lq);
     __syncthreads();
     // V~ = T Y (T zero above the diagonal), dV~ = w KG + P^T dO (P^T zero below it).  T enters V~
     // as a bf16 pair (high part and rounding residual, from N and beta): the log-gate gradient
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 32) {
       if (k0 <= 16 * rb) {
-        const int r = 16 * rb + m, kk = k0 + 8 * g4;
+        const int r = 16 * rb + mq, kk = k0 + 8 * gq;
         const floatx4 n0 = *reinterpret_cast<const floatx4*>(&s.N[r][kk]);
         const floatx4 n1 = *reinterpret_cast<const floatx4*>(&s.N[r][kk + 4]);
         const floatx4 b0 = *reinterpret_cast<const floatx4*>(&s.beta[kk]);
@@ -255,29 +260,29 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
           th[e] = (bf16)x;
           tl[e] = (bf16)(x - (float)th[e]);
         }
-        const bf16x8 yb = frag_cols(Yq, k0, 16 * ct, lane);
+        const bf16x8 yb = frag_cols(Yq, k0, 16 * ct, lq);
         vt = mma(tl, yb, mma(th, yb, vt));
       }
       if (k0 + 32 > 16 * rb)
-        dvt = mma(frag_cols(Pt, k0, 16 * rb, lane), frag_cols(Ot, k0, c0 + 16 * ct, lane), dvt);
+        dvt = mma(frag_cols(Pt, k0, 16 * rb, lq), frag_cols(Ot, k0, c0 + 16 * ct, lq), dvt);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dvt[j] += s.w[16 * rb + 4 * g4 + j] * kg[j];
-    put_tile(Vq, 16 * rb, 16 * ct, vt, lane);
-    put_tile(dVq, 16 * rb, 16 * ct, dvt, lane);
+    for (int j = 0; j < 4; ++j) dvt[j] += s.w[16 * rb + 4 * gq + j] * kg[j];
+    put_tile(Vq, 16 * rb, 16 * ct, vt, lq);
+    put_tile(dVq, 16 * rb, 16 * ct, dvt, lq);
     __syncthreads();
     // dY = T^T dV~ (T^T zero below the diagonal)
     {
       floatx4 dy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32)
-        if (k0 + 32 > 16 * rb) dy = mma(frag_cols(Tt, k0, 16 * rb, lane), frag_cols(dVq, k0, 16 * ct, lane), dy);
-      put_tile(dYq, 16 * rb, 16 * ct, dy, lane);
+        if (k0 + 32 > 16 * rb) dy = mma(frag_cols(Tt, k0, 16 * rb, lq), frag_cols(dVq, k0, 16 * ct, lq), dy);
+      put_tile(dYq, 16 * rb, 16 * ct, dy, lq);
       // dY is dv
-      float* dvp = p.dv + ((long)b * p.Lx + P0) * p.H * DV + (long)h * DV + c0 + 16 * ct + m;
+      float* dvp = p.dv + ((long)b * p.Lx + P0) * p.H * DV + (long)h * DV + c0 + 16 * ct + mq;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rb + 4 * g4 + j;
+        const int row = 16 * rb + 4 * gq + j;
         if (row < valid) dvp[(long)row * p.H * DV] = dy[j];
       }
     }
@@ -286,18 +291,18 @@ __global__ __launch_bounds__(NTH) void bwd_chunk_mfma_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int bi = wave / 4 + 2 * t, bj = wave % 4;
-      aT[t] = mma(frag_rows(dVq, 16 * bi, 0, lane), frag_rows(Yq, 16 * bj, 0, lane), aT[t]);
-      aO[t] = mma(frag_rows(Ot, 16 * bi, c0, lane), frag_rows(Vq, 16 * bj, 0, lane), aO[t]);
+      aT[t] = mma(frag_rows(dVq, 16 * bi, 0, lq), frag_rows(Yq, 16 * bj, 0, lq), aT[t]);
+      aO[t] = mma(frag_rows(Ot, 16 * bi, c0, lq), frag_rows(Vq, 16 * bj, 0, lq), aO[t]);
     }
     {
-      const bf16x8 sb = frag_cols(Sq, 0, 16 * wave, lane), gb = frag_cols(Gq, 0, 16 * wave, lane),
-                   gbl = frag_cols(Glq, 0, 16 * wave, lane);
+      const bf16x8 sb = frag_cols(Sq, 0, 16 * wave, lq), gb = frag_cols(Gq, 0, 16 * wave, lq),
+                   gbl = frag_cols(Glq, 0, 16 * wave, lq);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        aQ[r] = mma(frag_rows(Ot, 16 * r, c0, lane), sb, aQ[r]);
-        const bf16x8 vr = frag_rows(Vq, 16 * r, 0, lane);
+        aQ[r] = mma(frag_rows(Ot, 16 * r, c0, lq), sb, aQ[r]);
+        const bf16x8 vr = frag_rows(Vq, 16 * r, 0, lq);
         a1[r] = mma(vr, gbl, mma(vr, gb, a1[r]));
-        a2[r] = mma(frag_rows(dYq, 16 * r, 0, lane), sb, a2[r]);
+        a2[r] = mma(frag_rows(dYq, 16 * r, 0, lq), sb, a2[r]);
       }
     }
   }
