@@ -190,7 +190,12 @@ __device__ inline void conv_run(const FusedSeg& sg, int B, int H, float eps, int
   const E* x = static_cast<const E*>(sg.x) + (((long)b * sg.T) * H + h) * sg.d + i0;
   E* y = static_cast<E*>(sg.y) + (((long)b * sg.T) * H + h) * sg.d + i0;
   const long step = (long)H * sg.d;                       // one token along T
-  auto row = [&](int t) { return *reinterpret_cast<const u32x4*>(x + min(max(t, 0), sg.T - 1) * step); };
+  // inputs are read once: non-temporal loads (measured 71.8 against 81.8 us for q, k and v of
+  // the 32-head 8K-token shape; non-temporal stores of the outputs, which the forward pass reads
+  // next, were slower)
+  auto row = [&](int t) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + min(max(t, 0), sg.T - 1) * step));
+  };
   float wv[VE][W];
   {
     const float* wc = sg.w + ((long)h * sg.d + i0) * W;
